@@ -1,0 +1,112 @@
+"""Seeded synthetic workloads for the MoE layer (inputs only, no layer math).
+
+Shapes follow a Qwen3-30B-A3B-shaped MoE layer (hidden 2048, 128 experts,
+top-8, expert intermediate 768, SwiGLU) plus a tiny variant.  No trained
+weights or datasets are used: every tensor is drawn here.
+
+Recipe (one ``numpy.random.default_rng(seed)`` stream, draws in this order):
+  1. router weight Wr [E, H]          ~ N(0, 0.02)
+  2. W13 [E, 2I, H] (gate rows 0..I-1, up rows I..2I-1), expert by expert,
+     ~ N(0, 0.02)
+  3. Wd [E, H, I], expert by expert,   ~ N(0, 0.02)
+  4. activations X [T, H]             ~ N(0, 1)
+  5. (Zipf-biased prefill only) a rank permutation r = 1 + permutation(E);
+     the per-expert logit offset is b_e = -s * ln(r_e) with s = 1.1, i.e.
+     the log of a Zipf(s) pmf up to its normaliser.
+Normals are drawn as float32 and rounded to bf16 (round to nearest, ties to
+even); bf16 tensors are held as their uint16 bit patterns.
+
+The batch-size sweep draws B ~ U{1..512} for 200 steps from
+``default_rng((seed, 1))`` and the step-s activations from
+``default_rng((seed, 2, s))``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class MoEShape:
+    name: str
+    T: int
+    H: int
+    E: int
+    k: int
+    I: int
+    norm_topk: bool = True
+    zipf_s: Optional[float] = None  # logit offset b_e = -s ln(rank_e)
+
+
+TINY = MoEShape("tiny T=4 H=128 E=8 k=2 I=256", T=4, H=128, E=8, k=2, I=256)
+DECODE = MoEShape("qwen3-30b-a3b moe decode T=16", T=16, H=2048, E=128, k=8, I=768)
+PREFILL_ZIPF = MoEShape("qwen3-30b-a3b moe prefill T=256 zipf1.1", T=256, H=2048, E=128, k=8,
+                        I=768, zipf_s=1.1)
+SWEEP = MoEShape("qwen3-30b-a3b moe sweep B~U[1,512]", T=512, H=2048, E=128, k=8, I=768)
+SHAPES = {"tiny": TINY, "decode": DECODE, "prefill_zipf": PREFILL_ZIPF, "sweep": SWEEP}
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit pattern, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    return (r >> np.uint32(16)).astype(np.uint16)
+
+
+def _normal_bf16(rng, shape, std):
+    return to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+
+
+@dataclass
+class MoEWeights:
+    Wr: np.ndarray      # [E, H] bf16 bits
+    W13: np.ndarray     # [E, 2I, H]
+    Wd: np.ndarray      # [E, H, I]
+    bias: Optional[np.ndarray]  # [E] float32 or None
+    rng: np.random.Generator    # the stream, positioned after the weights
+
+
+def make_weights(shape: MoEShape, seed: int = 0, w_std: float = 0.02) -> MoEWeights:
+    rng = np.random.default_rng(seed)
+    E, H, I = shape.E, shape.H, shape.I
+    Wr = _normal_bf16(rng, (E, H), w_std)
+    W13 = np.empty((E, 2 * I, H), np.uint16)
+    for e in range(E):
+        W13[e] = _normal_bf16(rng, (2 * I, H), w_std)
+    Wd = np.empty((E, H, I), np.uint16)
+    for e in range(E):
+        Wd[e] = _normal_bf16(rng, (H, I), w_std)
+    return MoEWeights(Wr, W13, Wd, None, rng)
+
+
+def make_layer(shape: MoEShape, seed: int = 0):
+    """Weights, activations X [T, H] and the optional Zipf bias, in the
+    documented draw order."""
+    w = make_weights(shape, seed)
+    X = _normal_bf16(w.rng, (shape.T, shape.H), 1.0)
+    if shape.zipf_s is not None:
+        ranks = 1 + w.rng.permutation(shape.E)
+        w.bias = (-shape.zipf_s * np.log(ranks.astype(np.float64))).astype(np.float32)
+    return w, X
+
+
+def sweep_batches(seed: int = 0, steps: int = 200, bmax: int = 512) -> np.ndarray:
+    return np.random.default_rng((seed, 1)).integers(1, bmax + 1, size=steps)
+
+
+def sweep_tokens(shape: MoEShape, step: int, B: int, seed: int = 0) -> np.ndarray:
+    return _normal_bf16(np.random.default_rng((seed, 2, step)), (B, shape.H), 1.0)
+
+
+def algorithmic_bytes(shape: MoEShape, T: int, n_active: int) -> int:
+    """Bytes the layer must move: router weight, activations in and out,
+    and the weights of every expert that received a token."""
+    H, E, I = shape.H, shape.E, shape.I
+    return 2 * E * H + 2 * T * H + 6 * H * I * n_active + 2 * T * H
+
+
+def algorithmic_flops(shape: MoEShape, T: int) -> int:
+    H, E, I, k = shape.H, shape.E, shape.I, shape.k
+    return 2 * T * E * H + 6 * T * k * H * I

@@ -1,0 +1,343 @@
+/*
+ * Plain CPU oracle for one Mixture-of-Experts layer run as a graph of tiled
+ * tasks, and for the split-K row-sum example.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark load this library.  It shares no code,
+ * header, table or constant with the HIP path: every helper below (bf16
+ * conversion included) is written here on its own, straight from the
+ * definitions, in loops meant to be checked by eye.
+ *
+ * Sources (cited by page title and figure/table/cue, as printed on the pages):
+ *   [ET-fig N]      "Event Tensor: A Unified Abstraction for Compiling Dynamic
+ *                   Megakernel" (arXiv 2604.13327), caption of Figure N.
+ *   [ET-table N]    same paper, Table N.
+ *   [ET-cast cue N] podcast episode on the same paper ("prompt-boundary-aware
+ *                   scheduling with event tensors for dynamic kernels"),
+ *                   transcript cue N.
+ *
+ * What the pages fix: the router's top-k drives per-expert token counts and
+ * the exp_indptr prefix sum [ET-fig 2, ET-fig 5b, ET-cast cue 7, cue 9]; each
+ * expert's tile range is [exp_indptr[e], exp_indptr[e+1]) [ET-cast cue 9];
+ * the split-K example sums row i of A through an event of shape n with
+ * wait_count 4 [ET-fig 3, ET-cast cue 3].  Everything else (summation order
+ * of the router, tie-break, rounding points, SwiGLU, weighted combine) is a
+ * stated reading; each function says which.
+ *
+ * Floating point: fp64 everywhere except where a float decides an integer
+ * (the router logits feeding top-k), which follows the fixed fp32 order
+ * documented at oracle_router_logits, so both sides take the top-k decision
+ * on identical values.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_INVALID (-1)
+#define ORACLE_ERR_NONFINITE (-2)
+
+/* ------------------------------------------------------------------------ */
+/* bf16 <-> fp32, written from the format definition: bf16 is the upper 16
+ * bits of an IEEE binary32.  Rounding is round-to-nearest, ties-to-even.   */
+
+static float bf16_bits_to_float(uint16_t b) {
+  uint32_t u = ((uint32_t)b) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+static uint16_t float_to_bf16_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0u) {
+    /* NaN: keep it a quiet NaN with the same sign */
+    return (uint16_t)((u >> 16) | 0x0040u);
+  }
+  uint32_t lower = u & 0xffffu;      /* the 16 bits that are dropped   */
+  uint32_t upper = u >> 16;          /* the kept part                   */
+  if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+  return (uint16_t)upper;
+}
+
+uint16_t oracle_f32_to_bf16(float f) { return float_to_bf16_bits(f); }
+float oracle_bf16_to_f32(uint16_t b) { return bf16_bits_to_float(b); }
+
+/* ------------------------------------------------------------------------ */
+/* Router logits, fixed-order fp32 (reading; the pages give no order).
+ *
+ * L[t,e] = sum_h X[t,h] * Wr[e,h]  (+ bias[e]).
+ *
+ * The order is a contract, so that the top-k decision is taken on the same
+ * fp32 values on both sides:
+ *   - the hidden dimension is cut into 8-element chunks c = 0 .. H/8-1;
+ *     chunk c belongs to virtual lane l = c mod 64;
+ *   - each lane starts from +0.0f and, over its chunks in ascending c and
+ *     the 8 elements of a chunk in ascending h, does acc = fmaf(x, w, acc);
+ *   - the 64 lane sums are combined by a halving tree: for s = 32,16,...,1
+ *     and every l < s, acc[l] = acc[l] + acc[l + s];
+ *   - the logit is acc[0], then + bias[e] (one fp32 add) if a bias is given.
+ * H must be a multiple of 8; lanes that own no chunk keep +0.0f.           */
+int oracle_router_logits(int T, int H, int E, const uint16_t *X,
+                         const uint16_t *Wr, const float *bias, float *L) {
+  if (T < 0 || H <= 0 || E <= 0 || (H % 8) != 0) return ORACLE_ERR_INVALID;
+  const int nchunk = H / 8;
+  for (int t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e) {
+      float lane[64];
+      for (int l = 0; l < 64; ++l) lane[l] = 0.0f;
+      for (int c = 0; c < nchunk; ++c) {
+        int l = c % 64;
+        for (int q = 0; q < 8; ++q) {
+          int h = 8 * c + q;
+          float x = bf16_bits_to_float(X[(size_t)t * H + h]);
+          float w = bf16_bits_to_float(Wr[(size_t)e * H + h]);
+          lane[l] = fmaf(x, w, lane[l]);
+        }
+      }
+      for (int s = 32; s >= 1; s /= 2)
+        for (int l = 0; l < s; ++l) lane[l] = lane[l] + lane[l + s];
+      float v = lane[0];
+      if (bias) v = v + bias[e];
+      L[(size_t)t * E + e] = v;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Naive fp64 dot product of the same logits, for the sanity bound only.   */
+int oracle_router_logits_f64(int T, int H, int E, const uint16_t *X,
+                             const uint16_t *Wr, const float *bias, double *L) {
+  if (T < 0 || H <= 0 || E <= 0) return ORACLE_ERR_INVALID;
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h)
+        acc += (double)bf16_bits_to_float(X[(size_t)t * H + h]) *
+               (double)bf16_bits_to_float(Wr[(size_t)e * H + h]);
+      if (bias) acc += (double)bias[e];
+      L[(size_t)t * E + e] = acc;
+    }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Top-k and routing weights [ET-fig 2: the runtime tensor "topk"].
+ *
+ * Reading: per token the k largest logits, listed by descending logit; on
+ * equal logits the lower expert index ranks first.  Weights (fp64, stored
+ * fp32): with norm_topk, softmax over E renormalised over the chosen k,
+ * i.e. exp(l_j - l_max) / sum_{i in topk} exp(l_i - l_max); without it,
+ * the plain softmax over all E logits.  NaN logits are rejected.          */
+static int ranks_before(float a, int ia, float b, int ib) {
+  /* does (a, ia) rank strictly before (b, ib)? */
+  if (a > b) return 1;
+  if (a < b) return 0;
+  return ia < ib;
+}
+
+int oracle_topk(int T, int E, int k, const float *L, int norm_topk,
+                int32_t *ids, float *w) {
+  if (T < 0 || E <= 0 || k <= 0 || k > E) return ORACLE_ERR_INVALID;
+  int *order = (int *)malloc(sizeof(int) * (size_t)E);
+  if (!order) return ORACLE_ERR_INVALID;
+  for (int t = 0; t < T; ++t) {
+    const float *row = L + (size_t)t * E;
+    for (int e = 0; e < E; ++e) {
+      if (isnan(row[e])) { free(order); return ORACLE_ERR_NONFINITE; }
+      order[e] = e;
+    }
+    /* selection: position j receives the best of the remaining entries */
+    for (int j = 0; j < k; ++j) {
+      int best = j;
+      for (int m = j + 1; m < E; ++m)
+        if (ranks_before(row[order[m]], order[m], row[order[best]], order[best]))
+          best = m;
+      int tmp = order[j]; order[j] = order[best]; order[best] = tmp;
+    }
+    double lmax = (double)row[order[0]];
+    double denom = 0.0;
+    if (norm_topk) {
+      for (int j = 0; j < k; ++j) denom += exp((double)row[order[j]] - lmax);
+    } else {
+      for (int e = 0; e < E; ++e) denom += exp((double)row[e] - lmax);
+    }
+    for (int j = 0; j < k; ++j) {
+      ids[(size_t)t * k + j] = order[j];
+      w[(size_t)t * k + j] = (float)(exp((double)row[order[j]] - lmax) / denom);
+    }
+  }
+  free(order);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Counts, exp_indptr and the token permutation [ET-cast cue 7, cue 9;
+ * ET-fig 5b].  counts[e] is the number of (t,j) routed to e; exp_indptr is
+ * the exclusive prefix sum (length E+1, ends at T*k).  Reading: the
+ * permutation is the stable one, i.e. within expert e the routed pairs keep
+ * ascending flat index t*k+j.  perm[s] = flat index held by slot s;
+ * slot[f] = the slot of flat index f.                                       */
+int oracle_route_scan(int T, int E, int k, const int32_t *ids, int32_t *counts,
+                      int32_t *exp_indptr, int32_t *perm, int32_t *slot) {
+  if (T < 0 || E <= 0 || k <= 0) return ORACLE_ERR_INVALID;
+  const int n = T * k;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int f = 0; f < n; ++f) {
+    int e = ids[f];
+    if (e < 0 || e >= E) return ORACLE_ERR_INVALID;
+    counts[e] += 1;
+  }
+  exp_indptr[0] = 0;
+  for (int e = 0; e < E; ++e) exp_indptr[e + 1] = exp_indptr[e] + counts[e];
+  int32_t *fill = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+  if (!fill) return ORACLE_ERR_INVALID;
+  for (int f = 0; f < n; ++f) {
+    int e = ids[f];
+    int s = exp_indptr[e] + fill[e];
+    fill[e] += 1;
+    perm[s] = f;
+    slot[f] = s;
+  }
+  free(fill);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert computation for one routed row (reading: SwiGLU experts, with the
+ * stored intermediates rounded to bf16 because activations are bf16).
+ *   gate_i = sum_h x[h] * W13[e, i, h],   up_i = sum_h x[h] * W13[e, I+i, h]
+ *   hmid_i = bf16( float( silu(gate_i) * up_i ) ),  silu(z) = z / (1 + e^-z)
+ *   y_n    = bf16( float( sum_i hmid_i * Wd[e, n, i] ) )
+ * Sums in fp64.                                                             */
+static void expert_row(int H, int I, const uint16_t *x, const uint16_t *W13e,
+                       const uint16_t *Wde, uint16_t *hmid, uint16_t *y) {
+  for (int i = 0; i < I; ++i) {
+    double g = 0.0, u = 0.0;
+    const uint16_t *wg = W13e + (size_t)i * H;
+    const uint16_t *wu = W13e + (size_t)(I + i) * H;
+    for (int h = 0; h < H; ++h) {
+      double xv = (double)bf16_bits_to_float(x[h]);
+      g += xv * (double)bf16_bits_to_float(wg[h]);
+      u += xv * (double)bf16_bits_to_float(wu[h]);
+    }
+    double silu = g / (1.0 + exp(-g));
+    hmid[i] = float_to_bf16_bits((float)(silu * u));
+  }
+  for (int n = 0; n < H; ++n) {
+    double acc = 0.0;
+    const uint16_t *wd = Wde + (size_t)n * I;
+    for (int i = 0; i < I; ++i)
+      acc += (double)bf16_bits_to_float(hmid[i]) * (double)bf16_bits_to_float(wd[i]);
+    y[n] = float_to_bf16_bits((float)acc);
+  }
+}
+
+/* Weighted combine (reading of "followed by a weighted combine"):
+ *   out[t, n] = bf16( float( sum_{j<k} w[t,j] * Y[slot[t*k+j], n] ) ), fp64. */
+
+/* Full layer.  Inputs: X [T,H], Wr [E,H], bias [E] or NULL, W13 [E,2I,H],
+ * Wd [E,H,I] (bf16 bits).  Outputs: routing tensors and out [T,H] (bf16),
+ * plus the grouped intermediates Xp [T*k,H], Hmid [T*k,I], Y [T*k,H] when
+ * those pointers are non-NULL.                                              */
+int oracle_moe(int T, int H, int E, int k, int I, int norm_topk,
+               const uint16_t *X, const uint16_t *Wr, const float *bias,
+               const uint16_t *W13, const uint16_t *Wd, float *logits,
+               int32_t *ids, float *w, int32_t *counts, int32_t *exp_indptr,
+               int32_t *perm, int32_t *slot, uint16_t *Xp, uint16_t *Hmid,
+               uint16_t *Y, uint16_t *out) {
+  if (T < 0 || H <= 0 || E <= 0 || k <= 0 || k > E || I <= 0)
+    return ORACLE_ERR_INVALID;
+  int rc = oracle_router_logits(T, H, E, X, Wr, bias, logits);
+  if (rc) return rc;
+  rc = oracle_topk(T, E, k, logits, norm_topk, ids, w);
+  if (rc) return rc;
+  rc = oracle_route_scan(T, E, k, ids, counts, exp_indptr, perm, slot);
+  if (rc) return rc;
+  const int n = T * k;
+  uint16_t *hrow = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)I);
+  uint16_t *yall = Y ? Y : (uint16_t *)malloc(sizeof(uint16_t) * (size_t)n * H);
+  if (!hrow || !yall) { free(hrow); if (!Y) free(yall); return ORACLE_ERR_INVALID; }
+  for (int e = 0; e < E; ++e) {
+    for (int s = exp_indptr[e]; s < exp_indptr[e + 1]; ++s) {
+      int t = perm[s] / k;
+      const uint16_t *x = X + (size_t)t * H;
+      if (Xp) memcpy(Xp + (size_t)s * H, x, sizeof(uint16_t) * (size_t)H);
+      expert_row(H, I, x, W13 + (size_t)e * 2 * I * H, Wd + (size_t)e * H * I,
+                 hrow, yall + (size_t)s * H);
+      if (Hmid) memcpy(Hmid + (size_t)s * I, hrow, sizeof(uint16_t) * (size_t)I);
+    }
+  }
+  for (int t = 0; t < T; ++t)
+    for (int h = 0; h < H; ++h) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) {
+        int s = slot[(size_t)t * k + j];
+        acc += (double)w[(size_t)t * k + j] *
+               (double)bf16_bits_to_float(yall[(size_t)s * H + h]);
+      }
+      out[(size_t)t * H + h] = float_to_bf16_bits((float)acc);
+    }
+  free(hrow);
+  if (!Y) free(yall);
+  return ORACLE_OK;
+}
+
+/* Output rows for a subset of tokens, given routing already computed by
+ * oracle_moe's first three steps (ids, w).  Lets large workloads be checked
+ * token by token: out_rows[r, :] is the layer output of token tok[r].      */
+int oracle_moe_tokens(int H, int k, int I, int ntok, const int32_t *tok,
+                      const uint16_t *X, const uint16_t *W13, const uint16_t *Wd,
+                      const int32_t *ids, const float *w, uint16_t *out_rows) {
+  if (H <= 0 || k <= 0 || I <= 0 || ntok < 0) return ORACLE_ERR_INVALID;
+  uint16_t *hrow = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)I);
+  uint16_t *y = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)k * H);
+  if (!hrow || !y) { free(hrow); free(y); return ORACLE_ERR_INVALID; }
+  for (int r = 0; r < ntok; ++r) {
+    int t = tok[r];
+    for (int j = 0; j < k; ++j) {
+      int e = ids[(size_t)t * k + j];
+      expert_row(H, I, X + (size_t)t * H, W13 + (size_t)e * 2 * I * H,
+                 Wd + (size_t)e * H * I, hrow, y + (size_t)j * H);
+    }
+    for (int h = 0; h < H; ++h) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j)
+        acc += (double)w[(size_t)t * k + j] *
+               (double)bf16_bits_to_float(y[(size_t)j * H + h]);
+      out_rows[(size_t)r * H + h] = float_to_bf16_bits((float)acc);
+    }
+  }
+  free(hrow);
+  free(y);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Split-K row sum [ET-fig 3, ET-cast cue 3].  A is [n, nsplit*bk] int32.
+ * partial_sum(i, j): B[i, j] = sum of A[i, c] over tile j's columns
+ * c in [j*bk, (j+1)*bk), then notify event i (edge "ij->i").  final_sum(i)
+ * waits on event i (edge "i->i"), whose wait_count is nsplit, and writes
+ * C[i] = sum_j B[i, j].  Integer sums, so the order of completion is
+ * irrelevant.  Also returns the number of notifies each event receives.    */
+int oracle_splitk(int n, int nsplit, int bk, const int32_t *A, int32_t *B,
+                  int32_t *C, int32_t *notifies) {
+  if (n < 0 || nsplit <= 0 || bk <= 0) return ORACLE_ERR_INVALID;
+  for (int i = 0; i < n; ++i) notifies[i] = 0;
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < nsplit; ++j) {
+      int32_t acc = 0;
+      for (int c = j * bk; c < (j + 1) * bk; ++c)
+        acc += A[(size_t)i * nsplit * bk + c];
+      B[(size_t)i * nsplit + j] = acc;
+      notifies[i] += 1; /* edge "ij->i": tile (i, j) notifies event i */
+    }
+  for (int i = 0; i < n; ++i) {
+    int32_t acc = 0;
+    for (int j = 0; j < nsplit; ++j) acc += B[(size_t)i * nsplit + j];
+    C[i] = acc;
+  }
+  return ORACLE_OK;
+}

@@ -1,0 +1,441 @@
+"""CPU pins of the oracle against things other than itself: hand-derived
+values, closed forms, brute force on tiny inputs, library routines on special
+cases, and invariants.  No GPU, no HIP library."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dynamic_moe_task_amd import workloads as wl
+
+F32 = np.float32
+
+
+def bits(x):
+    """float32 value(s) -> bf16 bits via torch's own conversion (RNE)."""
+    t = torch.tensor(np.asarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def from_bits(b):
+    return oracle.bf16_bits_to_f64(b)
+
+
+# ---------------------------------------------------------------- bf16 RNE --
+@pytest.mark.parametrize("value,expect", [
+    (1.0, 0x3F80),
+    (-2.0, 0xC000),
+    (1.0 + 2.0 ** -8, 0x3F80),               # exact tie -> even (down)
+    (1.0 + 3 * 2.0 ** -8, 0x3F82),           # exact tie -> even (up)
+    (1.0 + 2.0 ** -8 + 2.0 ** -20, 0x3F81),  # just above the tie
+    (0.0, 0x0000),
+    (-0.0, 0x8000),
+    (3.0e38, 0x7F62),
+])
+def test_bf16_rne_hand_values(value, expect):
+    assert oracle.f32_to_bf16_bits(value) == expect
+
+
+def test_bf16_rne_matches_torch_on_random_and_ties():
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal(20000).astype(F32) * F32(37.0)
+    u = v.view(np.uint32)
+    ties = ((u & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)
+    allv = np.concatenate([v, ties])
+    mine = np.array([oracle.f32_to_bf16_bits(float(x)) for x in allv], np.uint16)
+    assert np.array_equal(mine, bits(allv))
+    # the input generator's vectorised rounding agrees with torch as well
+    assert np.array_equal(wl.to_bf16_bits(allv), bits(allv))
+
+
+# ---------------------------------------------------- router logit contract --
+def _one_row(H, xs, ws):
+    X = np.zeros((1, H), np.uint16)
+    W = np.zeros((1, H), np.uint16)
+    for h, v in xs.items():
+        X[0, h] = bits(v)
+    for h, v in ws.items():
+        W[0, h] = bits(v)
+    return X, W
+
+
+def test_logit_tree_order_hand_value():
+    # H = 512: 64 chunks, chunk c on lane c.  Lane 0 holds 2^24, lanes 1..63
+    # hold 1.  Halving tree: 2^24+1 ties to 2^24, then +2, +4, +8, +16, +32
+    # are exact: 2^24 + 62.  A sequential sum would give 2^24, fp64 2^24+63.
+    H = 512
+    X, W = _one_row(H, {8 * l: 1.0 for l in range(64)},
+                    {0: 2.0 ** 24, **{8 * l: 1.0 for l in range(1, 64)}})
+    L = oracle.router_logits(X, W)
+    assert L[0, 0] == F32(2.0 ** 24 + 62)
+    assert oracle.router_logits_f64(X, W)[0, 0] == 2.0 ** 24 + 63
+
+
+def test_logit_lane_order_hand_value():
+    # H = 1024: lane 0 owns chunks 0 and 64 (h = 0..7 and 512..519).  Its
+    # elements go in ascending h: 1 + 1 = 2, then 2 + 2^24 is exact.  The
+    # reverse order would lose both ones (2^24 + 1 ties to 2^24).
+    H = 1024
+    X, W = _one_row(H, {0: 1.0, 1: 1.0, 512: 1.0}, {0: 1.0, 1: 1.0, 512: 2.0 ** 24})
+    assert oracle.router_logits(X, W)[0, 0] == F32(2.0 ** 24 + 2)
+
+
+def test_logit_bias_added_last():
+    X, W = _one_row(512, {0: 1.0}, {0: 0.5})
+    b = np.array([0.25], np.float32)
+    assert oracle.router_logits(X, W, b)[0, 0] == F32(0.75)
+
+
+def test_logits_close_to_fp64_and_onehot_exact():
+    shape = wl.TINY
+    w, X = wl.make_layer(shape, 0)
+    L32 = oracle.router_logits(X, w.Wr)
+    L64 = oracle.router_logits_f64(X, w.Wr)
+    absprod = np.abs(from_bits(X)) @ np.abs(from_bits(w.Wr)).T
+    assert np.all(np.abs(L32 - L64) <= 64 * 2.0 ** -24 * absprod + 1e-30)
+    # one-hot activations select a single weight exactly
+    Xo = np.zeros((3, shape.H), np.uint16)
+    for t, h in enumerate([0, 77, 127]):
+        Xo[t, h] = bits(1.0)
+    Lo = oracle.router_logits(Xo, w.Wr)
+    for t, h in enumerate([0, 77, 127]):
+        assert np.array_equal(Lo[t], from_bits(w.Wr[:, h]).astype(np.float32))
+
+
+# ------------------------------------------------------------------- top-k --
+def _brute_topk(row, k):
+    # every k-subset, each listed in its own best-first order; the winner is
+    # the lexicographically greatest sequence of (value, -index) keys
+    best = None
+    for sub in itertools.combinations(range(len(row)), k):
+        seq = sorted(sub, key=lambda e: (-row[e], e))
+        key = [(row[e], -e) for e in seq]
+        if best is None or key > best[0]:
+            best = (key, seq)
+    return best[1]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_brute_force_with_ties(seed):
+    rng = np.random.default_rng(100 + seed)
+    E = int(rng.integers(2, 9))
+    k = int(rng.integers(1, E + 1))
+    T = 7
+    # few distinct values so that ties are frequent
+    L = rng.integers(-2, 3, size=(T, E)).astype(np.float32) * F32(0.5)
+    ids, w = oracle.topk(L, k, norm_topk=True)
+    for t in range(T):
+        assert list(ids[t]) == _brute_topk(list(L[t]), k)
+
+
+def test_topk_weights_two_formulas():
+    rng = np.random.default_rng(7)
+    L = (rng.standard_normal((5, 10)) * 2).astype(np.float32)
+    k = 3
+    ids, w = oracle.topk(L, k, norm_topk=True)
+    _, wfull = oracle.topk(L, k, norm_topk=False)
+    # softmax over all E, then renormalise over the chosen k
+    p = np.exp(L.astype(np.float64) - L.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    np.testing.assert_allclose(w, sel / sel.sum(axis=1, keepdims=True), rtol=1e-6)
+    np.testing.assert_allclose(wfull, sel, rtol=1e-6)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-6)
+    assert np.all(np.diff(w, axis=1) <= 0)
+
+
+def test_topk_rejects_nan():
+    L = np.zeros((1, 4), np.float32)
+    L[0, 2] = np.nan
+    with pytest.raises(ValueError):
+        oracle.topk(L, 2)
+
+
+# ---------------------------------------------- counts / indptr / permutation --
+def _check_routing_invariants(ids, E, counts, indptr, perm, slot):
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    assert counts.sum() == T * k
+    assert indptr[0] == 0 and indptr[-1] == T * k
+    assert np.all(np.diff(indptr) == counts) and np.all(np.diff(indptr) >= 0)
+    assert sorted(perm.tolist()) == list(range(T * k))
+    assert np.array_equal(slot[perm], np.arange(T * k))
+    for e in range(E):
+        seg = perm[indptr[e]:indptr[e + 1]]
+        assert np.all(flat[seg] == e)
+        assert np.all(np.diff(seg) > 0)  # stable: ascending flat index
+    np.testing.assert_array_equal(counts, np.bincount(flat, minlength=E))
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (4, 8, 2), (37, 16, 4), (64, 128, 8), (3, 5, 5)])
+def test_route_scan_invariants_and_stable_sort(T, E, k):
+    rng = np.random.default_rng(T * 1000 + E)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, indptr, perm, slot = oracle.route_scan(ids, E)
+    _check_routing_invariants(ids, E, counts, indptr, perm, slot)
+    # a library stable sort of the flat expert ids gives the same permutation
+    assert np.array_equal(perm, np.argsort(ids.reshape(-1), kind="stable"))
+
+
+def test_tiny_layer_routing_invariants():
+    w, X = wl.make_layer(wl.TINY, 0)
+    r = oracle.route(X, w.Wr, wl.TINY.k)
+    _check_routing_invariants(r["topk_ids"], wl.TINY.E, r["counts"], r["exp_indptr"],
+                              r["perm"], r["slot"])
+
+
+# ----------------------------------------------------- expert maths pins --
+def _dense_swiglu_ref(X, Wg, Wu, Wd):
+    """Dense SwiGLU MLP with the same rounding points, in torch fp64."""
+    x = torch.from_numpy(from_bits(X))
+    g = x @ torch.from_numpy(from_bits(Wg)).T
+    u = x @ torch.from_numpy(from_bits(Wu)).T
+    h = (g * torch.sigmoid(g) * u).float().to(torch.bfloat16).double()
+    y = (h @ torch.from_numpy(from_bits(Wd)).T).float().to(torch.bfloat16)
+    return y.view(torch.int16).numpy().view(np.uint16)
+
+
+def _ulp_close(a_bits, b_bits, ulps=1):
+    a = a_bits.astype(np.int32)
+    b = b_bits.astype(np.int32)
+    # same sign and within `ulps` of each other in the bf16 ordering
+    sa = np.where(a & 0x8000, -(a & 0x7FFF), a & 0x7FFF)
+    sb = np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    return np.abs(sa - sb) <= ulps
+
+
+def test_single_expert_is_dense_mlp():
+    # E = 1, k = 1: routing weight is exactly 1, so out = Y = dense MLP(X).
+    rng = np.random.default_rng(3)
+    T, H, I = 9, 64, 128
+    X = wl.to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    Wr = wl.to_bf16_bits(rng.standard_normal((1, H), dtype=np.float32) * F32(0.02))
+    W13 = wl.to_bf16_bits(rng.standard_normal((1, 2 * I, H), dtype=np.float32) * F32(0.1))
+    Wd = wl.to_bf16_bits(rng.standard_normal((1, H, I), dtype=np.float32) * F32(0.1))
+    r = oracle.moe(X, Wr, W13, Wd, k=1)
+    assert np.all(r["topk_w"] == 1.0)
+    ref = _dense_swiglu_ref(X, W13[0, :I], W13[0, I:], Wd[0])
+    assert np.mean(_ulp_close(r["out"], ref, 0)) > 0.99
+    assert np.all(_ulp_close(r["out"], ref, 1))
+
+
+def test_identical_experts_equal_dense_mlp():
+    # Every expert the same and norm_topk: out = bf16(sum_j w_j * Y) with
+    # sum_j w_j = 1, i.e. the dense MLP up to one final rounding.
+    rng = np.random.default_rng(4)
+    T, H, I, E, k = 6, 64, 64, 8, 3
+    X = wl.to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    Wr = wl.to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) * F32(0.3))
+    one13 = wl.to_bf16_bits(rng.standard_normal((2 * I, H), dtype=np.float32) * F32(0.1))
+    oned = wl.to_bf16_bits(rng.standard_normal((H, I), dtype=np.float32) * F32(0.1))
+    W13 = np.broadcast_to(one13, (E, 2 * I, H)).copy()
+    Wd = np.broadcast_to(oned, (E, H, I)).copy()
+    r = oracle.moe(X, Wr, W13, Wd, k=k)
+    ref = _dense_swiglu_ref(X, one13[:I], one13[I:], oned)
+    assert np.all(_ulp_close(r["out"], ref, 1))
+
+
+def test_scalar_permutation_experts_closed_form():
+    # Expert e: gate = a_e P_e x, up = b_e Q_e x, down = c_e R_e h with
+    # permutation matrices, so every output element has a closed form.  A
+    # transposed weight layout, swapped gate/up halves or a wrong expert
+    # index all change the answer.
+    rng = np.random.default_rng(5)
+    T, H, E, k = 5, 64, 4, 2
+    I = H
+    a = [0.5, 1.0, 2.0, -1.5]
+    b = [1.25, -0.75, 0.5, 2.0]
+    c = [1.0, 0.5, -2.0, 0.25]
+    P = [rng.permutation(H) for _ in range(E)]
+    Q = [rng.permutation(H) for _ in range(E)]
+    R = [rng.permutation(H) for _ in range(E)]
+    W13 = np.zeros((E, 2 * I, H), np.uint16)
+    Wd = np.zeros((E, H, I), np.uint16)
+    for e in range(E):
+        W13[e, np.arange(I), P[e]] = bits(a[e])
+        W13[e, I + np.arange(I), Q[e]] = bits(b[e])
+        Wd[e, np.arange(H), R[e]] = bits(c[e])
+    X = wl.to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    Wr = wl.to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32))
+    r = oracle.moe(X, Wr, W13, Wd, k=k, intermediates=True)
+    x = from_bits(X)
+    expect = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            e = r["topk_ids"][t, j]
+            g = a[e] * x[t, P[e]]
+            u = b[e] * x[t, Q[e]]
+            h = from_bits(wl.to_bf16_bits((g / (1 + np.exp(-g)) * u).astype(np.float32)))
+            y = from_bits(wl.to_bf16_bits((c[e] * h[R[e]]).astype(np.float32)))
+            expect[t] += float(r["topk_w"][t, j]) * y
+    ebits = wl.to_bf16_bits(expect.astype(np.float32))
+    assert np.all(_ulp_close(r["out"], ebits, 0))
+
+
+def test_moe_tokens_matches_full_layer():
+    w, X = wl.make_layer(wl.TINY, 0)
+    r = oracle.moe(X, w.Wr, w.W13, w.Wd, k=wl.TINY.k)
+    rows = oracle.moe_tokens([3, 0, 2], X, w.W13, w.Wd, r["topk_ids"], r["topk_w"])
+    assert np.array_equal(rows, r["out"][[3, 0, 2]])
+
+
+def test_tiny_layer_against_fp64_unrounded():
+    # The oracle rounds Hmid and Y to bf16; an fp64 version with no
+    # intermediate rounding stays within the output tolerance.
+    shape = wl.TINY
+    w, X = wl.make_layer(shape, 0)
+    r = oracle.moe(X, w.Wr, w.W13, w.Wd, k=shape.k)
+    x = from_bits(X)
+    W13 = from_bits(w.W13)
+    Wd = from_bits(w.Wd)
+    ref = np.zeros((shape.T, shape.H))
+    for t in range(shape.T):
+        for j in range(shape.k):
+            e = r["topk_ids"][t, j]
+            g = W13[e, :shape.I] @ x[t]
+            u = W13[e, shape.I:] @ x[t]
+            ref[t] += r["topk_w"][t, j] * (Wd[e] @ (g / (1 + np.exp(-g)) * u))
+    got = from_bits(r["out"])
+    err = np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)
+    assert np.all(err < 2e-2)
+
+
+# --------------------------------------------------------------- split-K --
+def _golden(name):
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", name)
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        if " = " in line:
+            k_, v_ = line.split(" = ", 1)
+            kv[k_.strip()] = v_.strip()
+        elif "->" in line:
+            k_, v_ = line.split("->", 1)
+            kv[k_.strip()] = v_.strip()
+    return kv
+
+
+def test_splitk_closed_form():
+    g = _golden("fig3_splitk_wiring.txt")
+    nsplit = int(g["wait_count"])
+    assert nsplit == 4
+    rng = np.random.default_rng(9)
+    n, bk = 50, 16
+    A = rng.integers(-1000, 1000, size=(n, nsplit * bk)).astype(np.int32)
+    B, C, notif = oracle.splitk(A, nsplit)
+    assert np.array_equal(C, A.sum(axis=1))
+    assert np.array_equal(B, A.reshape(n, nsplit, bk).sum(axis=2))
+    assert np.all(notif == nsplit)
+
+
+# ---------------------------------------------------------- event model --
+from oracle import events as ev  # noqa: E402
+
+
+def test_fig4_instantiation_shapes():
+    g = _golden("fig4_instantiation.txt")
+    t = ev.ETensor(["B", 2], wait_count=1)
+    assert t.instantiate(B=1) == tuple(int(v) for v in g["B=1"].split(","))
+    assert t.instantiate(B=2) == tuple(int(v) for v in g["B=2"].split(","))
+
+
+def test_rs_walkthrough_counter():
+    g = _golden("rs_walkthrough.txt")
+    st = ev.EventState()
+    st.declare("rs", (1,), int(g["initial"]))
+    key = ("rs", (0,))
+    assert st.remaining[key] == 2 and not st.ready(key)
+    st.notify(key)
+    assert st.remaining[key] == int(g["after_notify_1"].split()[0]) and not st.ready(key)
+    st.notify(key)
+    assert st.remaining[key] == 0 and st.ready(key) and st.fired[key] == 1
+    st.notify(key)
+    assert st.errors  # a third notify is an over-notification
+
+
+def test_edge_maps():
+    assert ev.edge_apply("ij->i", (3, 2)) == (3,)
+    assert ev.edge_apply("i->i", (5,)) == (5,)
+    with pytest.raises(ValueError):
+        ev.parse_edge("i->j")
+
+
+def _splitk_graph(A, nsplit):
+    n = A.shape[0]
+    bk = A.shape[1] // nsplit
+    g = _golden("fig3_splitk_wiring.txt")
+    B = np.zeros((n, nsplit), np.int64)
+    C = np.zeros(n, np.int64)
+    st = ev.EventState()
+    st.declare("ev", (n,), nsplit)
+    tasks = []
+    for i in range(n):
+        for j in range(nsplit):
+            def run(i=i, j=j):
+                B[i, j] = A[i, j * bk:(j + 1) * bk].sum()
+            tasks.append(ev.Task("partial_sum", (i, j), [],
+                                 [("ev", ev.edge_apply(g["out_edge"], (i, j)))], run))
+    for i in range(n):
+        def run(i=i):
+            C[i] = B[i].sum()
+        tasks.append(ev.Task("final_sum", (i,), [("ev", ev.edge_apply(g["in_edge"], (i,)))], [], run))
+    return tasks, st, B, C
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_splitk_through_event_model(seed):
+    rng = np.random.default_rng(seed)
+    n, nsplit, bk = 6, 4, 8
+    A = rng.integers(-50, 50, size=(n, nsplit * bk))
+    # dynamic schedule, random pop order
+    tasks, st, B, C = _splitk_graph(A, nsplit)
+    ev.run_dynamic(tasks, st, seed=seed)
+    assert np.array_equal(C, A.sum(axis=1)) and not st.errors
+    assert all(v == 1 for v in st.fired.values())
+    # static schedule: 3 workers, phase-ordered round-robin lists
+    tasks, st, B, C = _splitk_graph(A, nsplit)
+    W = 3
+    lists = [[i for i in range(len(tasks)) if i % W == w] for w in range(W)]
+    ev.run_static(tasks, st, W, lists)
+    assert np.array_equal(C, A.sum(axis=1)) and not st.errors
+
+
+def test_static_schedule_not_phase_ordered_deadlocks():
+    # A worker list that puts a waiter before the producer it waits on, on
+    # the same worker, can never progress: the model reports it.
+    A = np.ones((1, 8), np.int64)
+    tasks, st, B, C = _splitk_graph(A, 4)
+    lists = [[4, 0, 1, 2, 3]]
+    with pytest.raises(RuntimeError):
+        ev.run_static(tasks, st, 1, lists)
+
+
+def test_moe_event_graph_counts_and_single_fire():
+    # Data-dependent update: expert e's counter starts at counts[e]; each
+    # routed (t, j) notifies ids[t, j]; the expert's tiles over
+    # [exp_indptr[e], exp_indptr[e+1]) wait on it.  Every event fires once.
+    w, X = wl.make_layer(wl.TINY, 0)
+    r = oracle.route(X, w.Wr, wl.TINY.k)
+    E = wl.TINY.E
+    counts = r["counts"]
+    st = ev.EventState()
+    st.declare("exp", (E,), lambda idx: int(counts[idx[0]]))
+    tasks = []
+    ids = r["topk_ids"]
+    for t in range(ids.shape[0]):
+        tasks.append(ev.Task("dispatch", (t,), [], [("exp", (int(e),)) for e in ids[t]]))
+    bm = 2
+    for (e, lo, hi) in oracle.expected_tiles(r["exp_indptr"], bm):
+        tasks.append(ev.Task("g1", (e, lo), [("exp", (e,))], []))
+    ev.run_dynamic(tasks, st, seed=1)
+    for e in range(E):
+        assert st.notified[("exp", (e,))] == counts[e]
+        assert st.fired[("exp", (e,))] == 1
+    n_tiles = sum(math.ceil(c / bm) for c in counts)
+    assert len(oracle.expected_tiles(r["exp_indptr"], bm)) == n_tiles
