@@ -1,0 +1,196 @@
+"""Benchmark: one MoE layer (Qwen3-30B-A3B-shaped, 128 experts, top-8) on one
+MI355X through the C ABI.  A step is one launch of the whole hot path
+(router, top-k, scan, dispatch, gate/up+SwiGLU, down, combine) over one batch
+of synthetic tokens already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+                    [--sched static] [--copies R] [--no-cpu] [--traffic FILE]
+
+Prints ONE JSON line.  `value` is tokens/s of the chosen schedule; the other
+schedules, µs/layer and the roofline fraction ride along in the same line.
+Weights are rotated over R device copies so that consecutive steps do not
+reuse expert weights left in the 256 MB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+BF16_PEAK_TFS = 2500.0      # MI355X dense bf16 MFMA, published
+
+METRIC = "µs per MoE layer & tokens/s at 1 MI355X; %HBM peak (decode) / %MFMA (batch 256)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill_zipf", "tiny"])
+    ap.add_argument("--sched", default="static", choices=["static", "dynamic", "barrier", "kbk"])
+    ap.add_argument("--copies", type=int, default=4, help="weight copies rotated over steps")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM traffic per launch measured with rocprofv3 counters (JSON)")
+    ap.add_argument("--only-sched", action="store_true", help="time only --sched (for profiling)")
+    return ap.parse_args()
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def time_sched(bufs, T, sched, steps, warmup, w13s, w2s, stream_ptr):
+    """Average µs per launch over `steps` back-to-back launches, bracketed by
+    HIP events on the launch stream."""
+    import torch
+    from dynamic_moe_task_amd import binding as B
+    R = len(w13s)
+    args = [bufs.args(w13=w13s[i], w2=w2s[i]) for i in range(R)]
+    code = B.SCHEDS[sched]
+    for i in range(warmup):
+        B.check(B.moe_layer_launch(bufs.desc, T, args[i % R], code, stream_ptr))
+    B.check(B.etc_sync(stream_ptr))
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        B.check(B.moe_layer_launch(bufs.desc, T, args[i % R], code, stream_ptr))
+    end.record()
+    torch.cuda.synchronize()
+    rc = B.etc_sync(stream_ptr)
+    if rc != 0:
+        raise B.EtcError(rc, B.etc_last_error())
+    return start.elapsed_time(end) * 1e3 / steps
+
+
+def cpu_baseline(shape, w, X, seconds):
+    """The oracle as it stands, single-threaded C, on the same workload:
+    whole layers for decode/tiny; for the prefill workload a bounded sample
+    of tokens (routing for all T plus the expert rows of a token subset)."""
+    import oracle
+    k = shape.k
+    t0 = time.perf_counter()
+    n = 0
+    toks = 0
+    sample = ""
+    while True:
+        if shape.T <= 16:
+            oracle.moe(X, w.Wr, w.W13, w.Wd, k=k, norm_topk=shape.norm_topk, bias=w.bias)
+            toks += shape.T
+            sample = f"whole layer, T={shape.T}, repeated"
+        else:
+            r = oracle.route(X, w.Wr, k, bias=w.bias)
+            sub = np.arange(n * 8 % shape.T, n * 8 % shape.T + 8, dtype=np.int32) % shape.T
+            oracle.moe_tokens(sub, X, w.W13, w.Wd, r["topk_ids"], r["topk_w"])
+            toks += len(sub)
+            sample = f"routing of all {shape.T} tokens + expert rows of 8-token slices, repeated"
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": toks / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample}; {n} calls in {dt:.1f} s on {platform.processor() or platform.machine()}"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from dynamic_moe_task_amd import binding as B
+    from dynamic_moe_task_amd import workloads as wl
+
+    shape = wl.SHAPES[a.workload]
+    T = shape.T
+    w, X = wl.make_layer(shape, 0)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    Wr = dev_bf16(w.Wr)
+    W13 = dev_bf16(w.W13)
+    Wd = dev_bf16(w.Wd)
+    bias = torch.from_numpy(w.bias).cuda() if w.bias is not None else None
+    R = max(1, a.copies) if shape.E > 8 else 1
+    w13s = [W13] + [W13.clone() for _ in range(R - 1)]
+    w2s = [Wd] + [Wd.clone() for _ in range(R - 1)]
+    desc = B.moe_desc(T, shape.H, shape.E, shape.k, shape.I, shape.norm_topk, bias is not None)
+    bufs = B.MoELayerBuffers.allocate(desc, Wr, W13, Wd, bias)
+    bufs.x[:T].copy_(dev_bf16(X))
+    torch.cuda.synchronize()
+
+    # one checked launch first: routing of the benchmarked inputs
+    B.check(B.moe_layer_launch(desc, T, bufs.args(), B.SCHEDS[a.sched], sp))
+    B.check(B.etc_sync(sp))
+    counts = bufs.counts.cpu().numpy()
+    n_act = int((counts > 0).sum())
+    alg_bytes = wl.algorithmic_bytes(shape, T, n_act)
+    alg_flops = wl.algorithmic_flops(shape, T)
+
+    scheds = [a.sched] if a.only_sched else ["static", "dynamic", "barrier", "kbk"]
+    us = {}
+    for s in scheds:
+        steps = a.steps if s == a.sched else max(10, a.steps // 2)
+        us[s] = time_sched(bufs, T, s, steps, a.warmup, w13s, w2s, sp)
+    us_main = us[a.sched]
+
+    achieved_gbs = alg_bytes / (us_main * 1e-6) / 1e9
+    traffic = None
+    if a.traffic and os.path.exists(a.traffic):
+        try:
+            tr = json.load(open(a.traffic))
+            key = f"{a.workload}/{a.sched}"
+            if key in tr:
+                traffic = tr[key]
+        except Exception:
+            traffic = None
+    roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": f"moe_persistent<{a.sched}>" if a.sched != "kbk" else "kbk_* (7 launches)",
+                "algorithmic_bytes": alg_bytes}
+    mfma_frac = alg_flops / (us_main * 1e-6) / (BF16_PEAK_TFS * 1e12)
+
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline(shape, w, X, a.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(T / (us_main * 1e-6), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(us_main / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights N(0,0.02), tokens N(0,1))",
+        "config": {"workload": shape.name, "T": T, "H": shape.H, "E": shape.E, "k": shape.k, "I": shape.I,
+                   "schedule": a.sched, "weight_copies_rotated": R, "active_experts": n_act},
+        "us_per_layer": {s: round(v, 2) for s, v in us.items()},
+        "mfma_frac_whole_layer": round(mfma_frac, 5),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,441 @@
+// Host side of the C ABI declared in include/etc.h: argument validation,
+// event-tensor handles, workspace layout, grid sizing from the occupancy
+// query, launch, and the status report read back by etc_sync.  Allocates
+// nothing on the MoE launch path.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "etc_internal.h"
+
+using namespace etc;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ETC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Launches since the last etc_sync on each stream: where their status
+// report word lives.
+struct Pending {
+  void* stream;
+  uint32_t* report;
+};
+std::mutex g_mu;
+std::vector<Pending> g_pending;
+
+void add_pending(void* stream, uint32_t* report) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (const Pending& p : g_pending)
+    if (p.stream == stream && p.report == report) return;
+  g_pending.push_back({stream, report});
+}
+
+int status_to_code(uint32_t st) {
+  if (st & ST_TIMEOUT) return fail(ETC_ERR_TIMEOUT, "in-kernel wait exceeded its spin budget (status 0x%x)", st);
+  if (st & (ST_OVER_NOTIFY | ST_QUEUE_OVERFLOW))
+    return fail(ETC_ERR_INVARIANT, "event over-notified or queue overflow (status 0x%x)", st);
+  if (st & ST_NONFINITE) return fail(ETC_ERR_NONFINITE, "NaN router logit (status 0x%x)", st);
+  return ETC_OK;
+}
+
+// Per-device facts for grid sizing.
+struct DeviceFacts {
+  int cus = 0;
+};
+std::mutex g_dev_mu;
+std::vector<DeviceFacts> g_dev;
+
+int device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+  if (g_dev[dev].cus == 0) {
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
+    g_dev[dev].cus = v;
+  }
+  *cus = g_dev[dev].cus;
+  return ETC_OK;
+}
+
+int wg_per_cu_cap() {
+  const char* s = std::getenv("ETC_WG_PER_CU");
+  if (s && *s) {
+    int v = std::atoi(s);
+    if (v >= 1 && v <= 16) return v;
+  }
+  return 2;
+}
+
+int desc_check(const etc_moe_desc* d) {
+  if (!d) return fail(ETC_ERR_INVALID, "descriptor is NULL");
+  if (d->T_max < 1 || d->T_max > kMaxTmax) return fail(ETC_ERR_INVALID, "T_max %d outside [1, %d]", d->T_max, kMaxTmax);
+  if (d->H < 128 || d->H % 128 || d->H > kMaxHI) return fail(ETC_ERR_INVALID, "H %d must be a positive multiple of 128, <= %d", d->H, kMaxHI);
+  if (d->I < 128 || d->I % 128 || d->I > kMaxHI) return fail(ETC_ERR_INVALID, "I %d must be a positive multiple of 128, <= %d", d->I, kMaxHI);
+  if (d->E < 1 || d->E > kMaxE) return fail(ETC_ERR_INVALID, "E %d outside [1, %d]", d->E, kMaxE);
+  if (d->k < 1 || d->k > kMaxK || d->k > d->E) return fail(ETC_ERR_INVALID, "k %d outside [1, min(E, %d)]", d->k, kMaxK);
+  if ((int64_t)d->E * cdiv(d->T_max, 32) > kMaxBitmapWords)
+    return fail(ETC_ERR_INVALID, "E * ceil(T_max/32) = %lld exceeds %d", (long long)d->E * cdiv(d->T_max, 32), kMaxBitmapWords);
+  if (d->norm_topk != 0 && d->norm_topk != 1) return fail(ETC_ERR_INVALID, "norm_topk must be 0 or 1");
+  if (d->has_bias != 0 && d->has_bias != 1) return fail(ETC_ERR_INVALID, "has_bias must be 0 or 1");
+  return ETC_OK;
+}
+
+int64_t lds_bytes_for(const etc_moe_desc* d) {
+  int64_t s = scan_lds_bytes(d->E, d->T_max);
+  return s > kGemmLdsBytes ? s : kGemmLdsBytes;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int persistent_grid(int sched, int lds, int* grid) {
+  int cus = 0;
+  int rc = device_cus(&cus);
+  if (rc) return rc;
+  int nb = 0;
+  int e = moe_persistent_occupancy(sched, lds, &nb);
+  if (e != hipSuccess) return hip_fail((hipError_t)e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  if (nb < 1) return fail(ETC_ERR_UNSUPPORTED, "persistent kernel does not fit on a CU (lds %d)", lds);
+  const int cap = wg_per_cu_cap();
+  if (nb > cap) nb = cap;
+  *grid = nb * cus;
+  return ETC_OK;
+}
+
+// library-owned control block for the split-K example (one per device)
+struct SplitkCtl {
+  uint32_t* ctl = nullptr;
+  uint64_t* queue = nullptr;
+  int64_t q_cap = 0;
+};
+std::vector<SplitkCtl> g_sk;
+
+}  // namespace
+
+// ======================================================== event tensors ==
+struct etc_etensor {
+  int ndim;
+  int64_t shape[ETC_MAX_DIMS];  // declared (may hold ETC_DIM_SYMBOLIC)
+  int64_t bound[ETC_MAX_DIMS];  // current instantiation
+  int instantiated;
+  int32_t wait_count;
+  int32_t* counters;
+  int owns;
+  int64_t capacity;  // counters available
+  int needs_zero;
+};
+
+extern "C" int etensor_create(etc_etensor** out, int ndim, const int64_t* shape, int32_t wait_count,
+                              int32_t* dev_counters) {
+  if (!out || !shape) return fail(ETC_ERR_INVALID, "NULL argument");
+  *out = nullptr;
+  if (ndim < 1 || ndim > ETC_MAX_DIMS) return fail(ETC_ERR_INVALID, "ndim %d outside [1, %d]", ndim, ETC_MAX_DIMS);
+  if (wait_count < 0 && wait_count != ETC_WAIT_DATA_DEPENDENT) return fail(ETC_ERR_INVALID, "wait_count %d", wait_count);
+  for (int i = 0; i < ndim; ++i)
+    if (shape[i] < 1 && shape[i] != ETC_DIM_SYMBOLIC) return fail(ETC_ERR_INVALID, "shape[%d] = %lld", i, (long long)shape[i]);
+  etc_etensor* et = new (std::nothrow) etc_etensor();
+  if (!et) return fail(ETC_ERR_INVALID, "out of host memory");
+  et->ndim = ndim;
+  bool symbolic = false;
+  for (int i = 0; i < ETC_MAX_DIMS; ++i) {
+    et->shape[i] = i < ndim ? shape[i] : 1;
+    et->bound[i] = et->shape[i];
+    if (i < ndim && shape[i] == ETC_DIM_SYMBOLIC) symbolic = true;
+  }
+  et->instantiated = symbolic ? 0 : 1;
+  et->wait_count = wait_count;
+  et->counters = dev_counters;
+  et->owns = 0;
+  et->capacity = dev_counters ? INT64_MAX : 0;
+  et->needs_zero = 0;
+  *out = et;
+  return ETC_OK;
+}
+
+extern "C" int etensor_instantiate(etc_etensor* et, const int64_t* concrete) {
+  if (!et || !concrete) return fail(ETC_ERR_INVALID, "NULL argument");
+  for (int i = 0; i < et->ndim; ++i) {
+    if (concrete[i] < 1) return fail(ETC_ERR_INVALID, "concrete_shape[%d] = %lld", i, (long long)concrete[i]);
+    if (et->shape[i] != ETC_DIM_SYMBOLIC && et->shape[i] != concrete[i])
+      return fail(ETC_ERR_INVALID, "dimension %d is fixed at %lld, got %lld", i, (long long)et->shape[i],
+                  (long long)concrete[i]);
+  }
+  for (int i = 0; i < et->ndim; ++i) et->bound[i] = concrete[i];
+  et->instantiated = 1;
+  return ETC_OK;
+}
+
+extern "C" int etensor_shape(const etc_etensor* et, int64_t* shape_out, int* ndim_out, int64_t* numel_out) {
+  if (!et) return fail(ETC_ERR_INVALID, "NULL event tensor");
+  int64_t numel = 1;
+  for (int i = 0; i < et->ndim; ++i) {
+    const int64_t d = et->instantiated ? et->bound[i] : et->shape[i];
+    if (shape_out) shape_out[i] = d;
+    numel *= d;
+  }
+  if (shape_out)
+    for (int i = et->ndim; i < ETC_MAX_DIMS; ++i) shape_out[i] = 0;
+  if (ndim_out) *ndim_out = et->ndim;
+  if (numel_out) *numel_out = et->instantiated ? numel : 0;
+  return ETC_OK;
+}
+
+extern "C" int etensor_destroy(etc_etensor* et) {
+  if (!et) return ETC_OK;
+  if (et->owns && et->counters) (void)hipFree(et->counters);
+  delete et;
+  return ETC_OK;
+}
+
+static int etensor_numel(const etc_etensor* et) {
+  int64_t n = 0;
+  etensor_shape(et, nullptr, nullptr, &n);
+  return (int)n;
+}
+
+// Counters for a launch: caller-owned, or allocated here once (a set-up
+// cost, never on the MoE path) and zeroed.
+static int etensor_device_counters(etc_etensor* et, int64_t numel, void* stream) {
+  if (et->counters && et->capacity >= numel && !et->needs_zero) return ETC_OK;
+  if (!et->counters || et->capacity < numel) {
+    if (et->counters && !et->owns)
+      return fail(ETC_ERR_INVALID, "caller-owned counters are smaller than the instantiation");
+    if (et->counters) (void)hipFree(et->counters);
+    et->counters = nullptr;
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&et->counters), (size_t)numel * 4);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(event counters)");
+    et->owns = 1;
+    et->capacity = numel;
+    et->needs_zero = 1;
+  }
+  if (et->needs_zero) {
+    hipError_t e = hipMemsetAsync(et->counters, 0, (size_t)et->capacity * 4, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(event counters)");
+    et->needs_zero = 0;
+  }
+  return ETC_OK;
+}
+
+extern "C" int etc_splitk_launch(etc_etensor* ev, int32_t n, int32_t nsplit, int32_t bk, const int32_t* A,
+                                 int32_t* B, int32_t* C, int sched, void* stream) {
+  if (!ev || !A || !B || !C) return fail(ETC_ERR_INVALID, "NULL argument");
+  if (sched != ETC_SCHED_STATIC && sched != ETC_SCHED_DYNAMIC)
+    return fail(ETC_ERR_UNSUPPORTED, "split-K runs under STATIC or DYNAMIC only");
+  if (n < 1 || nsplit < 1 || bk < 1 || (int64_t)n * nsplit > (1 << 28))
+    return fail(ETC_ERR_INVALID, "bad sizes n=%d nsplit=%d bk=%d", n, nsplit, bk);
+  if (!ev->instantiated || ev->ndim != 1 || ev->bound[0] != n)
+    return fail(ETC_ERR_INVALID, "event tensor must be instantiated to shape [n=%d]", n);
+  if (ev->wait_count != nsplit)
+    return fail(ETC_ERR_INVALID, "event wait_count %d != nsplit %d", ev->wait_count, nsplit);
+  int rc = etensor_device_counters(ev, n, stream);
+  if (rc) return rc;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if ((int)g_sk.size() <= dev) g_sk.resize(dev + 1);
+  }
+  SplitkCtl& sk = g_sk[dev];
+  if (sk.q_cap < n) {
+    if (sk.ctl) (void)hipFree(sk.ctl);
+    const int64_t cap = n > 4096 ? n : 4096;
+    const size_t bytes = 256 + (size_t)cap * 8;
+    void* mem = nullptr;
+    e = hipMalloc(&mem, bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(split-K control)");
+    e = hipMemsetAsync(mem, 0, bytes, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(split-K control)");
+    sk.ctl = static_cast<uint32_t*>(mem);
+    sk.queue = reinterpret_cast<uint64_t*>(static_cast<char*>(mem) + 256);
+    sk.q_cap = cap;
+  }
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc) return rc;
+  int nb = 0;
+  e = (hipError_t)splitk_occupancy(sched, &nb);
+  if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  if (nb < 1) nb = 1;
+  if (nb > 2) nb = 2;
+  e = (hipError_t)launch_splitk(n, nsplit, bk, A, B, C, ev->counters, sk.ctl, sk.queue, sk.q_cap, sched, nb * cus,
+                                kDefaultSpins, stream);
+  if (e != hipSuccess) return hip_fail(e, "split-K launch");
+  add_pending(stream, sk.ctl + 4 /* report word */);
+  return ETC_OK;
+}
+
+// ============================================================ MoE layer ==
+extern "C" size_t moe_layer_workspace_size(const etc_moe_desc* d) {
+  if (desc_check(d) != ETC_OK) return 0;
+  return (size_t)moe_layout(*d).total_bytes;
+}
+
+extern "C" int moe_layer_info(const etc_moe_desc* d, etc_moe_info* info) {
+  int rc = desc_check(d);
+  if (rc) return rc;
+  if (!info) return fail(ETC_ERR_INVALID, "info is NULL");
+  std::memset(info, 0, sizeof *info);
+  info->bm = kBM;
+  info->bn1 = kBN1;
+  info->bn2 = kBN2;
+  info->router_tokens = kRouterT;
+  info->router_experts = kRouterE;
+  info->dispatch_tokens = kDispatchT;
+  info->combine_tokens = kCombineT;
+  info->threads = kThreads;
+  info->lds_bytes = (int32_t)lds_bytes_for(d);
+  int grid = 0;
+  rc = persistent_grid(ETC_SCHED_STATIC, info->lds_bytes, &grid);
+  if (rc) return rc;
+  info->grid = grid;
+  return ETC_OK;
+}
+
+extern "C" int moe_workspace_init(const etc_moe_desc* d, void* ws, size_t bytes, void* stream) {
+  int rc = desc_check(d);
+  if (rc) return rc;
+  const MoeLayout L = moe_layout(*d);
+  if (!ws || !aligned16(ws)) return fail(ETC_ERR_INVALID, "workspace NULL or not 16-byte aligned");
+  if (bytes < (size_t)L.total_bytes) return fail(ETC_ERR_INVALID, "workspace has %zu bytes, needs %lld", bytes, (long long)L.total_bytes);
+  hipError_t e = hipMemsetAsync(ws, 0, (size_t)L.b_meta, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(workspace control)");
+  return ETC_OK;
+}
+
+extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a, int sched, void* stream) {
+  int rc = desc_check(d);
+  if (rc) return rc;
+  if (!a) return fail(ETC_ERR_INVALID, "args is NULL");
+  if (T < 1 || T > d->T_max) return fail(ETC_ERR_INVALID, "T %d outside [1, T_max=%d]", T, d->T_max);
+  if (sched != ETC_SCHED_STATIC && sched != ETC_SCHED_DYNAMIC && sched != ETC_SCHED_KBK && sched != ETC_SCHED_BARRIER)
+    return fail(ETC_ERR_INVALID, "unknown schedule %d", sched);
+  const void* bf[] = {a->x, a->w_router, a->w13, a->w2, a->out, a->workspace};
+  const char* bfn[] = {"x", "w_router", "w13", "w2", "out", "workspace"};
+  for (int i = 0; i < 6; ++i)
+    if (!bf[i] || !aligned16(bf[i])) return fail(ETC_ERR_INVALID, "%s is NULL or not 16-byte aligned", bfn[i]);
+  const void* iv[] = {a->topk_ids, a->topk_w, a->counts, a->exp_indptr, a->perm, a->slot};
+  const char* ivn[] = {"topk_ids", "topk_w", "counts", "exp_indptr", "perm", "slot"};
+  for (int i = 0; i < 6; ++i)
+    if (!iv[i] || !aligned4(iv[i])) return fail(ETC_ERR_INVALID, "%s is NULL or not 4-byte aligned", ivn[i]);
+  if (d->has_bias && (!a->b_router || !aligned4(a->b_router))) return fail(ETC_ERR_INVALID, "b_router is NULL or misaligned");
+  if (a->debug && !aligned4(a->debug)) return fail(ETC_ERR_INVALID, "debug misaligned");
+  const MoeLayout L = moe_layout(*d);
+  if (a->workspace_bytes < (size_t)L.total_bytes)
+    return fail(ETC_ERR_INVALID, "workspace has %zu bytes, needs %lld", a->workspace_bytes, (long long)L.total_bytes);
+
+  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
+  MoeParams p{};
+  p.x = static_cast<const uint16_t*>(a->x);
+  p.wr = static_cast<const uint16_t*>(a->w_router);
+  p.br = d->has_bias ? a->b_router : nullptr;
+  p.w13 = static_cast<const uint16_t*>(a->w13);
+  p.w2 = static_cast<const uint16_t*>(a->w2);
+  p.out = static_cast<uint16_t*>(a->out);
+  p.ids = a->topk_ids;
+  p.topw = a->topk_w;
+  p.counts = a->counts;
+  p.indptr = a->exp_indptr;
+  p.perm = a->perm;
+  p.slot = a->slot;
+  p.debug = a->debug;
+  p.ctrl = reinterpret_cast<uint32_t*>(ws + L.b_ctrl);
+  p.set0 = reinterpret_cast<uint32_t*>(ws + L.b_set0);
+  p.set1 = reinterpret_cast<uint32_t*>(ws + L.b_set1);
+  p.meta = reinterpret_cast<uint32_t*>(ws + L.b_meta);
+  p.tile_indptr = reinterpret_cast<int32_t*>(ws + L.b_tile_indptr);
+  p.rt_info = reinterpret_cast<int32_t*>(ws + L.b_rt_info);
+  p.logits = reinterpret_cast<float*>(ws + L.b_logits);
+  p.xp = reinterpret_cast<uint16_t*>(ws + L.b_xp);
+  p.hh = reinterpret_cast<uint16_t*>(ws + L.b_hh);
+  p.y = reinterpret_cast<uint16_t*>(ws + L.b_y);
+  p.set_words = L.set_words;
+  p.o_ev_logit = L.o_ev_logit;
+  p.o_ev_exp = L.o_ev_exp;
+  p.o_ev_h = L.o_ev_h;
+  p.o_ev_c = L.o_ev_c;
+  p.o_queue = L.o_queue;
+  p.q_cap = L.q_cap;
+  p.T = T;
+  p.H = d->H;
+  p.E = d->E;
+  p.k = d->k;
+  p.I = d->I;
+  p.norm_topk = d->norm_topk;
+  p.has_bias = d->has_bias;
+  p.max_rt = L.max_rt;
+  p.budget = a->watchdog_spins ? a->watchdog_spins : kDefaultSpins;
+
+  const int lds = (int)lds_bytes_for(d);
+  int e;
+  if (sched == ETC_SCHED_KBK) {
+    e = launch_moe_kbk(p, (int)scan_lds_bytes(d->E, d->T_max), stream);
+  } else {
+    int grid = 0;
+    rc = persistent_grid(sched, lds, &grid);
+    if (rc) return rc;
+    e = launch_moe_persistent(p, sched, grid, lds, stream);
+  }
+  if (e != hipSuccess) return hip_fail((hipError_t)e, "MoE launch");
+  add_pending(stream, p.ctrl + C_REPORT);
+  return ETC_OK;
+}
+
+extern "C" int etc_sync(void* stream) {
+  hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  std::vector<uint32_t*> reports;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (size_t i = 0; i < g_pending.size();) {
+      if (g_pending[i].stream == stream) {
+        reports.push_back(g_pending[i].report);
+        g_pending[i] = g_pending.back();
+        g_pending.pop_back();
+      } else {
+        ++i;
+      }
+    }
+  }
+  int result = ETC_OK;
+  for (uint32_t* r : reports) {
+    uint32_t st = 0;
+    e = hipMemcpy(&st, r, 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(status report)");
+    if (st) {
+      const uint32_t zero = 0;
+      e = hipMemcpy(r, &zero, 4, hipMemcpyHostToDevice);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpy(clear status report)");
+      const int code = status_to_code(st);
+      if (result == ETC_OK) result = code;
+    }
+  }
+  if (result == ETC_OK) g_err.clear();
+  return result;
+}
+
+extern "C" const char* etc_last_error(void) { return g_err.c_str(); }

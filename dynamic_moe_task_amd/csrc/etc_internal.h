@@ -1,0 +1,158 @@
+// Internal shared definitions of libetc: tile constants, the workspace
+// layout (computed on the host, passed to the kernels) and the kernel
+// parameter block.  Not part of the public C ABI.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/etc.h"
+
+namespace etc {
+
+// status bits (word 0 of a counter set, OR-ed into the report word)
+enum : uint32_t {
+  ST_TIMEOUT = 1u,
+  ST_OVER_NOTIFY = 2u,
+  ST_NONFINITE = 4u,
+  ST_QUEUE_OVERFLOW = 8u,
+  ST_ABORT = 0x80000000u,
+};
+
+// ---- task geometry -------------------------------------------------------
+constexpr int kThreads = 256;   // 4 wave64 per workgroup
+constexpr int kRouterT = 4;     // R task: tokens ...
+constexpr int kRouterE = 4;     //         ... x experts (one expert per wave)
+constexpr int kBM = 16;         // grouped-GEMM row tile (one 16-row MFMA block)
+constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile
+constexpr int kBN2 = 64;        // G2: output columns per tile (4 MFMA column blocks)
+constexpr int kDispatchT = 2;   // D task: tokens per task
+constexpr int kCombineT = 2;    // C task: tokens per task
+constexpr int kMaxK = 16;
+constexpr int kMaxE = 256;
+constexpr int kMaxTmax = 4096;
+constexpr int kMaxHI = 16384;
+constexpr int kMaxBitmapWords = 8192;  // E * ceil(T_max / 32), LDS of the scan task
+// spin budget of one in-kernel wait (each spin: one agent-scope load plus a
+// short s_sleep); a healthy wait lasts well under a thousand spins
+constexpr uint32_t kDefaultSpins = 1u << 20;
+
+// task types (queue descriptors carry them in bits 60..63; 0 = empty slot)
+enum TaskType : int { TT_R = 1, TT_K = 2, TT_S = 3, TT_D = 4, TT_G1 = 5, TT_G2 = 6, TT_C = 7 };
+
+// ---- counter set (u32 words) ------------------------------------------------
+enum : int {
+  W_STATUS = 0,
+  W_DONE = 1,
+  W_HEAD = 2,
+  W_TAIL = 3,
+  W_TOTAL = 4,
+  W_BAR_COUNT = 5,
+  W_BAR_GEN = 6,
+  W_EV_ROUTE = 7,
+  W_EV_SCAN = 8,
+  W_FIXED = 16,  // start of the variable-size event tensors
+};
+// control block (u32 words)
+enum : int { C_EPOCH = 0, C_REPORT = 1, C_WORDS = 64 };
+
+struct MoeLayout {
+  // sizes derived from the descriptor's T_max
+  int32_t ntt_max, max_rt, nct_max, ndt_max;
+  int64_t q_cap;
+  // word offsets inside a counter set
+  int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_c, o_queue;  // o_queue in words, 8-byte aligned
+  int64_t set_words;
+  // byte offsets inside the workspace
+  int64_t b_ctrl, b_set0, b_set1, b_meta, b_tile_indptr, b_rt_info, b_logits, b_xp, b_hh, b_y;
+  int64_t total_bytes;
+};
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t align_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// meta words (outside the double-buffered sets): written by the scan task
+enum : int { M_NRT = 0, M_WORDS = 16 };
+
+inline MoeLayout moe_layout(const etc_moe_desc& d) {
+  MoeLayout L{};
+  const int64_t Tm = d.T_max;
+  L.ntt_max = (int32_t)cdiv(Tm, kRouterT);
+  L.nct_max = (int32_t)cdiv(Tm, kCombineT);
+  L.ndt_max = (int32_t)cdiv(Tm, kDispatchT);
+  const int64_t rows = Tm * d.k;
+  L.max_rt = (int32_t)(cdiv(rows, kBM) + (rows < d.E ? rows : d.E));
+  const int64_t nN1 = d.I / kBN1, nN2 = d.H / kBN2;
+  // every task except the router prefix goes through the queue
+  L.q_cap = L.ntt_max + 1 + L.ndt_max + (int64_t)L.max_rt * (nN1 + nN2) + L.nct_max + 64;
+  int64_t w = W_FIXED;
+  L.o_ev_logit = w; w += L.ntt_max;
+  L.o_ev_exp = w;   w += d.E;
+  L.o_ev_h = w;     w += L.max_rt;
+  L.o_ev_c = w;     w += L.nct_max;
+  w = align_up(w, 2);
+  L.o_queue = w;    w += 2 * L.q_cap;
+  L.set_words = align_up(w, 64);
+  int64_t b = 0;
+  L.b_ctrl = b;          b += C_WORDS * 4;
+  L.b_set0 = b;          b += L.set_words * 4;
+  L.b_set1 = b;          b += L.set_words * 4;
+  L.b_meta = b;          b += M_WORDS * 4;
+  L.b_tile_indptr = b;   b += align_up((int64_t)(d.E + 1) * 4, 256);
+  L.b_rt_info = b;       b += align_up((int64_t)L.max_rt * 16, 256);
+  L.b_logits = b;        b += align_up(Tm * d.E * 4, 256);
+  L.b_xp = b;            b += align_up(rows * d.H * 2, 256);
+  L.b_hh = b;            b += align_up(rows * d.I * 2, 256);
+  L.b_y = b;             b += align_up(rows * d.H * 2, 256);
+  L.total_bytes = b;
+  return L;
+}
+
+// LDS bytes the scan task needs: presence bitmap, per-word prefix (u16),
+// counts / exp_indptr / tile_indptr scratch.
+inline int64_t scan_lds_bytes(int E, int T_max) {
+  const int64_t W = cdiv(T_max, 32);
+  return align_up((int64_t)E * W * 4, 16) + align_up((int64_t)E * W * 2, 16) + 3 * 260 * 4 + 64;
+}
+constexpr int64_t kGemmLdsBytes = 4 * 4 * 256 * 4;  // G2 cross-wave reduction buffer
+
+struct MoeParams {
+  const uint16_t* x;
+  const uint16_t* wr;
+  const float* br;
+  const uint16_t* w13;
+  const uint16_t* w2;
+  uint16_t* out;
+  int32_t* ids;
+  float* topw;
+  int32_t* counts;
+  int32_t* indptr;
+  int32_t* perm;
+  int32_t* slot;
+  int32_t* debug;
+  uint32_t* ctrl;
+  uint32_t* set0;
+  uint32_t* set1;
+  uint32_t* meta;
+  int32_t* tile_indptr;
+  int32_t* rt_info;  // [max_rt][4]: expert, first grouped row, rows, 0
+  float* logits;
+  uint16_t* xp;
+  uint16_t* hh;
+  uint16_t* y;
+  int64_t set_words;
+  int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_c, o_queue, q_cap;
+  int32_t T, H, E, k, I, norm_topk, has_bias;
+  int32_t max_rt;
+  uint32_t budget;
+};
+
+// Host-side launchers (moe_kernels.hip).  Return a hipError_t value.
+int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes, void* stream);
+int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream);
+int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu);
+int launch_splitk(int n, int nsplit, int bk, const int32_t* A, int32_t* B, int32_t* C,
+                  int32_t* ev, uint32_t* ctl, uint64_t* queue, int64_t q_cap, int sched, int grid,
+                  uint32_t budget, void* stream);
+int splitk_occupancy(int sched, int* blocks_per_cu);
+
+}  // namespace etc

@@ -1,0 +1,969 @@
+// One MoE layer as a graph of tiled tasks inside one persistent HIP kernel
+// for gfx950 (MI355X), plus the kernel-by-kernel comparator built from the
+// same task bodies.
+//
+// Task graph (Event Tensor, arXiv 2604.13327: Fig. 2 and Fig. 5b; podcast
+// cues 7 and 9):
+//   R(tt, et)  router logits for a tile of tokens x experts (fixed-order fp32)
+//   K(tt)      top-k + routing weights for the tile's tokens      waits ev_logit[tt]
+//   S          counts, exp_indptr, stable permutation, row tiles   waits ev_route
+//   D(dt)      copy routed rows into expert-grouped order and notify
+//              ev_exp[e] once per routed (token, slot)             waits ev_scan
+//   G1(rt, nt) gate/up GEMM + SwiGLU for one row tile of one expert waits ev_exp[e]
+//              (ev_exp[e] is released after counts[e] notifies: the
+//              data-dependent update; expert e's tiles cover grouped rows
+//              [exp_indptr[e], exp_indptr[e+1]): the data-dependent trigger)
+//   G2(rt, nt) down projection                                     waits ev_h[rt]
+//   C(ct)      weighted combine of the k expert rows per token     waits ev_c[ct]
+//
+// Schedules: STATIC (closed-form phase-ordered per-workgroup lists, notify /
+// wait; Figs. 6-7), DYNAMIC (early push onto one HBM queue when a notify
+// completes an event, pop by idle workgroups; Figs. 8-9), BARRIER (same
+// lists, grid barriers instead of events), KBK (one launch per task type).
+// T is a kernel argument; every event shape and task count below is derived
+// from it in the kernel (Fig. 4: one template, instantiated per launch).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "etc_internal.h"
+#include "etc_rt.h"
+
+namespace etc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+enum Mode : int { MODE_STATIC = ETC_SCHED_STATIC, MODE_DYNAMIC = ETC_SCHED_DYNAMIC,
+                  MODE_KBK = ETC_SCHED_KBK, MODE_BARRIER = ETC_SCHED_BARRIER };
+
+constexpr uint64_t kDescExit = ~0ull;
+
+// ------------------------------------------------------------- helpers --
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ u32x4_t ld4(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ void st4(uint16_t* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+__device__ __forceinline__ bf16x8_t as_bf(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ void unpack8(u32x4_t v, float* f) {
+  f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+  f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+}
+__device__ __forceinline__ uint64_t make_desc(int type, uint32_t a, uint32_t b) {
+  return ((uint64_t)type << 60) | ((uint64_t)(a & 0x3fffffffu) << 30) | (uint64_t)(b & 0x3fffffffu);
+}
+__device__ __forceinline__ int desc_type(uint64_t d) { return (int)(d >> 60); }
+__device__ __forceinline__ uint32_t desc_a(uint64_t d) { return (uint32_t)((d >> 30) & 0x3fffffffu); }
+__device__ __forceinline__ uint32_t desc_b(uint64_t d) { return (uint32_t)(d & 0x3fffffffu); }
+__device__ __forceinline__ int first_of(int w, int64_t off, int G) {
+  int o = (int)(off % G);
+  return (w - o + G) % G;
+}
+
+struct RowTile {
+  int e, r0, nrows;
+};
+__device__ __forceinline__ RowTile load_rowtile(const MoeParams& p, int rt) {
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p.rt_info) + 4 * rt;
+  RowTile r;
+  r.e = (int)ld_relaxed(q + 0);
+  r.r0 = (int)ld_relaxed(q + 1);
+  r.nrows = (int)ld_relaxed(q + 2);
+  return r;
+}
+
+// Per-launch sizes, all derived from T (the symbolic batch dimension).
+struct Ctx {
+  uint32_t* set;     // counter set of this launch (NULL for kernel-by-kernel)
+  uint32_t* status;  // where error bits go
+  uint64_t* queue;
+  int T, H, E, k, I;
+  int nTT, nET, nR, nK, nD, nC, nN1, nN2;
+  uint32_t budget;
+};
+
+__device__ __forceinline__ Ctx make_ctx(const MoeParams& p, uint32_t* set) {
+  Ctx c;
+  c.set = set;
+  c.status = set ? set + W_STATUS : p.ctrl + C_REPORT;
+  c.queue = set ? reinterpret_cast<uint64_t*>(set + p.o_queue) : nullptr;
+  c.T = p.T; c.H = p.H; c.E = p.E; c.k = p.k; c.I = p.I;
+  c.nTT = (p.T + kRouterT - 1) / kRouterT;
+  c.nET = (p.E + kRouterE - 1) / kRouterE;
+  c.nR = c.nTT * c.nET;
+  c.nK = c.nTT;
+  c.nD = (p.T + kDispatchT - 1) / kDispatchT;
+  c.nC = (p.T + kCombineT - 1) / kCombineT;
+  c.nN1 = p.I / kBN1;
+  c.nN2 = p.H / kBN2;
+  c.budget = p.budget;
+  return c;
+}
+
+struct Shared {
+  uint64_t desc;
+  int n;           // number of completed events collected by this task
+  int base;        // first reserved queue slot
+  int total;       // descriptors to write
+  int list[kDispatchT * kMaxK + kBM];
+  int pref[kDispatchT * kMaxK + kBM + 1];
+};
+
+__device__ __forceinline__ void dbg_task(const MoeParams& p, int type) {
+  if (p.debug && threadIdx.x == 0) atomicAdd(p.debug + 2 * p.E + (type - 1), 1);
+}
+
+// ===================================================== task bodies ==========
+// R: router logits, L[t, e] = sum_h x[t, h] * wr[e, h] (+ b[e]).  Wave w of
+// the workgroup owns expert e = et*4 + w; lane l owns the 8-element chunks
+// c = l, l+64, ... of the hidden dimension and accumulates them in ascending
+// order with fused multiply-adds; the 64 lane sums are combined by a halving
+// xor butterfly whose lane-0 result equals the tree acc[l] += acc[l + s],
+// s = 32..1.  This fixed order is what makes the top-k decision
+// reproducible bit for bit.
+__device__ void task_router(const MoeParams& p, const Ctx& c, int tt, int et) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e = et * kRouterE + wv;
+  if (e >= c.E) return;
+  const int t0 = tt * kRouterT;
+  float acc[kRouterT];
+#pragma unroll
+  for (int r = 0; r < kRouterT; ++r) acc[r] = 0.0f;
+  const int nchunk = c.H >> 3;
+  const uint16_t* wrow = p.wr + (size_t)e * c.H;
+  for (int ch = lane; ch < nchunk; ch += 64) {
+    float wf[8];
+    unpack8(ld4(wrow + ch * 8), wf);
+#pragma unroll
+    for (int r = 0; r < kRouterT; ++r) {
+      if (t0 + r < c.T) {
+        float xf[8];
+        unpack8(ld4(p.x + (size_t)(t0 + r) * c.H + ch * 8), xf);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[r] = __builtin_fmaf(xf[q], wf[q], acc[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRouterT; ++r) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) acc[r] = acc[r] + __shfl_xor(acc[r], s);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < kRouterT; ++r) {
+      const int t = t0 + r;
+      if (t < c.T) {
+        float v = acc[r];
+        if (p.has_bias) v = v + p.br[e];
+        p.logits[(size_t)t * c.E + e] = v;
+      }
+    }
+  }
+}
+
+// K: top-k per token (one wave per token): k rounds of a wave-wide arg-max
+// on (logit descending, expert index ascending); weights exp(l_j - l_max)
+// normalised over the chosen k (norm_topk) or over all E.
+__device__ __forceinline__ bool ranks_before(float a, int ia, float b, int ib) {
+  return a > b || (a == b && ia < ib);
+}
+__device__ void task_topk(const MoeParams& p, const Ctx& c, int tt) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = tt * kRouterT + wv;
+  if (t >= c.T) return;
+  const float NEG_INF = -__builtin_inff();
+  const float* L = p.logits + (size_t)t * c.E;
+  float v[4];
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    float x = NEG_INF;
+    if (e < c.E) {
+      x = L[e];
+      if (x != x) { bad = true; x = NEG_INF; }
+    }
+    v[j] = x;
+  }
+  if (__any(bad) && lane == 0) or_relaxed(c.status, ST_NONFINITE);
+  uint32_t taken = 0;
+  float my_v = 0.0f, v0 = 0.0f;
+  int my_e = 0;
+  for (int r = 0; r < c.k; ++r) {
+    float bv = NEG_INF;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      if (e < c.E && !((taken >> j) & 1u) && ranks_before(v[j], e, bv, be)) { bv = v[j]; be = e; }
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+      const float ov = __shfl_xor(bv, s);
+      const int oe = __shfl_xor(be, s);
+      if (ranks_before(ov, oe, bv, be)) { bv = ov; be = oe; }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == r) { my_v = bv; my_e = be; }
+    if (r == 0) v0 = bv;
+  }
+  float part = 0.0f;
+  if (p.norm_topk) {
+    if (lane < c.k) part = expf(my_v - v0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j < c.E) part += expf(v[j] - v0);
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) part = part + __shfl_xor(part, s);
+  if (lane < c.k) {
+    p.ids[(size_t)t * c.k + lane] = my_e;
+    p.topw[(size_t)t * c.k + lane] = expf(my_v - v0) / part;
+  }
+}
+
+// Block-wide exclusive scan of one int per thread (256 threads).
+__device__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const int o = __shfl_up(incl, s);
+    if (lane >= s) incl += o;
+  }
+  if (lane == 63) tmp[wv] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int x = tmp[i];
+    if (i < wv) off += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + incl - v;
+}
+
+// S: counts, exp_indptr (exclusive prefix sum of counts, ends at T*k), the
+// stable permutation (rows of one expert keep ascending token order) and
+// the row-tile table.  One workgroup; a per-expert token bitmap in LDS gives
+// each routed pair its rank among the same expert's earlier tokens.
+__device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
+  const int tid = threadIdx.x;
+  const int E = c.E, k = c.k, n = c.T * c.k;
+  const int W = (c.T + 31) >> 5;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(smem);
+  uint16_t* pre = reinterpret_cast<uint16_t*>(smem + ((E * W * 4 + 15) & ~15));
+  int* cnt = reinterpret_cast<int*>(smem + ((E * W * 4 + 15) & ~15) + ((E * W * 2 + 15) & ~15));
+  int* iptr = cnt + 260;
+  int* tptr = iptr + 260;
+  int* tmp = tptr + 260;
+  for (int i = tid; i < E * W; i += kThreads) bits[i] = 0u;
+  __syncthreads();
+  for (int f = tid; f < n; f += kThreads) {
+    const int e = p.ids[f];
+    const int t = f / k;
+    atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    int run = 0;
+    for (int w = 0; w < W; ++w) {
+      pre[e * W + w] = (uint16_t)run;
+      run += __popc(bits[e * W + w]);
+    }
+    cnt[e] = run;
+  }
+  __syncthreads();
+  const int my = tid < E ? cnt[tid] : 0;
+  const int mytiles = (my + kBM - 1) / kBM;
+  int tot_rows = 0, tot_tiles = 0;
+  const int ex = block_excl_scan(my, tmp, &tot_rows);
+  const int ext = block_excl_scan(mytiles, tmp + 8, &tot_tiles);
+  if (tid < E) {
+    iptr[tid] = ex;
+    tptr[tid] = ext;
+    p.counts[tid] = my;
+    p.indptr[tid] = ex;
+    p.tile_indptr[tid] = ext;
+  }
+  if (tid == 0) {
+    iptr[E] = tot_rows;
+    tptr[E] = tot_tiles;
+    p.indptr[E] = tot_rows;
+    p.tile_indptr[E] = tot_tiles;
+    st_relaxed(p.meta + M_NRT, (uint32_t)tot_tiles);
+  }
+  __syncthreads();
+  for (int f = tid; f < n; f += kThreads) {
+    const int e = p.ids[f];
+    const int t = f / k;
+    const int w = t >> 5, b = t & 31;
+    const int s = iptr[e] + pre[e * W + w] + __popc(bits[e * W + w] & ((1u << b) - 1u));
+    p.slot[f] = s;
+    p.perm[s] = f;
+  }
+  for (int e = tid; e < E; e += kThreads) {
+    const int ce = cnt[e];
+    for (int mt = 0; mt * kBM < ce; ++mt) {
+      int* q = p.rt_info + 4 * (tptr[e] + mt);
+      q[0] = e;
+      q[1] = iptr[e] + mt * kBM;
+      q[2] = min(kBM, ce - mt * kBM);
+      q[3] = 0;
+    }
+  }
+}
+
+// D: copy every routed row of the task's tokens into expert-grouped order,
+// Xp[slot[t*k+j], :] = X[t, :] (16-byte coalesced chunks).
+__device__ void task_dispatch_copy(const MoeParams& p, const Ctx& c, int dt) {
+  const int t0 = dt * kDispatchT;
+  const int ntok = min(kDispatchT, c.T - t0);
+  const int rows = ntok * c.k;
+  const int cpr = c.H >> 3;
+  for (int i = threadIdx.x; i < rows * cpr; i += kThreads) {
+    const int r = i / cpr, ch = i - r * cpr;
+    const int f = t0 * c.k + r;
+    const int t = t0 + r / c.k;
+    const int s = p.slot[f];
+    st4(p.xp + (size_t)s * c.H + ch * 8, ld4(p.x + (size_t)t * c.H + ch * 8));
+  }
+}
+
+// G1: one 16-row tile of expert e times 16 gate and 16 up columns of W13,
+// SwiGLU, Hmid = bf16(silu(g) * u).  bf16 MFMA 16x16x32 with fp32
+// accumulation; the 4 waves split K = H in quarters and reduce in LDS.  The
+// weight tile (2 x 16 rows x H) streams straight from HBM into registers;
+// rows past the expert's count are zero-filled, never loaded.
+__device__ void task_g1(const MoeParams& p, const Ctx& c, int rt, int nt, float* red) {
+  const RowTile tile = load_rowtile(p, rt);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int m = lane & 15, kg = lane >> 4;
+  const int H = c.H, I = c.I;
+  const int kw = H >> 2;
+  const int nsteps = kw >> 5;
+  const bool valid = m < tile.nrows;
+  const uint16_t* pa = p.xp + (size_t)(tile.r0 + (valid ? m : 0)) * H + wv * kw + kg * 8;
+  const uint16_t* pg = p.w13 + ((size_t)tile.e * 2 * I + (size_t)nt * kBN1 + m) * H + wv * kw + kg * 8;
+  const uint16_t* pu = pg + (size_t)I * H;
+  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  constexpr int U = 8;
+  for (int s0 = 0; s0 < nsteps; s0 += U) {
+    u32x4_t a[U], bg[U], bu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < nsteps) {
+        a[u] = valid ? ld4(pa + (s0 + u) * 32) : zero;
+        bg[u] = ld4(pg + (s0 + u) * 32);
+        bu[u] = ld4(pu + (s0 + u) * 32);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < nsteps) {
+        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u]), as_bf(bg[u]), accg, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u]), as_bf(bu[u]), accu, 0, 0, 0);
+      }
+    }
+  }
+  // cross-wave reduction: red[w][0 = gate, 1 = up][lane * 4 + i]; the
+  // barrier keeps the previous task's readers of `red` ahead of these writes
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    red[(wv * 2 + 0) * 256 + lane * 4 + i] = accg[i];
+    red[(wv * 2 + 1) * 256 + lane * 4 + i] = accu[i];
+  }
+  __syncthreads();
+  const int tid = threadIdx.x;
+  float g = 0.f, u = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    g += red[(w * 2 + 0) * 256 + tid];
+    u += red[(w * 2 + 1) * 256 + tid];
+  }
+  // element (lane', i) of the 16x16 MFMA result: row 4*(lane'/16) + i, column lane' % 16
+  const int ol = tid >> 2, oi = tid & 3;
+  const int row = 4 * (ol >> 4) + oi, col = ol & 15;
+  if (row < tile.nrows) {
+    const float h = g / (1.0f + __expf(-g)) * u;
+    p.hh[(size_t)(tile.r0 + row) * I + nt * kBN1 + col] = (uint16_t)f2bf(h);
+  }
+}
+
+// G2: one 16-row tile times 64 output columns of Wd[e]: Y = bf16(Hmid Wd^T).
+// The 4 waves split K = I in quarters; each wave keeps 4 column blocks.
+__device__ void task_g2(const MoeParams& p, const Ctx& c, int rt, int nt2, float* red) {
+  const RowTile tile = load_rowtile(p, rt);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int m = lane & 15, kg = lane >> 4;
+  const int H = c.H, I = c.I;
+  const int kw = I >> 2;
+  const int nsteps = kw >> 5;
+  const bool valid = m < tile.nrows;
+  const uint16_t* pa = p.hh + (size_t)(tile.r0 + (valid ? m : 0)) * I + wv * kw + kg * 8;
+  const uint16_t* pb = p.w2 + ((size_t)tile.e * H + (size_t)nt2 * kBN2 + m) * I + wv * kw + kg * 8;
+  const size_t cbs = (size_t)16 * I;  // next 16-column block of Wd
+  f32x4_t acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  constexpr int U = 4;
+  for (int s0 = 0; s0 < nsteps; s0 += U) {
+    u32x4_t a[U], bb[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < nsteps) {
+        a[u] = valid ? ld4(pa + (s0 + u) * 32) : zero;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bb[u][b] = ld4(pb + b * cbs + (s0 + u) * 32);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < nsteps) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u]), as_bf(bb[u][b]), acc[b], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wv * 4 + b) * 256 + lane * 4 + i] = acc[b][i];
+  __syncthreads();
+  const int tid = threadIdx.x;
+  const int ol = tid >> 2, oi = tid & 3;
+  const int row = 4 * (ol >> 4) + oi, col = ol & 15;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    float y = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) y += red[(w * 4 + b) * 256 + tid];
+    if (row < tile.nrows)
+      p.y[(size_t)(tile.r0 + row) * H + nt2 * kBN2 + b * 16 + col] = (uint16_t)f2bf(y);
+  }
+}
+
+// C: out[t, :] = bf16(sum_j w[t, j] * Y[slot[t*k+j], :]), fp32 in j order.
+__device__ void task_combine(const MoeParams& p, const Ctx& c, int ct) {
+  const int t0 = ct * kCombineT;
+  const int ntok = min(kCombineT, c.T - t0);
+  const int cpr = c.H >> 3;
+  for (int i = threadIdx.x; i < ntok * cpr; i += kThreads) {
+    const int r = i / cpr, ch = i - r * cpr;
+    const int t = t0 + r;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < c.k; ++j) {
+      const float wj = p.topw[(size_t)t * c.k + j];
+      const int s = p.slot[(size_t)t * c.k + j];
+      float yf[8];
+      unpack8(ld4(p.y + (size_t)s * c.H + ch * 8), yf);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj, yf[q], acc[q]);
+    }
+    u32x4_t o;
+    o.x = f2bf(acc[0]) | (f2bf(acc[1]) << 16);
+    o.y = f2bf(acc[2]) | (f2bf(acc[3]) << 16);
+    o.z = f2bf(acc[4]) | (f2bf(acc[5]) << 16);
+    o.w = f2bf(acc[6]) | (f2bf(acc[7]) << 16);
+    st4(p.out + (size_t)t * c.H + ch * 8, o);
+  }
+}
+
+// =================================================== event plumbing ========
+__device__ __forceinline__ uint32_t* ev_logit(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_logit; }
+__device__ __forceinline__ uint32_t* ev_exp(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_exp; }
+__device__ __forceinline__ uint32_t* ev_h(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_h; }
+__device__ __forceinline__ uint32_t* ev_c(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_c; }
+__device__ __forceinline__ uint32_t ctile_target(const Ctx& c, int ct) {
+  return (uint32_t)(min(kCombineT, c.T - ct * kCombineT) * c.k * c.nN2);
+}
+
+// Notify one event element; returns true if this notify completed it.
+__device__ __forceinline__ bool notify1(const Ctx& c, uint32_t* ev, uint32_t target) {
+  const uint32_t old = add_acqrel(ev, 1u);
+  if (old + 1u > target) or_relaxed(c.status, ST_OVER_NOTIFY | ST_ABORT);
+  return old + 1u == target;
+}
+
+// Reserve `n` queue slots (thread 0); returns the first, or -1 on overflow.
+__device__ __forceinline__ int64_t q_reserve(const MoeParams& p, const Ctx& c, int n) {
+  const uint32_t base = add_relaxed(c.set + W_TAIL, (uint32_t)n);
+  if ((int64_t)base + n > p.q_cap) {
+    or_relaxed(c.status, ST_QUEUE_OVERFLOW | ST_ABORT);
+    return -1;
+  }
+  return base;
+}
+
+template <int MODE>
+__device__ void after_router(const MoeParams& p, const Ctx& c, int tt) {
+  if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC) {
+    wg_publish();
+    if (threadIdx.x == 0) {
+      if (notify1(c, ev_logit(p, c) + tt, (uint32_t)c.nET) && MODE == MODE_DYNAMIC) {
+        const int64_t q = q_reserve(p, c, 1);
+        if (q >= 0) st_release64(c.queue + q, make_desc(TT_K, tt, 0));
+      }
+    }
+  }
+}
+
+template <int MODE>
+__device__ void after_topk(const MoeParams& p, const Ctx& c) {
+  if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC) {
+    wg_publish();
+    if (threadIdx.x == 0) {
+      if (notify1(c, c.set + W_EV_ROUTE, (uint32_t)c.nK) && MODE == MODE_DYNAMIC) {
+        const int64_t q = q_reserve(p, c, 1);
+        if (q >= 0) st_release64(c.queue + q, make_desc(TT_S, 0, 0));
+      }
+    }
+  }
+}
+
+template <int MODE>
+__device__ void after_scan(const MoeParams& p, const Ctx& c, Shared& sh) {
+  if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC) {
+    wg_publish();
+    if (MODE == MODE_DYNAMIC) {
+      if (threadIdx.x == 0) {
+        const uint32_t nrt = ld_relaxed(p.meta + M_NRT);
+        const uint32_t total = (uint32_t)(c.nR + c.nK + 1 + c.nD + c.nC) + nrt * (uint32_t)(c.nN1 + c.nN2);
+        st_release(c.set + W_TOTAL, total);
+        sh.base = (int)q_reserve(p, c, c.nD);
+      }
+      __syncthreads();
+      const int base = sh.base;
+      if (base >= 0)
+        for (int i = threadIdx.x; i < c.nD; i += kThreads)
+          st_release64(c.queue + base + i, make_desc(TT_D, i, 0));
+      __syncthreads();
+    } else {
+      if (threadIdx.x == 0) notify1(c, c.set + W_EV_SCAN, 1u);
+    }
+  }
+}
+
+template <int MODE>
+__device__ void after_dispatch(const MoeParams& p, const Ctx& c, int dt, Shared& sh) {
+  if (MODE != MODE_STATIC && MODE != MODE_DYNAMIC) return;
+  const int t0 = dt * kDispatchT;
+  const int rows = min(kDispatchT, c.T - t0) * c.k;
+  wg_publish();
+  if (threadIdx.x == 0) sh.n = 0;
+  __syncthreads();
+  if (threadIdx.x < rows) {
+    const int f = t0 * c.k + threadIdx.x;
+    const int e = p.ids[f];
+    const uint32_t target = (uint32_t)p.counts[e];
+    const bool done = notify1(c, ev_exp(p, c) + e, target);
+    if (p.debug) {
+      atomicAdd(p.debug + e, 1);
+      if (done) atomicAdd(p.debug + c.E + e, 1);
+    }
+    if (done && MODE == MODE_DYNAMIC) sh.list[atomicAdd(&sh.n, 1)] = e;
+  }
+  if (MODE == MODE_DYNAMIC) {
+    __syncthreads();
+    const int n = sh.n;
+    if (n == 0) return;
+    if (threadIdx.x == 0) {
+      int acc = 0;
+      for (int i = 0; i < n; ++i) {
+        sh.pref[i] = acc;
+        const int e = sh.list[i];
+        acc += (p.tile_indptr[e + 1] - p.tile_indptr[e]) * c.nN1;
+      }
+      sh.pref[n] = acc;
+      sh.total = acc;
+      sh.base = (int)q_reserve(p, c, acc);
+    }
+    __syncthreads();
+    const int base = sh.base, total = sh.total;
+    if (base >= 0) {
+      for (int i = threadIdx.x; i < total; i += kThreads) {
+        int j = 0;
+        while (i >= sh.pref[j + 1]) ++j;
+        const int li = i - sh.pref[j];
+        const int rt = p.tile_indptr[sh.list[j]] + li / c.nN1;
+        st_release64(c.queue + base + i, make_desc(TT_G1, rt, li % c.nN1));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int MODE>
+__device__ void after_g1(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
+  if (MODE != MODE_STATIC && MODE != MODE_DYNAMIC) return;
+  wg_publish();
+  if (threadIdx.x == 0) {
+    sh.base = -1;
+    if (notify1(c, ev_h(p, c) + rt, (uint32_t)c.nN1) && MODE == MODE_DYNAMIC)
+      sh.base = (int)q_reserve(p, c, c.nN2);
+  }
+  if (MODE == MODE_DYNAMIC) {
+    __syncthreads();
+    const int base = sh.base;
+    if (base >= 0)
+      for (int i = threadIdx.x; i < c.nN2; i += kThreads)
+        st_release64(c.queue + base + i, make_desc(TT_G2, rt, i));
+    __syncthreads();
+  }
+}
+
+template <int MODE>
+__device__ void after_g2(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
+  if (MODE != MODE_STATIC && MODE != MODE_DYNAMIC) return;
+  const RowTile tile = load_rowtile(p, rt);
+  wg_publish();
+  if (threadIdx.x == 0) sh.n = 0;
+  __syncthreads();
+  if (threadIdx.x < tile.nrows) {
+    const int f = p.perm[tile.r0 + threadIdx.x];
+    const int ct = (f / c.k) / kCombineT;
+    if (notify1(c, ev_c(p, c) + ct, ctile_target(c, ct)) && MODE == MODE_DYNAMIC)
+      sh.list[atomicAdd(&sh.n, 1)] = ct;
+  }
+  if (MODE == MODE_DYNAMIC) {
+    __syncthreads();
+    const int n = sh.n;
+    if (n == 0) return;
+    if (threadIdx.x == 0) sh.base = (int)q_reserve(p, c, n);
+    __syncthreads();
+    const int base = sh.base;
+    if (base >= 0 && threadIdx.x < n)
+      st_release64(c.queue + base + threadIdx.x, make_desc(TT_C, sh.list[threadIdx.x], 0));
+    __syncthreads();
+  }
+}
+
+// ==================================================== schedules ==========
+// Grid-wide barrier (BARRIER comparator only): arrival counter plus a
+// generation word; the last arrival resets the counter and bumps the
+// generation.  Bounded by the same spin budget as every other wait.
+__device__ bool grid_barrier(const Ctx& c) {
+  wg_publish();
+  int fail = 0;
+  if (threadIdx.x == 0) {
+    uint32_t* cnt = c.set + W_BAR_COUNT;
+    uint32_t* gen = c.set + W_BAR_GEN;
+    const uint32_t g0 = ld_relaxed(gen);
+    const uint32_t old = add_acqrel(cnt, 1u);
+    if (old == gridDim.x - 1u) {
+      st_relaxed(cnt, 0u);
+      add_acqrel(gen, 1u);
+    } else {
+      uint32_t spins = 0;
+      while (ld_relaxed(gen) == g0) {
+        if (ld_relaxed(c.status) & ST_ABORT) { fail = 1; break; }
+        if (++spins > c.budget) { or_relaxed(c.status, ST_TIMEOUT | ST_ABORT); fail = 1; break; }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  }
+  fail = __syncthreads_or(fail);
+  fence_acquire();
+  return fail == 0;
+}
+
+// STATIC / BARRIER: each phase's tasks are dealt round-robin over the
+// workgroups, continuing from where the previous phase stopped, and every
+// workgroup runs its list in phase order.  In STATIC a task waits only on
+// events produced by earlier phases, so with every workgroup resident no
+// wait can be circular and the schedule cannot deadlock.  Task counts of the
+// phases after S are read from S's output (data-dependent instantiation).
+template <int MODE>
+__device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh) {
+  const int G = gridDim.x, w = blockIdx.x;
+  float* red = reinterpret_cast<float*>(smem);
+  constexpr bool EV = (MODE == MODE_STATIC);
+  int64_t off = 0;
+  for (int i = first_of(w, off, G); i < c.nR; i += G) {
+    task_router(p, c, i / c.nET, i % c.nET);
+    dbg_task(p, TT_R);
+    after_router<MODE>(p, c, i / c.nET);
+  }
+  off += c.nR;
+  if (!EV && !grid_barrier(c)) return;
+  for (int i = first_of(w, off, G); i < c.nK; i += G) {
+    if (EV && !wg_wait(ev_logit(p, c) + i, (uint32_t)c.nET, c.status, c.budget)) return;
+    task_topk(p, c, i);
+    dbg_task(p, TT_K);
+    after_topk<MODE>(p, c);
+  }
+  off += c.nK;
+  if (!EV && !grid_barrier(c)) return;
+  if (first_of(w, off, G) == 0) {
+    if (EV && !wg_wait(c.set + W_EV_ROUTE, (uint32_t)c.nK, c.status, c.budget)) return;
+    task_scan(p, c, smem);
+    dbg_task(p, TT_S);
+    after_scan<MODE>(p, c, sh);
+  }
+  off += 1;
+  if (!EV && !grid_barrier(c)) return;
+  for (int i = first_of(w, off, G); i < c.nD; i += G) {
+    if (EV && !wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;
+    task_dispatch_copy(p, c, i);
+    dbg_task(p, TT_D);
+    after_dispatch<MODE>(p, c, i, sh);
+  }
+  off += c.nD;
+  if (EV) {
+    if (!wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;
+  } else if (!grid_barrier(c)) {
+    return;
+  }
+  const int nrt = (int)ld_relaxed(p.meta + M_NRT);
+  const int nG1 = nrt * c.nN1, nG2 = nrt * c.nN2;
+  for (int i = first_of(w, off, G); i < nG1; i += G) {
+    const int rt = i / c.nN1;
+    if (EV) {
+      const RowTile tile = load_rowtile(p, rt);
+      const uint32_t target = ld_relaxed(reinterpret_cast<const uint32_t*>(p.counts) + tile.e);
+      if (!wg_wait(ev_exp(p, c) + tile.e, target, c.status, c.budget)) return;
+    }
+    task_g1(p, c, rt, i % c.nN1, red);
+    dbg_task(p, TT_G1);
+    after_g1<MODE>(p, c, rt, sh);
+  }
+  off += nG1;
+  if (!EV && !grid_barrier(c)) return;
+  for (int i = first_of(w, off, G); i < nG2; i += G) {
+    const int rt = i / c.nN2;
+    if (EV && !wg_wait(ev_h(p, c) + rt, (uint32_t)c.nN1, c.status, c.budget)) return;
+    task_g2(p, c, rt, i % c.nN2, red);
+    dbg_task(p, TT_G2);
+    after_g2<MODE>(p, c, rt, sh);
+  }
+  off += nG2;
+  if (!EV && !grid_barrier(c)) return;
+  for (int i = first_of(w, off, G); i < c.nC; i += G) {
+    if (EV && !wg_wait(ev_c(p, c) + i, ctile_target(c, i), c.status, c.budget)) return;
+    task_combine(p, c, i);
+    dbg_task(p, TT_C);
+  }
+}
+
+// DYNAMIC: one HBM queue.  Index i < nR is the implicit router prefix (ready
+// at launch); every other index is a slot filled by the notify that released
+// the task (early push).  A workgroup pops by bumping the head, waits for its
+// slot, and exits once the total task count (known after S) is passed.  Tasks
+// never wait on events here: they are only pushed when ready.
+__device__ void run_dynamic(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh) {
+  float* red = reinterpret_cast<float*>(smem);
+  for (;;) {
+    if (threadIdx.x == 0) {
+      uint64_t d = kDescExit;
+      const uint32_t idx = add_relaxed(c.set + W_HEAD, 1u);
+      if ((int64_t)idx < c.nR) {
+        d = make_desc(TT_R, idx / c.nET, idx % c.nET);
+      } else {
+        const int64_t qi = (int64_t)idx - c.nR;
+        if (qi < p.q_cap) {
+          uint32_t spins = 0;
+          for (;;) {
+            const uint64_t v = ld_relaxed64(c.queue + qi);
+            if (v) { d = v; break; }
+            const uint32_t tot = ld_relaxed(c.set + W_TOTAL);
+            if (tot && idx >= tot) break;
+            if (ld_relaxed(c.status) & ST_ABORT) break;
+            if (++spins > c.budget) { or_relaxed(c.status, ST_TIMEOUT | ST_ABORT); break; }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+      }
+      sh.desc = d;
+    }
+    __syncthreads();
+    const uint64_t d = sh.desc;
+    fence_acquire();
+    __syncthreads();
+    if (d == kDescExit) return;
+    const int a = (int)desc_a(d), b = (int)desc_b(d);
+    switch (desc_type(d)) {
+      case TT_R:
+        task_router(p, c, a, b);
+        dbg_task(p, TT_R);
+        after_router<MODE_DYNAMIC>(p, c, a);
+        break;
+      case TT_K:
+        task_topk(p, c, a);
+        dbg_task(p, TT_K);
+        after_topk<MODE_DYNAMIC>(p, c);
+        break;
+      case TT_S:
+        task_scan(p, c, smem);
+        dbg_task(p, TT_S);
+        after_scan<MODE_DYNAMIC>(p, c, sh);
+        break;
+      case TT_D:
+        task_dispatch_copy(p, c, a);
+        dbg_task(p, TT_D);
+        after_dispatch<MODE_DYNAMIC>(p, c, a, sh);
+        break;
+      case TT_G1:
+        task_g1(p, c, a, b, red);
+        dbg_task(p, TT_G1);
+        after_g1<MODE_DYNAMIC>(p, c, a, sh);
+        break;
+      case TT_G2:
+        task_g2(p, c, a, b, red);
+        dbg_task(p, TT_G2);
+        after_g2<MODE_DYNAMIC>(p, c, a, sh);
+        break;
+      case TT_C:
+        task_combine(p, c, a);
+        dbg_task(p, TT_C);
+        break;
+      default:
+        or_relaxed(c.status, ST_QUEUE_OVERFLOW | ST_ABORT);
+        return;
+    }
+  }
+}
+
+// The persistent megakernel.  Counter sets are double buffered by the
+// parity of a device-side epoch: this launch works in set[epoch & 1] (zeroed
+// by the previous launch) and zeroes set[1 - (epoch & 1)] for the next one;
+// the last workgroup to finish advances the epoch.  No host memset, no host
+// state: the workspace is self-resetting, also after an aborted launch.
+template <int MODE>
+__global__ void __launch_bounds__(kThreads) moe_persistent(MoeParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ Shared sh;
+  __shared__ uint32_t s_epoch;
+  if (threadIdx.x == 0) s_epoch = ld_relaxed(p.ctrl + C_EPOCH);
+  __syncthreads();
+  const uint32_t epoch = s_epoch;
+  uint32_t* set = (epoch & 1u) ? p.set1 : p.set0;
+  uint32_t* other = (epoch & 1u) ? p.set0 : p.set1;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < p.set_words;
+       i += (int64_t)gridDim.x * kThreads)
+    other[i] = 0u;
+  const Ctx c = make_ctx(p, set);
+  if (MODE == MODE_DYNAMIC)
+    run_dynamic(p, c, smem, sh);
+  else
+    run_lists<MODE>(p, c, smem, sh);
+  wg_publish();
+  if (threadIdx.x == 0) {
+    const uint32_t st = ld_relaxed(c.status) & ~ST_ABORT;
+    if (st) or_relaxed(p.ctrl + C_REPORT, st);
+    const uint32_t old = add_acqrel(set + W_DONE, 1u);
+    if (old == gridDim.x - 1u) st_release(p.ctrl + C_EPOCH, epoch + 1u);
+  }
+}
+
+// ------------------------------------------- kernel-by-kernel comparator --
+__global__ void __launch_bounds__(kThreads) kbk_router(MoeParams p) {
+  const Ctx c = make_ctx(p, nullptr);
+  task_router(p, c, blockIdx.x / c.nET, blockIdx.x % c.nET);
+}
+__global__ void __launch_bounds__(kThreads) kbk_topk(MoeParams p) {
+  const Ctx c = make_ctx(p, nullptr);
+  task_topk(p, c, blockIdx.x);
+}
+__global__ void __launch_bounds__(kThreads) kbk_scan(MoeParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const Ctx c = make_ctx(p, nullptr);
+  task_scan(p, c, smem);
+}
+__global__ void __launch_bounds__(kThreads) kbk_dispatch(MoeParams p) {
+  const Ctx c = make_ctx(p, nullptr);
+  task_dispatch_copy(p, c, blockIdx.x);
+}
+__global__ void __launch_bounds__(kThreads) kbk_g1(MoeParams p) {
+  __shared__ float red[4 * 2 * 256];
+  const Ctx c = make_ctx(p, nullptr);
+  const int nrt = (int)ld_relaxed(p.meta + M_NRT);
+  if ((int)blockIdx.x >= nrt * c.nN1) return;
+  task_g1(p, c, blockIdx.x / c.nN1, blockIdx.x % c.nN1, red);
+}
+__global__ void __launch_bounds__(kThreads) kbk_g2(MoeParams p) {
+  __shared__ float red[4 * 4 * 256];
+  const Ctx c = make_ctx(p, nullptr);
+  const int nrt = (int)ld_relaxed(p.meta + M_NRT);
+  if ((int)blockIdx.x >= nrt * c.nN2) return;
+  task_g2(p, c, blockIdx.x / c.nN2, blockIdx.x % c.nN2, red);
+}
+__global__ void __launch_bounds__(kThreads) kbk_combine(MoeParams p) {
+  const Ctx c = make_ctx(p, nullptr);
+  task_combine(p, c, blockIdx.x);
+}
+
+// ------------------------------------------------------- host launchers --
+int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (sched) {
+    case ETC_SCHED_STATIC:
+      hipLaunchKernelGGL((moe_persistent<MODE_STATIC>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+      break;
+    case ETC_SCHED_DYNAMIC:
+      hipLaunchKernelGGL((moe_persistent<MODE_DYNAMIC>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+      break;
+    case ETC_SCHED_BARRIER:
+      hipLaunchKernelGGL((moe_persistent<MODE_BARRIER>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+      break;
+    default:
+      return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu) {
+  hipError_t e;
+  switch (sched) {
+    case ETC_SCHED_STATIC:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_STATIC>, kThreads, lds_bytes);
+      break;
+    case ETC_SCHED_DYNAMIC:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_DYNAMIC>, kThreads, lds_bytes);
+      break;
+    case ETC_SCHED_BARRIER:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_BARRIER>, kThreads, lds_bytes);
+      break;
+    default:
+      return (int)hipErrorInvalidValue;
+  }
+  return (int)e;
+}
+
+int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int nTT = (p.T + kRouterT - 1) / kRouterT;
+  const int nET = (p.E + kRouterE - 1) / kRouterE;
+  const int nD = (p.T + kDispatchT - 1) / kDispatchT;
+  const int nC = (p.T + kCombineT - 1) / kCombineT;
+  const int64_t rows = (int64_t)p.T * p.k;
+  const int64_t max_rt = (rows + kBM - 1) / kBM + (rows < p.E ? rows : p.E);
+  const int nN1 = p.I / kBN1, nN2 = p.H / kBN2;
+  hipLaunchKernelGGL(kbk_router, dim3(nTT * nET), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(kbk_topk, dim3(nTT), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(kbk_scan, dim3(1), dim3(kThreads), lds_bytes, s, p);
+  hipLaunchKernelGGL(kbk_dispatch, dim3(nD), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(kbk_g1, dim3((unsigned)(max_rt * nN1)), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(kbk_g2, dim3((unsigned)(max_rt * nN2)), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(kbk_combine, dim3(nC), dim3(kThreads), 0, s, p);
+  return (int)hipGetLastError();
+}
+
+}  // namespace etc

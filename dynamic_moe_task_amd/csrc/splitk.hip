@@ -1,0 +1,184 @@
+// The split-K row-sum example through the device event runtime (Event
+// Tensor, arXiv 2604.13327, Fig. 3; podcast cue 3):
+//   partial_sum(i, j): B[i, j] = sum of A[i, j*bk .. (j+1)*bk), then notify
+//                      event i                                 (edge "ij->i")
+//   final_sum(i)     : wait on event i (wait_count = nsplit),  (edge "i->i")
+//                      C[i] = sum_j B[i, j]
+// Row i's final sum starts as soon as its own partial sums land, whatever the
+// other rows are doing.
+//
+// Counters: final_sum(i) is the only waiter of event i, so after its wait it
+// returns the counter to zero; the control words (queue head / tail, done
+// count) are returned to zero by the last workgroup to finish; each queue
+// slot is cleared by the workgroup that pops it.  The next launch therefore
+// finds everything at rest without a host-side memset.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "etc_internal.h"
+#include "etc_rt.h"
+
+namespace etc {
+
+enum : int { SK_STATUS = 0, SK_HEAD = 1, SK_TAIL = 2, SK_DONE = 3, SK_REPORT = 4, SK_WORDS = 16 };
+constexpr int SK_PARTIAL = 1, SK_FINAL = 2;
+constexpr uint64_t SK_EXIT = ~0ull;
+
+struct SkParams {
+  const int32_t* A;
+  int32_t* B;
+  int32_t* C;
+  uint32_t* ev;
+  uint32_t* ctl;
+  uint64_t* queue;
+  int64_t q_cap;
+  int n, nsplit, bk;
+  uint32_t budget;
+};
+
+__device__ int block_sum_i32(int v, int* tmp) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
+  if (lane == 0) tmp[wv] = v;
+  __syncthreads();
+  const int r = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  __syncthreads();
+  return r;
+}
+
+__device__ void sk_partial(const SkParams& p, int i, int j, int* tmp) {
+  const int32_t* row = p.A + ((size_t)i * p.nsplit + j) * p.bk;
+  int v = 0;
+  for (int c = threadIdx.x; c < p.bk; c += kThreads) v += row[c];
+  v = block_sum_i32(v, tmp);
+  if (threadIdx.x == 0) p.B[(size_t)i * p.nsplit + j] = v;
+}
+
+__device__ void sk_final(const SkParams& p, int i, int* tmp) {
+  int v = 0;
+  for (int j = threadIdx.x; j < p.nsplit; j += kThreads) v += p.B[(size_t)i * p.nsplit + j];
+  v = block_sum_i32(v, tmp);
+  if (threadIdx.x == 0) p.C[i] = v;
+}
+
+// notify event i; true if this notify released it
+__device__ __forceinline__ bool sk_notify(const SkParams& p, int i) {
+  const uint32_t old = add_acqrel(p.ev + i, 1u);
+  if (old + 1u > (uint32_t)p.nsplit) or_relaxed(p.ctl + SK_STATUS, ST_OVER_NOTIFY | ST_ABORT);
+  return old + 1u == (uint32_t)p.nsplit;
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
+  __shared__ int tmp[8];
+  __shared__ uint64_t s_desc;
+  const int G = gridDim.x, w = blockIdx.x;
+  const int nP = p.n * p.nsplit;
+  uint32_t* status = p.ctl + SK_STATUS;
+  if (MODE == ETC_SCHED_STATIC) {
+    // phase-ordered lists: all partial sums, then all final sums
+    for (int t = w; t < nP; t += G) {
+      sk_partial(p, t / p.nsplit, t % p.nsplit, tmp);
+      wg_publish();
+      if (threadIdx.x == 0) sk_notify(p, t / p.nsplit);
+    }
+    for (int i = (w - nP % G + G) % G; i < p.n; i += G) {
+      if (!wg_wait(p.ev + i, (uint32_t)p.nsplit, status, p.budget)) break;
+      if (threadIdx.x == 0) st_relaxed(p.ev + i, 0u);  // sole waiter: back to rest
+      sk_final(p, i, tmp);
+    }
+  } else {
+    // push / pop: the partial sums are the implicit ready prefix; the notify
+    // that completes event i pushes final_sum(i) at once
+    const uint32_t total = (uint32_t)(nP + p.n);
+    for (;;) {
+      if (threadIdx.x == 0) {
+        uint64_t d = SK_EXIT;
+        const uint32_t idx = add_relaxed(p.ctl + SK_HEAD, 1u);
+        if ((int)idx < nP) {
+          d = ((uint64_t)SK_PARTIAL << 60) | idx;
+        } else if (idx < total) {
+          const int64_t qi = (int64_t)idx - nP;
+          uint32_t spins = 0;
+          for (;;) {
+            const uint64_t v = ld_relaxed64(p.queue + qi);
+            if (v) {
+              d = v;
+              __hip_atomic_store(p.queue + qi, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+            if (ld_relaxed(status) & ST_ABORT) break;
+            if (++spins > p.budget) { or_relaxed(status, ST_TIMEOUT | ST_ABORT); break; }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+        s_desc = d;
+      }
+      __syncthreads();
+      const uint64_t d = s_desc;
+      fence_acquire();
+      __syncthreads();
+      if (d == SK_EXIT) break;
+      const int type = (int)(d >> 60);
+      const int a = (int)(d & 0x0fffffffffffffffull);
+      if (type == SK_PARTIAL) {
+        sk_partial(p, a / p.nsplit, a % p.nsplit, tmp);
+        wg_publish();
+        if (threadIdx.x == 0 && sk_notify(p, a / p.nsplit)) {
+          const uint32_t q = add_relaxed(p.ctl + SK_TAIL, 1u);
+          if ((int64_t)q < p.q_cap)
+            st_release64(p.queue + q, ((uint64_t)SK_FINAL << 60) | (uint64_t)(a / p.nsplit));
+          else
+            or_relaxed(status, ST_QUEUE_OVERFLOW | ST_ABORT);
+        }
+      } else {
+        if (threadIdx.x == 0) st_relaxed(p.ev + a, 0u);
+        sk_final(p, a, tmp);
+      }
+    }
+  }
+  wg_publish();
+  if (threadIdx.x == 0) {
+    const uint32_t old = add_acqrel(p.ctl + SK_DONE, 1u);
+    if (old == (uint32_t)G - 1u) {
+      const uint32_t st = ld_relaxed(status) & ~ST_ABORT;
+      if (st) or_relaxed(p.ctl + SK_REPORT, st);
+      st_relaxed(status, 0u);
+      st_relaxed(p.ctl + SK_HEAD, 0u);
+      st_relaxed(p.ctl + SK_TAIL, 0u);
+      st_relaxed(p.ctl + SK_DONE, 0u);
+    }
+  }
+}
+
+int launch_splitk(int n, int nsplit, int bk, const int32_t* A, int32_t* B, int32_t* C, int32_t* ev,
+                  uint32_t* ctl, uint64_t* queue, int64_t q_cap, int sched, int grid, uint32_t budget,
+                  void* stream) {
+  SkParams p;
+  p.A = A; p.B = B; p.C = C;
+  p.ev = reinterpret_cast<uint32_t*>(ev);
+  p.ctl = ctl;
+  p.queue = queue;
+  p.q_cap = q_cap;
+  p.n = n; p.nsplit = nsplit; p.bk = bk;
+  p.budget = budget;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (sched == ETC_SCHED_STATIC)
+    hipLaunchKernelGGL((splitk_persistent<ETC_SCHED_STATIC>), dim3(grid), dim3(kThreads), 0, s, p);
+  else if (sched == ETC_SCHED_DYNAMIC)
+    hipLaunchKernelGGL((splitk_persistent<ETC_SCHED_DYNAMIC>), dim3(grid), dim3(kThreads), 0, s, p);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int splitk_occupancy(int sched, int* blocks_per_cu) {
+  if (sched == ETC_SCHED_STATIC)
+    return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks_per_cu, splitk_persistent<ETC_SCHED_STATIC>, kThreads, 0);
+  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      blocks_per_cu, splitk_persistent<ETC_SCHED_DYNAMIC>, kThreads, 0);
+}
+
+}  // namespace etc

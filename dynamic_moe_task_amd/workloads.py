@@ -4,21 +4,24 @@ Shapes follow a Qwen3-30B-A3B-shaped MoE layer (hidden 2048, 128 experts,
 top-8, expert intermediate 768, SwiGLU) plus a tiny variant.  No trained
 weights or datasets are used: every tensor is drawn here.
 
-Recipe (one ``numpy.random.default_rng(seed)`` stream, draws in this order):
-  1. router weight Wr [E, H]          ~ N(0, 0.02)
-  2. W13 [E, 2I, H] (gate rows 0..I-1, up rows I..2I-1), expert by expert,
-     ~ N(0, 0.02)
-  3. Wd [E, H, I], expert by expert,   ~ N(0, 0.02)
-  4. activations X [T, H]             ~ N(0, 1)
-  5. (Zipf-biased prefill only) a rank permutation r = 1 + permutation(E);
-     the per-expert logit offset is b_e = -s * ln(r_e) with s = 1.1, i.e.
-     the log of a Zipf(s) pmf up to its normaliser.
+Recipe.  Every tensor (and every expert slice of the expert weights) has its
+own counter-seeded stream ``numpy.random.default_rng((seed, tag, ...))``, so
+slices can be drawn in parallel and any one of them regenerated alone:
+  router weight Wr [E, H]           tag 0          ~ N(0, 0.02)
+  W13[e] [2I, H] (gate rows 0..I-1,
+          up rows I..2I-1)          tag (1, e)     ~ N(0, 0.02)
+  Wd[e] [H, I]                      tag (2, e)     ~ N(0, 0.02)
+  activations X [T, H]              tag 3          ~ N(0, 1)
+  (Zipf-biased prefill only) rank permutation r = 1 + permutation(E),
+                                    tag 4; the per-expert logit offset is
+     b_e = -s * ln(r_e) with s = 1.1, i.e. the log of a Zipf(s) pmf up to its
+     normaliser, so a few experts draw most tokens and some draw none.
 Normals are drawn as float32 and rounded to bf16 (round to nearest, ties to
 even); bf16 tensors are held as their uint16 bit patterns.
 
 The batch-size sweep draws B ~ U{1..512} for 200 steps from
-``default_rng((seed, 1))`` and the step-s activations from
-``default_rng((seed, 2, s))``.
+``default_rng((seed, 5))`` and the step-s activations from
+``default_rng((seed, 6, s))``.
 """
 from __future__ import annotations
 
@@ -64,40 +67,50 @@ class MoEWeights:
     Wr: np.ndarray      # [E, H] bf16 bits
     W13: np.ndarray     # [E, 2I, H]
     Wd: np.ndarray      # [E, H, I]
-    bias: Optional[np.ndarray]  # [E] float32 or None
-    rng: np.random.Generator    # the stream, positioned after the weights
+    bias: Optional[np.ndarray] = None  # [E] float32 or None
+    seed: int = 0
 
 
-def make_weights(shape: MoEShape, seed: int = 0, w_std: float = 0.02) -> MoEWeights:
-    rng = np.random.default_rng(seed)
+def make_weights(shape: MoEShape, seed: int = 0, w_std: float = 0.02, threads: int = 8) -> MoEWeights:
+    from concurrent.futures import ThreadPoolExecutor
     E, H, I = shape.E, shape.H, shape.I
-    Wr = _normal_bf16(rng, (E, H), w_std)
+    Wr = _normal_bf16(np.random.default_rng((seed, 0)), (E, H), w_std)
     W13 = np.empty((E, 2 * I, H), np.uint16)
-    for e in range(E):
-        W13[e] = _normal_bf16(rng, (2 * I, H), w_std)
     Wd = np.empty((E, H, I), np.uint16)
-    for e in range(E):
-        Wd[e] = _normal_bf16(rng, (H, I), w_std)
-    return MoEWeights(Wr, W13, Wd, None, rng)
+
+    def fill(e):
+        W13[e] = _normal_bf16(np.random.default_rng((seed, 1, e)), (2 * I, H), w_std)
+        Wd[e] = _normal_bf16(np.random.default_rng((seed, 2, e)), (H, I), w_std)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(fill, range(E)))
+    return MoEWeights(Wr, W13, Wd, None, seed)
+
+
+def make_tokens(shape: MoEShape, T: int, seed: int = 0) -> np.ndarray:
+    return _normal_bf16(np.random.default_rng((seed, 3)), (T, shape.H), 1.0)
+
+
+def zipf_bias(shape: MoEShape, seed: int = 0) -> Optional[np.ndarray]:
+    if shape.zipf_s is None:
+        return None
+    ranks = 1 + np.random.default_rng((seed, 4)).permutation(shape.E)
+    return (-shape.zipf_s * np.log(ranks.astype(np.float64))).astype(np.float32)
 
 
 def make_layer(shape: MoEShape, seed: int = 0):
-    """Weights, activations X [T, H] and the optional Zipf bias, in the
-    documented draw order."""
+    """Weights (with the Zipf bias when the shape has one) and X [T, H]."""
     w = make_weights(shape, seed)
-    X = _normal_bf16(w.rng, (shape.T, shape.H), 1.0)
-    if shape.zipf_s is not None:
-        ranks = 1 + w.rng.permutation(shape.E)
-        w.bias = (-shape.zipf_s * np.log(ranks.astype(np.float64))).astype(np.float32)
-    return w, X
+    w.bias = zipf_bias(shape, seed)
+    return w, make_tokens(shape, shape.T, seed)
 
 
 def sweep_batches(seed: int = 0, steps: int = 200, bmax: int = 512) -> np.ndarray:
-    return np.random.default_rng((seed, 1)).integers(1, bmax + 1, size=steps)
+    return np.random.default_rng((seed, 5)).integers(1, bmax + 1, size=steps)
 
 
 def sweep_tokens(shape: MoEShape, step: int, B: int, seed: int = 0) -> np.ndarray:
-    return _normal_bf16(np.random.default_rng((seed, 2, step)), (B, shape.H), 1.0)
+    return _normal_bf16(np.random.default_rng((seed, 6, step)), (B, shape.H), 1.0)
 
 
 def algorithmic_bytes(shape: MoEShape, T: int, n_active: int) -> int:

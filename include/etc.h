@@ -1,0 +1,237 @@
+/*
+ * etc.h -- C ABI of the MI355X event-tensor MoE megakernel library (libetc.so).
+ *
+ * One Mixture-of-Experts layer runs as ONE persistent HIP kernel that executes
+ * a graph of tiled tasks coordinated through event tensors in HBM:
+ *
+ *   R(t-tile, e-tile) router logits  --ev_logit-->  K(t-tile) top-k + weights
+ *   --ev_route--> S scan: counts, exp_indptr, permutation, per-expert event
+ *   initialisation --ev_scan--> D(t-tile) dispatch rows, notify ev_exp[e]
+ *   --ev_exp[e]--> G1(row tile, n-tile) gate/up + SwiGLU --ev_h[row tile]-->
+ *   G2(row tile, n-tile) down projection --ev_c[t-tile]--> C(t-tile) combine.
+ *
+ * Sources (page title, then figure / table / transcript cue):
+ *   "Event Tensor: A Unified Abstraction for Compiling Dynamic Megakernel"
+ *   (arXiv 2604.13327): Fig. 2 (event tensor, runtime topk / exp_indptr),
+ *   Fig. 3 (split-K example), Fig. 4 (symbolic shapes instantiated at run
+ *   time), Fig. 5b (data-dependent MoE graph), Figs. 6-7 (static schedule,
+ *   notify/wait), Figs. 8-9 (dynamic schedule, push/pop), Fig. 10 (no task
+ *   graph materialised at run time), Table 2 (static vs dynamic on the MoE
+ *   layer).  The podcast episode on the paper, cues 3, 5, 7, 9, 11 and 13,
+ *   restates those mechanisms in prose.
+ *
+ * Conventions for every entry point:
+ *   - All tensor arguments are caller-owned DEVICE pointers (HBM), except
+ *     where a parameter says "host".  The library keeps no reference to them
+ *     after the call returns (launches are asynchronous: the memory must stay
+ *     valid until the stream reaches the launch).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Return value: ETC_OK (0) or a negative ETC_ERR_* code.  Nothing throws
+ *     across the ABI.  etc_last_error() gives a thread-local message.
+ *   - bf16 tensors are raw IEEE bfloat16 bit patterns, row-major, 16-byte
+ *     aligned base pointers.
+ */
+#ifndef ETC_H
+#define ETC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- codes -- */
+enum {
+  ETC_OK = 0,
+  ETC_ERR_INVALID = -1,     /* bad size, pointer, alignment, enum or state   */
+  ETC_ERR_UNSUPPORTED = -2, /* valid request this build does not implement   */
+  ETC_ERR_HIP = -3,         /* a HIP runtime call failed                     */
+  ETC_ERR_TIMEOUT = -4,     /* a bounded in-kernel wait ran out (watchdog)   */
+  ETC_ERR_INVARIANT = -5,   /* an event was notified beyond its wait_count,
+                               or a queue overflowed                          */
+  ETC_ERR_NONFINITE = -6    /* a router logit was NaN                        */
+};
+
+/* Scheduling of the persistent kernel.
+ *   STATIC : per-workgroup task lists fixed in closed form before any task
+ *            runs (phase ordered), every dependency a notify / wait on an
+ *            event counter [Figs. 6-7; podcast cue 11].
+ *   DYNAMIC: a notify that completes an event pushes the released tasks at
+ *            once onto one HBM queue; idle workgroups pop [Figs. 8-9].
+ *   KBK    : comparator, one kernel launch per task type (kernel-by-kernel
+ *            model of Fig. 1), same device task code.
+ *   BARRIER: comparator, the persistent kernel with a grid-wide barrier
+ *            between task types instead of fine-grained events (the
+ *            "unfused megakernel" reading of Table 2).                       */
+enum { ETC_SCHED_STATIC = 0, ETC_SCHED_DYNAMIC = 1, ETC_SCHED_KBK = 2, ETC_SCHED_BARRIER = 3 };
+
+/* ------------------------------------------------------- event tensors -- */
+/* An event tensor [Fig. 2; podcast cue 3]: a tensor of dependency counters,
+ * one per element, each released after `wait_count` notifies.  A dimension
+ * may be symbolic (ETC_DIM_SYMBOLIC): the tensor is then a template bound to
+ * a concrete shape at run time by etensor_instantiate, with nothing
+ * recompiled and nothing captured [Fig. 4; podcast cue 5].  The wait count
+ * may be data dependent (ETC_WAIT_DATA_DEPENDENT): it is then written at run
+ * time by the task that computes it [Fig. 5b; podcast cue 7].               */
+#define ETC_DIM_SYMBOLIC (-1)
+#define ETC_WAIT_DATA_DEPENDENT (-1)
+#define ETC_MAX_DIMS 8
+
+typedef struct etc_etensor etc_etensor;
+
+/* Declare an event tensor.  ndim in [1, ETC_MAX_DIMS]; shape (host array)
+ * holds positive sizes or ETC_DIM_SYMBOLIC; wait_count >= 0 or
+ * ETC_WAIT_DATA_DEPENDENT.  dev_counters: caller-owned device array of
+ * int32 counters with room for every instantiation the caller will use (it
+ * must start zeroed), or NULL to let the library allocate on first launch.
+ * The handle is library-owned until etensor_destroy.  Makes no HIP call.
+ * Errors: ETC_ERR_INVALID for a bad ndim, size or wait_count.               */
+int etensor_create(etc_etensor** out, int ndim, const int64_t* shape, int32_t wait_count,
+                   int32_t* dev_counters);
+
+/* Bind every dimension: concrete_shape (host, ndim entries) must match the
+ * fixed dimensions and give a positive size for each symbolic one.  May be
+ * called again with another shape (a new instantiation of the same
+ * template).  Makes no HIP call.  Errors: ETC_ERR_INVALID.                  */
+int etensor_instantiate(etc_etensor* et, const int64_t* concrete_shape);
+
+/* Current shape (host out-array of ETC_MAX_DIMS; symbolic dimensions read
+ * ETC_DIM_SYMBOLIC before instantiation), ndim and element count (0 when not
+ * instantiated).  Errors: ETC_ERR_INVALID for NULL arguments.               */
+int etensor_shape(const etc_etensor* et, int64_t* shape_out, int* ndim_out, int64_t* numel_out);
+
+/* Release the handle and any counters the library allocated for it.        */
+int etensor_destroy(etc_etensor* et);
+
+/* The split-K row-sum example of Fig. 3 (podcast cue 3), run through the
+ * same device runtime as the MoE layer: partial_sum(i, j) writes
+ * B[i, j] = sum of A[i, j*bk .. (j+1)*bk) and notifies event i (edge
+ * "ij->i"); final_sum(i) waits on event i (edge "i->i") and writes
+ * C[i] = sum_j B[i, j].  `ev` must be instantiated to shape [n] with
+ * wait_count == nsplit.  A is [n, nsplit*bk] int32, B [n, nsplit], C [n]
+ * (device).  sched: ETC_SCHED_STATIC or ETC_SCHED_DYNAMIC.  Asynchronous;
+ * errors found in the kernel are reported by etc_sync.
+ * Errors: ETC_ERR_INVALID (shape / wait_count mismatch, bad sizes),
+ * ETC_ERR_UNSUPPORTED (sched), ETC_ERR_HIP.                                  */
+int etc_splitk_launch(etc_etensor* ev, int32_t n, int32_t nsplit, int32_t bk, const int32_t* A,
+                      int32_t* B, int32_t* C, int sched, void* stream);
+
+/* ------------------------------------------------------------ MoE layer -- */
+/* Layer shape.  Router: logits = x @ w_router^T (+ b_router), top-k over E,
+ * weights = softmax renormalised over the chosen k (norm_topk = 1) or the
+ * plain softmax value (norm_topk = 0).  Experts: SwiGLU,
+ * y = (silu(x Wg^T) * (x Wu^T)) Wd^T with Wg = w13[e, 0:I, :],
+ * Wu = w13[e, I:2I, :], Wd = w2[e].  Output: sum_j topk_w[t, j] * y_j.
+ * Limits: H and I multiples of 128 and <= 16384; 1 <= E <= 256;
+ * 1 <= k <= min(E, 16); 1 <= T_max <= 4096 and E * ceil(T_max/32) <= 8192. */
+typedef struct {
+  int32_t T_max;     /* largest token count any launch will use            */
+  int32_t H;         /* hidden size                                        */
+  int32_t E;         /* number of experts                                  */
+  int32_t k;         /* experts per token                                  */
+  int32_t I;         /* expert intermediate size                           */
+  int32_t norm_topk; /* 1: renormalise the k weights to sum to 1           */
+  int32_t has_bias;  /* 1: b_router is read and added to the logits        */
+} etc_moe_desc;
+
+/* Device pointers of one launch.  Layouts (row-major):
+ *   x        [T, H]      bf16   input tokens
+ *   w_router [E, H]      bf16
+ *   b_router [E]         fp32   (read only when has_bias)
+ *   w13      [E, 2I, H]  bf16   rows 0..I-1 gate, rows I..2I-1 up
+ *   w2       [E, H, I]   bf16   down projection
+ *   out      [T, H]      bf16   layer output (written)
+ *   topk_ids [T, k] int32, topk_w [T, k] fp32: routing, by descending logit,
+ *            ties to the lower expert index (written)
+ *   counts   [E] int32: tokens routed to each expert (written)
+ *   exp_indptr [E+1] int32: exclusive prefix sum of counts, ends at T*k
+ *   perm     [T*k] int32: perm[s] = flat index t*k+j held by grouped row s;
+ *            rows of one expert keep ascending t (stable)      (written)
+ *   slot     [T*k] int32: inverse of perm                      (written)
+ *   workspace: moe_layer_workspace_size(desc) bytes, prepared once by
+ *            moe_workspace_init; one workspace serves one launch at a time
+ *            (launches that overlap on one workspace race).
+ *   debug    NULL, or ETC_DEBUG_WORDS(E) int32 zeroed by the caller; the
+ *            kernel adds per-event notify and fire counts (layout below).
+ *   watchdog_spins: 0 = default; else the spin budget of every in-kernel
+ *            wait before it reports ETC_ERR_TIMEOUT and the grid drains.    */
+typedef struct {
+  const void* x;
+  const void* w_router;
+  const float* b_router;
+  const void* w13;
+  const void* w2;
+  void* out;
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* exp_indptr;
+  int32_t* perm;
+  int32_t* slot;
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t* debug;
+  uint32_t watchdog_spins;
+} etc_moe_args;
+
+/* Debug counters (int32), when etc_moe_args.debug is non-NULL:
+ *   [0, E)        notifies received by ev_exp[e]   (expected: counts[e])
+ *   [E, 2E)       times ev_exp[e] was completed    (expected: 1 if counts[e] > 0)
+ *   [2E + i]      tasks executed of type i, i = 0..7 in the order
+ *                 R, K, S, D, G1, G2, C, (unused)                           */
+#define ETC_DEBUG_WORDS(E) (2 * (E) + 8)
+
+/* Tile geometry and task counts of this build, for tests and benchmarks.   */
+typedef struct {
+  int32_t bm;          /* rows per grouped-GEMM row tile                    */
+  int32_t bn1;         /* gate (and up) columns per G1 tile                 */
+  int32_t bn2;         /* output columns per G2 tile                        */
+  int32_t router_tokens, router_experts; /* R tile                          */
+  int32_t dispatch_tokens, combine_tokens;
+  int32_t grid;        /* persistent workgroups (0 before the first query)  */
+  int32_t threads;     /* threads per workgroup                             */
+  int32_t lds_bytes;   /* dynamic LDS per workgroup                         */
+} etc_moe_info;
+
+/* Fill `info` for `desc` (host struct).  Queries the device for the grid.
+ * Errors: ETC_ERR_INVALID (desc), ETC_ERR_HIP.                               */
+int moe_layer_info(const etc_moe_desc* desc, etc_moe_info* info);
+
+/* Bytes of workspace a launch with this descriptor needs (0 if the
+ * descriptor is invalid).  Makes no HIP call.                               */
+size_t moe_layer_workspace_size(const etc_moe_desc* desc);
+
+/* Zero the workspace's control block (once after allocation, and after an
+ * ETC_ERR_TIMEOUT if the caller wants a clean slate).  Asynchronous on
+ * `stream`.  Errors: ETC_ERR_INVALID, ETC_ERR_HIP.                           */
+int moe_workspace_init(const etc_moe_desc* desc, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Asynchronous launch of one MoE layer for T tokens, 1 <= T <= desc->T_max.
+ * T is a kernel argument: every event-tensor shape and task count is derived
+ * from it inside the kernel, so one compiled kernel serves every batch size
+ * with no recompile and no graph capture [Fig. 4].  Per-expert event counters
+ * are set from the routed counts at run time and release each expert's
+ * grouped-GEMM tiles over [exp_indptr[e], exp_indptr[e+1]) [Fig. 5b; podcast
+ * cues 7 and 9].  Allocates nothing, compiles nothing.
+ * Errors (returned before any launch): ETC_ERR_INVALID (descriptor limits, T
+ * range, NULL or misaligned pointer, small workspace, bad sched),
+ * ETC_ERR_HIP.  Errors inside the kernel are reported by etc_sync.           */
+int moe_layer_launch(const etc_moe_desc* desc, int32_t T, const etc_moe_args* args, int sched,
+                     void* stream);
+
+/* Wait for `stream`, then report the first in-kernel error of every launch
+ * made on it since the previous etc_sync (and clear it): ETC_OK,
+ * ETC_ERR_TIMEOUT, ETC_ERR_INVARIANT, ETC_ERR_NONFINITE or ETC_ERR_HIP.
+ * (Named etc_sync rather than sync so as not to shadow POSIX sync(2).)      */
+int etc_sync(void* stream);
+
+/* Thread-local description of the last error on this thread ("" if none).
+ * The string is library-owned and valid until the next call on the thread.  */
+const char* etc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ETC_H */
