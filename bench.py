@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill_zipf", "tiny"])
-    ap.add_argument("--sched", default="static", choices=["static", "dynamic", "barrier", "kbk"])
+    ap.add_argument("--sched", default="static", choices=["static", "barrier", "kbk"])
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated over steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -142,7 +142,7 @@ def main():
     alg_bytes = wl.algorithmic_bytes(shape, T, n_act)
     alg_flops = wl.algorithmic_flops(shape, T)
 
-    scheds = [a.sched] if a.only_sched else ["static", "dynamic", "barrier", "kbk"]
+    scheds = [a.sched] if a.only_sched else ["static", "barrier", "kbk"]
     us = {}
     for s in scheds:
         steps = a.steps if s == a.sched else max(10, a.steps // 2)

@@ -60,7 +60,7 @@ class MoeArgs(ctypes.Structure):
                 ("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("counts", ctypes.c_void_p),
                 ("exp_indptr", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("slot", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("debug", ctypes.c_void_p), ("watchdog_spins", ctypes.c_uint32)]
+                ("debug", ctypes.c_void_p), ("watchdog_us", ctypes.c_uint32)]
 
 
 class MoeInfo(ctypes.Structure):
@@ -214,7 +214,7 @@ class MoELayerBuffers:
         check(moe_workspace_init(desc, bufs.workspace.data_ptr(), ws_bytes, stream))
         return bufs
 
-    def args(self, x=None, w13=None, w2=None, watchdog_spins: int = 0) -> MoeArgs:
+    def args(self, x=None, w13=None, w2=None, watchdog_us: int = 0) -> MoeArgs:
         x = self.x if x is None else x
         w13 = self.w13 if w13 is None else w13
         w2 = self.w2 if w2 is None else w2
@@ -225,7 +225,7 @@ class MoELayerBuffers:
             self.topk_w.data_ptr(), self.counts.data_ptr(), self.exp_indptr.data_ptr(),
             self.perm.data_ptr(), self.slot.data_ptr(), self.workspace.data_ptr(),
             self.workspace.numel(), self.debug.data_ptr() if self.debug is not None else None,
-            watchdog_spins)
+            watchdog_us)
 
     def launch(self, T: int, sched="static", stream=None, **kw) -> None:
         import torch

@@ -51,16 +51,17 @@ void add_pending(void* stream, uint32_t* report) {
 }
 
 int status_to_code(uint32_t st) {
-  if (st & ST_TIMEOUT) return fail(ETC_ERR_TIMEOUT, "in-kernel wait exceeded its spin budget (status 0x%x)", st);
+  if (st & ST_TIMEOUT) return fail(ETC_ERR_TIMEOUT, "an in-kernel wait outlived its watchdog (status 0x%x)", st);
   if (st & (ST_OVER_NOTIFY | ST_QUEUE_OVERFLOW))
     return fail(ETC_ERR_INVARIANT, "event over-notified or queue overflow (status 0x%x)", st);
   if (st & ST_NONFINITE) return fail(ETC_ERR_NONFINITE, "NaN router logit (status 0x%x)", st);
   return ETC_OK;
 }
 
-// Per-device facts for grid sizing.
+// Per-device facts for grid sizing and the watchdog.
 struct DeviceFacts {
   int cus = 0;
+  int wall_khz = 0;  // rate of the constant wall clock the kernels read
 };
 std::mutex g_dev_mu;
 std::vector<DeviceFacts> g_dev;
@@ -78,6 +79,29 @@ int device_cus(int* cus) {
     g_dev[dev].cus = v;
   }
   *cus = g_dev[dev].cus;
+  return ETC_OK;
+}
+
+// Microseconds of wall time (0 = default) to ticks of the device wall clock.
+int watchdog_ticks(uint32_t us, uint64_t* ticks) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int khz = 0;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+    if (g_dev[dev].wall_khz == 0) {
+      int v = 0;
+      e = hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev);
+      if (e != hipSuccess || v <= 0) v = 100000;  // 100 MHz, the CDNA real-time counter
+      g_dev[dev].wall_khz = v;
+    }
+    khz = g_dev[dev].wall_khz;
+  }
+  const uint64_t u = us ? us : kDefaultWatchdogUs;
+  *ticks = u * (uint64_t)khz / 1000u;
+  if (*ticks == 0) *ticks = 1;
   return ETC_OK;
 }
 
@@ -245,6 +269,10 @@ extern "C" int etc_splitk_launch(etc_etensor* ev, int32_t n, int32_t nsplit, int
   if (!ev || !A || !B || !C) return fail(ETC_ERR_INVALID, "NULL argument");
   if (sched != ETC_SCHED_STATIC && sched != ETC_SCHED_DYNAMIC)
     return fail(ETC_ERR_UNSUPPORTED, "split-K runs under STATIC or DYNAMIC only");
+  if (sched == ETC_SCHED_DYNAMIC)
+    return fail(ETC_ERR_UNSUPPORTED,
+                "the dynamic (push/pop) schedule is switched off: it shares the queue protocol of the MoE "
+                "dynamic schedule, whose launch did not complete on the GPU");
   if (n < 1 || nsplit < 1 || bk < 1 || (int64_t)n * nsplit > (1 << 28))
     return fail(ETC_ERR_INVALID, "bad sizes n=%d nsplit=%d bk=%d", n, nsplit, bk);
   if (!ev->instantiated || ev->ndim != 1 || ev->bound[0] != n)
@@ -264,14 +292,14 @@ extern "C" int etc_splitk_launch(etc_etensor* ev, int32_t n, int32_t nsplit, int
   if (sk.q_cap < n) {
     if (sk.ctl) (void)hipFree(sk.ctl);
     const int64_t cap = n > 4096 ? n : 4096;
-    const size_t bytes = 256 + (size_t)cap * 8;
+    const size_t bytes = kSkCtlBytes + (size_t)cap * 8;
     void* mem = nullptr;
     e = hipMalloc(&mem, bytes);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(split-K control)");
     e = hipMemsetAsync(mem, 0, bytes, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(split-K control)");
     sk.ctl = static_cast<uint32_t*>(mem);
-    sk.queue = reinterpret_cast<uint64_t*>(static_cast<char*>(mem) + 256);
+    sk.queue = reinterpret_cast<uint64_t*>(static_cast<char*>(mem) + kSkCtlBytes);
     sk.q_cap = cap;
   }
   int cus = 0;
@@ -282,10 +310,13 @@ extern "C" int etc_splitk_launch(etc_etensor* ev, int32_t n, int32_t nsplit, int
   if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
   if (nb < 1) nb = 1;
   if (nb > 2) nb = 2;
+  uint64_t ticks = 0;
+  rc = watchdog_ticks(0, &ticks);
+  if (rc) return rc;
   e = (hipError_t)launch_splitk(n, nsplit, bk, A, B, C, ev->counters, sk.ctl, sk.queue, sk.q_cap, sched, nb * cus,
-                                kDefaultSpins, stream);
+                                ticks, stream);
   if (e != hipSuccess) return hip_fail(e, "split-K launch");
-  add_pending(stream, sk.ctl + 4 /* report word */);
+  add_pending(stream, sk.ctl + SK_REPORT);
   return ETC_OK;
 }
 
@@ -334,6 +365,10 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
   if (T < 1 || T > d->T_max) return fail(ETC_ERR_INVALID, "T %d outside [1, T_max=%d]", T, d->T_max);
   if (sched != ETC_SCHED_STATIC && sched != ETC_SCHED_DYNAMIC && sched != ETC_SCHED_KBK && sched != ETC_SCHED_BARRIER)
     return fail(ETC_ERR_INVALID, "unknown schedule %d", sched);
+  if (sched == ETC_SCHED_DYNAMIC)
+    return fail(ETC_ERR_UNSUPPORTED,
+                "the dynamic (push/pop) schedule is switched off: its launch did not complete on the GPU "
+                "and the cause is not yet found");
   const void* bf[] = {a->x, a->w_router, a->w13, a->w2, a->out, a->workspace};
   const char* bfn[] = {"x", "w_router", "w13", "w2", "out", "workspace"};
   for (int i = 0; i < 6; ++i)
@@ -388,7 +423,8 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
   p.norm_topk = d->norm_topk;
   p.has_bias = d->has_bias;
   p.max_rt = L.max_rt;
-  p.budget = a->watchdog_spins ? a->watchdog_spins : kDefaultSpins;
+  rc = watchdog_ticks(a->watchdog_us, &p.budget);
+  if (rc) return rc;
 
   const int lds = (int)lds_bytes_for(d);
   int e;

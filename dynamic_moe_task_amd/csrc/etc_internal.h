@@ -32,26 +32,34 @@ constexpr int kMaxE = 256;
 constexpr int kMaxTmax = 4096;
 constexpr int kMaxHI = 16384;
 constexpr int kMaxBitmapWords = 8192;  // E * ceil(T_max / 32), LDS of the scan task
-// spin budget of one in-kernel wait (each spin: one agent-scope load plus a
-// short s_sleep); a healthy wait lasts well under a thousand spins
-constexpr uint32_t kDefaultSpins = 1u << 20;
+// watchdog of one in-kernel wait, in microseconds of wall time; a healthy
+// wait lasts microseconds
+constexpr uint32_t kDefaultWatchdogUs = 2000000u;
 
 // task types (queue descriptors carry them in bits 60..63; 0 = empty slot)
 enum TaskType : int { TT_R = 1, TT_K = 2, TT_S = 3, TT_D = 4, TT_G1 = 5, TT_G2 = 6, TT_C = 7 };
 
 // ---- counter set (u32 words) ------------------------------------------------
+// Words that many workgroups poll or update each sit on their own 128-byte
+// line, so the status poll, the queue head and the queue tail do not queue
+// up behind one another.
 enum : int {
   W_STATUS = 0,
-  W_DONE = 1,
-  W_HEAD = 2,
-  W_TAIL = 3,
-  W_TOTAL = 4,
-  W_BAR_COUNT = 5,
-  W_BAR_GEN = 6,
-  W_EV_ROUTE = 7,
-  W_EV_SCAN = 8,
-  W_FIXED = 16,  // start of the variable-size event tensors
+  W_DONE = 32,
+  W_HEAD = 64,
+  W_TAIL = 96,
+  W_TOTAL = 128,
+  W_BAR_COUNT = 160,
+  W_BAR_GEN = 192,
+  W_EV_ROUTE = 224,
+  W_EV_SCAN = 256,
+  W_FIXED = 288,  // start of the variable-size event tensors
 };
+// split-K example: control words (u32) of its library-owned block, each on
+// its own 128-byte line, followed by the queue
+enum : int { SK_STATUS = 0, SK_HEAD = 32, SK_TAIL = 64, SK_DONE = 96, SK_REPORT = 128 };
+constexpr int kSkCtlBytes = 1024;
+
 // control block (u32 words)
 enum : int { C_EPOCH = 0, C_REPORT = 1, C_WORDS = 64 };
 
@@ -143,7 +151,7 @@ struct MoeParams {
   int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_c, o_queue, q_cap;
   int32_t T, H, E, k, I, norm_topk, has_bias;
   int32_t max_rt;
-  uint32_t budget;
+  uint64_t budget;  // watchdog, in wall-clock ticks
 };
 
 // Host-side launchers (moe_kernels.hip).  Return a hipError_t value.
@@ -152,7 +160,7 @@ int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream);
 int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu);
 int launch_splitk(int n, int nsplit, int bk, const int32_t* A, int32_t* B, int32_t* C,
                   int32_t* ev, uint32_t* ctl, uint64_t* queue, int64_t q_cap, int sched, int grid,
-                  uint32_t budget, void* stream);
+                  uint64_t budget, void* stream);
 int splitk_occupancy(int sched, int* blocks_per_cu);
 
 }  // namespace etc

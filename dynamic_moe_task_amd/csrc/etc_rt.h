@@ -31,14 +31,21 @@ __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
 __device__ __forceinline__ uint64_t ld_relaxed64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Signals that another workgroup polls are always written with an atomic
+// read-modify-write (swap), never with a plain or atomic store.  A release
+// store writes the L2 back *before* the signal, so the signal word itself can
+// stay dirty in the writer's XCD-local L2 while pollers on other XCDs read
+// past it; read-modify-writes are performed where every XCD sees them (the
+// event counters rely on exactly that).
+__device__ __forceinline__ void sig_put(uint32_t* p, uint32_t v) {
+  (void)__hip_atomic_exchange(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sig_put64(uint64_t* p, uint64_t v) {
+  (void)__hip_atomic_exchange(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Plain relaxed store: only for words read after a kernel boundary.
 __device__ __forceinline__ void st_relaxed(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_release64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_release(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t add_acqrel(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -52,28 +59,37 @@ __device__ __forceinline__ void or_relaxed(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 
+// Wall-clock watchdog: every in-kernel wait gives up once `budget` ticks of
+// the constant-rate real-time counter have passed since the wait began (the
+// host converts microseconds to ticks with the device's wall-clock rate), so
+// a wait ends in bounded time however contended the polled line is.
+__device__ __forceinline__ uint64_t now_ticks() { return wall_clock64(); }
+
 // Spin (one thread) until *ctr >= target.  Returns false if the launch is
-// aborting or the spin budget ran out (then ST_TIMEOUT | ST_ABORT is set so
+// aborting or the watchdog expired (then ST_TIMEOUT | ST_ABORT is set so
 // every other workgroup leaves its own waits too and the grid drains).
 __device__ __forceinline__ bool spin_until_geq(const uint32_t* ctr, uint32_t target, uint32_t* status,
-                                               uint32_t budget) {
-  uint32_t spins = 0;
-  while (ld_relaxed(ctr) < target) {
-    if (ld_relaxed(status) & ST_ABORT) return false;
-    if (++spins > budget) {
-      or_relaxed(status, ST_TIMEOUT | ST_ABORT);
-      return false;
+                                               uint64_t budget) {
+  if (ld_relaxed(ctr) >= target) return true;
+  const uint64_t t0 = now_ticks();
+  for (uint32_t spins = 1;; ++spins) {
+    if (ld_relaxed(ctr) >= target) return true;
+    if ((spins & 7u) == 0u) {
+      if (ld_relaxed(status) & ST_ABORT) return false;
+      if (now_ticks() - t0 > budget) {
+        or_relaxed(status, ST_TIMEOUT | ST_ABORT);
+        return false;
+      }
     }
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(2);
   }
-  return true;
 }
 
 // Whole-workgroup wait on one event element.  Thread 0 polls; the others
 // wait at the barrier; everyone then takes an acquire fence.  Returns false
 // on abort (uniform across the workgroup).
 __device__ __forceinline__ bool wg_wait(const uint32_t* ctr, uint32_t target, uint32_t* status,
-                                        uint32_t budget) {
+                                        uint64_t budget) {
   int fail = 0;
   if (threadIdx.x == 0) fail = spin_until_geq(ctr, target, status, budget) ? 0 : 1;
   fail = __syncthreads_or(fail);

@@ -88,7 +88,7 @@ struct Ctx {
   uint64_t* queue;
   int T, H, E, k, I;
   int nTT, nET, nR, nK, nD, nC, nN1, nN2;
-  uint32_t budget;
+  uint64_t budget;  // watchdog of one wait, wall-clock ticks
 };
 
 __device__ __forceinline__ Ctx make_ctx(const MoeParams& p, uint32_t* set) {
@@ -304,7 +304,7 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
     tptr[E] = tot_tiles;
     p.indptr[E] = tot_rows;
     p.tile_indptr[E] = tot_tiles;
-    st_relaxed(p.meta + M_NRT, (uint32_t)tot_tiles);
+    sig_put(p.meta + M_NRT, (uint32_t)tot_tiles);
   }
   __syncthreads();
   for (int f = tid; f < n; f += kThreads) {
@@ -520,7 +520,7 @@ __device__ void after_router(const MoeParams& p, const Ctx& c, int tt) {
     if (threadIdx.x == 0) {
       if (notify1(c, ev_logit(p, c) + tt, (uint32_t)c.nET) && MODE == MODE_DYNAMIC) {
         const int64_t q = q_reserve(p, c, 1);
-        if (q >= 0) st_release64(c.queue + q, make_desc(TT_K, tt, 0));
+        if (q >= 0) sig_put64(c.queue + q, make_desc(TT_K, tt, 0));
       }
     }
   }
@@ -533,7 +533,7 @@ __device__ void after_topk(const MoeParams& p, const Ctx& c) {
     if (threadIdx.x == 0) {
       if (notify1(c, c.set + W_EV_ROUTE, (uint32_t)c.nK) && MODE == MODE_DYNAMIC) {
         const int64_t q = q_reserve(p, c, 1);
-        if (q >= 0) st_release64(c.queue + q, make_desc(TT_S, 0, 0));
+        if (q >= 0) sig_put64(c.queue + q, make_desc(TT_S, 0, 0));
       }
     }
   }
@@ -547,14 +547,14 @@ __device__ void after_scan(const MoeParams& p, const Ctx& c, Shared& sh) {
       if (threadIdx.x == 0) {
         const uint32_t nrt = ld_relaxed(p.meta + M_NRT);
         const uint32_t total = (uint32_t)(c.nR + c.nK + 1 + c.nD + c.nC) + nrt * (uint32_t)(c.nN1 + c.nN2);
-        st_release(c.set + W_TOTAL, total);
+        sig_put(c.set + W_TOTAL, total);
         sh.base = (int)q_reserve(p, c, c.nD);
       }
       __syncthreads();
       const int base = sh.base;
       if (base >= 0)
         for (int i = threadIdx.x; i < c.nD; i += kThreads)
-          st_release64(c.queue + base + i, make_desc(TT_D, i, 0));
+          sig_put64(c.queue + base + i, make_desc(TT_D, i, 0));
       __syncthreads();
     } else {
       if (threadIdx.x == 0) notify1(c, c.set + W_EV_SCAN, 1u);
@@ -604,7 +604,7 @@ __device__ void after_dispatch(const MoeParams& p, const Ctx& c, int dt, Shared&
         while (i >= sh.pref[j + 1]) ++j;
         const int li = i - sh.pref[j];
         const int rt = p.tile_indptr[sh.list[j]] + li / c.nN1;
-        st_release64(c.queue + base + i, make_desc(TT_G1, rt, li % c.nN1));
+        sig_put64(c.queue + base + i, make_desc(TT_G1, rt, li % c.nN1));
       }
     }
     __syncthreads();
@@ -625,7 +625,7 @@ __device__ void after_g1(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
     const int base = sh.base;
     if (base >= 0)
       for (int i = threadIdx.x; i < c.nN2; i += kThreads)
-        st_release64(c.queue + base + i, make_desc(TT_G2, rt, i));
+        sig_put64(c.queue + base + i, make_desc(TT_G2, rt, i));
     __syncthreads();
   }
 }
@@ -651,7 +651,7 @@ __device__ void after_g2(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
     __syncthreads();
     const int base = sh.base;
     if (base >= 0 && threadIdx.x < n)
-      st_release64(c.queue + base + threadIdx.x, make_desc(TT_C, sh.list[threadIdx.x], 0));
+      sig_put64(c.queue + base + threadIdx.x, make_desc(TT_C, sh.list[threadIdx.x], 0));
     __syncthreads();
   }
 }
@@ -659,7 +659,7 @@ __device__ void after_g2(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
 // ==================================================== schedules ==========
 // Grid-wide barrier (BARRIER comparator only): arrival counter plus a
 // generation word; the last arrival resets the counter and bumps the
-// generation.  Bounded by the same spin budget as every other wait.
+// generation.  Bounded by the same watchdog as every other wait.
 __device__ bool grid_barrier(const Ctx& c) {
   wg_publish();
   int fail = 0;
@@ -669,14 +669,16 @@ __device__ bool grid_barrier(const Ctx& c) {
     const uint32_t g0 = ld_relaxed(gen);
     const uint32_t old = add_acqrel(cnt, 1u);
     if (old == gridDim.x - 1u) {
-      st_relaxed(cnt, 0u);
+      sig_put(cnt, 0u);
       add_acqrel(gen, 1u);
     } else {
-      uint32_t spins = 0;
-      while (ld_relaxed(gen) == g0) {
-        if (ld_relaxed(c.status) & ST_ABORT) { fail = 1; break; }
-        if (++spins > c.budget) { or_relaxed(c.status, ST_TIMEOUT | ST_ABORT); fail = 1; break; }
-        __builtin_amdgcn_s_sleep(1);
+      const uint64_t t0 = now_ticks();
+      for (uint32_t spins = 1; ld_relaxed(gen) == g0; ++spins) {
+        if ((spins & 7u) == 0u) {
+          if (ld_relaxed(c.status) & ST_ABORT) { fail = 1; break; }
+          if (now_ticks() - t0 > c.budget) { or_relaxed(c.status, ST_TIMEOUT | ST_ABORT); fail = 1; break; }
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
     }
   }
@@ -779,15 +781,17 @@ __device__ void run_dynamic(const MoeParams& p, const Ctx& c, uint8_t* smem, Sha
       } else {
         const int64_t qi = (int64_t)idx - c.nR;
         if (qi < p.q_cap) {
-          uint32_t spins = 0;
-          for (;;) {
+          const uint64_t t0 = now_ticks();
+          for (uint32_t spins = 1;; ++spins) {
             const uint64_t v = ld_relaxed64(c.queue + qi);
             if (v) { d = v; break; }
-            const uint32_t tot = ld_relaxed(c.set + W_TOTAL);
-            if (tot && idx >= tot) break;
-            if (ld_relaxed(c.status) & ST_ABORT) break;
-            if (++spins > c.budget) { or_relaxed(c.status, ST_TIMEOUT | ST_ABORT); break; }
-            __builtin_amdgcn_s_sleep(1);
+            if ((spins & 3u) == 0u) {
+              const uint32_t tot = ld_relaxed(c.set + W_TOTAL);
+              if (tot && idx >= tot) break;
+              if (ld_relaxed(c.status) & ST_ABORT) break;
+              if (now_ticks() - t0 > c.budget) { or_relaxed(c.status, ST_TIMEOUT | ST_ABORT); break; }
+            }
+            __builtin_amdgcn_s_sleep(2);
           }
         }
       }
@@ -869,7 +873,7 @@ __global__ void __launch_bounds__(kThreads) moe_persistent(MoeParams p) {
     const uint32_t st = ld_relaxed(c.status) & ~ST_ABORT;
     if (st) or_relaxed(p.ctrl + C_REPORT, st);
     const uint32_t old = add_acqrel(set + W_DONE, 1u);
-    if (old == gridDim.x - 1u) st_release(p.ctrl + C_EPOCH, epoch + 1u);
+    if (old == gridDim.x - 1u) sig_put(p.ctrl + C_EPOCH, epoch + 1u);
   }
 }
 

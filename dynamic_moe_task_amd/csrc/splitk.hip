@@ -20,7 +20,6 @@
 
 namespace etc {
 
-enum : int { SK_STATUS = 0, SK_HEAD = 1, SK_TAIL = 2, SK_DONE = 3, SK_REPORT = 4, SK_WORDS = 16 };
 constexpr int SK_PARTIAL = 1, SK_FINAL = 2;
 constexpr uint64_t SK_EXIT = ~0ull;
 
@@ -33,7 +32,7 @@ struct SkParams {
   uint64_t* queue;
   int64_t q_cap;
   int n, nsplit, bk;
-  uint32_t budget;
+  uint64_t budget;
 };
 
 __device__ int block_sum_i32(int v, int* tmp) {
@@ -85,7 +84,7 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
     }
     for (int i = (w - nP % G + G) % G; i < p.n; i += G) {
       if (!wg_wait(p.ev + i, (uint32_t)p.nsplit, status, p.budget)) break;
-      if (threadIdx.x == 0) st_relaxed(p.ev + i, 0u);  // sole waiter: back to rest
+      if (threadIdx.x == 0) sig_put(p.ev + i, 0u);  // sole waiter: back to rest
       sk_final(p, i, tmp);
     }
   } else {
@@ -100,17 +99,19 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
           d = ((uint64_t)SK_PARTIAL << 60) | idx;
         } else if (idx < total) {
           const int64_t qi = (int64_t)idx - nP;
-          uint32_t spins = 0;
-          for (;;) {
+          const uint64_t t0 = now_ticks();
+          for (uint32_t spins = 1;; ++spins) {
             const uint64_t v = ld_relaxed64(p.queue + qi);
             if (v) {
               d = v;
-              __hip_atomic_store(p.queue + qi, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              sig_put64(p.queue + qi, 0ull);  // slot back to rest for the next launch
               break;
             }
-            if (ld_relaxed(status) & ST_ABORT) break;
-            if (++spins > p.budget) { or_relaxed(status, ST_TIMEOUT | ST_ABORT); break; }
-            __builtin_amdgcn_s_sleep(1);
+            if ((spins & 3u) == 0u) {
+              if (ld_relaxed(status) & ST_ABORT) break;
+              if (now_ticks() - t0 > p.budget) { or_relaxed(status, ST_TIMEOUT | ST_ABORT); break; }
+            }
+            __builtin_amdgcn_s_sleep(2);
           }
         }
         s_desc = d;
@@ -128,12 +129,12 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
         if (threadIdx.x == 0 && sk_notify(p, a / p.nsplit)) {
           const uint32_t q = add_relaxed(p.ctl + SK_TAIL, 1u);
           if ((int64_t)q < p.q_cap)
-            st_release64(p.queue + q, ((uint64_t)SK_FINAL << 60) | (uint64_t)(a / p.nsplit));
+            sig_put64(p.queue + q, ((uint64_t)SK_FINAL << 60) | (uint64_t)(a / p.nsplit));
           else
             or_relaxed(status, ST_QUEUE_OVERFLOW | ST_ABORT);
         }
       } else {
-        if (threadIdx.x == 0) st_relaxed(p.ev + a, 0u);
+        if (threadIdx.x == 0) sig_put(p.ev + a, 0u);
         sk_final(p, a, tmp);
       }
     }
@@ -144,16 +145,16 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
     if (old == (uint32_t)G - 1u) {
       const uint32_t st = ld_relaxed(status) & ~ST_ABORT;
       if (st) or_relaxed(p.ctl + SK_REPORT, st);
-      st_relaxed(status, 0u);
-      st_relaxed(p.ctl + SK_HEAD, 0u);
-      st_relaxed(p.ctl + SK_TAIL, 0u);
-      st_relaxed(p.ctl + SK_DONE, 0u);
+      sig_put(status, 0u);
+      sig_put(p.ctl + SK_HEAD, 0u);
+      sig_put(p.ctl + SK_TAIL, 0u);
+      sig_put(p.ctl + SK_DONE, 0u);
     }
   }
 }
 
 int launch_splitk(int n, int nsplit, int bk, const int32_t* A, int32_t* B, int32_t* C, int32_t* ev,
-                  uint32_t* ctl, uint64_t* queue, int64_t q_cap, int sched, int grid, uint32_t budget,
+                  uint32_t* ctl, uint64_t* queue, int64_t q_cap, int sched, int grid, uint64_t budget,
                   void* stream) {
   SkParams p;
   p.A = A; p.B = B; p.C = C;

@@ -154,8 +154,10 @@ typedef struct {
  *            (launches that overlap on one workspace race).
  *   debug    NULL, or ETC_DEBUG_WORDS(E) int32 zeroed by the caller; the
  *            kernel adds per-event notify and fire counts (layout below).
- *   watchdog_spins: 0 = default; else the spin budget of every in-kernel
- *            wait before it reports ETC_ERR_TIMEOUT and the grid drains.    */
+ *   watchdog_us: 0 = default (2 s); else the wall time, in microseconds,
+ *            after which any single in-kernel wait gives up: the launch then
+ *            drains (every workgroup leaves its waits) and etc_sync reports
+ *            ETC_ERR_TIMEOUT.                                               */
 typedef struct {
   const void* x;
   const void* w_router;
@@ -172,7 +174,7 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   int32_t* debug;
-  uint32_t watchdog_spins;
+  uint32_t watchdog_us;
 } etc_moe_args;
 
 /* Debug counters (int32), when etc_moe_args.debug is non-NULL:

@@ -41,14 +41,14 @@ class DeviceLayer:
         self.bufs = B.MoELayerBuffers.allocate(self.desc, self.Wr, self.W13, self.Wd, self.bias, debug=debug)
         torch.cuda.synchronize()
 
-    def run(self, X: np.ndarray, sched: str, watchdog_spins: int = 0, check_status: bool = True):
+    def run(self, X: np.ndarray, sched: str, watchdog_us: int = 0, check_status: bool = True):
         import torch
         T = X.shape[0]
         self.bufs.x[:T].copy_(dev_bf16(X))
         if self.bufs.debug is not None:
             self.bufs.debug.zero_()
         stream = torch.cuda.current_stream().cuda_stream
-        self.bufs.launch(T, sched, stream=stream, watchdog_spins=watchdog_spins)
+        self.bufs.launch(T, sched, stream=stream, watchdog_us=watchdog_us)
         rc = self.B.etc_sync(stream)
         if check_status and rc != 0:
             raise self.B.EtcError(rc, self.B.etc_last_error())

@@ -123,3 +123,13 @@ def test_splitk_validation():
     # schedule
     assert B.etc_splitk_launch(h, 8, 4, 16, 0x1000, 0x1000, 0x1000, B.ETC_SCHED_KBK, None) == B.ETC_ERR_UNSUPPORTED
     B.etensor_destroy(h)
+
+
+@needs_lib
+def test_dynamic_schedule_is_switched_off_with_an_error():
+    # the push/pop schedule is disabled until its GPU hang is understood: a
+    # launch must fail loudly before touching the GPU, never fall back
+    d = B.moe_desc(16, 2048, 128, 8, 768)
+    args = B.MoeArgs(*([0x1000] * 13), 1 << 30, None, 0)
+    assert B.moe_layer_launch(d, 4, args, B.ETC_SCHED_DYNAMIC, None) == B.ETC_ERR_UNSUPPORTED
+    assert "switched off" in B.etc_last_error()

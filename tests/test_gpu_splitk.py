@@ -10,7 +10,12 @@ from gpu_util import announce
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("sched", [0, 1], ids=["static", "dynamic"])
+DYNAMIC_OFF = ("the dynamic push/pop schedule is switched off in the library: it shares the queue protocol "
+               "of the MoE dynamic schedule, whose first GPU launch did not complete")
+
+
+@pytest.mark.parametrize("sched", [0, pytest.param(1, marks=pytest.mark.skip(reason=DYNAMIC_OFF))],
+                         ids=["static", "dynamic"])
 @pytest.mark.parametrize("n,bk", [(1, 16), (50, 64), (1000, 256), (5000, 8)])
 def test_splitk_rowsum(sched, n, bk):
     import torch
