@@ -44,7 +44,52 @@ def parse():
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 counters (JSON)")
     ap.add_argument("--only-sched", action="store_true", help="time only --sched (for profiling)")
+    ap.add_argument("--trace", default="", help="write a per-task trace summary of each persistent "
+                    "schedule to this JSON file (one extra traced launch each, outside the timing)")
     return ap.parse_args()
+
+
+TASK_NAMES = {1: "R", 2: "K", 3: "S", 4: "D", 5: "G1", 6: "G2", 7: "C"}
+
+
+def trace_summary(bufs, T, sched, khz, stream_ptr, records=1 << 16):
+    """One traced launch: per task type, count, mean/max duration, mean
+    wait, and the first start / last end in µs from the earliest wait."""
+    import torch
+    from dynamic_moe_task_amd import binding as B
+    tr = torch.zeros(16 + 8 * records, dtype=torch.int32, device="cuda")
+    B.check(B.moe_layer_launch(bufs.desc, T, bufs.args(trace=tr), B.SCHEDS[sched], stream_ptr))
+    B.check(B.etc_sync(stream_ptr))
+    raw = tr.cpu().numpy().view(np.uint32)
+    n = min(int(raw[0]), records)
+    rec = raw[16:16 + 8 * n].reshape(n, 8).astype(np.int64)
+    wg, typ = rec[:, 0] & 0xFFFFFF, rec[:, 0] >> 24
+    tw = (rec[:, 4] << 32) | rec[:, 3]
+
+    def unwrap(lo):  # the later stamps share tw's high word unless they wrapped
+        t = (rec[:, 4] << 32) | lo
+        return np.where(t < tw, t + (1 << 32), t)
+
+    ts, tb, te = unwrap(rec[:, 5]), unwrap(rec[:, 6]), unwrap(rec[:, 7])
+    t0 = tw.min()
+    us = 1e3 / khz
+    out = {"records": n, "span_us": round(float((te.max() - t0) * us), 2)}
+    for t, name in TASK_NAMES.items():
+        m = typ == t
+        if not m.any():
+            continue
+        body = (tb[m] - ts[m]) * us
+        notify = (te[m] - tb[m]) * us
+        wt = (ts[m] - tw[m]) * us
+        out[name] = {"n": int(m.sum()), "body_mean_us": round(float(body.mean()), 2),
+                     "body_max_us": round(float(body.max()), 2),
+                     "notify_mean_us": round(float(notify.mean()), 2),
+                     "wait_mean_us": round(float(wt.mean()), 2), "wait_max_us": round(float(wt.max()), 2),
+                     "first_start_us": round(float((ts[m].min() - t0) * us), 2),
+                     "last_end_us": round(float((te[m].max() - t0) * us), 2)}
+    per_wg = np.bincount(wg, weights=(te - ts) * us)
+    out["busy_per_wg_us"] = {"mean": round(float(per_wg.mean()), 2), "max": round(float(per_wg.max()), 2)}
+    return out
 
 
 def dev_bf16(bits):
@@ -164,6 +209,13 @@ def main():
                 "kernel": f"moe_persistent<{a.sched}>" if a.sched != "kbk" else "kbk_* (7 launches)",
                 "algorithmic_bytes": alg_bytes}
     mfma_frac = alg_flops / (us_main * 1e-6) / (BF16_PEAK_TFS * 1e12)
+
+    if a.trace:
+        info = B.moe_layer_info(desc)
+        summ = {s: trace_summary(bufs, T, s, info.wall_clock_khz, sp) for s in ("static", "barrier")}
+        summ["grid"] = info.grid
+        with open(a.trace, "w") as f:
+            json.dump(summ, f, indent=1)
 
     cpu = None
     if not a.no_cpu:

@@ -60,14 +60,16 @@ class MoeArgs(ctypes.Structure):
                 ("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("counts", ctypes.c_void_p),
                 ("exp_indptr", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("slot", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("debug", ctypes.c_void_p), ("watchdog_us", ctypes.c_uint32)]
+                ("debug", ctypes.c_void_p), ("watchdog_us", ctypes.c_uint32),
+                ("trace_records", ctypes.c_uint32), ("trace", ctypes.c_void_p)]
 
 
 class MoeInfo(ctypes.Structure):
     _fields_ = [("bm", ctypes.c_int32), ("bn1", ctypes.c_int32), ("bn2", ctypes.c_int32),
                 ("router_tokens", ctypes.c_int32), ("router_experts", ctypes.c_int32),
                 ("dispatch_tokens", ctypes.c_int32), ("combine_tokens", ctypes.c_int32),
-                ("grid", ctypes.c_int32), ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32)]
+                ("grid", ctypes.c_int32), ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("wall_clock_khz", ctypes.c_int32)]
 
 
 _lib = None
@@ -214,7 +216,7 @@ class MoELayerBuffers:
         check(moe_workspace_init(desc, bufs.workspace.data_ptr(), ws_bytes, stream))
         return bufs
 
-    def args(self, x=None, w13=None, w2=None, watchdog_us: int = 0) -> MoeArgs:
+    def args(self, x=None, w13=None, w2=None, watchdog_us: int = 0, trace=None) -> MoeArgs:
         x = self.x if x is None else x
         w13 = self.w13 if w13 is None else w13
         w2 = self.w2 if w2 is None else w2
@@ -225,7 +227,8 @@ class MoELayerBuffers:
             self.topk_w.data_ptr(), self.counts.data_ptr(), self.exp_indptr.data_ptr(),
             self.perm.data_ptr(), self.slot.data_ptr(), self.workspace.data_ptr(),
             self.workspace.numel(), self.debug.data_ptr() if self.debug is not None else None,
-            watchdog_us)
+            watchdog_us, 0 if trace is None else (trace.numel() - 16) // 8,
+            None if trace is None else trace.data_ptr())
 
     def launch(self, T: int, sched="static", stream=None, **kw) -> None:
         import torch

@@ -121,6 +121,8 @@ int desc_check(const etc_moe_desc* d) {
   if (d->I < 128 || d->I % 128 || d->I > kMaxHI) return fail(ETC_ERR_INVALID, "I %d must be a positive multiple of 128, <= %d", d->I, kMaxHI);
   if (d->E < 1 || d->E > kMaxE) return fail(ETC_ERR_INVALID, "E %d outside [1, %d]", d->E, kMaxE);
   if (d->k < 1 || d->k > kMaxK || d->k > d->E) return fail(ETC_ERR_INVALID, "k %d outside [1, min(E, %d)]", d->k, kMaxK);
+  if ((int64_t)d->T_max * d->k * (d->H > d->I ? d->H : d->I) * 2 >= (int64_t)1 << 31)
+    return fail(ETC_ERR_INVALID, "T_max * k * max(H, I) * 2 bytes must stay below 2 GiB");
   if ((int64_t)d->E * cdiv(d->T_max, 32) > kMaxBitmapWords)
     return fail(ETC_ERR_INVALID, "E * ceil(T_max/32) = %lld exceeds %d", (long long)d->E * cdiv(d->T_max, 32), kMaxBitmapWords);
   if (d->norm_topk != 0 && d->norm_topk != 1) return fail(ETC_ERR_INVALID, "norm_topk must be 0 or 1");
@@ -344,6 +346,10 @@ extern "C" int moe_layer_info(const etc_moe_desc* d, etc_moe_info* info) {
   rc = persistent_grid(ETC_SCHED_STATIC, info->lds_bytes, &grid);
   if (rc) return rc;
   info->grid = grid;
+  uint64_t per_ms = 0;
+  rc = watchdog_ticks(1000, &per_ms);
+  if (rc) return rc;
+  info->wall_clock_khz = (int32_t)per_ms;
   return ETC_OK;
 }
 
@@ -379,6 +385,8 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
     if (!iv[i] || !aligned4(iv[i])) return fail(ETC_ERR_INVALID, "%s is NULL or not 4-byte aligned", ivn[i]);
   if (d->has_bias && (!a->b_router || !aligned4(a->b_router))) return fail(ETC_ERR_INVALID, "b_router is NULL or misaligned");
   if (a->debug && !aligned4(a->debug)) return fail(ETC_ERR_INVALID, "debug misaligned");
+  if (a->trace && (!aligned4(a->trace) || a->trace_records == 0))
+    return fail(ETC_ERR_INVALID, "trace misaligned or trace_records is 0");
   const MoeLayout L = moe_layout(*d);
   if (a->workspace_bytes < (size_t)L.total_bytes)
     return fail(ETC_ERR_INVALID, "workspace has %zu bytes, needs %lld", a->workspace_bytes, (long long)L.total_bytes);
@@ -423,6 +431,17 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
   p.norm_topk = d->norm_topk;
   p.has_bias = d->has_bias;
   p.max_rt = L.max_rt;
+  p.T_max = d->T_max;
+  {
+    const int64_t rows = (int64_t)d->T_max * d->k;
+    p.xp_bytes = (uint32_t)(rows * d->H * 2);
+    p.hh_bytes = (uint32_t)(rows * d->I * 2);
+    p.y_bytes = (uint32_t)(rows * d->H * 2);
+    p.logits_bytes = (uint32_t)((int64_t)d->T_max * d->E * 4);
+    p.rows_bytes = (uint32_t)(rows * 4);
+  }
+  p.trace = a->trace;
+  p.trace_records = a->trace ? a->trace_records : 0;
   rc = watchdog_ticks(a->watchdog_us, &p.budget);
   if (rc) return rc;
 

@@ -121,7 +121,9 @@ inline int64_t scan_lds_bytes(int E, int T_max) {
   const int64_t W = cdiv(T_max, 32);
   return align_up((int64_t)E * W * 4, 16) + align_up((int64_t)E * W * 2, 16) + 3 * 260 * 4 + 64;
 }
-constexpr int64_t kGemmLdsBytes = 4 * 4 * 256 * 4;  // G2 cross-wave reduction buffer
+// G2: cross-wave reduction buffer (4 waves x 4 blocks x 256 fp32) plus the
+// bf16 staging of the 16 x 64 output tile
+constexpr int64_t kGemmLdsBytes = 4 * 4 * 256 * 4 + 16 * 64 * 2;
 
 struct MoeParams {
   const uint16_t* x;
@@ -151,7 +153,12 @@ struct MoeParams {
   int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_c, o_queue, q_cap;
   int32_t T, H, E, k, I, norm_topk, has_bias;
   int32_t max_rt;
+  int32_t T_max;
+  // byte sizes of the device-coherent buffers (bounds of their resources)
+  uint32_t xp_bytes, hh_bytes, y_bytes, logits_bytes, rows_bytes;
   uint64_t budget;  // watchdog, in wall-clock ticks
+  uint32_t* trace;
+  uint32_t trace_records;
 };
 
 // Host-side launchers (moe_kernels.hip).  Return a hipError_t value.

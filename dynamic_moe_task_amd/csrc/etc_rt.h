@@ -1,22 +1,27 @@
 // Device-side event-tensor runtime for gfx950 (CDNA4): counters in HBM,
-// notify = agent-scope atomic add after a release fence, wait = relaxed
-// polling with s_sleep back-off and a spin budget, then an acquire fence.
+// notify = device-scope atomic add, wait = polling with s_sleep back-off and
+// a wall-clock watchdog.
 //
 // An event tensor element is a 32-bit arrival counter that starts at zero;
 // it is released once `wait_count` notifies have arrived.  The pages count
 // down from the wait_count to zero (Event Tensor, arXiv 2604.13327, Fig. 7;
 // podcast cue 11); counting arrivals up to the wait_count is the same state
 // machine (remaining = wait_count - arrivals) and lets a counter that the
-// kernel has just zeroed serve any wait_count, including one written later
-// by the task that computes it (data-dependent update, Fig. 5b; podcast
-// cue 7).
+// kernel has just zeroed serve any wait_count, including one written later by
+// the task that computes it (data-dependent update, Fig. 5b; podcast cue 7).
 //
-// Coherence across the 8 XCDs (each with its own L2) relies on the AMDGPU
-// memory model at agent scope: a release fence makes this wave's prior global
-// stores visible device-wide before the counter update; an acquire fence
-// after observing the counter makes the producer's data visible to the
-// following loads.  Counters themselves are only touched with agent-scope
-// atomics.
+// Coherence across the 8 XCDs (each with its own write-back L2).  Release and
+// acquire fences at agent scope are implemented on this chip as an L2-wide
+// write-back and an L2-wide invalidate; issued per task by hundreds of
+// workgroups they cost more than the tasks themselves.  The kernels therefore
+// never use them.  Instead every datum that crosses workgroups is written and
+// read with device-coherent accesses (the sc1 cache policy: buffer loads and
+// stores below, and device-scope atomics for counters), and a producer's
+// waves each wait until their own stores have completed (s_waitcnt) before
+// the workgroup barrier that precedes the notifying atomic.  A consumer that
+// has observed the counter then reads the data with device-coherent loads.
+// Ordinary (cached) accesses are used only for data no workgroup writes during
+// the launch (weights, activations) and for the final output.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -25,30 +30,22 @@
 
 namespace etc {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// ---- counters: device-scope atomics, relaxed (ordering comes from the
+// store-completion wait and barrier described above) -----------------------
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t ld_relaxed64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Signals that another workgroup polls are always written with an atomic
-// read-modify-write (swap), never with a plain or atomic store.  A release
-// store writes the L2 back *before* the signal, so the signal word itself can
-// stay dirty in the writer's XCD-local L2 while pollers on other XCDs read
-// past it; read-modify-writes are performed where every XCD sees them (the
-// event counters rely on exactly that).
-__device__ __forceinline__ void sig_put(uint32_t* p, uint32_t v) {
-  (void)__hip_atomic_exchange(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void sig_put64(uint64_t* p, uint64_t v) {
-  (void)__hip_atomic_exchange(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Plain relaxed store: only for words read after a kernel boundary.
 __device__ __forceinline__ void st_relaxed(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t add_acqrel(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_relaxed64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t add_relaxed(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -56,13 +53,41 @@ __device__ __forceinline__ uint32_t add_relaxed(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void or_relaxed(uint32_t* p, uint32_t v) {
   __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ uint32_t xchg_relaxed(uint32_t* p, uint32_t v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t xchg_relaxed64(uint64_t* p, uint64_t v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-// Wall-clock watchdog: every in-kernel wait gives up once `budget` ticks of
-// the constant-rate real-time counter have passed since the wait began (the
-// host converts microseconds to ticks with the device's wall-clock rate), so
-// a wait ends in bounded time however contended the polled line is.
+// ---- device-coherent data accesses through buffer resources --------------
+// A buffer resource also bounds every access: offsets past `bytes` read 0
+// and drop the store.
+constexpr int kCoherent = 16;  // cache policy bit sc1: device scope
+typedef unsigned int gcc_u32x4 __attribute__((__vector_size__(16)));
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t co_ld128(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent));
+}
+__device__ __forceinline__ void co_st128(rsrc_t r, uint32_t off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(gcc_u32x4, v), r, (int)off, 0, kCoherent);
+}
+__device__ __forceinline__ uint32_t co_ld32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCoherent);
+}
+__device__ __forceinline__ void co_st32(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kCoherent);
+}
+__device__ __forceinline__ float co_ldf(rsrc_t r, uint32_t off) { return __uint_as_float(co_ld32(r, off)); }
+__device__ __forceinline__ void co_stf(rsrc_t r, uint32_t off, float v) { co_st32(r, off, __float_as_uint(v)); }
+
+// ---- watchdog ---------------------------------------------------------------
+// Every in-kernel wait gives up once `budget` ticks of the constant-rate
+// wall clock have passed since it began (the host converts microseconds to
+// ticks with the device's wall-clock rate), so a wait ends in bounded time
+// however contended the polled line is.
 __device__ __forceinline__ uint64_t now_ticks() { return wall_clock64(); }
 
 // Spin (one thread) until *ctr >= target.  Returns false if the launch is
@@ -85,23 +110,23 @@ __device__ __forceinline__ bool spin_until_geq(const uint32_t* ctr, uint32_t tar
   }
 }
 
-// Whole-workgroup wait on one event element.  Thread 0 polls; the others
-// wait at the barrier; everyone then takes an acquire fence.  Returns false
-// on abort (uniform across the workgroup).
+// Whole-workgroup wait on one event element: thread 0 polls, the barrier
+// releases the others.  Data produced before the notifies is then read with
+// device-coherent loads.  Returns false on abort (uniform in the workgroup).
 __device__ __forceinline__ bool wg_wait(const uint32_t* ctr, uint32_t target, uint32_t* status,
                                         uint64_t budget) {
   int fail = 0;
   if (threadIdx.x == 0) fail = spin_until_geq(ctr, target, status, budget) ? 0 : 1;
   fail = __syncthreads_or(fail);
-  fence_acquire();
   return fail == 0;
 }
 
-// Publish the workgroup's global writes before a notify: every thread
-// releases its own stores at agent scope, then the barrier orders them
-// before the notifying thread's atomic.
+// Before a notify: each wave waits until its own (device-coherent) stores
+// have completed, then the barrier orders all of them before the notifying
+// thread's atomic.
 __device__ __forceinline__ void wg_publish() {
-  fence_release();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 }
 

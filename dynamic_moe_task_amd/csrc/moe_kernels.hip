@@ -22,6 +22,11 @@
 // lists, grid barriers instead of events), KBK (one launch per task type).
 // T is a kernel argument; every event shape and task count below is derived
 // from it in the kernel (Fig. 4: one template, instantiated per launch).
+//
+// Data that one workgroup writes and another reads (logits, routing tensors,
+// grouped rows Xp, intermediate Hmid, expert outputs Y) moves through
+// device-coherent loads and stores (etc_rt.h); weights and input tokens are
+// read through the caches.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -33,7 +38,6 @@ namespace etc {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 enum Mode : int { MODE_STATIC = ETC_SCHED_STATIC, MODE_DYNAMIC = ETC_SCHED_DYNAMIC,
                   MODE_KBK = ETC_SCHED_KBK, MODE_BARRIER = ETC_SCHED_BARRIER };
@@ -69,15 +73,31 @@ __device__ __forceinline__ int first_of(int w, int64_t off, int G) {
   return (w - o + G) % G;
 }
 
+// device-coherent resources of the arrays that cross workgroups
+__device__ __forceinline__ rsrc_t r_logits(const MoeParams& p) { return make_rsrc(p.logits, p.logits_bytes); }
+__device__ __forceinline__ rsrc_t r_ids(const MoeParams& p) { return make_rsrc(p.ids, p.rows_bytes); }
+__device__ __forceinline__ rsrc_t r_topw(const MoeParams& p) { return make_rsrc(p.topw, p.rows_bytes); }
+__device__ __forceinline__ rsrc_t r_perm(const MoeParams& p) { return make_rsrc(p.perm, p.rows_bytes); }
+__device__ __forceinline__ rsrc_t r_slot(const MoeParams& p) { return make_rsrc(p.slot, p.rows_bytes); }
+__device__ __forceinline__ rsrc_t r_counts(const MoeParams& p) { return make_rsrc(p.counts, (uint32_t)p.E * 4u); }
+__device__ __forceinline__ rsrc_t r_indptr(const MoeParams& p) { return make_rsrc(p.indptr, (uint32_t)(p.E + 1) * 4u); }
+__device__ __forceinline__ rsrc_t r_tptr(const MoeParams& p) {
+  return make_rsrc(p.tile_indptr, (uint32_t)(p.E + 1) * 4u);
+}
+__device__ __forceinline__ rsrc_t r_rtinfo(const MoeParams& p) { return make_rsrc(p.rt_info, (uint32_t)p.max_rt * 16u); }
+__device__ __forceinline__ rsrc_t r_xp(const MoeParams& p) { return make_rsrc(p.xp, p.xp_bytes); }
+__device__ __forceinline__ rsrc_t r_hh(const MoeParams& p) { return make_rsrc(p.hh, p.hh_bytes); }
+__device__ __forceinline__ rsrc_t r_y(const MoeParams& p) { return make_rsrc(p.y, p.y_bytes); }
+
 struct RowTile {
   int e, r0, nrows;
 };
 __device__ __forceinline__ RowTile load_rowtile(const MoeParams& p, int rt) {
-  const uint32_t* q = reinterpret_cast<const uint32_t*>(p.rt_info) + 4 * rt;
+  const u32x4_t v = co_ld128(r_rtinfo(p), (uint32_t)rt * 16u);
   RowTile r;
-  r.e = (int)ld_relaxed(q + 0);
-  r.r0 = (int)ld_relaxed(q + 1);
-  r.nrows = (int)ld_relaxed(q + 2);
+  r.e = (int)v.x;
+  r.r0 = (int)v.y;
+  r.nrows = (int)v.z;
   return r;
 }
 
@@ -122,6 +142,25 @@ __device__ __forceinline__ void dbg_task(const MoeParams& p, int type) {
   if (p.debug && threadIdx.x == 0) atomicAdd(p.debug + 2 * p.E + (type - 1), 1);
 }
 
+// Optional per-task trace (thread 0): wall-clock ticks before the wait,
+// after it, after the task body, and after the notifies.
+__device__ __forceinline__ void trace_task(const MoeParams& p, int type, int a, int b, uint64_t tw,
+                                           uint64_t ts, uint64_t tb) {
+  if (!p.trace || threadIdx.x != 0) return;
+  const uint64_t te = now_ticks();
+  const uint32_t r = atomicAdd(p.trace, 1u);
+  if (r >= p.trace_records) return;
+  uint32_t* q = p.trace + 16 + 8 * (size_t)r;
+  q[0] = blockIdx.x | ((uint32_t)type << 24);
+  q[1] = (uint32_t)a;
+  q[2] = (uint32_t)b;
+  q[3] = (uint32_t)tw;
+  q[4] = (uint32_t)(tw >> 32);
+  q[5] = (uint32_t)ts;
+  q[6] = (uint32_t)tb;
+  q[7] = (uint32_t)te;
+}
+
 // ===================================================== task bodies ==========
 // R: router logits, L[t, e] = sum_h x[t, h] * wr[e, h] (+ b[e]).  Wave w of
 // the workgroup owns expert e = et*4 + w; lane l owns the 8-element chunks
@@ -129,27 +168,48 @@ __device__ __forceinline__ void dbg_task(const MoeParams& p, int type) {
 // order with fused multiply-adds; the 64 lane sums are combined by a halving
 // xor butterfly whose lane-0 result equals the tree acc[l] += acc[l + s],
 // s = 32..1.  This fixed order is what makes the top-k decision
-// reproducible bit for bit.
+// reproducible bit for bit.  Loads of four chunks per lane are issued ahead
+// of their arithmetic.
 __device__ void task_router(const MoeParams& p, const Ctx& c, int tt, int et) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int e = et * kRouterE + wv;
   if (e >= c.E) return;
   const int t0 = tt * kRouterT;
+  const int ntok = min(kRouterT, c.T - t0);
   float acc[kRouterT];
 #pragma unroll
   for (int r = 0; r < kRouterT; ++r) acc[r] = 0.0f;
   const int nchunk = c.H >> 3;
   const uint16_t* wrow = p.wr + (size_t)e * c.H;
-  for (int ch = lane; ch < nchunk; ch += 64) {
-    float wf[8];
-    unpack8(ld4(wrow + ch * 8), wf);
+  const uint16_t* xrow = p.x + (size_t)t0 * c.H;
+  constexpr int U = 4;
+  for (int c0 = lane; c0 < nchunk; c0 += 64 * U) {
+    u32x4_t wv4[U], xv4[U][kRouterT];
 #pragma unroll
-    for (int r = 0; r < kRouterT; ++r) {
-      if (t0 + r < c.T) {
-        float xf[8];
-        unpack8(ld4(p.x + (size_t)(t0 + r) * c.H + ch * 8), xf);
+    for (int u = 0; u < U; ++u) {
+      const int ch = c0 + 64 * u;
+      if (ch < nchunk) {
+        wv4[u] = ld4(wrow + ch * 8);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[r] = __builtin_fmaf(xf[q], wf[q], acc[r]);
+        for (int r = 0; r < kRouterT; ++r)
+          if (r < ntok) xv4[u][r] = ld4(xrow + (size_t)r * c.H + ch * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ch = c0 + 64 * u;
+      if (ch < nchunk) {
+        float wf[8];
+        unpack8(wv4[u], wf);
+#pragma unroll
+        for (int r = 0; r < kRouterT; ++r) {
+          if (r < ntok) {
+            float xf[8];
+            unpack8(xv4[u][r], xf);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[r] = __builtin_fmaf(xf[q], wf[q], acc[r]);
+          }
+        }
       }
     }
   }
@@ -159,13 +219,13 @@ __device__ void task_router(const MoeParams& p, const Ctx& c, int tt, int et) {
     for (int s = 32; s >= 1; s >>= 1) acc[r] = acc[r] + __shfl_xor(acc[r], s);
   }
   if (lane == 0) {
+    const rsrc_t rl = r_logits(p);
 #pragma unroll
     for (int r = 0; r < kRouterT; ++r) {
-      const int t = t0 + r;
-      if (t < c.T) {
+      if (r < ntok) {
         float v = acc[r];
         if (p.has_bias) v = v + p.br[e];
-        p.logits[(size_t)t * c.E + e] = v;
+        co_stf(rl, (uint32_t)((t0 + r) * c.E + e) * 4u, v);
       }
     }
   }
@@ -182,7 +242,7 @@ __device__ void task_topk(const MoeParams& p, const Ctx& c, int tt) {
   const int t = tt * kRouterT + wv;
   if (t >= c.T) return;
   const float NEG_INF = -__builtin_inff();
-  const float* L = p.logits + (size_t)t * c.E;
+  const rsrc_t rl = r_logits(p);
   float v[4];
   bool bad = false;
 #pragma unroll
@@ -190,7 +250,7 @@ __device__ void task_topk(const MoeParams& p, const Ctx& c, int tt) {
     const int e = lane + 64 * j;
     float x = NEG_INF;
     if (e < c.E) {
-      x = L[e];
+      x = co_ldf(rl, (uint32_t)(t * c.E + e) * 4u);
       if (x != x) { bad = true; x = NEG_INF; }
     }
     v[j] = x;
@@ -228,8 +288,9 @@ __device__ void task_topk(const MoeParams& p, const Ctx& c, int tt) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) part = part + __shfl_xor(part, s);
   if (lane < c.k) {
-    p.ids[(size_t)t * c.k + lane] = my_e;
-    p.topw[(size_t)t * c.k + lane] = expf(my_v - v0) / part;
+    const uint32_t off = (uint32_t)(t * c.k + lane) * 4u;
+    co_st32(r_ids(p), off, (uint32_t)my_e);
+    co_stf(r_topw(p), off, expf(my_v - v0) / part);
   }
 }
 
@@ -270,10 +331,11 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   int* iptr = cnt + 260;
   int* tptr = iptr + 260;
   int* tmp = tptr + 260;
+  const rsrc_t rids = r_ids(p);
   for (int i = tid; i < E * W; i += kThreads) bits[i] = 0u;
   __syncthreads();
   for (int f = tid; f < n; f += kThreads) {
-    const int e = p.ids[f];
+    const int e = (int)co_ld32(rids, (uint32_t)f * 4u);
     const int t = f / k;
     atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
   }
@@ -292,54 +354,59 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   int tot_rows = 0, tot_tiles = 0;
   const int ex = block_excl_scan(my, tmp, &tot_rows);
   const int ext = block_excl_scan(mytiles, tmp + 8, &tot_tiles);
+  const rsrc_t rc = r_counts(p), ri = r_indptr(p), rtp = r_tptr(p);
   if (tid < E) {
     iptr[tid] = ex;
     tptr[tid] = ext;
-    p.counts[tid] = my;
-    p.indptr[tid] = ex;
-    p.tile_indptr[tid] = ext;
+    co_st32(rc, (uint32_t)tid * 4u, (uint32_t)my);
+    co_st32(ri, (uint32_t)tid * 4u, (uint32_t)ex);
+    co_st32(rtp, (uint32_t)tid * 4u, (uint32_t)ext);
   }
   if (tid == 0) {
     iptr[E] = tot_rows;
     tptr[E] = tot_tiles;
-    p.indptr[E] = tot_rows;
-    p.tile_indptr[E] = tot_tiles;
-    sig_put(p.meta + M_NRT, (uint32_t)tot_tiles);
+    co_st32(ri, (uint32_t)E * 4u, (uint32_t)tot_rows);
+    co_st32(rtp, (uint32_t)E * 4u, (uint32_t)tot_tiles);
+    st_relaxed(p.meta + M_NRT, (uint32_t)tot_tiles);
   }
   __syncthreads();
+  const rsrc_t rs = r_slot(p), rp = r_perm(p);
   for (int f = tid; f < n; f += kThreads) {
-    const int e = p.ids[f];
+    const int e = (int)co_ld32(rids, (uint32_t)f * 4u);
     const int t = f / k;
     const int w = t >> 5, b = t & 31;
     const int s = iptr[e] + pre[e * W + w] + __popc(bits[e * W + w] & ((1u << b) - 1u));
-    p.slot[f] = s;
-    p.perm[s] = f;
+    co_st32(rs, (uint32_t)f * 4u, (uint32_t)s);
+    co_st32(rp, (uint32_t)s * 4u, (uint32_t)f);
   }
+  const rsrc_t rr = r_rtinfo(p);
   for (int e = tid; e < E; e += kThreads) {
     const int ce = cnt[e];
     for (int mt = 0; mt * kBM < ce; ++mt) {
-      int* q = p.rt_info + 4 * (tptr[e] + mt);
-      q[0] = e;
-      q[1] = iptr[e] + mt * kBM;
-      q[2] = min(kBM, ce - mt * kBM);
-      q[3] = 0;
+      u32x4_t q;
+      q.x = (uint32_t)e;
+      q.y = (uint32_t)(iptr[e] + mt * kBM);
+      q.z = (uint32_t)min(kBM, ce - mt * kBM);
+      q.w = 0u;
+      co_st128(rr, (uint32_t)(tptr[e] + mt) * 16u, q);
     }
   }
 }
 
 // D: copy every routed row of the task's tokens into expert-grouped order,
-// Xp[slot[t*k+j], :] = X[t, :] (16-byte coalesced chunks).
+// Xp[slot[t*k+j], :] = X[t, :] (16-byte chunks).
 __device__ void task_dispatch_copy(const MoeParams& p, const Ctx& c, int dt) {
   const int t0 = dt * kDispatchT;
   const int ntok = min(kDispatchT, c.T - t0);
   const int rows = ntok * c.k;
   const int cpr = c.H >> 3;
+  const rsrc_t rs = r_slot(p), rx = r_xp(p);
   for (int i = threadIdx.x; i < rows * cpr; i += kThreads) {
     const int r = i / cpr, ch = i - r * cpr;
     const int f = t0 * c.k + r;
     const int t = t0 + r / c.k;
-    const int s = p.slot[f];
-    st4(p.xp + (size_t)s * c.H + ch * 8, ld4(p.x + (size_t)t * c.H + ch * 8));
+    const int s = (int)co_ld32(rs, (uint32_t)f * 4u);
+    co_st128(rx, (uint32_t)((size_t)s * c.H + ch * 8) * 2u, ld4(p.x + (size_t)t * c.H + ch * 8));
   }
 }
 
@@ -356,7 +423,8 @@ __device__ void task_g1(const MoeParams& p, const Ctx& c, int rt, int nt, float*
   const int kw = H >> 2;
   const int nsteps = kw >> 5;
   const bool valid = m < tile.nrows;
-  const uint16_t* pa = p.xp + (size_t)(tile.r0 + (valid ? m : 0)) * H + wv * kw + kg * 8;
+  const rsrc_t rx = r_xp(p);
+  const uint32_t aoff = (uint32_t)(((size_t)(tile.r0 + (valid ? m : 0)) * H + wv * kw + kg * 8) * 2);
   const uint16_t* pg = p.w13 + ((size_t)tile.e * 2 * I + (size_t)nt * kBN1 + m) * H + wv * kw + kg * 8;
   const uint16_t* pu = pg + (size_t)I * H;
   f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
@@ -367,7 +435,7 @@ __device__ void task_g1(const MoeParams& p, const Ctx& c, int rt, int nt, float*
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u < nsteps) {
-        a[u] = valid ? ld4(pa + (s0 + u) * 32) : zero;
+        a[u] = valid ? co_ld128(rx, aoff + (uint32_t)(s0 + u) * 64u) : zero;
         bg[u] = ld4(pg + (s0 + u) * 32);
         bu[u] = ld4(pu + (s0 + u) * 32);
       }
@@ -380,7 +448,7 @@ __device__ void task_g1(const MoeParams& p, const Ctx& c, int rt, int nt, float*
       }
     }
   }
-  // cross-wave reduction: red[w][0 = gate, 1 = up][lane * 4 + i]; the
+  // cross-wave reduction: red[w][0 = gate, 1 = up][lane * 4 + i]; the first
   // barrier keeps the previous task's readers of `red` ahead of these writes
   __syncthreads();
 #pragma unroll
@@ -399,9 +467,15 @@ __device__ void task_g1(const MoeParams& p, const Ctx& c, int rt, int nt, float*
   // element (lane', i) of the 16x16 MFMA result: row 4*(lane'/16) + i, column lane' % 16
   const int ol = tid >> 2, oi = tid & 3;
   const int row = 4 * (ol >> 4) + oi, col = ol & 15;
-  if (row < tile.nrows) {
-    const float h = g / (1.0f + __expf(-g)) * u;
-    p.hh[(size_t)(tile.r0 + row) * I + nt * kBN1 + col] = (uint16_t)f2bf(h);
+  uint16_t* stage = reinterpret_cast<uint16_t*>(red + 4096);  // [16 rows][16 cols] bf16
+  stage[row * 16 + col] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u);
+  __syncthreads();
+  if (tid < 32) {
+    const int r = tid >> 1, half = tid & 1;
+    if (r < tile.nrows) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * 16 + half * 8);
+      co_st128(r_hh(p), (uint32_t)(((size_t)(tile.r0 + r) * I + nt * kBN1 + half * 8) * 2), v);
+    }
   }
 }
 
@@ -415,7 +489,8 @@ __device__ void task_g2(const MoeParams& p, const Ctx& c, int rt, int nt2, float
   const int kw = I >> 2;
   const int nsteps = kw >> 5;
   const bool valid = m < tile.nrows;
-  const uint16_t* pa = p.hh + (size_t)(tile.r0 + (valid ? m : 0)) * I + wv * kw + kg * 8;
+  const rsrc_t rh = r_hh(p);
+  const uint32_t aoff = (uint32_t)(((size_t)(tile.r0 + (valid ? m : 0)) * I + wv * kw + kg * 8) * 2);
   const uint16_t* pb = p.w2 + ((size_t)tile.e * H + (size_t)nt2 * kBN2 + m) * I + wv * kw + kg * 8;
   const size_t cbs = (size_t)16 * I;  // next 16-column block of Wd
   f32x4_t acc[4];
@@ -428,7 +503,7 @@ __device__ void task_g2(const MoeParams& p, const Ctx& c, int rt, int nt2, float
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u < nsteps) {
-        a[u] = valid ? ld4(pa + (s0 + u) * 32) : zero;
+        a[u] = valid ? co_ld128(rh, aoff + (uint32_t)(s0 + u) * 64u) : zero;
 #pragma unroll
         for (int b = 0; b < 4; ++b) bb[u][b] = ld4(pb + b * cbs + (s0 + u) * 32);
       }
@@ -451,13 +526,21 @@ __device__ void task_g2(const MoeParams& p, const Ctx& c, int rt, int nt2, float
   const int tid = threadIdx.x;
   const int ol = tid >> 2, oi = tid & 3;
   const int row = 4 * (ol >> 4) + oi, col = ol & 15;
+  uint16_t* stage = reinterpret_cast<uint16_t*>(red + 4096);  // [16 rows][64 cols] bf16
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     float y = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) y += red[(w * 4 + b) * 256 + tid];
-    if (row < tile.nrows)
-      p.y[(size_t)(tile.r0 + row) * H + nt2 * kBN2 + b * 16 + col] = (uint16_t)f2bf(y);
+    stage[row * 64 + b * 16 + col] = (uint16_t)f2bf(y);
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const int r = tid >> 3, q = tid & 7;
+    if (r < tile.nrows) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * 64 + q * 8);
+      co_st128(r_y(p), (uint32_t)(((size_t)(tile.r0 + r) * H + nt2 * kBN2 + q * 8) * 2), v);
+    }
   }
 }
 
@@ -466,15 +549,17 @@ __device__ void task_combine(const MoeParams& p, const Ctx& c, int ct) {
   const int t0 = ct * kCombineT;
   const int ntok = min(kCombineT, c.T - t0);
   const int cpr = c.H >> 3;
+  const rsrc_t rw = r_topw(p), rs = r_slot(p), ry = r_y(p);
   for (int i = threadIdx.x; i < ntok * cpr; i += kThreads) {
     const int r = i / cpr, ch = i - r * cpr;
     const int t = t0 + r;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < c.k; ++j) {
-      const float wj = p.topw[(size_t)t * c.k + j];
-      const int s = p.slot[(size_t)t * c.k + j];
+      const uint32_t fo = (uint32_t)(t * c.k + j) * 4u;
+      const float wj = co_ldf(rw, fo);
+      const int s = (int)co_ld32(rs, fo);
       float yf[8];
-      unpack8(ld4(p.y + (size_t)s * c.H + ch * 8), yf);
+      unpack8(co_ld128(ry, (uint32_t)(((size_t)s * c.H + ch * 8) * 2)), yf);
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj, yf[q], acc[q]);
     }
@@ -498,7 +583,7 @@ __device__ __forceinline__ uint32_t ctile_target(const Ctx& c, int ct) {
 
 // Notify one event element; returns true if this notify completed it.
 __device__ __forceinline__ bool notify1(const Ctx& c, uint32_t* ev, uint32_t target) {
-  const uint32_t old = add_acqrel(ev, 1u);
+  const uint32_t old = add_relaxed(ev, 1u);
   if (old + 1u > target) or_relaxed(c.status, ST_OVER_NOTIFY | ST_ABORT);
   return old + 1u == target;
 }
@@ -512,6 +597,9 @@ __device__ __forceinline__ int64_t q_reserve(const MoeParams& p, const Ctx& c, i
   }
   return base;
 }
+__device__ __forceinline__ void q_put(const Ctx& c, int64_t slot, uint64_t desc) {
+  xchg_relaxed64(c.queue + slot, desc);
+}
 
 template <int MODE>
 __device__ void after_router(const MoeParams& p, const Ctx& c, int tt) {
@@ -520,7 +608,7 @@ __device__ void after_router(const MoeParams& p, const Ctx& c, int tt) {
     if (threadIdx.x == 0) {
       if (notify1(c, ev_logit(p, c) + tt, (uint32_t)c.nET) && MODE == MODE_DYNAMIC) {
         const int64_t q = q_reserve(p, c, 1);
-        if (q >= 0) sig_put64(c.queue + q, make_desc(TT_K, tt, 0));
+        if (q >= 0) q_put(c, q, make_desc(TT_K, tt, 0));
       }
     }
   }
@@ -533,7 +621,7 @@ __device__ void after_topk(const MoeParams& p, const Ctx& c) {
     if (threadIdx.x == 0) {
       if (notify1(c, c.set + W_EV_ROUTE, (uint32_t)c.nK) && MODE == MODE_DYNAMIC) {
         const int64_t q = q_reserve(p, c, 1);
-        if (q >= 0) sig_put64(c.queue + q, make_desc(TT_S, 0, 0));
+        if (q >= 0) q_put(c, q, make_desc(TT_S, 0, 0));
       }
     }
   }
@@ -547,14 +635,13 @@ __device__ void after_scan(const MoeParams& p, const Ctx& c, Shared& sh) {
       if (threadIdx.x == 0) {
         const uint32_t nrt = ld_relaxed(p.meta + M_NRT);
         const uint32_t total = (uint32_t)(c.nR + c.nK + 1 + c.nD + c.nC) + nrt * (uint32_t)(c.nN1 + c.nN2);
-        sig_put(c.set + W_TOTAL, total);
+        xchg_relaxed(c.set + W_TOTAL, total);
         sh.base = (int)q_reserve(p, c, c.nD);
       }
       __syncthreads();
       const int base = sh.base;
       if (base >= 0)
-        for (int i = threadIdx.x; i < c.nD; i += kThreads)
-          sig_put64(c.queue + base + i, make_desc(TT_D, i, 0));
+        for (int i = threadIdx.x; i < c.nD; i += kThreads) q_put(c, base + i, make_desc(TT_D, i, 0));
       __syncthreads();
     } else {
       if (threadIdx.x == 0) notify1(c, c.set + W_EV_SCAN, 1u);
@@ -572,8 +659,8 @@ __device__ void after_dispatch(const MoeParams& p, const Ctx& c, int dt, Shared&
   __syncthreads();
   if (threadIdx.x < rows) {
     const int f = t0 * c.k + threadIdx.x;
-    const int e = p.ids[f];
-    const uint32_t target = (uint32_t)p.counts[e];
+    const int e = (int)co_ld32(r_ids(p), (uint32_t)f * 4u);
+    const uint32_t target = co_ld32(r_counts(p), (uint32_t)e * 4u);
     const bool done = notify1(c, ev_exp(p, c) + e, target);
     if (p.debug) {
       atomicAdd(p.debug + e, 1);
@@ -586,11 +673,12 @@ __device__ void after_dispatch(const MoeParams& p, const Ctx& c, int dt, Shared&
     const int n = sh.n;
     if (n == 0) return;
     if (threadIdx.x == 0) {
+      const rsrc_t rtp = r_tptr(p);
       int acc = 0;
       for (int i = 0; i < n; ++i) {
         sh.pref[i] = acc;
         const int e = sh.list[i];
-        acc += (p.tile_indptr[e + 1] - p.tile_indptr[e]) * c.nN1;
+        acc += ((int)co_ld32(rtp, (uint32_t)(e + 1) * 4u) - (int)co_ld32(rtp, (uint32_t)e * 4u)) * c.nN1;
       }
       sh.pref[n] = acc;
       sh.total = acc;
@@ -599,12 +687,13 @@ __device__ void after_dispatch(const MoeParams& p, const Ctx& c, int dt, Shared&
     __syncthreads();
     const int base = sh.base, total = sh.total;
     if (base >= 0) {
+      const rsrc_t rtp = r_tptr(p);
       for (int i = threadIdx.x; i < total; i += kThreads) {
         int j = 0;
-        while (i >= sh.pref[j + 1]) ++j;
+        while (j + 1 < n && i >= sh.pref[j + 1]) ++j;
         const int li = i - sh.pref[j];
-        const int rt = p.tile_indptr[sh.list[j]] + li / c.nN1;
-        sig_put64(c.queue + base + i, make_desc(TT_G1, rt, li % c.nN1));
+        const int rt = (int)co_ld32(rtp, (uint32_t)sh.list[j] * 4u) + li / c.nN1;
+        q_put(c, base + i, make_desc(TT_G1, rt, li % c.nN1));
       }
     }
     __syncthreads();
@@ -624,8 +713,7 @@ __device__ void after_g1(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
     __syncthreads();
     const int base = sh.base;
     if (base >= 0)
-      for (int i = threadIdx.x; i < c.nN2; i += kThreads)
-        sig_put64(c.queue + base + i, make_desc(TT_G2, rt, i));
+      for (int i = threadIdx.x; i < c.nN2; i += kThreads) q_put(c, base + i, make_desc(TT_G2, rt, i));
     __syncthreads();
   }
 }
@@ -638,7 +726,7 @@ __device__ void after_g2(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
   if (threadIdx.x == 0) sh.n = 0;
   __syncthreads();
   if (threadIdx.x < tile.nrows) {
-    const int f = p.perm[tile.r0 + threadIdx.x];
+    const int f = (int)co_ld32(r_perm(p), (uint32_t)(tile.r0 + threadIdx.x) * 4u);
     const int ct = (f / c.k) / kCombineT;
     if (notify1(c, ev_c(p, c) + ct, ctile_target(c, ct)) && MODE == MODE_DYNAMIC)
       sh.list[atomicAdd(&sh.n, 1)] = ct;
@@ -650,8 +738,7 @@ __device__ void after_g2(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
     if (threadIdx.x == 0) sh.base = (int)q_reserve(p, c, n);
     __syncthreads();
     const int base = sh.base;
-    if (base >= 0 && threadIdx.x < n)
-      sig_put64(c.queue + base + threadIdx.x, make_desc(TT_C, sh.list[threadIdx.x], 0));
+    if (base >= 0 && threadIdx.x < n) q_put(c, base + threadIdx.x, make_desc(TT_C, sh.list[threadIdx.x], 0));
     __syncthreads();
   }
 }
@@ -667,10 +754,10 @@ __device__ bool grid_barrier(const Ctx& c) {
     uint32_t* cnt = c.set + W_BAR_COUNT;
     uint32_t* gen = c.set + W_BAR_GEN;
     const uint32_t g0 = ld_relaxed(gen);
-    const uint32_t old = add_acqrel(cnt, 1u);
+    const uint32_t old = add_relaxed(cnt, 1u);
     if (old == gridDim.x - 1u) {
-      sig_put(cnt, 0u);
-      add_acqrel(gen, 1u);
+      xchg_relaxed(cnt, 0u);
+      add_relaxed(gen, 1u);
     } else {
       const uint64_t t0 = now_ticks();
       for (uint32_t spins = 1; ld_relaxed(gen) == g0; ++spins) {
@@ -683,7 +770,6 @@ __device__ bool grid_barrier(const Ctx& c) {
     }
   }
   fail = __syncthreads_or(fail);
-  fence_acquire();
   return fail == 0;
 }
 
@@ -698,35 +784,52 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
   const int G = gridDim.x, w = blockIdx.x;
   float* red = reinterpret_cast<float*>(smem);
   constexpr bool EV = (MODE == MODE_STATIC);
+  const bool tr = p.trace != nullptr;
+  uint64_t tw = 0, ts = 0, tb = 0;
   int64_t off = 0;
   for (int i = first_of(w, off, G); i < c.nR; i += G) {
+    if (tr) tw = ts = now_ticks();
     task_router(p, c, i / c.nET, i % c.nET);
+    if (tr) tb = now_ticks();
     dbg_task(p, TT_R);
     after_router<MODE>(p, c, i / c.nET);
+    trace_task(p, TT_R, i / c.nET, i % c.nET, tw, ts, tb);
   }
   off += c.nR;
   if (!EV && !grid_barrier(c)) return;
   for (int i = first_of(w, off, G); i < c.nK; i += G) {
+    if (tr) tw = now_ticks();
     if (EV && !wg_wait(ev_logit(p, c) + i, (uint32_t)c.nET, c.status, c.budget)) return;
+    if (tr) ts = now_ticks();
     task_topk(p, c, i);
+    if (tr) tb = now_ticks();
     dbg_task(p, TT_K);
     after_topk<MODE>(p, c);
+    trace_task(p, TT_K, i, 0, tw, ts, tb);
   }
   off += c.nK;
   if (!EV && !grid_barrier(c)) return;
   if (first_of(w, off, G) == 0) {
+    if (tr) tw = now_ticks();
     if (EV && !wg_wait(c.set + W_EV_ROUTE, (uint32_t)c.nK, c.status, c.budget)) return;
+    if (tr) ts = now_ticks();
     task_scan(p, c, smem);
+    if (tr) tb = now_ticks();
     dbg_task(p, TT_S);
     after_scan<MODE>(p, c, sh);
+    trace_task(p, TT_S, 0, 0, tw, ts, tb);
   }
   off += 1;
   if (!EV && !grid_barrier(c)) return;
   for (int i = first_of(w, off, G); i < c.nD; i += G) {
+    if (tr) tw = now_ticks();
     if (EV && !wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;
+    if (tr) ts = now_ticks();
     task_dispatch_copy(p, c, i);
+    if (tr) tb = now_ticks();
     dbg_task(p, TT_D);
     after_dispatch<MODE>(p, c, i, sh);
+    trace_task(p, TT_D, i, 0, tw, ts, tb);
   }
   off += c.nD;
   if (EV) {
@@ -738,30 +841,42 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
   const int nG1 = nrt * c.nN1, nG2 = nrt * c.nN2;
   for (int i = first_of(w, off, G); i < nG1; i += G) {
     const int rt = i / c.nN1;
+    if (tr) tw = now_ticks();
     if (EV) {
       const RowTile tile = load_rowtile(p, rt);
-      const uint32_t target = ld_relaxed(reinterpret_cast<const uint32_t*>(p.counts) + tile.e);
+      const uint32_t target = co_ld32(r_counts(p), (uint32_t)tile.e * 4u);
       if (!wg_wait(ev_exp(p, c) + tile.e, target, c.status, c.budget)) return;
     }
+    if (tr) ts = now_ticks();
     task_g1(p, c, rt, i % c.nN1, red);
+    if (tr) tb = now_ticks();
     dbg_task(p, TT_G1);
     after_g1<MODE>(p, c, rt, sh);
+    trace_task(p, TT_G1, rt, i % c.nN1, tw, ts, tb);
   }
   off += nG1;
   if (!EV && !grid_barrier(c)) return;
   for (int i = first_of(w, off, G); i < nG2; i += G) {
     const int rt = i / c.nN2;
+    if (tr) tw = now_ticks();
     if (EV && !wg_wait(ev_h(p, c) + rt, (uint32_t)c.nN1, c.status, c.budget)) return;
+    if (tr) ts = now_ticks();
     task_g2(p, c, rt, i % c.nN2, red);
+    if (tr) tb = now_ticks();
     dbg_task(p, TT_G2);
     after_g2<MODE>(p, c, rt, sh);
+    trace_task(p, TT_G2, rt, i % c.nN2, tw, ts, tb);
   }
   off += nG2;
   if (!EV && !grid_barrier(c)) return;
   for (int i = first_of(w, off, G); i < c.nC; i += G) {
+    if (tr) tw = now_ticks();
     if (EV && !wg_wait(ev_c(p, c) + i, ctile_target(c, i), c.status, c.budget)) return;
+    if (tr) ts = now_ticks();
     task_combine(p, c, i);
+    if (tr) tb = now_ticks();
     dbg_task(p, TT_C);
+    trace_task(p, TT_C, i, 0, tw, ts, tb);
   }
 }
 
@@ -772,7 +887,10 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
 // never wait on events here: they are only pushed when ready.
 __device__ void run_dynamic(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh) {
   float* red = reinterpret_cast<float*>(smem);
+  const bool tr = p.trace != nullptr;
+  uint64_t tw = 0, ts = 0, tb = 0;
   for (;;) {
+    if (tr) tw = now_ticks();
     if (threadIdx.x == 0) {
       uint64_t d = kDescExit;
       const uint32_t idx = add_relaxed(c.set + W_HEAD, 1u);
@@ -799,44 +917,58 @@ __device__ void run_dynamic(const MoeParams& p, const Ctx& c, uint8_t* smem, Sha
     }
     __syncthreads();
     const uint64_t d = sh.desc;
-    fence_acquire();
     __syncthreads();
     if (d == kDescExit) return;
+    if (tr) ts = now_ticks();
     const int a = (int)desc_a(d), b = (int)desc_b(d);
     switch (desc_type(d)) {
       case TT_R:
         task_router(p, c, a, b);
+        if (tr) tb = now_ticks();
         dbg_task(p, TT_R);
         after_router<MODE_DYNAMIC>(p, c, a);
+        trace_task(p, TT_R, a, b, tw, ts, tb);
         break;
       case TT_K:
         task_topk(p, c, a);
+        if (tr) tb = now_ticks();
         dbg_task(p, TT_K);
         after_topk<MODE_DYNAMIC>(p, c);
+        trace_task(p, TT_K, a, b, tw, ts, tb);
         break;
       case TT_S:
         task_scan(p, c, smem);
+        if (tr) tb = now_ticks();
         dbg_task(p, TT_S);
         after_scan<MODE_DYNAMIC>(p, c, sh);
+        trace_task(p, TT_S, a, b, tw, ts, tb);
         break;
       case TT_D:
         task_dispatch_copy(p, c, a);
+        if (tr) tb = now_ticks();
         dbg_task(p, TT_D);
         after_dispatch<MODE_DYNAMIC>(p, c, a, sh);
+        trace_task(p, TT_D, a, b, tw, ts, tb);
         break;
       case TT_G1:
         task_g1(p, c, a, b, red);
+        if (tr) tb = now_ticks();
         dbg_task(p, TT_G1);
         after_g1<MODE_DYNAMIC>(p, c, a, sh);
+        trace_task(p, TT_G1, a, b, tw, ts, tb);
         break;
       case TT_G2:
         task_g2(p, c, a, b, red);
+        if (tr) tb = now_ticks();
         dbg_task(p, TT_G2);
         after_g2<MODE_DYNAMIC>(p, c, a, sh);
+        trace_task(p, TT_G2, a, b, tw, ts, tb);
         break;
       case TT_C:
         task_combine(p, c, a);
+        if (tr) tb = now_ticks();
         dbg_task(p, TT_C);
+        trace_task(p, TT_C, a, b, tw, ts, tb);
         break;
       default:
         or_relaxed(c.status, ST_QUEUE_OVERFLOW | ST_ABORT);
@@ -872,8 +1004,8 @@ __global__ void __launch_bounds__(kThreads) moe_persistent(MoeParams p) {
   if (threadIdx.x == 0) {
     const uint32_t st = ld_relaxed(c.status) & ~ST_ABORT;
     if (st) or_relaxed(p.ctrl + C_REPORT, st);
-    const uint32_t old = add_acqrel(set + W_DONE, 1u);
-    if (old == gridDim.x - 1u) sig_put(p.ctrl + C_EPOCH, epoch + 1u);
+    const uint32_t old = add_relaxed(set + W_DONE, 1u);
+    if (old == gridDim.x - 1u) xchg_relaxed(p.ctrl + C_EPOCH, epoch + 1u);
   }
 }
 
@@ -896,14 +1028,14 @@ __global__ void __launch_bounds__(kThreads) kbk_dispatch(MoeParams p) {
   task_dispatch_copy(p, c, blockIdx.x);
 }
 __global__ void __launch_bounds__(kThreads) kbk_g1(MoeParams p) {
-  __shared__ float red[4 * 2 * 256];
+  __shared__ float red[4 * 4 * 256 + 16 * 64 / 2];
   const Ctx c = make_ctx(p, nullptr);
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN1) return;
   task_g1(p, c, blockIdx.x / c.nN1, blockIdx.x % c.nN1, red);
 }
 __global__ void __launch_bounds__(kThreads) kbk_g2(MoeParams p) {
-  __shared__ float red[4 * 4 * 256];
+  __shared__ float red[4 * 4 * 256 + 16 * 64 / 2];
   const Ctx c = make_ctx(p, nullptr);
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN2) return;

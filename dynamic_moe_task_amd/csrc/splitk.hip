@@ -46,24 +46,30 @@ __device__ int block_sum_i32(int v, int* tmp) {
   return r;
 }
 
+// B crosses workgroups: written and read with device-coherent accesses
+__device__ __forceinline__ rsrc_t r_B(const SkParams& p) {
+  return make_rsrc(p.B, (uint32_t)((int64_t)p.n * p.nsplit * 4));
+}
+
 __device__ void sk_partial(const SkParams& p, int i, int j, int* tmp) {
   const int32_t* row = p.A + ((size_t)i * p.nsplit + j) * p.bk;
   int v = 0;
   for (int c = threadIdx.x; c < p.bk; c += kThreads) v += row[c];
   v = block_sum_i32(v, tmp);
-  if (threadIdx.x == 0) p.B[(size_t)i * p.nsplit + j] = v;
+  if (threadIdx.x == 0) co_st32(r_B(p), (uint32_t)(i * p.nsplit + j) * 4u, (uint32_t)v);
 }
 
 __device__ void sk_final(const SkParams& p, int i, int* tmp) {
+  const rsrc_t rb = r_B(p);
   int v = 0;
-  for (int j = threadIdx.x; j < p.nsplit; j += kThreads) v += p.B[(size_t)i * p.nsplit + j];
+  for (int j = threadIdx.x; j < p.nsplit; j += kThreads) v += (int)co_ld32(rb, (uint32_t)(i * p.nsplit + j) * 4u);
   v = block_sum_i32(v, tmp);
   if (threadIdx.x == 0) p.C[i] = v;
 }
 
 // notify event i; true if this notify released it
 __device__ __forceinline__ bool sk_notify(const SkParams& p, int i) {
-  const uint32_t old = add_acqrel(p.ev + i, 1u);
+  const uint32_t old = add_relaxed(p.ev + i, 1u);
   if (old + 1u > (uint32_t)p.nsplit) or_relaxed(p.ctl + SK_STATUS, ST_OVER_NOTIFY | ST_ABORT);
   return old + 1u == (uint32_t)p.nsplit;
 }
@@ -84,7 +90,7 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
     }
     for (int i = (w - nP % G + G) % G; i < p.n; i += G) {
       if (!wg_wait(p.ev + i, (uint32_t)p.nsplit, status, p.budget)) break;
-      if (threadIdx.x == 0) sig_put(p.ev + i, 0u);  // sole waiter: back to rest
+      if (threadIdx.x == 0) xchg_relaxed(p.ev + i, 0u);  // sole waiter: back to rest
       sk_final(p, i, tmp);
     }
   } else {
@@ -104,7 +110,7 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
             const uint64_t v = ld_relaxed64(p.queue + qi);
             if (v) {
               d = v;
-              sig_put64(p.queue + qi, 0ull);  // slot back to rest for the next launch
+              xchg_relaxed64(p.queue + qi, 0ull);  // slot back to rest for the next launch
               break;
             }
             if ((spins & 3u) == 0u) {
@@ -118,7 +124,6 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
       }
       __syncthreads();
       const uint64_t d = s_desc;
-      fence_acquire();
       __syncthreads();
       if (d == SK_EXIT) break;
       const int type = (int)(d >> 60);
@@ -129,26 +134,26 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
         if (threadIdx.x == 0 && sk_notify(p, a / p.nsplit)) {
           const uint32_t q = add_relaxed(p.ctl + SK_TAIL, 1u);
           if ((int64_t)q < p.q_cap)
-            sig_put64(p.queue + q, ((uint64_t)SK_FINAL << 60) | (uint64_t)(a / p.nsplit));
+            xchg_relaxed64(p.queue + q, ((uint64_t)SK_FINAL << 60) | (uint64_t)(a / p.nsplit));
           else
             or_relaxed(status, ST_QUEUE_OVERFLOW | ST_ABORT);
         }
       } else {
-        if (threadIdx.x == 0) sig_put(p.ev + a, 0u);
+        if (threadIdx.x == 0) xchg_relaxed(p.ev + a, 0u);
         sk_final(p, a, tmp);
       }
     }
   }
   wg_publish();
   if (threadIdx.x == 0) {
-    const uint32_t old = add_acqrel(p.ctl + SK_DONE, 1u);
+    const uint32_t old = add_relaxed(p.ctl + SK_DONE, 1u);
     if (old == (uint32_t)G - 1u) {
       const uint32_t st = ld_relaxed(status) & ~ST_ABORT;
       if (st) or_relaxed(p.ctl + SK_REPORT, st);
-      sig_put(status, 0u);
-      sig_put(p.ctl + SK_HEAD, 0u);
-      sig_put(p.ctl + SK_TAIL, 0u);
-      sig_put(p.ctl + SK_DONE, 0u);
+      xchg_relaxed(status, 0u);
+      xchg_relaxed(p.ctl + SK_HEAD, 0u);
+      xchg_relaxed(p.ctl + SK_TAIL, 0u);
+      xchg_relaxed(p.ctl + SK_DONE, 0u);
     }
   }
 }

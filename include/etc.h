@@ -175,7 +175,20 @@ typedef struct {
   size_t workspace_bytes;
   int32_t* debug;
   uint32_t watchdog_us;
+  uint32_t trace_records; /* capacity of `trace` in records (0 = no trace)  */
+  uint32_t* trace;        /* NULL, or ETC_TRACE_WORDS(trace_records) uint32,
+                             word 0 zeroed by the caller (see below)        */
 } etc_moe_args;
+
+/* Per-task trace, when etc_moe_args.trace is non-NULL (persistent schedules):
+ * word 0 counts records written (it may exceed the capacity; extra records
+ * are dropped); record r occupies words [16 + 8r, 16 + 8r + 8):
+ *   workgroup | task type << 24 (type 1..7 = R, K, S, D, G1, G2, C), task
+ *   index a, b, then wall-clock ticks: before the task's wait (low, high 32
+ *   bits), and the low 32 bits after the wait, after the task body, and after
+ *   its notifies.  Ticks are those of the device's constant wall clock
+ *   (etc_moe_info.wall_clock_khz).                                          */
+#define ETC_TRACE_WORDS(records) (16 + 8 * (size_t)(records))
 
 /* Debug counters (int32), when etc_moe_args.debug is non-NULL:
  *   [0, E)        notifies received by ev_exp[e]   (expected: counts[e])
@@ -194,6 +207,7 @@ typedef struct {
   int32_t grid;        /* persistent workgroups (0 before the first query)  */
   int32_t threads;     /* threads per workgroup                             */
   int32_t lds_bytes;   /* dynamic LDS per workgroup                         */
+  int32_t wall_clock_khz; /* rate of the clock the watchdog and trace read  */
 } etc_moe_info;
 
 /* Fill `info` for `desc` (host struct).  Queries the device for the grid.

@@ -99,7 +99,7 @@ def test_launch_validation_before_any_gpu_call():
     assert B.moe_layer_launch(d, 4, args, B.ETC_SCHED_STATIC, None) == B.ETC_ERR_INVALID
     assert "NULL" in B.etc_last_error()
     # misaligned pointer
-    args = B.MoeArgs(*([0x1000] * 13), 1 << 30, None, 0)
+    args = B.MoeArgs(*([0x1000] * 13), 1 << 30, None, 0, 0, None)
     args.x = 0x1002
     assert B.moe_layer_launch(d, 4, args, B.ETC_SCHED_STATIC, None) == B.ETC_ERR_INVALID
     assert "aligned" in B.etc_last_error()
@@ -130,6 +130,6 @@ def test_dynamic_schedule_is_switched_off_with_an_error():
     # the push/pop schedule is disabled until its GPU hang is understood: a
     # launch must fail loudly before touching the GPU, never fall back
     d = B.moe_desc(16, 2048, 128, 8, 768)
-    args = B.MoeArgs(*([0x1000] * 13), 1 << 30, None, 0)
+    args = B.MoeArgs(*([0x1000] * 13), 1 << 30, None, 0, 0, None)
     assert B.moe_layer_launch(d, 4, args, B.ETC_SCHED_DYNAMIC, None) == B.ETC_ERR_UNSUPPORTED
     assert "switched off" in B.etc_last_error()
