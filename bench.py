@@ -45,14 +45,41 @@ def parse():
                     help="HBM traffic per launch measured with rocprofv3 counters (JSON)")
     ap.add_argument("--only-sched", action="store_true", help="time only --sched (for profiling)")
     ap.add_argument("--trace", default="", help="write a per-task trace summary of each persistent "
-                    "schedule to this JSON file (one extra traced launch each, outside the timing)")
+                    "schedule to this JSON file (one extra traced launch each, outside the timing); the raw "
+                    "records go next to it as .npz")
+    ap.add_argument("--repeat", type=int, default=3, help="timing loops per schedule; the median is reported")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="calibration only: run a plain elementwise copy (read N MiB, write N MiB) --steps "
+                         "times and exit; its HBM counters scale the MoE kernel's")
     return ap.parse_args()
+
+
+def copy_calibration(mib, steps):
+    """A plain device copy of known size (torch.neg over bf16: reads and
+    writes `mib` MiB per launch), for scaling rocprofv3's FETCH_SIZE and
+    WRITE_SIZE readings to bytes."""
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.randn(n, device="cuda").to(torch.bfloat16)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        torch.neg(src, out=dst)
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / steps
+    nbytes = mib * (1 << 20)
+    print(json.dumps({"copy_read_bytes": nbytes, "copy_write_bytes": nbytes, "us_per_launch": round(us, 2),
+                      "GBps": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}))
 
 
 TASK_NAMES = {1: "R", 2: "K", 3: "S", 4: "D", 5: "G1", 6: "G2", 7: "C"}
 
 
-def trace_summary(bufs, T, sched, khz, stream_ptr, records=1 << 16):
+def trace_summary(bufs, T, sched, khz, stream_ptr, records=1 << 16, dump=None):
     """One traced launch: per task type, count, mean/max duration, mean
     wait, and the first start / last end in µs from the earliest wait."""
     import torch
@@ -62,6 +89,8 @@ def trace_summary(bufs, T, sched, khz, stream_ptr, records=1 << 16):
     B.check(B.etc_sync(stream_ptr))
     raw = tr.cpu().numpy().view(np.uint32)
     n = min(int(raw[0]), records)
+    if dump:
+        np.savez(dump, raw=raw[:16 + 8 * n], khz=khz)
     rec = raw[16:16 + 8 * n].reshape(n, 8).astype(np.int64)
     wg, typ = rec[:, 0] & 0xFFFFFF, rec[:, 0] >> 24
     tw = (rec[:, 4] << 32) | rec[:, 3]
@@ -157,6 +186,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
+    if a.copy_mib:
+        copy_calibration(a.copy_mib, a.steps)
+        return
     import torch
     from dynamic_moe_task_amd import binding as B
     from dynamic_moe_task_amd import workloads as wl
@@ -188,31 +220,40 @@ def main():
     alg_flops = wl.algorithmic_flops(shape, T)
 
     scheds = [a.sched] if a.only_sched else ["static", "barrier", "kbk"]
-    us = {}
-    for s in scheds:
-        steps = a.steps if s == a.sched else max(10, a.steps // 2)
-        us[s] = time_sched(bufs, T, s, steps, a.warmup, w13s, w2s, sp)
+    runs = {s: [] for s in scheds}
+    for _ in range(max(1, a.repeat)):  # interleave the schedules, then take medians
+        for s in scheds:
+            runs[s].append(time_sched(bufs, T, s, a.steps, a.warmup, w13s, w2s, sp))
+    us = {s: float(np.median(v)) for s, v in runs.items()}
     us_main = us[a.sched]
 
     achieved_gbs = alg_bytes / (us_main * 1e-6) / 1e9
+    # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by a
+    # copy kernel of known size); null unless taken on the current sources
     traffic = None
+    traffic_note = "no counter figures for this workload and schedule"
     if a.traffic and os.path.exists(a.traffic):
-        try:
-            tr = json.load(open(a.traffic))
-            key = f"{a.workload}/{a.sched}"
-            if key in tr:
-                traffic = tr[key]
-        except Exception:
-            traffic = None
+        from dynamic_moe_task_amd.profiling import kernel_source_digest
+        with open(a.traffic) as f:
+            tr = json.load(f).get(f"{a.workload}/{a.sched}")
+        if tr is not None:
+            if tr.get("source_digest") == kernel_source_digest():
+                traffic = tr["total_bytes"]
+                traffic_note = (f"fetch {tr['fetch_bytes']} B + write {tr['write_bytes']} B per launch "
+                                f"(scales {tr['fetch_scale']}, {tr['write_scale']})")
+            else:
+                traffic_note = "counters were taken on different kernel sources"
     roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": f"moe_persistent<{a.sched}>" if a.sched != "kbk" else "kbk_* (7 launches)",
-                "algorithmic_bytes": alg_bytes}
+                "algorithmic_bytes": alg_bytes, "traffic_note": traffic_note}
     mfma_frac = alg_flops / (us_main * 1e-6) / (BF16_PEAK_TFS * 1e12)
 
     if a.trace:
         info = B.moe_layer_info(desc)
-        summ = {s: trace_summary(bufs, T, s, info.wall_clock_khz, sp) for s in ("static", "barrier")}
+        base = os.path.splitext(a.trace)[0]
+        summ = {s: trace_summary(bufs, T, s, info.wall_clock_khz, sp, dump=f"{base}_{s}.npz")
+                for s in ("static", "barrier")}
         summ["grid"] = info.grid
         with open(a.trace, "w") as f:
             json.dump(summ, f, indent=1)
@@ -237,6 +278,7 @@ def main():
         "config": {"workload": shape.name, "T": T, "H": shape.H, "E": shape.E, "k": shape.k, "I": shape.I,
                    "schedule": a.sched, "weight_copies_rotated": R, "active_experts": n_act},
         "us_per_layer": {s: round(v, 2) for s, v in us.items()},
+        "us_per_layer_runs": {s: [round(x, 2) for x in v] for s, v in runs.items()},
         "mfma_frac_whole_layer": round(mfma_frac, 5),
         "roofline": roofline,
         "cpu_baseline": cpu,

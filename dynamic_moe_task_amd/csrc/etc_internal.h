@@ -25,7 +25,7 @@ constexpr int kRouterE = 4;     //         ... x experts (one expert per wave)
 constexpr int kBM = 16;         // grouped-GEMM row tile (one 16-row MFMA block)
 constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile
 constexpr int kBN2 = 64;        // G2: output columns per tile (4 MFMA column blocks)
-constexpr int kDispatchT = 2;   // D task: tokens per task
+constexpr int kDispatchT = 1;   // D task: tokens per task
 constexpr int kCombineT = 2;    // C task: tokens per task
 constexpr int kMaxK = 16;
 constexpr int kMaxE = 256;

@@ -136,6 +136,7 @@ struct Shared {
   int total;       // descriptors to write
   int list[kDispatchT * kMaxK + kBM];
   int pref[kDispatchT * kMaxK + kBM + 1];
+  int pairs[2 * kCombineT * kMaxK];  // D: slots; C: (weight, slot) pairs
 };
 
 __device__ __forceinline__ void dbg_task(const MoeParams& p, int type) {
@@ -395,18 +396,34 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
 
 // D: copy every routed row of the task's tokens into expert-grouped order,
 // Xp[slot[t*k+j], :] = X[t, :] (16-byte chunks).
-__device__ void task_dispatch_copy(const MoeParams& p, const Ctx& c, int dt) {
+__device__ void task_dispatch_copy(const MoeParams& p, const Ctx& c, int dt, int* s_slot) {
   const int t0 = dt * kDispatchT;
   const int ntok = min(kDispatchT, c.T - t0);
   const int rows = ntok * c.k;
   const int cpr = c.H >> 3;
-  const rsrc_t rs = r_slot(p), rx = r_xp(p);
-  for (int i = threadIdx.x; i < rows * cpr; i += kThreads) {
-    const int r = i / cpr, ch = i - r * cpr;
-    const int f = t0 * c.k + r;
-    const int t = t0 + r / c.k;
-    const int s = (int)co_ld32(rs, (uint32_t)f * 4u);
-    co_st128(rx, (uint32_t)((size_t)s * c.H + ch * 8) * 2u, ld4(p.x + (size_t)t * c.H + ch * 8));
+  const rsrc_t rx = r_xp(p);
+  if (threadIdx.x < rows) s_slot[threadIdx.x] = (int)co_ld32(r_slot(p), (uint32_t)(t0 * c.k + threadIdx.x) * 4u);
+  __syncthreads();
+  constexpr int U = 8;
+  const int items = rows * cpr;
+  for (int i0 = threadIdx.x; i0 < items; i0 += kThreads * U) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kThreads;
+      if (i < items) {
+        const int r = i / cpr, ch = i - r * cpr;
+        v[u] = ld4(p.x + (size_t)(t0 + r / c.k) * c.H + ch * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kThreads;
+      if (i < items) {
+        const int r = i / cpr, ch = i - r * cpr;
+        co_st128(rx, (uint32_t)((size_t)s_slot[r] * c.H + ch * 8) * 2u, v[u]);
+      }
+    }
   }
 }
 
@@ -415,8 +432,7 @@ __device__ void task_dispatch_copy(const MoeParams& p, const Ctx& c, int dt) {
 // accumulation; the 4 waves split K = H in quarters and reduce in LDS.  The
 // weight tile (2 x 16 rows x H) streams straight from HBM into registers;
 // rows past the expert's count are zero-filled, never loaded.
-__device__ void task_g1(const MoeParams& p, const Ctx& c, int rt, int nt, float* red) {
-  const RowTile tile = load_rowtile(p, rt);
+__device__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt, float* red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int m = lane & 15, kg = lane >> 4;
   const int H = c.H, I = c.I;
@@ -429,6 +445,8 @@ __device__ void task_g1(const MoeParams& p, const Ctx& c, int rt, int nt, float*
   const uint16_t* pu = pg + (size_t)I * H;
   f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+  // batches of 8 k-steps (24 loads of 16 bytes a lane in flight); two
+  // workgroups per CU overlap each other's batch boundaries
   constexpr int U = 8;
   for (int s0 = 0; s0 < nsteps; s0 += U) {
     u32x4_t a[U], bg[U], bu[U];
@@ -470,6 +488,8 @@ __device__ void task_g1(const MoeParams& p, const Ctx& c, int rt, int nt, float*
   uint16_t* stage = reinterpret_cast<uint16_t*>(red + 4096);  // [16 rows][16 cols] bf16
   stage[row * 16 + col] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u);
   __syncthreads();
+  // wave 0 alone writes the tile (16 rows x 32 bytes), so only wave 0 has
+  // stores to drain before the notify
   if (tid < 32) {
     const int r = tid >> 1, half = tid & 1;
     if (r < tile.nrows) {
@@ -481,8 +501,7 @@ __device__ void task_g1(const MoeParams& p, const Ctx& c, int rt, int nt, float*
 
 // G2: one 16-row tile times 64 output columns of Wd[e]: Y = bf16(Hmid Wd^T).
 // The 4 waves split K = I in quarters; each wave keeps 4 column blocks.
-__device__ void task_g2(const MoeParams& p, const Ctx& c, int rt, int nt2, float* red) {
-  const RowTile tile = load_rowtile(p, rt);
+__device__ void task_g2(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt2, float* red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int m = lane & 15, kg = lane >> 4;
   const int H = c.H, I = c.I;
@@ -497,7 +516,7 @@ __device__ void task_g2(const MoeParams& p, const Ctx& c, int rt, int nt2, float
 #pragma unroll
   for (int b = 0; b < 4; ++b) acc[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  constexpr int U = 4;
+  constexpr int U = 8;
   for (int s0 = 0; s0 < nsteps; s0 += U) {
     u32x4_t a[U], bb[U][4];
 #pragma unroll
@@ -535,33 +554,55 @@ __device__ void task_g2(const MoeParams& p, const Ctx& c, int rt, int nt2, float
     stage[row * 64 + b * 16 + col] = (uint16_t)f2bf(y);
   }
   __syncthreads();
-  if (tid < 128) {
-    const int r = tid >> 3, q = tid & 7;
-    if (r < tile.nrows) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * 64 + q * 8);
-      co_st128(r_y(p), (uint32_t)(((size_t)(tile.r0 + r) * H + nt2 * kBN2 + q * 8) * 2), v);
+  // wave 0 alone writes the tile (16 rows x 128 bytes, two chunks a lane)
+  if (tid < 64) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int idx = tid + 64 * h;
+      const int r = idx >> 3, q = idx & 7;
+      if (r < tile.nrows) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * 64 + q * 8);
+        co_st128(r_y(p), (uint32_t)(((size_t)(tile.r0 + r) * H + nt2 * kBN2 + q * 8) * 2), v);
+      }
     }
   }
 }
 
 // C: out[t, :] = bf16(sum_j w[t, j] * Y[slot[t*k+j], :]), fp32 in j order.
-__device__ void task_combine(const MoeParams& p, const Ctx& c, int ct) {
+// The task's (weight, slot) pairs are staged in LDS first; then each thread
+// issues the loads of all k expert rows of its chunk before the arithmetic.
+__device__ void task_combine(const MoeParams& p, const Ctx& c, int ct, int* s_pair) {
   const int t0 = ct * kCombineT;
   const int ntok = min(kCombineT, c.T - t0);
   const int cpr = c.H >> 3;
-  const rsrc_t rw = r_topw(p), rs = r_slot(p), ry = r_y(p);
+  const int k = c.k;
+  if (threadIdx.x < ntok * k) {
+    const uint32_t fo = (uint32_t)(t0 * k + threadIdx.x) * 4u;
+    s_pair[2 * threadIdx.x] = (int)co_ld32(r_topw(p), fo);
+    s_pair[2 * threadIdx.x + 1] = (int)co_ld32(r_slot(p), fo);
+  }
+  __syncthreads();
+  const rsrc_t ry = r_y(p);
   for (int i = threadIdx.x; i < ntok * cpr; i += kThreads) {
     const int r = i / cpr, ch = i - r * cpr;
     const int t = t0 + r;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < c.k; ++j) {
-      const uint32_t fo = (uint32_t)(t * c.k + j) * 4u;
-      const float wj = co_ldf(rw, fo);
-      const int s = (int)co_ld32(rs, fo);
-      float yf[8];
-      unpack8(co_ld128(ry, (uint32_t)(((size_t)s * c.H + ch * 8) * 2)), yf);
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      u32x4_t yv[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj, yf[q], acc[q]);
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < k)
+          yv[u] = co_ld128(ry, (uint32_t)(((size_t)s_pair[2 * (r * k + j0 + u) + 1] * c.H + ch * 8) * 2));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u < k) {
+          const float wj = __int_as_float(s_pair[2 * (r * k + j0 + u)]);
+          float yf[8];
+          unpack8(yv[u], yf);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj, yf[q], acc[q]);
+        }
+      }
     }
     u32x4_t o;
     o.x = f2bf(acc[0]) | (f2bf(acc[1]) << 16);
@@ -773,6 +814,111 @@ __device__ bool grid_barrier(const Ctx& c) {
   return fail == 0;
 }
 
+// Static G1 / G2 lists with the waits taken off the critical path: the row
+// tile of the task after next and the event state (arrivals, wait_count) of
+// the next task are loaded before the current task's weights, so by the time
+// a task starts its event is usually known to be released and thread 0 skips
+// polling.  Only wave 0 writes a task's outputs, so only wave 0 drains its
+// stores before the notify; the notify needs no workgroup barrier.  With the
+// debug buffer the notify also checks for over-notification.
+__device__ __forceinline__ void notify_fast(const MoeParams& p, const Ctx& c, uint32_t* ev, uint32_t target) {
+  if (p.debug) {
+    notify1(c, ev, target);
+  } else {
+    (void)__hip_atomic_fetch_add(ev, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__device__ bool wait_known(const uint32_t* ctr, uint32_t target, uint32_t known, const Ctx& c) {
+  int fail = 0;
+  if (threadIdx.x == 0 && known < target) fail = spin_until_geq(ctr, target, c.status, c.budget) ? 0 : 1;
+  fail = __syncthreads_or(fail);
+  return fail == 0;
+}
+
+__device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n) {
+  const int G = gridDim.x;
+  if (i0 >= n) return;
+  const bool tr = p.trace != nullptr;
+  uint64_t tw = 0, ts = 0, tb = 0;
+  uint32_t* evx = ev_exp(p, c);
+  uint32_t* evh = ev_h(p, c);
+  const rsrc_t rcnt = r_counts(p);
+  RowTile cur = load_rowtile(p, i0 / c.nN1);
+  RowTile nxt = cur;
+  if (i0 + G < n) nxt = load_rowtile(p, (i0 + G) / c.nN1);
+  uint32_t cur_tgt = 0, cur_arr = 0;
+  if (threadIdx.x == 0) {
+    cur_tgt = co_ld32(rcnt, (uint32_t)cur.e * 4u);
+    cur_arr = ld_relaxed(evx + cur.e);
+  }
+  for (int i = i0; i < n; i += G) {
+    const int rt = i / c.nN1, nt = i % c.nN1;
+    if (tr) tw = now_ticks();
+    if (!wait_known(evx + cur.e, cur_tgt, cur_arr, c)) return;
+    if (tr) ts = now_ticks();
+    RowTile nn = nxt;
+    if (i + 2 * G < n) nn = load_rowtile(p, (i + 2 * G) / c.nN1);
+    uint32_t nxt_tgt = 0, nxt_arr = 0;
+    if (threadIdx.x == 0 && i + G < n) {
+      nxt_tgt = co_ld32(rcnt, (uint32_t)nxt.e * 4u);
+      nxt_arr = ld_relaxed(evx + nxt.e);
+    }
+    task_g1(p, c, cur, rt, nt, red);
+    if (threadIdx.x == 0) {  // wave 0 wrote the tile: drain its stores, then notify
+      __builtin_amdgcn_s_waitcnt(0);
+      notify_fast(p, c, evh + rt, (uint32_t)c.nN1);
+    }
+    if (tr) tb = now_ticks();
+    dbg_task(p, TT_G1);
+    trace_task(p, TT_G1, rt, nt, tw, ts, tb);
+    cur = nxt;
+    nxt = nn;
+    cur_tgt = nxt_tgt;
+    cur_arr = nxt_arr;
+  }
+}
+
+__device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n) {
+  const int G = gridDim.x;
+  if (i0 >= n) return;
+  const bool tr = p.trace != nullptr;
+  uint64_t tw = 0, ts = 0, tb = 0;
+  uint32_t* evh = ev_h(p, c);
+  uint32_t* evc = ev_c(p, c);
+  const rsrc_t rperm = r_perm(p);
+  const uint32_t tgt = (uint32_t)c.nN1;
+  RowTile cur = load_rowtile(p, i0 / c.nN2);
+  RowTile nxt = cur;
+  if (i0 + G < n) nxt = load_rowtile(p, (i0 + G) / c.nN2);
+  uint32_t cur_arr = 0;
+  if (threadIdx.x == 0) cur_arr = ld_relaxed(evh + i0 / c.nN2);
+  for (int i = i0; i < n; i += G) {
+    const int rt = i / c.nN2, nt = i % c.nN2;
+    if (tr) tw = now_ticks();
+    if (!wait_known(evh + rt, tgt, cur_arr, c)) return;
+    if (tr) ts = now_ticks();
+    RowTile nn = nxt;
+    if (i + 2 * G < n) nn = load_rowtile(p, (i + 2 * G) / c.nN2);
+    uint32_t nxt_arr = 0;
+    if (threadIdx.x == 0 && i + G < n) nxt_arr = ld_relaxed(evh + (i + G) / c.nN2);
+    // combine tile of each row's token (wave 0, one row a lane)
+    int ct = 0;
+    if (threadIdx.x < cur.nrows) ct = ((int)co_ld32(rperm, (uint32_t)(cur.r0 + threadIdx.x) * 4u) / c.k) / kCombineT;
+    task_g2(p, c, cur, rt, nt, red);
+    if (threadIdx.x < cur.nrows) {  // wave 0 wrote the rows: one combine notify per row
+      __builtin_amdgcn_s_waitcnt(0);
+      notify_fast(p, c, evc + ct, ctile_target(c, ct));
+    }
+    if (tr) tb = now_ticks();
+    dbg_task(p, TT_G2);
+    trace_task(p, TT_G2, rt, nt, tw, ts, tb);
+    cur = nxt;
+    nxt = nn;
+    cur_arr = nxt_arr;
+  }
+}
+
 // STATIC / BARRIER: each phase's tasks are dealt round-robin over the
 // workgroups, continuing from where the previous phase stopped, and every
 // workgroup runs its list in phase order.  In STATIC a task waits only on
@@ -825,7 +971,7 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
     if (tr) tw = now_ticks();
     if (EV && !wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;
     if (tr) ts = now_ticks();
-    task_dispatch_copy(p, c, i);
+    task_dispatch_copy(p, c, i, sh.pairs);
     if (tr) tb = now_ticks();
     dbg_task(p, TT_D);
     after_dispatch<MODE>(p, c, i, sh);
@@ -839,33 +985,31 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
   }
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   const int nG1 = nrt * c.nN1, nG2 = nrt * c.nN2;
-  for (int i = first_of(w, off, G); i < nG1; i += G) {
-    const int rt = i / c.nN1;
-    if (tr) tw = now_ticks();
-    if (EV) {
-      const RowTile tile = load_rowtile(p, rt);
-      const uint32_t target = co_ld32(r_counts(p), (uint32_t)tile.e * 4u);
-      if (!wg_wait(ev_exp(p, c) + tile.e, target, c.status, c.budget)) return;
+  if (EV) {
+    run_g1_static(p, c, red, first_of(w, off, G), nG1);
+  } else {
+    for (int i = first_of(w, off, G); i < nG1; i += G) {
+      const int rt = i / c.nN1;
+      if (tr) tw = ts = now_ticks();
+      task_g1(p, c, load_rowtile(p, rt), rt, i % c.nN1, red);
+      if (tr) tb = now_ticks();
+      dbg_task(p, TT_G1);
+      trace_task(p, TT_G1, rt, i % c.nN1, tw, ts, tb);
     }
-    if (tr) ts = now_ticks();
-    task_g1(p, c, rt, i % c.nN1, red);
-    if (tr) tb = now_ticks();
-    dbg_task(p, TT_G1);
-    after_g1<MODE>(p, c, rt, sh);
-    trace_task(p, TT_G1, rt, i % c.nN1, tw, ts, tb);
   }
   off += nG1;
   if (!EV && !grid_barrier(c)) return;
-  for (int i = first_of(w, off, G); i < nG2; i += G) {
-    const int rt = i / c.nN2;
-    if (tr) tw = now_ticks();
-    if (EV && !wg_wait(ev_h(p, c) + rt, (uint32_t)c.nN1, c.status, c.budget)) return;
-    if (tr) ts = now_ticks();
-    task_g2(p, c, rt, i % c.nN2, red);
-    if (tr) tb = now_ticks();
-    dbg_task(p, TT_G2);
-    after_g2<MODE>(p, c, rt, sh);
-    trace_task(p, TT_G2, rt, i % c.nN2, tw, ts, tb);
+  if (EV) {
+    run_g2_static(p, c, red, first_of(w, off, G), nG2);
+  } else {
+    for (int i = first_of(w, off, G); i < nG2; i += G) {
+      const int rt = i / c.nN2;
+      if (tr) tw = ts = now_ticks();
+      task_g2(p, c, load_rowtile(p, rt), rt, i % c.nN2, red);
+      if (tr) tb = now_ticks();
+      dbg_task(p, TT_G2);
+      trace_task(p, TT_G2, rt, i % c.nN2, tw, ts, tb);
+    }
   }
   off += nG2;
   if (!EV && !grid_barrier(c)) return;
@@ -873,7 +1017,7 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
     if (tr) tw = now_ticks();
     if (EV && !wg_wait(ev_c(p, c) + i, ctile_target(c, i), c.status, c.budget)) return;
     if (tr) ts = now_ticks();
-    task_combine(p, c, i);
+    task_combine(p, c, i, sh.pairs);
     if (tr) tb = now_ticks();
     dbg_task(p, TT_C);
     trace_task(p, TT_C, i, 0, tw, ts, tb);
@@ -944,28 +1088,28 @@ __device__ void run_dynamic(const MoeParams& p, const Ctx& c, uint8_t* smem, Sha
         trace_task(p, TT_S, a, b, tw, ts, tb);
         break;
       case TT_D:
-        task_dispatch_copy(p, c, a);
+        task_dispatch_copy(p, c, a, sh.pairs);
         if (tr) tb = now_ticks();
         dbg_task(p, TT_D);
         after_dispatch<MODE_DYNAMIC>(p, c, a, sh);
         trace_task(p, TT_D, a, b, tw, ts, tb);
         break;
       case TT_G1:
-        task_g1(p, c, a, b, red);
+        task_g1(p, c, load_rowtile(p, a), a, b, red);
         if (tr) tb = now_ticks();
         dbg_task(p, TT_G1);
         after_g1<MODE_DYNAMIC>(p, c, a, sh);
         trace_task(p, TT_G1, a, b, tw, ts, tb);
         break;
       case TT_G2:
-        task_g2(p, c, a, b, red);
+        task_g2(p, c, load_rowtile(p, a), a, b, red);
         if (tr) tb = now_ticks();
         dbg_task(p, TT_G2);
         after_g2<MODE_DYNAMIC>(p, c, a, sh);
         trace_task(p, TT_G2, a, b, tw, ts, tb);
         break;
       case TT_C:
-        task_combine(p, c, a);
+        task_combine(p, c, a, sh.pairs);
         if (tr) tb = now_ticks();
         dbg_task(p, TT_C);
         trace_task(p, TT_C, a, b, tw, ts, tb);
@@ -983,7 +1127,8 @@ __device__ void run_dynamic(const MoeParams& p, const Ctx& c, uint8_t* smem, Sha
 // the last workgroup to finish advances the epoch.  No host memset, no host
 // state: the workspace is self-resetting, also after an aborted launch.
 template <int MODE>
-__global__ void __launch_bounds__(kThreads) moe_persistent(MoeParams p) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+moe_persistent(MoeParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ Shared sh;
   __shared__ uint32_t s_epoch;
@@ -1024,26 +1169,30 @@ __global__ void __launch_bounds__(kThreads) kbk_scan(MoeParams p) {
   task_scan(p, c, smem);
 }
 __global__ void __launch_bounds__(kThreads) kbk_dispatch(MoeParams p) {
+  __shared__ int pairs[2 * kCombineT * kMaxK];
   const Ctx c = make_ctx(p, nullptr);
-  task_dispatch_copy(p, c, blockIdx.x);
+  task_dispatch_copy(p, c, blockIdx.x, pairs);
 }
 __global__ void __launch_bounds__(kThreads) kbk_g1(MoeParams p) {
   __shared__ float red[4 * 4 * 256 + 16 * 64 / 2];
   const Ctx c = make_ctx(p, nullptr);
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN1) return;
-  task_g1(p, c, blockIdx.x / c.nN1, blockIdx.x % c.nN1, red);
+  const int rt = blockIdx.x / c.nN1;
+  task_g1(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN1, red);
 }
 __global__ void __launch_bounds__(kThreads) kbk_g2(MoeParams p) {
   __shared__ float red[4 * 4 * 256 + 16 * 64 / 2];
   const Ctx c = make_ctx(p, nullptr);
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN2) return;
-  task_g2(p, c, blockIdx.x / c.nN2, blockIdx.x % c.nN2, red);
+  const int rt = blockIdx.x / c.nN2;
+  task_g2(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN2, red);
 }
 __global__ void __launch_bounds__(kThreads) kbk_combine(MoeParams p) {
+  __shared__ int pairs[2 * kCombineT * kMaxK];
   const Ctx c = make_ctx(p, nullptr);
-  task_combine(p, c, blockIdx.x);
+  task_combine(p, c, blockIdx.x, pairs);
 }
 
 // ------------------------------------------------------- host launchers --
