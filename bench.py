@@ -48,6 +48,9 @@ def parse():
                     "schedule to this JSON file (one extra traced launch each, outside the timing); the raw "
                     "records go next to it as .npz")
     ap.add_argument("--repeat", type=int, default=3, help="timing loops per schedule; the median is reported")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the prefill (T=256, Zipf-biased) and batch-size-sweep measurements")
+    ap.add_argument("--sweep-steps", type=int, default=200)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="calibration only: run a plain elementwise copy (read N MiB, write N MiB) --steps "
                          "times and exit; its HBM counters scale the MoE kernel's")
@@ -84,14 +87,16 @@ def trace_summary(bufs, T, sched, khz, stream_ptr, records=1 << 16, dump=None):
     wait, and the first start / last end in µs from the earliest wait."""
     import torch
     from dynamic_moe_task_amd import binding as B
-    tr = torch.zeros(16 + 8 * records, dtype=torch.int32, device="cuda")
+    tr = torch.zeros(B.trace_words(records), dtype=torch.int32, device="cuda")
     B.check(B.moe_layer_launch(bufs.desc, T, bufs.args(trace=tr), B.SCHEDS[sched], stream_ptr))
     B.check(B.etc_sync(stream_ptr))
     raw = tr.cpu().numpy().view(np.uint32)
-    n = min(int(raw[0]), records)
+    allrec = raw[16:16 + 8 * records].reshape(records, 8)
+    rec = allrec[allrec[:, 0] != 0]  # each workgroup fills its own slots; unused ones stay zero
+    n = len(rec)
     if dump:
-        np.savez(dump, raw=raw[:16 + 8 * n], khz=khz)
-    rec = raw[16:16 + 8 * n].reshape(n, 8).astype(np.int64)
+        np.savez(dump, raw=np.concatenate([raw[:16], rec.reshape(-1)]), khz=khz)
+    rec = rec.astype(np.int64)
     wg, typ = rec[:, 0] & 0xFFFFFF, rec[:, 0] >> 24
     tw = (rec[:, 4] << 32) | rec[:, 3]
 
@@ -180,6 +185,82 @@ def cpu_baseline(shape, w, X, seconds):
             "sample": f"{sample}; {n} calls in {dt:.1f} s on {platform.processor() or platform.machine()}"}
 
 
+RIDGE = BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte where MFMA and HBM bounds meet
+
+
+def measure_prefill(Wr, w13s, w2s, sp, steps, warmup, repeat):
+    """Prefill chunk: T=256 with the Zipf(1.1) logit bias (hot experts get
+    most tokens, some get none).  Same expert weights as the decode layer."""
+    import torch
+    from dynamic_moe_task_amd import binding as B
+    from dynamic_moe_task_amd import workloads as wl
+    shape = wl.PREFILL_ZIPF
+    T = shape.T
+    X = wl.make_tokens(shape, T, 0)
+    bias = torch.from_numpy(wl.zipf_bias(shape, 0)).cuda()
+    desc = B.moe_desc(T, shape.H, shape.E, shape.k, shape.I, shape.norm_topk, True)
+    bufs = B.MoELayerBuffers.allocate(desc, Wr, w13s[0], w2s[0], bias)
+    bufs.x[:T].copy_(dev_bf16(X))
+    B.check(B.moe_layer_launch(desc, T, bufs.args(), B.SCHEDS["static"], sp))
+    B.check(B.etc_sync(sp))
+    counts = bufs.counts.cpu().numpy()
+    n_act = int((counts > 0).sum())
+    alg_bytes = wl.algorithmic_bytes(shape, T, n_act)
+    alg_flops = wl.algorithmic_flops(shape, T)
+    us = {}
+    for sch in ("static", "barrier", "kbk"):
+        us[sch] = float(np.median([time_sched(bufs, T, sch, steps, warmup, w13s, w2s, sp) for _ in range(repeat)]))
+    best = min(us.values())
+    ai = alg_flops / alg_bytes
+    return {
+        "workload": shape.name, "T": T, "active_experts": n_act, "max_expert_tokens": int(counts.max()),
+        "us_per_layer": {k: round(v, 2) for k, v in us.items()},
+        "tokens_per_s_static": round(T / (us["static"] * 1e-6), 1),
+        "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops,
+        "hbm_frac_static": round(alg_bytes / (us["static"] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+        "mfma_frac_whole_layer_static": round(alg_flops / (us["static"] * 1e-6) / (BF16_PEAK_TFS * 1e12), 5),
+        "mfma_frac_cap": round(ai / RIDGE, 4),
+        "note": "whole-layer MFMA use is capped at AI/ridge: at this batch the layer is HBM-bound",
+        "fastest": min(us, key=us.get), "fastest_us": round(best, 2),
+    }
+
+
+def measure_sweep(Wr, w13s, w2s, sp, steps):
+    """Shape dynamism: one template (T_max=512), batch B ~ U{1..512} per step,
+    fresh tokens each step; per-launch latency from HIP events."""
+    import torch
+    from dynamic_moe_task_amd import binding as B
+    from dynamic_moe_task_amd import workloads as wl
+    shape = wl.SWEEP
+    Bs = wl.sweep_batches(0, steps)
+    desc = B.moe_desc(shape.T, shape.H, shape.E, shape.k, shape.I, shape.norm_topk, False)
+    bufs = B.MoELayerBuffers.allocate(desc, Wr, w13s[0], w2s[0], None)
+    xs = [dev_bf16(wl.sweep_tokens(shape, i, int(b), 0)) for i, b in enumerate(Bs)]
+    R = len(w13s)
+    args = [bufs.args(x=xs[i], w13=w13s[i % R], w2=w2s[i % R]) for i in range(steps)]
+    code = B.SCHEDS["static"]
+    for i in range(3):  # warm-up launches at a few sizes
+        B.check(B.moe_layer_launch(desc, int(Bs[i]), args[i], code, sp))
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        B.check(B.moe_layer_launch(desc, int(Bs[i]), args[i], code, sp))
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    B.check(B.etc_sync(sp))
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    small = Bs <= 64
+    return {
+        "steps": steps, "B_min": int(Bs.min()), "B_max": int(Bs.max()), "schedule": "static",
+        "us_p50": round(float(np.percentile(us, 50)), 2), "us_p90": round(float(np.percentile(us, 90)), 2),
+        "us_p99": round(float(np.percentile(us, 99)), 2), "us_max": round(float(us.max()), 2),
+        "us_p50_B_le_64": round(float(np.median(us[small])), 2) if small.any() else None,
+        "tokens_per_s": round(float(Bs.sum() / (us.sum() * 1e-6)), 1),
+        "recompiles": 0, "graph_captures": 0, "code_objects": 1,
+    }
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -206,14 +287,19 @@ def main():
     R = max(1, a.copies) if shape.E > 8 else 1
     w13s = [W13] + [W13.clone() for _ in range(R - 1)]
     w2s = [Wd] + [Wd.clone() for _ in range(R - 1)]
-    desc = B.moe_desc(T, shape.H, shape.E, shape.k, shape.I, shape.norm_topk, bias is not None)
-    bufs = B.MoELayerBuffers.allocate(desc, Wr, W13, Wd, bias)
-    bufs.x[:T].copy_(dev_bf16(X))
+    xd = dev_bf16(X)
     torch.cuda.synchronize()
 
-    # one checked launch first: routing of the benchmarked inputs
+    # first-step warm-up: library load, workspace set-up and the first launch
+    # (code-object load included) up to its completion, all on the host clock
+    t_w0 = time.perf_counter()
+    B.lib()
+    desc = B.moe_desc(T, shape.H, shape.E, shape.k, shape.I, shape.norm_topk, bias is not None)
+    bufs = B.MoELayerBuffers.allocate(desc, Wr, W13, Wd, bias)
+    bufs.x[:T].copy_(xd)
     B.check(B.moe_layer_launch(desc, T, bufs.args(), B.SCHEDS[a.sched], sp))
     B.check(B.etc_sync(sp))
+    warmup_ms = (time.perf_counter() - t_w0) * 1e3
     counts = bufs.counts.cpu().numpy()
     n_act = int((counts > 0).sum())
     alg_bytes = wl.algorithmic_bytes(shape, T, n_act)
@@ -258,6 +344,11 @@ def main():
         with open(a.trace, "w") as f:
             json.dump(summ, f, indent=1)
 
+    extra = {}
+    if not a.no_extra and a.workload == "decode":
+        extra["prefill_zipf"] = measure_prefill(Wr, w13s, w2s, sp, max(10, a.steps // 2), a.warmup, a.repeat)
+        extra["sweep"] = measure_sweep(Wr, w13s, w2s, sp, a.sweep_steps)
+
     cpu = None
     if not a.no_cpu:
         cpu = cpu_baseline(shape, w, X, a.cpu_seconds)
@@ -282,7 +373,9 @@ def main():
         "mfma_frac_whole_layer": round(mfma_frac, 5),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "first_step_warmup_ms": round(warmup_ms, 2),
     }
+    line.update(extra)
     print(json.dumps(line), flush=True)
 
 

@@ -152,6 +152,11 @@ def moe_layer_workspace_size(desc: MoeDesc) -> int:
     return lib().moe_layer_workspace_size(ctypes.byref(desc))
 
 
+def trace_words(records: int) -> int:
+    """ETC_TRACE_WORDS: uint32 words of a trace buffer holding `records`."""
+    return 16 + 8 * int(records)
+
+
 def moe_layer_info(desc: MoeDesc) -> MoeInfo:
     info = MoeInfo()
     check(lib().moe_layer_info(ctypes.byref(desc), ctypes.byref(info)))

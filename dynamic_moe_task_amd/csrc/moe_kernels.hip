@@ -145,13 +145,27 @@ __device__ __forceinline__ void dbg_task(const MoeParams& p, int type) {
 
 // Optional per-task trace (thread 0): wall-clock ticks before the wait,
 // after it, after the task body, and after the notifies.
+// Records of workgroup w fill slots [w*per_wg, (w+1)*per_wg) in task order;
+// only thread 0 writes them, so the running count lives in LDS.
+__shared__ uint32_t s_trace_n;
+
+__device__ __forceinline__ void trace_init(const MoeParams& p) {
+  if (threadIdx.x != 0) return;
+  s_trace_n = 0;
+  if (p.trace && blockIdx.x == 0) {
+    p.trace[1] = p.trace_records / gridDim.x;
+    p.trace[2] = gridDim.x;
+  }
+}
+
 __device__ __forceinline__ void trace_task(const MoeParams& p, int type, int a, int b, uint64_t tw,
                                            uint64_t ts, uint64_t tb) {
   if (!p.trace || threadIdx.x != 0) return;
   const uint64_t te = now_ticks();
-  const uint32_t r = atomicAdd(p.trace, 1u);
-  if (r >= p.trace_records) return;
-  uint32_t* q = p.trace + 16 + 8 * (size_t)r;
+  const uint32_t per_wg = p.trace_records / gridDim.x;
+  const uint32_t j = s_trace_n++;
+  if (j >= per_wg) return;
+  uint32_t* q = p.trace + 16 + 8 * ((size_t)blockIdx.x * per_wg + j);
   q[0] = blockIdx.x | ((uint32_t)type << 24);
   q[1] = (uint32_t)a;
   q[2] = (uint32_t)b;
@@ -235,8 +249,28 @@ __device__ void task_router(const MoeParams& p, const Ctx& c, int tt, int et) {
 // K: top-k per token (one wave per token): k rounds of a wave-wide arg-max
 // on (logit descending, expert index ascending); weights exp(l_j - l_max)
 // normalised over the chosen k (norm_topk) or over all E.
-__device__ __forceinline__ bool ranks_before(float a, int ia, float b, int ib) {
-  return a > b || (a == b && ia < ib);
+//
+// Each round takes the wave maximum of the lanes' best remaining logits with
+// six DPP steps (pair swap, quad swap, half-row and row mirror, then the two
+// row broadcasts that carry a row's maximum into the next rows; lane 63 ends
+// with the maximum of all 64 lanes), then picks the lowest expert index that
+// holds that value from one ballot per 64-expert slice: expert e = lane +
+// 64 j, so the first slice with a hit and its lowest set lane give the lowest
+// index.  Ties therefore go to the lower expert, and equality is float
+// equality (+0 and -0 tie), as in a (logit desc, index asc) ordering.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_step(float x) {
+  const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xf, false);
+  return fmaxf(x, __int_as_float(y));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = dpp_max_step<0xB1, 0xf>(x);   // quad_perm [1,0,3,2]
+  x = dpp_max_step<0x4E, 0xf>(x);   // quad_perm [2,3,0,1]
+  x = dpp_max_step<0x141, 0xf>(x);  // row_half_mirror
+  x = dpp_max_step<0x140, 0xf>(x);  // row_mirror
+  x = dpp_max_step<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_max_step<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 __device__ void task_topk(const MoeParams& p, const Ctx& c, int tt) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -257,26 +291,27 @@ __device__ void task_topk(const MoeParams& p, const Ctx& c, int tt) {
     v[j] = x;
   }
   if (__any(bad) && lane == 0) or_relaxed(c.status, ST_NONFINITE);
-  uint32_t taken = 0;
+  uint32_t avail = 0;  // bit j: expert lane + 64 j exists and is not yet taken
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (lane + 64 * j < c.E) avail |= 1u << j;
   float my_v = 0.0f, v0 = 0.0f;
   int my_e = 0;
   for (int r = 0; r < c.k; ++r) {
-    float bv = NEG_INF;
-    int be = 0x7fffffff;
+    float lv = NEG_INF;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((avail >> j) & 1u) lv = fmaxf(lv, v[j]);
+    const float m = wave_max(lv);
+    int be = -1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (e < c.E && !((taken >> j) & 1u) && ranks_before(v[j], e, bv, be)) { bv = v[j]; be = e; }
+      const unsigned long long hit = __ballot(((avail >> j) & 1u) && v[j] == m);
+      if (be < 0 && hit) be = 64 * j + (__ffsll(hit) - 1);
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-      const float ov = __shfl_xor(bv, s);
-      const int oe = __shfl_xor(be, s);
-      if (ranks_before(ov, oe, bv, be)) { bv = ov; be = oe; }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == r) { my_v = bv; my_e = be; }
-    if (r == 0) v0 = bv;
+    if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
+    if (lane == r) { my_v = m; my_e = be; }
+    if (r == 0) v0 = m;
   }
   float part = 0.0f;
   if (p.norm_topk) {
@@ -823,6 +858,7 @@ __device__ bool grid_barrier(const Ctx& c) {
 // debug buffer the notify also checks for over-notification.
 __device__ __forceinline__ void notify_fast(const MoeParams& p, const Ctx& c, uint32_t* ev, uint32_t target) {
   if (p.debug) {
+    asm volatile("" ::: "memory");  // keeps the two atomics from being merged into one returning atomic
     notify1(c, ev, target);
   } else {
     (void)__hip_atomic_fetch_add(ev, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1133,6 +1169,7 @@ moe_persistent(MoeParams p) {
   __shared__ Shared sh;
   __shared__ uint32_t s_epoch;
   if (threadIdx.x == 0) s_epoch = ld_relaxed(p.ctrl + C_EPOCH);
+  trace_init(p);
   __syncthreads();
   const uint32_t epoch = s_epoch;
   uint32_t* set = (epoch & 1u) ? p.set1 : p.set0;

@@ -177,12 +177,15 @@ typedef struct {
   uint32_t watchdog_us;
   uint32_t trace_records; /* capacity of `trace` in records (0 = no trace)  */
   uint32_t* trace;        /* NULL, or ETC_TRACE_WORDS(trace_records) uint32,
-                             word 0 zeroed by the caller (see below)        */
+                             zeroed by the caller (see below)               */
 } etc_moe_args;
 
-/* Per-task trace, when etc_moe_args.trace is non-NULL (persistent schedules):
- * word 0 counts records written (it may exceed the capacity; extra records
- * are dropped); record r occupies words [16 + 8r, 16 + 8r + 8):
+/* Per-task trace, when etc_moe_args.trace is non-NULL (persistent schedules).
+ * Each workgroup owns per_wg = trace_records / grid consecutive records and
+ * fills them in task order with plain stores (no atomics, so tracing barely
+ * perturbs the timing); records past per_wg are dropped, unused ones stay
+ * zero.  Words 1 and 2 receive per_wg and the grid size.  Record r occupies
+ * words [16 + 8r, 16 + 8r + 8), workgroup w's records start at r = w*per_wg:
  *   workgroup | task type << 24 (type 1..7 = R, K, S, D, G1, G2, C), task
  *   index a, b, then wall-clock ticks: before the task's wait (low, high 32
  *   bits), and the low 32 bits after the wait, after the task body, and after

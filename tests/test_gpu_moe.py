@@ -107,6 +107,42 @@ def test_event_invariants(qwen_weights, decode_case, sched):
     assert list(dbg[2 * E:2 * E + 7]) == expect
 
 
+@pytest.mark.parametrize("sched", ["static", "barrier"])
+def test_task_trace(qwen_weights, decode_case, sched):
+    # the per-task trace holds one record per task, in per-workgroup slots,
+    # with wait <= start <= end-of-body <= end-of-notify in every record
+    import torch
+    s = wl.DECODE
+    X, ref = decode_case
+    layer = DeviceLayer((s.H, s.E, s.k, s.I), qwen_weights.Wr, qwen_weights.W13, qwen_weights.Wd, T_max=64)
+    B = layer.B
+    info = B.moe_layer_info(layer.desc)
+    records = info.grid * 64
+    tr = torch.zeros(B.trace_words(records), dtype=torch.int32, device="cuda")
+    layer.bufs.x[:s.T].copy_(torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).cuda())
+    stream = torch.cuda.current_stream().cuda_stream
+    announce(f"decode trace sched={sched}")
+    B.check(B.moe_layer_launch(layer.desc, s.T, layer.bufs.args(trace=tr), B.SCHEDS[sched], stream))
+    B.check(B.etc_sync(stream))
+    raw = tr.cpu().numpy().view(np.uint32)
+    assert raw[1] == records // info.grid and raw[2] == info.grid
+    rec = raw[16:].reshape(-1, 8)
+    rec = rec[rec[:, 0] != 0].astype(np.int64)
+    typ, wg = rec[:, 0] >> 24, rec[:, 0] & 0xFFFFFF
+    n_rt = len(oracle.expected_tiles(ref["exp_indptr"], info.bm))
+    T, E = s.T, s.E
+    expect = {1: -(-T // info.router_tokens) * -(-E // info.router_experts), 2: -(-T // info.router_tokens),
+              3: 1, 4: -(-T // info.dispatch_tokens), 5: n_rt * (s.I // info.bn1), 6: n_rt * (s.H // info.bn2),
+              7: -(-T // info.combine_tokens)}
+    assert {t: int((typ == t).sum()) for t in expect} == expect
+    assert wg.max() < info.grid
+    tw = (rec[:, 4] << 32) | rec[:, 3]
+    stamps = [tw] + [((rec[:, 4] << 32) | rec[:, j]) for j in (5, 6, 7)]
+    stamps = [np.where(t < tw, t + (1 << 32), t) for t in stamps]
+    for a, b in zip(stamps, stamps[1:]):
+        assert (a <= b).all()
+
+
 # --------------------------------------------------------------- prefill --
 def _sample_tokens(ids, T, n_each=4):
     hot = np.bincount(ids.reshape(-1)).argmax()
