@@ -22,7 +22,7 @@ enum : uint32_t {
 constexpr int kThreads = 256;   // 4 wave64 per workgroup
 constexpr int kRouterT = 4;     // R task: tokens ...
 constexpr int kRouterE = 4;     //         ... x experts (one expert per wave)
-constexpr int kBM = 16;         // grouped-GEMM row tile (one 16-row MFMA block)
+constexpr int kBM = 64;         // grouped-GEMM row tile (up to four 16-row MFMA blocks)
 constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile
 constexpr int kBN2 = 64;        // G2: output columns per tile (4 MFMA column blocks)
 constexpr int kDispatchT = 1;   // D task: tokens per task
@@ -122,8 +122,8 @@ inline int64_t scan_lds_bytes(int E, int T_max) {
   return align_up((int64_t)E * W * 4, 16) + align_up((int64_t)E * W * 2, 16) + 3 * 260 * 4 + 64;
 }
 // G2: cross-wave reduction buffer (4 waves x 4 blocks x 256 fp32) plus the
-// bf16 staging of the 16 x 64 output tile
-constexpr int64_t kGemmLdsBytes = 4 * 4 * 256 * 4 + 16 * 64 * 2;
+// bf16 staging of the kBM x 64 output tile
+constexpr int64_t kGemmLdsBytes = 4 * 4 * 256 * 4 + kBM * 64 * 2;
 
 struct MoeParams {
   const uint16_t* x;

@@ -462,33 +462,50 @@ __device__ void task_dispatch_copy(const MoeParams& p, const Ctx& c, int dt, int
   }
 }
 
-// G1: one 16-row tile of expert e times 16 gate and 16 up columns of W13,
+// Grouped-GEMM tasks.  A row tile holds up to kBM = 64 grouped rows of one
+// expert: NB = 1, 2 or 4 row blocks of 16 (three round up to four).  The 4
+// waves always split K in quarters, and each wave multiplies every row block
+// of the tile with the same weight fragment, so a weight byte is loaded once
+// per task and feeds up to four MFMA row blocks (a decode tile has one block;
+// a prefill tile of a hot expert has four).  The per-wave partial sums are
+// reduced in LDS in wave order, block by block.
+__device__ __forceinline__ int row_blocks(int nrows) { return nrows <= 16 ? 1 : (nrows <= 32 ? 2 : 4); }
+
+// G1: one row tile of expert e times 16 gate and 16 up columns of W13,
 // SwiGLU, Hmid = bf16(silu(g) * u).  bf16 MFMA 16x16x32 with fp32
-// accumulation; the 4 waves split K = H in quarters and reduce in LDS.  The
-// weight tile (2 x 16 rows x H) streams straight from HBM into registers;
-// rows past the expert's count are zero-filled, never loaded.
-__device__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt, float* red) {
+// accumulation; the weight slab (2 x 16 rows x H) streams from HBM straight
+// into registers; rows past the expert's count are zero-filled, never loaded.
+template <int NB, int U>
+__device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const RowTile tile, int nt, float* red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int m = lane & 15, kg = lane >> 4;
   const int H = c.H, I = c.I;
   const int kw = H >> 2;
   const int nsteps = kw >> 5;
-  const bool valid = m < tile.nrows;
   const rsrc_t rx = r_xp(p);
-  const uint32_t aoff = (uint32_t)(((size_t)(tile.r0 + (valid ? m : 0)) * H + wv * kw + kg * 8) * 2);
+  bool valid[NB];
+  uint32_t aoff[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int r = b * 16 + m;
+    valid[b] = r < tile.nrows;
+    aoff[b] = (uint32_t)(((size_t)(tile.r0 + (valid[b] ? r : 0)) * H + wv * kw + kg * 8) * 2);
+  }
   const uint16_t* pg = p.w13 + ((size_t)tile.e * 2 * I + (size_t)nt * kBN1 + m) * H + wv * kw + kg * 8;
   const uint16_t* pu = pg + (size_t)I * H;
-  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t accg[NB], accu[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) accg[b] = accu[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  // batches of 8 k-steps (24 loads of 16 bytes a lane in flight); two
+  // batches of U k-steps (about 24 loads of 16 bytes a lane in flight); two
   // workgroups per CU overlap each other's batch boundaries
-  constexpr int U = 8;
   for (int s0 = 0; s0 < nsteps; s0 += U) {
-    u32x4_t a[U], bg[U], bu[U];
+    u32x4_t a[U][NB], bg[U], bu[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u < nsteps) {
-        a[u] = valid ? co_ld128(rx, aoff + (uint32_t)(s0 + u) * 64u) : zero;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) a[u][b] = valid[b] ? co_ld128(rx, aoff[b] + (uint32_t)(s0 + u) * 64u) : zero;
         bg[u] = ld4(pg + (s0 + u) * 32);
         bu[u] = ld4(pu + (s0 + u) * 32);
       }
@@ -496,110 +513,150 @@ __device__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, in
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u < nsteps) {
-        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u]), as_bf(bg[u]), accg, 0, 0, 0);
-        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u]), as_bf(bu[u]), accu, 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          accg[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u][b]), as_bf(bg[u]), accg[b], 0, 0, 0);
+          accu[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u][b]), as_bf(bu[u]), accu[b], 0, 0, 0);
+        }
       }
     }
   }
-  // cross-wave reduction: red[w][0 = gate, 1 = up][lane * 4 + i]; the first
-  // barrier keeps the previous task's readers of `red` ahead of these writes
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    red[(wv * 2 + 0) * 256 + lane * 4 + i] = accg[i];
-    red[(wv * 2 + 1) * 256 + lane * 4 + i] = accu[i];
-  }
-  __syncthreads();
   const int tid = threadIdx.x;
-  float g = 0.f, u = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    g += red[(w * 2 + 0) * 256 + tid];
-    u += red[(w * 2 + 1) * 256 + tid];
-  }
-  // element (lane', i) of the 16x16 MFMA result: row 4*(lane'/16) + i, column lane' % 16
+  // element (lane', i) of a 16x16 MFMA result: row 4*(lane'/16) + i, column lane' % 16
   const int ol = tid >> 2, oi = tid & 3;
   const int row = 4 * (ol >> 4) + oi, col = ol & 15;
-  uint16_t* stage = reinterpret_cast<uint16_t*>(red + 4096);  // [16 rows][16 cols] bf16
-  stage[row * 16 + col] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u);
+  uint16_t* stage = reinterpret_cast<uint16_t*>(red + 4096);  // [64 rows][16 cols] bf16
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    // cross-wave reduction: red[w][0 = gate, 1 = up][lane * 4 + i]; the first
+    // barrier keeps earlier readers of `red` ahead of these writes
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      red[(wv * 2 + 0) * 256 + lane * 4 + i] = accg[b][i];
+      red[(wv * 2 + 1) * 256 + lane * 4 + i] = accu[b][i];
+    }
+    __syncthreads();
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      g += red[(w * 2 + 0) * 256 + tid];
+      u += red[(w * 2 + 1) * 256 + tid];
+    }
+    stage[(b * 16 + row) * 16 + col] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u);
+  }
   __syncthreads();
-  // wave 0 alone writes the tile (16 rows x 32 bytes), so only wave 0 has
-  // stores to drain before the notify
-  if (tid < 32) {
-    const int r = tid >> 1, half = tid & 1;
-    if (r < tile.nrows) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * 16 + half * 8);
-      co_st128(r_hh(p), (uint32_t)(((size_t)(tile.r0 + r) * I + nt * kBN1 + half * 8) * 2), v);
+  // wave 0 alone writes the tile (rows x 32 bytes, two chunks a row), so
+  // only wave 0 has stores to drain before the notify
+  if (tid < 64) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int idx = tid + 64 * h;
+      const int r = idx >> 1, half = idx & 1;
+      if (r < tile.nrows) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * 16 + half * 8);
+        co_st128(r_hh(p), (uint32_t)(((size_t)(tile.r0 + r) * I + nt * kBN1 + half * 8) * 2), v);
+      }
     }
   }
 }
 
-// G2: one 16-row tile times 64 output columns of Wd[e]: Y = bf16(Hmid Wd^T).
-// The 4 waves split K = I in quarters; each wave keeps 4 column blocks.
-__device__ void task_g2(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt2, float* red) {
+__device__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt, float* red) {
+  (void)rt;
+  switch (row_blocks(tile.nrows)) {
+    case 1: g1_body<1, 8>(p, c, tile, nt, red); break;
+    case 2: g1_body<2, 6>(p, c, tile, nt, red); break;
+    default: g1_body<4, 4>(p, c, tile, nt, red); break;
+  }
+}
+
+// G2: one row tile times 64 output columns of Wd[e]: Y = bf16(Hmid Wd^T).
+// K = I split in quarters over the waves; each wave keeps 4 column blocks
+// for every row block.
+template <int NB, int U>
+__device__ __forceinline__ void g2_body(const MoeParams& p, const Ctx& c, const RowTile tile, int nt2, float* red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int m = lane & 15, kg = lane >> 4;
   const int H = c.H, I = c.I;
   const int kw = I >> 2;
   const int nsteps = kw >> 5;
-  const bool valid = m < tile.nrows;
   const rsrc_t rh = r_hh(p);
-  const uint32_t aoff = (uint32_t)(((size_t)(tile.r0 + (valid ? m : 0)) * I + wv * kw + kg * 8) * 2);
+  bool valid[NB];
+  uint32_t aoff[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int r = b * 16 + m;
+    valid[b] = r < tile.nrows;
+    aoff[b] = (uint32_t)(((size_t)(tile.r0 + (valid[b] ? r : 0)) * I + wv * kw + kg * 8) * 2);
+  }
   const uint16_t* pb = p.w2 + ((size_t)tile.e * H + (size_t)nt2 * kBN2 + m) * I + wv * kw + kg * 8;
   const size_t cbs = (size_t)16 * I;  // next 16-column block of Wd
-  f32x4_t acc[4];
+  f32x4_t acc[NB][4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[b][q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  constexpr int U = 8;
   for (int s0 = 0; s0 < nsteps; s0 += U) {
-    u32x4_t a[U], bb[U][4];
+    u32x4_t a[U][NB], bb[U][4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u < nsteps) {
-        a[u] = valid ? co_ld128(rh, aoff + (uint32_t)(s0 + u) * 64u) : zero;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) bb[u][b] = ld4(pb + b * cbs + (s0 + u) * 32);
+        for (int b = 0; b < NB; ++b) a[u][b] = valid[b] ? co_ld128(rh, aoff[b] + (uint32_t)(s0 + u) * 64u) : zero;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bb[u][q] = ld4(pb + q * cbs + (s0 + u) * 32);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u < nsteps) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u]), as_bf(bb[u][b]), acc[b], 0, 0, 0);
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[b][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u][b]), as_bf(bb[u][q]), acc[b][q], 0, 0, 0);
       }
     }
   }
-  __syncthreads();
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[(wv * 4 + b) * 256 + lane * 4 + i] = acc[b][i];
-  __syncthreads();
   const int tid = threadIdx.x;
   const int ol = tid >> 2, oi = tid & 3;
   const int row = 4 * (ol >> 4) + oi, col = ol & 15;
-  uint16_t* stage = reinterpret_cast<uint16_t*>(red + 4096);  // [16 rows][64 cols] bf16
+  uint16_t* stage = reinterpret_cast<uint16_t*>(red + 4096);  // [64 rows][64 cols] bf16
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    float y = 0.f;
+  for (int b = 0; b < NB; ++b) {
+    __syncthreads();
 #pragma unroll
-    for (int w = 0; w < 4; ++w) y += red[(w * 4 + b) * 256 + tid];
-    stage[row * 64 + b * 16 + col] = (uint16_t)f2bf(y);
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(wv * 4 + q) * 256 + lane * 4 + i] = acc[b][q][i];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float y = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) y += red[(w * 4 + q) * 256 + tid];
+      stage[(b * 16 + row) * 64 + q * 16 + col] = (uint16_t)f2bf(y);
+    }
   }
   __syncthreads();
-  // wave 0 alone writes the tile (16 rows x 128 bytes, two chunks a lane)
+  // wave 0 alone writes the tile (rows x 128 bytes, eight chunks a row)
   if (tid < 64) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int idx = tid + 64 * h;
+    const int nchunks = tile.nrows * 8;
+    for (int idx = tid; idx < nchunks; idx += 64) {
       const int r = idx >> 3, q = idx & 7;
-      if (r < tile.nrows) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * 64 + q * 8);
-        co_st128(r_y(p), (uint32_t)(((size_t)(tile.r0 + r) * H + nt2 * kBN2 + q * 8) * 2), v);
-      }
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * 64 + q * 8);
+      co_st128(r_y(p), (uint32_t)(((size_t)(tile.r0 + r) * H + nt2 * kBN2 + q * 8) * 2), v);
     }
+  }
+}
+
+__device__ void task_g2(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt2, float* red) {
+  (void)rt;
+  switch (row_blocks(tile.nrows)) {
+    case 1: g2_body<1, 8>(p, c, tile, nt2, red); break;
+    case 2: g2_body<2, 4>(p, c, tile, nt2, red); break;
+    default: g2_body<4, 2>(p, c, tile, nt2, red); break;
   }
 }
 
@@ -1210,16 +1267,16 @@ __global__ void __launch_bounds__(kThreads) kbk_dispatch(MoeParams p) {
   const Ctx c = make_ctx(p, nullptr);
   task_dispatch_copy(p, c, blockIdx.x, pairs);
 }
-__global__ void __launch_bounds__(kThreads) kbk_g1(MoeParams p) {
-  __shared__ float red[4 * 4 * 256 + 16 * 64 / 2];
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) kbk_g1(MoeParams p) {
+  __shared__ float red[4 * 4 * 256 + kBM * 64 / 2];
   const Ctx c = make_ctx(p, nullptr);
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN1) return;
   const int rt = blockIdx.x / c.nN1;
   task_g1(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN1, red);
 }
-__global__ void __launch_bounds__(kThreads) kbk_g2(MoeParams p) {
-  __shared__ float red[4 * 4 * 256 + 16 * 64 / 2];
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) kbk_g2(MoeParams p) {
+  __shared__ float red[4 * 4 * 256 + kBM * 64 / 2];
   const Ctx c = make_ctx(p, nullptr);
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN2) return;
