@@ -338,7 +338,7 @@ extern "C" int moe_layer_info(const etc_moe_desc* d, etc_moe_info* info) {
   info->bn2 = kBN2;
   info->router_tokens = kRouterT;
   info->router_experts = kRouterE;
-  info->dispatch_tokens = kDispatchT;
+  info->dispatch_tokens = 0;  // no dispatch tasks: G1 gathers its rows from x
   info->combine_tokens = kCombineT;
   info->threads = kThreads;
   info->lds_bytes = (int32_t)lds_bytes_for(d);
@@ -413,7 +413,6 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
   p.tile_indptr = reinterpret_cast<int32_t*>(ws + L.b_tile_indptr);
   p.rt_info = reinterpret_cast<int32_t*>(ws + L.b_rt_info);
   p.logits = reinterpret_cast<float*>(ws + L.b_logits);
-  p.xp = reinterpret_cast<uint16_t*>(ws + L.b_xp);
   p.hh = reinterpret_cast<uint16_t*>(ws + L.b_hh);
   p.y = reinterpret_cast<uint16_t*>(ws + L.b_y);
   p.set_words = L.set_words;
@@ -434,7 +433,6 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
   p.T_max = d->T_max;
   {
     const int64_t rows = (int64_t)d->T_max * d->k;
-    p.xp_bytes = (uint32_t)(rows * d->H * 2);
     p.hh_bytes = (uint32_t)(rows * d->I * 2);
     p.y_bytes = (uint32_t)(rows * d->H * 2);
     p.logits_bytes = (uint32_t)((int64_t)d->T_max * d->E * 4);

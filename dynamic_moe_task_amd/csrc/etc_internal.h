@@ -25,7 +25,6 @@ constexpr int kRouterE = 4;     //         ... x experts (one expert per wave)
 constexpr int kBM = 64;         // grouped-GEMM row tile (up to four 16-row MFMA blocks)
 constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile
 constexpr int kBN2 = 64;        // G2: output columns per tile (4 MFMA column blocks)
-constexpr int kDispatchT = 1;   // D task: tokens per task
 constexpr int kCombineT = 2;    // C task: tokens per task
 constexpr int kMaxK = 16;
 constexpr int kMaxE = 256;
@@ -65,13 +64,13 @@ enum : int { C_EPOCH = 0, C_REPORT = 1, C_WORDS = 64 };
 
 struct MoeLayout {
   // sizes derived from the descriptor's T_max
-  int32_t ntt_max, max_rt, nct_max, ndt_max;
+  int32_t ntt_max, max_rt, nct_max;
   int64_t q_cap;
   // word offsets inside a counter set
   int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_c, o_queue;  // o_queue in words, 8-byte aligned
   int64_t set_words;
   // byte offsets inside the workspace
-  int64_t b_ctrl, b_set0, b_set1, b_meta, b_tile_indptr, b_rt_info, b_logits, b_xp, b_hh, b_y;
+  int64_t b_ctrl, b_set0, b_set1, b_meta, b_tile_indptr, b_rt_info, b_logits, b_hh, b_y;
   int64_t total_bytes;
 };
 
@@ -86,12 +85,11 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
   const int64_t Tm = d.T_max;
   L.ntt_max = (int32_t)cdiv(Tm, kRouterT);
   L.nct_max = (int32_t)cdiv(Tm, kCombineT);
-  L.ndt_max = (int32_t)cdiv(Tm, kDispatchT);
   const int64_t rows = Tm * d.k;
   L.max_rt = (int32_t)(cdiv(rows, kBM) + (rows < d.E ? rows : d.E));
   const int64_t nN1 = d.I / kBN1, nN2 = d.H / kBN2;
   // every task except the router prefix goes through the queue
-  L.q_cap = L.ntt_max + 1 + L.ndt_max + (int64_t)L.max_rt * (nN1 + nN2) + L.nct_max + 64;
+  L.q_cap = L.ntt_max + 1 + (int64_t)L.max_rt * (nN1 + nN2) + L.nct_max + 64;
   int64_t w = W_FIXED;
   L.o_ev_logit = w; w += L.ntt_max;
   L.o_ev_exp = w;   w += d.E;
@@ -108,7 +106,6 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
   L.b_tile_indptr = b;   b += align_up((int64_t)(d.E + 1) * 4, 256);
   L.b_rt_info = b;       b += align_up((int64_t)L.max_rt * 16, 256);
   L.b_logits = b;        b += align_up(Tm * d.E * 4, 256);
-  L.b_xp = b;            b += align_up(rows * d.H * 2, 256);
   L.b_hh = b;            b += align_up(rows * d.I * 2, 256);
   L.b_y = b;             b += align_up(rows * d.H * 2, 256);
   L.total_bytes = b;
@@ -146,7 +143,6 @@ struct MoeParams {
   int32_t* tile_indptr;
   int32_t* rt_info;  // [max_rt][4]: expert, first grouped row, rows, 0
   float* logits;
-  uint16_t* xp;
   uint16_t* hh;
   uint16_t* y;
   int64_t set_words;
@@ -155,7 +151,7 @@ struct MoeParams {
   int32_t max_rt;
   int32_t T_max;
   // byte sizes of the device-coherent buffers (bounds of their resources)
-  uint32_t xp_bytes, hh_bytes, y_bytes, logits_bytes, rows_bytes;
+  uint32_t hh_bytes, y_bytes, logits_bytes, rows_bytes;
   uint64_t budget;  // watchdog, in wall-clock ticks
   uint32_t* trace;
   uint32_t trace_records;

@@ -5,13 +5,13 @@
 // Task graph (Event Tensor, arXiv 2604.13327: Fig. 2 and Fig. 5b; podcast
 // cues 7 and 9):
 //   R(tt, et)  router logits for a tile of tokens x experts (fixed-order fp32)
-//   K(tt)      top-k + routing weights for the tile's tokens      waits ev_logit[tt]
+//   K(tt)      top-k + routing weights for the tile's tokens; notifies
+//              ev_exp[e] once per routed (token, slot)           waits ev_logit[tt]
 //   S          counts, exp_indptr, stable permutation, row tiles   waits ev_route
-//   D(dt)      copy routed rows into expert-grouped order and notify
-//              ev_exp[e] once per routed (token, slot)             waits ev_scan
-//   G1(rt, nt) gate/up GEMM + SwiGLU for one row tile of one expert waits ev_exp[e]
-//              (ev_exp[e] is released after counts[e] notifies: the
-//              data-dependent update; expert e's tiles cover grouped rows
+//   G1(rt, nt) gate/up GEMM + SwiGLU for one row tile of one expert, its
+//              rows gathered from x through the permutation   waits ev_scan and
+//              ev_exp[e] (released after counts[e] arrivals: the data-dependent
+//              update; expert e's tiles cover grouped rows
 //              [exp_indptr[e], exp_indptr[e+1]): the data-dependent trigger)
 //   G2(rt, nt) down projection                                     waits ev_h[rt]
 //   C(ct)      weighted combine of the k expert rows per token     waits ev_c[ct]
@@ -24,7 +24,7 @@
 // from it in the kernel (Fig. 4: one template, instantiated per launch).
 //
 // Data that one workgroup writes and another reads (logits, routing tensors,
-// grouped rows Xp, intermediate Hmid, expert outputs Y) moves through
+// intermediate Hmid, expert outputs Y) moves through
 // device-coherent loads and stores (etc_rt.h); weights and input tokens are
 // read through the caches.
 #include <hip/hip_runtime.h>
@@ -85,7 +85,6 @@ __device__ __forceinline__ rsrc_t r_tptr(const MoeParams& p) {
   return make_rsrc(p.tile_indptr, (uint32_t)(p.E + 1) * 4u);
 }
 __device__ __forceinline__ rsrc_t r_rtinfo(const MoeParams& p) { return make_rsrc(p.rt_info, (uint32_t)p.max_rt * 16u); }
-__device__ __forceinline__ rsrc_t r_xp(const MoeParams& p) { return make_rsrc(p.xp, p.xp_bytes); }
 __device__ __forceinline__ rsrc_t r_hh(const MoeParams& p) { return make_rsrc(p.hh, p.hh_bytes); }
 __device__ __forceinline__ rsrc_t r_y(const MoeParams& p) { return make_rsrc(p.y, p.y_bytes); }
 
@@ -107,7 +106,7 @@ struct Ctx {
   uint32_t* status;  // where error bits go
   uint64_t* queue;
   int T, H, E, k, I;
-  int nTT, nET, nR, nK, nD, nC, nN1, nN2;
+  int nTT, nET, nR, nK, nC, nN1, nN2;
   uint64_t budget;  // watchdog of one wait, wall-clock ticks
 };
 
@@ -121,7 +120,6 @@ __device__ __forceinline__ Ctx make_ctx(const MoeParams& p, uint32_t* set) {
   c.nET = (p.E + kRouterE - 1) / kRouterE;
   c.nR = c.nTT * c.nET;
   c.nK = c.nTT;
-  c.nD = (p.T + kDispatchT - 1) / kDispatchT;
   c.nC = (p.T + kCombineT - 1) / kCombineT;
   c.nN1 = p.I / kBN1;
   c.nN2 = p.H / kBN2;
@@ -134,8 +132,7 @@ struct Shared {
   int n;           // number of completed events collected by this task
   int base;        // first reserved queue slot
   int total;       // descriptors to write
-  int list[kDispatchT * kMaxK + kBM];
-  int pref[kDispatchT * kMaxK + kBM + 1];
+  int list[kBM];
   int pairs[2 * kCombineT * kMaxK];  // D: slots; C: (weight, slot) pairs
 };
 
@@ -174,6 +171,35 @@ __device__ __forceinline__ void trace_task(const MoeParams& p, int type, int a, 
   q[5] = (uint32_t)ts;
   q[6] = (uint32_t)tb;
   q[7] = (uint32_t)te;
+}
+
+// ====================================================== event helpers ========
+// Event elements live in the launch's counter set; see etc_rt.h for the
+// counting and coherence rules.
+__device__ __forceinline__ uint32_t* ev_logit(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_logit; }
+__device__ __forceinline__ uint32_t* ev_exp(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_exp; }
+__device__ __forceinline__ uint32_t* ev_h(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_h; }
+__device__ __forceinline__ uint32_t* ev_c(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_c; }
+__device__ __forceinline__ uint32_t ctile_target(const Ctx& c, int ct) {
+  return (uint32_t)(min(kCombineT, c.T - ct * kCombineT) * c.k * c.nN2);
+}
+
+// Notify one event element; returns true if this notify completed it.
+__device__ __forceinline__ bool notify1(const Ctx& c, uint32_t* ev, uint32_t target) {
+  const uint32_t old = add_relaxed(ev, 1u);
+  if (old + 1u > target) or_relaxed(c.status, ST_OVER_NOTIFY | ST_ABORT);
+  return old + 1u == target;
+}
+
+// Notify without checking for over-notification unless the debug buffer is
+// set (then notify1 records any notify past the wait count).
+__device__ __forceinline__ void notify_fast(const MoeParams& p, const Ctx& c, uint32_t* ev, uint32_t target) {
+  if (p.debug) {
+    asm volatile("" ::: "memory");  // keeps the two atomics from being merged into one returning atomic
+    notify1(c, ev, target);
+  } else {
+    (void)__hip_atomic_fetch_add(ev, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ===================================================== task bodies ==========
@@ -327,6 +353,15 @@ __device__ void task_topk(const MoeParams& p, const Ctx& c, int tt) {
     const uint32_t off = (uint32_t)(t * c.k + lane) * 4u;
     co_st32(r_ids(p), off, (uint32_t)my_e);
     co_stf(r_topw(p), off, expf(my_v - v0) / part);
+    // the routed (token, slot) joins its expert's event: ev_exp[e] counts
+    // arrivals up to counts[e], a wait count known only once S has run
+    // (data-dependent event update).  Nothing it guards is written here
+    // (G1 reads x, an input, and S's tables, ordered by S's own event), so
+    // the notify needs no drain.
+    if (c.set) {
+      notify_fast(p, c, ev_exp(p, c) + my_e, 0xffffffffu);
+      if (p.debug) atomicAdd(p.debug + my_e, 1);
+    }
   }
 }
 
@@ -398,6 +433,11 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
     co_st32(ri, (uint32_t)tid * 4u, (uint32_t)ex);
     co_st32(rtp, (uint32_t)tid * 4u, (uint32_t)ext);
   }
+  if (tid < E && c.set && p.debug) {
+    // every routed pair has notified by now (S runs after all of K): the
+    // expert event holds exactly counts[e] arrivals and fires once
+    if (my > 0 && ld_relaxed(ev_exp(p, c) + tid) == (uint32_t)my) atomicAdd(p.debug + E + tid, 1);
+  }
   if (tid == 0) {
     iptr[E] = tot_rows;
     tptr[E] = tot_tiles;
@@ -429,39 +469,6 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   }
 }
 
-// D: copy every routed row of the task's tokens into expert-grouped order,
-// Xp[slot[t*k+j], :] = X[t, :] (16-byte chunks).
-__device__ void task_dispatch_copy(const MoeParams& p, const Ctx& c, int dt, int* s_slot) {
-  const int t0 = dt * kDispatchT;
-  const int ntok = min(kDispatchT, c.T - t0);
-  const int rows = ntok * c.k;
-  const int cpr = c.H >> 3;
-  const rsrc_t rx = r_xp(p);
-  if (threadIdx.x < rows) s_slot[threadIdx.x] = (int)co_ld32(r_slot(p), (uint32_t)(t0 * c.k + threadIdx.x) * 4u);
-  __syncthreads();
-  constexpr int U = 8;
-  const int items = rows * cpr;
-  for (int i0 = threadIdx.x; i0 < items; i0 += kThreads * U) {
-    u32x4_t v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * kThreads;
-      if (i < items) {
-        const int r = i / cpr, ch = i - r * cpr;
-        v[u] = ld4(p.x + (size_t)(t0 + r / c.k) * c.H + ch * 8);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * kThreads;
-      if (i < items) {
-        const int r = i / cpr, ch = i - r * cpr;
-        co_st128(rx, (uint32_t)((size_t)s_slot[r] * c.H + ch * 8) * 2u, v[u]);
-      }
-    }
-  }
-}
-
 // Grouped-GEMM tasks.  A row tile holds up to kBM = 64 grouped rows of one
 // expert: NB = 1, 2 or 4 row blocks of 16 (three round up to four).  The 4
 // waves always split K in quarters, and each wave multiplies every row block
@@ -475,21 +482,32 @@ __device__ __forceinline__ int row_blocks(int nrows) { return nrows <= 16 ? 1 : 
 // SwiGLU, Hmid = bf16(silu(g) * u).  bf16 MFMA 16x16x32 with fp32
 // accumulation; the weight slab (2 x 16 rows x H) streams from HBM straight
 // into registers; rows past the expert's count are zero-filled, never loaded.
+// The A rows are gathered from x itself: grouped row r of the tile is token
+// perm[r] / k (the dispatch is fused into this load), and x is never written
+// during a launch, so ordinary cached loads serve.  `tok` holds, per lane,
+// the token of row 16 b + (lane % 16) of each row block when the caller has
+// loaded them ahead; otherwise they are loaded here.
+__device__ __forceinline__ uint32_t row_perm(const MoeParams& p, const RowTile tile, int b) {
+  const int r = b * 16 + (threadIdx.x & 15);
+  return r < tile.nrows ? co_ld32(r_perm(p), (uint32_t)(tile.r0 + r) * 4u) : 0u;
+}
 template <int NB, int U>
-__device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const RowTile tile, int nt, float* red) {
+__device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const RowTile tile, int nt, float* red,
+                                        const uint32_t* pre) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int m = lane & 15, kg = lane >> 4;
   const int H = c.H, I = c.I;
   const int kw = H >> 2;
   const int nsteps = kw >> 5;
-  const rsrc_t rx = r_xp(p);
   bool valid[NB];
-  uint32_t aoff[NB];
+  const uint16_t* pa[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int r = b * 16 + m;
     valid[b] = r < tile.nrows;
-    aoff[b] = (uint32_t)(((size_t)(tile.r0 + (valid[b] ? r : 0)) * H + wv * kw + kg * 8) * 2);
+    const uint32_t f = pre ? pre[b] : row_perm(p, tile, b);
+    const int t = valid[b] ? (int)(f / (uint32_t)c.k) : 0;
+    pa[b] = p.x + (size_t)t * H + wv * kw + kg * 8;
   }
   const uint16_t* pg = p.w13 + ((size_t)tile.e * 2 * I + (size_t)nt * kBN1 + m) * H + wv * kw + kg * 8;
   const uint16_t* pu = pg + (size_t)I * H;
@@ -505,7 +523,7 @@ __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const 
     for (int u = 0; u < U; ++u) {
       if (s0 + u < nsteps) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) a[u][b] = valid[b] ? co_ld128(rx, aoff[b] + (uint32_t)(s0 + u) * 64u) : zero;
+        for (int b = 0; b < NB; ++b) a[u][b] = valid[b] ? ld4(pa[b] + (s0 + u) * 32) : zero;
         bg[u] = ld4(pg + (s0 + u) * 32);
         bu[u] = ld4(pu + (s0 + u) * 32);
       }
@@ -561,12 +579,13 @@ __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const 
   }
 }
 
-__device__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt, float* red) {
+__device__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt, float* red,
+                        const uint32_t* pre = nullptr) {
   (void)rt;
   switch (row_blocks(tile.nrows)) {
-    case 1: g1_body<1, 8>(p, c, tile, nt, red); break;
-    case 2: g1_body<2, 6>(p, c, tile, nt, red); break;
-    default: g1_body<4, 4>(p, c, tile, nt, red); break;
+    case 1: g1_body<1, 8>(p, c, tile, nt, red, pre); break;
+    case 2: g1_body<2, 6>(p, c, tile, nt, red, pre); break;
+    default: g1_body<4, 4>(p, c, tile, nt, red, pre); break;
   }
 }
 
@@ -706,21 +725,6 @@ __device__ void task_combine(const MoeParams& p, const Ctx& c, int ct, int* s_pa
 }
 
 // =================================================== event plumbing ========
-__device__ __forceinline__ uint32_t* ev_logit(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_logit; }
-__device__ __forceinline__ uint32_t* ev_exp(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_exp; }
-__device__ __forceinline__ uint32_t* ev_h(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_h; }
-__device__ __forceinline__ uint32_t* ev_c(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_c; }
-__device__ __forceinline__ uint32_t ctile_target(const Ctx& c, int ct) {
-  return (uint32_t)(min(kCombineT, c.T - ct * kCombineT) * c.k * c.nN2);
-}
-
-// Notify one event element; returns true if this notify completed it.
-__device__ __forceinline__ bool notify1(const Ctx& c, uint32_t* ev, uint32_t target) {
-  const uint32_t old = add_relaxed(ev, 1u);
-  if (old + 1u > target) or_relaxed(c.status, ST_OVER_NOTIFY | ST_ABORT);
-  return old + 1u == target;
-}
-
 // Reserve `n` queue slots (thread 0); returns the first, or -1 on overflow.
 __device__ __forceinline__ int64_t q_reserve(const MoeParams& p, const Ctx& c, int n) {
   const uint32_t base = add_relaxed(c.set + W_TAIL, (uint32_t)n);
@@ -765,71 +769,23 @@ __device__ void after_scan(const MoeParams& p, const Ctx& c, Shared& sh) {
   if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC) {
     wg_publish();
     if (MODE == MODE_DYNAMIC) {
+      // every expert event is complete once S runs (K notified all routed
+      // pairs before S was pushed), so S pushes the G1 tiles of all experts
       if (threadIdx.x == 0) {
         const uint32_t nrt = ld_relaxed(p.meta + M_NRT);
-        const uint32_t total = (uint32_t)(c.nR + c.nK + 1 + c.nD + c.nC) + nrt * (uint32_t)(c.nN1 + c.nN2);
+        const uint32_t total = (uint32_t)(c.nR + c.nK + 1 + c.nC) + nrt * (uint32_t)(c.nN1 + c.nN2);
         xchg_relaxed(c.set + W_TOTAL, total);
-        sh.base = (int)q_reserve(p, c, c.nD);
+        sh.n = (int)(nrt * (uint32_t)c.nN1);
+        sh.base = (int)q_reserve(p, c, sh.n);
       }
       __syncthreads();
-      const int base = sh.base;
+      const int base = sh.base, n1 = sh.n;
       if (base >= 0)
-        for (int i = threadIdx.x; i < c.nD; i += kThreads) q_put(c, base + i, make_desc(TT_D, i, 0));
+        for (int i = threadIdx.x; i < n1; i += kThreads) q_put(c, base + i, make_desc(TT_G1, i / c.nN1, i % c.nN1));
       __syncthreads();
     } else {
       if (threadIdx.x == 0) notify1(c, c.set + W_EV_SCAN, 1u);
     }
-  }
-}
-
-template <int MODE>
-__device__ void after_dispatch(const MoeParams& p, const Ctx& c, int dt, Shared& sh) {
-  if (MODE != MODE_STATIC && MODE != MODE_DYNAMIC) return;
-  const int t0 = dt * kDispatchT;
-  const int rows = min(kDispatchT, c.T - t0) * c.k;
-  wg_publish();
-  if (threadIdx.x == 0) sh.n = 0;
-  __syncthreads();
-  if (threadIdx.x < rows) {
-    const int f = t0 * c.k + threadIdx.x;
-    const int e = (int)co_ld32(r_ids(p), (uint32_t)f * 4u);
-    const uint32_t target = co_ld32(r_counts(p), (uint32_t)e * 4u);
-    const bool done = notify1(c, ev_exp(p, c) + e, target);
-    if (p.debug) {
-      atomicAdd(p.debug + e, 1);
-      if (done) atomicAdd(p.debug + c.E + e, 1);
-    }
-    if (done && MODE == MODE_DYNAMIC) sh.list[atomicAdd(&sh.n, 1)] = e;
-  }
-  if (MODE == MODE_DYNAMIC) {
-    __syncthreads();
-    const int n = sh.n;
-    if (n == 0) return;
-    if (threadIdx.x == 0) {
-      const rsrc_t rtp = r_tptr(p);
-      int acc = 0;
-      for (int i = 0; i < n; ++i) {
-        sh.pref[i] = acc;
-        const int e = sh.list[i];
-        acc += ((int)co_ld32(rtp, (uint32_t)(e + 1) * 4u) - (int)co_ld32(rtp, (uint32_t)e * 4u)) * c.nN1;
-      }
-      sh.pref[n] = acc;
-      sh.total = acc;
-      sh.base = (int)q_reserve(p, c, acc);
-    }
-    __syncthreads();
-    const int base = sh.base, total = sh.total;
-    if (base >= 0) {
-      const rsrc_t rtp = r_tptr(p);
-      for (int i = threadIdx.x; i < total; i += kThreads) {
-        int j = 0;
-        while (j + 1 < n && i >= sh.pref[j + 1]) ++j;
-        const int li = i - sh.pref[j];
-        const int rt = (int)co_ld32(rtp, (uint32_t)sh.list[j] * 4u) + li / c.nN1;
-        q_put(c, base + i, make_desc(TT_G1, rt, li % c.nN1));
-      }
-    }
-    __syncthreads();
   }
 }
 
@@ -913,14 +869,6 @@ __device__ bool grid_barrier(const Ctx& c) {
 // polling.  Only wave 0 writes a task's outputs, so only wave 0 drains its
 // stores before the notify; the notify needs no workgroup barrier.  With the
 // debug buffer the notify also checks for over-notification.
-__device__ __forceinline__ void notify_fast(const MoeParams& p, const Ctx& c, uint32_t* ev, uint32_t target) {
-  if (p.debug) {
-    asm volatile("" ::: "memory");  // keeps the two atomics from being merged into one returning atomic
-    notify1(c, ev, target);
-  } else {
-    (void)__hip_atomic_fetch_add(ev, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
 
 __device__ bool wait_known(const uint32_t* ctr, uint32_t target, uint32_t known, const Ctx& c) {
   int fail = 0;
@@ -945,6 +893,10 @@ __device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int 
     cur_tgt = co_ld32(rcnt, (uint32_t)cur.e * 4u);
     cur_arr = ld_relaxed(evx + cur.e);
   }
+  // grouped-row permutation entries of the tile's rows (A gather), one task ahead
+  uint32_t cur_f[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) cur_f[b] = row_perm(p, cur, b);
   for (int i = i0; i < n; i += G) {
     const int rt = i / c.nN1, nt = i % c.nN1;
     if (tr) tw = now_ticks();
@@ -957,7 +909,10 @@ __device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int 
       nxt_tgt = co_ld32(rcnt, (uint32_t)nxt.e * 4u);
       nxt_arr = ld_relaxed(evx + nxt.e);
     }
-    task_g1(p, c, cur, rt, nt, red);
+    uint32_t nxt_f[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) nxt_f[b] = i + G < n ? row_perm(p, nxt, b) : 0u;
+    task_g1(p, c, cur, rt, nt, red, cur_f);
     if (threadIdx.x == 0) {  // wave 0 wrote the tile: drain its stores, then notify
       __builtin_amdgcn_s_waitcnt(0);
       notify_fast(p, c, evh + rt, (uint32_t)c.nN1);
@@ -969,6 +924,8 @@ __device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int 
     nxt = nn;
     cur_tgt = nxt_tgt;
     cur_arr = nxt_arr;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) cur_f[b] = nxt_f[b];
   }
 }
 
@@ -1060,17 +1017,6 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
   }
   off += 1;
   if (!EV && !grid_barrier(c)) return;
-  for (int i = first_of(w, off, G); i < c.nD; i += G) {
-    if (tr) tw = now_ticks();
-    if (EV && !wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;
-    if (tr) ts = now_ticks();
-    task_dispatch_copy(p, c, i, sh.pairs);
-    if (tr) tb = now_ticks();
-    dbg_task(p, TT_D);
-    after_dispatch<MODE>(p, c, i, sh);
-    trace_task(p, TT_D, i, 0, tw, ts, tb);
-  }
-  off += c.nD;
   if (EV) {
     if (!wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;
   } else if (!grid_barrier(c)) {
@@ -1180,13 +1126,6 @@ __device__ void run_dynamic(const MoeParams& p, const Ctx& c, uint8_t* smem, Sha
         after_scan<MODE_DYNAMIC>(p, c, sh);
         trace_task(p, TT_S, a, b, tw, ts, tb);
         break;
-      case TT_D:
-        task_dispatch_copy(p, c, a, sh.pairs);
-        if (tr) tb = now_ticks();
-        dbg_task(p, TT_D);
-        after_dispatch<MODE_DYNAMIC>(p, c, a, sh);
-        trace_task(p, TT_D, a, b, tw, ts, tb);
-        break;
       case TT_G1:
         task_g1(p, c, load_rowtile(p, a), a, b, red);
         if (tr) tb = now_ticks();
@@ -1262,11 +1201,6 @@ __global__ void __launch_bounds__(kThreads) kbk_scan(MoeParams p) {
   const Ctx c = make_ctx(p, nullptr);
   task_scan(p, c, smem);
 }
-__global__ void __launch_bounds__(kThreads) kbk_dispatch(MoeParams p) {
-  __shared__ int pairs[2 * kCombineT * kMaxK];
-  const Ctx c = make_ctx(p, nullptr);
-  task_dispatch_copy(p, c, blockIdx.x, pairs);
-}
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) kbk_g1(MoeParams p) {
   __shared__ float red[4 * 4 * 256 + kBM * 64 / 2];
   const Ctx c = make_ctx(p, nullptr);
@@ -1330,7 +1264,6 @@ int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int nTT = (p.T + kRouterT - 1) / kRouterT;
   const int nET = (p.E + kRouterE - 1) / kRouterE;
-  const int nD = (p.T + kDispatchT - 1) / kDispatchT;
   const int nC = (p.T + kCombineT - 1) / kCombineT;
   const int64_t rows = (int64_t)p.T * p.k;
   const int64_t max_rt = (rows + kBM - 1) / kBM + (rows < p.E ? rows : p.E);
@@ -1338,7 +1271,6 @@ int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream) {
   hipLaunchKernelGGL(kbk_router, dim3(nTT * nET), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_topk, dim3(nTT), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_scan, dim3(1), dim3(kThreads), lds_bytes, s, p);
-  hipLaunchKernelGGL(kbk_dispatch, dim3(nD), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_g1, dim3((unsigned)(max_rt * nN1)), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_g2, dim3((unsigned)(max_rt * nN2)), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_combine, dim3(nC), dim3(kThreads), 0, s, p);

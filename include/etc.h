@@ -206,7 +206,9 @@ typedef struct {
   int32_t bn1;         /* gate (and up) columns per G1 tile                 */
   int32_t bn2;         /* output columns per G2 tile                        */
   int32_t router_tokens, router_experts; /* R tile                          */
-  int32_t dispatch_tokens, combine_tokens;
+  int32_t dispatch_tokens; /* tokens per dispatch task; 0: there are none, the
+                              gate/up tiles gather their rows from x      */
+  int32_t combine_tokens;
   int32_t grid;        /* persistent workgroups (0 before the first query)  */
   int32_t threads;     /* threads per workgroup                             */
   int32_t lds_bytes;   /* dynamic LDS per workgroup                         */
