@@ -143,6 +143,23 @@ def test_task_trace(qwen_weights, decode_case, sched):
         assert (a <= b).all()
 
 
+@pytest.mark.parametrize("sched", ["static", "barrier"])
+def test_watchdog_timeout_is_reported_and_workspace_recovers(qwen_layer, decode_case, sched):
+    # a 1 us wait budget makes the first wait that has to poll give up: the
+    # launch aborts, every other wait sees the abort, the grid drains, and
+    # etc_sync reports ETC_ERR_TIMEOUT.  The next launch on the same workspace
+    # (counter sets reset by the epoch, also after an abort) is correct.
+    X, ref = decode_case
+    B = qwen_layer.B
+    announce(f"decode watchdog 1us sched={sched}")
+    got = qwen_layer.run(X, sched, watchdog_us=1, check_status=False)
+    assert got["rc"] == B.ETC_ERR_TIMEOUT
+    announce(f"decode after watchdog sched={sched}")
+    again = qwen_layer.run(X, sched)
+    assert_routing_equal(again, ref)
+    assert_rows_close(again["out"], ref["out"])
+
+
 # --------------------------------------------------------------- prefill --
 def _sample_tokens(ids, T, n_each=4):
     hot = np.bincount(ids.reshape(-1)).argmax()
