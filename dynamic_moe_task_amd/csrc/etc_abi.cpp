@@ -410,7 +410,6 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
   p.set0 = reinterpret_cast<uint32_t*>(ws + L.b_set0);
   p.set1 = reinterpret_cast<uint32_t*>(ws + L.b_set1);
   p.meta = reinterpret_cast<uint32_t*>(ws + L.b_meta);
-  p.tile_indptr = reinterpret_cast<int32_t*>(ws + L.b_tile_indptr);
   p.rt_info = reinterpret_cast<int32_t*>(ws + L.b_rt_info);
   p.logits = reinterpret_cast<float*>(ws + L.b_logits);
   p.hh = reinterpret_cast<uint16_t*>(ws + L.b_hh);

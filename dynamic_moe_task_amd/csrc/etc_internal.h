@@ -70,7 +70,7 @@ struct MoeLayout {
   int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_c, o_queue;  // o_queue in words, 8-byte aligned
   int64_t set_words;
   // byte offsets inside the workspace
-  int64_t b_ctrl, b_set0, b_set1, b_meta, b_tile_indptr, b_rt_info, b_logits, b_hh, b_y;
+  int64_t b_ctrl, b_set0, b_set1, b_meta, b_rt_info, b_logits, b_hh, b_y;
   int64_t total_bytes;
 };
 
@@ -103,7 +103,6 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
   L.b_set0 = b;          b += L.set_words * 4;
   L.b_set1 = b;          b += L.set_words * 4;
   L.b_meta = b;          b += M_WORDS * 4;
-  L.b_tile_indptr = b;   b += align_up((int64_t)(d.E + 1) * 4, 256);
   L.b_rt_info = b;       b += align_up((int64_t)L.max_rt * 16, 256);
   L.b_logits = b;        b += align_up(Tm * d.E * 4, 256);
   L.b_hh = b;            b += align_up(rows * d.I * 2, 256);
@@ -113,10 +112,10 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
 }
 
 // LDS bytes the scan task needs: presence bitmap, per-word prefix (u16),
-// counts / exp_indptr / tile_indptr scratch.
+// counts / exp_indptr scratch and the scan's partial sums.
 inline int64_t scan_lds_bytes(int E, int T_max) {
   const int64_t W = cdiv(T_max, 32);
-  return align_up((int64_t)E * W * 4, 16) + align_up((int64_t)E * W * 2, 16) + 3 * 260 * 4 + 64;
+  return align_up((int64_t)E * W * 4, 16) + align_up((int64_t)E * W * 2, 16) + 2 * 260 * 4 + 64;
 }
 // G2: cross-wave reduction buffer (4 waves x 4 blocks x 256 fp32) plus the
 // bf16 staging of the kBM x 64 output tile
@@ -140,7 +139,6 @@ struct MoeParams {
   uint32_t* set0;
   uint32_t* set1;
   uint32_t* meta;
-  int32_t* tile_indptr;
   int32_t* rt_info;  // [max_rt][4]: expert, first grouped row, rows, 0
   float* logits;
   uint16_t* hh;

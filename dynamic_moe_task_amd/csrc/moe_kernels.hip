@@ -81,9 +81,6 @@ __device__ __forceinline__ rsrc_t r_perm(const MoeParams& p) { return make_rsrc(
 __device__ __forceinline__ rsrc_t r_slot(const MoeParams& p) { return make_rsrc(p.slot, p.rows_bytes); }
 __device__ __forceinline__ rsrc_t r_counts(const MoeParams& p) { return make_rsrc(p.counts, (uint32_t)p.E * 4u); }
 __device__ __forceinline__ rsrc_t r_indptr(const MoeParams& p) { return make_rsrc(p.indptr, (uint32_t)(p.E + 1) * 4u); }
-__device__ __forceinline__ rsrc_t r_tptr(const MoeParams& p) {
-  return make_rsrc(p.tile_indptr, (uint32_t)(p.E + 1) * 4u);
-}
 __device__ __forceinline__ rsrc_t r_rtinfo(const MoeParams& p) { return make_rsrc(p.rt_info, (uint32_t)p.max_rt * 16u); }
 __device__ __forceinline__ rsrc_t r_hh(const MoeParams& p) { return make_rsrc(p.hh, p.hh_bytes); }
 __device__ __forceinline__ rsrc_t r_y(const MoeParams& p) { return make_rsrc(p.y, p.y_bytes); }
@@ -392,6 +389,11 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
 // stable permutation (rows of one expert keep ascending token order) and
 // the row-tile table.  One workgroup; a per-expert token bitmap in LDS gives
 // each routed pair its rank among the same expert's earlier tokens.
+//
+// Row tiles are numbered heaviest first: tiles of four 16-row blocks (more
+// than 32 rows), then of two, then of one, each class in expert order.  The
+// lists deal G1 and G2 tasks in tile order, so the longest tasks start first
+// and the short ones fill in at the end (longest processing time first).
 __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   const int tid = threadIdx.x;
   const int E = c.E, k = c.k, n = c.T * c.k;
@@ -400,8 +402,7 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   uint16_t* pre = reinterpret_cast<uint16_t*>(smem + ((E * W * 4 + 15) & ~15));
   int* cnt = reinterpret_cast<int*>(smem + ((E * W * 4 + 15) & ~15) + ((E * W * 2 + 15) & ~15));
   int* iptr = cnt + 260;
-  int* tptr = iptr + 260;
-  int* tmp = tptr + 260;
+  int* tmp = iptr + 260;
   const rsrc_t rids = r_ids(p);
   for (int i = tid; i < E * W; i += kThreads) bits[i] = 0u;
   __syncthreads();
@@ -422,16 +423,20 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   __syncthreads();
   const int my = tid < E ? cnt[tid] : 0;
   const int mytiles = (my + kBM - 1) / kBM;
-  int tot_rows = 0, tot_tiles = 0;
+  const int rem = my % kBM;
+  const int n4 = my / kBM + (rem > 32 ? 1 : 0), n2 = (rem > 16 && rem <= 32) ? 1 : 0,
+            n1 = (rem > 0 && rem <= 16) ? 1 : 0;
+  int tot_rows = 0, tot_tiles = 0, tot4 = 0, tot2 = 0, tot1 = 0;
   const int ex = block_excl_scan(my, tmp, &tot_rows);
-  const int ext = block_excl_scan(mytiles, tmp + 8, &tot_tiles);
-  const rsrc_t rc = r_counts(p), ri = r_indptr(p), rtp = r_tptr(p);
+  (void)block_excl_scan(mytiles, tmp, &tot_tiles);
+  const int ex4 = block_excl_scan(n4, tmp, &tot4);
+  const int ex2 = block_excl_scan(n2, tmp, &tot2);
+  const int ex1 = block_excl_scan(n1, tmp, &tot1);
+  const rsrc_t rc = r_counts(p), ri = r_indptr(p);
   if (tid < E) {
     iptr[tid] = ex;
-    tptr[tid] = ext;
     co_st32(rc, (uint32_t)tid * 4u, (uint32_t)my);
     co_st32(ri, (uint32_t)tid * 4u, (uint32_t)ex);
-    co_st32(rtp, (uint32_t)tid * 4u, (uint32_t)ext);
   }
   if (tid < E && c.set && p.debug) {
     // every routed pair has notified by now (S runs after all of K): the
@@ -440,9 +445,7 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   }
   if (tid == 0) {
     iptr[E] = tot_rows;
-    tptr[E] = tot_tiles;
     co_st32(ri, (uint32_t)E * 4u, (uint32_t)tot_rows);
-    co_st32(rtp, (uint32_t)E * 4u, (uint32_t)tot_tiles);
     st_relaxed(p.meta + M_NRT, (uint32_t)tot_tiles);
   }
   __syncthreads();
@@ -456,15 +459,16 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
     co_st32(rp, (uint32_t)s * 4u, (uint32_t)f);
   }
   const rsrc_t rr = r_rtinfo(p);
-  for (int e = tid; e < E; e += kThreads) {
-    const int ce = cnt[e];
-    for (int mt = 0; mt * kBM < ce; ++mt) {
+  if (tid < E) {
+    for (int mt = 0; mt * kBM < my; ++mt) {
+      const int rows = min(kBM, my - mt * kBM);
+      const int rt = rows > 32 ? ex4 + mt : (rows > 16 ? tot4 + ex2 : tot4 + tot2 + ex1);
       u32x4_t q;
-      q.x = (uint32_t)e;
-      q.y = (uint32_t)(iptr[e] + mt * kBM);
-      q.z = (uint32_t)min(kBM, ce - mt * kBM);
+      q.x = (uint32_t)tid;
+      q.y = (uint32_t)(ex + mt * kBM);
+      q.z = (uint32_t)rows;
       q.w = 0u;
-      co_st128(rr, (uint32_t)(tptr[e] + mt) * 16u, q);
+      co_st128(rr, (uint32_t)rt * 16u, q);
     }
   }
 }
