@@ -221,7 +221,29 @@ EDGE = [
     (3, 128, 1, 1, 128, True, False, 4),       # one expert: dense MLP
     (64, 384, 256, 16, 128, False, False, 64), # E = 256, k = 16, plain softmax weights
     (2, 640, 64, 6, 384, True, False, 2),      # most experts get no token
+    (4096, 128, 64, 8, 128, True, False, 4096),  # largest T: T == T_max == 4096, E * ceil(T_max/32) == 8192
+    (8, 16384, 8, 2, 128, True, False, 8),     # largest hidden size
+    (8, 128, 8, 2, 16384, True, False, 8),     # largest expert intermediate size
 ]
+
+
+_EDGE_CACHE = {}
+
+
+def _edge_inputs(case):
+    # inputs and the oracle's result, computed once per case for all schedules
+    # (a few hundred MB at most over all cases)
+    if case not in _EDGE_CACHE:
+        T, H, E, k, I, norm, has_bias, T_max = case
+        rng = np.random.default_rng(T * 7919 + E)
+        Wr = wl.to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.05))
+        W13 = wl.to_bf16_bits(rng.standard_normal((E, 2 * I, H), dtype=np.float32) * np.float32(0.05))
+        Wd = wl.to_bf16_bits(rng.standard_normal((E, H, I), dtype=np.float32) * np.float32(0.05))
+        X = wl.to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+        bias = (rng.standard_normal(E) * 0.5).astype(np.float32) if has_bias else None
+        ref = oracle.moe(X, Wr, W13, Wd, k=k, norm_topk=norm, bias=bias)
+        _EDGE_CACHE[case] = (Wr, W13, Wd, X, bias, ref)
+    return _EDGE_CACHE[case]
 
 
 @pytest.mark.parametrize("case", EDGE, ids=[f"T{c[0]}H{c[1]}E{c[2]}k{c[3]}I{c[4]}" for c in EDGE])
@@ -229,14 +251,8 @@ EDGE = [
                                    "kbk", "barrier"])
 def test_edge_shapes(case, sched):
     T, H, E, k, I, norm, has_bias, T_max = case
-    rng = np.random.default_rng(T * 7919 + E)
-    Wr = wl.to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.05))
-    W13 = wl.to_bf16_bits(rng.standard_normal((E, 2 * I, H), dtype=np.float32) * np.float32(0.05))
-    Wd = wl.to_bf16_bits(rng.standard_normal((E, H, I), dtype=np.float32) * np.float32(0.05))
-    X = wl.to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
-    bias = (rng.standard_normal(E) * 0.5).astype(np.float32) if has_bias else None
+    Wr, W13, Wd, X, bias, ref = _edge_inputs(case)
     announce(f"edge {case} sched={sched}")
-    ref = oracle.moe(X, Wr, W13, Wd, k=k, norm_topk=norm, bias=bias)
     layer = DeviceLayer((H, E, k, I), Wr, W13, Wd, T_max=T_max, bias=bias, norm_topk=norm)
     got = layer.run(X, sched)
     assert_routing_equal(got, ref)
