@@ -261,6 +261,32 @@ def measure_sweep(Wr, w13s, w2s, sp, steps):
     }
 
 
+def measure_token_counts(Wr, w13s, w2s, sp, steps, warmup, repeat, counts=(1, 128, 1024)):
+    """The pages compare schedules on the same MoE layer at several token
+    counts (Event Tensor paper, Table 2).  Same Qwen3-30B-A3B shape, no bias;
+    µs per layer of each schedule and the static/barrier ratio."""
+    import torch
+    from dynamic_moe_task_amd import binding as B
+    from dynamic_moe_task_amd import workloads as wl
+    shape = wl.DECODE
+    out = {}
+    for T in counts:
+        X = wl.make_tokens(shape, T, 0)
+        desc = B.moe_desc(T, shape.H, shape.E, shape.k, shape.I, shape.norm_topk, False)
+        bufs = B.MoELayerBuffers.allocate(desc, Wr, w13s[0], w2s[0], None)
+        bufs.x[:T].copy_(dev_bf16(X))
+        us = {s: float(np.median([time_sched(bufs, T, s, steps, warmup, w13s, w2s, sp) for _ in range(repeat)]))
+              for s in ("static", "barrier", "kbk")}
+        out[f"T={T}"] = {"us_per_layer": {s: round(v, 2) for s, v in us.items()},
+                         "static_over_barrier_speedup": round(us["barrier"] / us["static"], 3),
+                         "static_over_kbk_speedup": round(us["kbk"] / us["static"], 3)}
+        del bufs
+        torch.cuda.synchronize()
+    out["note"] = ("T=4096 (the pages' largest count) exceeds this build's routing-bitmap limit "
+                   "E*ceil(T_max/32) <= 8192 at E=128")
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -348,6 +374,7 @@ def main():
     if not a.no_extra and a.workload == "decode":
         extra["prefill_zipf"] = measure_prefill(Wr, w13s, w2s, sp, max(10, a.steps // 2), a.warmup, a.repeat)
         extra["sweep"] = measure_sweep(Wr, w13s, w2s, sp, a.sweep_steps)
+        extra["token_counts"] = measure_token_counts(Wr, w13s, w2s, sp, max(10, a.steps // 2), a.warmup, a.repeat)
 
     cpu = None
     if not a.no_cpu:

@@ -4,11 +4,12 @@
  * One Mixture-of-Experts layer runs as ONE persistent HIP kernel that executes
  * a graph of tiled tasks coordinated through event tensors in HBM:
  *
- *   R(t-tile, e-tile) router logits  --ev_logit-->  K(t-tile) top-k + weights
- *   --ev_route--> S scan: counts, exp_indptr, permutation, per-expert event
- *   initialisation --ev_scan--> D(t-tile) dispatch rows, notify ev_exp[e]
- *   --ev_exp[e]--> G1(row tile, n-tile) gate/up + SwiGLU --ev_h[row tile]-->
- *   G2(row tile, n-tile) down projection --ev_c[t-tile]--> C(t-tile) combine.
+ *   R(t-tile, e-tile) router logits  --ev_logit-->  K(t-tile) top-k + weights,
+ *   one ev_exp[e] arrival per routed (token, slot)  --ev_route--> S scan:
+ *   counts (the wait counts of ev_exp), exp_indptr, permutation, row tiles
+ *   --ev_scan, ev_exp[e]--> G1(row tile, n-tile) gate/up + SwiGLU on rows
+ *   gathered from x --ev_h[row tile]--> G2(row tile, n-tile) down projection
+ *   --ev_c[t-tile]--> C(t-tile) combine.
  *
  * Sources (page title, then figure / table / transcript cue):
  *   "Event Tensor: A Unified Abstraction for Compiling Dynamic Megakernel"
@@ -197,7 +198,8 @@ typedef struct {
  *   [0, E)        notifies received by ev_exp[e]   (expected: counts[e])
  *   [E, 2E)       times ev_exp[e] was completed    (expected: 1 if counts[e] > 0)
  *   [2E + i]      tasks executed of type i, i = 0..7 in the order
- *                 R, K, S, D, G1, G2, C, (unused)                           */
+ *                 R, K, S, D, G1, G2, C, (unused); D stays 0 (the dispatch
+ *                 is fused into G1's row gather)                            */
 #define ETC_DEBUG_WORDS(E) (2 * (E) + 8)
 
 /* Tile geometry and task counts of this build, for tests and benchmarks.   */
