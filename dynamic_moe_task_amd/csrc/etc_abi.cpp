@@ -138,7 +138,10 @@ int64_t lds_bytes_for(const etc_moe_desc* d) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-int persistent_grid(int sched, int lds, int* grid) {
+// Persistent grid: as many workgroups as stay resident together (capped per
+// CU).  `solo` is the CU count when the grid holds several workgroups a CU
+// (the first `solo` workgroups are then placed on distinct CUs), else 0.
+int persistent_grid(int sched, int lds, int* grid, int* solo = nullptr) {
   int cus = 0;
   int rc = device_cus(&cus);
   if (rc) return rc;
@@ -149,6 +152,7 @@ int persistent_grid(int sched, int lds, int* grid) {
   const int cap = wg_per_cu_cap();
   if (nb > cap) nb = cap;
   *grid = nb * cus;
+  if (solo) *solo = nb >= 2 ? cus : 0;
   return ETC_OK;
 }
 
@@ -447,9 +451,10 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
   if (sched == ETC_SCHED_KBK) {
     e = launch_moe_kbk(p, (int)scan_lds_bytes(d->E, d->T_max), stream);
   } else {
-    int grid = 0;
-    rc = persistent_grid(sched, lds, &grid);
+    int grid = 0, solo = 0;
+    rc = persistent_grid(sched, lds, &grid, &solo);
     if (rc) return rc;
+    p.solo_wgs = solo;
     e = launch_moe_persistent(p, sched, grid, lds, stream);
   }
   if (e != hipSuccess) return hip_fail((hipError_t)e, "MoE launch");

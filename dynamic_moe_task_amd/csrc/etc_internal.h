@@ -148,6 +148,7 @@ struct MoeParams {
   int32_t T, H, E, k, I, norm_topk, has_bias;
   int32_t max_rt;
   int32_t T_max;
+  int32_t solo_wgs;  // persistent grids: workgroups that each have a CU to themselves (0: no such split)
   // byte sizes of the device-coherent buffers (bounds of their resources)
   uint32_t hh_bytes, y_bytes, logits_bytes, rows_bytes;
   uint64_t budget;  // watchdog, in wall-clock ticks

@@ -840,7 +840,7 @@ __device__ void after_g2(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
 // Grid-wide barrier (BARRIER comparator only): arrival counter plus a
 // generation word; the last arrival resets the counter and bumps the
 // generation.  Bounded by the same watchdog as every other wait.
-__device__ bool grid_barrier(const Ctx& c) {
+__device__ bool grid_barrier(const Ctx& c, int parties) {
   wg_publish();
   int fail = 0;
   if (threadIdx.x == 0) {
@@ -848,7 +848,7 @@ __device__ bool grid_barrier(const Ctx& c) {
     uint32_t* gen = c.set + W_BAR_GEN;
     const uint32_t g0 = ld_relaxed(gen);
     const uint32_t old = add_relaxed(cnt, 1u);
-    if (old == gridDim.x - 1u) {
+    if (old == (uint32_t)parties - 1u) {
       xchg_relaxed(cnt, 0u);
       add_relaxed(gen, 1u);
     } else {
@@ -881,8 +881,7 @@ __device__ bool wait_known(const uint32_t* ctr, uint32_t target, uint32_t known,
   return fail == 0;
 }
 
-__device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n) {
-  const int G = gridDim.x;
+__device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G) {
   if (i0 >= n) return;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
@@ -933,8 +932,7 @@ __device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int 
   }
 }
 
-__device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n) {
-  const int G = gridDim.x;
+__device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G) {
   if (i0 >= n) return;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
@@ -996,7 +994,7 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
     trace_task(p, TT_R, i / c.nET, i % c.nET, tw, ts, tb);
   }
   off += c.nR;
-  if (!EV && !grid_barrier(c)) return;
+  if (!EV && !grid_barrier(c, G)) return;
   for (int i = first_of(w, off, G); i < c.nK; i += G) {
     if (tr) tw = now_ticks();
     if (EV && !wg_wait(ev_logit(p, c) + i, (uint32_t)c.nET, c.status, c.budget)) return;
@@ -1008,7 +1006,7 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
     trace_task(p, TT_K, i, 0, tw, ts, tb);
   }
   off += c.nK;
-  if (!EV && !grid_barrier(c)) return;
+  if (!EV && !grid_barrier(c, G)) return;
   if (first_of(w, off, G) == 0) {
     if (tr) tw = now_ticks();
     if (EV && !wg_wait(c.set + W_EV_ROUTE, (uint32_t)c.nK, c.status, c.budget)) return;
@@ -1020,18 +1018,24 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
     trace_task(p, TT_S, 0, 0, tw, ts, tb);
   }
   off += 1;
-  if (!EV && !grid_barrier(c)) return;
   if (EV) {
     if (!wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;
-  } else if (!grid_barrier(c)) {
+  } else if (!grid_barrier(c, G)) {
     return;
   }
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   const int nG1 = nrt * c.nN1, nG2 = nrt * c.nN2;
+  // Few GEMM tasks (at most three a CU): deal G1, G2 and C over only the
+  // first workgroup of each CU, so that no two weight streams share a CU's
+  // load path; the other workgroups are done (and BARRIER's later barriers
+  // count only the ones left).  Workgroups are placed one a CU before any
+  // CU takes a second, so the first solo_wgs workgroups sit on distinct CUs.
+  const int Gt = (p.solo_wgs > 0 && nG1 <= 3 * p.solo_wgs) ? p.solo_wgs : G;
+  if (w >= Gt) return;
   if (EV) {
-    run_g1_static(p, c, red, first_of(w, off, G), nG1);
+    run_g1_static(p, c, red, first_of(w, off, Gt), nG1, Gt);
   } else {
-    for (int i = first_of(w, off, G); i < nG1; i += G) {
+    for (int i = first_of(w, off, Gt); i < nG1; i += Gt) {
       const int rt = i / c.nN1;
       if (tr) tw = ts = now_ticks();
       task_g1(p, c, load_rowtile(p, rt), rt, i % c.nN1, red);
@@ -1041,11 +1045,11 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
     }
   }
   off += nG1;
-  if (!EV && !grid_barrier(c)) return;
+  if (!EV && !grid_barrier(c, Gt)) return;
   if (EV) {
-    run_g2_static(p, c, red, first_of(w, off, G), nG2);
+    run_g2_static(p, c, red, first_of(w, off, Gt), nG2, Gt);
   } else {
-    for (int i = first_of(w, off, G); i < nG2; i += G) {
+    for (int i = first_of(w, off, Gt); i < nG2; i += Gt) {
       const int rt = i / c.nN2;
       if (tr) tw = ts = now_ticks();
       task_g2(p, c, load_rowtile(p, rt), rt, i % c.nN2, red);
@@ -1055,8 +1059,8 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
     }
   }
   off += nG2;
-  if (!EV && !grid_barrier(c)) return;
-  for (int i = first_of(w, off, G); i < c.nC; i += G) {
+  if (!EV && !grid_barrier(c, Gt)) return;
+  for (int i = first_of(w, off, Gt); i < c.nC; i += Gt) {
     if (tr) tw = now_ticks();
     if (EV && !wg_wait(ev_c(p, c) + i, ctile_target(c, i), c.status, c.budget)) return;
     if (tr) ts = now_ticks();
