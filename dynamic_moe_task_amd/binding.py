@@ -28,8 +28,9 @@ ETC_SCHED_STATIC = 0
 ETC_SCHED_DYNAMIC = 1
 ETC_SCHED_KBK = 2
 ETC_SCHED_BARRIER = 3
+ETC_SCHED_ORDERED = 4
 SCHEDS = {"static": ETC_SCHED_STATIC, "dynamic": ETC_SCHED_DYNAMIC, "kbk": ETC_SCHED_KBK,
-          "barrier": ETC_SCHED_BARRIER}
+          "barrier": ETC_SCHED_BARRIER, "ordered": ETC_SCHED_ORDERED}
 
 ETC_DIM_SYMBOLIC = -1
 ETC_WAIT_DATA_DEPENDENT = -1

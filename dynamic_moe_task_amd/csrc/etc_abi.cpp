@@ -373,7 +373,8 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
   if (rc) return rc;
   if (!a) return fail(ETC_ERR_INVALID, "args is NULL");
   if (T < 1 || T > d->T_max) return fail(ETC_ERR_INVALID, "T %d outside [1, T_max=%d]", T, d->T_max);
-  if (sched != ETC_SCHED_STATIC && sched != ETC_SCHED_DYNAMIC && sched != ETC_SCHED_KBK && sched != ETC_SCHED_BARRIER)
+  if (sched != ETC_SCHED_STATIC && sched != ETC_SCHED_DYNAMIC && sched != ETC_SCHED_KBK && sched != ETC_SCHED_BARRIER &&
+      sched != ETC_SCHED_ORDERED)
     return fail(ETC_ERR_INVALID, "unknown schedule %d", sched);
   if (sched == ETC_SCHED_DYNAMIC)
     return fail(ETC_ERR_UNSUPPORTED,
@@ -415,6 +416,7 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
   p.set1 = reinterpret_cast<uint32_t*>(ws + L.b_set1);
   p.meta = reinterpret_cast<uint32_t*>(ws + L.b_meta);
   p.rt_info = reinterpret_cast<int32_t*>(ws + L.b_rt_info);
+  p.row_rt = reinterpret_cast<int32_t*>(ws + L.b_row_rt);
   p.logits = reinterpret_cast<float*>(ws + L.b_logits);
   p.hh = reinterpret_cast<uint16_t*>(ws + L.b_hh);
   p.y = reinterpret_cast<uint16_t*>(ws + L.b_y);
@@ -422,6 +424,7 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
   p.o_ev_logit = L.o_ev_logit;
   p.o_ev_exp = L.o_ev_exp;
   p.o_ev_h = L.o_ev_h;
+  p.o_ev_y = L.o_ev_y;
   p.o_ev_c = L.o_ev_c;
   p.o_queue = L.o_queue;
   p.q_cap = L.q_cap;

@@ -52,7 +52,9 @@ enum : int {
   W_BAR_GEN = 192,
   W_EV_ROUTE = 224,
   W_EV_SCAN = 256,
-  W_FIXED = 288,  // start of the variable-size event tensors
+  W_CLAIM_G1 = 288,  // ORDERED: 8 claim counters for G1 tiles, 32 words apart
+  W_CLAIM_G2 = 544,  // ORDERED: the same for G2 tiles
+  W_FIXED = 800,     // start of the variable-size event tensors
 };
 // split-K example: control words (u32) of its library-owned block, each on
 // its own 128-byte line, followed by the queue
@@ -67,10 +69,10 @@ struct MoeLayout {
   int32_t ntt_max, max_rt, nct_max;
   int64_t q_cap;
   // word offsets inside a counter set
-  int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_c, o_queue;  // o_queue in words, 8-byte aligned
+  int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_y, o_ev_c, o_queue;  // o_queue in words, 8-byte aligned
   int64_t set_words;
   // byte offsets inside the workspace
-  int64_t b_ctrl, b_set0, b_set1, b_meta, b_rt_info, b_logits, b_hh, b_y;
+  int64_t b_ctrl, b_set0, b_set1, b_meta, b_rt_info, b_row_rt, b_logits, b_hh, b_y;
   int64_t total_bytes;
 };
 
@@ -94,6 +96,7 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
   L.o_ev_logit = w; w += L.ntt_max;
   L.o_ev_exp = w;   w += d.E;
   L.o_ev_h = w;     w += L.max_rt;
+  L.o_ev_y = w;     w += L.max_rt;
   L.o_ev_c = w;     w += L.nct_max;
   w = align_up(w, 2);
   L.o_queue = w;    w += 2 * L.q_cap;
@@ -104,6 +107,7 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
   L.b_set1 = b;          b += L.set_words * 4;
   L.b_meta = b;          b += M_WORDS * 4;
   L.b_rt_info = b;       b += align_up((int64_t)L.max_rt * 16, 256);
+  L.b_row_rt = b;        b += align_up(rows * 4, 256);
   L.b_logits = b;        b += align_up(Tm * d.E * 4, 256);
   L.b_hh = b;            b += align_up(rows * d.I * 2, 256);
   L.b_y = b;             b += align_up(rows * d.H * 2, 256);
@@ -115,7 +119,7 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
 // counts / exp_indptr scratch and the scan's partial sums.
 inline int64_t scan_lds_bytes(int E, int T_max) {
   const int64_t W = cdiv(T_max, 32);
-  return align_up((int64_t)E * W * 4, 16) + align_up((int64_t)E * W * 2, 16) + 2 * 260 * 4 + 64;
+  return align_up((int64_t)E * W * 4, 16) + align_up((int64_t)E * W * 2, 16) + 4 * 260 * 4 + 64;
 }
 // G2: cross-wave reduction buffer (4 waves x 4 blocks x 256 fp32) plus the
 // bf16 staging of the kBM x 64 output tile
@@ -140,11 +144,12 @@ struct MoeParams {
   uint32_t* set1;
   uint32_t* meta;
   int32_t* rt_info;  // [max_rt][4]: expert, first grouped row, rows, 0
+  int32_t* row_rt;   // [T_max*k]: row tile of each grouped row
   float* logits;
   uint16_t* hh;
   uint16_t* y;
   int64_t set_words;
-  int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_c, o_queue, q_cap;
+  int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_y, o_ev_c, o_queue, q_cap;
   int32_t T, H, E, k, I, norm_topk, has_bias;
   int32_t max_rt;
   int32_t T_max;

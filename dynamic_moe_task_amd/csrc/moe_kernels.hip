@@ -13,8 +13,10 @@
 //              ev_exp[e] (released after counts[e] arrivals: the data-dependent
 //              update; expert e's tiles cover grouped rows
 //              [exp_indptr[e], exp_indptr[e+1]): the data-dependent trigger)
-//   G2(rt, nt) down projection                                     waits ev_h[rt]
-//   C(ct)      weighted combine of the k expert rows per token     waits ev_c[ct]
+//   G2(rt, nt) down projection; notifies ev_y[rt]                 waits ev_h[rt]
+//   C(ct)      weighted combine of the k expert rows per token: waits ev_y of
+//              every row tile that holds one of its rows (DYNAMIC: ev_c[ct],
+//              one arrival per row and G2 column tile)
 //
 // Schedules: STATIC (closed-form phase-ordered per-workgroup lists, notify /
 // wait; Figs. 6-7), DYNAMIC (early push onto one HBM queue when a notify
@@ -40,7 +42,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 enum Mode : int { MODE_STATIC = ETC_SCHED_STATIC, MODE_DYNAMIC = ETC_SCHED_DYNAMIC,
-                  MODE_KBK = ETC_SCHED_KBK, MODE_BARRIER = ETC_SCHED_BARRIER };
+                  MODE_KBK = ETC_SCHED_KBK, MODE_BARRIER = ETC_SCHED_BARRIER,
+                  MODE_ORDERED = ETC_SCHED_ORDERED };
 
 constexpr uint64_t kDescExit = ~0ull;
 
@@ -82,6 +85,7 @@ __device__ __forceinline__ rsrc_t r_slot(const MoeParams& p) { return make_rsrc(
 __device__ __forceinline__ rsrc_t r_counts(const MoeParams& p) { return make_rsrc(p.counts, (uint32_t)p.E * 4u); }
 __device__ __forceinline__ rsrc_t r_indptr(const MoeParams& p) { return make_rsrc(p.indptr, (uint32_t)(p.E + 1) * 4u); }
 __device__ __forceinline__ rsrc_t r_rtinfo(const MoeParams& p) { return make_rsrc(p.rt_info, (uint32_t)p.max_rt * 16u); }
+__device__ __forceinline__ rsrc_t r_rowrt(const MoeParams& p) { return make_rsrc(p.row_rt, p.rows_bytes); }
 __device__ __forceinline__ rsrc_t r_hh(const MoeParams& p) { return make_rsrc(p.hh, p.hh_bytes); }
 __device__ __forceinline__ rsrc_t r_y(const MoeParams& p) { return make_rsrc(p.y, p.y_bytes); }
 
@@ -131,6 +135,7 @@ struct Shared {
   int total;       // descriptors to write
   int list[kBM];
   int pairs[2 * kCombineT * kMaxK];  // D: slots; C: (weight, slot) pairs
+  uint32_t claim[4];                 // ORDERED: claimed ordinals handed to every thread
 };
 
 __device__ __forceinline__ void dbg_task(const MoeParams& p, int type) {
@@ -176,6 +181,7 @@ __device__ __forceinline__ void trace_task(const MoeParams& p, int type, int a, 
 __device__ __forceinline__ uint32_t* ev_logit(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_logit; }
 __device__ __forceinline__ uint32_t* ev_exp(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_exp; }
 __device__ __forceinline__ uint32_t* ev_h(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_h; }
+__device__ __forceinline__ uint32_t* ev_y(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_y; }
 __device__ __forceinline__ uint32_t* ev_c(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_c; }
 __device__ __forceinline__ uint32_t ctile_target(const Ctx& c, int ct) {
   return (uint32_t)(min(kCombineT, c.T - ct * kCombineT) * c.k * c.nN2);
@@ -402,7 +408,9 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   uint16_t* pre = reinterpret_cast<uint16_t*>(smem + ((E * W * 4 + 15) & ~15));
   int* cnt = reinterpret_cast<int*>(smem + ((E * W * 4 + 15) & ~15) + ((E * W * 2 + 15) & ~15));
   int* iptr = cnt + 260;
-  int* tmp = iptr + 260;
+  int* tmp = iptr + 260;         // 16 words for block_excl_scan
+  int* tfirst = tmp + 16;        // per expert: first four-block tile | (number of them << 16)
+  int* ttail = tfirst + 260;     // per expert: the tile of its last rows when that tile is smaller
   const rsrc_t rids = r_ids(p);
   for (int i = tid; i < E * W; i += kThreads) bits[i] = 0u;
   __syncthreads();
@@ -435,6 +443,8 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   const rsrc_t rc = r_counts(p), ri = r_indptr(p);
   if (tid < E) {
     iptr[tid] = ex;
+    tfirst[tid] = ex4 | (n4 << 16);
+    ttail[tid] = rem > 32 ? -1 : (rem > 16 ? tot4 + ex2 : tot4 + tot2 + ex1);
     co_st32(rc, (uint32_t)tid * 4u, (uint32_t)my);
     co_st32(ri, (uint32_t)tid * 4u, (uint32_t)ex);
   }
@@ -449,7 +459,7 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
     st_relaxed(p.meta + M_NRT, (uint32_t)tot_tiles);
   }
   __syncthreads();
-  const rsrc_t rs = r_slot(p), rp = r_perm(p);
+  const rsrc_t rs = r_slot(p), rp = r_perm(p), rrt = r_rowrt(p);
   for (int f = tid; f < n; f += kThreads) {
     const int e = (int)co_ld32(rids, (uint32_t)f * 4u);
     const int t = f / k;
@@ -457,6 +467,8 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
     const int s = iptr[e] + pre[e * W + w] + __popc(bits[e * W + w] & ((1u << b) - 1u));
     co_st32(rs, (uint32_t)f * 4u, (uint32_t)s);
     co_st32(rp, (uint32_t)s * 4u, (uint32_t)f);
+    const int mt = (s - iptr[e]) / kBM, tf = tfirst[e];  // the row's tile, numbered as below
+    co_st32(rrt, (uint32_t)s * 4u, (uint32_t)(mt < (tf >> 16) ? (tf & 0xffff) + mt : ttail[e]));
   }
   const rsrc_t rr = r_rtinfo(p);
   if (tid < E) {
@@ -519,8 +531,8 @@ __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const 
 #pragma unroll
   for (int b = 0; b < NB; ++b) accg[b] = accu[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  // batches of U k-steps (about 24 loads of 16 bytes a lane in flight); two
-  // workgroups per CU overlap each other's batch boundaries
+  // batches of U k-steps ((NB + 2) * U loads of 16 bytes a lane in flight);
+  // two workgroups per CU overlap each other's batch boundaries
   for (int s0 = 0; s0 < nsteps; s0 += U) {
     u32x4_t a[U][NB], bg[U], bu[U];
 #pragma unroll
@@ -583,13 +595,18 @@ __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const 
   }
 }
 
+// k-steps per load batch (U) by row blocks, measured on MI355X: short
+// batches stream better in the persistent kernel (two workgroups per CU);
+// the separate G kernels of the kernel-by-kernel launch keep longer batches
+// for four-block tiles, where they are faster there.
+template <bool KBK = false>
 __device__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt, float* red,
                         const uint32_t* pre = nullptr) {
   (void)rt;
   switch (row_blocks(tile.nrows)) {
-    case 1: g1_body<1, 8>(p, c, tile, nt, red, pre); break;
-    case 2: g1_body<2, 6>(p, c, tile, nt, red, pre); break;
-    default: g1_body<4, 4>(p, c, tile, nt, red, pre); break;
+    case 1: g1_body<1, 4>(p, c, tile, nt, red, pre); break;
+    case 2: g1_body<2, 4>(p, c, tile, nt, red, pre); break;
+    default: g1_body<4, KBK ? 4 : 2>(p, c, tile, nt, red, pre); break;
   }
 }
 
@@ -674,12 +691,13 @@ __device__ __forceinline__ void g2_body(const MoeParams& p, const Ctx& c, const 
   }
 }
 
+template <bool KBK = false>
 __device__ void task_g2(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt2, float* red) {
   (void)rt;
   switch (row_blocks(tile.nrows)) {
-    case 1: g2_body<1, 8>(p, c, tile, nt2, red); break;
-    case 2: g2_body<2, 4>(p, c, tile, nt2, red); break;
-    default: g2_body<4, 2>(p, c, tile, nt2, red); break;
+    case 1: g2_body<1, 2>(p, c, tile, nt2, red); break;
+    case 2: g2_body<2, 2>(p, c, tile, nt2, red); break;
+    default: g2_body<4, KBK ? 2 : 1>(p, c, tile, nt2, red); break;
   }
 }
 
@@ -744,7 +762,7 @@ __device__ __forceinline__ void q_put(const Ctx& c, int64_t slot, uint64_t desc)
 
 template <int MODE>
 __device__ void after_router(const MoeParams& p, const Ctx& c, int tt) {
-  if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC) {
+  if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC || MODE == MODE_ORDERED) {
     wg_publish();
     if (threadIdx.x == 0) {
       if (notify1(c, ev_logit(p, c) + tt, (uint32_t)c.nET) && MODE == MODE_DYNAMIC) {
@@ -757,7 +775,7 @@ __device__ void after_router(const MoeParams& p, const Ctx& c, int tt) {
 
 template <int MODE>
 __device__ void after_topk(const MoeParams& p, const Ctx& c) {
-  if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC) {
+  if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC || MODE == MODE_ORDERED) {
     wg_publish();
     if (threadIdx.x == 0) {
       if (notify1(c, c.set + W_EV_ROUTE, (uint32_t)c.nK) && MODE == MODE_DYNAMIC) {
@@ -770,7 +788,7 @@ __device__ void after_topk(const MoeParams& p, const Ctx& c) {
 
 template <int MODE>
 __device__ void after_scan(const MoeParams& p, const Ctx& c, Shared& sh) {
-  if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC) {
+  if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC || MODE == MODE_ORDERED) {
     wg_publish();
     if (MODE == MODE_DYNAMIC) {
       // every expert event is complete once S runs (K notified all routed
@@ -881,6 +899,44 @@ __device__ bool wait_known(const uint32_t* ctr, uint32_t target, uint32_t known,
   return fail == 0;
 }
 
+// C(ct) may run once every row tile holding one of its tokens' k rows has
+// finished all of its G2 column tiles: wave 0 polls those ev_y elements, one
+// row a lane (at most kCombineT * k <= 32 rows), under the watchdog.
+__device__ bool wait_rows_done(const MoeParams& p, const Ctx& c, int ct) {
+  int fail = 0;
+  if (threadIdx.x < 64) {
+    const int t0 = ct * kCombineT, nrow = min(kCombineT, c.T - t0) * c.k;
+    const bool mine = (int)threadIdx.x < nrow;
+    uint32_t* ctr = ev_y(p, c);
+    if (mine) {
+      const uint32_t s = co_ld32(r_slot(p), (uint32_t)(t0 * c.k + (int)threadIdx.x) * 4u);
+      const uint32_t rt = co_ld32(r_rowrt(p), s * 4u);
+      ctr += rt;
+      if (p.debug) {  // count the rows whose mapped tile really holds them
+        const u32x4_t q = co_ld128(r_rtinfo(p), rt * 16u);
+        if (s >= q.y && s < q.y + q.z) atomicAdd(p.debug + 2 * c.E + 7, 1);
+      }
+    }
+    const uint32_t tgt = (uint32_t)c.nN2;
+    const uint64_t t_start = now_ticks();
+    for (uint32_t spins = 1;; ++spins) {
+      const bool ok = !mine || ld_relaxed(ctr) >= tgt;
+      if (__all(ok)) break;
+      if ((spins & 7u) == 0u) {
+        if (ld_relaxed(c.status) & ST_ABORT) { fail = 1; break; }
+        if (now_ticks() - t_start > c.budget) {
+          if (threadIdx.x == 0) or_relaxed(c.status, ST_TIMEOUT | ST_ABORT);
+          fail = 1;
+          break;
+        }
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  fail = __syncthreads_or(fail);
+  return fail == 0;
+}
+
 __device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G) {
   if (i0 >= n) return;
   const bool tr = p.trace != nullptr;
@@ -937,8 +993,7 @@ __device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int 
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
   uint32_t* evh = ev_h(p, c);
-  uint32_t* evc = ev_c(p, c);
-  const rsrc_t rperm = r_perm(p);
+  uint32_t* evy = ev_y(p, c);
   const uint32_t tgt = (uint32_t)c.nN1;
   RowTile cur = load_rowtile(p, i0 / c.nN2);
   RowTile nxt = cur;
@@ -955,12 +1010,10 @@ __device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int 
     uint32_t nxt_arr = 0;
     if (threadIdx.x == 0 && i + G < n) nxt_arr = ld_relaxed(evh + (i + G) / c.nN2);
     // combine tile of each row's token (wave 0, one row a lane)
-    int ct = 0;
-    if (threadIdx.x < cur.nrows) ct = ((int)co_ld32(rperm, (uint32_t)(cur.r0 + threadIdx.x) * 4u) / c.k) / kCombineT;
     task_g2(p, c, cur, rt, nt, red);
-    if (threadIdx.x < cur.nrows) {  // wave 0 wrote the rows: one combine notify per row
+    if (threadIdx.x == 0) {  // wave 0 wrote the rows: drain its stores, then notify
       __builtin_amdgcn_s_waitcnt(0);
-      notify_fast(p, c, evc + ct, ctile_target(c, ct));
+      notify_fast(p, c, evy + rt, (uint32_t)c.nN2);
     }
     if (tr) tb = now_ticks();
     dbg_task(p, TT_G2);
@@ -969,6 +1022,166 @@ __device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int 
     nxt = nn;
     cur_arr = nxt_arr;
   }
+}
+
+// ORDERED: the G1 tiles and then the G2 tiles are claimed in index order
+// from one counter per group of workgroups (group = workgroup index mod 8;
+// the dispatcher deals consecutive workgroups over the 8 XCDs, so a group is
+// one XCD's workgroups).  Ordinal k of group g is tile k * ngrp + g.  A
+// workgroup that streams faster (the first of the two on a CU, a CU whose
+// tiles are cheaper) claims more tiles, so both phases end together, while
+// every tile still waits on its event as in STATIC.  Deadlock freedom: G1
+// waits only on K, which is complete before S, so every claimed G1 tile
+// completes and every G2 wait is met; C waits only on G2.  Claims from one
+// thread to one counter are ordered (same-location coherence), so a
+// workgroup's ordinals increase and the first one past the end ends its
+// stream (a pipeline fill takes three consecutive ordinals in one claim).  The runners keep three ordinals ahead of the running tile: the
+// claim round trip, the next row-tile descriptor and the next event state
+// arrive while earlier tiles stream, as in the STATIC runners.
+struct ClaimQ {
+  uint32_t* ctr;
+  int grp, ngrp, n;
+};
+__device__ __forceinline__ int claimed_task(const ClaimQ& q, uint32_t k) {
+  const int64_t i = (int64_t)k * q.ngrp + q.grp;
+  return i < q.n ? (int)i : q.n;
+}
+
+// returns false when a wait gave up (the launch is aborting)
+__device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q, const ClaimQ& q2,
+                               uint32_t* sk) {
+  const int n = q.n;
+  const bool tr = p.trace != nullptr;
+  uint64_t tw = 0, ts = 0, tb = 0;
+  uint32_t* evx = ev_exp(p, c);
+  uint32_t* evh = ev_h(p, c);
+  const rsrc_t rcnt = r_counts(p);
+  if (threadIdx.x == 0) {  // one claim of three consecutive ordinals fills the pipeline
+    const uint32_t k = add_relaxed(q.ctr, 3u);
+    sk[0] = k;
+    sk[1] = k + 1u;
+    sk[2] = k + 2u;
+  }
+  __syncthreads();
+  int cur = claimed_task(q, sk[0]), nxt = claimed_task(q, sk[1]);
+  uint32_t g2k = 0;  // thread 0: the first three G2 ordinals, claimed during the last G1 tile
+  bool g2_taken = false;
+  if (cur < n) {
+    RowTile rc = load_rowtile(p, cur / c.nN1);
+    RowTile rn = rc;
+    if (nxt < n) rn = load_rowtile(p, nxt / c.nN1);
+    uint32_t cur_tgt = 0, cur_arr = 0;
+    if (threadIdx.x == 0) {
+      cur_tgt = co_ld32(rcnt, (uint32_t)rc.e * 4u);
+      cur_arr = ld_relaxed(evx + rc.e);
+    }
+    uint32_t cur_f[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) cur_f[b] = row_perm(p, rc, b);
+    int par = 2;  // claim slot that holds the ordinal after nxt
+    for (;;) {
+      const int rt = cur / c.nN1, nt = cur % c.nN1;
+      if (tr) tw = now_ticks();
+      if (!wait_known(evx + rc.e, cur_tgt, cur_arr, c)) return false;
+      if (tr) ts = now_ticks();
+      const int aft = claimed_task(q, sk[par]);
+      uint32_t knew = 0xffffffffu;
+      if (threadIdx.x == 0) {
+        if (aft < n) {
+          knew = add_relaxed(q.ctr, 1u);
+        } else if (nxt >= n) {  // this is the last G1 tile: claim the first G2 tiles now
+          g2k = add_relaxed(q2.ctr, 3u);
+          g2_taken = true;
+        }
+      }
+      RowTile ra = rn;
+      if (aft < n) ra = load_rowtile(p, aft / c.nN1);
+      uint32_t nxt_tgt = 0, nxt_arr = 0;
+      if (threadIdx.x == 0 && nxt < n) {
+        nxt_tgt = co_ld32(rcnt, (uint32_t)rn.e * 4u);
+        nxt_arr = ld_relaxed(evx + rn.e);
+      }
+      uint32_t nxt_f[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) nxt_f[b] = nxt < n ? row_perm(p, rn, b) : 0u;
+      task_g1(p, c, rc, rt, nt, red, cur_f);
+      if (threadIdx.x == 0) {  // wave 0 wrote the tile: drain its stores, then notify
+        __builtin_amdgcn_s_waitcnt(0);
+        notify_fast(p, c, evh + rt, (uint32_t)c.nN1);
+        sk[par ^ 1] = knew;
+      }
+      if (tr) tb = now_ticks();
+      dbg_task(p, TT_G1);
+      trace_task(p, TT_G1, rt, nt, tw, ts, tb);
+      cur = nxt;
+      nxt = aft;
+      rc = rn;
+      rn = ra;
+      cur_tgt = nxt_tgt;
+      cur_arr = nxt_arr;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) cur_f[b] = nxt_f[b];
+      par ^= 1;
+      if (cur >= n) break;
+    }
+  }
+  __syncthreads();  // every thread has read its last claim slot
+  if (threadIdx.x == 0) {
+    if (!g2_taken) g2k = add_relaxed(q2.ctr, 3u);
+    sk[0] = g2k;
+    sk[1] = g2k + 1u;
+    sk[2] = g2k + 2u;
+  }
+  return true;
+}
+
+// G2 tiles from the claims that run_g1_ordered left in sk[0..2]
+__device__ bool run_g2_ordered(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q, uint32_t* sk) {
+  const int n = q.n;
+  const bool tr = p.trace != nullptr;
+  uint64_t tw = 0, ts = 0, tb = 0;
+  uint32_t* evh = ev_h(p, c);
+  uint32_t* evy = ev_y(p, c);
+  const uint32_t tgt = (uint32_t)c.nN1;
+  __syncthreads();
+  int cur = claimed_task(q, sk[0]), nxt = claimed_task(q, sk[1]);
+  if (cur >= n) return true;
+  RowTile rc = load_rowtile(p, cur / c.nN2);
+  RowTile rn = rc;
+  if (nxt < n) rn = load_rowtile(p, nxt / c.nN2);
+  uint32_t cur_arr = 0;
+  if (threadIdx.x == 0) cur_arr = ld_relaxed(evh + cur / c.nN2);
+  int par = 2;
+  for (;;) {
+    const int rt = cur / c.nN2, nt = cur % c.nN2;
+    if (tr) tw = now_ticks();
+    if (!wait_known(evh + rt, tgt, cur_arr, c)) return false;
+    if (tr) ts = now_ticks();
+    const int aft = claimed_task(q, sk[par]);
+    uint32_t knew = 0xffffffffu;
+    if (threadIdx.x == 0 && aft < n) knew = add_relaxed(q.ctr, 1u);
+    RowTile ra = rn;
+    if (aft < n) ra = load_rowtile(p, aft / c.nN2);
+    uint32_t nxt_arr = 0;
+    if (threadIdx.x == 0 && nxt < n) nxt_arr = ld_relaxed(evh + nxt / c.nN2);
+    task_g2(p, c, rc, rt, nt, red);
+    if (threadIdx.x == 0) {  // wave 0 wrote the rows: drain its stores, then notify
+      __builtin_amdgcn_s_waitcnt(0);
+      notify_fast(p, c, evy + rt, (uint32_t)c.nN2);
+      sk[par ^ 1] = knew;
+    }
+    if (tr) tb = now_ticks();
+    dbg_task(p, TT_G2);
+    trace_task(p, TT_G2, rt, nt, tw, ts, tb);
+    cur = nxt;
+    nxt = aft;
+    rc = rn;
+    rn = ra;
+    cur_arr = nxt_arr;
+    par ^= 1;
+    if (cur >= n) break;
+  }
+  return true;
 }
 
 // STATIC / BARRIER: each phase's tasks are dealt round-robin over the
@@ -981,7 +1194,7 @@ template <int MODE>
 __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh) {
   const int G = gridDim.x, w = blockIdx.x;
   float* red = reinterpret_cast<float*>(smem);
-  constexpr bool EV = (MODE == MODE_STATIC);
+  constexpr bool EV = (MODE == MODE_STATIC || MODE == MODE_ORDERED);
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
   int64_t off = 0;
@@ -1032,6 +1245,14 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
   // CU takes a second, so the first solo_wgs workgroups sit on distinct CUs.
   const int Gt = (p.solo_wgs > 0 && nG1 <= 3 * p.solo_wgs) ? p.solo_wgs : G;
   if (w >= Gt) return;
+  if (MODE == MODE_ORDERED) {
+    const int ngrp = Gt % 8 == 0 ? 8 : 1, grp = w % ngrp;
+    const ClaimQ q1{c.set + W_CLAIM_G1 + grp * 32, grp, ngrp, nG1};
+    const ClaimQ q2{c.set + W_CLAIM_G2 + grp * 32, grp, ngrp, nG2};
+    if (!run_g1_ordered(p, c, red, q1, q2, sh.claim)) return;
+    if (!run_g2_ordered(p, c, red, q2, sh.claim)) return;
+    off += nG1 + nG2;
+  } else {
   if (EV) {
     run_g1_static(p, c, red, first_of(w, off, Gt), nG1, Gt);
   } else {
@@ -1060,9 +1281,10 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
   }
   off += nG2;
   if (!EV && !grid_barrier(c, Gt)) return;
+  }
   for (int i = first_of(w, off, Gt); i < c.nC; i += Gt) {
     if (tr) tw = now_ticks();
-    if (EV && !wg_wait(ev_c(p, c) + i, ctile_target(c, i), c.status, c.budget)) return;
+    if (EV && !wait_rows_done(p, c, i)) return;
     if (tr) ts = now_ticks();
     task_combine(p, c, i, sh.pairs);
     if (tr) tb = now_ticks();
@@ -1215,7 +1437,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN1) return;
   const int rt = blockIdx.x / c.nN1;
-  task_g1(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN1, red);
+  task_g1<true>(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN1, red);
 }
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) kbk_g2(MoeParams p) {
   __shared__ float red[4 * 4 * 256 + kBM * 64 / 2];
@@ -1223,7 +1445,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN2) return;
   const int rt = blockIdx.x / c.nN2;
-  task_g2(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN2, red);
+  task_g2<true>(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN2, red);
 }
 __global__ void __launch_bounds__(kThreads) kbk_combine(MoeParams p) {
   __shared__ int pairs[2 * kCombineT * kMaxK];
@@ -1244,6 +1466,9 @@ int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes
     case ETC_SCHED_BARRIER:
       hipLaunchKernelGGL((moe_persistent<MODE_BARRIER>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
       break;
+    case ETC_SCHED_ORDERED:
+      hipLaunchKernelGGL((moe_persistent<MODE_ORDERED>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+      break;
     default:
       return (int)hipErrorInvalidValue;
   }
@@ -1261,6 +1486,9 @@ int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu) {
       break;
     case ETC_SCHED_BARRIER:
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_BARRIER>, kThreads, lds_bytes);
+      break;
+    case ETC_SCHED_ORDERED:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_ORDERED>, kThreads, lds_bytes);
       break;
     default:
       return (int)hipErrorInvalidValue;

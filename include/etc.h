@@ -64,8 +64,14 @@ enum {
  *            model of Fig. 1), same device task code.
  *   BARRIER: comparator, the persistent kernel with a grid-wide barrier
  *            between task types instead of fine-grained events (the
- *            "unfused megakernel" reading of Table 2).                       */
-enum { ETC_SCHED_STATIC = 0, ETC_SCHED_DYNAMIC = 1, ETC_SCHED_KBK = 2, ETC_SCHED_BARRIER = 3 };
+ *            "unfused megakernel" reading of Table 2).
+ *   ORDERED: STATIC's events and routing front, but the G1 and then the G2
+ *            tiles are claimed in index order from a counter per group of
+ *            workgroups instead of being dealt in fixed lists: a workgroup
+ *            that streams faster takes more tiles.  Each claimed tile still
+ *            waits on its event before it runs.                              */
+enum { ETC_SCHED_STATIC = 0, ETC_SCHED_DYNAMIC = 1, ETC_SCHED_KBK = 2, ETC_SCHED_BARRIER = 3,
+       ETC_SCHED_ORDERED = 4 };
 
 /* ------------------------------------------------------- event tensors -- */
 /* An event tensor [Fig. 2; podcast cue 3]: a tensor of dependency counters,
@@ -197,9 +203,11 @@ typedef struct {
 /* Debug counters (int32), when etc_moe_args.debug is non-NULL:
  *   [0, E)        notifies received by ev_exp[e]   (expected: counts[e])
  *   [E, 2E)       times ev_exp[e] was completed    (expected: 1 if counts[e] > 0)
- *   [2E + i]      tasks executed of type i, i = 0..7 in the order
- *                 R, K, S, D, G1, G2, C, (unused); D stays 0 (the dispatch
- *                 is fused into G1's row gather)                            */
+ *   [2E + i]      tasks executed of type i, i = 0..6 in the order
+ *                 R, K, S, D, G1, G2, C; D stays 0 (the dispatch is fused
+ *                 into G1's row gather)
+ *   [2E + 7]      STATIC / ORDERED: rows whose row tile, as looked up by
+ *                 their C task, holds them              (expected: T*k)     */
 #define ETC_DEBUG_WORDS(E) (2 * (E) + 8)
 
 /* Tile geometry and task counts of this build, for tests and benchmarks.   */
