@@ -1035,7 +1035,8 @@ __device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int 
 // completes and every G2 wait is met; C waits only on G2.  Claims from one
 // thread to one counter are ordered (same-location coherence), so a
 // workgroup's ordinals increase and the first one past the end ends its
-// stream (a pipeline fill takes three consecutive ordinals in one claim).  The runners keep three ordinals ahead of the running tile: the
+// stream.  A pipeline fill is three separate claims, so that with few tiles
+// the first claims of all workgroups interleave and spread the tiles.  The runners keep three ordinals ahead of the running tile: the
 // claim round trip, the next row-tile descriptor and the next event state
 // arrive while earlier tiles stream, as in the STATIC runners.
 struct ClaimQ {
@@ -1056,15 +1057,14 @@ __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, con
   uint32_t* evx = ev_exp(p, c);
   uint32_t* evh = ev_h(p, c);
   const rsrc_t rcnt = r_counts(p);
-  if (threadIdx.x == 0) {  // one claim of three consecutive ordinals fills the pipeline
-    const uint32_t k = add_relaxed(q.ctr, 3u);
-    sk[0] = k;
-    sk[1] = k + 1u;
-    sk[2] = k + 2u;
+  if (threadIdx.x == 0) {
+    sk[0] = add_relaxed(q.ctr, 1u);
+    sk[1] = add_relaxed(q.ctr, 1u);
+    sk[2] = add_relaxed(q.ctr, 1u);
   }
   __syncthreads();
   int cur = claimed_task(q, sk[0]), nxt = claimed_task(q, sk[1]);
-  uint32_t g2k = 0;  // thread 0: the first three G2 ordinals, claimed during the last G1 tile
+  uint32_t g2k0 = 0, g2k1 = 0, g2k2 = 0;  // thread 0: first G2 claims, taken during the last G1 tile
   bool g2_taken = false;
   if (cur < n) {
     RowTile rc = load_rowtile(p, cur / c.nN1);
@@ -1090,7 +1090,9 @@ __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, con
         if (aft < n) {
           knew = add_relaxed(q.ctr, 1u);
         } else if (nxt >= n) {  // this is the last G1 tile: claim the first G2 tiles now
-          g2k = add_relaxed(q2.ctr, 3u);
+          g2k0 = add_relaxed(q2.ctr, 1u);
+          g2k1 = add_relaxed(q2.ctr, 1u);
+          g2k2 = add_relaxed(q2.ctr, 1u);
           g2_taken = true;
         }
       }
@@ -1127,10 +1129,14 @@ __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, con
   }
   __syncthreads();  // every thread has read its last claim slot
   if (threadIdx.x == 0) {
-    if (!g2_taken) g2k = add_relaxed(q2.ctr, 3u);
-    sk[0] = g2k;
-    sk[1] = g2k + 1u;
-    sk[2] = g2k + 2u;
+    if (!g2_taken) {
+      g2k0 = add_relaxed(q2.ctr, 1u);
+      g2k1 = add_relaxed(q2.ctr, 1u);
+      g2k2 = add_relaxed(q2.ctr, 1u);
+    }
+    sk[0] = g2k0;
+    sk[1] = g2k1;
+    sk[2] = g2k2;
   }
   return true;
 }
