@@ -24,7 +24,8 @@ constexpr int kRouterT = 4;     // R task: tokens ...
 constexpr int kRouterE = 4;     //         ... x experts (one expert per wave)
 constexpr int kBM = 64;         // grouped-GEMM row tile (up to four 16-row MFMA blocks)
 constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile
-constexpr int kBN2 = 64;        // G2: output columns per tile (4 MFMA column blocks)
+constexpr int kBN2 = 64;        // G2: output columns per tile
+constexpr int kCB2 = kBN2 / 16;  // G2: 16-column MFMA blocks per tile
 constexpr int kCombineT = 2;    // C task: tokens per task
 constexpr int kMaxK = 16;
 constexpr int kMaxE = 256;
@@ -123,7 +124,7 @@ inline int64_t scan_lds_bytes(int E, int T_max) {
 }
 // G2: cross-wave reduction buffer (4 waves x 4 blocks x 256 fp32) plus the
 // bf16 staging of the kBM x 64 output tile
-constexpr int64_t kGemmLdsBytes = 4 * 4 * 256 * 4 + kBM * 64 * 2;
+constexpr int64_t kGemmLdsBytes = 4 * kCB2 * 256 * 4 + kBM * kBN2 * 2;
 
 struct MoeParams {
   const uint16_t* x;

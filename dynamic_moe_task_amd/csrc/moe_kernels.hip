@@ -610,8 +610,8 @@ __device__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, in
   }
 }
 
-// G2: one row tile times 64 output columns of Wd[e]: Y = bf16(Hmid Wd^T).
-// K = I split in quarters over the waves; each wave keeps 4 column blocks
+// G2: one row tile times kBN2 output columns of Wd[e]: Y = bf16(Hmid Wd^T).
+// K = I split in quarters over the waves; each wave keeps kBN2 / 16 column blocks
 // for every row block.
 template <int NB, int U>
 __device__ __forceinline__ void g2_body(const MoeParams& p, const Ctx& c, const RowTile tile, int nt2, float* red) {
@@ -631,21 +631,21 @@ __device__ __forceinline__ void g2_body(const MoeParams& p, const Ctx& c, const 
   }
   const uint16_t* pb = p.w2 + ((size_t)tile.e * H + (size_t)nt2 * kBN2 + m) * I + wv * kw + kg * 8;
   const size_t cbs = (size_t)16 * I;  // next 16-column block of Wd
-  f32x4_t acc[NB][4];
+  f32x4_t acc[NB][kCB2];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[b][q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < kCB2; ++q) acc[b][q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   for (int s0 = 0; s0 < nsteps; s0 += U) {
-    u32x4_t a[U][NB], bb[U][4];
+    u32x4_t a[U][NB], bb[U][kCB2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u < nsteps) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) a[u][b] = valid[b] ? co_ld128(rh, aoff[b] + (uint32_t)(s0 + u) * 64u) : zero;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bb[u][q] = ld4(pb + q * cbs + (s0 + u) * 32);
+        for (int q = 0; q < kCB2; ++q) bb[u][q] = ld4(pb + q * cbs + (s0 + u) * 32);
       }
     }
 #pragma unroll
@@ -654,7 +654,7 @@ __device__ __forceinline__ void g2_body(const MoeParams& p, const Ctx& c, const 
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < kCB2; ++q)
             acc[b][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u][b]), as_bf(bb[u][q]), acc[b][q], 0, 0, 0);
       }
     }
@@ -662,30 +662,31 @@ __device__ __forceinline__ void g2_body(const MoeParams& p, const Ctx& c, const 
   const int tid = threadIdx.x;
   const int ol = tid >> 2, oi = tid & 3;
   const int row = 4 * (ol >> 4) + oi, col = ol & 15;
-  uint16_t* stage = reinterpret_cast<uint16_t*>(red + 4096);  // [64 rows][64 cols] bf16
+  uint16_t* stage = reinterpret_cast<uint16_t*>(red + 4 * kCB2 * 256);  // [64 rows][kBN2 cols] bf16
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < kCB2; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[(wv * 4 + q) * 256 + lane * 4 + i] = acc[b][q][i];
+      for (int i = 0; i < 4; ++i) red[(wv * kCB2 + q) * 256 + lane * 4 + i] = acc[b][q][i];
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kCB2; ++q) {
       float y = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) y += red[(w * 4 + q) * 256 + tid];
-      stage[(b * 16 + row) * 64 + q * 16 + col] = (uint16_t)f2bf(y);
+      for (int w = 0; w < 4; ++w) y += red[(w * kCB2 + q) * 256 + tid];
+      stage[(b * 16 + row) * kBN2 + q * 16 + col] = (uint16_t)f2bf(y);
     }
   }
   __syncthreads();
-  // wave 0 alone writes the tile (rows x 128 bytes, eight chunks a row)
+  // wave 0 alone writes the tile (rows x kBN2 * 2 bytes, 16-byte chunks)
   if (tid < 64) {
-    const int nchunks = tile.nrows * 8;
+    constexpr int cpr = kBN2 / 8;
+    const int nchunks = tile.nrows * cpr;
     for (int idx = tid; idx < nchunks; idx += 64) {
-      const int r = idx >> 3, q = idx & 7;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * 64 + q * 8);
+      const int r = idx / cpr, q = idx % cpr;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * kBN2 + q * 8);
       co_st128(r_y(p), (uint32_t)(((size_t)(tile.r0 + r) * H + nt2 * kBN2 + q * 8) * 2), v);
     }
   }
@@ -972,10 +973,11 @@ __device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int 
 #pragma unroll
     for (int b = 0; b < 4; ++b) nxt_f[b] = i + G < n ? row_perm(p, nxt, b) : 0u;
     task_g1(p, c, cur, rt, nt, red, cur_f);
-    if (threadIdx.x == 0) {  // wave 0 wrote the tile: drain its stores, then notify
-      __builtin_amdgcn_s_waitcnt(0);
-      notify_fast(p, c, evh + rt, (uint32_t)c.nN1);
-    }
+    // wave 0 wrote the tile: drain its stores, then notify.  The drain is
+    // outside the notify branch so that, after the branch, only the notify
+    // is in flight and the prefetched registers need no further wait.
+    __builtin_amdgcn_s_waitcnt(0);
+    if (threadIdx.x == 0) notify_fast(p, c, evh + rt, (uint32_t)c.nN1);
     if (tr) tb = now_ticks();
     dbg_task(p, TT_G1);
     trace_task(p, TT_G1, rt, nt, tw, ts, tb);
@@ -1011,10 +1013,8 @@ __device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int 
     if (threadIdx.x == 0 && i + G < n) nxt_arr = ld_relaxed(evh + (i + G) / c.nN2);
     // combine tile of each row's token (wave 0, one row a lane)
     task_g2(p, c, cur, rt, nt, red);
-    if (threadIdx.x == 0) {  // wave 0 wrote the rows: drain its stores, then notify
-      __builtin_amdgcn_s_waitcnt(0);
-      notify_fast(p, c, evy + rt, (uint32_t)c.nN2);
-    }
+    __builtin_amdgcn_s_waitcnt(0);  // wave 0 wrote the rows: drain, then notify (as in G1)
+    if (threadIdx.x == 0) notify_fast(p, c, evy + rt, (uint32_t)c.nN2);
     if (tr) tb = now_ticks();
     dbg_task(p, TT_G2);
     trace_task(p, TT_G2, rt, nt, tw, ts, tb);
@@ -1107,8 +1107,8 @@ __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, con
 #pragma unroll
       for (int b = 0; b < 4; ++b) nxt_f[b] = nxt < n ? row_perm(p, rn, b) : 0u;
       task_g1(p, c, rc, rt, nt, red, cur_f);
-      if (threadIdx.x == 0) {  // wave 0 wrote the tile: drain its stores, then notify
-        __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_waitcnt(0);  // drain, then notify (see run_g1_static)
+      if (threadIdx.x == 0) {
         notify_fast(p, c, evh + rt, (uint32_t)c.nN1);
         sk[par ^ 1] = knew;
       }
@@ -1171,8 +1171,8 @@ __device__ bool run_g2_ordered(const MoeParams& p, const Ctx& c, float* red, con
     uint32_t nxt_arr = 0;
     if (threadIdx.x == 0 && nxt < n) nxt_arr = ld_relaxed(evh + nxt / c.nN2);
     task_g2(p, c, rc, rt, nt, red);
-    if (threadIdx.x == 0) {  // wave 0 wrote the rows: drain its stores, then notify
-      __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(0);  // drain, then notify (see run_g1_static)
+    if (threadIdx.x == 0) {
       notify_fast(p, c, evy + rt, (uint32_t)c.nN2);
       sk[par ^ 1] = knew;
     }
@@ -1438,7 +1438,7 @@ __global__ void __launch_bounds__(kThreads) kbk_scan(MoeParams p) {
   task_scan(p, c, smem);
 }
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) kbk_g1(MoeParams p) {
-  __shared__ float red[4 * 4 * 256 + kBM * 64 / 2];
+  __shared__ float red[4 * kCB2 * 256 + kBM * kBN2 / 2];
   const Ctx c = make_ctx(p, nullptr);
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN1) return;
@@ -1446,7 +1446,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   task_g1<true>(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN1, red);
 }
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) kbk_g2(MoeParams p) {
-  __shared__ float red[4 * 4 * 256 + kBM * 64 / 2];
+  __shared__ float red[4 * kCB2 * 256 + kBM * kBN2 / 2];
   const Ctx c = make_ctx(p, nullptr);
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN2) return;
