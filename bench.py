@@ -4,7 +4,7 @@ MI355X through the C ABI.  A step is one launch of the whole hot path
 of synthetic tokens already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
-                    [--sched static] [--copies R] [--no-cpu] [--traffic FILE]
+                    [--sched ordered] [--copies R] [--no-cpu] [--traffic FILE]
 
 Prints ONE JSON line.  `value` is tokens/s of the chosen schedule; the other
 schedules, µs/layer and the roofline fraction ride along in the same line.
@@ -29,6 +29,9 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 BF16_PEAK_TFS = 2500.0      # MI355X dense bf16 MFMA, published
 
 METRIC = "µs per MoE layer & tokens/s at 1 MI355X; %HBM peak (decode) / %MFMA (batch 256)"
+# live schedules, persistent ones first; the dynamic push/pop schedule is
+# switched off in the library
+SCHEDS = ("static", "ordered", "barrier", "kbk")
 
 
 def parse():
@@ -37,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill_zipf", "tiny"])
-    ap.add_argument("--sched", default="static", choices=["static", "barrier", "kbk"])
+    ap.add_argument("--sched", default="ordered", choices=list(SCHEDS),
+                    help="schedule behind `value` (the others are timed alongside)")
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated over steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -188,7 +192,7 @@ def cpu_baseline(shape, w, X, seconds):
 RIDGE = BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte where MFMA and HBM bounds meet
 
 
-def measure_prefill(Wr, w13s, w2s, sp, steps, warmup, repeat):
+def measure_prefill(Wr, w13s, w2s, sp, steps, warmup, repeat, main_sched):
     """Prefill chunk: T=256 with the Zipf(1.1) logit bias (hot experts get
     most tokens, some get none).  Same expert weights as the decode layer."""
     import torch
@@ -207,25 +211,29 @@ def measure_prefill(Wr, w13s, w2s, sp, steps, warmup, repeat):
     n_act = int((counts > 0).sum())
     alg_bytes = wl.algorithmic_bytes(shape, T, n_act)
     alg_flops = wl.algorithmic_flops(shape, T)
-    us = {}
-    for sch in ("static", "barrier", "kbk"):
-        us[sch] = float(np.median([time_sched(bufs, T, sch, steps, warmup, w13s, w2s, sp) for _ in range(repeat)]))
+    runs = {s: [] for s in SCHEDS}
+    for _ in range(repeat):  # interleaved, then medians
+        for sch in SCHEDS:
+            runs[sch].append(time_sched(bufs, T, sch, steps, warmup, w13s, w2s, sp))
+    us = {s: float(np.median(v)) for s, v in runs.items()}
     best = min(us.values())
     ai = alg_flops / alg_bytes
+    m = us[main_sched]
     return {
         "workload": shape.name, "T": T, "active_experts": n_act, "max_expert_tokens": int(counts.max()),
         "us_per_layer": {k: round(v, 2) for k, v in us.items()},
-        "tokens_per_s_static": round(T / (us["static"] * 1e-6), 1),
+        "schedule": main_sched,
+        "tokens_per_s": round(T / (m * 1e-6), 1),
         "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops,
-        "hbm_frac_static": round(alg_bytes / (us["static"] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
-        "mfma_frac_whole_layer_static": round(alg_flops / (us["static"] * 1e-6) / (BF16_PEAK_TFS * 1e12), 5),
+        "hbm_frac": round(alg_bytes / (m * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+        "mfma_frac_whole_layer": round(alg_flops / (m * 1e-6) / (BF16_PEAK_TFS * 1e12), 5),
         "mfma_frac_cap": round(ai / RIDGE, 4),
         "note": "whole-layer MFMA use is capped at AI/ridge: at this batch the layer is HBM-bound",
         "fastest": min(us, key=us.get), "fastest_us": round(best, 2),
     }
 
 
-def measure_sweep(Wr, w13s, w2s, sp, steps):
+def measure_sweep(Wr, w13s, w2s, sp, steps, main_sched):
     """Shape dynamism: one template (T_max=512), batch B ~ U{1..512} per step,
     fresh tokens each step; per-launch latency from HIP events."""
     import torch
@@ -238,7 +246,7 @@ def measure_sweep(Wr, w13s, w2s, sp, steps):
     xs = [dev_bf16(wl.sweep_tokens(shape, i, int(b), 0)) for i, b in enumerate(Bs)]
     R = len(w13s)
     args = [bufs.args(x=xs[i], w13=w13s[i % R], w2=w2s[i % R]) for i in range(steps)]
-    code = B.SCHEDS["static"]
+    code = B.SCHEDS[main_sched]
     for i in range(3):  # warm-up launches at a few sizes
         B.check(B.moe_layer_launch(desc, int(Bs[i]), args[i], code, sp))
     torch.cuda.synchronize()
@@ -252,7 +260,7 @@ def measure_sweep(Wr, w13s, w2s, sp, steps):
     us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
     small = Bs <= 64
     return {
-        "steps": steps, "B_min": int(Bs.min()), "B_max": int(Bs.max()), "schedule": "static",
+        "steps": steps, "B_min": int(Bs.min()), "B_max": int(Bs.max()), "schedule": main_sched,
         "us_p50": round(float(np.percentile(us, 50)), 2), "us_p90": round(float(np.percentile(us, 90)), 2),
         "us_p99": round(float(np.percentile(us, 99)), 2), "us_max": round(float(us.max()), 2),
         "us_p50_B_le_64": round(float(np.median(us[small])), 2) if small.any() else None,
@@ -264,7 +272,8 @@ def measure_sweep(Wr, w13s, w2s, sp, steps):
 def measure_token_counts(Wr, w13s, w2s, sp, steps, warmup, repeat, counts=(1, 128, 1024)):
     """The pages compare schedules on the same MoE layer at several token
     counts (Event Tensor paper, Table 2).  Same Qwen3-30B-A3B shape, no bias;
-    µs per layer of each schedule and the static/barrier ratio."""
+    µs per layer of each schedule, and the speed-ups of the two event-driven
+    megakernel schedules over the barrier megakernel and over KBK."""
     import torch
     from dynamic_moe_task_amd import binding as B
     from dynamic_moe_task_amd import workloads as wl
@@ -275,11 +284,16 @@ def measure_token_counts(Wr, w13s, w2s, sp, steps, warmup, repeat, counts=(1, 12
         desc = B.moe_desc(T, shape.H, shape.E, shape.k, shape.I, shape.norm_topk, False)
         bufs = B.MoELayerBuffers.allocate(desc, Wr, w13s[0], w2s[0], None)
         bufs.x[:T].copy_(dev_bf16(X))
-        us = {s: float(np.median([time_sched(bufs, T, s, steps, warmup, w13s, w2s, sp) for _ in range(repeat)]))
-              for s in ("static", "barrier", "kbk")}
-        out[f"T={T}"] = {"us_per_layer": {s: round(v, 2) for s, v in us.items()},
-                         "static_over_barrier_speedup": round(us["barrier"] / us["static"], 3),
-                         "static_over_kbk_speedup": round(us["kbk"] / us["static"], 3)}
+        runs = {s: [] for s in SCHEDS}
+        for _ in range(repeat):
+            for s in SCHEDS:
+                runs[s].append(time_sched(bufs, T, s, steps, warmup, w13s, w2s, sp))
+        us = {s: float(np.median(v)) for s, v in runs.items()}
+        row = {"us_per_layer": {s: round(v, 2) for s, v in us.items()}}
+        for s in ("static", "ordered"):
+            row[f"{s}_over_barrier_speedup"] = round(us["barrier"] / us[s], 3)
+            row[f"{s}_over_kbk_speedup"] = round(us["kbk"] / us[s], 3)
+        out[f"T={T}"] = row
         del bufs
         torch.cuda.synchronize()
     out["note"] = ("T=4096 (the pages' largest count) exceeds this build's routing-bitmap limit "
@@ -331,7 +345,7 @@ def main():
     alg_bytes = wl.algorithmic_bytes(shape, T, n_act)
     alg_flops = wl.algorithmic_flops(shape, T)
 
-    scheds = [a.sched] if a.only_sched else ["static", "barrier", "kbk"]
+    scheds = [a.sched] if a.only_sched else list(SCHEDS)
     runs = {s: [] for s in scheds}
     for _ in range(max(1, a.repeat)):  # interleave the schedules, then take medians
         for s in scheds:
@@ -357,7 +371,7 @@ def main():
                 traffic_note = "counters were taken on different kernel sources"
     roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": f"moe_persistent<{a.sched}>" if a.sched != "kbk" else "kbk_* (7 launches)",
+                "kernel": f"moe_persistent<{a.sched}>" if a.sched != "kbk" else "kbk_* (6 launches)",
                 "algorithmic_bytes": alg_bytes, "traffic_note": traffic_note}
     mfma_frac = alg_flops / (us_main * 1e-6) / (BF16_PEAK_TFS * 1e12)
 
@@ -365,15 +379,16 @@ def main():
         info = B.moe_layer_info(desc)
         base = os.path.splitext(a.trace)[0]
         summ = {s: trace_summary(bufs, T, s, info.wall_clock_khz, sp, dump=f"{base}_{s}.npz")
-                for s in ("static", "barrier")}
+                for s in ("static", "ordered", "barrier")}
         summ["grid"] = info.grid
         with open(a.trace, "w") as f:
             json.dump(summ, f, indent=1)
 
     extra = {}
     if not a.no_extra and a.workload == "decode":
-        extra["prefill_zipf"] = measure_prefill(Wr, w13s, w2s, sp, max(10, a.steps // 2), a.warmup, a.repeat)
-        extra["sweep"] = measure_sweep(Wr, w13s, w2s, sp, a.sweep_steps)
+        extra["prefill_zipf"] = measure_prefill(Wr, w13s, w2s, sp, max(10, a.steps // 2), a.warmup, a.repeat,
+                                                a.sched)
+        extra["sweep"] = measure_sweep(Wr, w13s, w2s, sp, a.sweep_steps, a.sched)
         extra["token_counts"] = measure_token_counts(Wr, w13s, w2s, sp, max(10, a.steps // 2), a.warmup, a.repeat)
 
     cpu = None
