@@ -27,6 +27,7 @@ constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per
 constexpr int kBN2 = 64;        // G2: output columns per tile
 constexpr int kCB2 = kBN2 / 16;  // G2: 16-column MFMA blocks per tile
 constexpr int kCombineT = 2;    // C task: tokens per task
+constexpr int kEvStride = 32;   // words between event elements (one 128-byte line each)
 constexpr int kMaxK = 16;
 constexpr int kMaxE = 256;
 constexpr int kMaxTmax = 4096;
@@ -94,11 +95,11 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
   // every task except the router prefix goes through the queue
   L.q_cap = L.ntt_max + 1 + (int64_t)L.max_rt * (nN1 + nN2) + L.nct_max + 64;
   int64_t w = W_FIXED;
-  L.o_ev_logit = w; w += L.ntt_max;
-  L.o_ev_exp = w;   w += d.E;
-  L.o_ev_h = w;     w += L.max_rt;
-  L.o_ev_y = w;     w += L.max_rt;
-  L.o_ev_c = w;     w += L.nct_max;
+  L.o_ev_logit = w; w += (int64_t)L.ntt_max * kEvStride;
+  L.o_ev_exp = w;   w += (int64_t)d.E * kEvStride;
+  L.o_ev_h = w;     w += (int64_t)L.max_rt * kEvStride;
+  L.o_ev_y = w;     w += (int64_t)L.max_rt * kEvStride;
+  L.o_ev_c = w;     w += (int64_t)L.nct_max * kEvStride;
   w = align_up(w, 2);
   L.o_queue = w;    w += 2 * L.q_cap;
   L.set_words = align_up(w, 64);

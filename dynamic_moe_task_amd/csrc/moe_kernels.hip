@@ -178,11 +178,24 @@ __device__ __forceinline__ void trace_task(const MoeParams& p, int type, int a, 
 // ====================================================== event helpers ========
 // Event elements live in the launch's counter set; see etc_rt.h for the
 // counting and coherence rules.
-__device__ __forceinline__ uint32_t* ev_logit(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_logit; }
-__device__ __forceinline__ uint32_t* ev_exp(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_exp; }
-__device__ __forceinline__ uint32_t* ev_h(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_h; }
-__device__ __forceinline__ uint32_t* ev_y(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_y; }
-__device__ __forceinline__ uint32_t* ev_c(const MoeParams& p, const Ctx& c) { return c.set + p.o_ev_c; }
+// Each element sits on its own 128-byte line (kEvStride words apart): the
+// atomics of producers that notify different elements at the same time then
+// do not queue behind one another on a shared line.
+__device__ __forceinline__ uint32_t* ev_logit(const MoeParams& p, const Ctx& c, int i) {
+  return c.set + p.o_ev_logit + (int64_t)i * kEvStride;
+}
+__device__ __forceinline__ uint32_t* ev_exp(const MoeParams& p, const Ctx& c, int e) {
+  return c.set + p.o_ev_exp + (int64_t)e * kEvStride;
+}
+__device__ __forceinline__ uint32_t* ev_h(const MoeParams& p, const Ctx& c, int rt) {
+  return c.set + p.o_ev_h + (int64_t)rt * kEvStride;
+}
+__device__ __forceinline__ uint32_t* ev_y(const MoeParams& p, const Ctx& c, int rt) {
+  return c.set + p.o_ev_y + (int64_t)rt * kEvStride;
+}
+__device__ __forceinline__ uint32_t* ev_c(const MoeParams& p, const Ctx& c, int ct) {
+  return c.set + p.o_ev_c + (int64_t)ct * kEvStride;
+}
 __device__ __forceinline__ uint32_t ctile_target(const Ctx& c, int ct) {
   return (uint32_t)(min(kCombineT, c.T - ct * kCombineT) * c.k * c.nN2);
 }
@@ -362,7 +375,7 @@ __device__ void task_topk(const MoeParams& p, const Ctx& c, int tt) {
     // (G1 reads x, an input, and S's tables, ordered by S's own event), so
     // the notify needs no drain.
     if (c.set) {
-      notify_fast(p, c, ev_exp(p, c) + my_e, 0xffffffffu);
+      notify_fast(p, c, ev_exp(p, c, my_e), 0xffffffffu);
       if (p.debug) atomicAdd(p.debug + my_e, 1);
     }
   }
@@ -451,7 +464,7 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   if (tid < E && c.set && p.debug) {
     // every routed pair has notified by now (S runs after all of K): the
     // expert event holds exactly counts[e] arrivals and fires once
-    if (my > 0 && ld_relaxed(ev_exp(p, c) + tid) == (uint32_t)my) atomicAdd(p.debug + E + tid, 1);
+    if (my > 0 && ld_relaxed(ev_exp(p, c, tid)) == (uint32_t)my) atomicAdd(p.debug + E + tid, 1);
   }
   if (tid == 0) {
     iptr[E] = tot_rows;
@@ -766,7 +779,7 @@ __device__ void after_router(const MoeParams& p, const Ctx& c, int tt) {
   if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC || MODE == MODE_ORDERED) {
     wg_publish();
     if (threadIdx.x == 0) {
-      if (notify1(c, ev_logit(p, c) + tt, (uint32_t)c.nET) && MODE == MODE_DYNAMIC) {
+      if (notify1(c, ev_logit(p, c, tt), (uint32_t)c.nET) && MODE == MODE_DYNAMIC) {
         const int64_t q = q_reserve(p, c, 1);
         if (q >= 0) q_put(c, q, make_desc(TT_K, tt, 0));
       }
@@ -818,7 +831,7 @@ __device__ void after_g1(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
   wg_publish();
   if (threadIdx.x == 0) {
     sh.base = -1;
-    if (notify1(c, ev_h(p, c) + rt, (uint32_t)c.nN1) && MODE == MODE_DYNAMIC)
+    if (notify1(c, ev_h(p, c, rt), (uint32_t)c.nN1) && MODE == MODE_DYNAMIC)
       sh.base = (int)q_reserve(p, c, c.nN2);
   }
   if (MODE == MODE_DYNAMIC) {
@@ -840,7 +853,7 @@ __device__ void after_g2(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
   if (threadIdx.x < tile.nrows) {
     const int f = (int)co_ld32(r_perm(p), (uint32_t)(tile.r0 + threadIdx.x) * 4u);
     const int ct = (f / c.k) / kCombineT;
-    if (notify1(c, ev_c(p, c) + ct, ctile_target(c, ct)) && MODE == MODE_DYNAMIC)
+    if (notify1(c, ev_c(p, c, ct), ctile_target(c, ct)) && MODE == MODE_DYNAMIC)
       sh.list[atomicAdd(&sh.n, 1)] = ct;
   }
   if (MODE == MODE_DYNAMIC) {
@@ -908,11 +921,11 @@ __device__ bool wait_rows_done(const MoeParams& p, const Ctx& c, int ct) {
   if (threadIdx.x < 64) {
     const int t0 = ct * kCombineT, nrow = min(kCombineT, c.T - t0) * c.k;
     const bool mine = (int)threadIdx.x < nrow;
-    uint32_t* ctr = ev_y(p, c);
+    uint32_t* ctr = ev_y(p, c, 0);
     if (mine) {
       const uint32_t s = co_ld32(r_slot(p), (uint32_t)(t0 * c.k + (int)threadIdx.x) * 4u);
       const uint32_t rt = co_ld32(r_rowrt(p), s * 4u);
-      ctr += rt;
+      ctr = ev_y(p, c, (int)rt);
       if (p.debug) {  // count the rows whose mapped tile really holds them
         const u32x4_t q = co_ld128(r_rtinfo(p), rt * 16u);
         if (s >= q.y && s < q.y + q.z) atomicAdd(p.debug + 2 * c.E + 7, 1);
@@ -942,8 +955,6 @@ __device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int 
   if (i0 >= n) return;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
-  uint32_t* evx = ev_exp(p, c);
-  uint32_t* evh = ev_h(p, c);
   const rsrc_t rcnt = r_counts(p);
   RowTile cur = load_rowtile(p, i0 / c.nN1);
   RowTile nxt = cur;
@@ -951,23 +962,28 @@ __device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int 
   uint32_t cur_tgt = 0, cur_arr = 0;
   if (threadIdx.x == 0) {
     cur_tgt = co_ld32(rcnt, (uint32_t)cur.e * 4u);
-    cur_arr = ld_relaxed(evx + cur.e);
+    cur_arr = ld_relaxed(ev_exp(p, c, cur.e));
   }
   // grouped-row permutation entries of the tile's rows (A gather), one task ahead
   uint32_t cur_f[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) cur_f[b] = row_perm(p, cur, b);
+  // Enter the loop with nothing in flight: otherwise the compiler, merging
+  // the entry path (prefetch loads pending) with the back edge (only the
+  // notify pending), waits for all memory operations at the top of every
+  // task, the previous notify's round trip included.
+  __builtin_amdgcn_s_waitcnt(0);
   for (int i = i0; i < n; i += G) {
     const int rt = i / c.nN1, nt = i % c.nN1;
     if (tr) tw = now_ticks();
-    if (!wait_known(evx + cur.e, cur_tgt, cur_arr, c)) return;
+    if (!wait_known(ev_exp(p, c, cur.e), cur_tgt, cur_arr, c)) return;
     if (tr) ts = now_ticks();
     RowTile nn = nxt;
     if (i + 2 * G < n) nn = load_rowtile(p, (i + 2 * G) / c.nN1);
     uint32_t nxt_tgt = 0, nxt_arr = 0;
     if (threadIdx.x == 0 && i + G < n) {
       nxt_tgt = co_ld32(rcnt, (uint32_t)nxt.e * 4u);
-      nxt_arr = ld_relaxed(evx + nxt.e);
+      nxt_arr = ld_relaxed(ev_exp(p, c, nxt.e));
     }
     uint32_t nxt_f[4];
 #pragma unroll
@@ -977,7 +993,7 @@ __device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int 
     // outside the notify branch so that, after the branch, only the notify
     // is in flight and the prefetched registers need no further wait.
     __builtin_amdgcn_s_waitcnt(0);
-    if (threadIdx.x == 0) notify_fast(p, c, evh + rt, (uint32_t)c.nN1);
+    if (threadIdx.x == 0) notify_fast(p, c, ev_h(p, c, rt), (uint32_t)c.nN1);
     if (tr) tb = now_ticks();
     dbg_task(p, TT_G1);
     trace_task(p, TT_G1, rt, nt, tw, ts, tb);
@@ -994,27 +1010,26 @@ __device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int 
   if (i0 >= n) return;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
-  uint32_t* evh = ev_h(p, c);
-  uint32_t* evy = ev_y(p, c);
   const uint32_t tgt = (uint32_t)c.nN1;
   RowTile cur = load_rowtile(p, i0 / c.nN2);
   RowTile nxt = cur;
   if (i0 + G < n) nxt = load_rowtile(p, (i0 + G) / c.nN2);
   uint32_t cur_arr = 0;
-  if (threadIdx.x == 0) cur_arr = ld_relaxed(evh + i0 / c.nN2);
+  if (threadIdx.x == 0) cur_arr = ld_relaxed(ev_h(p, c, i0 / c.nN2));
+  __builtin_amdgcn_s_waitcnt(0);  // loop entry with nothing in flight (see run_g1_static)
   for (int i = i0; i < n; i += G) {
     const int rt = i / c.nN2, nt = i % c.nN2;
     if (tr) tw = now_ticks();
-    if (!wait_known(evh + rt, tgt, cur_arr, c)) return;
+    if (!wait_known(ev_h(p, c, rt), tgt, cur_arr, c)) return;
     if (tr) ts = now_ticks();
     RowTile nn = nxt;
     if (i + 2 * G < n) nn = load_rowtile(p, (i + 2 * G) / c.nN2);
     uint32_t nxt_arr = 0;
-    if (threadIdx.x == 0 && i + G < n) nxt_arr = ld_relaxed(evh + (i + G) / c.nN2);
+    if (threadIdx.x == 0 && i + G < n) nxt_arr = ld_relaxed(ev_h(p, c, (i + G) / c.nN2));
     // combine tile of each row's token (wave 0, one row a lane)
     task_g2(p, c, cur, rt, nt, red);
     __builtin_amdgcn_s_waitcnt(0);  // wave 0 wrote the rows: drain, then notify (as in G1)
-    if (threadIdx.x == 0) notify_fast(p, c, evy + rt, (uint32_t)c.nN2);
+    if (threadIdx.x == 0) notify_fast(p, c, ev_y(p, c, rt), (uint32_t)c.nN2);
     if (tr) tb = now_ticks();
     dbg_task(p, TT_G2);
     trace_task(p, TT_G2, rt, nt, tw, ts, tb);
@@ -1054,8 +1069,6 @@ __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, con
   const int n = q.n;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
-  uint32_t* evx = ev_exp(p, c);
-  uint32_t* evh = ev_h(p, c);
   const rsrc_t rcnt = r_counts(p);
   if (threadIdx.x == 0) {
     sk[0] = add_relaxed(q.ctr, 1u);
@@ -1073,16 +1086,17 @@ __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, con
     uint32_t cur_tgt = 0, cur_arr = 0;
     if (threadIdx.x == 0) {
       cur_tgt = co_ld32(rcnt, (uint32_t)rc.e * 4u);
-      cur_arr = ld_relaxed(evx + rc.e);
+      cur_arr = ld_relaxed(ev_exp(p, c, rc.e));
     }
     uint32_t cur_f[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) cur_f[b] = row_perm(p, rc, b);
+    __builtin_amdgcn_s_waitcnt(0);  // loop entry with nothing in flight (see run_g1_static)
     int par = 2;  // claim slot that holds the ordinal after nxt
     for (;;) {
       const int rt = cur / c.nN1, nt = cur % c.nN1;
       if (tr) tw = now_ticks();
-      if (!wait_known(evx + rc.e, cur_tgt, cur_arr, c)) return false;
+      if (!wait_known(ev_exp(p, c, rc.e), cur_tgt, cur_arr, c)) return false;
       if (tr) ts = now_ticks();
       const int aft = claimed_task(q, sk[par]);
       uint32_t knew = 0xffffffffu;
@@ -1101,7 +1115,7 @@ __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, con
       uint32_t nxt_tgt = 0, nxt_arr = 0;
       if (threadIdx.x == 0 && nxt < n) {
         nxt_tgt = co_ld32(rcnt, (uint32_t)rn.e * 4u);
-        nxt_arr = ld_relaxed(evx + rn.e);
+        nxt_arr = ld_relaxed(ev_exp(p, c, rn.e));
       }
       uint32_t nxt_f[4];
 #pragma unroll
@@ -1109,7 +1123,7 @@ __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, con
       task_g1(p, c, rc, rt, nt, red, cur_f);
       __builtin_amdgcn_s_waitcnt(0);  // drain, then notify (see run_g1_static)
       if (threadIdx.x == 0) {
-        notify_fast(p, c, evh + rt, (uint32_t)c.nN1);
+        notify_fast(p, c, ev_h(p, c, rt), (uint32_t)c.nN1);
         sk[par ^ 1] = knew;
       }
       if (tr) tb = now_ticks();
@@ -1146,8 +1160,6 @@ __device__ bool run_g2_ordered(const MoeParams& p, const Ctx& c, float* red, con
   const int n = q.n;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
-  uint32_t* evh = ev_h(p, c);
-  uint32_t* evy = ev_y(p, c);
   const uint32_t tgt = (uint32_t)c.nN1;
   __syncthreads();
   int cur = claimed_task(q, sk[0]), nxt = claimed_task(q, sk[1]);
@@ -1156,12 +1168,13 @@ __device__ bool run_g2_ordered(const MoeParams& p, const Ctx& c, float* red, con
   RowTile rn = rc;
   if (nxt < n) rn = load_rowtile(p, nxt / c.nN2);
   uint32_t cur_arr = 0;
-  if (threadIdx.x == 0) cur_arr = ld_relaxed(evh + cur / c.nN2);
+  if (threadIdx.x == 0) cur_arr = ld_relaxed(ev_h(p, c, cur / c.nN2));
+  __builtin_amdgcn_s_waitcnt(0);  // loop entry with nothing in flight (see run_g1_static)
   int par = 2;
   for (;;) {
     const int rt = cur / c.nN2, nt = cur % c.nN2;
     if (tr) tw = now_ticks();
-    if (!wait_known(evh + rt, tgt, cur_arr, c)) return false;
+    if (!wait_known(ev_h(p, c, rt), tgt, cur_arr, c)) return false;
     if (tr) ts = now_ticks();
     const int aft = claimed_task(q, sk[par]);
     uint32_t knew = 0xffffffffu;
@@ -1169,11 +1182,11 @@ __device__ bool run_g2_ordered(const MoeParams& p, const Ctx& c, float* red, con
     RowTile ra = rn;
     if (aft < n) ra = load_rowtile(p, aft / c.nN2);
     uint32_t nxt_arr = 0;
-    if (threadIdx.x == 0 && nxt < n) nxt_arr = ld_relaxed(evh + nxt / c.nN2);
+    if (threadIdx.x == 0 && nxt < n) nxt_arr = ld_relaxed(ev_h(p, c, nxt / c.nN2));
     task_g2(p, c, rc, rt, nt, red);
     __builtin_amdgcn_s_waitcnt(0);  // drain, then notify (see run_g1_static)
     if (threadIdx.x == 0) {
-      notify_fast(p, c, evy + rt, (uint32_t)c.nN2);
+      notify_fast(p, c, ev_y(p, c, rt), (uint32_t)c.nN2);
       sk[par ^ 1] = knew;
     }
     if (tr) tb = now_ticks();
@@ -1216,7 +1229,7 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
   if (!EV && !grid_barrier(c, G)) return;
   for (int i = first_of(w, off, G); i < c.nK; i += G) {
     if (tr) tw = now_ticks();
-    if (EV && !wg_wait(ev_logit(p, c) + i, (uint32_t)c.nET, c.status, c.budget)) return;
+    if (EV && !wg_wait(ev_logit(p, c, i), (uint32_t)c.nET, c.status, c.budget)) return;
     if (tr) ts = now_ticks();
     task_topk(p, c, i);
     if (tr) tb = now_ticks();
