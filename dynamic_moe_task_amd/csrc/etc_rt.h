@@ -110,6 +110,27 @@ __device__ __forceinline__ bool spin_until_geq(const uint32_t* ctr, uint32_t tar
   }
 }
 
+// As spin_until_geq, and hands back the value that satisfied the wait.
+__device__ __forceinline__ bool spin_value_geq(const uint32_t* ctr, uint32_t target, uint32_t* status,
+                                               uint64_t budget, uint32_t* seen) {
+  const uint64_t t0 = now_ticks();
+  for (uint32_t spins = 1;; ++spins) {
+    const uint32_t v = ld_relaxed(ctr);
+    if (v >= target) {
+      *seen = v;
+      return true;
+    }
+    if ((spins & 7u) == 0u) {
+      if (ld_relaxed(status) & ST_ABORT) return false;
+      if (now_ticks() - t0 > budget) {
+        or_relaxed(status, ST_TIMEOUT | ST_ABORT);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 // Whole-workgroup wait on one event element: thread 0 polls, the barrier
 // releases the others.  Data produced before the notifies is then read with
 // device-coherent loads.  Returns false on abort (uniform in the workgroup).

@@ -413,7 +413,8 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
 // than 32 rows), then of two, then of one, each class in expert order.  The
 // lists deal G1 and G2 tasks in tile order, so the longest tasks start first
 // and the short ones fill in at the end (longest processing time first).
-__device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
+// Returns the number of row tiles (uniform over the workgroup).
+__device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   const int tid = threadIdx.x;
   const int E = c.E, k = c.k, n = c.T * c.k;
   const int W = (c.T + 31) >> 5;
@@ -496,6 +497,7 @@ __device__ void task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
       co_st128(rr, (uint32_t)rt * 16u, q);
     }
   }
+  return tot_tiles;
 }
 
 // Grouped-GEMM tasks.  A row tile holds up to kBM = 64 grouped rows of one
@@ -801,7 +803,7 @@ __device__ void after_topk(const MoeParams& p, const Ctx& c) {
 }
 
 template <int MODE>
-__device__ void after_scan(const MoeParams& p, const Ctx& c, Shared& sh) {
+__device__ void after_scan(const MoeParams& p, const Ctx& c, Shared& sh, int nrt) {
   if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC || MODE == MODE_ORDERED) {
     wg_publish();
     if (MODE == MODE_DYNAMIC) {
@@ -820,7 +822,9 @@ __device__ void after_scan(const MoeParams& p, const Ctx& c, Shared& sh) {
         for (int i = threadIdx.x; i < n1; i += kThreads) q_put(c, base + i, make_desc(TT_G1, i / c.nN1, i % c.nN1));
       __syncthreads();
     } else {
-      if (threadIdx.x == 0) notify1(c, c.set + W_EV_SCAN, 1u);
+      // the scan event is complete at any value >= 1; S stores nrt + 1, so
+      // that a waiter learns the row-tile count from the poll that frees it
+      if (threadIdx.x == 0) xchg_relaxed(c.set + W_EV_SCAN, (uint32_t)nrt + 1u);
     }
   }
 }
@@ -1070,12 +1074,7 @@ __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, con
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
   const rsrc_t rcnt = r_counts(p);
-  if (threadIdx.x == 0) {
-    sk[0] = add_relaxed(q.ctr, 1u);
-    sk[1] = add_relaxed(q.ctr, 1u);
-    sk[2] = add_relaxed(q.ctr, 1u);
-  }
-  __syncthreads();
+  // sk[0..2] hold the first three claims, taken by the caller before S ended
   int cur = claimed_task(q, sk[0]), nxt = claimed_task(q, sk[1]);
   uint32_t g2k0 = 0, g2k1 = 0, g2k2 = 0;  // thread 0: first G2 claims, taken during the last G1 tile
   bool g2_taken = false;
@@ -1243,29 +1242,44 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
     if (tr) tw = now_ticks();
     if (EV && !wg_wait(c.set + W_EV_ROUTE, (uint32_t)c.nK, c.status, c.budget)) return;
     if (tr) ts = now_ticks();
-    task_scan(p, c, smem);
+    const int nrt_s = task_scan(p, c, smem);
     if (tr) tb = now_ticks();
     dbg_task(p, TT_S);
-    after_scan<MODE>(p, c, sh);
+    after_scan<MODE>(p, c, sh, nrt_s);
     trace_task(p, TT_S, 0, 0, tw, ts, tb);
   }
   off += 1;
-  if (EV) {
-    if (!wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;
-  } else if (!grid_barrier(c, G)) {
-    return;
+  // ORDERED: the first three G1 claims are taken while S still runs (an
+  // ordinal does not depend on S's result)
+  const int ngrp = G % 8 == 0 ? 8 : 1, grp = w % ngrp;
+  if (MODE == MODE_ORDERED && threadIdx.x == 0) {
+    uint32_t* ctr = c.set + W_CLAIM_G1 + grp * 32;
+    sh.claim[0] = add_relaxed(ctr, 1u);
+    sh.claim[1] = add_relaxed(ctr, 1u);
+    sh.claim[2] = add_relaxed(ctr, 1u);
   }
-  const int nrt = (int)ld_relaxed(p.meta + M_NRT);
+  int nrt;
+  if (EV) {
+    if (threadIdx.x == 0) {
+      uint32_t v = 0;
+      sh.claim[3] = spin_value_geq(c.set + W_EV_SCAN, 1u, c.status, c.budget, &v) ? v : 0u;
+    }
+    __syncthreads();
+    if (sh.claim[3] == 0u) return;  // aborting
+    nrt = (int)sh.claim[3] - 1;
+  } else {
+    if (!grid_barrier(c, G)) return;
+    nrt = (int)ld_relaxed(p.meta + M_NRT);
+  }
   const int nG1 = nrt * c.nN1, nG2 = nrt * c.nN2;
   // Few GEMM tasks (at most three a CU): deal G1, G2 and C over only the
   // first workgroup of each CU, so that no two weight streams share a CU's
   // load path; the other workgroups are done (and BARRIER's later barriers
   // count only the ones left).  Workgroups are placed one a CU before any
   // CU takes a second, so the first solo_wgs workgroups sit on distinct CUs.
-  const int Gt = (p.solo_wgs > 0 && nG1 <= 3 * p.solo_wgs) ? p.solo_wgs : G;
+  const int Gt = (MODE != MODE_ORDERED && p.solo_wgs > 0 && nG1 <= 3 * p.solo_wgs) ? p.solo_wgs : G;
   if (w >= Gt) return;
   if (MODE == MODE_ORDERED) {
-    const int ngrp = Gt % 8 == 0 ? 8 : 1, grp = w % ngrp;
     const ClaimQ q1{c.set + W_CLAIM_G1 + grp * 32, grp, ngrp, nG1};
     const ClaimQ q2{c.set + W_CLAIM_G2 + grp * 32, grp, ngrp, nG2};
     if (!run_g1_ordered(p, c, red, q1, q2, sh.claim)) return;
@@ -1368,13 +1382,14 @@ __device__ void run_dynamic(const MoeParams& p, const Ctx& c, uint8_t* smem, Sha
         after_topk<MODE_DYNAMIC>(p, c);
         trace_task(p, TT_K, a, b, tw, ts, tb);
         break;
-      case TT_S:
-        task_scan(p, c, smem);
+      case TT_S: {
+        const int nrt_s = task_scan(p, c, smem);
         if (tr) tb = now_ticks();
         dbg_task(p, TT_S);
-        after_scan<MODE_DYNAMIC>(p, c, sh);
+        after_scan<MODE_DYNAMIC>(p, c, sh, nrt_s);
         trace_task(p, TT_S, a, b, tw, ts, tb);
         break;
+      }
       case TT_G1:
         task_g1(p, c, load_rowtile(p, a), a, b, red);
         if (tr) tb = now_ticks();
