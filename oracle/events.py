@@ -21,6 +21,11 @@ scheduling transformations use it:
 * Dynamic schedule: when a notify takes a counter to zero the waiting task
   is pushed at once onto a shared queue, and idle workers pop from it.
   [Figs. 8-9; podcast cue 11]
+* Ordered claiming (this build's own variant, no passage of the pages):
+  the tasks of a phase are claimed in index order from one counter per
+  group of workers, a few ordinals ahead, and each claimed task still waits
+  on its events; run_ordered checks that such a schedule cannot deadlock
+  when the phases respect the graph's order.
 """
 from __future__ import annotations
 
@@ -161,3 +166,80 @@ def run_dynamic(tasks: List[Task], state: EventState, seed: int = 0) -> List[int
     if len(order) != len(tasks):
         raise RuntimeError("dynamic schedule stalled: some task never became ready")
     return order
+
+
+def run_ordered(tasks: List[Task], state: EventState, workers: int,
+                phases: Sequence[Tuple[str, Sequence[int]]], groups: int = 8, ahead: int = 3,
+                seed: int = 0) -> List[int]:
+    """Workers go through `phases` in order.  A ("deal", ids) phase gives
+    worker w every task ids[i] with (i + off) % workers == w, where off is
+    the number of tasks dealt in earlier phases (round-robin continuing from
+    where the previous phase stopped).  A ("claim", ids) phase hands out
+    ordinals from one counter per group (group = worker % groups when the
+    worker count is a multiple of `groups`, else one group): ordinal k of
+    group g is ids[k * ngroups + g]; a worker holds `ahead` ordinals from the
+    start of the phase and claims one more each time it finishes a task,
+    until an ordinal falls past the end.  Each step advances one worker
+    chosen at random (random speeds); a worker whose next task waits on an
+    unreleased event stalls.  Returns the completion order; raises
+    RuntimeError on deadlock."""
+    rng = random.Random(seed)
+    ngrp = groups if workers % groups == 0 else 1
+    counters = [[0] * ngrp for _ in phases]
+    offs, off = [], 0
+    for mode, ids in phases:
+        offs.append(off)
+        if mode == "deal":
+            off += len(ids)
+    phase = [0] * workers
+    queue: List[List[int]] = [[] for _ in range(workers)]  # tasks (or held ordinals) of the current phase
+
+    def enter(w: int) -> None:
+        while phase[w] < len(phases):
+            mode, ids = phases[phase[w]]
+            if mode == "deal":
+                queue[w] = [ids[i] for i in range(len(ids)) if (i + offs[phase[w]]) % workers == w]
+            else:
+                queue[w] = []
+                for _ in range(ahead):
+                    claim(w)
+            if queue[w]:
+                return
+            phase[w] += 1
+
+    def claim(w: int) -> None:
+        mode, ids = phases[phase[w]]
+        g = w % ngrp
+        k = counters[phase[w]][g]
+        counters[phase[w]][g] += 1
+        i = k * ngrp + g
+        if i < len(ids):
+            queue[w].append(ids[i])
+
+    for w in range(workers):
+        enter(w)
+    order: List[int] = []
+    live = [w for w in range(workers) if phase[w] < len(phases)]
+    while live:
+        rng.shuffle(live)
+        progressed = False
+        for w in live:
+            t = tasks[queue[w][0]]
+            if all(state.ready(k) for k in t.waits):
+                if t.run:
+                    t.run()
+                for k in t.notifies:
+                    state.notify(k)
+                order.append(queue[w].pop(0))
+                if phases[phase[w]][0] == "claim" and len(queue[w]) == ahead - 1:
+                    claim(w)  # the stream continues while its last claim was inside the phase
+                if not queue[w]:
+                    phase[w] += 1
+                    enter(w)
+                progressed = True
+                break
+        if not progressed:
+            raise RuntimeError("ordered schedule deadlocked")
+        live = [w for w in range(workers) if phase[w] < len(phases)]
+    return order
+

@@ -439,3 +439,86 @@ def test_moe_event_graph_counts_and_single_fire():
         assert st.fired[("exp", (e,))] == 1
     n_tiles = sum(math.ceil(c / bm) for c in counts)
     assert len(oracle.expected_tiles(r["exp_indptr"], bm)) == n_tiles
+
+
+def _moe_layer_graph(T, E, k, bm, n1, n2, seed):
+    """Event graph of one MoE layer as the megakernel runs it: R(tt, et) ->
+    ev_logit[tt] -> K(tt) -> (ev_exp[e] once per routed pair, ev_route) ->
+    S -> ev_scan -> G1(rt, n) -> ev_h[rt] -> G2(rt, n) -> ev_y[rt] -> C(ct),
+    where C waits on every row tile holding one of its tokens' rows.  Row
+    tiles are cut from exp_indptr as the oracle defines them."""
+    rng = np.random.default_rng(seed)
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int64)
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    indptr = np.concatenate([[0], np.cumsum(counts)])
+    tiles = oracle.expected_tiles(indptr, bm)
+    row_tile = {}
+    for rt, (e, lo, hi) in enumerate(tiles):
+        for r in range(lo, hi):
+            row_tile[r] = rt
+    rank = {}
+    slot = np.zeros((T, k), np.int64)
+    for t in range(T):  # stable: rows of one expert in ascending token order
+        for j in range(k):
+            e = int(ids[t, j])
+            slot[t, j] = indptr[e] + rank.get(e, 0)
+            rank[e] = rank.get(e, 0) + 1
+    rt_tok, et_exp, ct_tok = 4, 4, 2
+    ntt, net, nct = -(-T // rt_tok), -(-E // et_exp), -(-T // ct_tok)
+    st = ev.EventState()
+    st.declare("logit", (ntt,), net)
+    st.declare("route", (1,), ntt)
+    st.declare("exp", (E,), lambda i: int(counts[i[0]]))
+    st.declare("scan", (1,), 1)
+    st.declare("h", (len(tiles),), n1)
+    st.declare("y", (len(tiles),), n2)
+    tasks, ph = [], {n: [] for n in ("R", "K", "S", "G1", "G2", "C")}
+
+    def add(name, key, waits, notifies):
+        ph[name].append(len(tasks))
+        tasks.append(ev.Task(name, key, waits, notifies))
+
+    for tt in range(ntt):
+        for et in range(net):
+            add("R", (tt, et), [], [("logit", (tt,))])
+    for tt in range(ntt):
+        pairs = [("exp", (int(ids[t, j]),)) for t in range(tt * rt_tok, min(T, tt * rt_tok + rt_tok))
+                 for j in range(k)]
+        add("K", (tt,), [("logit", (tt,))], pairs + [("route", (0,))])
+    add("S", (0,), [("route", (0,))], [("scan", (0,))])
+    for rt, (e, lo, hi) in enumerate(tiles):
+        for n in range(n1):
+            add("G1", (rt, n), [("scan", (0,)), ("exp", (e,))], [("h", (rt,))])
+    for rt in range(len(tiles)):
+        for n in range(n2):
+            add("G2", (rt, n), [("h", (rt,))], [("y", (rt,))])
+    for ct in range(nct):
+        rts = sorted({row_tile[int(slot[t, j])] for t in range(ct * ct_tok, min(T, ct * ct_tok + ct_tok))
+                      for j in range(k)})
+        add("C", (ct,), [("scan", (0,))] + [("y", (rt,)) for rt in rts], [])
+    return tasks, st, ph
+
+
+@pytest.mark.parametrize("workers", [5, 8, 16])
+@pytest.mark.parametrize("seed", range(3))
+def test_ordered_claims_complete_the_moe_graph(workers, seed):
+    # The ORDERED schedule: R, K, S dealt in phase order, then G1 and G2
+    # tiles claimed in index order from per-group counters three ahead,
+    # then C dealt.  With workers of random speed every task completes and
+    # every non-empty event fires exactly once.
+    tasks, st, ph = _moe_layer_graph(T=12, E=8, k=2, bm=4, n1=3, n2=2, seed=seed)
+    phases = [("deal", ph["R"]), ("deal", ph["K"]), ("deal", ph["S"]), ("claim", ph["G1"]),
+              ("claim", ph["G2"]), ("deal", ph["C"])]
+    order = ev.run_ordered(tasks, st, workers, phases, groups=4, seed=seed)
+    assert sorted(order) == list(range(len(tasks))) and not st.errors
+    assert all(v == 1 for v in st.fired.values())
+
+
+def test_ordered_claims_out_of_graph_order_deadlock():
+    # Claiming G2 tiles before G1 tiles breaks the argument: every worker
+    # then holds a G2 tile whose G1 producers nobody can start.
+    tasks, st, ph = _moe_layer_graph(T=12, E=8, k=2, bm=4, n1=3, n2=2, seed=0)
+    phases = [("deal", ph["R"]), ("deal", ph["K"]), ("deal", ph["S"]), ("claim", ph["G2"]),
+              ("claim", ph["G1"]), ("deal", ph["C"])]
+    with pytest.raises(RuntimeError):
+        ev.run_ordered(tasks, st, 4, phases, groups=4, seed=0)
