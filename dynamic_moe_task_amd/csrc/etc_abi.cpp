@@ -123,8 +123,6 @@ int desc_check(const etc_moe_desc* d) {
   if (d->k < 1 || d->k > kMaxK || d->k > d->E) return fail(ETC_ERR_INVALID, "k %d outside [1, min(E, %d)]", d->k, kMaxK);
   if ((int64_t)d->T_max * d->k * (d->H > d->I ? d->H : d->I) * 2 >= (int64_t)1 << 31)
     return fail(ETC_ERR_INVALID, "T_max * k * max(H, I) * 2 bytes must stay below 2 GiB");
-  if ((int64_t)d->E * cdiv(d->T_max, 32) > kMaxBitmapWords)
-    return fail(ETC_ERR_INVALID, "E * ceil(T_max/32) = %lld exceeds %d", (long long)d->E * cdiv(d->T_max, 32), kMaxBitmapWords);
   if (d->norm_topk != 0 && d->norm_topk != 1) return fail(ETC_ERR_INVALID, "norm_topk must be 0 or 1");
   if (d->has_bias != 0 && d->has_bias != 1) return fail(ETC_ERR_INVALID, "has_bias must be 0 or 1");
   return ETC_OK;

@@ -30,9 +30,10 @@ constexpr int kCombineT = 2;    // C task: tokens per task
 constexpr int kEvStride = 32;   // words between event elements (one 128-byte line each)
 constexpr int kMaxK = 16;
 constexpr int kMaxE = 256;
-constexpr int kMaxTmax = 4096;
+constexpr int kMaxTmax = 16384;
 constexpr int kMaxHI = 16384;
-constexpr int kMaxBitmapWords = 8192;  // E * ceil(T_max / 32), LDS of the scan task
+constexpr int kScanChunkT = 512;       // S: tokens per bitmap pass
+constexpr int kScanW = kScanChunkT / 32;  // S: bitmap words per expert and pass
 // watchdog of one in-kernel wait, in microseconds of wall time; a healthy
 // wait lasts microseconds
 constexpr uint32_t kDefaultWatchdogUs = 2000000u;
@@ -117,11 +118,12 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
   return L;
 }
 
-// LDS bytes the scan task needs: presence bitmap, per-word prefix (u16),
-// counts / exp_indptr scratch and the scan's partial sums.
+// LDS bytes the scan task needs: one chunk's presence bitmap and per-word
+// prefixes, counts / exp_indptr / tile-numbering scratch and the scan's
+// partial sums.  Independent of T_max (the scan walks the tokens in chunks).
 inline int64_t scan_lds_bytes(int E, int T_max) {
-  const int64_t W = cdiv(T_max, 32);
-  return align_up((int64_t)E * W * 4, 16) + align_up((int64_t)E * W * 2, 16) + 4 * 260 * 4 + 64;
+  (void)T_max;
+  return (int64_t)E * kScanW * 4 * 2 + 4 * 260 * 4 + 64;
 }
 // G2: cross-wave reduction buffer (4 waves x 4 blocks x 256 fp32) plus the
 // bf16 staging of the kBM x 64 output tile

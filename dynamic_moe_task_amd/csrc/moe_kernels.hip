@@ -406,8 +406,11 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
 
 // S: counts, exp_indptr (exclusive prefix sum of counts, ends at T*k), the
 // stable permutation (rows of one expert keep ascending token order) and
-// the row-tile table.  One workgroup; a per-expert token bitmap in LDS gives
-// each routed pair its rank among the same expert's earlier tokens.
+// the row-tile table.  One workgroup.  Tokens are taken kScanChunkT at a
+// time: a per-expert token bitmap of the chunk in LDS gives each routed pair
+// its rank among the same expert's earlier tokens of the chunk, and a
+// per-expert running count carries the ranks across chunks, so the LDS the
+// scan needs does not grow with T.
 //
 // Row tiles are numbered heaviest first: tiles of four 16-row blocks (more
 // than 32 rows), then of two, then of one, each class in expert order.  The
@@ -417,30 +420,40 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
 __device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   const int tid = threadIdx.x;
   const int E = c.E, k = c.k, n = c.T * c.k;
-  const int W = (c.T + 31) >> 5;
+  const int nch = (c.T + kScanChunkT - 1) / kScanChunkT;
+  const int W = (min(c.T, kScanChunkT) + 31) >> 5;  // bitmap words per expert and chunk
   uint32_t* bits = reinterpret_cast<uint32_t*>(smem);
-  uint16_t* pre = reinterpret_cast<uint16_t*>(smem + ((E * W * 4 + 15) & ~15));
-  int* cnt = reinterpret_cast<int*>(smem + ((E * W * 4 + 15) & ~15) + ((E * W * 2 + 15) & ~15));
+  int* pre = reinterpret_cast<int*>(smem + E * kScanW * 4);
+  int* cnt = pre + E * kScanW;
   int* iptr = cnt + 260;
   int* tmp = iptr + 260;         // 16 words for block_excl_scan
   int* tfirst = tmp + 16;        // per expert: first four-block tile | (number of them << 16)
   int* ttail = tfirst + 260;     // per expert: the tile of its last rows when that tile is smaller
   const rsrc_t rids = r_ids(p);
-  for (int i = tid; i < E * W; i += kThreads) bits[i] = 0u;
-  __syncthreads();
-  for (int f = tid; f < n; f += kThreads) {
-    const int e = (int)co_ld32(rids, (uint32_t)f * 4u);
-    const int t = f / k;
-    atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += kThreads) {
-    int run = 0;
-    for (int w = 0; w < W; ++w) {
-      pre[e * W + w] = (uint16_t)run;
-      run += __popc(bits[e * W + w]);
+  // the bitmap of chunk `ch`: bit t - ch * kScanChunkT of word row e is set
+  // when token t routes to expert e
+  auto build_bits = [&](int ch) {
+    for (int i = tid; i < E * W; i += kThreads) bits[i] = 0u;
+    __syncthreads();
+    const int f1 = min(n, (ch + 1) * kScanChunkT * k);
+    for (int f = ch * kScanChunkT * k + tid; f < f1; f += kThreads) {
+      const int e = (int)co_ld32(rids, (uint32_t)f * 4u);
+      const int tl = f / k - ch * kScanChunkT;
+      atomicOr(&bits[e * W + (tl >> 5)], 1u << (tl & 31));
     }
-    cnt[e] = run;
+    __syncthreads();
+  };
+  if (nch == 1) {  // one chunk: the counts come from its bitmap
+    build_bits(0);
+    for (int e = tid; e < E; e += kThreads) {
+      int run = 0;
+      for (int w = 0; w < W; ++w) run += __popc(bits[e * W + w]);
+      cnt[e] = run;
+    }
+  } else {
+    for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
+    __syncthreads();
+    for (int f = tid; f < n; f += kThreads) atomicAdd(&cnt[co_ld32(rids, (uint32_t)f * 4u)], 1);
   }
   __syncthreads();
   const int my = tid < E ? cnt[tid] : 0;
@@ -474,15 +487,28 @@ __device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   }
   __syncthreads();
   const rsrc_t rs = r_slot(p), rp = r_perm(p), rrt = r_rowrt(p);
-  for (int f = tid; f < n; f += kThreads) {
-    const int e = (int)co_ld32(rids, (uint32_t)f * 4u);
-    const int t = f / k;
-    const int w = t >> 5, b = t & 31;
-    const int s = iptr[e] + pre[e * W + w] + __popc(bits[e * W + w] & ((1u << b) - 1u));
-    co_st32(rs, (uint32_t)f * 4u, (uint32_t)s);
-    co_st32(rp, (uint32_t)s * 4u, (uint32_t)f);
-    const int mt = (s - iptr[e]) / kBM, tf = tfirst[e];  // the row's tile, numbered as below
-    co_st32(rrt, (uint32_t)s * 4u, (uint32_t)(mt < (tf >> 16) ? (tf & 0xffff) + mt : ttail[e]));
+  int run = 0;  // thread e: rows of expert e in earlier chunks
+  for (int ch = 0; ch < nch; ++ch) {
+    if (nch > 1) build_bits(ch);
+    for (int e = tid; e < E; e += kThreads) {
+      for (int w = 0; w < W; ++w) {
+        pre[e * W + w] = run;
+        run += __popc(bits[e * W + w]);
+      }
+    }
+    __syncthreads();
+    const int f1 = min(n, (ch + 1) * kScanChunkT * k);
+    for (int f = ch * kScanChunkT * k + tid; f < f1; f += kThreads) {
+      const int e = (int)co_ld32(rids, (uint32_t)f * 4u);
+      const int tl = f / k - ch * kScanChunkT;
+      const int w = tl >> 5, b = tl & 31;
+      const int s = iptr[e] + pre[e * W + w] + __popc(bits[e * W + w] & ((1u << b) - 1u));
+      co_st32(rs, (uint32_t)f * 4u, (uint32_t)s);
+      co_st32(rp, (uint32_t)s * 4u, (uint32_t)f);
+      const int mt = (s - iptr[e]) / kBM, tf = tfirst[e];  // the row's tile, numbered as below
+      co_st32(rrt, (uint32_t)s * 4u, (uint32_t)(mt < (tf >> 16) ? (tf & 0xffff) + mt : ttail[e]));
+    }
+    __syncthreads();  // the chunk's bitmap and prefixes are read before the next chunk rebuilds them
   }
   const rsrc_t rr = r_rtinfo(p);
   if (tid < E) {

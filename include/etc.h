@@ -131,7 +131,8 @@ int etc_splitk_launch(etc_etensor* ev, int32_t n, int32_t nsplit, int32_t bk, co
  * y = (silu(x Wg^T) * (x Wu^T)) Wd^T with Wg = w13[e, 0:I, :],
  * Wu = w13[e, I:2I, :], Wd = w2[e].  Output: sum_j topk_w[t, j] * y_j.
  * Limits: H and I multiples of 128 and <= 16384; 1 <= E <= 256;
- * 1 <= k <= min(E, 16); 1 <= T_max <= 4096 and E * ceil(T_max/32) <= 8192. */
+ * 1 <= k <= min(E, 16); 1 <= T_max <= 16384 and T_max * k * max(H, I) * 2
+ * bytes below 2 GiB.                                                        */
 typedef struct {
   int32_t T_max;     /* largest token count any launch will use            */
   int32_t H;         /* hidden size                                        */

@@ -226,7 +226,9 @@ EDGE = [
     (3, 128, 1, 1, 128, True, False, 4),       # one expert: dense MLP
     (64, 384, 256, 16, 128, False, False, 64), # E = 256, k = 16, plain softmax weights
     (2, 640, 64, 6, 384, True, False, 2),      # most experts get no token
-    (4096, 128, 64, 8, 128, True, False, 4096),  # largest T: T == T_max == 4096, E * ceil(T_max/32) == 8192
+    (4096, 128, 64, 8, 128, True, False, 4096),  # T == T_max == 4096: eight scan chunks
+    (700, 128, 16, 4, 128, True, True, 800),   # two scan chunks, the second ragged
+    (16384, 128, 8, 2, 128, True, False, 16384),  # largest T_max: 32 scan chunks, 8 experts
     (8, 16384, 8, 2, 128, True, False, 8),     # largest hidden size
     (8, 128, 8, 2, 16384, True, False, 8),     # largest expert intermediate size
 ]
