@@ -34,6 +34,10 @@ constexpr int kMaxTmax = 16384;
 constexpr int kMaxHI = 16384;
 constexpr int kScanChunkT = 512;       // S: tokens per bitmap pass
 constexpr int kScanW = kScanChunkT / 32;  // S: bitmap words per expert and pass
+// Small batches (T <= kScanChunkT and T*k <= kLocalRows): every persistent
+// workgroup rebuilds the routing tables in its own LDS
+constexpr int kLocalRows = 1024;
+constexpr int kLocalTiles = kLocalRows / 64 + 256 + 16;
 // watchdog of one in-kernel wait, in microseconds of wall time; a healthy
 // wait lasts microseconds
 constexpr uint32_t kDefaultWatchdogUs = 2000000u;
@@ -123,7 +127,7 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
 // partial sums.  Independent of T_max (the scan walks the tokens in chunks).
 inline int64_t scan_lds_bytes(int E, int T_max) {
   (void)T_max;
-  return (int64_t)E * kScanW * 4 * 2 + 4 * 260 * 4 + 64;
+  return (int64_t)E * kScanW * 4 * 2 + 4 * 260 * 4 + 128;
 }
 // G2: cross-wave reduction buffer (4 waves x 4 blocks x 256 fp32) plus the
 // bf16 staging of the kBM x 64 output tile

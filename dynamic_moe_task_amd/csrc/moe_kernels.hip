@@ -101,6 +101,25 @@ __device__ __forceinline__ RowTile load_rowtile(const MoeParams& p, int rt) {
   return r;
 }
 
+// Routing tables of a small batch, rebuilt by every persistent workgroup in
+// its own LDS once all top-k tasks are done (see run_lists): G1 then starts
+// without waiting for S, and the G runners read tile descriptors and the
+// permutation from LDS instead of memory.
+struct LocalRoute {
+  uint32_t tile[kLocalTiles];  // expert | rows << 9 | first grouped row << 16
+  uint16_t perm[kLocalRows];   // grouped row -> flat pair index t * k + j
+  uint16_t cnt[kMaxE];         // rows per expert
+};
+__device__ __forceinline__ RowTile get_tile(const MoeParams& p, const LocalRoute* lr, int rt) {
+  if (!lr) return load_rowtile(p, rt);
+  const uint32_t v = lr->tile[rt];
+  RowTile r;
+  r.e = (int)(v & 511u);
+  r.nrows = (int)((v >> 9) & 127u);
+  r.r0 = (int)(v >> 16);
+  return r;
+}
+
 // Per-launch sizes, all derived from T (the symbolic batch dimension).
 struct Ctx {
   uint32_t* set;     // counter set of this launch (NULL for kernel-by-kernel)
@@ -381,27 +400,40 @@ __device__ void task_topk(const MoeParams& p, const Ctx& c, int tt) {
   }
 }
 
-// Block-wide exclusive scan of one int per thread (256 threads).
-__device__ int block_excl_scan(int v, int* tmp, int* total) {
+// N exclusive scans at once over the workgroup (one pair of barriers for
+// all of them); tmp holds 4 * N ints.
+template <int N>
+__device__ void block_excl_scan_n(const int (&v)[N], int (&ex)[N], int (&total)[N], int* tmp) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int incl = v;
+  int incl[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) incl[q] = v[q];
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) {
-    const int o = __shfl_up(incl, s);
-    if (lane >= s) incl += o;
-  }
-  if (lane == 63) tmp[wv] = incl;
-  __syncthreads();
-  int off = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int x = tmp[i];
-    if (i < wv) off += x;
-    tot += x;
+    for (int q = 0; q < N; ++q) {
+      const int o = __shfl_up(incl[q], s);
+      if (lane >= s) incl[q] += o;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) tmp[wv * N + q] = incl[q];
   }
   __syncthreads();
-  *total = tot;
-  return off + incl - v;
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int x = tmp[i * N + q];
+      if (i < wv) off += x;
+      tot += x;
+    }
+    ex[q] = off + incl[q] - v[q];
+    total[q] = tot;
+  }
+  __syncthreads();
 }
 
 // S: counts, exp_indptr (exclusive prefix sum of counts, ends at T*k), the
@@ -417,7 +449,11 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
 // lists deal G1 and G2 tasks in tile order, so the longest tasks start first
 // and the short ones fill in at the end (longest processing time first).
 // Returns the number of row tiles (uniform over the workgroup).
-__device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
+//
+// LOCAL: the same computation for a small batch (one chunk) into `lr`, in
+// the workgroup's own LDS, with no memory written.
+template <bool LOCAL = false>
+__device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem, LocalRoute* lr = nullptr) {
   const int tid = threadIdx.x;
   const int E = c.E, k = c.k, n = c.T * c.k;
   const int nch = (c.T + kScanChunkT - 1) / kScanChunkT;
@@ -426,8 +462,8 @@ __device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   int* pre = reinterpret_cast<int*>(smem + E * kScanW * 4);
   int* cnt = pre + E * kScanW;
   int* iptr = cnt + 260;
-  int* tmp = iptr + 260;         // 16 words for block_excl_scan
-  int* tfirst = tmp + 16;        // per expert: first four-block tile | (number of them << 16)
+  int* tmp = iptr + 260;         // 32 words for the block scans
+  int* tfirst = tmp + 32;        // per expert: first four-block tile | (number of them << 16)
   int* ttail = tfirst + 260;     // per expert: the tile of its last rows when that tile is smaller
   const rsrc_t rids = r_ids(p);
   // the bitmap of chunk `ch`: bit t - ch * kScanChunkT of word row e is set
@@ -461,29 +497,34 @@ __device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
   const int rem = my % kBM;
   const int n4 = my / kBM + (rem > 32 ? 1 : 0), n2 = (rem > 16 && rem <= 32) ? 1 : 0,
             n1 = (rem > 0 && rem <= 16) ? 1 : 0;
-  int tot_rows = 0, tot_tiles = 0, tot4 = 0, tot2 = 0, tot1 = 0;
-  const int ex = block_excl_scan(my, tmp, &tot_rows);
-  (void)block_excl_scan(mytiles, tmp, &tot_tiles);
-  const int ex4 = block_excl_scan(n4, tmp, &tot4);
-  const int ex2 = block_excl_scan(n2, tmp, &tot2);
-  const int ex1 = block_excl_scan(n1, tmp, &tot1);
+  const int sv[5] = {my, mytiles, n4, n2, n1};
+  int sx[5], st[5];
+  block_excl_scan_n<5>(sv, sx, st, tmp);
+  const int ex = sx[0], ex4 = sx[2], ex2 = sx[3], ex1 = sx[4];
+  const int tot_rows = st[0], tot_tiles = st[1], tot4 = st[2], tot2 = st[3];
   const rsrc_t rc = r_counts(p), ri = r_indptr(p);
   if (tid < E) {
     iptr[tid] = ex;
     tfirst[tid] = ex4 | (n4 << 16);
     ttail[tid] = rem > 32 ? -1 : (rem > 16 ? tot4 + ex2 : tot4 + tot2 + ex1);
-    co_st32(rc, (uint32_t)tid * 4u, (uint32_t)my);
-    co_st32(ri, (uint32_t)tid * 4u, (uint32_t)ex);
+    if (LOCAL) {
+      lr->cnt[tid] = (uint16_t)my;
+    } else {
+      co_st32(rc, (uint32_t)tid * 4u, (uint32_t)my);
+      co_st32(ri, (uint32_t)tid * 4u, (uint32_t)ex);
+    }
   }
-  if (tid < E && c.set && p.debug) {
+  if (!LOCAL && tid < E && c.set && p.debug) {
     // every routed pair has notified by now (S runs after all of K): the
     // expert event holds exactly counts[e] arrivals and fires once
     if (my > 0 && ld_relaxed(ev_exp(p, c, tid)) == (uint32_t)my) atomicAdd(p.debug + E + tid, 1);
   }
   if (tid == 0) {
     iptr[E] = tot_rows;
-    co_st32(ri, (uint32_t)E * 4u, (uint32_t)tot_rows);
-    st_relaxed(p.meta + M_NRT, (uint32_t)tot_tiles);
+    if (!LOCAL) {
+      co_st32(ri, (uint32_t)E * 4u, (uint32_t)tot_rows);
+      st_relaxed(p.meta + M_NRT, (uint32_t)tot_tiles);
+    }
   }
   __syncthreads();
   const rsrc_t rs = r_slot(p), rp = r_perm(p), rrt = r_rowrt(p);
@@ -503,6 +544,10 @@ __device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
       const int tl = f / k - ch * kScanChunkT;
       const int w = tl >> 5, b = tl & 31;
       const int s = iptr[e] + pre[e * W + w] + __popc(bits[e * W + w] & ((1u << b) - 1u));
+      if (LOCAL) {
+        lr->perm[s] = (uint16_t)f;
+        continue;
+      }
       co_st32(rs, (uint32_t)f * 4u, (uint32_t)s);
       co_st32(rp, (uint32_t)s * 4u, (uint32_t)f);
       const int mt = (s - iptr[e]) / kBM, tf = tfirst[e];  // the row's tile, numbered as below
@@ -515,6 +560,10 @@ __device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
     for (int mt = 0; mt * kBM < my; ++mt) {
       const int rows = min(kBM, my - mt * kBM);
       const int rt = rows > 32 ? ex4 + mt : (rows > 16 ? tot4 + ex2 : tot4 + tot2 + ex1);
+      if (LOCAL) {
+        lr->tile[rt] = (uint32_t)tid | ((uint32_t)rows << 9) | ((uint32_t)(ex + mt * kBM) << 16);
+        continue;
+      }
       u32x4_t q;
       q.x = (uint32_t)tid;
       q.y = (uint32_t)(ex + mt * kBM);
@@ -523,6 +572,7 @@ __device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem) {
       co_st128(rr, (uint32_t)rt * 16u, q);
     }
   }
+  if (LOCAL) __syncthreads();  // the tables are read by every thread next
   return tot_tiles;
 }
 
@@ -544,9 +594,11 @@ __device__ __forceinline__ int row_blocks(int nrows) { return nrows <= 16 ? 1 : 
 // during a launch, so ordinary cached loads serve.  `tok` holds, per lane,
 // the token of row 16 b + (lane % 16) of each row block when the caller has
 // loaded them ahead; otherwise they are loaded here.
-__device__ __forceinline__ uint32_t row_perm(const MoeParams& p, const RowTile tile, int b) {
+__device__ __forceinline__ uint32_t row_perm(const MoeParams& p, const RowTile tile, int b,
+                                             const LocalRoute* lr = nullptr) {
   const int r = b * 16 + (threadIdx.x & 15);
-  return r < tile.nrows ? co_ld32(r_perm(p), (uint32_t)(tile.r0 + r) * 4u) : 0u;
+  if (r >= tile.nrows) return 0u;
+  return lr ? (uint32_t)lr->perm[tile.r0 + r] : co_ld32(r_perm(p), (uint32_t)(tile.r0 + r) * 4u);
 }
 template <int NB, int U>
 __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const RowTile tile, int nt, float* red,
@@ -981,23 +1033,24 @@ __device__ bool wait_rows_done(const MoeParams& p, const Ctx& c, int ct) {
   return fail == 0;
 }
 
-__device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G) {
+__device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G,
+                              const LocalRoute* lr) {
   if (i0 >= n) return;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
   const rsrc_t rcnt = r_counts(p);
-  RowTile cur = load_rowtile(p, i0 / c.nN1);
+  RowTile cur = get_tile(p, lr, i0 / c.nN1);
   RowTile nxt = cur;
-  if (i0 + G < n) nxt = load_rowtile(p, (i0 + G) / c.nN1);
+  if (i0 + G < n) nxt = get_tile(p, lr, (i0 + G) / c.nN1);
   uint32_t cur_tgt = 0, cur_arr = 0;
   if (threadIdx.x == 0) {
-    cur_tgt = co_ld32(rcnt, (uint32_t)cur.e * 4u);
+    cur_tgt = (lr ? (uint32_t)lr->cnt[cur.e] : co_ld32(rcnt, (uint32_t)cur.e * 4u));
     cur_arr = ld_relaxed(ev_exp(p, c, cur.e));
   }
   // grouped-row permutation entries of the tile's rows (A gather), one task ahead
   uint32_t cur_f[4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) cur_f[b] = row_perm(p, cur, b);
+  for (int b = 0; b < 4; ++b) cur_f[b] = row_perm(p, cur, b, lr);
   // Enter the loop with nothing in flight: otherwise the compiler, merging
   // the entry path (prefetch loads pending) with the back edge (only the
   // notify pending), waits for all memory operations at the top of every
@@ -1009,15 +1062,15 @@ __device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int 
     if (!wait_known(ev_exp(p, c, cur.e), cur_tgt, cur_arr, c)) return;
     if (tr) ts = now_ticks();
     RowTile nn = nxt;
-    if (i + 2 * G < n) nn = load_rowtile(p, (i + 2 * G) / c.nN1);
+    if (i + 2 * G < n) nn = get_tile(p, lr, (i + 2 * G) / c.nN1);
     uint32_t nxt_tgt = 0, nxt_arr = 0;
     if (threadIdx.x == 0 && i + G < n) {
-      nxt_tgt = co_ld32(rcnt, (uint32_t)nxt.e * 4u);
+      nxt_tgt = (lr ? (uint32_t)lr->cnt[nxt.e] : co_ld32(rcnt, (uint32_t)nxt.e * 4u));
       nxt_arr = ld_relaxed(ev_exp(p, c, nxt.e));
     }
     uint32_t nxt_f[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) nxt_f[b] = i + G < n ? row_perm(p, nxt, b) : 0u;
+    for (int b = 0; b < 4; ++b) nxt_f[b] = i + G < n ? row_perm(p, nxt, b, lr) : 0u;
     task_g1(p, c, cur, rt, nt, red, cur_f);
     // wave 0 wrote the tile: drain its stores, then notify.  The drain is
     // outside the notify branch so that, after the branch, only the notify
@@ -1036,14 +1089,15 @@ __device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int 
   }
 }
 
-__device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G) {
+__device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G,
+                              const LocalRoute* lr) {
   if (i0 >= n) return;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
   const uint32_t tgt = (uint32_t)c.nN1;
-  RowTile cur = load_rowtile(p, i0 / c.nN2);
+  RowTile cur = get_tile(p, lr, i0 / c.nN2);
   RowTile nxt = cur;
-  if (i0 + G < n) nxt = load_rowtile(p, (i0 + G) / c.nN2);
+  if (i0 + G < n) nxt = get_tile(p, lr, (i0 + G) / c.nN2);
   uint32_t cur_arr = 0;
   if (threadIdx.x == 0) cur_arr = ld_relaxed(ev_h(p, c, i0 / c.nN2));
   __builtin_amdgcn_s_waitcnt(0);  // loop entry with nothing in flight (see run_g1_static)
@@ -1053,7 +1107,7 @@ __device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int 
     if (!wait_known(ev_h(p, c, rt), tgt, cur_arr, c)) return;
     if (tr) ts = now_ticks();
     RowTile nn = nxt;
-    if (i + 2 * G < n) nn = load_rowtile(p, (i + 2 * G) / c.nN2);
+    if (i + 2 * G < n) nn = get_tile(p, lr, (i + 2 * G) / c.nN2);
     uint32_t nxt_arr = 0;
     if (threadIdx.x == 0 && i + G < n) nxt_arr = ld_relaxed(ev_h(p, c, (i + G) / c.nN2));
     // combine tile of each row's token (wave 0, one row a lane)
@@ -1095,7 +1149,7 @@ __device__ __forceinline__ int claimed_task(const ClaimQ& q, uint32_t k) {
 
 // returns false when a wait gave up (the launch is aborting)
 __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q, const ClaimQ& q2,
-                               uint32_t* sk) {
+                               uint32_t* sk, const LocalRoute* lr) {
   const int n = q.n;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
@@ -1105,17 +1159,17 @@ __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, con
   uint32_t g2k0 = 0, g2k1 = 0, g2k2 = 0;  // thread 0: first G2 claims, taken during the last G1 tile
   bool g2_taken = false;
   if (cur < n) {
-    RowTile rc = load_rowtile(p, cur / c.nN1);
+    RowTile rc = get_tile(p, lr, cur / c.nN1);
     RowTile rn = rc;
-    if (nxt < n) rn = load_rowtile(p, nxt / c.nN1);
+    if (nxt < n) rn = get_tile(p, lr, nxt / c.nN1);
     uint32_t cur_tgt = 0, cur_arr = 0;
     if (threadIdx.x == 0) {
-      cur_tgt = co_ld32(rcnt, (uint32_t)rc.e * 4u);
+      cur_tgt = (lr ? (uint32_t)lr->cnt[rc.e] : co_ld32(rcnt, (uint32_t)rc.e * 4u));
       cur_arr = ld_relaxed(ev_exp(p, c, rc.e));
     }
     uint32_t cur_f[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) cur_f[b] = row_perm(p, rc, b);
+    for (int b = 0; b < 4; ++b) cur_f[b] = row_perm(p, rc, b, lr);
     __builtin_amdgcn_s_waitcnt(0);  // loop entry with nothing in flight (see run_g1_static)
     int par = 2;  // claim slot that holds the ordinal after nxt
     for (;;) {
@@ -1136,15 +1190,15 @@ __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, con
         }
       }
       RowTile ra = rn;
-      if (aft < n) ra = load_rowtile(p, aft / c.nN1);
+      if (aft < n) ra = get_tile(p, lr, aft / c.nN1);
       uint32_t nxt_tgt = 0, nxt_arr = 0;
       if (threadIdx.x == 0 && nxt < n) {
-        nxt_tgt = co_ld32(rcnt, (uint32_t)rn.e * 4u);
+        nxt_tgt = (lr ? (uint32_t)lr->cnt[rn.e] : co_ld32(rcnt, (uint32_t)rn.e * 4u));
         nxt_arr = ld_relaxed(ev_exp(p, c, rn.e));
       }
       uint32_t nxt_f[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) nxt_f[b] = nxt < n ? row_perm(p, rn, b) : 0u;
+      for (int b = 0; b < 4; ++b) nxt_f[b] = nxt < n ? row_perm(p, rn, b, lr) : 0u;
       task_g1(p, c, rc, rt, nt, red, cur_f);
       __builtin_amdgcn_s_waitcnt(0);  // drain, then notify (see run_g1_static)
       if (threadIdx.x == 0) {
@@ -1181,7 +1235,8 @@ __device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, con
 }
 
 // G2 tiles from the claims that run_g1_ordered left in sk[0..2]
-__device__ bool run_g2_ordered(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q, uint32_t* sk) {
+__device__ bool run_g2_ordered(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q, uint32_t* sk,
+                               const LocalRoute* lr) {
   const int n = q.n;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
@@ -1189,9 +1244,9 @@ __device__ bool run_g2_ordered(const MoeParams& p, const Ctx& c, float* red, con
   __syncthreads();
   int cur = claimed_task(q, sk[0]), nxt = claimed_task(q, sk[1]);
   if (cur >= n) return true;
-  RowTile rc = load_rowtile(p, cur / c.nN2);
+  RowTile rc = get_tile(p, lr, cur / c.nN2);
   RowTile rn = rc;
-  if (nxt < n) rn = load_rowtile(p, nxt / c.nN2);
+  if (nxt < n) rn = get_tile(p, lr, nxt / c.nN2);
   uint32_t cur_arr = 0;
   if (threadIdx.x == 0) cur_arr = ld_relaxed(ev_h(p, c, cur / c.nN2));
   __builtin_amdgcn_s_waitcnt(0);  // loop entry with nothing in flight (see run_g1_static)
@@ -1205,7 +1260,7 @@ __device__ bool run_g2_ordered(const MoeParams& p, const Ctx& c, float* red, con
     uint32_t knew = 0xffffffffu;
     if (threadIdx.x == 0 && aft < n) knew = add_relaxed(q.ctr, 1u);
     RowTile ra = rn;
-    if (aft < n) ra = load_rowtile(p, aft / c.nN2);
+    if (aft < n) ra = get_tile(p, lr, aft / c.nN2);
     uint32_t nxt_arr = 0;
     if (threadIdx.x == 0 && nxt < n) nxt_arr = ld_relaxed(ev_h(p, c, nxt / c.nN2));
     task_g2(p, c, rc, rt, nt, red);
@@ -1285,7 +1340,17 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
     sh.claim[2] = add_relaxed(ctr, 1u);
   }
   int nrt;
-  if (EV) {
+  // Small batch: each workgroup rebuilds the routing tables in its own LDS
+  // as soon as every top-k task is done, so G1 does not wait for S (S still
+  // writes the routing outputs, which C reads).
+  const bool local = EV && c.T <= kScanChunkT && c.T * c.k <= kLocalRows;
+  __shared__ LocalRoute lroute;
+  const LocalRoute* lr = nullptr;
+  if (local) {
+    if (!wg_wait(c.set + W_EV_ROUTE, (uint32_t)c.nK, c.status, c.budget)) return;
+    nrt = task_scan<true>(p, c, smem, &lroute);
+    lr = &lroute;
+  } else if (EV) {
     if (threadIdx.x == 0) {
       uint32_t v = 0;
       sh.claim[3] = spin_value_geq(c.set + W_EV_SCAN, 1u, c.status, c.budget, &v) ? v : 0u;
@@ -1308,12 +1373,12 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
   if (MODE == MODE_ORDERED) {
     const ClaimQ q1{c.set + W_CLAIM_G1 + grp * 32, grp, ngrp, nG1};
     const ClaimQ q2{c.set + W_CLAIM_G2 + grp * 32, grp, ngrp, nG2};
-    if (!run_g1_ordered(p, c, red, q1, q2, sh.claim)) return;
-    if (!run_g2_ordered(p, c, red, q2, sh.claim)) return;
+    if (!run_g1_ordered(p, c, red, q1, q2, sh.claim, lr)) return;
+    if (!run_g2_ordered(p, c, red, q2, sh.claim, lr)) return;
     off += nG1 + nG2;
   } else {
   if (EV) {
-    run_g1_static(p, c, red, first_of(w, off, Gt), nG1, Gt);
+    run_g1_static(p, c, red, first_of(w, off, Gt), nG1, Gt, lr);
   } else {
     for (int i = first_of(w, off, Gt); i < nG1; i += Gt) {
       const int rt = i / c.nN1;
@@ -1327,7 +1392,7 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
   off += nG1;
   if (!EV && !grid_barrier(c, Gt)) return;
   if (EV) {
-    run_g2_static(p, c, red, first_of(w, off, Gt), nG2, Gt);
+    run_g2_static(p, c, red, first_of(w, off, Gt), nG2, Gt, lr);
   } else {
     for (int i = first_of(w, off, Gt); i < nG2; i += Gt) {
       const int rt = i / c.nN2;
@@ -1341,6 +1406,8 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
   off += nG2;
   if (!EV && !grid_barrier(c, Gt)) return;
   }
+  // C reads S's routing outputs (slot, row -> tile map)
+  if (local && first_of(w, off, Gt) < c.nC && !wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;
   for (int i = first_of(w, off, Gt); i < c.nC; i += Gt) {
     if (tr) tw = now_ticks();
     if (EV && !wait_rows_done(p, c, i)) return;
