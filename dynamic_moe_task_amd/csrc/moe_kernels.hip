@@ -798,12 +798,12 @@ __device__ void task_g2(const MoeParams& p, const Ctx& c, const RowTile tile, in
 // C: out[t, :] = bf16(sum_j w[t, j] * Y[slot[t*k+j], :]), fp32 in j order.
 // The task's (weight, slot) pairs are staged in LDS first; then each thread
 // issues the loads of all k expert rows of its chunk before the arithmetic.
-__device__ void task_combine(const MoeParams& p, const Ctx& c, int ct, int* s_pair) {
+__device__ void task_combine(const MoeParams& p, const Ctx& c, int ct, int* s_pair, bool staged = false) {
   const int t0 = ct * kCombineT;
   const int ntok = min(kCombineT, c.T - t0);
   const int cpr = c.H >> 3;
   const int k = c.k;
-  if (threadIdx.x < ntok * k) {
+  if (!staged && threadIdx.x < ntok * k) {
     const uint32_t fo = (uint32_t)(t0 * k + threadIdx.x) * 4u;
     s_pair[2 * threadIdx.x] = (int)co_ld32(r_topw(p), fo);
     s_pair[2 * threadIdx.x + 1] = (int)co_ld32(r_slot(p), fo);
@@ -998,14 +998,19 @@ __device__ bool wait_known(const uint32_t* ctr, uint32_t target, uint32_t known,
 // C(ct) may run once every row tile holding one of its tokens' k rows has
 // finished all of its G2 column tiles: wave 0 polls those ev_y elements, one
 // row a lane (at most kCombineT * k <= 32 rows), under the watchdog.
-__device__ bool wait_rows_done(const MoeParams& p, const Ctx& c, int ct) {
+// It also stages the task's (weight, slot) pairs in `s_pair` for task_combine,
+// so that the combine, on the critical path's tail, starts with its Y loads.
+__device__ bool wait_rows_done(const MoeParams& p, const Ctx& c, int ct, int* s_pair) {
   int fail = 0;
   if (threadIdx.x < 64) {
     const int t0 = ct * kCombineT, nrow = min(kCombineT, c.T - t0) * c.k;
     const bool mine = (int)threadIdx.x < nrow;
     uint32_t* ctr = ev_y(p, c, 0);
     if (mine) {
-      const uint32_t s = co_ld32(r_slot(p), (uint32_t)(t0 * c.k + (int)threadIdx.x) * 4u);
+      const uint32_t fo = (uint32_t)(t0 * c.k + (int)threadIdx.x) * 4u;
+      const uint32_t s = co_ld32(r_slot(p), fo);
+      s_pair[2 * threadIdx.x] = (int)co_ld32(r_topw(p), fo);
+      s_pair[2 * threadIdx.x + 1] = (int)s;
       const uint32_t rt = co_ld32(r_rowrt(p), s * 4u);
       ctr = ev_y(p, c, (int)rt);
       if (p.debug) {  // count the rows whose mapped tile really holds them
@@ -1410,9 +1415,9 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
   if (local && first_of(w, off, Gt) < c.nC && !wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;
   for (int i = first_of(w, off, Gt); i < c.nC; i += Gt) {
     if (tr) tw = now_ticks();
-    if (EV && !wait_rows_done(p, c, i)) return;
+    if (EV && !wait_rows_done(p, c, i, sh.pairs)) return;
     if (tr) ts = now_ticks();
-    task_combine(p, c, i, sh.pairs);
+    task_combine(p, c, i, sh.pairs, EV);
     if (tr) tb = now_ticks();
     dbg_task(p, TT_C);
     trace_task(p, TT_C, i, 0, tw, ts, tb);
