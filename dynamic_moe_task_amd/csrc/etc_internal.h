@@ -59,9 +59,8 @@ enum : int {
   W_BAR_GEN = 192,
   W_EV_ROUTE = 224,
   W_EV_SCAN = 256,
-  W_CLAIM_G1 = 288,  // ORDERED: 8 claim counters for G1 tiles, 32 words apart
-  W_CLAIM_G2 = 544,  // ORDERED: the same for G2 tiles
-  W_FIXED = 800,     // start of the variable-size event tensors
+  W_CLAIM_G1 = 288,  // ORDERED: 8 claim counters for the G tiles, 32 words apart
+  W_FIXED = 544,     // start of the variable-size event tensors
 };
 // split-K example: control words (u32) of its library-owned block, each on
 // its own 128-byte line, followed by the queue

@@ -1128,21 +1128,24 @@ __device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int 
   }
 }
 
-// ORDERED: the G1 tiles and then the G2 tiles are claimed in index order
-// from one counter per group of workgroups (group = workgroup index mod 8;
-// the dispatcher deals consecutive workgroups over the 8 XCDs, so a group is
-// one XCD's workgroups).  Ordinal k of group g is tile k * ngrp + g.  A
-// workgroup that streams faster (the first of the two on a CU, a CU whose
-// tiles are cheaper) claims more tiles, so both phases end together, while
+// ORDERED: the G tiles are claimed in index order, all G1 tiles before any
+// G2 tile, from one counter per group of workgroups (group = workgroup index
+// mod 8; the dispatcher deals consecutive workgroups over the 8 XCDs, so a
+// group is one XCD's workgroups).  Ordinal k of group g is tile k * ngrp + g.
+// A workgroup that streams faster (the first of the two on a CU, a CU whose
+// tiles are cheaper) claims more tiles, so the phases end together, while
 // every tile still waits on its event as in STATIC.  Deadlock freedom: G1
 // waits only on K, which is complete before S, so every claimed G1 tile
-// completes and every G2 wait is met; C waits only on G2.  Claims from one
-// thread to one counter are ordered (same-location coherence), so a
-// workgroup's ordinals increase and the first one past the end ends its
-// stream.  A pipeline fill is three separate claims, so that with few tiles
-// the first claims of all workgroups interleave and spread the tiles.  The runners keep three ordinals ahead of the running tile: the
-// claim round trip, the next row-tile descriptor and the next event state
-// arrive while earlier tiles stream, as in the STATIC runners.
+// completes; a workgroup holds a G2 ordinal only once its group has handed
+// out all of its G1 tiles, so every G1 tile is claimed and every G2 wait is
+// met; C waits only on G2.  Claims from one thread to one counter are
+// ordered (same-location coherence), so a workgroup's ordinals increase and
+// the first one past the end ends its stream.  The first three claims are
+// separate claims, so that with few tiles the first claims of all
+// workgroups interleave and spread the tiles.  The runner keeps three
+// ordinals ahead of the running tile: the claim round trip, the next
+// row-tile descriptor and the next event state arrive while earlier tiles
+// stream, as in the STATIC runners.
 struct ClaimQ {
   uint32_t* ctr;
   int grp, ngrp, n;
@@ -1152,136 +1155,107 @@ __device__ __forceinline__ int claimed_task(const ClaimQ& q, uint32_t k) {
   return i < q.n ? (int)i : q.n;
 }
 
-// returns false when a wait gave up (the launch is aborting)
-__device__ bool run_g1_ordered(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q, const ClaimQ& q2,
-                               uint32_t* sk, const LocalRoute* lr) {
+// The G tiles of one stream: index i < nG1 is G1 tile (i / nN1, i % nN1),
+// otherwise G2 tile j = i - nG1 is (j / nN2, j % nN2).
+struct GTask {
+  int g2, rt, nt;
+};
+__device__ __forceinline__ GTask gtask(const Ctx& c, int i, int nG1) {
+  GTask t;
+  t.g2 = i >= nG1;
+  const int j = t.g2 ? i - nG1 : i, nn = t.g2 ? c.nN2 : c.nN1;
+  t.rt = j / nn;
+  t.nt = j % nn;
+  return t;
+}
+
+// ORDERED: one claim stream per group over the G1 tiles and then the G2
+// tiles, so the pipeline runs on across the G1 -> G2 boundary.  The event a
+// tile waits on is ev_exp[e] (target counts[e]) for G1 and ev_h[rt] (target
+// I/16) for G2; its state is fetched one tile ahead, the row-tile descriptor
+// two ahead and the claim three ahead.  Returns false when a wait gave up
+// (the launch is aborting).
+__device__ bool run_g_ordered(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q, int nG1, uint32_t* sk,
+                              const LocalRoute* lr) {
   const int n = q.n;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
   const rsrc_t rcnt = r_counts(p);
   // sk[0..2] hold the first three claims, taken by the caller before S ended
   int cur = claimed_task(q, sk[0]), nxt = claimed_task(q, sk[1]);
-  uint32_t g2k0 = 0, g2k1 = 0, g2k2 = 0;  // thread 0: first G2 claims, taken during the last G1 tile
-  bool g2_taken = false;
-  if (cur < n) {
-    RowTile rc = get_tile(p, lr, cur / c.nN1);
-    RowTile rn = rc;
-    if (nxt < n) rn = get_tile(p, lr, nxt / c.nN1);
-    uint32_t cur_tgt = 0, cur_arr = 0;
-    if (threadIdx.x == 0) {
-      cur_tgt = (lr ? (uint32_t)lr->cnt[rc.e] : co_ld32(rcnt, (uint32_t)rc.e * 4u));
-      cur_arr = ld_relaxed(ev_exp(p, c, rc.e));
-    }
-    uint32_t cur_f[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) cur_f[b] = row_perm(p, rc, b, lr);
-    __builtin_amdgcn_s_waitcnt(0);  // loop entry with nothing in flight (see run_g1_static)
-    int par = 2;  // claim slot that holds the ordinal after nxt
-    for (;;) {
-      const int rt = cur / c.nN1, nt = cur % c.nN1;
-      if (tr) tw = now_ticks();
-      if (!wait_known(ev_exp(p, c, rc.e), cur_tgt, cur_arr, c)) return false;
-      if (tr) ts = now_ticks();
-      const int aft = claimed_task(q, sk[par]);
-      uint32_t knew = 0xffffffffu;
-      if (threadIdx.x == 0) {
-        if (aft < n) {
-          knew = add_relaxed(q.ctr, 1u);
-        } else if (nxt >= n) {  // this is the last G1 tile: claim the first G2 tiles now
-          g2k0 = add_relaxed(q2.ctr, 1u);
-          g2k1 = add_relaxed(q2.ctr, 1u);
-          g2k2 = add_relaxed(q2.ctr, 1u);
-          g2_taken = true;
-        }
-      }
-      RowTile ra = rn;
-      if (aft < n) ra = get_tile(p, lr, aft / c.nN1);
-      uint32_t nxt_tgt = 0, nxt_arr = 0;
-      if (threadIdx.x == 0 && nxt < n) {
-        nxt_tgt = (lr ? (uint32_t)lr->cnt[rn.e] : co_ld32(rcnt, (uint32_t)rn.e * 4u));
-        nxt_arr = ld_relaxed(ev_exp(p, c, rn.e));
-      }
-      uint32_t nxt_f[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) nxt_f[b] = nxt < n ? row_perm(p, rn, b, lr) : 0u;
-      task_g1(p, c, rc, rt, nt, red, cur_f);
-      __builtin_amdgcn_s_waitcnt(0);  // drain, then notify (see run_g1_static)
-      if (threadIdx.x == 0) {
-        notify_fast(p, c, ev_h(p, c, rt), (uint32_t)c.nN1);
-        sk[par ^ 1] = knew;
-      }
-      if (tr) tb = now_ticks();
-      dbg_task(p, TT_G1);
-      trace_task(p, TT_G1, rt, nt, tw, ts, tb);
-      cur = nxt;
-      nxt = aft;
-      rc = rn;
-      rn = ra;
-      cur_tgt = nxt_tgt;
-      cur_arr = nxt_arr;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) cur_f[b] = nxt_f[b];
-      par ^= 1;
-      if (cur >= n) break;
-    }
-  }
-  __syncthreads();  // every thread has read its last claim slot
-  if (threadIdx.x == 0) {
-    if (!g2_taken) {
-      g2k0 = add_relaxed(q2.ctr, 1u);
-      g2k1 = add_relaxed(q2.ctr, 1u);
-      g2k2 = add_relaxed(q2.ctr, 1u);
-    }
-    sk[0] = g2k0;
-    sk[1] = g2k1;
-    sk[2] = g2k2;
-  }
-  return true;
-}
-
-// G2 tiles from the claims that run_g1_ordered left in sk[0..2]
-__device__ bool run_g2_ordered(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q, uint32_t* sk,
-                               const LocalRoute* lr) {
-  const int n = q.n;
-  const bool tr = p.trace != nullptr;
-  uint64_t tw = 0, ts = 0, tb = 0;
-  const uint32_t tgt = (uint32_t)c.nN1;
-  __syncthreads();
-  int cur = claimed_task(q, sk[0]), nxt = claimed_task(q, sk[1]);
   if (cur >= n) return true;
-  RowTile rc = get_tile(p, lr, cur / c.nN2);
+  // event element and target of a tile; thread 0 loads the arrival count
+  auto ev_of = [&](const GTask& t, const RowTile& r) -> uint32_t* {
+    return t.g2 ? ev_h(p, c, t.rt) : ev_exp(p, c, r.e);
+  };
+  auto tgt_of = [&](const GTask& t, const RowTile& r) -> uint32_t {
+    if (t.g2) return (uint32_t)c.nN1;
+    return lr ? (uint32_t)lr->cnt[r.e] : co_ld32(rcnt, (uint32_t)r.e * 4u);
+  };
+  GTask tc = gtask(c, cur, nG1), tn = tc;
+  RowTile rc = get_tile(p, lr, tc.rt);
   RowTile rn = rc;
-  if (nxt < n) rn = get_tile(p, lr, nxt / c.nN2);
-  uint32_t cur_arr = 0;
-  if (threadIdx.x == 0) cur_arr = ld_relaxed(ev_h(p, c, cur / c.nN2));
+  if (nxt < n) {
+    tn = gtask(c, nxt, nG1);
+    rn = get_tile(p, lr, tn.rt);
+  }
+  uint32_t cur_tgt = 0, cur_arr = 0;
+  if (threadIdx.x == 0) {
+    cur_tgt = tgt_of(tc, rc);
+    cur_arr = ld_relaxed(ev_of(tc, rc));
+  }
+  uint32_t cur_f[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) cur_f[b] = tc.g2 ? 0u : row_perm(p, rc, b, lr);
   __builtin_amdgcn_s_waitcnt(0);  // loop entry with nothing in flight (see run_g1_static)
-  int par = 2;
+  int par = 2;  // claim slot that holds the ordinal after nxt
   for (;;) {
-    const int rt = cur / c.nN2, nt = cur % c.nN2;
     if (tr) tw = now_ticks();
-    if (!wait_known(ev_h(p, c, rt), tgt, cur_arr, c)) return false;
+    if (!wait_known(ev_of(tc, rc), cur_tgt, cur_arr, c)) return false;
     if (tr) ts = now_ticks();
     const int aft = claimed_task(q, sk[par]);
     uint32_t knew = 0xffffffffu;
     if (threadIdx.x == 0 && aft < n) knew = add_relaxed(q.ctr, 1u);
+    GTask ta = tn;
     RowTile ra = rn;
-    if (aft < n) ra = get_tile(p, lr, aft / c.nN2);
-    uint32_t nxt_arr = 0;
-    if (threadIdx.x == 0 && nxt < n) nxt_arr = ld_relaxed(ev_h(p, c, nxt / c.nN2));
-    task_g2(p, c, rc, rt, nt, red);
-    __builtin_amdgcn_s_waitcnt(0);  // drain, then notify (see run_g1_static)
+    if (aft < n) {
+      ta = gtask(c, aft, nG1);
+      ra = get_tile(p, lr, ta.rt);
+    }
+    uint32_t nxt_tgt = 0, nxt_arr = 0;
+    if (threadIdx.x == 0 && nxt < n) {
+      nxt_tgt = tgt_of(tn, rn);
+      nxt_arr = ld_relaxed(ev_of(tn, rn));
+    }
+    uint32_t nxt_f[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) nxt_f[b] = (nxt < n && !tn.g2) ? row_perm(p, rn, b, lr) : 0u;
+    if (!tc.g2) {
+      task_g1(p, c, rc, tc.rt, tc.nt, red, cur_f);
+    } else {
+      task_g2(p, c, rc, tc.rt, tc.nt, red);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // wave 0 wrote the tile: drain, then notify (see run_g1_static)
     if (threadIdx.x == 0) {
-      notify_fast(p, c, ev_y(p, c, rt), (uint32_t)c.nN2);
+      if (!tc.g2)
+        notify_fast(p, c, ev_h(p, c, tc.rt), (uint32_t)c.nN1);
+      else
+        notify_fast(p, c, ev_y(p, c, tc.rt), (uint32_t)c.nN2);
       sk[par ^ 1] = knew;
     }
     if (tr) tb = now_ticks();
-    dbg_task(p, TT_G2);
-    trace_task(p, TT_G2, rt, nt, tw, ts, tb);
+    dbg_task(p, tc.g2 ? TT_G2 : TT_G1);
+    trace_task(p, tc.g2 ? TT_G2 : TT_G1, tc.rt, tc.nt, tw, ts, tb);
     cur = nxt;
     nxt = aft;
+    tc = tn;
+    tn = ta;
     rc = rn;
     rn = ra;
+    cur_tgt = nxt_tgt;
     cur_arr = nxt_arr;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) cur_f[b] = nxt_f[b];
     par ^= 1;
     if (cur >= n) break;
   }
@@ -1376,10 +1350,8 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
   const int Gt = (MODE != MODE_ORDERED && p.solo_wgs > 0 && nG1 <= 3 * p.solo_wgs) ? p.solo_wgs : G;
   if (w >= Gt) return;
   if (MODE == MODE_ORDERED) {
-    const ClaimQ q1{c.set + W_CLAIM_G1 + grp * 32, grp, ngrp, nG1};
-    const ClaimQ q2{c.set + W_CLAIM_G2 + grp * 32, grp, ngrp, nG2};
-    if (!run_g1_ordered(p, c, red, q1, q2, sh.claim, lr)) return;
-    if (!run_g2_ordered(p, c, red, q2, sh.claim, lr)) return;
+    const ClaimQ q{c.set + W_CLAIM_G1 + grp * 32, grp, ngrp, nG1 + nG2};
+    if (!run_g_ordered(p, c, red, q, nG1, sh.claim, lr)) return;
     off += nG1 + nG2;
   } else {
   if (EV) {

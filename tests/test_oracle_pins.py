@@ -502,13 +502,13 @@ def _moe_layer_graph(T, E, k, bm, n1, n2, seed):
 @pytest.mark.parametrize("workers", [5, 8, 16])
 @pytest.mark.parametrize("seed", range(3))
 def test_ordered_claims_complete_the_moe_graph(workers, seed):
-    # The ORDERED schedule: R, K, S dealt in phase order, then G1 and G2
-    # tiles claimed in index order from per-group counters three ahead,
-    # then C dealt.  With workers of random speed every task completes and
-    # every non-empty event fires exactly once.
+    # The ORDERED schedule: R, K, S dealt in phase order, then one stream
+    # of G1 tiles followed by G2 tiles claimed in index order from per-group
+    # counters three ahead, then C dealt.  With workers of random speed every
+    # task completes and every non-empty event fires exactly once.
     tasks, st, ph = _moe_layer_graph(T=12, E=8, k=2, bm=4, n1=3, n2=2, seed=seed)
-    phases = [("deal", ph["R"]), ("deal", ph["K"]), ("deal", ph["S"]), ("claim", ph["G1"]),
-              ("claim", ph["G2"]), ("deal", ph["C"])]
+    phases = [("deal", ph["R"]), ("deal", ph["K"]), ("deal", ph["S"]), ("claim", ph["G1"] + ph["G2"]),
+              ("deal", ph["C"])]
     order = ev.run_ordered(tasks, st, workers, phases, groups=4, seed=seed)
     assert sorted(order) == list(range(len(tasks))) and not st.errors
     assert all(v == 1 for v in st.fired.values())
@@ -518,7 +518,7 @@ def test_ordered_claims_out_of_graph_order_deadlock():
     # Claiming G2 tiles before G1 tiles breaks the argument: every worker
     # then holds a G2 tile whose G1 producers nobody can start.
     tasks, st, ph = _moe_layer_graph(T=12, E=8, k=2, bm=4, n1=3, n2=2, seed=0)
-    phases = [("deal", ph["R"]), ("deal", ph["K"]), ("deal", ph["S"]), ("claim", ph["G2"]),
-              ("claim", ph["G1"]), ("deal", ph["C"])]
+    phases = [("deal", ph["R"]), ("deal", ph["K"]), ("deal", ph["S"]), ("claim", ph["G2"] + ph["G1"]),
+              ("deal", ph["C"])]
     with pytest.raises(RuntimeError):
         ev.run_ordered(tasks, st, 4, phases, groups=4, seed=0)
