@@ -122,11 +122,12 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
 }
 
 // LDS bytes the scan task needs: one chunk's presence bitmap and per-word
-// prefixes, counts / exp_indptr / tile-numbering scratch and the scan's
-// partial sums.  Independent of T_max (the scan walks the tokens in chunks).
+// prefixes, counts / exp_indptr / tile-numbering scratch, the scan's partial
+// sums and the chunk's expert ids.  Independent of T_max (the scan walks the
+// tokens in chunks).
 inline int64_t scan_lds_bytes(int E, int T_max) {
   (void)T_max;
-  return (int64_t)E * kScanW * 4 * 2 + 4 * 260 * 4 + 128;
+  return (int64_t)E * kScanW * 4 * 2 + 4 * 260 * 4 + 128 + kScanChunkT * kMaxK;
 }
 // G2: cross-wave reduction buffer (4 waves x 4 blocks x 256 fp32) plus the
 // bf16 staging of the kBM x 64 output tile

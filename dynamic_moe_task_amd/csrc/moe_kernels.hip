@@ -465,15 +465,36 @@ __device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem, LocalR
   int* tmp = iptr + 260;         // 32 words for the block scans
   int* tfirst = tmp + 32;        // per expert: first four-block tile | (number of them << 16)
   int* ttail = tfirst + 260;     // per expert: the tile of its last rows when that tile is smaller
+  uint8_t* eid = reinterpret_cast<uint8_t*>(ttail + 260);  // the chunk's expert ids (E <= 256)
   const rsrc_t rids = r_ids(p);
+  // the chunk's ids, all loads issued before any is used (one latency, not
+  // one per pair), then kept in LDS for the passes below
+  auto load_ids = [&](int ch) {
+    constexpr int kPer = 8;  // loads in flight a thread
+    const int f0 = ch * kScanChunkT * k, f1 = min(n, f0 + kScanChunkT * k);
+    for (int g0 = f0; g0 < f1; g0 += kPer * kThreads) {
+      uint32_t v[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int f = g0 + i * kThreads + tid;
+        v[i] = f < f1 ? co_ld32(rids, (uint32_t)f * 4u) : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int f = g0 + i * kThreads + tid;
+        if (f < f1) eid[f - f0] = (uint8_t)v[i];
+      }
+    }
+  };
   // the bitmap of chunk `ch`: bit t - ch * kScanChunkT of word row e is set
   // when token t routes to expert e
   auto build_bits = [&](int ch) {
     for (int i = tid; i < E * W; i += kThreads) bits[i] = 0u;
+    load_ids(ch);
     __syncthreads();
-    const int f1 = min(n, (ch + 1) * kScanChunkT * k);
-    for (int f = ch * kScanChunkT * k + tid; f < f1; f += kThreads) {
-      const int e = (int)co_ld32(rids, (uint32_t)f * 4u);
+    const int f0 = ch * kScanChunkT * k, f1 = min(n, f0 + kScanChunkT * k);
+    for (int f = f0 + tid; f < f1; f += kThreads) {
+      const int e = eid[f - f0];
       const int tl = f / k - ch * kScanChunkT;
       atomicOr(&bits[e * W + (tl >> 5)], 1u << (tl & 31));
     }
@@ -488,8 +509,13 @@ __device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem, LocalR
     }
   } else {
     for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
-    __syncthreads();
-    for (int f = tid; f < n; f += kThreads) atomicAdd(&cnt[co_ld32(rids, (uint32_t)f * 4u)], 1);
+    for (int ch = 0; ch < nch; ++ch) {
+      load_ids(ch);
+      __syncthreads();
+      const int f0 = ch * kScanChunkT * k, f1 = min(n, f0 + kScanChunkT * k);
+      for (int f = f0 + tid; f < f1; f += kThreads) atomicAdd(&cnt[eid[f - f0]], 1);
+      __syncthreads();  // the ids are read before the next chunk's are stored
+    }
   }
   __syncthreads();
   const int my = tid < E ? cnt[tid] : 0;
@@ -538,9 +564,9 @@ __device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem, LocalR
       }
     }
     __syncthreads();
-    const int f1 = min(n, (ch + 1) * kScanChunkT * k);
-    for (int f = ch * kScanChunkT * k + tid; f < f1; f += kThreads) {
-      const int e = (int)co_ld32(rids, (uint32_t)f * 4u);
+    const int f0 = ch * kScanChunkT * k, f1 = min(n, f0 + kScanChunkT * k);
+    for (int f = f0 + tid; f < f1; f += kThreads) {
+      const int e = eid[f - f0];
       const int tl = f / k - ch * kScanChunkT;
       const int w = tl >> 5, b = tl & 31;
       const int s = iptr[e] + pre[e * W + w] + __popc(bits[e * W + w] & ((1u << b) - 1u));
