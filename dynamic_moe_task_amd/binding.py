@@ -70,7 +70,12 @@ class MoeInfo(ctypes.Structure):
                 ("router_tokens", ctypes.c_int32), ("router_experts", ctypes.c_int32),
                 ("dispatch_tokens", ctypes.c_int32), ("combine_tokens", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-                ("wall_clock_khz", ctypes.c_int32)]
+                ("wall_clock_khz", ctypes.c_int32), ("router_experts_large", ctypes.c_int32),
+                ("router_large_from", ctypes.c_int32)]
+
+    def router_experts_for(self, T: int) -> int:
+        """Experts per router task at batch T."""
+        return self.router_experts if T <= self.router_large_from else self.router_experts_large
 
 
 _lib = None

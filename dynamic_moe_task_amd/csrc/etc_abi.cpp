@@ -340,6 +340,8 @@ extern "C" int moe_layer_info(const etc_moe_desc* d, etc_moe_info* info) {
   info->bn2 = kBN2;
   info->router_tokens = kRouterT;
   info->router_experts = kRouterE;
+  info->router_experts_large = kRouterEL;
+  info->router_large_from = kRouterLargeT;
   info->dispatch_tokens = 0;  // no dispatch tasks: G1 gathers its rows from x
   info->combine_tokens = kCombineT;
   info->threads = kThreads;

@@ -21,7 +21,10 @@ enum : uint32_t {
 // ---- task geometry -------------------------------------------------------
 constexpr int kThreads = 256;   // 4 wave64 per workgroup
 constexpr int kRouterT = 4;     // R task: tokens ...
-constexpr int kRouterE = 4;     //         ... x experts (one expert per wave)
+constexpr int kRouterE = 4;     //         ... x experts (one expert per wave) up to
+constexpr int kRouterLargeT = 64;  //     T = kRouterLargeT; above it four experts per
+constexpr int kRouterEL = 16;      //     wave, so that fewer, longer R tasks cover E
+__host__ __device__ inline int router_experts(int T) { return T > kRouterLargeT ? kRouterEL : kRouterE; }
 constexpr int kBM = 64;         // grouped-GEMM row tile (up to four 16-row MFMA blocks)
 constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile
 constexpr int kBN2 = 64;        // G2: output columns per tile

@@ -137,7 +137,7 @@ __device__ __forceinline__ Ctx make_ctx(const MoeParams& p, uint32_t* set) {
   c.queue = set ? reinterpret_cast<uint64_t*>(set + p.o_queue) : nullptr;
   c.T = p.T; c.H = p.H; c.E = p.E; c.k = p.k; c.I = p.I;
   c.nTT = (p.T + kRouterT - 1) / kRouterT;
-  c.nET = (p.E + kRouterE - 1) / kRouterE;
+  c.nET = (p.E + router_experts(p.T) - 1) / router_experts(p.T);
   c.nR = c.nTT * c.nET;
   c.nK = c.nTT;
   c.nC = (p.T + kCombineT - 1) / kCombineT;
@@ -246,65 +246,91 @@ __device__ __forceinline__ void notify_fast(const MoeParams& p, const Ctx& c, ui
 // s = 32..1.  This fixed order is what makes the top-k decision
 // reproducible bit for bit.  Loads of four chunks per lane are issued ahead
 // of their arithmetic.
-__device__ void task_router(const MoeParams& p, const Ctx& c, int tt, int et) {
+// R: logits of kRouterT tokens x (4 * EPW) experts; wave w computes experts
+// et * 4 * EPW + w * EPW + j, j < EPW.  Each logit is one wave's sum in the
+// fixed order: lane l takes 8-element chunks l, l + 64, ... with ascending
+// fused multiply-adds, then an xor butterfly over the lanes, then the bias.
+template <int EPW>
+__device__ __forceinline__ void router_body(const MoeParams& p, const Ctx& c, int tt, int et) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int e = et * kRouterE + wv;
-  if (e >= c.E) return;
+  const int e0 = et * 4 * EPW + wv * EPW;
+  if (e0 >= c.E) return;
   const int t0 = tt * kRouterT;
   const int ntok = min(kRouterT, c.T - t0);
-  float acc[kRouterT];
+  const int ne = min(EPW, c.E - e0);
+  float acc[EPW][kRouterT];
 #pragma unroll
-  for (int r = 0; r < kRouterT; ++r) acc[r] = 0.0f;
+  for (int j = 0; j < EPW; ++j)
+#pragma unroll
+    for (int r = 0; r < kRouterT; ++r) acc[j][r] = 0.0f;
   const int nchunk = c.H >> 3;
-  const uint16_t* wrow = p.wr + (size_t)e * c.H;
   const uint16_t* xrow = p.x + (size_t)t0 * c.H;
+  const uint16_t* wrow = p.wr + (size_t)e0 * c.H;
   constexpr int U = 4;
   for (int c0 = lane; c0 < nchunk; c0 += 64 * U) {
-    u32x4_t wv4[U], xv4[U][kRouterT];
+    // the batch's token chunks, then each expert's weight chunks against them
+    u32x4_t xv4[U][kRouterT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ch = c0 + 64 * u;
-      if (ch < nchunk) {
-        wv4[u] = ld4(wrow + ch * 8);
 #pragma unroll
-        for (int r = 0; r < kRouterT; ++r)
-          if (r < ntok) xv4[u][r] = ld4(xrow + (size_t)r * c.H + ch * 8);
-      }
+      for (int r = 0; r < kRouterT; ++r)
+        if (ch < nchunk && r < ntok) xv4[u][r] = ld4(xrow + (size_t)r * c.H + ch * 8);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ch = c0 + 64 * u;
-      if (ch < nchunk) {
-        float wf[8];
-        unpack8(wv4[u], wf);
+    for (int j = 0; j < EPW; ++j) {
+      u32x4_t wv4[U];
 #pragma unroll
-        for (int r = 0; r < kRouterT; ++r) {
-          if (r < ntok) {
-            float xf[8];
-            unpack8(xv4[u][r], xf);
+      for (int u = 0; u < U; ++u) {
+        const int ch = c0 + 64 * u;
+        if (ch < nchunk && j < ne) wv4[u] = ld4(wrow + (size_t)j * c.H + ch * 8);
+      }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc[r] = __builtin_fmaf(xf[q], wf[q], acc[r]);
+      for (int u = 0; u < U; ++u) {
+        const int ch = c0 + 64 * u;
+        if (ch < nchunk && j < ne) {
+          float wf[8];
+          unpack8(wv4[u], wf);
+#pragma unroll
+          for (int r = 0; r < kRouterT; ++r) {
+            if (r < ntok) {
+              float xf[8];
+              unpack8(xv4[u][r], xf);
+#pragma unroll
+              for (int q = 0; q < 8; ++q) acc[j][r] = __builtin_fmaf(xf[q], wf[q], acc[j][r]);
+            }
           }
         }
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < kRouterT; ++r) {
+  for (int j = 0; j < EPW; ++j)
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) acc[r] = acc[r] + __shfl_xor(acc[r], s);
-  }
+    for (int r = 0; r < kRouterT; ++r) {
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) acc[j][r] = acc[j][r] + __shfl_xor(acc[j][r], s);
+    }
   if (lane == 0) {
     const rsrc_t rl = r_logits(p);
 #pragma unroll
-    for (int r = 0; r < kRouterT; ++r) {
-      if (r < ntok) {
-        float v = acc[r];
-        if (p.has_bias) v = v + p.br[e];
-        co_stf(rl, (uint32_t)((t0 + r) * c.E + e) * 4u, v);
+    for (int j = 0; j < EPW; ++j) {
+#pragma unroll
+      for (int r = 0; r < kRouterT; ++r) {
+        if (j < ne && r < ntok) {
+          float v = acc[j][r];
+          if (p.has_bias) v = v + p.br[e0 + j];
+          co_stf(rl, (uint32_t)((t0 + r) * c.E + e0 + j) * 4u, v);
+        }
       }
     }
   }
+}
+__device__ __forceinline__ void task_router(const MoeParams& p, const Ctx& c, int tt, int et) {
+  if (router_experts(c.T) == kRouterEL)
+    router_body<kRouterEL / 4>(p, c, tt, et);
+  else
+    router_body<kRouterE / 4>(p, c, tt, et);
 }
 
 // K: top-k per token (one wave per token): k rounds of a wave-wide arg-max
@@ -333,7 +359,7 @@ __device__ __forceinline__ float wave_max(float x) {
   x = dpp_max_step<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
-__device__ void task_topk(const MoeParams& p, const Ctx& c, int tt) {
+__device__ __forceinline__ void task_topk(const MoeParams& p, const Ctx& c, int tt) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = tt * kRouterT + wv;
   if (t >= c.T) return;
@@ -453,7 +479,7 @@ __device__ void block_excl_scan_n(const int (&v)[N], int (&ex)[N], int (&total)[
 // LOCAL: the same computation for a small batch (one chunk) into `lr`, in
 // the workgroup's own LDS, with no memory written.
 template <bool LOCAL = false>
-__device__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem, LocalRoute* lr = nullptr) {
+__device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem, LocalRoute* lr = nullptr) {
   const int tid = threadIdx.x;
   const int E = c.E, k = c.k, n = c.T * c.k;
   const int nch = (c.T + kScanChunkT - 1) / kScanChunkT;
@@ -719,7 +745,7 @@ __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const 
 // the separate G kernels of the kernel-by-kernel launch keep longer batches
 // for four-block tiles, where they are faster there.
 template <bool KBK = false>
-__device__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt, float* red,
+__device__ __forceinline__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt, float* red,
                         const uint32_t* pre = nullptr) {
   (void)rt;
   switch (row_blocks(tile.nrows)) {
@@ -812,7 +838,7 @@ __device__ __forceinline__ void g2_body(const MoeParams& p, const Ctx& c, const 
 }
 
 template <bool KBK = false>
-__device__ void task_g2(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt2, float* red) {
+__device__ __forceinline__ void task_g2(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt2, float* red) {
   (void)rt;
   switch (row_blocks(tile.nrows)) {
     case 1: g2_body<1, 2>(p, c, tile, nt2, red); break;
@@ -824,7 +850,7 @@ __device__ void task_g2(const MoeParams& p, const Ctx& c, const RowTile tile, in
 // C: out[t, :] = bf16(sum_j w[t, j] * Y[slot[t*k+j], :]), fp32 in j order.
 // The task's (weight, slot) pairs are staged in LDS first; then each thread
 // issues the loads of all k expert rows of its chunk before the arithmetic.
-__device__ void task_combine(const MoeParams& p, const Ctx& c, int ct, int* s_pair, bool staged = false) {
+__device__ __forceinline__ void task_combine(const MoeParams& p, const Ctx& c, int ct, int* s_pair, bool staged = false) {
   const int t0 = ct * kCombineT;
   const int ntok = min(kCombineT, c.T - t0);
   const int cpr = c.H >> 3;
@@ -881,7 +907,7 @@ __device__ __forceinline__ void q_put(const Ctx& c, int64_t slot, uint64_t desc)
 }
 
 template <int MODE>
-__device__ void after_router(const MoeParams& p, const Ctx& c, int tt) {
+__device__ __forceinline__ void after_router(const MoeParams& p, const Ctx& c, int tt) {
   if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC || MODE == MODE_ORDERED) {
     wg_publish();
     if (threadIdx.x == 0) {
@@ -894,7 +920,7 @@ __device__ void after_router(const MoeParams& p, const Ctx& c, int tt) {
 }
 
 template <int MODE>
-__device__ void after_topk(const MoeParams& p, const Ctx& c) {
+__device__ __forceinline__ void after_topk(const MoeParams& p, const Ctx& c) {
   if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC || MODE == MODE_ORDERED) {
     wg_publish();
     if (threadIdx.x == 0) {
@@ -907,7 +933,7 @@ __device__ void after_topk(const MoeParams& p, const Ctx& c) {
 }
 
 template <int MODE>
-__device__ void after_scan(const MoeParams& p, const Ctx& c, Shared& sh, int nrt) {
+__device__ __forceinline__ void after_scan(const MoeParams& p, const Ctx& c, Shared& sh, int nrt) {
   if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC || MODE == MODE_ORDERED) {
     wg_publish();
     if (MODE == MODE_DYNAMIC) {
@@ -934,7 +960,7 @@ __device__ void after_scan(const MoeParams& p, const Ctx& c, Shared& sh, int nrt
 }
 
 template <int MODE>
-__device__ void after_g1(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
+__device__ __forceinline__ void after_g1(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
   if (MODE != MODE_STATIC && MODE != MODE_DYNAMIC) return;
   wg_publish();
   if (threadIdx.x == 0) {
@@ -952,7 +978,7 @@ __device__ void after_g1(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
 }
 
 template <int MODE>
-__device__ void after_g2(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
+__device__ __forceinline__ void after_g2(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
   if (MODE != MODE_STATIC && MODE != MODE_DYNAMIC) return;
   const RowTile tile = load_rowtile(p, rt);
   wg_publish();
@@ -980,7 +1006,7 @@ __device__ void after_g2(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
 // Grid-wide barrier (BARRIER comparator only): arrival counter plus a
 // generation word; the last arrival resets the counter and bumps the
 // generation.  Bounded by the same watchdog as every other wait.
-__device__ bool grid_barrier(const Ctx& c, int parties) {
+__device__ __forceinline__ bool grid_barrier(const Ctx& c, int parties) {
   wg_publish();
   int fail = 0;
   if (threadIdx.x == 0) {
@@ -1026,7 +1052,7 @@ __device__ bool wait_known(const uint32_t* ctr, uint32_t target, uint32_t known,
 // row a lane (at most kCombineT * k <= 32 rows), under the watchdog.
 // It also stages the task's (weight, slot) pairs in `s_pair` for task_combine,
 // so that the combine, on the critical path's tail, starts with its Y loads.
-__device__ bool wait_rows_done(const MoeParams& p, const Ctx& c, int ct, int* s_pair) {
+__device__ __forceinline__ bool wait_rows_done(const MoeParams& p, const Ctx& c, int ct, int* s_pair) {
   int fail = 0;
   if (threadIdx.x < 64) {
     const int t0 = ct * kCombineT, nrow = min(kCombineT, c.T - t0) * c.k;
@@ -1064,7 +1090,7 @@ __device__ bool wait_rows_done(const MoeParams& p, const Ctx& c, int ct, int* s_
   return fail == 0;
 }
 
-__device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G,
+__device__ __forceinline__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G,
                               const LocalRoute* lr) {
   if (i0 >= n) return;
   const bool tr = p.trace != nullptr;
@@ -1120,7 +1146,7 @@ __device__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int 
   }
 }
 
-__device__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G,
+__device__ __forceinline__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G,
                               const LocalRoute* lr) {
   if (i0 >= n) return;
   const bool tr = p.trace != nullptr;
@@ -1201,7 +1227,7 @@ __device__ __forceinline__ GTask gtask(const Ctx& c, int i, int nG1) {
 // I/16) for G2; its state is fetched one tile ahead, the row-tile descriptor
 // two ahead and the claim three ahead.  Returns false when a wait gave up
 // (the launch is aborting).
-__device__ bool run_g_ordered(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q, int nG1, uint32_t* sk,
+__device__ __forceinline__ bool run_g_ordered(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q, int nG1, uint32_t* sk,
                               const LocalRoute* lr) {
   const int n = q.n;
   const bool tr = p.trace != nullptr;
@@ -1295,7 +1321,7 @@ __device__ bool run_g_ordered(const MoeParams& p, const Ctx& c, float* red, cons
 // wait can be circular and the schedule cannot deadlock.  Task counts of the
 // phases after S are read from S's output (data-dependent instantiation).
 template <int MODE>
-__device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh) {
+__device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh) {
   const int G = gridDim.x, w = blockIdx.x;
   float* red = reinterpret_cast<float*>(smem);
   constexpr bool EV = (MODE == MODE_STATIC || MODE == MODE_ORDERED);
@@ -1427,7 +1453,7 @@ __device__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Share
 // the task (early push).  A workgroup pops by bumping the head, waits for its
 // slot, and exits once the total task count (known after S) is passed.  Tasks
 // never wait on events here: they are only pushed when ready.
-__device__ void run_dynamic(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh) {
+__device__ __forceinline__ void run_dynamic(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh) {
   float* red = reinterpret_cast<float*>(smem);
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
@@ -1629,7 +1655,7 @@ int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu) {
 int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int nTT = (p.T + kRouterT - 1) / kRouterT;
-  const int nET = (p.E + kRouterE - 1) / kRouterE;
+  const int nET = (p.E + router_experts(p.T) - 1) / router_experts(p.T);
   const int nC = (p.T + kCombineT - 1) / kCombineT;
   const int64_t rows = (int64_t)p.T * p.k;
   const int64_t max_rt = (rows + kBM - 1) / kBM + (rows < p.E ? rows : p.E);

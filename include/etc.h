@@ -224,6 +224,8 @@ typedef struct {
   int32_t threads;     /* threads per workgroup                             */
   int32_t lds_bytes;   /* dynamic LDS per workgroup                         */
   int32_t wall_clock_khz; /* rate of the clock the watchdog and trace read  */
+  int32_t router_experts_large; /* R tile's experts when T > router_large_from */
+  int32_t router_large_from;    /* (router_experts applies up to that T)       */
 } etc_moe_info;
 
 /* Fill `info` for `desc` (host struct).  Queries the device for the grid.

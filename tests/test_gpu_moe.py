@@ -98,7 +98,7 @@ def test_event_invariants(qwen_weights, decode_case, sched):
     n_rt = len(oracle.expected_tiles(ref["exp_indptr"], info.bm))
     T = s.T
     expect = [
-        -(-T // info.router_tokens) * -(-E // info.router_experts),  # R
+        -(-T // info.router_tokens) * -(-E // info.router_experts_for(T)),  # R
         -(-T // info.router_tokens),                                 # K
         1,                                                           # S
         -(-T // info.dispatch_tokens) if info.dispatch_tokens else 0,  # D (0: fused into G1's row gather)
@@ -135,7 +135,7 @@ def test_task_trace(qwen_weights, decode_case, sched):
     typ, wg = rec[:, 0] >> 24, rec[:, 0] & 0xFFFFFF
     n_rt = len(oracle.expected_tiles(ref["exp_indptr"], info.bm))
     T, E = s.T, s.E
-    expect = {1: -(-T // info.router_tokens) * -(-E // info.router_experts), 2: -(-T // info.router_tokens),
+    expect = {1: -(-T // info.router_tokens) * -(-E // info.router_experts_for(T)), 2: -(-T // info.router_tokens),
               3: 1, 4: -(-T // info.dispatch_tokens) if info.dispatch_tokens else 0, 5: n_rt * (s.I // info.bn1), 6: n_rt * (s.H // info.bn2),
               7: -(-T // info.combine_tokens)}
     assert {t: int((typ == t).sum()) for t in expect} == expect
