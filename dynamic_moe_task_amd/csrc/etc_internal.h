@@ -124,13 +124,16 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
   return L;
 }
 
-// LDS bytes the scan task needs: one chunk's presence bitmap and per-word
-// prefixes, counts / exp_indptr / tile-numbering scratch, the scan's partial
-// sums and the chunk's expert ids.  Independent of T_max (the scan walks the
-// tokens in chunks).
+// LDS bytes the scan task needs: five per-expert tables (counts,
+// exp_indptr, tile numbering, the chunk's grouped base), the scan's partial
+// sums, one chunk's presence bitmap and per-word prefixes, and the chunk's
+// expert ids (a byte each) and grouped pair order (two bytes each).  Sized
+// for kMaxE so every table sits at a fixed offset; independent of T_max
+// (the scan walks the tokens in chunks).
 inline int64_t scan_lds_bytes(int E, int T_max) {
+  (void)E;
   (void)T_max;
-  return (int64_t)E * kScanW * 4 * 2 + 4 * 260 * 4 + 128 + kScanChunkT * kMaxK;
+  return 5 * 260 * 4 + 128 + (int64_t)kMaxE * kScanW * 4 * 2 + kScanChunkT * kMaxK * 3;
 }
 // G2: cross-wave reduction buffer (4 waves x 4 blocks x 256 fp32) plus the
 // bf16 staging of the kBM x 64 output tile

@@ -145,6 +145,16 @@ __device__ __forceinline__ bool wg_wait(const uint32_t* ctr, uint32_t target, ui
 // Before a notify: each wave waits until its own (device-coherent) stores
 // have completed, then the barrier orders all of them before the notifying
 // thread's atomic.
+// Workgroup barrier that orders LDS accesses only: global stores issued
+// before it keep draining across it (__syncthreads also waits for their
+// acknowledgements).  For phases that hand each other LDS tables while
+// their results go out to memory; a wg_publish still precedes any notify.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void wg_publish() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);

@@ -238,18 +238,15 @@ __device__ __forceinline__ void notify_fast(const MoeParams& p, const Ctx& c, ui
 }
 
 // ===================================================== task bodies ==========
-// R: router logits, L[t, e] = sum_h x[t, h] * wr[e, h] (+ b[e]).  Wave w of
-// the workgroup owns expert e = et*4 + w; lane l owns the 8-element chunks
-// c = l, l+64, ... of the hidden dimension and accumulates them in ascending
-// order with fused multiply-adds; the 64 lane sums are combined by a halving
-// xor butterfly whose lane-0 result equals the tree acc[l] += acc[l + s],
-// s = 32..1.  This fixed order is what makes the top-k decision
-// reproducible bit for bit.  Loads of four chunks per lane are issued ahead
-// of their arithmetic.
-// R: logits of kRouterT tokens x (4 * EPW) experts; wave w computes experts
-// et * 4 * EPW + w * EPW + j, j < EPW.  Each logit is one wave's sum in the
-// fixed order: lane l takes 8-element chunks l, l + 64, ... with ascending
-// fused multiply-adds, then an xor butterfly over the lanes, then the bias.
+// R: router logits L[t, e] = sum_h x[t, h] * wr[e, h] (+ b[e]) of kRouterT
+// tokens x (4 * EPW) experts; wave w computes experts et * 4 * EPW + w * EPW
+// + j, j < EPW.  Each logit is one wave's sum in a fixed order: lane l takes
+// the 8-element chunks l, l + 64, ... of the hidden dimension with ascending
+// fused multiply-adds, then a halving xor butterfly combines the 64 lane sums
+// (its lane-0 result equals the tree acc[l] += acc[l + s], s = 32..1), then
+// the bias.  This fixed order is what makes the top-k decision reproducible
+// bit for bit.  A batch of four chunks per lane is loaded before its
+// arithmetic.
 template <int EPW>
 __device__ __forceinline__ void router_body(const MoeParams& p, const Ctx& c, int tt, int et) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -267,8 +264,38 @@ __device__ __forceinline__ void router_body(const MoeParams& p, const Ctx& c, in
   const uint16_t* xrow = p.x + (size_t)t0 * c.H;
   const uint16_t* wrow = p.wr + (size_t)e0 * c.H;
   constexpr int U = 4;
+  if (ntok == kRouterT && ne == EPW && nchunk % (64 * U) == 0) {
+    // full tile: no per-load or per-product predicates.  Per logit the
+    // products still go chunk by chunk in ascending order, 8 elements each.
+    for (int c0 = lane; c0 < nchunk; c0 += 64 * U) {
+      u32x4_t xv4[U][kRouterT], wv4[EPW][U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < kRouterT; ++r) xv4[u][r] = ld4(xrow + (size_t)r * c.H + (c0 + 64 * u) * 8);
+#pragma unroll
+      for (int j = 0; j < EPW; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) wv4[j][u] = ld4(wrow + (size_t)j * c.H + (c0 + 64 * u) * 8);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float wf[EPW][8];
+#pragma unroll
+        for (int j = 0; j < EPW; ++j) unpack8(wv4[j][u], wf[j]);
+#pragma unroll
+        for (int r = 0; r < kRouterT; ++r) {
+          float xf[8];
+          unpack8(xv4[u][r], xf);
+#pragma unroll
+          for (int j = 0; j < EPW; ++j)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[j][r] = __builtin_fmaf(xf[q], wf[j][q], acc[j][r]);
+        }
+      }
+    }
+  } else {
   for (int c0 = lane; c0 < nchunk; c0 += 64 * U) {
-    // the batch's token chunks, then each expert's weight chunks against them
+    // the batch's token chunks and every expert's weight chunks
     u32x4_t xv4[U][kRouterT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -277,20 +304,22 @@ __device__ __forceinline__ void router_body(const MoeParams& p, const Ctx& c, in
       for (int r = 0; r < kRouterT; ++r)
         if (ch < nchunk && r < ntok) xv4[u][r] = ld4(xrow + (size_t)r * c.H + ch * 8);
     }
+    u32x4_t wv4[EPW][U];  // all weight chunks of the batch in flight together
 #pragma unroll
-    for (int j = 0; j < EPW; ++j) {
-      u32x4_t wv4[U];
+    for (int j = 0; j < EPW; ++j)
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int ch = c0 + 64 * u;
-        if (ch < nchunk && j < ne) wv4[u] = ld4(wrow + (size_t)j * c.H + ch * 8);
+        if (ch < nchunk && j < ne) wv4[j][u] = ld4(wrow + (size_t)j * c.H + ch * 8);
       }
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int ch = c0 + 64 * u;
         if (ch < nchunk && j < ne) {
           float wf[8];
-          unpack8(wv4[u], wf);
+          unpack8(wv4[j][u], wf);
 #pragma unroll
           for (int r = 0; r < kRouterT; ++r) {
             if (r < ntok) {
@@ -303,6 +332,7 @@ __device__ __forceinline__ void router_body(const MoeParams& p, const Ctx& c, in
         }
       }
     }
+  }
   }
 #pragma unroll
   for (int j = 0; j < EPW; ++j)
@@ -446,7 +476,7 @@ __device__ void block_excl_scan_n(const int (&v)[N], int (&ex)[N], int (&total)[
 #pragma unroll
     for (int q = 0; q < N; ++q) tmp[wv * N + q] = incl[q];
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int q = 0; q < N; ++q) {
     int off = 0, tot = 0;
@@ -459,7 +489,7 @@ __device__ void block_excl_scan_n(const int (&v)[N], int (&ex)[N], int (&total)[
     ex[q] = off + incl[q] - v[q];
     total[q] = tot;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // S: counts, exp_indptr (exclusive prefix sum of counts, ends at T*k), the
@@ -468,7 +498,12 @@ __device__ void block_excl_scan_n(const int (&v)[N], int (&ex)[N], int (&total)[
 // time: a per-expert token bitmap of the chunk in LDS gives each routed pair
 // its rank among the same expert's earlier tokens of the chunk, and a
 // per-expert running count carries the ranks across chunks, so the LDS the
-// scan needs does not grow with T.
+// scan needs does not grow with T.  The ids are read with 128-bit loads, a
+// whole chunk's in flight at once.  The slot of each pair is stored in pair
+// order; perm and row_rt are indexed by grouped row, so each chunk's pairs
+// are first placed in LDS by grouped position and then stored in that
+// order, as runs of consecutive rows (stored in pair order they would scatter
+// one row per transaction).
 //
 // Row tiles are numbered heaviest first: tiles of four 16-row blocks (more
 // than 32 rows), then of two, then of one, each class in expert order.  The
@@ -478,72 +513,113 @@ __device__ void block_excl_scan_n(const int (&v)[N], int (&ex)[N], int (&total)[
 //
 // LOCAL: the same computation for a small batch (one chunk) into `lr`, in
 // the workgroup's own LDS, with no memory written.
-template <bool LOCAL = false>
+template <bool LOCAL = false, bool PREFETCH = true>
 __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem, LocalRoute* lr = nullptr) {
   const int tid = threadIdx.x;
   const int E = c.E, k = c.k, n = c.T * c.k;
   const int nch = (c.T + kScanChunkT - 1) / kScanChunkT;
   const int W = (min(c.T, kScanChunkT) + 31) >> 5;  // bitmap words per expert and chunk
-  uint32_t* bits = reinterpret_cast<uint32_t*>(smem);
-  int* pre = reinterpret_cast<int*>(smem + E * kScanW * 4);
-  int* cnt = pre + E * kScanW;
+  // LDS at fixed offsets (sized for kMaxE), so that no table address is
+  // kept in a register
+  int* cnt = reinterpret_cast<int*>(smem);
   int* iptr = cnt + 260;
   int* tmp = iptr + 260;         // 32 words for the block scans
   int* tfirst = tmp + 32;        // per expert: first four-block tile | (number of them << 16)
   int* ttail = tfirst + 260;     // per expert: the tile of its last rows when that tile is smaller
-  uint8_t* eid = reinterpret_cast<uint8_t*>(ttail + 260);  // the chunk's expert ids (E <= 256)
+  int* base = ttail + 260;       // per expert: grouped row of the chunk's grouped position 0
+  // [w][e] word-major, so that thread e walking its words touches one bank
+  // per lane: the chunk's token bitmap and each word's first rank
+  uint32_t* bits = reinterpret_cast<uint32_t*>(base + 260);
+  int* pre = reinterpret_cast<int*>(bits + kMaxE * kScanW);
+  uint32_t* eid4 = reinterpret_cast<uint32_t*>(pre + kMaxE * kScanW);  // the chunk's expert ids, a byte each
+  const uint8_t* eid = reinterpret_cast<const uint8_t*>(eid4);
+  uint16_t* lrow = reinterpret_cast<uint16_t*>(eid4 + kScanChunkT * kMaxK / 4);  // the chunk's pairs, grouped
   const rsrc_t rids = r_ids(p);
-  // the chunk's ids, all loads issued before any is used (one latency, not
-  // one per pair), then kept in LDS for the passes below
-  auto load_ids = [&](int ch) {
-    constexpr int kPer = 8;  // loads in flight a thread
-    const int f0 = ch * kScanChunkT * k, f1 = min(n, f0 + kScanChunkT * k);
-    for (int g0 = f0; g0 < f1; g0 += kPer * kThreads) {
-      uint32_t v[kPer];
+  auto tok = [&](int f) { return f / k; };  // the token of pair f
+  // Ids [g0, g1) into registers with 128-bit loads (g0 a multiple of 4),
+  // every load of the batch in flight at once: one latency per batch.
+  constexpr int kLd = 4;
+  constexpr int kBatch = 4 * kThreads * kLd;  // ids a batch covers (a whole chunk for k <= 8)
+  auto load_ids = [&](int g0, int g1, u32x4_t (&v)[kLd]) {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int f = g0 + i * kThreads + tid;
-        v[i] = f < f1 ? co_ld32(rids, (uint32_t)f * 4u) : 0u;
-      }
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int f = g0 + i * kThreads + tid;
-        if (f < f1) eid[f - f0] = (uint8_t)v[i];
+    for (int i = 0; i < kLd; ++i) {
+      const int f = g0 + 4 * (i * kThreads + tid);
+      v[i] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (f + 4 <= g1) {
+        v[i] = co_ld128(rids, (uint32_t)f * 4u);
+      } else if (f < g1) {  // the last one to three ids: no load reaches past g1
+        v[i].x = co_ld32(rids, (uint32_t)f * 4u);
+        if (f + 1 < g1) v[i].y = co_ld32(rids, (uint32_t)(f + 1) * 4u);
+        if (f + 2 < g1) v[i].z = co_ld32(rids, (uint32_t)(f + 2) * 4u);
       }
     }
   };
-  // the bitmap of chunk `ch`: bit t - ch * kScanChunkT of word row e is set
-  // when token t routes to expert e
-  auto build_bits = [&](int ch) {
-    for (int i = tid; i < E * W; i += kThreads) bits[i] = 0u;
-    load_ids(ch);
-    __syncthreads();
-    const int f0 = ch * kScanChunkT * k, f1 = min(n, f0 + kScanChunkT * k);
-    for (int f = f0 + tid; f < f1; f += kThreads) {
-      const int e = eid[f - f0];
-      const int tl = f / k - ch * kScanChunkT;
-      atomicOr(&bits[e * W + (tl >> 5)], 1u << (tl & 31));
+  // fn(e, t, ok) for each id of the batch: pair f = t * k + slot routes to
+  // expert e; ok is false past g1 (then e = t = 0 and fn must change
+  // nothing).  Selects, not branches, so that no per-id lane masks are kept.
+  auto each_id = [&](int g0, int g1, const u32x4_t (&v)[kLd], auto&& fn) {
+#pragma unroll
+    for (int i = 0; i < kLd; ++i) {
+      const int f = g0 + 4 * (i * kThreads + tid);
+      const uint32_t ids[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = f + j < g1;
+        fn(ok ? (int)ids[j] : 0, ok ? tok(f + j) : 0, ok);
+      }
     }
-    __syncthreads();
   };
+  auto chunk_end = [&](int ch) { return min(n, (ch + 1) * kScanChunkT * k); };
+  // chunk `ch`: its ids into LDS and its bitmap (bit t - ch * kScanChunkT of
+  // word (w, e) is set when token t routes to expert e); `v` holds the
+  // chunk's first batch when `loaded`
+  auto build_bits = [&](int ch, u32x4_t (&v)[kLd], bool loaded) {
+    const int f0 = ch * kScanChunkT * k, f1 = chunk_end(ch);
+    if (tid < E)
+      for (int w = 0; w < W; ++w) bits[w * kMaxE + tid] = 0u;
+    lds_barrier();  // the bitmap is clear before the ors
+    for (int g0 = f0; g0 < f1; g0 += kBatch) {
+      const int g1 = min(f1, g0 + kBatch);
+      if (g0 != f0 || !loaded) load_ids(g0, g1, v);
+#pragma unroll
+      for (int i = 0; i < kLd; ++i) {
+        const int f = g0 + 4 * (i * kThreads + tid);
+        if (f < g1)
+          eid4[(f - f0) >> 2] = (v[i].x & 0xffu) | ((v[i].y & 0xffu) << 8) | ((v[i].z & 0xffu) << 16) | (v[i].w << 24);
+      }
+      each_id(g0, g1, v, [&](int e, int t, bool ok) {
+        const int tl = ok ? t - ch * kScanChunkT : 0;
+        atomicOr(&bits[(tl >> 5) * kMaxE + e], ok ? 1u << (tl & 31) : 0u);
+      });
+    }
+    lds_barrier();
+  };
+  // PREFETCH: the next chunk's first batch of ids is loaded while the
+  // current chunk is stored (sixteen more registers held across the chunk)
+  u32x4_t v[kLd];
   if (nch == 1) {  // one chunk: the counts come from its bitmap
-    build_bits(0);
-    for (int e = tid; e < E; e += kThreads) {
+    build_bits(0, v, false);
+    if (tid < E) {
       int run = 0;
-      for (int w = 0; w < W; ++w) run += __popc(bits[e * W + w]);
-      cnt[e] = run;
+      for (int w = 0; w < W; ++w) run += __popc(bits[w * kMaxE + tid]);
+      cnt[tid] = run;
     }
+  } else if (c.set) {
+    // several chunks with events on: S runs after every top-k task, whose
+    // arrivals on expert e's event count exactly the pairs routed to e
+    if (PREFETCH) load_ids(0, chunk_end(0), v);
+    if (tid < E) cnt[tid] = (int)ld_relaxed(ev_exp(p, c, tid));
   } else {
-    for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
-    for (int ch = 0; ch < nch; ++ch) {
-      load_ids(ch);
-      __syncthreads();
-      const int f0 = ch * kScanChunkT * k, f1 = min(n, f0 + kScanChunkT * k);
-      for (int f = f0 + tid; f < f1; f += kThreads) atomicAdd(&cnt[eid[f - f0]], 1);
-      __syncthreads();  // the ids are read before the next chunk's are stored
+    if (tid < E) cnt[tid] = 0;
+    lds_barrier();
+    for (int g0 = 0; g0 < n; g0 += kBatch) {
+      const int g1 = min(n, g0 + kBatch);
+      load_ids(g0, g1, v);
+      each_id(g0, g1, v, [&](int e, int, bool ok) { atomicAdd(&cnt[e], ok ? 1 : 0); });
     }
+    if (PREFETCH) load_ids(0, chunk_end(0), v);
   }
-  __syncthreads();
+  lds_barrier();
   const int my = tid < E ? cnt[tid] : 0;
   const int mytiles = (my + kBM - 1) / kBM;
   const int rem = my % kBM;
@@ -578,34 +654,97 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
       st_relaxed(p.meta + M_NRT, (uint32_t)tot_tiles);
     }
   }
-  __syncthreads();
-  const rsrc_t rs = r_slot(p), rp = r_perm(p), rrt = r_rowrt(p);
-  int run = 0;  // thread e: rows of expert e in earlier chunks
-  for (int ch = 0; ch < nch; ++ch) {
-    if (nch > 1) build_bits(ch);
-    for (int e = tid; e < E; e += kThreads) {
+  lds_barrier();
+  if constexpr (LOCAL) {
+    // one chunk: grouped row of a pair = iptr[e] + rank among e's tokens
+    if (tid < E) {
+      int r = ex;
       for (int w = 0; w < W; ++w) {
-        pre[e * W + w] = run;
-        run += __popc(bits[e * W + w]);
+        pre[w * kMaxE + tid] = r;
+        r += __popc(bits[w * kMaxE + tid]);
       }
     }
-    __syncthreads();
-    const int f0 = ch * kScanChunkT * k, f1 = min(n, f0 + kScanChunkT * k);
-    for (int f = f0 + tid; f < f1; f += kThreads) {
-      const int e = eid[f - f0];
-      const int tl = f / k - ch * kScanChunkT;
-      const int w = tl >> 5, b = tl & 31;
-      const int s = iptr[e] + pre[e * W + w] + __popc(bits[e * W + w] & ((1u << b) - 1u));
-      if (LOCAL) {
-        lr->perm[s] = (uint16_t)f;
-        continue;
-      }
-      co_st32(rs, (uint32_t)f * 4u, (uint32_t)s);
-      co_st32(rp, (uint32_t)s * 4u, (uint32_t)f);
-      const int mt = (s - iptr[e]) / kBM, tf = tfirst[e];  // the row's tile, numbered as below
-      co_st32(rrt, (uint32_t)s * 4u, (uint32_t)(mt < (tf >> 16) ? (tf & 0xffff) + mt : ttail[e]));
+    lds_barrier();
+    for (int f = tid; f < n; f += kThreads) {
+      const int e = eid[f];
+      const int tl = tok(f);
+      const int i = (tl >> 5) * kMaxE + e;
+      lr->perm[pre[i] + __popc(bits[i] & ((1u << (tl & 31)) - 1u))] = (uint16_t)f;
     }
-    __syncthreads();  // the chunk's bitmap and prefixes are read before the next chunk rebuilds them
+  } else {
+    const rsrc_t rs = r_slot(p), rp = r_perm(p), rrt = r_rowrt(p);
+    int run = 0;  // thread e: rows of expert e in earlier chunks
+    for (int ch = 0; ch < nch; ++ch) {
+      if (nch > 1) build_bits(ch, v, PREFETCH);
+      const int f0 = ch * kScanChunkT * k, f1 = chunk_end(ch);
+      if (PREFETCH && ch + 1 < nch) load_ids(f1, chunk_end(ch + 1), v);  // in flight while this chunk is stored
+      // The chunk's pairs in grouped order (expert, then token) get positions
+      // 0, 1, ...; thread e numbers its words from the chunk's earlier
+      // experts on, and expert e's rows of this chunk follow its rows of the
+      // earlier chunks.
+      int ce = 0;
+      if (tid < E) {
+        for (int w = 0; w < W; ++w) {
+          pre[w * kMaxE + tid] = ce;
+          ce += __popc(bits[w * kMaxE + tid]);
+        }
+      }
+      const int cv[1] = {ce};
+      int cx[1], ct[1];
+      block_excl_scan_n<1>(cv, cx, ct, tmp);
+      if (tid < E) {
+        for (int w = 0; w < W; ++w) pre[w * kMaxE + tid] += cx[0];
+        base[tid] = ex + run - cx[0];
+        run += ce;
+      }
+      lds_barrier();
+      // pair order: the slot of each pair (a contiguous store) and the pair
+      // at each grouped position, in LDS; four pairs a thread at a time so
+      // that their LDS round trips overlap
+      for (int fa = f0 + tid; fa < f1; fa += 4 * kThreads) {
+        int e[4], tl[4], q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int f = fa + u * kThreads;
+          e[u] = f < f1 ? eid[f - f0] : 0;
+          tl[u] = f < f1 ? tok(f) - ch * kScanChunkT : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = (tl[u] >> 5) * kMaxE + e[u];
+          q[u] = pre[i] + __popc(bits[i] & ((1u << (tl[u] & 31)) - 1u));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int f = fa + u * kThreads;
+          if (f < f1) {
+            lrow[q[u]] = (uint16_t)(f - f0);
+            co_st32(rs, (uint32_t)f * 4u, (uint32_t)(base[e[u]] + q[u]));
+          }
+        }
+      }
+      lds_barrier();
+      // grouped order: perm and row_rt of consecutive rows go out as runs
+      const int np = f1 - f0;
+      for (int qa = tid; qa < np; qa += 4 * kThreads) {
+        int fl[4], e[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) fl[u] = qa + u * kThreads < np ? lrow[qa + u * kThreads] : 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = eid[fl[u]];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = qa + u * kThreads;
+          if (q < np) {
+            const int s = base[e[u]] + q;
+            co_st32(rp, (uint32_t)s * 4u, (uint32_t)(f0 + fl[u]));
+            const int mt = (s - iptr[e[u]]) / kBM, tf = tfirst[e[u]];  // the row's tile, numbered as below
+            co_st32(rrt, (uint32_t)s * 4u, (uint32_t)(mt < (tf >> 16) ? (tf & 0xffff) + mt : ttail[e[u]]));
+          }
+        }
+      }
+      lds_barrier();  // this chunk's LDS tables are read before the next chunk rebuilds them
+    }
   }
   const rsrc_t rr = r_rtinfo(p);
   if (tid < E) {
@@ -624,7 +763,7 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
       co_st128(rr, (uint32_t)rt * 16u, q);
     }
   }
-  if (LOCAL) __syncthreads();  // the tables are read by every thread next
+  if (LOCAL) lds_barrier();  // the tables are read by every thread next
   return tot_tiles;
 }
 
@@ -1505,7 +1644,7 @@ __device__ __forceinline__ void run_dynamic(const MoeParams& p, const Ctx& c, ui
         trace_task(p, TT_K, a, b, tw, ts, tb);
         break;
       case TT_S: {
-        const int nrt_s = task_scan(p, c, smem);
+        const int nrt_s = task_scan<false, false>(p, c, smem);
         if (tr) tb = now_ticks();
         dbg_task(p, TT_S);
         after_scan<MODE_DYNAMIC>(p, c, sh, nrt_s);

@@ -1,0 +1,45 @@
+"""Compile-time resource check of the HIP kernels (CPU only).
+
+The persistent megakernel holds every task body; if the compiler stops
+inlining one of them, the kernel arguments are copied to per-lane scratch
+memory and every access to them becomes a memory round trip.  This test
+compiles the kernels for gfx950 with the resource-usage remarks and requires
+that no kernel uses scratch or spills registers, and that the persistent
+kernels keep two workgroups per CU (at most 256 VGPRs)."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "dynamic_moe_task_amd", "csrc")
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_kernels_use_no_scratch(tmp_path):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-c", "--cuda-device-only",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", CSRC,
+           os.path.join(CSRC, "moe_kernels.hip"), "-o", str(tmp_path / "k.o"),
+           "-Rpass-analysis=kernel-resource-usage"]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    kernels = {}
+    name = None
+    for line in r.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            kernels[name] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[bytes/lane\])?: (\d+)", line)
+        if m and name:
+            kernels[name][m.group(1).strip()] = int(m.group(2))
+    persistent = [k for k in kernels if "moe_persistent" in k]
+    assert len(persistent) == 4, sorted(kernels)
+    for k, v in kernels.items():
+        assert v.get("ScratchSize", 0) == 0, (k, v)
+        assert v.get("VGPRs Spill", 0) == 0, (k, v)
+    for k in persistent:
+        assert kernels[k]["VGPRs"] + kernels[k].get("AGPRs", 0) <= 256, (k, kernels[k])
