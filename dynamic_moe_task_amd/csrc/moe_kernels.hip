@@ -545,6 +545,7 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
     for (int i = 0; i < kLd; ++i) {
       const int f = g0 + 4 * (i * kThreads + tid);
       v[i] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (g0 + 4 * i * kThreads >= g1) continue;  // uniform
       if (f + 4 <= g1) {
         v[i] = co_ld128(rids, (uint32_t)f * 4u);
       } else if (f < g1) {  // the last one to three ids: no load reaches past g1
@@ -560,6 +561,7 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
   auto each_id = [&](int g0, int g1, const u32x4_t (&v)[kLd], auto&& fn) {
 #pragma unroll
     for (int i = 0; i < kLd; ++i) {
+      if (g0 + 4 * i * kThreads >= g1) break;  // uniform: no thread has ids from load i on
       const int f = g0 + 4 * (i * kThreads + tid);
       const uint32_t ids[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
@@ -584,7 +586,7 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
 #pragma unroll
       for (int i = 0; i < kLd; ++i) {
         const int f = g0 + 4 * (i * kThreads + tid);
-        if (f < g1)
+        if (f < g1)  // f0 and g0 are multiples of 4: one word a load
           eid4[(f - f0) >> 2] = (v[i].x & 0xffu) | ((v[i].y & 0xffu) << 8) | ((v[i].z & 0xffu) << 16) | (v[i].w << 24);
       }
       each_id(g0, g1, v, [&](int e, int t, bool ok) {
