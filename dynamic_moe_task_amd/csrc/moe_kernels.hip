@@ -1342,9 +1342,10 @@ __device__ __forceinline__ void run_g2_static(const MoeParams& p, const Ctx& c, 
 struct ClaimQ {
   uint32_t* ctr;
   int grp, ngrp, n;
+  int base;  // tile of ordinal 0 (tiles below it are dealt, not claimed)
 };
 __device__ __forceinline__ int claimed_task(const ClaimQ& q, uint32_t k) {
-  const int64_t i = (int64_t)k * q.ngrp + q.grp;
+  const int64_t i = q.base + (int64_t)k * q.ngrp + q.grp;
   return i < q.n ? (int)i : q.n;
 }
 
@@ -1455,6 +1456,102 @@ __device__ __forceinline__ bool run_g_ordered(const MoeParams& p, const Ctx& c, 
   return true;
 }
 
+// ORDERED with the routing tables in LDS (small batches): the same stream
+// with one claimed tile fewer held ahead.  Descriptors, row indices and
+// wait counts come from LDS, so the next tile's state needs no second
+// stage of lookahead: at the start of a tile the next one is known and the
+// claim for the one after it is in flight.  Holding fewer claimed tiles
+// leaves fewer of them queued behind a running tile at the end of the
+// stream.  One counter serves the whole grid, so the XCDs, which stream at
+// somewhat different rates, end together (with one counter per XCD group
+// the groups ended up to 6 us apart at decode); workgroup w's first two
+// tiles are dealt (w and G + w), so that the grid's first claims do not
+// all meet on that counter at once (claimed, they held the first G1 tile
+// back by 6 us), and ordinal o of the counter is tile 2G + o.  Deadlock
+// freedom as in run_g_ordered: a workgroup's tiles still come in ascending
+// index order, every G1 tile below every G2 tile.
+// sk[0] and sk[1] hold the first two tiles' ordinals; thread 0 hands each
+// later claim to the other threads in sk[1] or sk[2], alternately (a slot
+// is rewritten only after the task barriers that follow every thread's read
+// of it).
+__device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q,
+                                                    int nG1, uint32_t* sk, const LocalRoute* lr) {
+  const int n = q.n;
+  const bool tr = p.trace != nullptr;
+  uint64_t tw = 0, ts = 0, tb = 0;
+  const int G = gridDim.x, w = blockIdx.x;
+  const int t0 = w, t1 = G + w;  // dealt; claimed ordinals start at 2G
+  int cur = t0 < n ? t0 : n;
+  if (cur >= n) return true;
+  auto ev_of = [&](const GTask& t, const RowTile& r) -> uint32_t* {
+    return t.g2 ? ev_h(p, c, t.rt) : ev_exp(p, c, r.e);
+  };
+  auto tgt_of = [&](const GTask& t, const RowTile& r) -> uint32_t {
+    return t.g2 ? (uint32_t)c.nN1 : (uint32_t)lr->cnt[r.e];
+  };
+  GTask tc = gtask(c, cur, nG1);
+  RowTile rc = get_tile(p, lr, tc.rt);
+  uint32_t cur_tgt = 0, cur_arr = 0;
+  if (threadIdx.x == 0) {
+    cur_tgt = tgt_of(tc, rc);
+    cur_arr = ld_relaxed(ev_of(tc, rc));
+  }
+  uint32_t cur_f[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) cur_f[b] = tc.g2 ? 0u : row_perm(p, rc, b, lr);
+  __builtin_amdgcn_s_waitcnt(0);  // loop entry with nothing in flight (see run_g1_static)
+  int rd = 1;  // slot that holds the next tile's ordinal
+  bool second = true;  // the next tile is the dealt t1
+  for (;;) {
+    if (tr) tw = now_ticks();
+    if (!wait_known(ev_of(tc, rc), cur_tgt, cur_arr, c)) return false;
+    if (tr) ts = now_ticks();
+    const int nxt = second ? (t1 < n ? t1 : n) : claimed_task(q, sk[rd]);
+    second = false;
+    uint32_t knew = 0xffffffffu;
+    if (threadIdx.x == 0 && nxt < n) knew = add_relaxed(q.ctr, 1u);
+    GTask tn = tc;
+    RowTile rn = rc;
+    uint32_t nxt_tgt = 0, nxt_arr = 0;
+    uint32_t nxt_f[4] = {0u, 0u, 0u, 0u};
+    if (nxt < n) {
+      tn = gtask(c, nxt, nG1);
+      rn = get_tile(p, lr, tn.rt);
+      if (threadIdx.x == 0) {
+        nxt_tgt = tgt_of(tn, rn);
+        nxt_arr = ld_relaxed(ev_of(tn, rn));
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) nxt_f[b] = tn.g2 ? 0u : row_perm(p, rn, b, lr);
+    }
+    if (!tc.g2) {
+      task_g1(p, c, rc, tc.rt, tc.nt, red, cur_f);
+    } else {
+      task_g2(p, c, rc, tc.rt, tc.nt, red);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // wave 0 wrote the tile: drain, then notify (see run_g1_static)
+    if (threadIdx.x == 0) {
+      if (!tc.g2)
+        notify_fast(p, c, ev_h(p, c, tc.rt), (uint32_t)c.nN1);
+      else
+        notify_fast(p, c, ev_y(p, c, tc.rt), (uint32_t)c.nN2);
+      sk[3 - rd] = knew;
+    }
+    if (tr) tb = now_ticks();
+    dbg_task(p, tc.g2 ? TT_G2 : TT_G1);
+    trace_task(p, tc.g2 ? TT_G2 : TT_G1, tc.rt, tc.nt, tw, ts, tb);
+    if (nxt >= n) break;
+    tc = tn;
+    rc = rn;
+    cur_tgt = nxt_tgt;
+    cur_arr = nxt_arr;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) cur_f[b] = nxt_f[b];
+    rd = 3 - rd;
+  }
+  return true;
+}
+
 // STATIC / BARRIER: each phase's tasks are dealt round-robin over the
 // workgroups, continuing from where the previous phase stopped, and every
 // workgroup runs its list in phase order.  In STATIC a task waits only on
@@ -1502,20 +1599,22 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
     trace_task(p, TT_S, 0, 0, tw, ts, tb);
   }
   off += 1;
-  // ORDERED: the first three G1 claims are taken while S still runs (an
-  // ordinal does not depend on S's result)
-  const int ngrp = G % 8 == 0 ? 8 : 1, grp = w % ngrp;
-  if (MODE == MODE_ORDERED && threadIdx.x == 0) {
+  // Small batch: each workgroup rebuilds the routing tables in its own LDS
+  // as soon as every top-k task is done, so G1 does not wait for S (S still
+  // writes the routing outputs, which C reads).
+  const bool local = EV && c.T <= kScanChunkT && c.T * c.k <= kLocalRows;
+  // ORDERED claim counters: one per XCD group for large batches, where the
+  // first three claims are taken while S still runs (an ordinal does not
+  // depend on S's result); one for the whole grid with the LDS tables,
+  // whose runner deals its first two tiles instead of claiming them.
+  const int ngrp = (G % 8 == 0 && !local) ? 8 : 1, grp = w % ngrp;
+  if (MODE == MODE_ORDERED && !local && threadIdx.x == 0) {
     uint32_t* ctr = c.set + W_CLAIM_G1 + grp * 32;
     sh.claim[0] = add_relaxed(ctr, 1u);
     sh.claim[1] = add_relaxed(ctr, 1u);
     sh.claim[2] = add_relaxed(ctr, 1u);
   }
   int nrt;
-  // Small batch: each workgroup rebuilds the routing tables in its own LDS
-  // as soon as every top-k task is done, so G1 does not wait for S (S still
-  // writes the routing outputs, which C reads).
-  const bool local = EV && c.T <= kScanChunkT && c.T * c.k <= kLocalRows;
   __shared__ LocalRoute lroute;
   const LocalRoute* lr = nullptr;
   if (local) {
@@ -1543,8 +1642,9 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   const int Gt = (MODE != MODE_ORDERED && p.solo_wgs > 0 && nG1 <= 3 * p.solo_wgs) ? p.solo_wgs : G;
   if (w >= Gt) return;
   if (MODE == MODE_ORDERED) {
-    const ClaimQ q{c.set + W_CLAIM_G1 + grp * 32, grp, ngrp, nG1 + nG2};
-    if (!run_g_ordered(p, c, red, q, nG1, sh.claim, lr)) return;
+    const ClaimQ q{c.set + W_CLAIM_G1 + grp * 32, grp, ngrp, nG1 + nG2, local ? 2 * G : 0};
+    if (lr ? !run_g_ordered_local(p, c, red, q, nG1, sh.claim, lr) : !run_g_ordered(p, c, red, q, nG1, sh.claim, lr))
+      return;
     off += nG1 + nG2;
   } else {
   if (EV) {

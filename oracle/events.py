@@ -170,7 +170,7 @@ def run_dynamic(tasks: List[Task], state: EventState, seed: int = 0) -> List[int
 
 def run_ordered(tasks: List[Task], state: EventState, workers: int,
                 phases: Sequence[Tuple[str, Sequence[int]]], groups: int = 8, ahead: int = 3,
-                seed: int = 0) -> List[int]:
+                seed: int = 0, dealt: int = 0) -> List[int]:
     """Workers go through `phases` in order.  A ("deal", ids) phase gives
     worker w every task ids[i] with (i + off) % workers == w, where off is
     the number of tasks dealt in earlier phases (round-robin continuing from
@@ -179,7 +179,10 @@ def run_ordered(tasks: List[Task], state: EventState, workers: int,
     worker count is a multiple of `groups`, else one group): ordinal k of
     group g is ids[k * ngroups + g]; a worker holds `ahead` ordinals from the
     start of the phase and claims one more each time it finishes a task,
-    until an ordinal falls past the end.  Each step advances one worker
+    until an ordinal falls past the end.  With `dealt` = d > 0 the first d
+    of a worker's `ahead` tasks are dealt instead (worker w gets ids[w],
+    ids[workers + w], ...) and ordinal k of group g is ids[d * workers +
+    k * ngroups + g].  Each step advances one worker
     chosen at random (random speeds); a worker whose next task waits on an
     unreleased event stalls.  Returns the completion order; raises
     RuntimeError on deadlock."""
@@ -200,8 +203,8 @@ def run_ordered(tasks: List[Task], state: EventState, workers: int,
             if mode == "deal":
                 queue[w] = [ids[i] for i in range(len(ids)) if (i + offs[phase[w]]) % workers == w]
             else:
-                queue[w] = []
-                for _ in range(ahead):
+                queue[w] = [ids[r * workers + w] for r in range(dealt) if r * workers + w < len(ids)]
+                for _ in range(ahead - dealt):
                     claim(w)
             if queue[w]:
                 return
@@ -212,7 +215,7 @@ def run_ordered(tasks: List[Task], state: EventState, workers: int,
         g = w % ngrp
         k = counters[phase[w]][g]
         counters[phase[w]][g] += 1
-        i = k * ngrp + g
+        i = dealt * workers + k * ngrp + g
         if i < len(ids):
             queue[w].append(ids[i])
 
