@@ -1243,7 +1243,10 @@ __device__ __forceinline__ void run_g1_static(const MoeParams& p, const Ctx& c, 
   uint32_t cur_tgt = 0, cur_arr = 0;
   if (threadIdx.x == 0) {
     cur_tgt = (lr ? (uint32_t)lr->cnt[cur.e] : co_ld32(rcnt, (uint32_t)cur.e * 4u));
-    cur_arr = ld_relaxed(ev_exp(p, c, cur.e));
+    // with the LDS tables every expert event is known released: the tables
+    // were built after the route event, which each top-k task notifies only
+    // once its expert notifies have completed
+    cur_arr = lr ? cur_tgt : ld_relaxed(ev_exp(p, c, cur.e));
   }
   // grouped-row permutation entries of the tile's rows (A gather), one task ahead
   uint32_t cur_f[4];
@@ -1457,32 +1460,34 @@ __device__ __forceinline__ bool run_g_ordered(const MoeParams& p, const Ctx& c, 
 }
 
 // ORDERED with the routing tables in LDS (small batches): the same stream
-// with one claimed tile fewer held ahead.  Descriptors, row indices and
-// wait counts come from LDS, so the next tile's state needs no second
-// stage of lookahead: at the start of a tile the next one is known and the
-// claim for the one after it is in flight.  Holding fewer claimed tiles
-// leaves fewer of them queued behind a running tile at the end of the
-// stream.  One counter serves the whole grid, so the XCDs, which stream at
-// somewhat different rates, end together (with one counter per XCD group
-// the groups ended up to 6 us apart at decode); workgroup w's first two
-// tiles are dealt (w and G + w), so that the grid's first claims do not
-// all meet on that counter at once (claimed, they held the first G1 tile
-// back by 6 us), and ordinal o of the counter is tile 2G + o.  Deadlock
-// freedom as in run_g_ordered: a workgroup's tiles still come in ascending
-// index order, every G1 tile below every G2 tile.
-// sk[0] and sk[1] hold the first two tiles' ordinals; thread 0 hands each
-// later claim to the other threads in sk[1] or sk[2], alternately (a slot
-// is rewritten only after the task barriers that follow every thread's read
-// of it).
+// with fewer claimed tiles held ahead.  Descriptors, row indices and wait
+// counts come from LDS, so the next tile's state needs no second stage of
+// lookahead: at the start of a tile the next one is known and the claim
+// for the one after it is in flight.  Once the held tile is among the
+// stream's last 2G, a workgroup claims only when it holds none (the claim
+// in flight is then the next tile), so fewer tiles wait behind a running
+// one while other workgroups have run out: with one tile held to the end,
+// a third of the grid started its last tile after the first workgroup had
+// gone idle (decode 169.3 us; 168.8 with this endgame).
+// One counter serves the whole grid, so the XCDs, which stream at somewhat
+// different rates, end together (with one counter per XCD group the groups
+// ended up to 6 us apart at decode).  Workgroup w's first two tiles are
+// dealt (w and G + w), so that the grid's first claims do not all meet on
+// that counter at once (claimed, they held the first G1 tile back by
+// 6 us); ordinal o of the counter is tile 2G + o.  Thread 0 hands a
+// claim's result to the other threads through sk[0] and an LDS barrier.
+// Deadlock freedom as in run_g_ordered: a workgroup's tiles come in
+// ascending index order, every G1 tile below every G2 tile.
 __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q,
                                                     int nG1, uint32_t* sk, const LocalRoute* lr) {
   const int n = q.n;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
   const int G = gridDim.x, w = blockIdx.x;
-  const int t0 = w, t1 = G + w;  // dealt; claimed ordinals start at 2G
-  int cur = t0 < n ? t0 : n;
+  int cur = w < n ? w : n;
   if (cur >= n) return true;
+  int nxt = G + w < n ? G + w : n;  // the tile held after the running one (n: none)
+  bool more = true;                 // the counter may still hand out tiles
   auto ev_of = [&](const GTask& t, const RowTile& r) -> uint32_t* {
     return t.g2 ? ev_h(p, c, t.rt) : ev_exp(p, c, r.e);
   };
@@ -1494,22 +1499,24 @@ __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ct
   uint32_t cur_tgt = 0, cur_arr = 0;
   if (threadIdx.x == 0) {
     cur_tgt = tgt_of(tc, rc);
-    cur_arr = ld_relaxed(ev_of(tc, rc));
+    // a G1 tile's expert event is known released (the tables were built
+    // after the route event; see run_g1_static), so the first tile starts
+    // without a load round trip
+    cur_arr = tc.g2 ? ld_relaxed(ev_of(tc, rc)) : cur_tgt;
   }
   uint32_t cur_f[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) cur_f[b] = tc.g2 ? 0u : row_perm(p, rc, b, lr);
   __builtin_amdgcn_s_waitcnt(0);  // loop entry with nothing in flight (see run_g1_static)
-  int rd = 1;  // slot that holds the next tile's ordinal
-  bool second = true;  // the next tile is the dealt t1
   for (;;) {
     if (tr) tw = now_ticks();
     if (!wait_known(ev_of(tc, rc), cur_tgt, cur_arr, c)) return false;
     if (tr) ts = now_ticks();
-    const int nxt = second ? (t1 < n ? t1 : n) : claimed_task(q, sk[rd]);
-    second = false;
+    // claim the tile after the held one while the stream is long; near its
+    // end (held tile within the last 2G) claim only with none held
+    const bool claim = more && (nxt < n ? nxt < n - 2 * G : true);
     uint32_t knew = 0xffffffffu;
-    if (threadIdx.x == 0 && nxt < n) knew = add_relaxed(q.ctr, 1u);
+    if (threadIdx.x == 0 && claim) knew = add_relaxed(q.ctr, 1u);
     GTask tn = tc;
     RowTile rn = rc;
     uint32_t nxt_tgt = 0, nxt_arr = 0;
@@ -1535,19 +1542,40 @@ __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ct
         notify_fast(p, c, ev_h(p, c, tc.rt), (uint32_t)c.nN1);
       else
         notify_fast(p, c, ev_y(p, c, tc.rt), (uint32_t)c.nN2);
-      sk[3 - rd] = knew;
+      if (claim) sk[0] = knew;
     }
     if (tr) tb = now_ticks();
     dbg_task(p, tc.g2 ? TT_G2 : TT_G1);
     trace_task(p, tc.g2 ? TT_G2 : TT_G1, tc.rt, tc.nt, tw, ts, tb);
-    if (nxt >= n) break;
-    tc = tn;
-    rc = rn;
-    cur_tgt = nxt_tgt;
-    cur_arr = nxt_arr;
+    int got = n;  // the claimed tile, handed to every thread (sk[0] is next
+                  // written only after this task's and the next task's barriers)
+    if (claim) {
+      lds_barrier();
+      got = claimed_task(q, sk[0]);
+      if (got >= n) more = false;
+    }
+    if (nxt < n) {
+      tc = tn;
+      rc = rn;
+      cur_tgt = nxt_tgt;
+      cur_arr = nxt_arr;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) cur_f[b] = nxt_f[b];
-    rd = 3 - rd;
+      for (int b = 0; b < 4; ++b) cur_f[b] = nxt_f[b];
+      nxt = got;
+    } else if (got < n) {
+      // none was held: the tile claimed during this one runs next; its
+      // event state is polled by the wait (a G1 tile's is known released)
+      tc = gtask(c, got, nG1);
+      rc = get_tile(p, lr, tc.rt);
+      if (threadIdx.x == 0) {
+        cur_tgt = tgt_of(tc, rc);
+        cur_arr = tc.g2 ? 0u : cur_tgt;
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) cur_f[b] = tc.g2 ? 0u : row_perm(p, rc, b, lr);
+    } else {
+      break;
+    }
   }
   return true;
 }
