@@ -39,7 +39,7 @@ constexpr int kScanChunkT = 512;       // S: tokens per bitmap pass
 constexpr int kScanW = kScanChunkT / 32;  // S: bitmap words per expert and pass
 // Small batches (T <= kScanChunkT and T*k <= kLocalRows): every persistent
 // workgroup rebuilds the routing tables in its own LDS
-constexpr int kLocalRows = 1024;
+constexpr int kLocalRows = 4096;
 constexpr int kLocalTiles = kLocalRows / 64 + 256 + 16;
 // watchdog of one in-kernel wait, in microseconds of wall time; a healthy
 // wait lasts microseconds
