@@ -86,9 +86,50 @@ def copy_calibration(mib, steps):
 TASK_NAMES = {1: "R", 2: "K", 3: "S", 4: "D", 5: "G1", 6: "G2", 7: "C"}
 
 
-def trace_summary(bufs, T, sched, khz, stream_ptr, records=1 << 16, dump=None):
+def tile_rows(counts, bm=64):
+    """Rows of each row tile, in the kernel's numbering: tiles of more than
+    32 rows (four 16-row MFMA blocks) first, then of 17-32 rows, then of at
+    most 16, each class in expert order; expert e with c rows has c // bm
+    full tiles and one tile of the remainder (measurement bookkeeping)."""
+    four, two, one = [], [], []
+    for c in (int(x) for x in counts):
+        full, rem = divmod(c, bm)
+        four += [bm] * full
+        if rem > 32:
+            four.append(rem)
+        elif rem > 16:
+            two.append(rem)
+        elif rem > 0:
+            one.append(rem)
+    return four + two + one
+
+
+def tile_mfma(rec_typ, rec_a, body_us, rows, H, I, grid):
+    """Tile-level MFMA use of the G tasks whose row tile has four row blocks
+    (33-64 rows): the tile's FLOPs over its body time, against the
+    workgroup's share of the bf16 peak (the grid shares the chip evenly)."""
+    peak_wg = BF16_PEAK_TFS * 1e12 / grid
+    out = {}
+    for t, name, cols, kdim in ((5, "G1", 32, H), (6, "G2", 64, I)):
+        m = rec_typ == t
+        r = np.array([rows[a] if a < len(rows) else 0 for a in rec_a[m]])
+        big = r > 32
+        if not big.any():
+            continue
+        flops = 2.0 * r[big] * cols * kdim
+        eff = flops / (body_us[m][big] * 1e-6) / peak_wg
+        wbytes = cols * kdim * 2
+        out[name] = {"tiles": int(big.sum()), "rows_mean": round(float(r[big].mean()), 1),
+                     "body_us_mean": round(float(body_us[m][big].mean()), 2),
+                     "mfma_frac_mean": round(float(eff.mean()), 4),
+                     "flop_per_weight_byte": round(float(flops.mean() / wbytes), 1)}
+    return out
+
+
+def trace_summary(bufs, T, sched, khz, stream_ptr, records=1 << 16, dump=None, shape=None):
     """One traced launch: per task type, count, mean/max duration, mean
-    wait, and the first start / last end in µs from the earliest wait."""
+    wait, and the first start / last end in µs from the earliest wait; with
+    `shape`, the tile-level MFMA use of the four-block G tiles."""
     import torch
     from dynamic_moe_task_amd import binding as B
     tr = torch.zeros(B.trace_words(records), dtype=torch.int32, device="cuda")
@@ -127,6 +168,10 @@ def trace_summary(bufs, T, sched, khz, stream_ptr, records=1 << 16, dump=None):
                      "last_end_us": round(float((te[m].max() - t0) * us), 2)}
     per_wg = np.bincount(wg, weights=(te - ts) * us)
     out["busy_per_wg_us"] = {"mean": round(float(per_wg.mean()), 2), "max": round(float(per_wg.max()), 2)}
+    if shape is not None:
+        rows = tile_rows(bufs.counts.cpu().numpy())
+        grid = int(raw[2])
+        out["tile_mfma_four_block"] = tile_mfma(typ, rec[:, 1], (tb - ts) * us, rows, shape.H, shape.I, grid)
     return out
 
 
@@ -290,6 +335,10 @@ def measure_token_counts(Wr, w13s, w2s, sp, steps, warmup, repeat, counts=(1, 12
                 runs[s].append(time_sched(bufs, T, s, steps, warmup, w13s, w2s, sp))
         us = {s: float(np.median(v)) for s, v in runs.items()}
         row = {"us_per_layer": {s: round(v, 2) for s, v in us.items()}}
+        # whole-layer MFMA use of the ORDERED megakernel (the layer's
+        # algorithmic FLOPs over its time, against the bf16 peak)
+        row["ordered_mfma_frac_whole_layer"] = round(
+            wl.algorithmic_flops(shape, T) / (us["ordered"] * 1e-6) / (BF16_PEAK_TFS * 1e12), 5)
         for s in ("static", "ordered"):
             row[f"{s}_over_barrier_speedup"] = round(us["barrier"] / us[s], 3)
             row[f"{s}_over_kbk_speedup"] = round(us["kbk"] / us[s], 3)
@@ -376,7 +425,7 @@ def main():
     if a.trace:
         info = B.moe_layer_info(desc)
         base = os.path.splitext(a.trace)[0]
-        summ = {s: trace_summary(bufs, T, s, info.wall_clock_khz, sp, dump=f"{base}_{s}.npz")
+        summ = {s: trace_summary(bufs, T, s, info.wall_clock_khz, sp, dump=f"{base}_{s}.npz", shape=shape)
                 for s in ("static", "ordered", "barrier")}
         summ["grid"] = info.grid
         with open(a.trace, "w") as f:
