@@ -104,13 +104,13 @@ def tile_rows(counts, bm=64):
     return four + two + one
 
 
-def tile_mfma(rec_typ, rec_a, body_us, rows, H, I, grid):
+def tile_mfma(rec_typ, rec_a, body_us, rows, H, I, grid, bn1, bn2):
     """Tile-level MFMA use of the G tasks whose row tile has four row blocks
     (33-64 rows): the tile's FLOPs over its body time, against the
     workgroup's share of the bf16 peak (the grid shares the chip evenly)."""
     peak_wg = BF16_PEAK_TFS * 1e12 / grid
     out = {}
-    for t, name, cols, kdim in ((5, "G1", 32, H), (6, "G2", 64, I)):
+    for t, name, cols, kdim in ((5, "G1", 2 * bn1, H), (6, "G2", bn2, I)):
         m = rec_typ == t
         r = np.array([rows[a] if a < len(rows) else 0 for a in rec_a[m]])
         big = r > 32
@@ -171,7 +171,9 @@ def trace_summary(bufs, T, sched, khz, stream_ptr, records=1 << 16, dump=None, s
     if shape is not None:
         rows = tile_rows(bufs.counts.cpu().numpy())
         grid = int(raw[2])
-        out["tile_mfma_four_block"] = tile_mfma(typ, rec[:, 1], (tb - ts) * us, rows, shape.H, shape.I, grid)
+        info = B.moe_layer_info(bufs.desc)
+        out["tile_mfma_four_block"] = tile_mfma(typ, rec[:, 1], (tb - ts) * us, rows, shape.H, shape.I, grid,
+                                                info.bn1_for(T, shape.k), info.bn2)
     return out
 
 

@@ -71,11 +71,16 @@ class MoeInfo(ctypes.Structure):
                 ("dispatch_tokens", ctypes.c_int32), ("combine_tokens", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("wall_clock_khz", ctypes.c_int32), ("router_experts_large", ctypes.c_int32),
-                ("router_large_from", ctypes.c_int32)]
+                ("router_large_from", ctypes.c_int32), ("bn1_large", ctypes.c_int32),
+                ("bn1_large_from_rows", ctypes.c_int32)]
 
     def router_experts_for(self, T: int) -> int:
         """Experts per router task at batch T."""
         return self.router_experts if T <= self.router_large_from else self.router_experts_large
+
+    def bn1_for(self, T: int, k: int) -> int:
+        """Gate (and up) columns per G1 tile at batch T, top-k k."""
+        return self.bn1_large if T * k >= self.bn1_large_from_rows else self.bn1
 
 
 _lib = None

@@ -26,7 +26,9 @@ constexpr int kRouterLargeT = 64;  //     T = kRouterLargeT; above it four exper
 constexpr int kRouterEL = 16;      //     wave, so that fewer, longer R tasks cover E
 __host__ __device__ inline int router_experts(int T) { return T > kRouterLargeT ? kRouterEL : kRouterE; }
 constexpr int kBM = 64;         // grouped-GEMM row tile (up to four 16-row MFMA blocks)
-constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile
+constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile ...
+constexpr int kWideG1Rows = 2048;  // ... and twice that from T * k routed rows on
+__host__ __device__ inline int g1_cols(int T, int k) { return T * k >= kWideG1Rows ? 2 * kBN1 : kBN1; }
 constexpr int kBN2 = 64;        // G2: output columns per tile
 constexpr int kCB2 = kBN2 / 16;  // G2: 16-column MFMA blocks per tile
 constexpr int kCombineT = 2;    // C task: tokens per task

@@ -126,6 +126,7 @@ struct Ctx {
   uint32_t* status;  // where error bits go
   uint64_t* queue;
   int T, H, E, k, I;
+  int bn1;  // G1 gate (and up) columns per tile, chosen per launch from T
   int nTT, nET, nR, nK, nC, nN1, nN2;
   uint64_t budget;  // watchdog of one wait, wall-clock ticks
 };
@@ -141,7 +142,8 @@ __device__ __forceinline__ Ctx make_ctx(const MoeParams& p, uint32_t* set) {
   c.nR = c.nTT * c.nET;
   c.nK = c.nTT;
   c.nC = (p.T + kCombineT - 1) / kCombineT;
-  c.nN1 = p.I / kBN1;
+  c.bn1 = g1_cols(p.T, p.k);
+  c.nN1 = p.I / c.bn1;
   c.nN2 = p.H / kBN2;
   c.budget = p.budget;
   return c;
@@ -793,7 +795,7 @@ __device__ __forceinline__ uint32_t row_perm(const MoeParams& p, const RowTile t
   if (r >= tile.nrows) return 0u;
   return lr ? (uint32_t)lr->perm[tile.r0 + r] : co_ld32(r_perm(p), (uint32_t)(tile.r0 + r) * 4u);
 }
-template <int NB, int U>
+template <int NB, int U, int CB>
 __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const RowTile tile, int nt, float* red,
                                         const uint32_t* pre) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -801,6 +803,7 @@ __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const 
   const int H = c.H, I = c.I;
   const int kw = H >> 2;
   const int nsteps = kw >> 5;
+  constexpr int BN = 16 * CB;  // gate (and up) columns of the tile
   bool valid[NB];
   const uint16_t* pa[NB];
 #pragma unroll
@@ -811,33 +814,41 @@ __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const 
     const int t = valid[b] ? (int)(f / (uint32_t)c.k) : 0;
     pa[b] = p.x + (size_t)t * H + wv * kw + kg * 8;
   }
-  const uint16_t* pg = p.w13 + ((size_t)tile.e * 2 * I + (size_t)nt * kBN1 + m) * H + wv * kw + kg * 8;
+  const uint16_t* pg = p.w13 + ((size_t)tile.e * 2 * I + (size_t)nt * BN + m) * H + wv * kw + kg * 8;
   const uint16_t* pu = pg + (size_t)I * H;
-  f32x4_t accg[NB], accu[NB];
+  const size_t cbs = (size_t)16 * H;  // next 16-column block of W13
+  f32x4_t accg[NB][CB], accu[NB][CB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) accg[b] = accu[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int q = 0; q < CB; ++q) accg[b][q] = accu[b][q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  // batches of U k-steps ((NB + 2) * U loads of 16 bytes a lane in flight);
-  // two workgroups per CU overlap each other's batch boundaries
+  // batches of U k-steps ((NB + 2 CB) * U loads of 16 bytes a lane in
+  // flight); two workgroups per CU overlap each other's batch boundaries
   for (int s0 = 0; s0 < nsteps; s0 += U) {
-    u32x4_t a[U][NB], bg[U], bu[U];
+    u32x4_t a[U][NB], bg[U][CB], bu[U][CB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u < nsteps) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) a[u][b] = valid[b] ? ld4(pa[b] + (s0 + u) * 32) : zero;
-        bg[u] = ld4(pg + (s0 + u) * 32);
-        bu[u] = ld4(pu + (s0 + u) * 32);
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+          bg[u][q] = ld4(pg + q * cbs + (s0 + u) * 32);
+          bu[u][q] = ld4(pu + q * cbs + (s0 + u) * 32);
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u < nsteps) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          accg[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u][b]), as_bf(bg[u]), accg[b], 0, 0, 0);
-          accu[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u][b]), as_bf(bu[u]), accu[b], 0, 0, 0);
-        }
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int q = 0; q < CB; ++q) {
+            accg[b][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u][b]), as_bf(bg[u][q]), accg[b][q], 0, 0, 0);
+            accu[b][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u][b]), as_bf(bu[u][q]), accu[b][q], 0, 0, 0);
+          }
       }
     }
   }
@@ -845,37 +856,43 @@ __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const 
   // element (lane', i) of a 16x16 MFMA result: row 4*(lane'/16) + i, column lane' % 16
   const int ol = tid >> 2, oi = tid & 3;
   const int row = 4 * (ol >> 4) + oi, col = ol & 15;
-  uint16_t* stage = reinterpret_cast<uint16_t*>(red + 4096);  // [64 rows][16 cols] bf16
+  uint16_t* stage = reinterpret_cast<uint16_t*>(red + 4096);  // [64 rows][BN cols] bf16
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    // cross-wave reduction: red[w][0 = gate, 1 = up][lane * 4 + i]; the first
-    // barrier keeps earlier readers of `red` ahead of these writes
+    // cross-wave reduction: red[w][q][0 = gate, 1 = up][lane * 4 + i]; the
+    // first barrier keeps earlier readers of `red` ahead of these writes
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      red[(wv * 2 + 0) * 256 + lane * 4 + i] = accg[b][i];
-      red[(wv * 2 + 1) * 256 + lane * 4 + i] = accu[b][i];
-    }
-    __syncthreads();
-    float g = 0.f, u = 0.f;
+    for (int q = 0; q < CB; ++q)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      g += red[(w * 2 + 0) * 256 + tid];
-      u += red[(w * 2 + 1) * 256 + tid];
+      for (int i = 0; i < 4; ++i) {
+        red[((wv * CB + q) * 2 + 0) * 256 + lane * 4 + i] = accg[b][q][i];
+        red[((wv * CB + q) * 2 + 1) * 256 + lane * 4 + i] = accu[b][q][i];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < CB; ++q) {
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        g += red[((w * CB + q) * 2 + 0) * 256 + tid];
+        u += red[((w * CB + q) * 2 + 1) * 256 + tid];
+      }
+      stage[(b * 16 + row) * BN + q * 16 + col] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u);
     }
-    stage[(b * 16 + row) * 16 + col] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u);
   }
   __syncthreads();
-  // wave 0 alone writes the tile (rows x 32 bytes, two chunks a row), so
+  // wave 0 alone writes the tile (rows x 2 BN bytes, 16-byte chunks), so
   // only wave 0 has stores to drain before the notify
   if (tid < 64) {
+    constexpr int cpr = BN / 8;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < cpr; ++h) {
       const int idx = tid + 64 * h;
-      const int r = idx >> 1, half = idx & 1;
+      const int r = idx / cpr, q8 = idx % cpr;
       if (r < tile.nrows) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * 16 + half * 8);
-        co_st128(r_hh(p), (uint32_t)(((size_t)(tile.r0 + r) * I + nt * kBN1 + half * 8) * 2), v);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * BN + q8 * 8);
+        co_st128(r_hh(p), (uint32_t)(((size_t)(tile.r0 + r) * I + nt * BN + q8 * 8) * 2), v);
       }
     }
   }
@@ -884,15 +901,26 @@ __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const 
 // k-steps per load batch (U) by row blocks, measured on MI355X: short
 // batches stream better in the persistent kernel (two workgroups per CU);
 // the separate G kernels of the kernel-by-kernel launch keep longer batches
-// for four-block tiles, where they are faster there.
-template <bool KBK = false>
+// for four-block tiles, where they are faster there.  Tiles twice as wide
+// (c.bn1 = 32: large batches, where a four-block tile's gathered x rows
+// outweigh its weights) read each tile's x rows once for 32 gate and 32 up
+// columns instead of 16.
+template <bool KBK = false, bool WIDE = true>
 __device__ __forceinline__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt, float* red,
                         const uint32_t* pre = nullptr) {
   (void)rt;
+  if (WIDE && c.bn1 == 2 * kBN1) {
+    switch (row_blocks(tile.nrows)) {
+      case 1: g1_body<1, 2, 2>(p, c, tile, nt, red, pre); break;
+      case 2: g1_body<2, 2, 2>(p, c, tile, nt, red, pre); break;
+      default: g1_body<4, KBK ? 2 : 1, 2>(p, c, tile, nt, red, pre); break;
+    }
+    return;
+  }
   switch (row_blocks(tile.nrows)) {
-    case 1: g1_body<1, 4>(p, c, tile, nt, red, pre); break;
-    case 2: g1_body<2, 4>(p, c, tile, nt, red, pre); break;
-    default: g1_body<4, KBK ? 4 : 2>(p, c, tile, nt, red, pre); break;
+    case 1: g1_body<1, 4, 1>(p, c, tile, nt, red, pre); break;
+    case 2: g1_body<2, 4, 1>(p, c, tile, nt, red, pre); break;
+    default: g1_body<4, KBK ? 4 : 2, 1>(p, c, tile, nt, red, pre); break;
   }
 }
 
@@ -1782,7 +1810,7 @@ __device__ __forceinline__ void run_dynamic(const MoeParams& p, const Ctx& c, ui
         break;
       }
       case TT_G1:
-        task_g1(p, c, load_rowtile(p, a), a, b, red);
+        task_g1<false, false>(p, c, load_rowtile(p, a), a, b, red);
         if (tr) tb = now_ticks();
         dbg_task(p, TT_G1);
         after_g1<MODE_DYNAMIC>(p, c, a, sh);
@@ -1828,11 +1856,14 @@ moe_persistent(MoeParams p) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < p.set_words;
        i += (int64_t)gridDim.x * kThreads)
     other[i] = 0u;
-  const Ctx c = make_ctx(p, set);
-  if (MODE == MODE_DYNAMIC)
+  Ctx c = make_ctx(p, set);
+  if (MODE == MODE_DYNAMIC) {
+    c.bn1 = kBN1;  // the dynamic schedule runs the narrow G1 tiles only
+    c.nN1 = p.I / kBN1;
     run_dynamic(p, c, smem, sh);
-  else
+  } else {
     run_lists<MODE>(p, c, smem, sh);
+  }
   wg_publish();
   if (threadIdx.x == 0) {
     const uint32_t st = ld_relaxed(c.status) & ~ST_ABORT;
@@ -1928,7 +1959,7 @@ int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream) {
   const int nC = (p.T + kCombineT - 1) / kCombineT;
   const int64_t rows = (int64_t)p.T * p.k;
   const int64_t max_rt = (rows + kBM - 1) / kBM + (rows < p.E ? rows : p.E);
-  const int nN1 = p.I / kBN1, nN2 = p.H / kBN2;
+  const int nN1 = p.I / g1_cols(p.T, p.k), nN2 = p.H / kBN2;
   hipLaunchKernelGGL(kbk_router, dim3(nTT * nET), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_topk, dim3(nTT), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_scan, dim3(1), dim3(kThreads), lds_bytes, s, p);

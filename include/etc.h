@@ -226,6 +226,9 @@ typedef struct {
   int32_t wall_clock_khz; /* rate of the clock the watchdog and trace read  */
   int32_t router_experts_large; /* R tile's experts when T > router_large_from */
   int32_t router_large_from;    /* (router_experts applies up to that T)       */
+  int32_t bn1_large;   /* gate (and up) columns per G1 tile when T*k >=
+                          bn1_large_from_rows (bn1 applies below)          */
+  int32_t bn1_large_from_rows;
 } etc_moe_info;
 
 /* Fill `info` for `desc` (host struct).  Queries the device for the grid.
