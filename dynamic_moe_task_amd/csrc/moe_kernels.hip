@@ -913,7 +913,7 @@ __device__ __forceinline__ void task_g1(const MoeParams& p, const Ctx& c, const 
     switch (row_blocks(tile.nrows)) {
       case 1: g1_body<1, 2, 2>(p, c, tile, nt, red, pre); break;
       case 2: g1_body<2, 2, 2>(p, c, tile, nt, red, pre); break;
-      default: g1_body<4, KBK ? 2 : 1, 2>(p, c, tile, nt, red, pre); break;
+      default: g1_body<4, 2, 2>(p, c, tile, nt, red, pre); break;
     }
     return;
   }
@@ -1259,6 +1259,7 @@ __device__ __forceinline__ bool wait_rows_done(const MoeParams& p, const Ctx& c,
   return fail == 0;
 }
 
+template <bool WG>
 __device__ __forceinline__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G,
                               const LocalRoute* lr) {
   if (i0 >= n) return;
@@ -1300,7 +1301,7 @@ __device__ __forceinline__ void run_g1_static(const MoeParams& p, const Ctx& c, 
     uint32_t nxt_f[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) nxt_f[b] = i + G < n ? row_perm(p, nxt, b, lr) : 0u;
-    task_g1(p, c, cur, rt, nt, red, cur_f);
+    task_g1<false, WG>(p, c, cur, rt, nt, red, cur_f);
     // wave 0 wrote the tile: drain its stores, then notify.  The drain is
     // outside the notify branch so that, after the branch, only the notify
     // is in flight and the prefetched registers need no further wait.
@@ -1400,6 +1401,7 @@ __device__ __forceinline__ GTask gtask(const Ctx& c, int i, int nG1) {
 // I/16) for G2; its state is fetched one tile ahead, the row-tile descriptor
 // two ahead and the claim three ahead.  Returns false when a wait gave up
 // (the launch is aborting).
+template <bool WG>
 __device__ __forceinline__ bool run_g_ordered(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q, int nG1, uint32_t* sk,
                               const LocalRoute* lr) {
   const int n = q.n;
@@ -1456,7 +1458,7 @@ __device__ __forceinline__ bool run_g_ordered(const MoeParams& p, const Ctx& c, 
 #pragma unroll
     for (int b = 0; b < 4; ++b) nxt_f[b] = (nxt < n && !tn.g2) ? row_perm(p, rn, b, lr) : 0u;
     if (!tc.g2) {
-      task_g1(p, c, rc, tc.rt, tc.nt, red, cur_f);
+      task_g1<false, WG>(p, c, rc, tc.rt, tc.nt, red, cur_f);
     } else {
       task_g2(p, c, rc, tc.rt, tc.nt, red);
     }
@@ -1506,6 +1508,7 @@ __device__ __forceinline__ bool run_g_ordered(const MoeParams& p, const Ctx& c, 
 // claim's result to the other threads through sk[0] and an LDS barrier.
 // Deadlock freedom as in run_g_ordered: a workgroup's tiles come in
 // ascending index order, every G1 tile below every G2 tile.
+template <bool WG>
 __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q,
                                                     int nG1, uint32_t* sk, const LocalRoute* lr) {
   const int n = q.n;
@@ -1560,7 +1563,7 @@ __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ct
       for (int b = 0; b < 4; ++b) nxt_f[b] = tn.g2 ? 0u : row_perm(p, rn, b, lr);
     }
     if (!tc.g2) {
-      task_g1(p, c, rc, tc.rt, tc.nt, red, cur_f);
+      task_g1<false, WG>(p, c, rc, tc.rt, tc.nt, red, cur_f);
     } else {
       task_g2(p, c, rc, tc.rt, tc.nt, red);
     }
@@ -1614,7 +1617,7 @@ __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ct
 // events produced by earlier phases, so with every workgroup resident no
 // wait can be circular and the schedule cannot deadlock.  Task counts of the
 // phases after S are read from S's output (data-dependent instantiation).
-template <int MODE>
+template <int MODE, bool WG>
 __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh) {
   const int G = gridDim.x, w = blockIdx.x;
   float* red = reinterpret_cast<float*>(smem);
@@ -1699,17 +1702,17 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   if (w >= Gt) return;
   if (MODE == MODE_ORDERED) {
     const ClaimQ q{c.set + W_CLAIM_G1 + grp * 32, grp, ngrp, nG1 + nG2, local ? 2 * G : 0};
-    if (lr ? !run_g_ordered_local(p, c, red, q, nG1, sh.claim, lr) : !run_g_ordered(p, c, red, q, nG1, sh.claim, lr))
+    if (lr ? !run_g_ordered_local<WG>(p, c, red, q, nG1, sh.claim, lr) : !run_g_ordered<WG>(p, c, red, q, nG1, sh.claim, lr))
       return;
     off += nG1 + nG2;
   } else {
   if (EV) {
-    run_g1_static(p, c, red, first_of(w, off, Gt), nG1, Gt, lr);
+    run_g1_static<WG>(p, c, red, first_of(w, off, Gt), nG1, Gt, lr);
   } else {
     for (int i = first_of(w, off, Gt); i < nG1; i += Gt) {
       const int rt = i / c.nN1;
       if (tr) tw = ts = now_ticks();
-      task_g1(p, c, load_rowtile(p, rt), rt, i % c.nN1, red);
+      task_g1<false, WG>(p, c, load_rowtile(p, rt), rt, i % c.nN1, red);
       if (tr) tb = now_ticks();
       dbg_task(p, TT_G1);
       trace_task(p, TT_G1, rt, i % c.nN1, tw, ts, tb);
@@ -1841,7 +1844,11 @@ __device__ __forceinline__ void run_dynamic(const MoeParams& p, const Ctx& c, ui
 // by the previous launch) and zeroes set[1 - (epoch & 1)] for the next one;
 // the last workgroup to finish advances the epoch.  No host memset, no host
 // state: the workspace is self-resetting, also after an aborted launch.
-template <int MODE>
+// WG: the variant that holds the wide G1 tiles (launched when T * k selects
+// them); the other variant holds the narrow tiles only, so that small
+// batches run code that carries none of the wide tiles' register pressure.
+// Both come from the one code object; T stays a kernel argument.
+template <int MODE, bool WG>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 moe_persistent(MoeParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -1857,13 +1864,14 @@ moe_persistent(MoeParams p) {
        i += (int64_t)gridDim.x * kThreads)
     other[i] = 0u;
   Ctx c = make_ctx(p, set);
-  if (MODE == MODE_DYNAMIC) {
-    c.bn1 = kBN1;  // the dynamic schedule runs the narrow G1 tiles only
+  if (!WG) {  // the narrow variant (and the dynamic schedule) runs narrow G1 tiles
+    c.bn1 = kBN1;
     c.nN1 = p.I / kBN1;
-    run_dynamic(p, c, smem, sh);
-  } else {
-    run_lists<MODE>(p, c, smem, sh);
   }
+  if (MODE == MODE_DYNAMIC)
+    run_dynamic(p, c, smem, sh);
+  else
+    run_lists<MODE, WG>(p, c, smem, sh);
   wg_publish();
   if (threadIdx.x == 0) {
     const uint32_t st = ld_relaxed(c.status) & ~ST_ABORT;
@@ -1910,20 +1918,32 @@ __global__ void __launch_bounds__(kThreads) kbk_combine(MoeParams p) {
 }
 
 // ------------------------------------------------------- host launchers --
+// The variant a launch of T tokens runs: the wide G1 tiles from T * k on.
+static bool wide_g1(const MoeParams& p) { return g1_cols(p.T, p.k) > kBN1; }
+
+template <int MODE>
+static void launch_variant(const MoeParams& p, bool wide, int grid, int lds_bytes, hipStream_t s) {
+  if (wide)
+    hipLaunchKernelGGL((moe_persistent<MODE, true>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+  else
+    hipLaunchKernelGGL((moe_persistent<MODE, false>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+}
+
 int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool wide = wide_g1(p);
   switch (sched) {
     case ETC_SCHED_STATIC:
-      hipLaunchKernelGGL((moe_persistent<MODE_STATIC>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+      launch_variant<MODE_STATIC>(p, wide, grid, lds_bytes, s);
       break;
     case ETC_SCHED_DYNAMIC:
-      hipLaunchKernelGGL((moe_persistent<MODE_DYNAMIC>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+      hipLaunchKernelGGL((moe_persistent<MODE_DYNAMIC, false>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
       break;
     case ETC_SCHED_BARRIER:
-      hipLaunchKernelGGL((moe_persistent<MODE_BARRIER>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+      launch_variant<MODE_BARRIER>(p, wide, grid, lds_bytes, s);
       break;
     case ETC_SCHED_ORDERED:
-      hipLaunchKernelGGL((moe_persistent<MODE_ORDERED>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+      launch_variant<MODE_ORDERED>(p, wide, grid, lds_bytes, s);
       break;
     default:
       return (int)hipErrorInvalidValue;
@@ -1931,20 +1951,33 @@ int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes
   return (int)hipGetLastError();
 }
 
+// Workgroups per CU that stay resident: the smaller of the two variants'
+// (the grid must be resident whichever variant a launch runs).
+template <int MODE>
+static hipError_t occupancy_both(int* blocks_per_cu, int lds_bytes) {
+  int a = 0, b = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, moe_persistent<MODE, false>, kThreads, lds_bytes);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, moe_persistent<MODE, true>, kThreads, lds_bytes);
+  *blocks_per_cu = a < b ? a : b;
+  return e;
+}
+
 int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu) {
   hipError_t e;
   switch (sched) {
     case ETC_SCHED_STATIC:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_STATIC>, kThreads, lds_bytes);
+      e = occupancy_both<MODE_STATIC>(blocks_per_cu, lds_bytes);
       break;
     case ETC_SCHED_DYNAMIC:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_DYNAMIC>, kThreads, lds_bytes);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_DYNAMIC, false>, kThreads,
+                                                       lds_bytes);
       break;
     case ETC_SCHED_BARRIER:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_BARRIER>, kThreads, lds_bytes);
+      e = occupancy_both<MODE_BARRIER>(blocks_per_cu, lds_bytes);
       break;
     case ETC_SCHED_ORDERED:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_ORDERED>, kThreads, lds_bytes);
+      e = occupancy_both<MODE_ORDERED>(blocks_per_cu, lds_bytes);
       break;
     default:
       return (int)hipErrorInvalidValue;
