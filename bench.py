@@ -83,7 +83,7 @@ def copy_calibration(mib, steps):
                       "GBps": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}))
 
 
-TASK_NAMES = {1: "R", 2: "K", 3: "S", 4: "D", 5: "G1", 6: "G2", 7: "C"}
+TASK_NAMES = {1: "R", 2: "K", 3: "S", 4: "D", 5: "G1", 6: "G2", 7: "C", 8: "L"}  # L: LDS routing tables
 
 
 def tile_rows(counts, bm=64):

@@ -48,7 +48,8 @@ constexpr int kLocalTiles = kLocalRows / 64 + 256 + 16;
 constexpr uint32_t kDefaultWatchdogUs = 2000000u;
 
 // task types (queue descriptors carry them in bits 60..63; 0 = empty slot)
-enum TaskType : int { TT_R = 1, TT_K = 2, TT_S = 3, TT_D = 4, TT_G1 = 5, TT_G2 = 6, TT_C = 7 };
+enum TaskType : int { TT_R = 1, TT_K = 2, TT_S = 3, TT_D = 4, TT_G1 = 5, TT_G2 = 6, TT_C = 7,
+                      TT_L = 8 /* trace only: a workgroup's LDS routing tables */ };
 
 // ---- counter set (u32 words) ------------------------------------------------
 // Words that many workgroups poll or update each sit on their own 128-byte

@@ -1677,9 +1677,13 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   __shared__ LocalRoute lroute;
   const LocalRoute* lr = nullptr;
   if (local) {
+    if (tr) tw = now_ticks();
     if (!wg_wait(c.set + W_EV_ROUTE, (uint32_t)c.nK, c.status, c.budget)) return;
+    if (tr) ts = now_ticks();
     nrt = task_scan<true>(p, c, smem, &lroute);
     lr = &lroute;
+    if (tr) tb = now_ticks();
+    trace_task(p, TT_L, nrt, 0, tw, ts, tb);
   } else if (EV) {
     if (threadIdx.x == 0) {
       uint32_t v = 0;

@@ -194,7 +194,9 @@ typedef struct {
  * perturbs the timing); records past per_wg are dropped, unused ones stay
  * zero.  Words 1 and 2 receive per_wg and the grid size.  Record r occupies
  * words [16 + 8r, 16 + 8r + 8), workgroup w's records start at r = w*per_wg:
- *   workgroup | task type << 24 (type 1..7 = R, K, S, D, G1, G2, C), task
+ *   workgroup | task type << 24 (type 1..7 = R, K, S, D, G1, G2, C; type 8 =
+ *   the routing tables a workgroup rebuilds in its LDS for a small batch,
+ *   waiting on the route event), task
  *   index a, b, then wall-clock ticks: before the task's wait (low, high 32
  *   bits), and the low 32 bits after the wait, after the task body, and after
  *   its notifies.  Ticks are those of the device's constant wall clock
