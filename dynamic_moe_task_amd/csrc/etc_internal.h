@@ -27,8 +27,11 @@ constexpr int kRouterEL = 16;      //     wave, so that fewer, longer R tasks co
 __host__ __device__ inline int router_experts(int T) { return T > kRouterLargeT ? kRouterEL : kRouterE; }
 constexpr int kBM = 64;         // grouped-GEMM row tile (up to four 16-row MFMA blocks)
 constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile ...
-constexpr int kWideG1Rows = 2048;  // ... and twice that from T * k routed rows on
-__host__ __device__ inline int g1_cols(int T, int k) { return T * k >= kWideG1Rows ? 2 * kBN1 : kBN1; }
+constexpr int kWideG1Rows = 2048;  // ... and from T * k routed rows on four times that
+// (column-split tiles; H a multiple of 128, else the narrow tiles stay)
+__host__ __device__ inline int g1_cols(int T, int k, int H) {
+  return (T * k >= kWideG1Rows && H % 128 == 0) ? 4 * kBN1 : kBN1;
+}
 constexpr int kBN2 = 64;        // G2: output columns per tile
 constexpr int kCB2 = kBN2 / 16;  // G2: 16-column MFMA blocks per tile
 constexpr int kCombineT = 2;    // C task: tokens per task
@@ -140,7 +143,11 @@ inline int64_t scan_lds_bytes(int E, int T_max) {
 }
 // G2: cross-wave reduction buffer (4 waves x 4 blocks x 256 fp32) plus the
 // bf16 staging of the kBM x 64 output tile
-constexpr int64_t kGemmLdsBytes = 4 * kCB2 * 256 * 4 + kBM * kBN2 * 2;
+// G tasks' LDS: the K-split bodies' reduction and output stage, or the
+// column-split G1 body's two staged A chunks (64 rows of 128 k, padded)
+constexpr int64_t kGemmLdsBytes = (4 * kCB2 * 256 * 4 + kBM * kBN2 * 2) > 2 * 64 * (128 * 2 + 16)
+                                      ? (4 * kCB2 * 256 * 4 + kBM * kBN2 * 2)
+                                      : 2 * 64 * (128 * 2 + 16);
 
 struct MoeParams {
   const uint16_t* x;

@@ -142,7 +142,7 @@ __device__ __forceinline__ Ctx make_ctx(const MoeParams& p, uint32_t* set) {
   c.nR = c.nTT * c.nET;
   c.nK = c.nTT;
   c.nC = (p.T + kCombineT - 1) / kCombineT;
-  c.bn1 = g1_cols(p.T, p.k);
+  c.bn1 = g1_cols(p.T, p.k, p.H);
   c.nN1 = p.I / c.bn1;
   c.nN2 = p.H / kBN2;
   c.budget = p.budget;
@@ -898,6 +898,113 @@ __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const 
   }
 }
 
+// G1 for large batches, 64-column tiles (c.bn1 = 64): the four waves split
+// the columns instead of K.  Wave w owns gate columns nt * 64 + 16 w .. + 16
+// and the same up columns over all of H, so it holds complete dot products
+// (no cross-wave reduction).  The tile's A rows (up to 64 gathered x rows)
+// are shared through LDS: they are staged 128 k at a time (wave b stages
+// row block b, with the row's token from `pre`), double buffered, so each x
+// row is read from memory once per 64 columns.  Rows are padded to 272
+// bytes so that the 16 rows of an MFMA fragment read fall in distinct
+// banks.  The next chunk's A rows and weights are loaded while the current
+// chunk multiplies; the barrier that ends a chunk orders LDS only.
+constexpr int kCsKC = 128;                  // k per staged chunk (4 MFMA k-steps)
+constexpr int kCsRowB = kCsKC * 2 + 16;     // bytes per staged row
+template <int NB>
+__device__ __forceinline__ void g1_cs_body(const MoeParams& p, const Ctx& c, const RowTile tile, int nt, float* red,
+                                           const uint32_t* pre) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int m = lane & 15, kg = lane >> 4;
+  const int H = c.H, I = c.I;
+  const int nch = H / kCsKC;
+  uint8_t* lds = reinterpret_cast<uint8_t*>(red);  // two [64][kCsRowB] A buffers, then the output stage
+  // A staging: wave b (< NB) loads row block b; lane (m, kg) loads 16-byte
+  // column groups kg, kg + 4, kg + 8, kg + 12 of row 16 b + m
+  const bool stager = wv < NB;
+  const int srow = wv * 16 + m;
+  // this wave's row block's entry of pre[], blended with masks (an indexed
+  // pick would put the array on the stack)
+  const uint32_t f = (pre[0] & (0u - (uint32_t)(wv == 0))) | (pre[1] & (0u - (uint32_t)(wv == 1))) |
+                     (pre[2] & (0u - (uint32_t)(wv == 2))) | (pre[3] & (0u - (uint32_t)(wv == 3)));
+  const int stok = (stager && srow < tile.nrows) ? (int)(f / (uint32_t)c.k) : 0;  // rows past the count: any row
+  const uint16_t* sa = p.x + (size_t)stok * H + kg * 8;
+  const uint16_t* pg = p.w13 + ((size_t)tile.e * 2 * I + (size_t)nt * 64 + wv * 16 + m) * H + kg * 8;
+  const uint16_t* pu = pg + (size_t)I * H;
+  f32x4_t accg[NB], accu[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) accg[b] = accu[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  u32x4_t ar[4], bc[4][2], bn[4][2];
+  auto load_a = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ar[i] = ld4(sa + j * kCsKC + i * 32);
+  };
+  auto store_a = [&](int buf) {
+    uint8_t* dst = lds + buf * 64 * kCsRowB + srow * kCsRowB + kg * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(dst + i * 64) = ar[i];
+  };
+  auto load_b = [&](int j, u32x4_t (&bb)[4][2]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bb[s][0] = ld4(pg + j * kCsKC + s * 32);
+      bb[s][1] = ld4(pu + j * kCsKC + s * 32);
+    }
+  };
+  if (stager) load_a(0);
+  load_b(0, bc);
+  if (stager) store_a(0);
+  lds_barrier();
+  for (int j = 0; j < nch; ++j) {
+    const bool more = j + 1 < nch;
+    if (more) {
+      if (stager) load_a(j + 1);
+      load_b(j + 1, bn);
+    }
+    const uint8_t* src = lds + (j & 1) * 64 * kCsRowB + m * kCsRowB + kg * 16;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(src + b * 16 * kCsRowB + s * 64);
+        accg[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a), as_bf(bc[s][0]), accg[b], 0, 0, 0);
+        accu[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a), as_bf(bc[s][1]), accu[b], 0, 0, 0);
+      }
+    }
+    if (more && stager) store_a((j + 1) & 1);
+    lds_barrier();  // the next chunk is staged; this chunk's buffer is free again
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bc[s][0] = bn[s][0];
+      bc[s][1] = bn[s][1];
+    }
+  }
+  // SwiGLU into the output stage [64 rows][64 cols] bf16 (the A buffers are
+  // free: every wave passed the last chunk's barrier)
+  uint16_t* stage = reinterpret_cast<uint16_t*>(lds);
+  const int col = wv * 16 + (lane & 15);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float g = accg[b][i], u = accu[b][i];
+      stage[(b * 16 + 4 * (lane >> 4) + i) * 64 + col] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u);
+    }
+  __syncthreads();
+  // wave 0 alone writes the tile (rows x 128 bytes, 16-byte chunks), so only
+  // wave 0 has stores to drain before the notify
+  if (threadIdx.x < 64) {
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const int idx = threadIdx.x + 64 * h;
+      const int r = idx >> 3, q8 = idx & 7;
+      if (r < tile.nrows) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * 64 + q8 * 8);
+        co_st128(r_hh(p), (uint32_t)(((size_t)(tile.r0 + r) * I + nt * 64 + q8 * 8) * 2), v);
+      }
+    }
+  }
+}
+
 // k-steps per load batch (U) by row blocks, measured on MI355X: short
 // batches stream better in the persistent kernel (two workgroups per CU);
 // the separate G kernels of the kernel-by-kernel launch keep longer batches
@@ -909,11 +1016,16 @@ template <bool KBK = false, bool WIDE = true>
 __device__ __forceinline__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt, float* red,
                         const uint32_t* pre = nullptr) {
   (void)rt;
-  if (WIDE && c.bn1 == 2 * kBN1) {
+  if (WIDE && c.bn1 == 4 * kBN1) {
+    // column-split tiles need their row tokens per row block: load them
+    // here when the caller has not
+    uint32_t f[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) f[b] = pre ? pre[b] : row_perm(p, tile, b);
     switch (row_blocks(tile.nrows)) {
-      case 1: g1_body<1, 2, 2>(p, c, tile, nt, red, pre); break;
-      case 2: g1_body<2, 2, 2>(p, c, tile, nt, red, pre); break;
-      default: g1_body<4, 2, 2>(p, c, tile, nt, red, pre); break;
+      case 1: g1_cs_body<1>(p, c, tile, nt, red, f); break;
+      case 2: g1_cs_body<2>(p, c, tile, nt, red, f); break;
+      default: g1_cs_body<4>(p, c, tile, nt, red, f); break;
     }
     return;
   }
@@ -1900,7 +2012,10 @@ __global__ void __launch_bounds__(kThreads) kbk_scan(MoeParams p) {
   task_scan(p, c, smem);
 }
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) kbk_g1(MoeParams p) {
-  __shared__ float red[4 * kCB2 * 256 + kBM * kBN2 / 2];
+  // the larger of the K-split bodies' reduction and stage and the
+  // column-split body's two staged A buffers
+  __shared__ float red[(2 * 64 * kCsRowB) / 4 > 4 * kCB2 * 256 + kBM * kBN2 / 2 ? (2 * 64 * kCsRowB) / 4
+                                                                                 : 4 * kCB2 * 256 + kBM * kBN2 / 2];
   const Ctx c = make_ctx(p, nullptr);
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN1) return;
@@ -1923,7 +2038,7 @@ __global__ void __launch_bounds__(kThreads) kbk_combine(MoeParams p) {
 
 // ------------------------------------------------------- host launchers --
 // The variant a launch of T tokens runs: the wide G1 tiles from T * k on.
-static bool wide_g1(const MoeParams& p) { return g1_cols(p.T, p.k) > kBN1; }
+static bool wide_g1(const MoeParams& p) { return g1_cols(p.T, p.k, p.H) > kBN1; }
 
 template <int MODE>
 static void launch_variant(const MoeParams& p, bool wide, int grid, int lds_bytes, hipStream_t s) {
@@ -1996,7 +2111,7 @@ int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream) {
   const int nC = (p.T + kCombineT - 1) / kCombineT;
   const int64_t rows = (int64_t)p.T * p.k;
   const int64_t max_rt = (rows + kBM - 1) / kBM + (rows < p.E ? rows : p.E);
-  const int nN1 = p.I / g1_cols(p.T, p.k), nN2 = p.H / kBN2;
+  const int nN1 = p.I / g1_cols(p.T, p.k, p.H), nN2 = p.H / kBN2;
   hipLaunchKernelGGL(kbk_router, dim3(nTT * nET), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_topk, dim3(nTT), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_scan, dim3(1), dim3(kThreads), lds_bytes, s, p);
