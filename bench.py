@@ -173,7 +173,7 @@ def trace_summary(bufs, T, sched, khz, stream_ptr, records=1 << 16, dump=None, s
         grid = int(raw[2])
         info = B.moe_layer_info(bufs.desc)
         out["tile_mfma_four_block"] = tile_mfma(typ, rec[:, 1], (tb - ts) * us, rows, shape.H, shape.I, grid,
-                                                info.bn1_for(T, shape.k), info.bn2)
+                                                info.bn1_for(T, shape.k), info.bn2_for(T, shape.k))
     return out
 
 

@@ -34,6 +34,11 @@ __host__ __device__ inline int g1_cols(int T, int k, int H) {
 }
 constexpr int kBN2 = 64;        // G2: output columns per tile
 constexpr int kCB2 = kBN2 / 16;  // G2: 16-column MFMA blocks per tile
+// G2 output columns per tile: twice kBN2 (column-split tiles) from the same
+// batch on when I is a multiple of 128
+__host__ __device__ inline int g2_cols(int T, int k, int I) {
+  return (T * k >= kWideG1Rows && I % 128 == 0) ? 2 * kBN2 : kBN2;
+}
 constexpr int kCombineT = 2;    // C task: tokens per task
 constexpr int kEvStride = 32;   // words between event elements (one 128-byte line each)
 constexpr int kMaxK = 16;

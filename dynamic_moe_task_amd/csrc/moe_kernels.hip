@@ -127,6 +127,7 @@ struct Ctx {
   uint64_t* queue;
   int T, H, E, k, I;
   int bn1;  // G1 gate (and up) columns per tile, chosen per launch from T
+  int bn2;  // G2 output columns per tile, chosen per launch from T
   int nTT, nET, nR, nK, nC, nN1, nN2;
   uint64_t budget;  // watchdog of one wait, wall-clock ticks
 };
@@ -144,7 +145,8 @@ __device__ __forceinline__ Ctx make_ctx(const MoeParams& p, uint32_t* set) {
   c.nC = (p.T + kCombineT - 1) / kCombineT;
   c.bn1 = g1_cols(p.T, p.k, p.H);
   c.nN1 = p.I / c.bn1;
-  c.nN2 = p.H / kBN2;
+  c.bn2 = g2_cols(p.T, p.k, p.I);
+  c.nN2 = p.H / c.bn2;
   c.budget = p.budget;
   return c;
 }
@@ -1118,9 +1120,105 @@ __device__ __forceinline__ void g2_body(const MoeParams& p, const Ctx& c, const 
   }
 }
 
-template <bool KBK = false>
+// G2 for large batches, 128-column tiles (c.bn2 = 128): as g1_cs_body, the
+// waves split the columns (wave w owns output columns nt2 * 128 + 32 w ..
+// + 32, two MFMA column blocks, over all of I) and share the tile's Hmid
+// rows through LDS, staged 128 k at a time with device-coherent loads (G1
+// tasks of other workgroups wrote them), so each Hmid row is read once per
+// 128 output columns instead of 64.
+template <int NB>
+__device__ __forceinline__ void g2_cs_body(const MoeParams& p, const Ctx& c, const RowTile tile, int nt2, float* red) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int m = lane & 15, kg = lane >> 4;
+  const int H = c.H, I = c.I;
+  const int nch = I / kCsKC;
+  uint8_t* lds = reinterpret_cast<uint8_t*>(red);  // two [64][kCsRowB] A buffers, then the output stage
+  const rsrc_t rh = r_hh(p);
+  const bool stager = wv < NB;
+  const int srow = wv * 16 + m;
+  const int grow = tile.r0 + (srow < tile.nrows ? srow : 0);  // rows past the count: any row of the tile
+  const uint32_t sa = (uint32_t)(((size_t)grow * I + kg * 8) * 2);
+  const uint16_t* pb = p.w2 + ((size_t)tile.e * H + (size_t)nt2 * 128 + wv * 32 + m) * I + kg * 8;
+  const size_t cbs = (size_t)16 * I;  // the wave's second 16-column block of Wd
+  f32x4_t acc[NB][2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b][0] = acc[b][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  u32x4_t ar[4], bc[4][2], bn[4][2];
+  auto load_a = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ar[i] = co_ld128(rh, sa + (uint32_t)(j * kCsKC + i * 32) * 2u);
+  };
+  auto store_a = [&](int buf) {
+    uint8_t* dst = lds + buf * 64 * kCsRowB + srow * kCsRowB + kg * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(dst + i * 64) = ar[i];
+  };
+  auto load_b = [&](int j, u32x4_t (&bb)[4][2]) {
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      bb[s2][0] = ld4(pb + j * kCsKC + s2 * 32);
+      bb[s2][1] = ld4(pb + cbs + j * kCsKC + s2 * 32);
+    }
+  };
+  if (stager) load_a(0);
+  load_b(0, bc);
+  if (stager) store_a(0);
+  lds_barrier();
+  for (int j = 0; j < nch; ++j) {
+    const bool more = j + 1 < nch;
+    if (more) {
+      if (stager) load_a(j + 1);
+      load_b(j + 1, bn);
+    }
+    const uint8_t* src = lds + (j & 1) * 64 * kCsRowB + m * kCsRowB + kg * 16;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(src + b * 16 * kCsRowB + s2 * 64);
+        acc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a), as_bf(bc[s2][0]), acc[b][0], 0, 0, 0);
+        acc[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a), as_bf(bc[s2][1]), acc[b][1], 0, 0, 0);
+      }
+    }
+    if (more && stager) store_a((j + 1) & 1);
+    lds_barrier();  // the next chunk is staged; this chunk's buffer is free again
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      bc[s2][0] = bn[s2][0];
+      bc[s2][1] = bn[s2][1];
+    }
+  }
+  // Y in bf16 into the output stage [64 rows][128 cols] (the A buffers are free)
+  uint16_t* stage = reinterpret_cast<uint16_t*>(lds);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        stage[(b * 16 + 4 * (lane >> 4) + i) * 128 + wv * 32 + q * 16 + (lane & 15)] = (uint16_t)f2bf(acc[b][q][i]);
+  __syncthreads();
+  // wave 0 alone writes the tile (rows x 256 bytes, 16-byte chunks)
+  if (threadIdx.x < 64) {
+    for (int idx = threadIdx.x; idx < tile.nrows * 16; idx += 64) {
+      const int r = idx >> 4, q8 = idx & 15;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * 128 + q8 * 8);
+      co_st128(r_y(p), (uint32_t)(((size_t)(tile.r0 + r) * H + nt2 * 128 + q8 * 8) * 2), v);
+    }
+  }
+}
+
+template <bool KBK = false, bool WIDE = true>
 __device__ __forceinline__ void task_g2(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt2, float* red) {
   (void)rt;
+  if (WIDE && c.bn2 == 2 * kBN2) {
+    switch (row_blocks(tile.nrows)) {
+      case 1: g2_cs_body<1>(p, c, tile, nt2, red); break;
+      case 2: g2_cs_body<2>(p, c, tile, nt2, red); break;
+      default: g2_cs_body<4>(p, c, tile, nt2, red); break;
+    }
+    return;
+  }
   switch (row_blocks(tile.nrows)) {
     case 1: g2_body<1, 2>(p, c, tile, nt2, red); break;
     case 2: g2_body<2, 2>(p, c, tile, nt2, red); break;
@@ -1431,6 +1529,7 @@ __device__ __forceinline__ void run_g1_static(const MoeParams& p, const Ctx& c, 
   }
 }
 
+template <bool WG>
 __device__ __forceinline__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G,
                               const LocalRoute* lr) {
   if (i0 >= n) return;
@@ -1453,7 +1552,7 @@ __device__ __forceinline__ void run_g2_static(const MoeParams& p, const Ctx& c, 
     uint32_t nxt_arr = 0;
     if (threadIdx.x == 0 && i + G < n) nxt_arr = ld_relaxed(ev_h(p, c, (i + G) / c.nN2));
     // combine tile of each row's token (wave 0, one row a lane)
-    task_g2(p, c, cur, rt, nt, red);
+    task_g2<false, WG>(p, c, cur, rt, nt, red);
     __builtin_amdgcn_s_waitcnt(0);  // wave 0 wrote the rows: drain, then notify (as in G1)
     if (threadIdx.x == 0) notify_fast(p, c, ev_y(p, c, rt), (uint32_t)c.nN2);
     if (tr) tb = now_ticks();
@@ -1572,7 +1671,7 @@ __device__ __forceinline__ bool run_g_ordered(const MoeParams& p, const Ctx& c, 
     if (!tc.g2) {
       task_g1<false, WG>(p, c, rc, tc.rt, tc.nt, red, cur_f);
     } else {
-      task_g2(p, c, rc, tc.rt, tc.nt, red);
+      task_g2<false, WG>(p, c, rc, tc.rt, tc.nt, red);
     }
     __builtin_amdgcn_s_waitcnt(0);  // wave 0 wrote the tile: drain, then notify (see run_g1_static)
     if (threadIdx.x == 0) {
@@ -1677,7 +1776,7 @@ __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ct
     if (!tc.g2) {
       task_g1<false, WG>(p, c, rc, tc.rt, tc.nt, red, cur_f);
     } else {
-      task_g2(p, c, rc, tc.rt, tc.nt, red);
+      task_g2<false, WG>(p, c, rc, tc.rt, tc.nt, red);
     }
     __builtin_amdgcn_s_waitcnt(0);  // wave 0 wrote the tile: drain, then notify (see run_g1_static)
     if (threadIdx.x == 0) {
@@ -1837,12 +1936,12 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   off += nG1;
   if (!EV && !grid_barrier(c, Gt)) return;
   if (EV) {
-    run_g2_static(p, c, red, first_of(w, off, Gt), nG2, Gt, lr);
+    run_g2_static<WG>(p, c, red, first_of(w, off, Gt), nG2, Gt, lr);
   } else {
     for (int i = first_of(w, off, Gt); i < nG2; i += Gt) {
       const int rt = i / c.nN2;
       if (tr) tw = ts = now_ticks();
-      task_g2(p, c, load_rowtile(p, rt), rt, i % c.nN2, red);
+      task_g2<false, WG>(p, c, load_rowtile(p, rt), rt, i % c.nN2, red);
       if (tr) tb = now_ticks();
       dbg_task(p, TT_G2);
       trace_task(p, TT_G2, rt, i % c.nN2, tw, ts, tb);
@@ -1936,7 +2035,7 @@ __device__ __forceinline__ void run_dynamic(const MoeParams& p, const Ctx& c, ui
         trace_task(p, TT_G1, a, b, tw, ts, tb);
         break;
       case TT_G2:
-        task_g2(p, c, load_rowtile(p, a), a, b, red);
+        task_g2<false, false>(p, c, load_rowtile(p, a), a, b, red);
         if (tr) tb = now_ticks();
         dbg_task(p, TT_G2);
         after_g2<MODE_DYNAMIC>(p, c, a, sh);
@@ -1980,9 +2079,11 @@ moe_persistent(MoeParams p) {
        i += (int64_t)gridDim.x * kThreads)
     other[i] = 0u;
   Ctx c = make_ctx(p, set);
-  if (!WG) {  // the narrow variant (and the dynamic schedule) runs narrow G1 tiles
+  if (!WG) {  // the narrow variant (and the dynamic schedule) runs narrow G tiles
     c.bn1 = kBN1;
     c.nN1 = p.I / kBN1;
+    c.bn2 = kBN2;
+    c.nN2 = p.H / kBN2;
   }
   if (MODE == MODE_DYNAMIC)
     run_dynamic(p, c, smem, sh);
@@ -2023,7 +2124,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   task_g1<true>(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN1, red);
 }
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) kbk_g2(MoeParams p) {
-  __shared__ float red[4 * kCB2 * 256 + kBM * kBN2 / 2];
+  __shared__ float red[(2 * 64 * kCsRowB) / 4 > 4 * kCB2 * 256 + kBM * kBN2 / 2 ? (2 * 64 * kCsRowB) / 4
+                                                                                 : 4 * kCB2 * 256 + kBM * kBN2 / 2];
   const Ctx c = make_ctx(p, nullptr);
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN2) return;
@@ -2038,7 +2140,7 @@ __global__ void __launch_bounds__(kThreads) kbk_combine(MoeParams p) {
 
 // ------------------------------------------------------- host launchers --
 // The variant a launch of T tokens runs: the wide G1 tiles from T * k on.
-static bool wide_g1(const MoeParams& p) { return g1_cols(p.T, p.k, p.H) > kBN1; }
+static bool wide_g1(const MoeParams& p) { return g1_cols(p.T, p.k, p.H) > kBN1 || g2_cols(p.T, p.k, p.I) > kBN2; }
 
 template <int MODE>
 static void launch_variant(const MoeParams& p, bool wide, int grid, int lds_bytes, hipStream_t s) {
@@ -2111,7 +2213,7 @@ int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream) {
   const int nC = (p.T + kCombineT - 1) / kCombineT;
   const int64_t rows = (int64_t)p.T * p.k;
   const int64_t max_rt = (rows + kBM - 1) / kBM + (rows < p.E ? rows : p.E);
-  const int nN1 = p.I / g1_cols(p.T, p.k, p.H), nN2 = p.H / kBN2;
+  const int nN1 = p.I / g1_cols(p.T, p.k, p.H), nN2 = p.H / g2_cols(p.T, p.k, p.I);
   hipLaunchKernelGGL(kbk_router, dim3(nTT * nET), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_topk, dim3(nTT), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_scan, dim3(1), dim3(kThreads), lds_bytes, s, p);

@@ -231,6 +231,7 @@ typedef struct {
   int32_t bn1_large;   /* gate (and up) columns per G1 tile when T*k >=
                           bn1_large_from_rows (bn1 applies below)          */
   int32_t bn1_large_from_rows;
+  int32_t bn2_large;   /* output columns per G2 tile from the same T*k on   */
 } etc_moe_info;
 
 /* Fill `info` for `desc` (host struct).  Queries the device for the grid.
