@@ -234,6 +234,8 @@ EDGE = [
     (512, 128, 16, 8, 128, True, False, 512),  # T * k = 4096: the largest batch with the routing tables in LDS
     (300, 128, 32, 14, 128, True, False, 320), # T * k = 4200: one scan chunk, routing tables in memory
     (12, 128, 64, 8, 256, True, False, 16),    # between one and two G tiles per workgroup of the grid
+    (256, 384, 32, 8, 640, True, True, 256),   # column-split G tiles over 3 (G1) and 5 (G2) staged chunks
+    (300, 256, 16, 8, 384, True, False, 320),  # column-split G tiles, 2 (G1) and 3 (G2) chunks, T < T_max
 ]
 
 
