@@ -28,8 +28,7 @@ __host__ __device__ inline int router_experts(int T) { return T > kRouterLargeT 
 constexpr int kBM = 64;         // grouped-GEMM row tile (up to four 16-row MFMA blocks)
 constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile ...
 constexpr int kWideG1Rows = 2048;  // ... and from T * k routed rows on four times that
-// (column-split tiles, which need H to be a multiple of 128, as the ABI
-// requires of H and I)
+// (column-split tiles; H a multiple of 128, else the narrow tiles stay)
 __host__ __device__ inline int g1_cols(int T, int k, int H) {
   return (T * k >= kWideG1Rows && H % 128 == 0) ? 4 * kBN1 : kBN1;
 }
