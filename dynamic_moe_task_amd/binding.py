@@ -72,7 +72,8 @@ class MoeInfo(ctypes.Structure):
                 ("grid", ctypes.c_int32), ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("wall_clock_khz", ctypes.c_int32), ("router_experts_large", ctypes.c_int32),
                 ("router_large_from", ctypes.c_int32), ("bn1_large", ctypes.c_int32),
-                ("bn1_large_from_rows", ctypes.c_int32), ("bn2_large", ctypes.c_int32)]
+                ("bn1_large_from_rows", ctypes.c_int32), ("bn2_large", ctypes.c_int32),
+                ("bn1_mid", ctypes.c_int32), ("bn1_mid_from_rows", ctypes.c_int32)]
 
     def router_experts_for(self, T: int) -> int:
         """Experts per router task at batch T."""
@@ -80,7 +81,9 @@ class MoeInfo(ctypes.Structure):
 
     def bn1_for(self, T: int, k: int) -> int:
         """Gate (and up) columns per G1 tile at batch T, top-k k."""
-        return self.bn1_large if T * k >= self.bn1_large_from_rows else self.bn1
+        if T * k >= self.bn1_large_from_rows:
+            return self.bn1_large
+        return self.bn1_mid if T * k >= self.bn1_mid_from_rows else self.bn1
 
     def bn2_for(self, T: int, k: int) -> int:
         """Output columns per G2 tile at batch T, top-k k."""

@@ -340,6 +340,8 @@ extern "C" int moe_layer_info(const etc_moe_desc* d, etc_moe_info* info) {
   info->bn1_large = g1_cols(kWideG1Rows, 1, d->H);
   info->bn1_large_from_rows = kWideG1Rows;
   info->bn2_large = g2_cols(kWideG1Rows, 1, d->I);
+  info->bn1_mid = g1_cols(kMidG1Rows, 1, d->H);
+  info->bn1_mid_from_rows = kMidG1Rows;
   info->bn2 = kBN2;
   info->router_tokens = kRouterT;
   info->router_experts = kRouterE;

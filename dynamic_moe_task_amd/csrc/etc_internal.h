@@ -27,10 +27,11 @@ constexpr int kRouterEL = 16;      //     wave, so that fewer, longer R tasks co
 __host__ __device__ inline int router_experts(int T) { return T > kRouterLargeT ? kRouterEL : kRouterE; }
 constexpr int kBM = 64;         // grouped-GEMM row tile (up to four 16-row MFMA blocks)
 constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile ...
-constexpr int kWideG1Rows = 2048;  // ... and from T * k routed rows on four times that
-// (column-split tiles; H a multiple of 128, else the narrow tiles stay)
+constexpr int kMidG1Rows = 512;    // ... twice that from T * k routed rows on ...
+constexpr int kWideG1Rows = 2048;  // ... and four times that from these on
+// (column-split tiles; H a multiple of 128, as the ABI requires)
 __host__ __device__ inline int g1_cols(int T, int k, int H) {
-  return (T * k >= kWideG1Rows && H % 128 == 0) ? 4 * kBN1 : kBN1;
+  return (T * k >= kWideG1Rows && H % 128 == 0) ? 4 * kBN1 : (T * k >= kMidG1Rows ? 2 * kBN1 : kBN1);
 }
 constexpr int kBN2 = 64;        // G2: output columns per tile
 constexpr int kCB2 = kBN2 / 16;  // G2: 16-column MFMA blocks per tile

@@ -1031,6 +1031,14 @@ __device__ __forceinline__ void task_g1(const MoeParams& p, const Ctx& c, const 
     }
     return;
   }
+  if (c.bn1 == 2 * kBN1) {  // mid-size batches: 32 gate + 32 up columns, K-split
+    switch (row_blocks(tile.nrows)) {
+      case 1: g1_body<1, 2, 2>(p, c, tile, nt, red, pre); break;
+      case 2: g1_body<2, 2, 2>(p, c, tile, nt, red, pre); break;
+      default: g1_body<4, 1, 2>(p, c, tile, nt, red, pre); break;
+    }
+    return;
+  }
   switch (row_blocks(tile.nrows)) {
     case 1: g1_body<1, 4, 1>(p, c, tile, nt, red, pre); break;
     case 2: g1_body<2, 4, 1>(p, c, tile, nt, red, pre); break;
@@ -2079,9 +2087,9 @@ moe_persistent(MoeParams p) {
        i += (int64_t)gridDim.x * kThreads)
     other[i] = 0u;
   Ctx c = make_ctx(p, set);
-  if (!WG) {  // the narrow variant (and the dynamic schedule) runs narrow G tiles
-    c.bn1 = kBN1;
-    c.nN1 = p.I / kBN1;
+  if (!WG) {  // the small-batch variant runs K-split G tiles (the dynamic schedule the narrowest)
+    c.bn1 = MODE == MODE_DYNAMIC ? kBN1 : g1_cols(p.T, p.k, p.H);
+    c.nN1 = p.I / c.bn1;
     c.bn2 = kBN2;
     c.nN2 = p.H / kBN2;
   }
@@ -2140,7 +2148,7 @@ __global__ void __launch_bounds__(kThreads) kbk_combine(MoeParams p) {
 
 // ------------------------------------------------------- host launchers --
 // The variant a launch of T tokens runs: the wide G1 tiles from T * k on.
-static bool wide_g1(const MoeParams& p) { return g1_cols(p.T, p.k, p.H) > kBN1 || g2_cols(p.T, p.k, p.I) > kBN2; }
+static bool wide_g1(const MoeParams& p) { return g1_cols(p.T, p.k, p.H) > 2 * kBN1 || g2_cols(p.T, p.k, p.I) > kBN2; }
 
 template <int MODE>
 static void launch_variant(const MoeParams& p, bool wide, int grid, int lds_bytes, hipStream_t s) {

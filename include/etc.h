@@ -232,6 +232,9 @@ typedef struct {
                           bn1_large_from_rows (bn1 applies below)          */
   int32_t bn1_large_from_rows;
   int32_t bn2_large;   /* output columns per G2 tile from the same T*k on   */
+  int32_t bn1_mid;     /* gate (and up) columns per G1 tile when
+                          bn1_mid_from_rows <= T*k < bn1_large_from_rows  */
+  int32_t bn1_mid_from_rows;
 } etc_moe_info;
 
 /* Fill `info` for `desc` (host struct).  Queries the device for the grid.

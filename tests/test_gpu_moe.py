@@ -102,8 +102,8 @@ def test_event_invariants(qwen_weights, decode_case, sched):
         -(-T // info.router_tokens),                                 # K
         1,                                                           # S
         -(-T // info.dispatch_tokens) if info.dispatch_tokens else 0,  # D (0: fused into G1's row gather)
-        n_rt * (s.I // info.bn1),                                    # G1
-        n_rt * (s.H // info.bn2),                                    # G2
+        n_rt * (s.I // info.bn1_for(T, s.k)),                        # G1
+        n_rt * (s.H // info.bn2_for(T, s.k)),                        # G2
         -(-T // info.combine_tokens),                                # C
     ]
     assert list(dbg[2 * E:2 * E + 7]) == expect
@@ -136,7 +136,7 @@ def test_task_trace(qwen_weights, decode_case, sched):
     n_rt = len(oracle.expected_tiles(ref["exp_indptr"], info.bm))
     T, E = s.T, s.E
     expect = {1: -(-T // info.router_tokens) * -(-E // info.router_experts_for(T)), 2: -(-T // info.router_tokens),
-              3: 1, 4: -(-T // info.dispatch_tokens) if info.dispatch_tokens else 0, 5: n_rt * (s.I // info.bn1), 6: n_rt * (s.H // info.bn2),
+              3: 1, 4: -(-T // info.dispatch_tokens) if info.dispatch_tokens else 0, 5: n_rt * (s.I // info.bn1_for(T, s.k)), 6: n_rt * (s.H // info.bn2_for(T, s.k)),
               7: -(-T // info.combine_tokens)}
     assert {t: int((typ == t).sum()) for t in expect} == expect
     assert wg.max() < info.grid
