@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill_zipf", "tiny"])
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload's layer at this many tokens instead of its own T (diagnostics, "
+                         "e.g. a per-task trace at T=1)")
     ap.add_argument("--sched", default="ordered", choices=list(SCHEDS),
                     help="schedule behind `value` (the others are timed alongside)")
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated over steps")
@@ -364,6 +367,9 @@ def main():
     from dynamic_moe_task_amd import workloads as wl
 
     shape = wl.SHAPES[a.workload]
+    if a.tokens > 0:
+        import dataclasses
+        shape = dataclasses.replace(shape, T=a.tokens, name=f"{shape.name} at T={a.tokens}")
     T = shape.T
     w, X = wl.make_layer(shape, 0)
     torch.cuda.set_device(0)
