@@ -73,10 +73,13 @@ class MoeInfo(ctypes.Structure):
                 ("wall_clock_khz", ctypes.c_int32), ("router_experts_large", ctypes.c_int32),
                 ("router_large_from", ctypes.c_int32), ("bn1_large", ctypes.c_int32),
                 ("bn1_large_from_rows", ctypes.c_int32), ("bn2_large", ctypes.c_int32),
-                ("bn1_mid", ctypes.c_int32), ("bn1_mid_from_rows", ctypes.c_int32)]
+                ("bn1_mid", ctypes.c_int32), ("bn1_mid_from_rows", ctypes.c_int32),
+                ("router_experts_xl", ctypes.c_int32), ("router_xl_from", ctypes.c_int32)]
 
     def router_experts_for(self, T: int) -> int:
         """Experts per router task at batch T."""
+        if T >= self.router_xl_from:
+            return self.router_experts_xl
         return self.router_experts if T <= self.router_large_from else self.router_experts_large
 
     def bn1_for(self, T: int, k: int) -> int:

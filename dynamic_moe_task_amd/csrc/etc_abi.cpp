@@ -346,6 +346,8 @@ extern "C" int moe_layer_info(const etc_moe_desc* d, etc_moe_info* info) {
   info->router_tokens = kRouterT;
   info->router_experts = kRouterE;
   info->router_experts_large = kRouterEL;
+  info->router_experts_xl = kRouterEXL;
+  info->router_xl_from = kRouterXLT;
   info->router_large_from = kRouterLargeT;
   info->dispatch_tokens = 0;  // no dispatch tasks: G1 gathers its rows from x
   info->combine_tokens = kCombineT;

@@ -23,8 +23,12 @@ constexpr int kThreads = 256;   // 4 wave64 per workgroup
 constexpr int kRouterT = 4;     // R task: tokens ...
 constexpr int kRouterE = 4;     //         ... x experts (one expert per wave) up to
 constexpr int kRouterLargeT = 64;  //     T = kRouterLargeT; above it four experts per
-constexpr int kRouterEL = 16;      //     wave, so that fewer, longer R tasks cover E
-__host__ __device__ inline int router_experts(int T) { return T > kRouterLargeT ? kRouterEL : kRouterE; }
+constexpr int kRouterEL = 16;      //     wave, so that fewer, longer R tasks cover E,
+constexpr int kRouterEXL = 32;     //     and eight from T = kRouterXLT on, where even
+constexpr int kRouterXLT = 2048;   //     these fill the grid several times over (a
+__host__ __device__ inline int router_experts(int T) {  // T that the large-batch
+  return T >= kRouterXLT ? kRouterEXL : (T > kRouterLargeT ? kRouterEL : kRouterE);  // variant runs)
+}
 constexpr int kBM = 64;         // grouped-GEMM row tile (up to four 16-row MFMA blocks)
 constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile ...
 constexpr int kMidG1Rows = 512;    // ... twice that from T * k routed rows on ...

@@ -251,7 +251,7 @@ __device__ __forceinline__ void notify_fast(const MoeParams& p, const Ctx& c, ui
 // the bias.  This fixed order is what makes the top-k decision reproducible
 // bit for bit.  A batch of four chunks per lane is loaded before its
 // arithmetic.
-template <int EPW>
+template <int EPW, int U>
 __device__ __forceinline__ void router_body(const MoeParams& p, const Ctx& c, int tt, int et) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int e0 = et * 4 * EPW + wv * EPW;
@@ -267,7 +267,6 @@ __device__ __forceinline__ void router_body(const MoeParams& p, const Ctx& c, in
   const int nchunk = c.H >> 3;
   const uint16_t* xrow = p.x + (size_t)t0 * c.H;
   const uint16_t* wrow = p.wr + (size_t)e0 * c.H;
-  constexpr int U = 4;
   if (ntok == kRouterT && ne == EPW && nchunk % (64 * U) == 0) {
     // full tile: no per-load or per-product predicates.  Per logit the
     // products still go chunk by chunk in ascending order, 8 elements each.
@@ -360,11 +359,20 @@ __device__ __forceinline__ void router_body(const MoeParams& p, const Ctx& c, in
     }
   }
 }
+template <bool XL = true>
 __device__ __forceinline__ void task_router(const MoeParams& p, const Ctx& c, int tt, int et) {
-  if (router_experts(c.T) == kRouterEL)
-    router_body<kRouterEL / 4>(p, c, tt, et);
+  // The tile's experts follow the same rule as the task count (nET); the
+  // eight-experts-a-wave tile exists only where XL is set, and the variant
+  // without it counts its tasks for four experts a wave.  U: 8-element chunks
+  // a lane loads per batch, halved for eight experts a wave to bound the
+  // registers.
+  const int re = router_experts(c.T);
+  if (XL && re == kRouterEXL)
+    router_body<kRouterEXL / 4, 2>(p, c, tt, et);
+  else if (re >= kRouterEL)
+    router_body<kRouterEL / 4, 4>(p, c, tt, et);
   else
-    router_body<kRouterE / 4>(p, c, tt, et);
+    router_body<kRouterE / 4, 4>(p, c, tt, et);
 }
 
 // K: top-k per token (one wave per token): k rounds of a wave-wide arg-max
@@ -1846,7 +1854,7 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   int64_t off = 0;
   for (int i = first_of(w, off, G); i < c.nR; i += G) {
     if (tr) tw = ts = now_ticks();
-    task_router(p, c, i / c.nET, i % c.nET);
+    task_router<WG>(p, c, i / c.nET, i % c.nET);
     if (tr) tb = now_ticks();
     dbg_task(p, TT_R);
     after_router<MODE>(p, c, i / c.nET);
@@ -2014,7 +2022,7 @@ __device__ __forceinline__ void run_dynamic(const MoeParams& p, const Ctx& c, ui
     const int a = (int)desc_a(d), b = (int)desc_b(d);
     switch (desc_type(d)) {
       case TT_R:
-        task_router(p, c, a, b);
+        task_router<false>(p, c, a, b);
         if (tr) tb = now_ticks();
         dbg_task(p, TT_R);
         after_router<MODE_DYNAMIC>(p, c, a);
@@ -2088,6 +2096,8 @@ moe_persistent(MoeParams p) {
     other[i] = 0u;
   Ctx c = make_ctx(p, set);
   if (!WG) {  // the small-batch variant runs K-split G tiles (the dynamic schedule the narrowest)
+    // and no eight-experts-a-wave router tiles
+    if (router_experts(p.T) == kRouterEXL) c.nET = (p.E + kRouterEL - 1) / kRouterEL;
     c.bn1 = MODE == MODE_DYNAMIC ? kBN1 : g1_cols(p.T, p.k, p.H);
     c.nN1 = p.I / c.bn1;
     c.bn2 = kBN2;

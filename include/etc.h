@@ -235,6 +235,8 @@ typedef struct {
   int32_t bn1_mid;     /* gate (and up) columns per G1 tile when
                           bn1_mid_from_rows <= T*k < bn1_large_from_rows  */
   int32_t bn1_mid_from_rows;
+  int32_t router_experts_xl; /* R tile's experts when T >= router_xl_from      */
+  int32_t router_xl_from;    /* (below it, router_experts / _large apply)       */
 } etc_moe_info;
 
 /* Fill `info` for `desc` (host struct).  Queries the device for the grid.
