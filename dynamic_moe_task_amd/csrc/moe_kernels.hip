@@ -1940,8 +1940,12 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   if (EV) {
     run_g1_static<WG>(p, c, red, first_of(w, off, Gt), nG1, Gt, lr);
   } else {
+    // no wait separates this loop's tasks: a barrier keeps the next task's
+    // LDS writes (A staging, partial sums) behind the previous task's last
+    // LDS reads (wave 0 reads the output stage while it stores the tile)
     for (int i = first_of(w, off, Gt); i < nG1; i += Gt) {
       const int rt = i / c.nN1;
+      if (i >= Gt) lds_barrier();
       if (tr) tw = ts = now_ticks();
       task_g1<false, WG>(p, c, load_rowtile(p, rt), rt, i % c.nN1, red);
       if (tr) tb = now_ticks();
@@ -1956,6 +1960,7 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   } else {
     for (int i = first_of(w, off, Gt); i < nG2; i += Gt) {
       const int rt = i / c.nN2;
+      if (i >= Gt) lds_barrier();  // as in the G1 loop
       if (tr) tw = ts = now_ticks();
       task_g2<false, WG>(p, c, load_rowtile(p, rt), rt, i % c.nN2, red);
       if (tr) tb = now_ticks();
