@@ -1974,6 +1974,9 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   // C reads S's routing outputs (slot, row -> tile map)
   if (local && first_of(w, off, Gt) < c.nC && !wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;
   for (int i = first_of(w, off, Gt); i < c.nC; i += Gt) {
+    // wave 0 fills sh.pairs for this task (in the wait, or in the combine)
+    // while the other waves may still read the previous task's pairs
+    if (i >= Gt) lds_barrier();
     if (tr) tw = now_ticks();
     if (EV && !wait_rows_done(p, c, i, sh.pairs)) return;
     if (tr) ts = now_ticks();

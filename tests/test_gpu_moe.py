@@ -236,7 +236,8 @@ EDGE = [
     (12, 128, 64, 8, 256, True, False, 16),    # between one and two G tiles per workgroup of the grid
     (256, 384, 32, 8, 640, True, True, 256),   # column-split G tiles over 3 (G1) and 5 (G2) staged chunks
     (300, 256, 16, 8, 384, True, False, 320),  # column-split G tiles, 2 (G1) and 3 (G2) chunks, T < T_max
-    (2048, 1024, 64, 8, 128, True, False, 2048),  # 32-expert router tiles, unpredicated (H a multiple of 1024)
+    (2048, 2048, 64, 4, 128, True, False, 2048),  # 32-expert router tiles, unpredicated (H a multiple of 1024);
+                                                  # two C tasks a workgroup, two row chunks a thread in each
     (2050, 128, 44, 4, 128, True, True, 2304),  # 32-expert router tiles: a 2-token tile, a 12-expert tile
 ]
 
