@@ -157,7 +157,7 @@ int persistent_grid(int sched, int lds, int* grid, int* solo = nullptr) {
 // library-owned control block for the split-K example (one per device)
 struct SplitkCtl {
   uint32_t* ctl = nullptr;
-  uint64_t* queue = nullptr;
+  uint32_t* queue = nullptr;
   int64_t q_cap = 0;
 };
 std::vector<SplitkCtl> g_sk;
@@ -296,14 +296,14 @@ extern "C" int etc_splitk_launch(etc_etensor* ev, int32_t n, int32_t nsplit, int
   if (sk.q_cap < n) {
     if (sk.ctl) (void)hipFree(sk.ctl);
     const int64_t cap = n > 4096 ? n : 4096;
-    const size_t bytes = kSkCtlBytes + (size_t)cap * 8;
+    const size_t bytes = kSkCtlBytes + (size_t)cap * 4;
     void* mem = nullptr;
     e = hipMalloc(&mem, bytes);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(split-K control)");
     e = hipMemsetAsync(mem, 0, bytes, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(split-K control)");
     sk.ctl = static_cast<uint32_t*>(mem);
-    sk.queue = reinterpret_cast<uint64_t*>(static_cast<char*>(mem) + kSkCtlBytes);
+    sk.queue = reinterpret_cast<uint32_t*>(static_cast<char*>(mem) + kSkCtlBytes);
     sk.q_cap = cap;
   }
   int cus = 0;

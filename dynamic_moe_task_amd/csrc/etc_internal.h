@@ -7,6 +7,12 @@
 
 #include "../../include/etc.h"
 
+#ifndef ETC_HD
+#define ETC_HD __host__ __device__ inline __attribute__((always_inline))
+#endif
+#include "etc_tiles.h"
+#include "dyn_sched.h"
+
 namespace etc {
 
 // status bits (word 0 of a counter set, OR-ed into the report word)
@@ -17,34 +23,10 @@ enum : uint32_t {
   ST_QUEUE_OVERFLOW = 8u,
   ST_ABORT = 0x80000000u,
 };
+static_assert(ST_TIMEOUT == dyn::kStTimeout && ST_OVER_NOTIFY == dyn::kStOverNotify &&
+                  ST_QUEUE_OVERFLOW == dyn::kStOverflow && ST_ABORT == dyn::kStAbort,
+              "one status word, one set of bits");
 
-// ---- task geometry -------------------------------------------------------
-constexpr int kThreads = 256;   // 4 wave64 per workgroup
-constexpr int kRouterT = 4;     // R task: tokens ...
-constexpr int kRouterE = 4;     //         ... x experts (one expert per wave) up to
-constexpr int kRouterLargeT = 64;  //     T = kRouterLargeT; above it four experts per
-constexpr int kRouterEL = 16;      //     wave, so that fewer, longer R tasks cover E,
-constexpr int kRouterEXL = 32;     //     and eight from T = kRouterXLT on, where even
-constexpr int kRouterXLT = 2048;   //     these fill the grid several times over (a
-__host__ __device__ inline int router_experts(int T) {  // T that the large-batch
-  return T >= kRouterXLT ? kRouterEXL : (T > kRouterLargeT ? kRouterEL : kRouterE);  // variant runs)
-}
-constexpr int kBM = 64;         // grouped-GEMM row tile (up to four 16-row MFMA blocks)
-constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile ...
-constexpr int kMidG1Rows = 512;    // ... twice that from T * k routed rows on ...
-constexpr int kWideG1Rows = 2048;  // ... and four times that from these on
-// (column-split tiles; H a multiple of 128, as the ABI requires)
-__host__ __device__ inline int g1_cols(int T, int k, int H) {
-  return (T * k >= kWideG1Rows && H % 128 == 0) ? 4 * kBN1 : (T * k >= kMidG1Rows ? 2 * kBN1 : kBN1);
-}
-constexpr int kBN2 = 64;        // G2: output columns per tile
-constexpr int kCB2 = kBN2 / 16;  // G2: 16-column MFMA blocks per tile
-// G2 output columns per tile: twice kBN2 (column-split tiles) from the same
-// batch on when I is a multiple of 128
-__host__ __device__ inline int g2_cols(int T, int k, int I) {
-  return (T * k >= kWideG1Rows && I % 128 == 0) ? 2 * kBN2 : kBN2;
-}
-constexpr int kCombineT = 2;    // C task: tokens per task
 constexpr int kEvStride = 32;   // words between event elements (one 128-byte line each)
 constexpr int kMaxK = 16;
 constexpr int kMaxE = 256;
@@ -60,9 +42,13 @@ constexpr int kLocalTiles = kLocalRows / 64 + 256 + 16;
 // wait lasts microseconds
 constexpr uint32_t kDefaultWatchdogUs = 2000000u;
 
-// task types (queue descriptors carry them in bits 60..63; 0 = empty slot)
+// task types (the dynamic schedule's queue descriptors carry them in their
+// top three bits, dyn_sched.h; 0 = empty slot)
 enum TaskType : int { TT_R = 1, TT_K = 2, TT_S = 3, TT_D = 4, TT_G1 = 5, TT_G2 = 6, TT_C = 7,
                       TT_L = 8 /* trace only: a workgroup's LDS routing tables */ };
+static_assert(dyn::T_R == TT_R && dyn::T_K == TT_K && dyn::T_S == TT_S && dyn::T_G1 == TT_G1 &&
+                  dyn::T_G2 == TT_G2 && dyn::T_C == TT_C,
+              "the dynamic runner's task types are the kernels' task types");
 
 // ---- counter set (u32 words) ------------------------------------------------
 // Words that many workgroups poll or update each sit on their own 128-byte
@@ -94,7 +80,7 @@ struct MoeLayout {
   int32_t ntt_max, max_rt, nct_max;
   int64_t q_cap;
   // word offsets inside a counter set
-  int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_y, o_ev_c, o_queue;  // o_queue in words, 8-byte aligned
+  int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_y, o_ev_c, o_queue;  // word offsets
   int64_t set_words;
   // byte offsets inside the workspace
   int64_t b_ctrl, b_set0, b_set1, b_meta, b_rt_info, b_row_rt, b_logits, b_hh, b_y;
@@ -114,17 +100,15 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
   L.nct_max = (int32_t)cdiv(Tm, kCombineT);
   const int64_t rows = Tm * d.k;
   L.max_rt = (int32_t)(cdiv(rows, kBM) + (rows < d.E ? rows : d.E));
-  const int64_t nN1 = d.I / kBN1, nN2 = d.H / kBN2;
   // every task except the router prefix goes through the queue
-  L.q_cap = L.ntt_max + 1 + (int64_t)L.max_rt * (nN1 + nN2) + L.nct_max + 64;
+  L.q_cap = dyn::moe_queue_capacity(Tm, L.max_rt, d.I, d.H, kBN1, kBN2, kRouterT, kCombineT);
   int64_t w = W_FIXED;
   L.o_ev_logit = w; w += (int64_t)L.ntt_max * kEvStride;
   L.o_ev_exp = w;   w += (int64_t)d.E * kEvStride;
   L.o_ev_h = w;     w += (int64_t)L.max_rt * kEvStride;
   L.o_ev_y = w;     w += (int64_t)L.max_rt * kEvStride;
   L.o_ev_c = w;     w += (int64_t)L.nct_max * kEvStride;
-  w = align_up(w, 2);
-  L.o_queue = w;    w += 2 * L.q_cap;
+  L.o_queue = w;    w += L.q_cap;  // 32-bit descriptors
   L.set_words = align_up(w, 64);
   int64_t b = 0;
   L.b_ctrl = b;          b += C_WORDS * 4;
@@ -200,7 +184,7 @@ int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes
 int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream);
 int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu);
 int launch_splitk(int n, int nsplit, int bk, const int32_t* A, int32_t* B, int32_t* C,
-                  int32_t* ev, uint32_t* ctl, uint64_t* queue, int64_t q_cap, int sched, int grid,
+                  int32_t* ev, uint32_t* ctl, uint32_t* queue, int64_t q_cap, int sched, int grid,
                   uint64_t budget, void* stream);
 int splitk_occupancy(int sched, int* blocks_per_cu);
 

@@ -38,13 +38,7 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t ld_relaxed64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void st_relaxed(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_relaxed64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t add_relaxed(uint32_t* p, uint32_t v) {
@@ -54,9 +48,6 @@ __device__ __forceinline__ void or_relaxed(uint32_t* p, uint32_t v) {
   __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t xchg_relaxed(uint32_t* p, uint32_t v) {
-  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t xchg_relaxed64(uint64_t* p, uint64_t v) {
   return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -160,5 +151,24 @@ __device__ __forceinline__ void wg_publish() {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 }
+
+// The device side of the dynamic schedule's platform interface (dyn_sched.h):
+// relaxed device-scope atomics, the coherent polling load, s_sleep, the
+// wall clock and the workgroup barriers above.
+struct DevPlat {
+  static constexpr int kThreads = etc::kThreads;
+  __device__ __forceinline__ static int tid() { return (int)threadIdx.x; }
+  __device__ __forceinline__ static uint32_t add(uint32_t* p, uint32_t v) { return add_relaxed(p, v); }
+  __device__ __forceinline__ static uint32_t load(const uint32_t* p) { return ld_relaxed(p); }
+  // descriptors and the total are published with a swap (a read-modify-write
+  // is performed where every XCD's coherent loads see it)
+  __device__ __forceinline__ static void put(uint32_t* p, uint32_t v) { (void)xchg_relaxed(p, v); }
+  __device__ __forceinline__ static void orr(uint32_t* p, uint32_t v) { or_relaxed(p, v); }
+  __device__ __forceinline__ static uint64_t now() { return now_ticks(); }
+  __device__ __forceinline__ static void pause() { __builtin_amdgcn_s_sleep(2); }
+  __device__ __forceinline__ static void barrier() { __syncthreads(); }
+  __device__ __forceinline__ static void publish() { wg_publish(); }
+  __device__ __forceinline__ static int lds_add(int* p, int v) { return atomicAdd(p, v); }
+};
 
 }  // namespace etc

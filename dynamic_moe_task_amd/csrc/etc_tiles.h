@@ -1,0 +1,45 @@
+// Task geometry of the MoE layer graph: tile shapes and the rules that
+// pick them from the batch size T.  Plain constants and inline functions, so
+// that the kernels, the host library and a host-only test harness (g++) all
+// read the same rules; a file compiled by hipcc defines ETC_HD as
+// __host__ __device__ before including it.
+#pragma once
+
+#ifndef ETC_HD
+#define ETC_HD inline
+#endif
+
+namespace etc {
+
+constexpr int kThreads = 256;      // 4 wave64 per workgroup
+// R task: kRouterT tokens x router_experts(T) experts.  One expert a wave up
+// to T = kRouterLargeT; four a wave above it (fewer, longer tasks); eight a
+// wave from T = kRouterXLT on, where even those fill the grid several times
+// over (that tile exists only in the large-batch kernel variant).
+constexpr int kRouterT = 4;
+constexpr int kRouterE = 4;
+constexpr int kRouterLargeT = 64;
+constexpr int kRouterEL = 16;
+constexpr int kRouterEXL = 32;
+constexpr int kRouterXLT = 2048;
+ETC_HD int router_experts(int T) {
+  return T >= kRouterXLT ? kRouterEXL : (T > kRouterLargeT ? kRouterEL : kRouterE);
+}
+constexpr int kBM = 64;         // grouped-GEMM row tile (up to four 16-row MFMA blocks)
+constexpr int kBN1 = 16;        // G1: gate columns (and as many up columns) per tile ...
+constexpr int kMidG1Rows = 512;    // ... twice that from T * k routed rows on ...
+constexpr int kWideG1Rows = 2048;  // ... and four times that from these on
+// (column-split tiles; H a multiple of 128, as the ABI requires)
+ETC_HD int g1_cols(int T, int k, int H) {
+  return (T * k >= kWideG1Rows && H % 128 == 0) ? 4 * kBN1 : (T * k >= kMidG1Rows ? 2 * kBN1 : kBN1);
+}
+constexpr int kBN2 = 64;        // G2: output columns per tile
+constexpr int kCB2 = kBN2 / 16;  // G2: 16-column MFMA blocks per tile
+// G2 output columns per tile: twice kBN2 (column-split tiles) from the same
+// batch on when I is a multiple of 128
+ETC_HD int g2_cols(int T, int k, int I) {
+  return (T * k >= kWideG1Rows && I % 128 == 0) ? 2 * kBN2 : kBN2;
+}
+constexpr int kCombineT = 2;    // C task: tokens per task
+
+}  // namespace etc

@@ -45,8 +45,6 @@ enum Mode : int { MODE_STATIC = ETC_SCHED_STATIC, MODE_DYNAMIC = ETC_SCHED_DYNAM
                   MODE_KBK = ETC_SCHED_KBK, MODE_BARRIER = ETC_SCHED_BARRIER,
                   MODE_ORDERED = ETC_SCHED_ORDERED };
 
-constexpr uint64_t kDescExit = ~0ull;
-
 // ------------------------------------------------------------- helpers --
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
@@ -65,12 +63,6 @@ __device__ __forceinline__ void unpack8(u32x4_t v, float* f) {
   f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
   f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
 }
-__device__ __forceinline__ uint64_t make_desc(int type, uint32_t a, uint32_t b) {
-  return ((uint64_t)type << 60) | ((uint64_t)(a & 0x3fffffffu) << 30) | (uint64_t)(b & 0x3fffffffu);
-}
-__device__ __forceinline__ int desc_type(uint64_t d) { return (int)(d >> 60); }
-__device__ __forceinline__ uint32_t desc_a(uint64_t d) { return (uint32_t)((d >> 30) & 0x3fffffffu); }
-__device__ __forceinline__ uint32_t desc_b(uint64_t d) { return (uint32_t)(d & 0x3fffffffu); }
 __device__ __forceinline__ int first_of(int w, int64_t off, int G) {
   int o = (int)(off % G);
   return (w - o + G) % G;
@@ -124,7 +116,6 @@ __device__ __forceinline__ RowTile get_tile(const MoeParams& p, const LocalRoute
 struct Ctx {
   uint32_t* set;     // counter set of this launch (NULL for kernel-by-kernel)
   uint32_t* status;  // where error bits go
-  uint64_t* queue;
   int T, H, E, k, I;
   int bn1;  // G1 gate (and up) columns per tile, chosen per launch from T
   int bn2;  // G2 output columns per tile, chosen per launch from T
@@ -136,7 +127,6 @@ __device__ __forceinline__ Ctx make_ctx(const MoeParams& p, uint32_t* set) {
   Ctx c;
   c.set = set;
   c.status = set ? set + W_STATUS : p.ctrl + C_REPORT;
-  c.queue = set ? reinterpret_cast<uint64_t*>(set + p.o_queue) : nullptr;
   c.T = p.T; c.H = p.H; c.E = p.E; c.k = p.k; c.I = p.I;
   c.nTT = (p.T + kRouterT - 1) / kRouterT;
   c.nET = (p.E + router_experts(p.T) - 1) / router_experts(p.T);
@@ -152,12 +142,7 @@ __device__ __forceinline__ Ctx make_ctx(const MoeParams& p, uint32_t* set) {
 }
 
 struct Shared {
-  uint64_t desc;
-  int n;           // number of completed events collected by this task
-  int base;        // first reserved queue slot
-  int total;       // descriptors to write
-  int list[kBM];
-  int pairs[2 * kCombineT * kMaxK];  // D: slots; C: (weight, slot) pairs
+  int pairs[2 * kCombineT * kMaxK];  // C: (weight, slot) pairs
   uint32_t claim[4];                 // ORDERED: claimed ordinals handed to every thread
 };
 
@@ -218,9 +203,6 @@ __device__ __forceinline__ uint32_t* ev_y(const MoeParams& p, const Ctx& c, int 
 }
 __device__ __forceinline__ uint32_t* ev_c(const MoeParams& p, const Ctx& c, int ct) {
   return c.set + p.o_ev_c + (int64_t)ct * kEvStride;
-}
-__device__ __forceinline__ uint32_t ctile_target(const Ctx& c, int ct) {
-  return (uint32_t)(min(kCombineT, c.T - ct * kCombineT) * c.k * c.nN2);
 }
 
 // Notify one event element; returns true if this notify completed it.
@@ -1288,112 +1270,32 @@ __device__ __forceinline__ void task_combine(const MoeParams& p, const Ctx& c, i
 }
 
 // =================================================== event plumbing ========
-// Reserve `n` queue slots (thread 0); returns the first, or -1 on overflow.
-__device__ __forceinline__ int64_t q_reserve(const MoeParams& p, const Ctx& c, int n) {
-  const uint32_t base = add_relaxed(c.set + W_TAIL, (uint32_t)n);
-  if ((int64_t)base + n > p.q_cap) {
-    or_relaxed(c.status, ST_QUEUE_OVERFLOW | ST_ABORT);
-    return -1;
-  }
-  return base;
-}
-__device__ __forceinline__ void q_put(const Ctx& c, int64_t slot, uint64_t desc) {
-  xchg_relaxed64(c.queue + slot, desc);
-}
-
+// STATIC and ORDERED: the notifies after the router, top-k and scan tasks
+// (the G runners notify inline).  The dynamic schedule's notifies and
+// pushes live in dyn_sched.h.
 template <int MODE>
 __device__ __forceinline__ void after_router(const MoeParams& p, const Ctx& c, int tt) {
-  if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC || MODE == MODE_ORDERED) {
+  if (MODE == MODE_STATIC || MODE == MODE_ORDERED) {
     wg_publish();
-    if (threadIdx.x == 0) {
-      if (notify1(c, ev_logit(p, c, tt), (uint32_t)c.nET) && MODE == MODE_DYNAMIC) {
-        const int64_t q = q_reserve(p, c, 1);
-        if (q >= 0) q_put(c, q, make_desc(TT_K, tt, 0));
-      }
-    }
+    if (threadIdx.x == 0) notify1(c, ev_logit(p, c, tt), (uint32_t)c.nET);
   }
 }
 
 template <int MODE>
 __device__ __forceinline__ void after_topk(const MoeParams& p, const Ctx& c) {
-  if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC || MODE == MODE_ORDERED) {
+  if (MODE == MODE_STATIC || MODE == MODE_ORDERED) {
     wg_publish();
-    if (threadIdx.x == 0) {
-      if (notify1(c, c.set + W_EV_ROUTE, (uint32_t)c.nK) && MODE == MODE_DYNAMIC) {
-        const int64_t q = q_reserve(p, c, 1);
-        if (q >= 0) q_put(c, q, make_desc(TT_S, 0, 0));
-      }
-    }
+    if (threadIdx.x == 0) notify1(c, c.set + W_EV_ROUTE, (uint32_t)c.nK);
   }
 }
 
 template <int MODE>
-__device__ __forceinline__ void after_scan(const MoeParams& p, const Ctx& c, Shared& sh, int nrt) {
-  if (MODE == MODE_STATIC || MODE == MODE_DYNAMIC || MODE == MODE_ORDERED) {
+__device__ __forceinline__ void after_scan(const MoeParams& p, const Ctx& c, int nrt) {
+  if (MODE == MODE_STATIC || MODE == MODE_ORDERED) {
     wg_publish();
-    if (MODE == MODE_DYNAMIC) {
-      // every expert event is complete once S runs (K notified all routed
-      // pairs before S was pushed), so S pushes the G1 tiles of all experts
-      if (threadIdx.x == 0) {
-        const uint32_t nrt = ld_relaxed(p.meta + M_NRT);
-        const uint32_t total = (uint32_t)(c.nR + c.nK + 1 + c.nC) + nrt * (uint32_t)(c.nN1 + c.nN2);
-        xchg_relaxed(c.set + W_TOTAL, total);
-        sh.n = (int)(nrt * (uint32_t)c.nN1);
-        sh.base = (int)q_reserve(p, c, sh.n);
-      }
-      __syncthreads();
-      const int base = sh.base, n1 = sh.n;
-      if (base >= 0)
-        for (int i = threadIdx.x; i < n1; i += kThreads) q_put(c, base + i, make_desc(TT_G1, i / c.nN1, i % c.nN1));
-      __syncthreads();
-    } else {
-      // the scan event is complete at any value >= 1; S stores nrt + 1, so
-      // that a waiter learns the row-tile count from the poll that frees it
-      if (threadIdx.x == 0) xchg_relaxed(c.set + W_EV_SCAN, (uint32_t)nrt + 1u);
-    }
-  }
-}
-
-template <int MODE>
-__device__ __forceinline__ void after_g1(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
-  if (MODE != MODE_STATIC && MODE != MODE_DYNAMIC) return;
-  wg_publish();
-  if (threadIdx.x == 0) {
-    sh.base = -1;
-    if (notify1(c, ev_h(p, c, rt), (uint32_t)c.nN1) && MODE == MODE_DYNAMIC)
-      sh.base = (int)q_reserve(p, c, c.nN2);
-  }
-  if (MODE == MODE_DYNAMIC) {
-    __syncthreads();
-    const int base = sh.base;
-    if (base >= 0)
-      for (int i = threadIdx.x; i < c.nN2; i += kThreads) q_put(c, base + i, make_desc(TT_G2, rt, i));
-    __syncthreads();
-  }
-}
-
-template <int MODE>
-__device__ __forceinline__ void after_g2(const MoeParams& p, const Ctx& c, int rt, Shared& sh) {
-  if (MODE != MODE_STATIC && MODE != MODE_DYNAMIC) return;
-  const RowTile tile = load_rowtile(p, rt);
-  wg_publish();
-  if (threadIdx.x == 0) sh.n = 0;
-  __syncthreads();
-  if (threadIdx.x < tile.nrows) {
-    const int f = (int)co_ld32(r_perm(p), (uint32_t)(tile.r0 + threadIdx.x) * 4u);
-    const int ct = (f / c.k) / kCombineT;
-    if (notify1(c, ev_c(p, c, ct), ctile_target(c, ct)) && MODE == MODE_DYNAMIC)
-      sh.list[atomicAdd(&sh.n, 1)] = ct;
-  }
-  if (MODE == MODE_DYNAMIC) {
-    __syncthreads();
-    const int n = sh.n;
-    if (n == 0) return;
-    if (threadIdx.x == 0) sh.base = (int)q_reserve(p, c, n);
-    __syncthreads();
-    const int base = sh.base;
-    if (base >= 0 && threadIdx.x < n) q_put(c, base + threadIdx.x, make_desc(TT_C, sh.list[threadIdx.x], 0));
-    __syncthreads();
+    // the scan event is complete at any value >= 1; S stores nrt + 1, so
+    // that a waiter learns the row-tile count from the poll that frees it
+    if (threadIdx.x == 0) xchg_relaxed(c.set + W_EV_SCAN, (uint32_t)nrt + 1u);
   }
 }
 
@@ -1881,7 +1783,7 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
     const int nrt_s = task_scan(p, c, smem);
     if (tr) tb = now_ticks();
     dbg_task(p, TT_S);
-    after_scan<MODE>(p, c, sh, nrt_s);
+    after_scan<MODE>(p, c, nrt_s);
     trace_task(p, TT_S, 0, 0, tw, ts, tb);
   }
   off += 1;
@@ -1987,96 +1889,50 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   }
 }
 
-// DYNAMIC: one HBM queue.  Index i < nR is the implicit router prefix (ready
-// at launch); every other index is a slot filled by the notify that released
-// the task (early push).  A workgroup pops by bumping the head, waits for its
-// slot, and exits once the total task count (known after S) is passed.  Tasks
-// never wait on events here: they are only pushed when ready.
-__device__ __forceinline__ void run_dynamic(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh) {
-  float* red = reinterpret_cast<float*>(smem);
-  const bool tr = p.trace != nullptr;
-  uint64_t tw = 0, ts = 0, tb = 0;
-  for (;;) {
-    if (tr) tw = now_ticks();
-    if (threadIdx.x == 0) {
-      uint64_t d = kDescExit;
-      const uint32_t idx = add_relaxed(c.set + W_HEAD, 1u);
-      if ((int64_t)idx < c.nR) {
-        d = make_desc(TT_R, idx / c.nET, idx % c.nET);
-      } else {
-        const int64_t qi = (int64_t)idx - c.nR;
-        if (qi < p.q_cap) {
-          const uint64_t t0 = now_ticks();
-          for (uint32_t spins = 1;; ++spins) {
-            const uint64_t v = ld_relaxed64(c.queue + qi);
-            if (v) { d = v; break; }
-            if ((spins & 3u) == 0u) {
-              const uint32_t tot = ld_relaxed(c.set + W_TOTAL);
-              if (tot && idx >= tot) break;
-              if (ld_relaxed(c.status) & ST_ABORT) break;
-              if (now_ticks() - t0 > c.budget) { or_relaxed(c.status, ST_TIMEOUT | ST_ABORT); break; }
-            }
-            __builtin_amdgcn_s_sleep(2);
-          }
-        }
-      }
-      sh.desc = d;
-    }
-    __syncthreads();
-    const uint64_t d = sh.desc;
-    __syncthreads();
-    if (d == kDescExit) return;
-    if (tr) ts = now_ticks();
-    const int a = (int)desc_a(d), b = (int)desc_b(d);
-    switch (desc_type(d)) {
-      case TT_R:
-        task_router<false>(p, c, a, b);
-        if (tr) tb = now_ticks();
-        dbg_task(p, TT_R);
-        after_router<MODE_DYNAMIC>(p, c, a);
-        trace_task(p, TT_R, a, b, tw, ts, tb);
-        break;
-      case TT_K:
-        task_topk(p, c, a);
-        if (tr) tb = now_ticks();
-        dbg_task(p, TT_K);
-        after_topk<MODE_DYNAMIC>(p, c);
-        trace_task(p, TT_K, a, b, tw, ts, tb);
-        break;
-      case TT_S: {
-        const int nrt_s = task_scan<false, false>(p, c, smem);
-        if (tr) tb = now_ticks();
-        dbg_task(p, TT_S);
-        after_scan<MODE_DYNAMIC>(p, c, sh, nrt_s);
-        trace_task(p, TT_S, a, b, tw, ts, tb);
-        break;
-      }
-      case TT_G1:
-        task_g1<false, false>(p, c, load_rowtile(p, a), a, b, red);
-        if (tr) tb = now_ticks();
-        dbg_task(p, TT_G1);
-        after_g1<MODE_DYNAMIC>(p, c, a, sh);
-        trace_task(p, TT_G1, a, b, tw, ts, tb);
-        break;
-      case TT_G2:
-        task_g2<false, false>(p, c, load_rowtile(p, a), a, b, red);
-        if (tr) tb = now_ticks();
-        dbg_task(p, TT_G2);
-        after_g2<MODE_DYNAMIC>(p, c, a, sh);
-        trace_task(p, TT_G2, a, b, tw, ts, tb);
-        break;
-      case TT_C:
-        task_combine(p, c, a, sh.pairs);
-        if (tr) tb = now_ticks();
-        dbg_task(p, TT_C);
-        trace_task(p, TT_C, a, b, tw, ts, tb);
-        break;
-      default:
-        or_relaxed(c.status, ST_QUEUE_OVERFLOW | ST_ABORT);
-        return;
-    }
+// DYNAMIC (Event Tensor pages, Figs. 8 and 9; podcast cue 11): the control
+// logic (queue, pushes on completed events, the exit rule) is dyn::run_moe
+// in dyn_sched.h, shared with a host harness that drives it with threads.
+// DynTasks gives it this kernel's task bodies, event elements and trace.
+template <bool WG>
+struct DynTasks {
+  const MoeParams& p;
+  const Ctx& c;
+  uint8_t* smem;
+  Shared& ksh;
+  RowTile tile;  // the row tile of the last G2 task (its rows arrive at their combine events)
+  uint64_t tw, tb;
+  __device__ __forceinline__ void router(int tt, int et) { task_router<WG>(p, c, tt, et); }
+  __device__ __forceinline__ void topk(int tt) { task_topk(p, c, tt); }
+  __device__ __forceinline__ int scan() { return task_scan<false, false>(p, c, smem); }
+  __device__ __forceinline__ void g1(int rt, int nt) {
+    task_g1<false, WG>(p, c, load_rowtile(p, rt), rt, nt, reinterpret_cast<float*>(smem));
   }
-}
+  __device__ __forceinline__ void g2(int rt, int nt) {
+    tile = load_rowtile(p, rt);
+    task_g2<false, WG>(p, c, tile, rt, nt, reinterpret_cast<float*>(smem));
+  }
+  __device__ __forceinline__ void combine(int ct) { task_combine(p, c, ct, ksh.pairs); }
+  __device__ __forceinline__ uint32_t* ev_logit(int tt) { return etc::ev_logit(p, c, tt); }
+  __device__ __forceinline__ uint32_t* ev_route() { return c.set + W_EV_ROUTE; }
+  __device__ __forceinline__ uint32_t* ev_h(int rt) { return etc::ev_h(p, c, rt); }
+  __device__ __forceinline__ uint32_t* ev_y(int rt) { return etc::ev_y(p, c, rt); }
+  __device__ __forceinline__ uint32_t* ev_c(int ct) { return etc::ev_c(p, c, ct); }
+  __device__ __forceinline__ int tile_rows(int) { return tile.nrows; }
+  __device__ __forceinline__ int row_ctile(int, int r) {
+    const int f = (int)co_ld32(r_perm(p), (uint32_t)(tile.r0 + r) * 4u);
+    return (f / c.k) / kCombineT;
+  }
+  __device__ __forceinline__ void trace_start() {
+    if (p.trace) tw = now_ticks();
+  }
+  __device__ __forceinline__ void trace_body() {
+    if (p.trace) tb = now_ticks();
+  }
+  __device__ __forceinline__ void trace_end(int type, int a, int b) {
+    dbg_task(p, type);
+    trace_task(p, type, a, b, tw, tw, tb);
+  }
+};
 
 // The persistent megakernel.  Counter sets are double buffered by the
 // parity of a device-side epoch: this launch works in set[epoch & 1] (zeroed
@@ -2103,18 +1959,34 @@ moe_persistent(MoeParams p) {
        i += (int64_t)gridDim.x * kThreads)
     other[i] = 0u;
   Ctx c = make_ctx(p, set);
-  if (!WG) {  // the small-batch variant runs K-split G tiles (the dynamic schedule the narrowest)
-    // and no eight-experts-a-wave router tiles
-    if (router_experts(p.T) == kRouterEXL) c.nET = (p.E + kRouterEL - 1) / kRouterEL;
-    c.bn1 = MODE == MODE_DYNAMIC ? kBN1 : g1_cols(p.T, p.k, p.H);
-    c.nN1 = p.I / c.bn1;
-    c.bn2 = kBN2;
-    c.nN2 = p.H / kBN2;
+  {
+    // task counts and tile widths of the variant this launch runs (the
+    // small-batch variant holds neither the eight-experts-a-wave router tile
+    // nor the column-split G tiles)
+    const dyn::MoeGraph g = dyn::launch_graph(p.T, p.E, p.k, p.H, p.I, WG);
+    c.nET = g.nET;
+    c.nR = g.nR;
+    c.nN1 = g.nN1;
+    c.bn1 = p.I / g.nN1;
+    c.nN2 = g.nN2;
+    c.bn2 = p.H / g.nN2;
+    if (MODE == MODE_DYNAMIC) {
+      dyn::Queue q;
+      q.head = set + W_HEAD;
+      q.tail = set + W_TAIL;
+      q.total = set + W_TOTAL;
+      q.status = c.status;
+      q.slot = set + p.o_queue;
+      q.cap = p.q_cap;
+      q.prefix = (uint32_t)g.nR;
+      q.known_total = 0u;
+      q.budget = p.budget;
+      __shared__ dyn::Shared dsh;
+      DynTasks<WG> tk{p, c, smem, sh, RowTile{0, 0, 0}, 0, 0};
+      dyn::run_moe<DevPlat>(tk, q, g, dsh);
+    }
   }
-  if (MODE == MODE_DYNAMIC)
-    run_dynamic(p, c, smem, sh);
-  else
-    run_lists<MODE, WG>(p, c, smem, sh);
+  if (MODE != MODE_DYNAMIC) run_lists<MODE, WG>(p, c, smem, sh);
   wg_publish();
   if (threadIdx.x == 0) {
     const uint32_t st = ld_relaxed(c.status) & ~ST_ABORT;
@@ -2166,7 +2038,7 @@ __global__ void __launch_bounds__(kThreads) kbk_combine(MoeParams p) {
 
 // ------------------------------------------------------- host launchers --
 // The variant a launch of T tokens runs: the wide G1 tiles from T * k on.
-static bool wide_g1(const MoeParams& p) { return g1_cols(p.T, p.k, p.H) > 2 * kBN1 || g2_cols(p.T, p.k, p.I) > kBN2; }
+static bool wide_g1(const MoeParams& p) { return wide_variant(p.T, p.k, p.H, p.I); }
 
 template <int MODE>
 static void launch_variant(const MoeParams& p, bool wide, int grid, int lds_bytes, hipStream_t s) {
@@ -2184,7 +2056,7 @@ int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes
       launch_variant<MODE_STATIC>(p, wide, grid, lds_bytes, s);
       break;
     case ETC_SCHED_DYNAMIC:
-      hipLaunchKernelGGL((moe_persistent<MODE_DYNAMIC, false>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+      launch_variant<MODE_DYNAMIC>(p, wide, grid, lds_bytes, s);
       break;
     case ETC_SCHED_BARRIER:
       launch_variant<MODE_BARRIER>(p, wide, grid, lds_bytes, s);
@@ -2217,8 +2089,7 @@ int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu) {
       e = occupancy_both<MODE_STATIC>(blocks_per_cu, lds_bytes);
       break;
     case ETC_SCHED_DYNAMIC:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_DYNAMIC, false>, kThreads,
-                                                       lds_bytes);
+      e = occupancy_both<MODE_DYNAMIC>(blocks_per_cu, lds_bytes);
       break;
     case ETC_SCHED_BARRIER:
       e = occupancy_both<MODE_BARRIER>(blocks_per_cu, lds_bytes);

@@ -20,16 +20,13 @@
 
 namespace etc {
 
-constexpr int SK_PARTIAL = 1, SK_FINAL = 2;
-constexpr uint64_t SK_EXIT = ~0ull;
-
 struct SkParams {
   const int32_t* A;
   int32_t* B;
   int32_t* C;
   uint32_t* ev;
   uint32_t* ctl;
-  uint64_t* queue;
+  uint32_t* queue;
   int64_t q_cap;
   int n, nsplit, bk;
   uint64_t budget;
@@ -74,13 +71,32 @@ __device__ __forceinline__ bool sk_notify(const SkParams& p, int i) {
   return old + 1u == (uint32_t)p.nsplit;
 }
 
+struct SkTasks {
+  const SkParams& p;
+  int* tmp;
+  __device__ __forceinline__ void partial(uint32_t i, uint32_t j) { sk_partial(p, (int)i, (int)j, tmp); }
+  __device__ __forceinline__ void final_sum(uint32_t i) {
+    if (threadIdx.x == 0) xchg_relaxed(p.ev + i, 0u);  // sole waiter: back to rest
+    sk_final(p, (int)i, tmp);
+  }
+};
+
 template <int MODE>
 __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
   __shared__ int tmp[8];
-  __shared__ uint64_t s_desc;
   const int G = gridDim.x, w = blockIdx.x;
   const int nP = p.n * p.nsplit;
   uint32_t* status = p.ctl + SK_STATUS;
+  dyn::Queue q;
+  q.head = p.ctl + SK_HEAD;
+  q.tail = p.ctl + SK_TAIL;
+  q.total = nullptr;
+  q.status = status;
+  q.slot = p.queue;
+  q.cap = p.q_cap;
+  q.prefix = (uint32_t)nP;
+  q.known_total = (uint32_t)(nP + p.n);
+  q.budget = p.budget;
   if (MODE == ETC_SCHED_STATIC) {
     // phase-ordered lists: all partial sums, then all final sums
     for (int t = w; t < nP; t += G) {
@@ -94,55 +110,11 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
       sk_final(p, i, tmp);
     }
   } else {
-    // push / pop: the partial sums are the implicit ready prefix; the notify
-    // that completes event i pushes final_sum(i) at once
-    const uint32_t total = (uint32_t)(nP + p.n);
-    for (;;) {
-      if (threadIdx.x == 0) {
-        uint64_t d = SK_EXIT;
-        const uint32_t idx = add_relaxed(p.ctl + SK_HEAD, 1u);
-        if ((int)idx < nP) {
-          d = ((uint64_t)SK_PARTIAL << 60) | idx;
-        } else if (idx < total) {
-          const int64_t qi = (int64_t)idx - nP;
-          const uint64_t t0 = now_ticks();
-          for (uint32_t spins = 1;; ++spins) {
-            const uint64_t v = ld_relaxed64(p.queue + qi);
-            if (v) {
-              d = v;
-              xchg_relaxed64(p.queue + qi, 0ull);  // slot back to rest for the next launch
-              break;
-            }
-            if ((spins & 3u) == 0u) {
-              if (ld_relaxed(status) & ST_ABORT) break;
-              if (now_ticks() - t0 > p.budget) { or_relaxed(status, ST_TIMEOUT | ST_ABORT); break; }
-            }
-            __builtin_amdgcn_s_sleep(2);
-          }
-        }
-        s_desc = d;
-      }
-      __syncthreads();
-      const uint64_t d = s_desc;
-      __syncthreads();
-      if (d == SK_EXIT) break;
-      const int type = (int)(d >> 60);
-      const int a = (int)(d & 0x0fffffffffffffffull);
-      if (type == SK_PARTIAL) {
-        sk_partial(p, a / p.nsplit, a % p.nsplit, tmp);
-        wg_publish();
-        if (threadIdx.x == 0 && sk_notify(p, a / p.nsplit)) {
-          const uint32_t q = add_relaxed(p.ctl + SK_TAIL, 1u);
-          if ((int64_t)q < p.q_cap)
-            xchg_relaxed64(p.queue + q, ((uint64_t)SK_FINAL << 60) | (uint64_t)(a / p.nsplit));
-          else
-            or_relaxed(status, ST_QUEUE_OVERFLOW | ST_ABORT);
-        }
-      } else {
-        if (threadIdx.x == 0) xchg_relaxed(p.ev + a, 0u);
-        sk_final(p, a, tmp);
-      }
-    }
+    // push / pop (dyn_sched.h): the partial sums are the ready prefix; the
+    // notify that completes event i pushes final_sum(i) at once
+    __shared__ dyn::Shared dsh;
+    SkTasks tk{p, tmp};
+    dyn::run_splitk<DevPlat>(tk, q, (uint32_t)p.nsplit, p.ev, dsh);
   }
   wg_publish();
   if (threadIdx.x == 0) {
@@ -150,16 +122,14 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
     if (old == (uint32_t)G - 1u) {
       const uint32_t st = ld_relaxed(status) & ~ST_ABORT;
       if (st) or_relaxed(p.ctl + SK_REPORT, st);
-      xchg_relaxed(status, 0u);
-      xchg_relaxed(p.ctl + SK_HEAD, 0u);
-      xchg_relaxed(p.ctl + SK_TAIL, 0u);
+      dyn::splitk_reset<DevPlat>(q);
       xchg_relaxed(p.ctl + SK_DONE, 0u);
     }
   }
 }
 
 int launch_splitk(int n, int nsplit, int bk, const int32_t* A, int32_t* B, int32_t* C, int32_t* ev,
-                  uint32_t* ctl, uint64_t* queue, int64_t q_cap, int sched, int grid, uint64_t budget,
+                  uint32_t* ctl, uint32_t* queue, int64_t q_cap, int sched, int grid, uint64_t budget,
                   void* stream) {
   SkParams p;
   p.A = A; p.B = B; p.C = C;
