@@ -185,9 +185,11 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def time_sched(bufs, T, sched, steps, warmup, w13s, w2s, stream_ptr):
+def time_sched(bufs, T, sched, steps, warmup, w13s, w2s, stream_ptr, per_launch=None):
     """Average µs per launch over `steps` back-to-back launches, bracketed by
-    HIP events on the launch stream."""
+    HIP events on the launch stream.  With a list `per_launch`, a second pass
+    brackets every launch with its own pair of events and appends the
+    per-launch µs to it (for the median and the p10/p90 spread)."""
     import torch
     from dynamic_moe_task_amd import binding as B
     R = len(w13s)
@@ -207,19 +209,48 @@ def time_sched(bufs, T, sched, steps, warmup, w13s, w2s, stream_ptr):
     rc = B.etc_sync(stream_ptr)
     if rc != 0:
         raise B.EtcError(rc, B.etc_last_error())
+    if per_launch is not None:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record()
+            B.check(B.moe_layer_launch(bufs.desc, T, args[i % R], code, stream_ptr))
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        B.check(B.etc_sync(stream_ptr))
+        per_launch += [a.elapsed_time(b) * 1e3 for a, b in evs]
     return start.elapsed_time(end) * 1e3 / steps
 
 
-def cpu_baseline(shape, w, X, seconds):
-    """The oracle as it stands, single-threaded C, on the same workload:
-    whole layers for decode/tiny; for the prefill workload a bounded sample
-    of tokens (routing for all T plus the expert rows of a token subset)."""
+def dist(samples):
+    """Median and p10 / p90 of per-launch µs."""
+    x = np.asarray(samples, np.float64)
+    return {"p10": round(float(np.percentile(x, 10)), 2), "median": round(float(np.median(x)), 2),
+            "p90": round(float(np.percentile(x, 90)), 2), "n": int(x.size)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_oracle_rate(shape, w, X, seconds, threads):
+    """Tokens/s of the oracle as it stands (plain C, fp64) on `threads`
+    threads: whole layers for decode/tiny; for larger batches a bounded
+    sample (routing for all T plus the expert rows of a token slice)."""
     import oracle
     k = shape.k
+    used = oracle.set_threads(threads)
     t0 = time.perf_counter()
     n = 0
     toks = 0
     sample = ""
+    step = 8 * max(1, used)
     while True:
         if shape.T <= 16:
             oracle.moe(X, w.Wr, w.W13, w.Wd, k=k, norm_topk=shape.norm_topk, bias=w.bias)
@@ -227,16 +258,31 @@ def cpu_baseline(shape, w, X, seconds):
             sample = f"whole layer, T={shape.T}, repeated"
         else:
             r = oracle.route(X, w.Wr, k, bias=w.bias)
-            sub = np.arange(n * 8 % shape.T, n * 8 % shape.T + 8, dtype=np.int32) % shape.T
+            sub = np.arange(n * step % shape.T, n * step % shape.T + step, dtype=np.int32) % shape.T
             oracle.moe_tokens(sub, X, w.W13, w.Wd, r["topk_ids"], r["topk_w"])
             toks += len(sub)
-            sample = f"routing of all {shape.T} tokens + expert rows of 8-token slices, repeated"
+            sample = f"routing of all {shape.T} tokens + expert rows of {step}-token slices, repeated"
         n += 1
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": toks / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{sample}; {n} calls in {dt:.1f} s on {platform.processor() or platform.machine()}"}
+    return toks / dt, used, f"{sample}; {n} calls in {dt:.1f} s"
+
+
+def cpu_baseline(shape, w, X, seconds):
+    """The oracle timed on this host's cores in the same run: one thread,
+    then OpenMP over the rows on every core this process may use
+    (sched_getaffinity, capped by OMP_NUM_THREADS when the host sets it).
+    `value`/`cores` are the multi-core leg."""
+    ncores = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        ncores = min(ncores, int(env))
+    v1, _, s1 = cpu_oracle_rate(shape, w, X, seconds / 2, 1)
+    vn, used, sn = cpu_oracle_rate(shape, w, X, seconds / 2, ncores)
+    return {"value": vn, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{sn}; OpenMP over rows", "cpu_model": cpu_model(),
+            "single_thread": {"value": v1, "unit": "tokens/s", "cores": 1, "sample": s1}}
 
 
 RIDGE = BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte where MFMA and HBM bounds meet
@@ -402,9 +448,10 @@ def main():
 
     scheds = [a.sched] if a.only_sched else list(SCHEDS)
     runs = {s: [] for s in scheds}
+    per_launch = {s: [] for s in scheds}
     for _ in range(max(1, a.repeat)):  # interleave the schedules, then take medians
         for s in scheds:
-            runs[s].append(time_sched(bufs, T, s, a.steps, a.warmup, w13s, w2s, sp))
+            runs[s].append(time_sched(bufs, T, s, a.steps, a.warmup, w13s, w2s, sp, per_launch[s]))
     us = {s: float(np.median(v)) for s, v in runs.items()}
     us_main = us[a.sched]
 
@@ -467,6 +514,7 @@ def main():
                    "schedule": a.sched, "weight_copies_rotated": R, "active_experts": n_act},
         "us_per_layer": {s: round(v, 2) for s, v in us.items()},
         "us_per_layer_runs": {s: [round(x, 2) for x in v] for s, v in runs.items()},
+        "us_per_launch_dist": {s: dist(v) for s, v in per_launch.items()},
         "mfma_frac_whole_layer": round(mfma_frac, 5),
         "roofline": roofline,
         "cpu_baseline": cpu,

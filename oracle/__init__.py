@@ -29,7 +29,7 @@ def build(force: bool = False) -> str:
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
         subprocess.check_call([
-            "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+            "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fopenmp",
             "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
@@ -53,6 +53,8 @@ def _load():
         lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
         lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_f32.restype = ctypes.c_float
+        lib.oracle_set_threads.argtypes = [i]
+        lib.oracle_max_threads.restype = i
         _lib = lib
     return _lib
 
@@ -179,6 +181,14 @@ def moe_tokens(tokens, X, W13, Wd, topk_ids, topk_w):
     _check(_load().oracle_moe_tokens(H, k, I, len(tok), _p(tok), _p(X), _p(W13), _p(Wd),
                                      _p(ids), _p(w), _p(out)), "moe_tokens")
     return out
+
+
+def set_threads(n: int) -> int:
+    """Threads for the per-row loops (OpenMP); returns the count now in force.
+    The results do not depend on it."""
+    lib = _load()
+    lib.oracle_set_threads(int(n))
+    return int(lib.oracle_max_threads())
 
 
 def splitk(A, nsplit: int):

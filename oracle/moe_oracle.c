@@ -24,12 +24,17 @@
  * of the router, tie-break, rounding points, SwiGLU, weighted combine) is a
  * stated reading; each function says which.
  *
+ * The per-row loops of oracle_moe and oracle_moe_tokens carry an OpenMP
+ * pragma: rows are independent and each is computed in the same order on
+ * any thread, so the thread count changes the time, never a value.
+ *
  * Floating point: fp64 everywhere except where a float decides an integer
  * (the router logits feeding top-k), which follows the fixed fp32 order
  * documented at oracle_router_logits, so both sides take the top-k decision
  * on identical values.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -63,6 +68,14 @@ static uint16_t float_to_bf16_bits(float f) {
 }
 
 uint16_t oracle_f32_to_bf16(float f) { return float_to_bf16_bits(f); }
+
+/* Threads for the per-row loops below (OpenMP; each routed row and each
+ * token is computed on its own, in the same order, so the results do not
+ * depend on the thread count).  n <= 0 leaves the OpenMP default.          */
+void oracle_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+int oracle_max_threads(void) { return omp_get_max_threads(); }
 float oracle_bf16_to_f32(uint16_t b) { return bf16_bits_to_float(b); }
 
 /* ------------------------------------------------------------------------ */
@@ -257,11 +270,23 @@ int oracle_moe(int T, int H, int E, int k, int I, int norm_topk,
   rc = oracle_route_scan(T, E, k, ids, counts, exp_indptr, perm, slot);
   if (rc) return rc;
   const int n = T * k;
-  uint16_t *hrow = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)I);
   uint16_t *yall = Y ? Y : (uint16_t *)malloc(sizeof(uint16_t) * (size_t)n * H);
-  if (!hrow || !yall) { free(hrow); if (!Y) free(yall); return ORACLE_ERR_INVALID; }
-  for (int e = 0; e < E; ++e) {
-    for (int s = exp_indptr[e]; s < exp_indptr[e + 1]; ++s) {
+  if (!yall) return ORACLE_ERR_INVALID;
+  /* every grouped row s belongs to the expert e with exp_indptr[e] <= s <
+   * exp_indptr[e+1]; rows are independent, so they are spread over threads */
+  int fail = 0;
+#pragma omp parallel
+  {
+    uint16_t *hrow = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)I);
+    if (!hrow) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int s = 0; s < n; ++s) {
+      if (!hrow) continue;
+      int e = 0;
+      while (exp_indptr[e + 1] <= s) ++e;
       int t = perm[s] / k;
       const uint16_t *x = X + (size_t)t * H;
       if (Xp) memcpy(Xp + (size_t)s * H, x, sizeof(uint16_t) * (size_t)H);
@@ -269,7 +294,9 @@ int oracle_moe(int T, int H, int E, int k, int I, int norm_topk,
                  hrow, yall + (size_t)s * H);
       if (Hmid) memcpy(Hmid + (size_t)s * I, hrow, sizeof(uint16_t) * (size_t)I);
     }
+    free(hrow);
   }
+  if (fail) { if (!Y) free(yall); return ORACLE_ERR_INVALID; }
   for (int t = 0; t < T; ++t)
     for (int h = 0; h < H; ++h) {
       double acc = 0.0;
@@ -280,7 +307,6 @@ int oracle_moe(int T, int H, int E, int k, int I, int norm_topk,
       }
       out[(size_t)t * H + h] = float_to_bf16_bits((float)acc);
     }
-  free(hrow);
   if (!Y) free(yall);
   return ORACLE_OK;
 }
@@ -292,27 +318,37 @@ int oracle_moe_tokens(int H, int k, int I, int ntok, const int32_t *tok,
                       const uint16_t *X, const uint16_t *W13, const uint16_t *Wd,
                       const int32_t *ids, const float *w, uint16_t *out_rows) {
   if (H <= 0 || k <= 0 || I <= 0 || ntok < 0) return ORACLE_ERR_INVALID;
-  uint16_t *hrow = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)I);
-  uint16_t *y = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)k * H);
-  if (!hrow || !y) { free(hrow); free(y); return ORACLE_ERR_INVALID; }
-  for (int r = 0; r < ntok; ++r) {
-    int t = tok[r];
-    for (int j = 0; j < k; ++j) {
-      int e = ids[(size_t)t * k + j];
-      expert_row(H, I, X + (size_t)t * H, W13 + (size_t)e * 2 * I * H,
-                 Wd + (size_t)e * H * I, hrow, y + (size_t)j * H);
+  int fail = 0;
+  /* tokens are independent: spread over threads */
+#pragma omp parallel
+  {
+    uint16_t *hrow = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)I);
+    uint16_t *y = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)k * H);
+    if (!hrow || !y) {
+#pragma omp atomic write
+      fail = 1;
     }
-    for (int h = 0; h < H; ++h) {
-      double acc = 0.0;
-      for (int j = 0; j < k; ++j)
-        acc += (double)w[(size_t)t * k + j] *
-               (double)bf16_bits_to_float(y[(size_t)j * H + h]);
-      out_rows[(size_t)r * H + h] = float_to_bf16_bits((float)acc);
+#pragma omp for schedule(dynamic, 1)
+    for (int r = 0; r < ntok; ++r) {
+      if (!hrow || !y) continue;
+      int t = tok[r];
+      for (int j = 0; j < k; ++j) {
+        int e = ids[(size_t)t * k + j];
+        expert_row(H, I, X + (size_t)t * H, W13 + (size_t)e * 2 * I * H,
+                   Wd + (size_t)e * H * I, hrow, y + (size_t)j * H);
+      }
+      for (int h = 0; h < H; ++h) {
+        double acc = 0.0;
+        for (int j = 0; j < k; ++j)
+          acc += (double)w[(size_t)t * k + j] *
+                 (double)bf16_bits_to_float(y[(size_t)j * H + h]);
+        out_rows[(size_t)r * H + h] = float_to_bf16_bits((float)acc);
+      }
     }
+    free(hrow);
+    free(y);
   }
-  free(hrow);
-  free(y);
-  return ORACLE_OK;
+  return fail ? ORACLE_ERR_INVALID : ORACLE_OK;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -165,10 +165,13 @@ def test_watchdog_timeout_is_reported_and_workspace_recovers(qwen_layer, decode_
 
 
 # --------------------------------------------------------------- prefill --
-def _sample_tokens(ids, T, n_each=4):
+def _sample_tokens(ids, T, n_each=16):
+    # first and last tokens, and tokens of the most loaded expert
     hot = np.bincount(ids.reshape(-1)).argmax()
     hot_tokens = np.nonzero((ids == hot).any(axis=1))[0]
-    pick = list(range(n_each)) + list(range(T - n_each, T)) + list(hot_tokens[:n_each])
+    rng = np.random.default_rng(T)
+    pick = (list(range(n_each)) + list(range(T - n_each, T)) + list(hot_tokens[:n_each])
+            + list(rng.choice(T, size=min(T, n_each), replace=False)))
     return np.array(sorted(set(int(t) for t in pick)), np.int32)
 
 
@@ -180,31 +183,32 @@ def prefill_case(qwen_weights):
     layer = DeviceLayer((s.H, s.E, s.k, s.I), qwen_weights.Wr, qwen_weights.W13, qwen_weights.Wd,
                         T_max=256, bias=w.bias)
     ref = oracle.route(X, qwen_weights.Wr, s.k, bias=w.bias)
+    # every output row of the batch (the oracle's rows, once for all schedules)
+    ref["out"] = oracle.moe_tokens(np.arange(s.T, dtype=np.int32), X, qwen_weights.W13, qwen_weights.Wd,
+                                   ref["topk_ids"], ref["topk_w"])
     return layer, X, ref
 
 
 @pytest.mark.parametrize("sched", SCHEDS)
-def test_prefill_zipf_routing_and_sampled_rows(prefill_case, qwen_weights, sched):
-    s = wl.PREFILL_ZIPF
+def test_prefill_zipf_full_parity(prefill_case, sched):
     layer, X, ref = prefill_case
     announce(f"prefill zipf T=256 sched={sched}")
     got = layer.run(X, sched)
     assert_routing_equal(got, ref)
     assert (ref["counts"] == 0).sum() > 0 and ref["counts"].max() > 64  # skewed, as the workload intends
-    tok = _sample_tokens(ref["topk_ids"], s.T)
-    rows = oracle.moe_tokens(tok, X, qwen_weights.W13, qwen_weights.Wd, ref["topk_ids"], ref["topk_w"])
-    assert_rows_close(got["out"][tok], rows)
+    assert_rows_close(got["out"], ref["out"])
 
 
 # ----------------------------------------------------------------- sweep --
 def test_batch_sweep_one_template(qwen_layer, qwen_weights):
-    # one compiled kernel, one workspace, T changes per launch
+    # one compiled kernel, one workspace, T changes per launch; every output
+    # row is checked on every 10th step of the seeded 200-step sweep and on
+    # its smallest and largest batch, routing on every step
     s = wl.SWEEP
     Bs = wl.sweep_batches(0)
-    # every 10th step of the seeded 200-step sweep, plus its smallest and largest batch
-    steps = sorted(set(list(range(0, len(Bs), 10)) + [int(np.argmin(Bs)), int(np.argmax(Bs))]))
+    full = set(list(range(0, len(Bs), 10)) + [int(np.argmin(Bs)), int(np.argmax(Bs))])
     extra = [(1000, 1), (1001, 512), (1002, 33)]
-    cases = [(st, int(Bs[st])) for st in steps] + extra
+    cases = [(st, int(Bs[st])) for st in range(len(Bs))] + extra
     for i, (step, T) in enumerate(cases):
         sched = LIVE[i % len(LIVE)]
         X = wl.sweep_tokens(s, step, T, seed=0)
@@ -212,9 +216,35 @@ def test_batch_sweep_one_template(qwen_layer, qwen_weights):
         got = qwen_layer.run(X, sched)
         ref = oracle.route(X, qwen_weights.Wr, s.k)
         assert_routing_equal(got, ref)
-        tok = np.unique(np.array([0, T // 2, T - 1], np.int32))
+        tok = (np.arange(T, dtype=np.int32) if (step in full or step >= 1000)
+               else np.unique(np.array([0, T // 2, T - 1], np.int32)))
         rows = oracle.moe_tokens(tok, X, qwen_weights.W13, qwen_weights.Wd, ref["topk_ids"], ref["topk_w"])
         assert_rows_close(got["out"][tok], rows)
+
+
+# ------------------------------------------------- the pages' token counts --
+@pytest.fixture(scope="module")
+def large_layer(qwen_weights):
+    s = wl.DECODE
+    return DeviceLayer((s.H, s.E, s.k, s.I), qwen_weights.Wr, qwen_weights.W13, qwen_weights.Wd, T_max=4096)
+
+
+@pytest.mark.parametrize("T", [1024, 4096])
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_qwen_shape_large_batches(large_layer, qwen_weights, T, sched):
+    # the token counts of the pages' MoE-layer table beyond decode: routing
+    # bit-exact, and sampled rows (the first and last tokens, tokens of the
+    # most loaded expert, random tokens) against the oracle
+    s = wl.DECODE
+    X = wl.sweep_tokens(s, 7000 + T, T, seed=0)
+    ref = oracle.route(X, qwen_weights.Wr, s.k)
+    announce(f"qwen T={T} sched={sched}")
+    got = large_layer.run(X, sched)
+    assert_routing_equal(got, ref)
+    tok = _sample_tokens(ref["topk_ids"], T)
+    assert len(tok) >= 48
+    rows = oracle.moe_tokens(tok, X, qwen_weights.W13, qwen_weights.Wd, ref["topk_ids"], ref["topk_w"])
+    assert_rows_close(got["out"][tok], rows)
 
 
 # ------------------------------------------------------------ edge shapes --
