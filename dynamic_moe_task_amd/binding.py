@@ -38,7 +38,7 @@ ETC_MAX_DIMS = 8
 
 EXPORTED = [
     "etensor_create", "etensor_instantiate", "etensor_shape", "etensor_destroy",
-    "etc_splitk_launch", "moe_layer_info", "moe_layer_workspace_size", "moe_workspace_init",
+    "etc_edge_compile", "etc_edge_index", "etc_splitk_launch", "moe_layer_info", "moe_layer_workspace_size", "moe_workspace_init",
     "moe_layer_launch", "etc_sync", "etc_last_error",
 ]
 
@@ -47,6 +47,14 @@ class EtcError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"etc error {code}: {msg}")
         self.code = code
+
+
+class Edge(ctypes.Structure):
+    """etc_edge: an edge spec compiled against an event tensor and a task grid."""
+    _fields_ = [("task_ndim", ctypes.c_int32), ("event_ndim", ctypes.c_int32),
+                ("src", ctypes.c_int32 * ETC_MAX_DIMS), ("stride", ctypes.c_int64 * ETC_MAX_DIMS),
+                ("task_shape", ctypes.c_int64 * ETC_MAX_DIMS), ("event_numel", ctypes.c_int64),
+                ("fan_in", ctypes.c_int64)]
 
 
 class MoeDesc(ctypes.Structure):
@@ -108,7 +116,11 @@ def lib():
         L.etensor_instantiate.argtypes = [P, ctypes.POINTER(I64)]
         L.etensor_shape.argtypes = [P, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_int), ctypes.POINTER(I64)]
         L.etensor_destroy.argtypes = [P]
-        L.etc_splitk_launch.argtypes = [P, I32, I32, I32, P, P, P, ctypes.c_int, P]
+        L.etc_edge_compile.argtypes = [P, ctypes.c_char_p, ctypes.POINTER(I64), ctypes.c_int, ctypes.POINTER(Edge)]
+        L.etc_edge_index.argtypes = [ctypes.POINTER(Edge), ctypes.POINTER(I64)]
+        L.etc_edge_index.restype = I64
+        L.etc_splitk_launch.argtypes = [P, I32, I32, I32, P, P, P, ctypes.POINTER(Edge), ctypes.POINTER(Edge),
+                                        ctypes.c_int, P]
         L.moe_layer_info.argtypes = [ctypes.POINTER(MoeDesc), ctypes.POINTER(MoeInfo)]
         L.moe_layer_workspace_size.argtypes = [ctypes.POINTER(MoeDesc)]
         L.moe_layer_workspace_size.restype = ctypes.c_size_t
@@ -118,7 +130,7 @@ def lib():
         L.etc_last_error.argtypes = []
         L.etc_last_error.restype = ctypes.c_char_p
         for name in ["etensor_create", "etensor_instantiate", "etensor_shape", "etensor_destroy",
-                     "etc_splitk_launch", "moe_layer_info", "moe_workspace_init", "moe_layer_launch",
+                     "etc_edge_compile", "etc_splitk_launch", "moe_layer_info", "moe_workspace_init", "moe_layer_launch",
                      "etc_sync"]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -160,8 +172,22 @@ def etensor_destroy(h) -> None:
     check(lib().etensor_destroy(h))
 
 
-def etc_splitk_launch(ev, n, nsplit, bk, A_ptr, B_ptr, C_ptr, sched, stream) -> int:
-    return lib().etc_splitk_launch(ev, n, nsplit, bk, A_ptr, B_ptr, C_ptr, sched, stream)
+def etc_edge_compile(ev, spec: str, task_shape) -> Edge:
+    e = Edge()
+    arr = (ctypes.c_int64 * len(task_shape))(*task_shape)
+    check(lib().etc_edge_compile(ev, spec.encode(), arr, len(task_shape), ctypes.byref(e)))
+    return e
+
+
+def etc_edge_index(edge: Edge, coord) -> int:
+    arr = (ctypes.c_int64 * len(coord))(*coord)
+    return int(lib().etc_edge_index(ctypes.byref(edge), arr))
+
+
+def etc_splitk_launch(ev, n, nsplit, bk, A_ptr, B_ptr, C_ptr, notify_edge: Edge, wait_edge: Edge, sched,
+                      stream) -> int:
+    return lib().etc_splitk_launch(ev, n, nsplit, bk, A_ptr, B_ptr, C_ptr, ctypes.byref(notify_edge),
+                                   ctypes.byref(wait_edge), sched, stream)
 
 
 # ---------------------------------------------------------------- MoE layer --

@@ -326,12 +326,13 @@ ETC_HD void run_moe(K& tk, const Queue& q, const MoeGraph& g, Shared& sh) {
 
 // The split-K row-sum example (Event Tensor pages, Fig. 3; podcast cue 3)
 // under the same queue: partial_sum(i, j) for every (i, j) is the ready
-// prefix (pop index i * nsplit + j); the notify that completes event i
-// (nsplit arrivals, edge "ij->i") pushes final_sum(i) (edge "i->i").  The
-// total n * (nsplit + 1) is known at launch.  Each popped slot is cleared
-// again, so the ring is at rest for the next launch once the control words
-// are reset.  Descriptors: type in bits 29..31, the 29-bit row or pair index
-// below.
+// prefix (pop index i * nsplit + j); it notifies the event element its
+// out-edge maps (i, j) to (tk.notify_elem), and the notify that completes an
+// element (wait_count arrivals) pushes the final_sum that waits on it
+// (tk.waiter, the inverse of the in-edge).  The total n * (nsplit + 1) is
+// known at launch.  Each popped slot is cleared again, so the ring is at
+// rest for the next launch once the control words are reset.  Descriptors:
+// type in bits 29..31, the 29-bit row or pair index below.
 enum : int { T_SK_PART = 1, T_SK_FINAL = 2 };
 // the last workgroup of a launch returns the control words to rest
 template <class P>
@@ -343,7 +344,7 @@ ETC_HD void splitk_reset(const Queue& q) {
 ETC_HD uint32_t sk_desc(int type, uint32_t v) { return ((uint32_t)type << 29) | (v & 0x1fffffffu); }
 
 template <class P, class K>
-ETC_HD void run_splitk(K& tk, const Queue& q, uint32_t nsplit, uint32_t* ev, Shared& sh) {
+ETC_HD void run_splitk(K& tk, const Queue& q, uint32_t nsplit, uint32_t wait_count, uint32_t* ev, Shared& sh) {
   const int tid = P::tid();
   uint32_t idx = 0;
   if (tid == 0) idx = P::add(q.head, 1u);
@@ -365,12 +366,15 @@ ETC_HD void run_splitk(K& tk, const Queue& q, uint32_t nsplit, uint32_t* ev, Sha
     if (!d) return;
     const uint32_t v = d & 0x1fffffffu;
     if ((int)(d >> 29) == T_SK_PART) {
-      const uint32_t i = v / nsplit;
-      tk.partial(i, v % nsplit);
+      const uint32_t i = v / nsplit, j = v % nsplit;
+      tk.partial(i, j);
       P::publish();
-      if (tid == 0 && notify<P>(q, ev + i, nsplit)) {
-        const int64_t s = reserve<P>(q, 1u);
-        if (s >= 0) P::put(q.slot + s, sk_desc(T_SK_FINAL, i));
+      if (tid == 0) {
+        const uint32_t e = tk.notify_elem(i, j);
+        if (notify<P>(q, ev + e, wait_count)) {
+          const int64_t s = reserve<P>(q, 1u);
+          if (s >= 0) P::put(q.slot + s, sk_desc(T_SK_FINAL, tk.waiter(e)));
+        }
       }
     } else {
       tk.final_sum(v);

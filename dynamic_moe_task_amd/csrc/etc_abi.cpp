@@ -59,9 +59,13 @@ int status_to_code(uint32_t st) {
 }
 
 // Per-device facts for grid sizing and the watchdog.
+struct OccEntry {
+  int sched, lds, blocks_per_cu;
+};
 struct DeviceFacts {
   int cus = 0;
   int wall_khz = 0;  // rate of the constant wall clock the kernels read
+  std::vector<OccEntry> occ;  // persistent kernels' occupancy, queried once per (schedule, LDS bytes)
 };
 std::mutex g_dev_mu;
 std::vector<DeviceFacts> g_dev;
@@ -143,9 +147,21 @@ int persistent_grid(int sched, int lds, int* grid, int* solo = nullptr) {
   int cus = 0;
   int rc = device_cus(&cus);
   if (rc) return rc;
-  int nb = 0;
-  int e = moe_persistent_occupancy(sched, lds, &nb);
-  if (e != hipSuccess) return hip_fail((hipError_t)e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  int nb = -1;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    for (const OccEntry& o : g_dev[dev].occ)
+      if (o.sched == sched && o.lds == lds) nb = o.blocks_per_cu;
+  }
+  if (nb < 0) {  // first launch of this schedule and LDS size on this device
+    int e = moe_persistent_occupancy(sched, lds, &nb);
+    if (e != hipSuccess) return hip_fail((hipError_t)e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    g_dev[dev].occ.push_back({sched, lds, nb});
+  }
   if (nb < 1) return fail(ETC_ERR_UNSUPPORTED, "persistent kernel does not fit on a CU (lds %d)", lds);
   const int cap = wg_per_cu_cap();
   if (nb > cap) nb = cap;
@@ -268,9 +284,70 @@ static int etensor_device_counters(etc_etensor* et, int64_t numel, void* stream)
   return ETC_OK;
 }
 
+// ================================================================= edges ==
+extern "C" int etc_edge_compile(const etc_etensor* et, const char* spec, const int64_t* task_shape, int task_ndim,
+                                etc_edge* out) {
+  if (!et || !spec || !task_shape || !out) return fail(ETC_ERR_INVALID, "NULL argument");
+  if (!et->instantiated) return fail(ETC_ERR_INVALID, "event tensor is not instantiated");
+  if (task_ndim < 1 || task_ndim > ETC_MAX_DIMS)
+    return fail(ETC_ERR_INVALID, "task_ndim %d outside [1, %d]", task_ndim, ETC_MAX_DIMS);
+  const char* arrow = std::strstr(spec, "->");
+  if (!arrow || std::strstr(arrow + 2, "->")) return fail(ETC_ERR_INVALID, "edge \"%s\": expected one \"->\"", spec);
+  std::string L, R;
+  for (const char* c = spec; *c; ++c) {
+    if (c == arrow || c == arrow + 1) continue;
+    if (*c == ' ') continue;
+    if (*c < 'a' || *c > 'z') return fail(ETC_ERR_INVALID, "edge \"%s\": '%c' is not a lowercase letter", spec, *c);
+    (c < arrow ? L : R).push_back(*c);
+  }
+  if ((int)L.size() != task_ndim)
+    return fail(ETC_ERR_INVALID, "edge \"%s\" names %zu task dimensions, the grid has %d", spec, L.size(), task_ndim);
+  if ((int)R.size() != et->ndim)
+    return fail(ETC_ERR_INVALID, "edge \"%s\" names %zu event dimensions, the tensor has %d", spec, R.size(),
+                et->ndim);
+  for (size_t a = 0; a < L.size(); ++a)
+    for (size_t b = a + 1; b < L.size(); ++b)
+      if (L[a] == L[b]) return fail(ETC_ERR_INVALID, "edge \"%s\": task letter '%c' repeats", spec, L[a]);
+  for (size_t a = 0; a < R.size(); ++a)
+    for (size_t b = a + 1; b < R.size(); ++b)
+      if (R[a] == R[b]) return fail(ETC_ERR_INVALID, "edge \"%s\": event letter '%c' repeats", spec, R[a]);
+  for (int i = 0; i < task_ndim; ++i)
+    if (task_shape[i] < 1) return fail(ETC_ERR_INVALID, "task_shape[%d] = %lld", i, (long long)task_shape[i]);
+  etc_edge e{};
+  e.task_ndim = task_ndim;
+  e.event_ndim = et->ndim;
+  for (int i = 0; i < task_ndim; ++i) e.task_shape[i] = task_shape[i];
+  int64_t stride = 1;
+  for (int d = et->ndim - 1; d >= 0; --d) {
+    const size_t pos = L.find(R[d]);
+    if (pos == std::string::npos)
+      return fail(ETC_ERR_INVALID, "edge \"%s\": event letter '%c' is not a task letter", spec, R[d]);
+    if (task_shape[pos] != et->bound[d])
+      return fail(ETC_ERR_INVALID, "edge \"%s\": task dimension '%c' has %lld, event dimension %d has %lld", spec,
+                  R[d], (long long)task_shape[pos], d, (long long)et->bound[d]);
+    e.src[d] = (int32_t)pos;
+    e.stride[d] = stride;
+    stride *= et->bound[d];
+  }
+  e.event_numel = stride;
+  e.fan_in = 1;
+  for (int i = 0; i < task_ndim; ++i)
+    if (R.find(L[i]) == std::string::npos) e.fan_in *= task_shape[i];
+  *out = e;
+  return ETC_OK;
+}
+
+extern "C" int64_t etc_edge_index(const etc_edge* edge, const int64_t* task_coord) {
+  if (!edge || !task_coord) return -1;
+  int64_t f = 0;
+  for (int d = 0; d < edge->event_ndim; ++d) f += task_coord[edge->src[d]] * edge->stride[d];
+  return f;
+}
+
 extern "C" int etc_splitk_launch(etc_etensor* ev, int32_t n, int32_t nsplit, int32_t bk, const int32_t* A,
-                                 int32_t* B, int32_t* C, int sched, void* stream) {
-  if (!ev || !A || !B || !C) return fail(ETC_ERR_INVALID, "NULL argument");
+                                 int32_t* B, int32_t* C, const etc_edge* notify_edge, const etc_edge* wait_edge,
+                                 int sched, void* stream) {
+  if (!ev || !A || !B || !C || !notify_edge || !wait_edge) return fail(ETC_ERR_INVALID, "NULL argument");
   if (sched != ETC_SCHED_STATIC && sched != ETC_SCHED_DYNAMIC)
     return fail(ETC_ERR_UNSUPPORTED, "split-K runs under STATIC or DYNAMIC only");
   if (sched == ETC_SCHED_DYNAMIC)
@@ -279,11 +356,24 @@ extern "C" int etc_splitk_launch(etc_etensor* ev, int32_t n, int32_t nsplit, int
                 "dynamic schedule, whose launch did not complete on the GPU");
   if (n < 1 || nsplit < 1 || bk < 1 || (int64_t)n * nsplit > (1 << 28))
     return fail(ETC_ERR_INVALID, "bad sizes n=%d nsplit=%d bk=%d", n, nsplit, bk);
-  if (!ev->instantiated || ev->ndim != 1 || ev->bound[0] != n)
-    return fail(ETC_ERR_INVALID, "event tensor must be instantiated to shape [n=%d]", n);
-  if (ev->wait_count != nsplit)
-    return fail(ETC_ERR_INVALID, "event wait_count %d != nsplit %d", ev->wait_count, nsplit);
-  int rc = etensor_device_counters(ev, n, stream);
+  if (!ev->instantiated) return fail(ETC_ERR_INVALID, "event tensor is not instantiated");
+  const int64_t numel = etensor_numel(ev);
+  const etc_edge& ne = *notify_edge;
+  const etc_edge& we = *wait_edge;
+  if (ne.task_ndim != 2 || ne.task_shape[0] != n || ne.task_shape[1] != nsplit)
+    return fail(ETC_ERR_INVALID, "notify edge must be compiled for the partial-sum grid [n=%d, nsplit=%d]", n, nsplit);
+  if (we.task_ndim != 1 || we.task_shape[0] != n)
+    return fail(ETC_ERR_INVALID, "wait edge must be compiled for the final-sum grid [n=%d]", n);
+  if (ne.event_ndim != ev->ndim || we.event_ndim != ev->ndim || ne.event_numel != numel || we.event_numel != numel)
+    return fail(ETC_ERR_INVALID, "edges were compiled for another instantiation of the event tensor");
+  if (ev->wait_count != ne.fan_in)
+    return fail(ETC_ERR_INVALID, "event wait_count %d != the notify edge's fan-in %lld", ev->wait_count,
+                (long long)ne.fan_in);
+  // every element is waited on by exactly one final sum (it returns the
+  // counter to rest after its wait, and the dynamic schedule pushes it)
+  if (we.fan_in != 1 || numel != n)
+    return fail(ETC_ERR_INVALID, "wait edge must pair each event element with one final sum");
+  int rc = etensor_device_counters(ev, numel, stream);
   if (rc) return rc;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -317,8 +407,8 @@ extern "C" int etc_splitk_launch(etc_etensor* ev, int32_t n, int32_t nsplit, int
   uint64_t ticks = 0;
   rc = watchdog_ticks(0, &ticks);
   if (rc) return rc;
-  e = (hipError_t)launch_splitk(n, nsplit, bk, A, B, C, ev->counters, sk.ctl, sk.queue, sk.q_cap, sched, nb * cus,
-                                ticks, stream);
+  e = (hipError_t)launch_splitk(n, nsplit, bk, A, B, C, ev->counters, ne, we, ev->wait_count, sk.ctl, sk.queue,
+                                sk.q_cap, sched, nb * cus, ticks, stream);
   if (e != hipSuccess) return hip_fail(e, "split-K launch");
   add_pending(stream, sk.ctl + SK_REPORT);
   return ETC_OK;
@@ -375,7 +465,10 @@ extern "C" int moe_workspace_init(const etc_moe_desc* d, void* ws, size_t bytes,
   return ETC_OK;
 }
 
-extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a, int sched, void* stream) {
+// One launch on the workspace `ws`: validation of everything but the
+// workspace pointer, the kernel parameters, the grid and the launch.
+static int layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a, int sched, void* stream,
+                        uint8_t* ws, size_t ws_bytes) {
   int rc = desc_check(d);
   if (rc) return rc;
   if (!a) return fail(ETC_ERR_INVALID, "args is NULL");
@@ -387,7 +480,7 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
     return fail(ETC_ERR_UNSUPPORTED,
                 "the dynamic (push/pop) schedule is switched off: its launch did not complete on the GPU "
                 "and the cause is not yet found");
-  const void* bf[] = {a->x, a->w_router, a->w13, a->w2, a->out, a->workspace};
+  const void* bf[] = {a->x, a->w_router, a->w13, a->w2, a->out, ws};
   const char* bfn[] = {"x", "w_router", "w13", "w2", "out", "workspace"};
   for (int i = 0; i < 6; ++i)
     if (!bf[i] || !aligned16(bf[i])) return fail(ETC_ERR_INVALID, "%s is NULL or not 16-byte aligned", bfn[i]);
@@ -400,10 +493,9 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
   if (a->trace && (!aligned4(a->trace) || a->trace_records == 0))
     return fail(ETC_ERR_INVALID, "trace misaligned or trace_records is 0");
   const MoeLayout L = moe_layout(*d);
-  if (a->workspace_bytes < (size_t)L.total_bytes)
-    return fail(ETC_ERR_INVALID, "workspace has %zu bytes, needs %lld", a->workspace_bytes, (long long)L.total_bytes);
+  if (ws_bytes < (size_t)L.total_bytes)
+    return fail(ETC_ERR_INVALID, "workspace has %zu bytes, needs %lld", ws_bytes, (long long)L.total_bytes);
 
-  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
   MoeParams p{};
   p.x = static_cast<const uint16_t*>(a->x);
   p.wr = static_cast<const uint16_t*>(a->w_router);
@@ -470,6 +562,11 @@ extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_
   if (e != hipSuccess) return hip_fail((hipError_t)e, "MoE launch");
   add_pending(stream, p.ctrl + C_REPORT);
   return ETC_OK;
+}
+
+extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a, int sched, void* stream) {
+  if (!a) return fail(ETC_ERR_INVALID, "args is NULL");
+  return layer_launch(d, T, a, sched, stream, static_cast<uint8_t*>(a->workspace), a->workspace_bytes);
 }
 
 extern "C" int etc_sync(void* stream) {

@@ -61,7 +61,7 @@ enum : int {
   W_TAIL = 96,
   W_TOTAL = 128,
   W_BAR_COUNT = 160,
-  W_BAR_GEN = 192,
+  W_BAR_RELEASE = 192,
   W_EV_ROUTE = 224,
   W_EV_SCAN = 256,
   W_CLAIM_G1 = 288,  // ORDERED: 8 claim counters for the G tiles, 32 words apart
@@ -183,8 +183,9 @@ struct MoeParams {
 int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes, void* stream);
 int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream);
 int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu);
-int launch_splitk(int n, int nsplit, int bk, const int32_t* A, int32_t* B, int32_t* C,
-                  int32_t* ev, uint32_t* ctl, uint32_t* queue, int64_t q_cap, int sched, int grid,
+int launch_splitk(int n, int nsplit, int bk, const int32_t* A, int32_t* B, int32_t* C, int32_t* ev,
+                  const etc_edge& notify_edge, const etc_edge& wait_edge, int32_t wait_count, uint32_t* ctl,
+                  uint32_t* queue, int64_t q_cap, int sched, int grid,
                   uint64_t budget, void* stream);
 int splitk_occupancy(int sched, int* blocks_per_cu);
 

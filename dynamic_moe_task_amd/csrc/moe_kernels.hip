@@ -1300,30 +1300,25 @@ __device__ __forceinline__ void after_scan(const MoeParams& p, const Ctx& c, int
 }
 
 // ==================================================== schedules ==========
-// Grid-wide barrier (BARRIER comparator only): arrival counter plus a
-// generation word; the last arrival resets the counter and bumps the
-// generation.  Bounded by the same watchdog as every other wait.
-__device__ __forceinline__ bool grid_barrier(const Ctx& c, int parties) {
+// Grid-wide barrier (BARRIER comparator only).  Two words that only grow
+// (the counter set is zeroed before every launch): the arrival count, and
+// the release word, on its own line so that the waiters' polls do not slow
+// the arrivals' atomics.  Barrier b completes at the sum of the party counts
+// of barriers 1..b, which every workgroup reaching barrier b holds in
+// `target` (all of them passed the same earlier barriers); the arrival that
+// brings the count there stores that sum into the release word, which the
+// others poll.  Barrier b + 1 cannot complete before barrier b's release, so
+// the release word only grows.  No reset, no generation: no arrival can be
+// lost to a late reset.  Bounded by the same watchdog as every other wait.
+__device__ __forceinline__ bool grid_barrier(const Ctx& c, int parties, uint32_t& target) {
   wg_publish();
+  target += (uint32_t)parties;
   int fail = 0;
   if (threadIdx.x == 0) {
-    uint32_t* cnt = c.set + W_BAR_COUNT;
-    uint32_t* gen = c.set + W_BAR_GEN;
-    const uint32_t g0 = ld_relaxed(gen);
-    const uint32_t old = add_relaxed(cnt, 1u);
-    if (old == (uint32_t)parties - 1u) {
-      xchg_relaxed(cnt, 0u);
-      add_relaxed(gen, 1u);
-    } else {
-      const uint64_t t0 = now_ticks();
-      for (uint32_t spins = 1; ld_relaxed(gen) == g0; ++spins) {
-        if ((spins & 7u) == 0u) {
-          if (ld_relaxed(c.status) & ST_ABORT) { fail = 1; break; }
-          if (now_ticks() - t0 > c.budget) { or_relaxed(c.status, ST_TIMEOUT | ST_ABORT); fail = 1; break; }
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
+    if (add_relaxed(c.set + W_BAR_COUNT, 1u) + 1u == target)
+      (void)xchg_relaxed(c.set + W_BAR_RELEASE, target);
+    else
+      fail = spin_until_geq(c.set + W_BAR_RELEASE, target, c.status, c.budget) ? 0 : 1;
   }
   fail = __syncthreads_or(fail);
   return fail == 0;
@@ -1751,6 +1746,7 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   const int G = gridDim.x, w = blockIdx.x;
   float* red = reinterpret_cast<float*>(smem);
   constexpr bool EV = (MODE == MODE_STATIC || MODE == MODE_ORDERED);
+  uint32_t bar = 0;  // BARRIER: arrivals that complete the next grid barrier
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
   int64_t off = 0;
@@ -1763,7 +1759,7 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
     trace_task(p, TT_R, i / c.nET, i % c.nET, tw, ts, tb);
   }
   off += c.nR;
-  if (!EV && !grid_barrier(c, G)) return;
+  if (!EV && !grid_barrier(c, G, bar)) return;
   for (int i = first_of(w, off, G); i < c.nK; i += G) {
     if (tr) tw = now_ticks();
     if (EV && !wg_wait(ev_logit(p, c, i), (uint32_t)c.nET, c.status, c.budget)) return;
@@ -1775,7 +1771,7 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
     trace_task(p, TT_K, i, 0, tw, ts, tb);
   }
   off += c.nK;
-  if (!EV && !grid_barrier(c, G)) return;
+  if (!EV && !grid_barrier(c, G, bar)) return;
   if (first_of(w, off, G) == 0) {
     if (tr) tw = now_ticks();
     if (EV && !wg_wait(c.set + W_EV_ROUTE, (uint32_t)c.nK, c.status, c.budget)) return;
@@ -1822,7 +1818,7 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
     if (sh.claim[3] == 0u) return;  // aborting
     nrt = (int)sh.claim[3] - 1;
   } else {
-    if (!grid_barrier(c, G)) return;
+    if (!grid_barrier(c, G, bar)) return;
     nrt = (int)ld_relaxed(p.meta + M_NRT);
   }
   const int nG1 = nrt * c.nN1, nG2 = nrt * c.nN2;
@@ -1856,7 +1852,7 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
     }
   }
   off += nG1;
-  if (!EV && !grid_barrier(c, Gt)) return;
+  if (!EV && !grid_barrier(c, Gt, bar)) return;
   if (EV) {
     run_g2_static<WG>(p, c, red, first_of(w, off, Gt), nG2, Gt, lr);
   } else {
@@ -1871,7 +1867,7 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
     }
   }
   off += nG2;
-  if (!EV && !grid_barrier(c, Gt)) return;
+  if (!EV && !grid_barrier(c, Gt, bar)) return;
   }
   // C reads S's routing outputs (slot, row -> tile map)
   if (local && first_of(w, off, Gt) < c.nC && !wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;

@@ -1,14 +1,16 @@
 // The split-K row-sum example through the device event runtime (Event
 // Tensor, arXiv 2604.13327, Fig. 3; podcast cue 3):
 //   partial_sum(i, j): B[i, j] = sum of A[i, j*bk .. (j+1)*bk), then notify
-//                      event i                                 (edge "ij->i")
-//   final_sum(i)     : wait on event i (wait_count = nsplit),  (edge "i->i")
-//                      C[i] = sum_j B[i, j]
-// Row i's final sum starts as soon as its own partial sums land, whatever the
-// other rows are doing.
+//                      the event element of its out-edge     (the pages: "ij->i")
+//   final_sum(i)     : wait on the element of its in-edge      (the pages: "i->i")
+//                      until wait_count notifies, then C[i] = sum_j B[i, j]
+// The edges arrive compiled (etc_edge_compile): an element index is
+// sum_d coord[src[d]] * stride[d] of the task's coordinate.  Row i's final
+// sum starts as soon as its own partial sums land, whatever the other rows
+// are doing.
 //
-// Counters: final_sum(i) is the only waiter of event i, so after its wait it
-// returns the counter to zero; the control words (queue head / tail, done
+// Counters: final_sum(i) is the only waiter of its element, so after its
+// wait it returns the counter to zero; the control words (queue head / tail, done
 // count) are returned to zero by the last workgroup to finish; each queue
 // slot is cleared by the workgroup that pops it.  The next launch therefore
 // finds everything at rest without a host-side memset.
@@ -25,6 +27,8 @@ struct SkParams {
   int32_t* B;
   int32_t* C;
   uint32_t* ev;
+  etc_edge ne, we;      // out-edge of partial_sum (grid [n, nsplit]), in-edge of final_sum (grid [n])
+  uint32_t wait_count;  // notifies that complete an element (the out-edge's fan-in)
   uint32_t* ctl;
   uint32_t* queue;
   int64_t q_cap;
@@ -64,19 +68,29 @@ __device__ void sk_final(const SkParams& p, int i, int* tmp) {
   if (threadIdx.x == 0) p.C[i] = v;
 }
 
-// notify event i; true if this notify released it
-__device__ __forceinline__ bool sk_notify(const SkParams& p, int i) {
-  const uint32_t old = add_relaxed(p.ev + i, 1u);
-  if (old + 1u > (uint32_t)p.nsplit) or_relaxed(p.ctl + SK_STATUS, ST_OVER_NOTIFY | ST_ABORT);
-  return old + 1u == (uint32_t)p.nsplit;
+// the element an edge maps a task coordinate to
+__device__ __forceinline__ uint32_t edge_elem(const etc_edge& e, int c0, int c1) {
+  int64_t f = 0;
+  for (int d = 0; d < e.event_ndim; ++d) f += (int64_t)(e.src[d] == 0 ? c0 : c1) * e.stride[d];
+  return (uint32_t)f;
+}
+// notify element e; true if this notify released it
+__device__ __forceinline__ bool sk_notify(const SkParams& p, uint32_t e) {
+  const uint32_t old = add_relaxed(p.ev + e, 1u);
+  if (old + 1u > p.wait_count) or_relaxed(p.ctl + SK_STATUS, ST_OVER_NOTIFY | ST_ABORT);
+  return old + 1u == p.wait_count;
 }
 
 struct SkTasks {
   const SkParams& p;
   int* tmp;
+  __device__ __forceinline__ uint32_t notify_elem(uint32_t i, uint32_t j) { return edge_elem(p.ne, (int)i, (int)j); }
+  // the in-edge pairs every element with one final sum (the host checked):
+  // a 1-d grid onto a 1-d tensor, element e is waited on by final_sum(e)
+  __device__ __forceinline__ uint32_t waiter(uint32_t e) { return e; }
   __device__ __forceinline__ void partial(uint32_t i, uint32_t j) { sk_partial(p, (int)i, (int)j, tmp); }
   __device__ __forceinline__ void final_sum(uint32_t i) {
-    if (threadIdx.x == 0) xchg_relaxed(p.ev + i, 0u);  // sole waiter: back to rest
+    if (threadIdx.x == 0) xchg_relaxed(p.ev + edge_elem(p.we, (int)i, 0), 0u);  // sole waiter: back to rest
     sk_final(p, (int)i, tmp);
   }
 };
@@ -100,13 +114,15 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
   if (MODE == ETC_SCHED_STATIC) {
     // phase-ordered lists: all partial sums, then all final sums
     for (int t = w; t < nP; t += G) {
-      sk_partial(p, t / p.nsplit, t % p.nsplit, tmp);
+      const int i = t / p.nsplit, j = t % p.nsplit;
+      sk_partial(p, i, j, tmp);
       wg_publish();
-      if (threadIdx.x == 0) sk_notify(p, t / p.nsplit);
+      if (threadIdx.x == 0) sk_notify(p, edge_elem(p.ne, i, j));
     }
     for (int i = (w - nP % G + G) % G; i < p.n; i += G) {
-      if (!wg_wait(p.ev + i, (uint32_t)p.nsplit, status, p.budget)) break;
-      if (threadIdx.x == 0) xchg_relaxed(p.ev + i, 0u);  // sole waiter: back to rest
+      const uint32_t e = edge_elem(p.we, i, 0);
+      if (!wg_wait(p.ev + e, p.wait_count, status, p.budget)) break;
+      if (threadIdx.x == 0) xchg_relaxed(p.ev + e, 0u);  // sole waiter: back to rest
       sk_final(p, i, tmp);
     }
   } else {
@@ -114,7 +130,7 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
     // notify that completes event i pushes final_sum(i) at once
     __shared__ dyn::Shared dsh;
     SkTasks tk{p, tmp};
-    dyn::run_splitk<DevPlat>(tk, q, (uint32_t)p.nsplit, p.ev, dsh);
+    dyn::run_splitk<DevPlat>(tk, q, (uint32_t)p.nsplit, p.wait_count, p.ev, dsh);
   }
   wg_publish();
   if (threadIdx.x == 0) {
@@ -129,11 +145,14 @@ __global__ void __launch_bounds__(kThreads) splitk_persistent(SkParams p) {
 }
 
 int launch_splitk(int n, int nsplit, int bk, const int32_t* A, int32_t* B, int32_t* C, int32_t* ev,
-                  uint32_t* ctl, uint32_t* queue, int64_t q_cap, int sched, int grid, uint64_t budget,
-                  void* stream) {
+                  const etc_edge& notify_edge, const etc_edge& wait_edge, int32_t wait_count, uint32_t* ctl,
+                  uint32_t* queue, int64_t q_cap, int sched, int grid, uint64_t budget, void* stream) {
   SkParams p;
   p.A = A; p.B = B; p.C = C;
   p.ev = reinterpret_cast<uint32_t*>(ev);
+  p.ne = notify_edge;
+  p.we = wait_edge;
+  p.wait_count = (uint32_t)wait_count;
   p.ctl = ctl;
   p.queue = queue;
   p.q_cap = q_cap;

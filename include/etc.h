@@ -111,18 +111,61 @@ int etensor_shape(const etc_etensor* et, int64_t* shape_out, int* ndim_out, int6
 /* Release the handle and any counters the library allocated for it.        */
 int etensor_destroy(etc_etensor* et);
 
+/* --------------------------------------------------------------- edges -- */
+/* An edge wires a grid of tasks to an event tensor [Fig. 3; podcast cue 3].
+ * It is written "<task letters>-><event letters>": one distinct lowercase
+ * letter per dimension of the task grid on the left, and on the right one
+ * letter per dimension of the event tensor, each naming the task dimension
+ * whose coordinate indexes that event dimension.  Task (c_0, c_1, ...) then
+ * touches the event element whose d-th coordinate is c[src[d]].  As an
+ * out-edge every task notifies the element it touches, so an element
+ * receives one notify per task that maps to it: fan_in, the product of the
+ * task-grid sizes of the letters missing on the right.  As an in-edge the
+ * task waits on the element it touches.  "ij->i": task (i, j) notifies event
+ * i; "i->i": task i waits on event i.                                       */
+typedef struct {
+  int32_t task_ndim;                /* letters left of "->"                    */
+  int32_t event_ndim;               /* letters right of "->" (the tensor's ndim) */
+  int32_t src[ETC_MAX_DIMS];        /* event dimension d is task coordinate src[d] */
+  int64_t stride[ETC_MAX_DIMS];     /* row-major element stride of event dimension d */
+  int64_t task_shape[ETC_MAX_DIMS]; /* the task grid the edge was compiled for */
+  int64_t event_numel;              /* elements of the instantiated tensor     */
+  int64_t fan_in;                   /* tasks that touch one event element      */
+} etc_edge;
+
+/* Compile `spec` (host string) against the instantiated event tensor `et`
+ * and a task grid of shape task_shape[task_ndim] (host array).  The task
+ * grid's size along each letter on the right must equal the event tensor's
+ * size along that dimension.  Host only: makes no HIP call.
+ * Errors: ETC_ERR_INVALID (syntax; a repeated, unknown or non-lowercase
+ * letter; rank or size mismatch; `et` not instantiated; NULL argument).      */
+int etc_edge_compile(const etc_etensor* et, const char* spec, const int64_t* task_shape, int task_ndim,
+                     etc_edge* out);
+
+/* The flat event element a task at task_coord (host array of task_ndim
+ * entries) touches through `edge`: sum_d task_coord[src[d]] * stride[d], the
+ * index the kernels compute.  Returns -1 for a NULL argument.               */
+int64_t etc_edge_index(const etc_edge* edge, const int64_t* task_coord);
+
 /* The split-K row-sum example of Fig. 3 (podcast cue 3), run through the
- * same device runtime as the MoE layer: partial_sum(i, j) writes
- * B[i, j] = sum of A[i, j*bk .. (j+1)*bk) and notifies event i (edge
- * "ij->i"); final_sum(i) waits on event i (edge "i->i") and writes
- * C[i] = sum_j B[i, j].  `ev` must be instantiated to shape [n] with
- * wait_count == nsplit.  A is [n, nsplit*bk] int32, B [n, nsplit], C [n]
- * (device).  sched: ETC_SCHED_STATIC or ETC_SCHED_DYNAMIC.  Asynchronous;
- * errors found in the kernel are reported by etc_sync.
- * Errors: ETC_ERR_INVALID (shape / wait_count mismatch, bad sizes),
- * ETC_ERR_UNSUPPORTED (sched), ETC_ERR_HIP.                                  */
+ * same device runtime as the MoE layer, its event wiring given by compiled
+ * edges: partial_sum(i, j) writes B[i, j] = sum of A[i, j*bk .. (j+1)*bk)
+ * and notifies the element `notify_edge` maps (i, j) to (the pages' wiring:
+ * "ij->i" over a task grid [n, nsplit]); final_sum(i) waits on the element
+ * `wait_edge` maps i to ("i->i" over a task grid [n]) and writes
+ * C[i] = sum_j B[i, j].  `ev` must be instantiated, with wait_count equal to
+ * notify_edge's fan_in; under DYNAMIC the wait edge must pair every element
+ * with exactly one final_sum (then the notify that completes an element
+ * pushes that task).  A is [n, nsplit*bk] int32, B [n, nsplit], C [n]
+ * (device); the edges are host structs.  sched: ETC_SCHED_STATIC or
+ * ETC_SCHED_DYNAMIC.  Asynchronous; errors found in the kernel are reported
+ * by etc_sync.
+ * Errors: ETC_ERR_INVALID (edges that do not fit the task grids or the
+ * tensor, wait_count != fan_in, bad sizes), ETC_ERR_UNSUPPORTED (sched),
+ * ETC_ERR_HIP.                                                              */
 int etc_splitk_launch(etc_etensor* ev, int32_t n, int32_t nsplit, int32_t bk, const int32_t* A,
-                      int32_t* B, int32_t* C, int sched, void* stream);
+                      int32_t* B, int32_t* C, const etc_edge* notify_edge, const etc_edge* wait_edge,
+                      int sched, void* stream);
 
 /* ------------------------------------------------------------ MoE layer -- */
 /* Layer shape.  Router: logits = x @ w_router^T (+ b_router), top-k over E,

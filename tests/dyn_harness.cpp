@@ -298,6 +298,9 @@ struct SkSim {
 SkSim sk;
 
 struct SkTasks {
+  // the pages' wiring: out-edge "ij->i", in-edge "i->i"
+  uint32_t notify_elem(uint32_t i, uint32_t) { return i; }
+  uint32_t waiter(uint32_t e) { return e; }
   void partial(uint32_t i, uint32_t j) {
     Host::barrier();
     if (t_wave == 0) {
@@ -447,7 +450,7 @@ int splitk_main(int argc, char** argv) {
     q.budget = (uint64_t)std::max(2, opt.timeout_s / 3) * 1000000000ull;
     run_grid(G, [&](int) {
       SkTasks tk;
-      run_splitk<Host>(tk, q, sk.nsplit, sk.ev.data(), t_wg->sh);
+      run_splitk<Host>(tk, q, sk.nsplit, sk.nsplit, sk.ev.data(), t_wg->sh);
     });
     const uint32_t st = ctl[96];
     bool rest = true;  // everything the next launch reads is back at rest

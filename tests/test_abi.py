@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 from dynamic_moe_task_amd import binding as B
@@ -118,14 +119,94 @@ def test_launch_validation_before_any_gpu_call():
 @needs_lib
 def test_splitk_validation():
     h = B.etensor_create([B.ETC_DIM_SYMBOLIC], 4)
-    # not instantiated
-    assert B.etc_splitk_launch(h, 8, 4, 16, 0x1000, 0x1000, 0x1000, 0, None) == B.ETC_ERR_INVALID
+    # not instantiated: no edge compiles against it
+    with pytest.raises(B.EtcError):
+        B.etc_edge_compile(h, "ij->i", [8, 4])
     B.etensor_instantiate(h, [8])
-    # wait_count must equal nsplit
-    assert B.etc_splitk_launch(h, 8, 3, 16, 0x1000, 0x1000, 0x1000, 0, None) == B.ETC_ERR_INVALID
+    notify = B.etc_edge_compile(h, "ij->i", [8, 4])
+    wait = B.etc_edge_compile(h, "i->i", [8])
+    P = 0x1000
+    # the edges must fit the launch's task grids
+    assert B.etc_splitk_launch(h, 8, 3, 16, P, P, P, notify, wait, 0, None) == B.ETC_ERR_INVALID
+    assert B.etc_splitk_launch(h, 8, 4, 16, P, P, P, wait, notify, 0, None) == B.ETC_ERR_INVALID
+    # wait_count must equal the out-edge's fan-in: 4 notifies per element
+    h3 = B.etensor_create([8], 3)
+    n3 = B.etc_edge_compile(h3, "ij->i", [8, 4])
+    w3 = B.etc_edge_compile(h3, "i->i", [8])
+    assert B.etc_splitk_launch(h3, 8, 4, 16, P, P, P, n3, w3, 0, None) == B.ETC_ERR_INVALID
+    assert "fan-in" in B.etc_last_error()
+    # edges compiled for another instantiation of the template
+    B.etensor_instantiate(h, [6])
+    assert B.etc_splitk_launch(h, 6, 4, 16, P, P, P, notify, wait, 0, None) == B.ETC_ERR_INVALID
+    B.etensor_instantiate(h, [8])
     # schedule
-    assert B.etc_splitk_launch(h, 8, 4, 16, 0x1000, 0x1000, 0x1000, B.ETC_SCHED_KBK, None) == B.ETC_ERR_UNSUPPORTED
+    assert B.etc_splitk_launch(h, 8, 4, 16, P, P, P, notify, wait, B.ETC_SCHED_KBK, None) == B.ETC_ERR_UNSUPPORTED
     B.etensor_destroy(h)
+    B.etensor_destroy(h3)
+
+
+def _flat(idx, shape):
+    f = 0
+    for i, n in zip(idx, shape):
+        f = f * n + i
+    return f
+
+
+EDGE_CASES = [
+    # spec, event shape, task grid
+    ("ij->i", [5], [5, 4]),          # split-K out-edge [ET Fig. 3]
+    ("i->i", [5], [5]),              # split-K in-edge
+    ("ij->j", [4], [5, 4]),          # column reduction
+    ("ijk->ki", [3, 2], [2, 5, 3]),  # permuted, one dimension reduced
+    ("bh->hb", [4, 3], [3, 4]),      # transpose
+    ("abc->abc", [2, 3, 4], [2, 3, 4]),
+    (" i j -> i ", [7], [7, 2]),     # spaces are ignored
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("spec,eshape,tshape", EDGE_CASES, ids=[c[0].replace(" ", "") for c in EDGE_CASES])
+def test_edge_compile_matches_the_event_model(spec, eshape, tshape):
+    # the library's compiled index function against the plain event model
+    # (oracle/events.py edge_apply) on every task coordinate
+    import itertools
+    from oracle import events
+    h = B.etensor_create([B.ETC_DIM_SYMBOLIC] + eshape[1:], 1)
+    B.etensor_instantiate(h, eshape)
+    e = B.etc_edge_compile(h, spec, tshape)
+    src, dst = events.parse_edge(spec)
+    missing = [n for c, n in zip(src, tshape) if c not in dst]
+    assert e.fan_in == int(np.prod(missing)) if missing else e.fan_in == 1
+    assert e.event_numel == int(np.prod(eshape))
+    hits = np.zeros(int(np.prod(eshape)), np.int64)
+    for coord in itertools.product(*[range(n) for n in tshape]):
+        f = B.etc_edge_index(e, list(coord))
+        assert f == _flat(events.edge_apply(spec, coord), eshape)
+        hits[f] += 1
+    assert (hits == e.fan_in).all()  # every element receives fan_in notifies
+    B.etensor_destroy(h)
+
+
+@needs_lib
+@pytest.mark.parametrize("spec,tshape", [
+    ("ij-i", [8, 4]),      # no arrow
+    ("ij->i->i", [8, 4]),  # two arrows
+    ("ij->k", [8, 4]),     # event letter that names no task dimension
+    ("ii->i", [8, 4]),     # repeated task letter
+    ("ij->ii", [8, 4]),    # rank of the tensor is 1
+    ("iJ->i", [8, 4]),     # not lowercase
+    ("ij->i", [8]),        # the grid has one dimension, the spec two
+    ("ij->i", [7, 4]),     # task size 7 against event size 8
+    ("ij->j", [8, 4]),     # event size 8 against task size 4
+])
+def test_edge_compile_rejects(spec, tshape):
+    h = B.etensor_create([8], 4)
+    with pytest.raises(B.EtcError) as ei:
+        B.etc_edge_compile(h, spec, tshape)
+    assert ei.value.code == B.ETC_ERR_INVALID
+    B.etensor_destroy(h)
+
+
 
 
 @needs_lib

@@ -1,5 +1,6 @@
 """The split-K row-sum example (event tensor of shape n, wait_count 4, edges
-"ij->i" and "i->i") through the device runtime, against the closed form
+"ij->i" and "i->i", compiled from those strings by etc_edge_compile) through
+the device runtime, against the closed form
 C = rowsum(A) and the oracle's B; integer inputs make parity exact."""
 import numpy as np
 import pytest
@@ -26,6 +27,10 @@ def test_splitk_rowsum(sched, n, bk):
     Bref, Cref, _ = oracle.splitk(A, nsplit)
     ev = B.etensor_create([B.ETC_DIM_SYMBOLIC], nsplit)
     B.etensor_instantiate(ev, [n])
+    # the pages' wiring, compiled from its edge strings
+    notify = B.etc_edge_compile(ev, "ij->i", [n, nsplit])
+    wait = B.etc_edge_compile(ev, "i->i", [n])
+    assert notify.fan_in == nsplit and wait.fan_in == 1
     dA = torch.from_numpy(A).cuda()
     dB = torch.zeros((n, nsplit), dtype=torch.int32, device="cuda")
     dC = torch.zeros(n, dtype=torch.int32, device="cuda")
@@ -33,7 +38,8 @@ def test_splitk_rowsum(sched, n, bk):
     for rep in range(3):  # counters return to rest after every launch
         announce(f"splitk n={n} bk={bk} sched={sched} rep={rep}")
         dC.zero_()
-        B.check(B.etc_splitk_launch(ev, n, nsplit, bk, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), sched, stream))
+        B.check(B.etc_splitk_launch(ev, n, nsplit, bk, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), notify, wait,
+                                    sched, stream))
         B.check(B.etc_sync(stream))
         assert np.array_equal(dC.cpu().numpy(), A.sum(axis=1))
         assert np.array_equal(dC.cpu().numpy(), Cref)

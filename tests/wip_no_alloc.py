@@ -1,0 +1,66 @@
+"""moe_layer_launch_noalloc (static scratch instead of a caller workspace)
+against moe_layer_launch on the same inputs, through the C ABI: every
+routing tensor and every output row must match bit for bit (the same
+kernels run on the same inputs), on two calls in a row, the second with a
+smaller batch, and after a call with another descriptor."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dynamic_moe_task_amd import binding as B
+from dynamic_moe_task_amd import workloads as wl
+from gpu_util import DeviceLayer, announce, assert_routing_equal, assert_rows_close, dev_bf16, host_bits
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("topk_ids", "topk_w", "counts", "exp_indptr", "perm", "slot")
+
+
+def _run_noalloc(layer, X, sched):
+    T = X.shape[0]
+    b = layer.bufs
+    b.x[:T].copy_(dev_bf16(X))
+    b.out.zero_()
+    args = b.args()
+    args.workspace = None
+    args.workspace_bytes = 0
+    stream = torch.cuda.current_stream().cuda_stream
+    B.check(B.moe_layer_launch_noalloc(layer.desc, T, args, B.SCHEDS[sched], stream))
+    B.check(B.etc_sync(stream))
+    k = layer.k
+    return {"out": host_bits(b.out[:T]), "topk_ids": b.topk_ids[:T].cpu().numpy(),
+            "topk_w": b.topk_w[:T].cpu().numpy(), "counts": b.counts.cpu().numpy(),
+            "exp_indptr": b.exp_indptr.cpu().numpy(), "perm": b.perm[:T * k].cpu().numpy(),
+            "slot": b.slot[:T * k].cpu().numpy()}
+
+
+@pytest.mark.parametrize("sched", ["static", "ordered", "kbk", "barrier"])
+def test_noalloc_matches_the_workspace_launch(sched):
+    s = wl.DECODE
+    w = wl.make_weights(s, seed=0)
+    layer = DeviceLayer((s.H, s.E, s.k, s.I), w.Wr, w.W13, w.Wd, T_max=64)
+    for i, T in enumerate((16, 5)):  # two calls in a row, the second smaller
+        X = wl.sweep_tokens(s, 9000 + i, T, seed=0)
+        announce(f"noalloc decode T={T} sched={sched} (workspace launch)")
+        ref = layer.run(X, sched)
+        announce(f"noalloc decode T={T} sched={sched} (no-alloc launch)")
+        got = _run_noalloc(layer, X, sched)
+        for key in KEYS + ("out",):
+            assert np.array_equal(got[key], ref[key]), f"call {i}: {key} differs"
+    # another descriptor on the same scratch (its layout differs), then the
+    # first descriptor again, both against the oracle
+    t = wl.TINY
+    tw, tX = wl.make_layer(t, 0)
+    tiny = DeviceLayer((t.H, t.E, t.k, t.I), tw.Wr, tw.W13, tw.Wd, T_max=8)
+    announce(f"noalloc tiny sched={sched}")
+    got = _run_noalloc(tiny, tX, sched)
+    ref = oracle.moe(tX, tw.Wr, tw.W13, tw.Wd, k=t.k)
+    assert_routing_equal(got, ref)
+    assert_rows_close(got["out"], ref["out"])
+    X = wl.sweep_tokens(s, 9100, 3, seed=0)
+    announce(f"noalloc decode T=3 sched={sched} after the tiny layer")
+    got = _run_noalloc(layer, X, sched)
+    ref = layer.run(X, sched)
+    for key in KEYS + ("out",):
+        assert np.array_equal(got[key], ref[key]), f"after the tiny layer: {key} differs"
