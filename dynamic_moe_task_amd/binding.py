@@ -39,7 +39,7 @@ ETC_MAX_DIMS = 8
 EXPORTED = [
     "etensor_create", "etensor_instantiate", "etensor_shape", "etensor_destroy",
     "etc_edge_compile", "etc_edge_index", "etc_splitk_launch", "moe_layer_info", "moe_layer_workspace_size", "moe_workspace_init",
-    "moe_layer_launch", "etc_sync", "etc_last_error",
+    "moe_layer_launch", "moe_layer_launch_noalloc", "etc_sync", "etc_last_error",
 ]
 
 
@@ -126,11 +126,13 @@ def lib():
         L.moe_layer_workspace_size.restype = ctypes.c_size_t
         L.moe_workspace_init.argtypes = [ctypes.POINTER(MoeDesc), P, ctypes.c_size_t, P]
         L.moe_layer_launch.argtypes = [ctypes.POINTER(MoeDesc), I32, ctypes.POINTER(MoeArgs), ctypes.c_int, P]
+        L.moe_layer_launch_noalloc.argtypes = [ctypes.POINTER(MoeDesc), I32, ctypes.POINTER(MoeArgs), ctypes.c_int, P]
         L.etc_sync.argtypes = [P]
         L.etc_last_error.argtypes = []
         L.etc_last_error.restype = ctypes.c_char_p
         for name in ["etensor_create", "etensor_instantiate", "etensor_shape", "etensor_destroy",
                      "etc_edge_compile", "etc_splitk_launch", "moe_layer_info", "moe_workspace_init", "moe_layer_launch",
+                     "moe_layer_launch_noalloc",
                      "etc_sync"]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -216,6 +218,10 @@ def moe_workspace_init(desc: MoeDesc, ws_ptr: int, ws_bytes: int, stream) -> int
 
 def moe_layer_launch(desc: MoeDesc, T: int, args: MoeArgs, sched: int, stream) -> int:
     return lib().moe_layer_launch(ctypes.byref(desc), T, ctypes.byref(args), sched, stream)
+
+
+def moe_layer_launch_noalloc(desc: MoeDesc, T: int, args: MoeArgs, sched: int, stream) -> int:
+    return lib().moe_layer_launch_noalloc(ctypes.byref(desc), T, ctypes.byref(args), sched, stream)
 
 
 def etc_sync(stream) -> int:

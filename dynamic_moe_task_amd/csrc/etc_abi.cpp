@@ -465,8 +465,9 @@ extern "C" int moe_workspace_init(const etc_moe_desc* d, void* ws, size_t bytes,
   return ETC_OK;
 }
 
-// One launch on the workspace `ws`: validation of everything but the
-// workspace pointer, the kernel parameters, the grid and the launch.
+// One launch on the workspace `ws` (the caller's, or the static scratch of
+// moe_layer_launch_noalloc): validation of everything but the workspace
+// pointer, the kernel parameters, the grid and the launch.
 static int layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a, int sched, void* stream,
                         uint8_t* ws, size_t ws_bytes) {
   int rc = desc_check(d);
@@ -567,6 +568,51 @@ static int layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a,
 extern "C" int moe_layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a, int sched, void* stream) {
   if (!a) return fail(ETC_ERR_INVALID, "args is NULL");
   return layer_launch(d, T, a, sched, stream, static_cast<uint8_t*>(a->workspace), a->workspace_bytes);
+}
+
+// ------------------------------------------------- no-allocation variant --
+// The workspace of the last no-allocation launch on each device: its layout
+// follows the descriptor, so a launch with another descriptor starts from a
+// cleared control block and counter sets.
+namespace {
+struct ScratchState {
+  bool init = false;
+  etc_moe_desc last{};
+};
+std::mutex g_scr_mu;
+std::vector<ScratchState> g_scr;
+}  // namespace
+
+extern "C" int moe_layer_launch_noalloc(const etc_moe_desc* d, int32_t T, const etc_moe_args* a, int sched,
+                                        void* stream) {
+  int rc = desc_check(d);
+  if (rc) return rc;
+  if (!a) return fail(ETC_ERR_INVALID, "args is NULL");
+  if (a->workspace || a->workspace_bytes)
+    return fail(ETC_ERR_INVALID, "the no-allocation launch takes no workspace (workspace must be NULL, 0 bytes)");
+  const MoeLayout L = moe_layout(*d);
+  if ((uint64_t)L.total_bytes > (uint64_t)kNoallocScratchBytes)
+    return fail(ETC_ERR_INVALID, "this descriptor needs %lld bytes of workspace; the static scratch holds %llu",
+                (long long)L.total_bytes, (unsigned long long)kNoallocScratchBytes);
+  void* scr = nullptr;
+  int e = moe_scratch(&scr);
+  if (e != hipSuccess) return hip_fail((hipError_t)e, "hipGetSymbolAddress(scratch)");
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  {
+    std::lock_guard<std::mutex> lk(g_scr_mu);
+    if ((int)g_scr.size() <= dev) g_scr.resize(dev + 1);
+    ScratchState& st = g_scr[dev];
+    if (!st.init || std::memcmp(&st.last, d, sizeof *d) != 0) {
+      // control block and both counter sets to zero, with a fill kernel
+      e = moe_scratch_clear(scr, (size_t)L.b_meta, stream);
+      if (e != hipSuccess) return hip_fail((hipError_t)e, "scratch clear");
+      st.init = true;
+      st.last = *d;
+    }
+  }
+  return layer_launch(d, T, a, sched, stream, static_cast<uint8_t*>(scr), kNoallocScratchBytes);
 }
 
 extern "C" int etc_sync(void* stream) {

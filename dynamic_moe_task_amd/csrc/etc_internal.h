@@ -179,6 +179,14 @@ struct MoeParams {
   uint32_t trace_records;
 };
 
+// Static device scratch of moe_layer_launch_noalloc (moe_kernels.hip): one
+// per GPU the library runs on, held until the process ends.
+constexpr size_t kNoallocScratchBytes = (size_t)8 << 20;
+// Its device address on the current device (hipGetSymbolAddress, taken once
+// per device), and a fill kernel that zeroes its first `bytes`.
+int moe_scratch(void** ptr);
+int moe_scratch_clear(void* ptr, size_t bytes, void* stream);
+
 // Host-side launchers (moe_kernels.hip).  Return a hipError_t value.
 int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes, void* stream);
 int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream);

@@ -33,6 +33,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <vector>
+
 #include "etc_internal.h"
 #include "etc_rt.h"
 
@@ -2113,6 +2116,45 @@ int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream) {
   hipLaunchKernelGGL(kbk_g1, dim3((unsigned)(max_rt * nN1)), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_g2, dim3((unsigned)(max_rt * nN2)), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_combine, dim3(nC), dim3(kThreads), 0, s, p);
+  return (int)hipGetLastError();
+}
+
+// ------------------------------------------- static scratch (no-alloc) --
+// The workspace of moe_layer_launch_noalloc, for callers that cannot
+// allocate device memory.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address comes from hipGetSymbolAddress,
+// once per device with that device current, and only that address is handed
+// to kernels and to the fill kernel below.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static std::vector<void*> g_scratch_ptr;  // per device
+
+int moe_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return (int)hipSuccess;
+}
+
+__global__ void __launch_bounds__(256) fill_zero_u32(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+int moe_scratch_clear(void* ptr, size_t bytes, void* stream) {
+  const size_t n = bytes / 4;
+  const unsigned blocks = (unsigned)(n / 256 + 1 < 1024 ? n / 256 + 1 : 1024);
+  hipLaunchKernelGGL(fill_zero_u32, dim3(blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<uint32_t*>(ptr), n);
   return (int)hipGetLastError();
 }
 

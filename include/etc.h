@@ -309,6 +309,26 @@ int moe_workspace_init(const etc_moe_desc* desc, void* workspace, size_t workspa
 int moe_layer_launch(const etc_moe_desc* desc, int32_t T, const etc_moe_args* args, int sched,
                      void* stream);
 
+/* moe_layer_launch without a caller workspace, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array
+ * of the library, 8 MiB on each GPU it runs on, held until the process ends:
+ * descriptors whose moe_layer_workspace_size exceeds 8 MiB are rejected
+ * (at the Qwen3-30B-A3B MoE shape that admits T_max up to 178).
+ * args->workspace must be NULL and args->workspace_bytes 0; everything else
+ * is as for moe_layer_launch.  Calls no hipMalloc, hipFree or allocating
+ * routine: the array's device address is looked up once per device, and
+ * when the descriptor differs from the previous call's on the device, the
+ * array's control block and counter sets are zeroed by a small fill kernel
+ * on `stream` first.  Every call on one GPU shares its array, so calls that
+ * overlap on one GPU (on different streams, or with another process-wide
+ * user of the array) race.
+ * Errors: as moe_layer_launch; ETC_ERR_INVALID also for a non-NULL
+ * workspace or a descriptor too large for the array (checked before any HIP
+ * call).                                                                    */
+int moe_layer_launch_noalloc(const etc_moe_desc* desc, int32_t T, const etc_moe_args* args, int sched,
+                             void* stream);
+
 /* Wait for `stream`, then report the first in-kernel error of every launch
  * made on it since the previous etc_sync (and clear it): ETC_OK,
  * ETC_ERR_TIMEOUT, ETC_ERR_INVARIANT, ETC_ERR_NONFINITE or ETC_ERR_HIP.

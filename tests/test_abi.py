@@ -207,6 +207,21 @@ def test_edge_compile_rejects(spec, tshape):
     B.etensor_destroy(h)
 
 
+@needs_lib
+def test_noalloc_launch_rejects_before_touching_the_gpu():
+    # a descriptor whose workspace exceeds the static scratch, or a caller
+    # workspace, is refused by host checks alone (no HIP call is made)
+    args = B.MoeArgs(*([0x1000] * 13), 0, None, 0, 0, None)
+    args.workspace = None
+    big = B.moe_desc(4096, 2048, 128, 8, 768)
+    assert B.moe_layer_workspace_size(big) > 8 << 20
+    assert B.moe_layer_launch_noalloc(big, 16, args, B.ETC_SCHED_STATIC, None) == B.ETC_ERR_INVALID
+    assert "static scratch" in B.etc_last_error()
+    small = B.moe_desc(64, 2048, 128, 8, 768)
+    args.workspace = 0x1000
+    args.workspace_bytes = 1 << 30
+    assert B.moe_layer_launch_noalloc(small, 16, args, B.ETC_SCHED_STATIC, None) == B.ETC_ERR_INVALID
+    assert "no workspace" in B.etc_last_error()
 
 
 @needs_lib
