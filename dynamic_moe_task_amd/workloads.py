@@ -22,6 +22,16 @@ even); bf16 tensors are held as their uint16 bit patterns.
 The batch-size sweep draws B ~ U{1..512} for 200 steps from
 ``default_rng((seed, 5))`` and the step-s activations from
 ``default_rng((seed, 6, s))``.
+
+The decoder layer around the MoE layer (batch 8 at decode, 32 query heads,
+4 key/value heads of 128, a bf16 KV cache holding 4096 earlier positions per
+sequence, then the same 128-expert MoE) draws:
+  RMSNorm weights g1, g2 [H]           tags 7, 8      ~ N(1, 0.05)
+  Wqkv [(nq + 2 nkv) d, H]             tag 9          ~ N(0, 0.02)
+  Wo [H, nq d]                         tag 10         ~ N(0, 0.02)
+  key / value caches [T, nkv, Lcap, d] tags 11, 12    ~ N(0, 1)
+  residual input x [T, H]              tag 13         ~ N(0, 1)
+and the MoE weights of make_weights with the same seed.
 """
 from __future__ import annotations
 
@@ -103,6 +113,55 @@ def make_layer(shape: MoEShape, seed: int = 0):
     w = make_weights(shape, seed)
     w.bias = zipf_bias(shape, seed)
     return w, make_tokens(shape, shape.T, seed)
+
+
+@dataclass(frozen=True)
+class DecoderShape:
+    name: str
+    T: int          # tokens (sequences) decoding together
+    H: int
+    nq: int         # query heads
+    nkv: int        # key / value heads
+    d: int          # head size
+    pos: int        # position of the new token (= earlier entries in each cache)
+    Lcap: int       # cache capacity per sequence and head
+    theta: float
+    eps: float
+    moe: MoEShape
+
+
+DECODER = DecoderShape("qwen3-30b-a3b decoder layer decode B=8 kv=4096", T=8, H=2048, nq=32, nkv=4, d=128,
+                       pos=4096, Lcap=4160, theta=1e6, eps=1e-6,
+                       moe=MoEShape("qwen3-30b-a3b moe T=8", T=8, H=2048, E=128, k=8, I=768))
+
+
+@dataclass
+class DecoderWeights:
+    g1: np.ndarray    # [H] bf16 bits
+    Wqkv: np.ndarray  # [(nq + 2 nkv) d, H]
+    Wo: np.ndarray    # [H, nq d]
+    g2: np.ndarray    # [H]
+    moe: MoEWeights
+
+
+def make_decoder(shape: DecoderShape, seed: int = 0, w_std: float = 0.02, moe: Optional[MoEWeights] = None):
+    """Weights, the residual input x [T, H] and the key / value caches
+    [T, nkv, Lcap, d] (entries 0..pos-1 drawn, the rest zero)."""
+    H, d = shape.H, shape.d
+    nqkv = (shape.nq + 2 * shape.nkv) * d
+    g1 = to_bf16_bits(1.0 + 0.05 * np.random.default_rng((seed, 7)).standard_normal(H, dtype=np.float32))
+    g2 = to_bf16_bits(1.0 + 0.05 * np.random.default_rng((seed, 8)).standard_normal(H, dtype=np.float32))
+    Wqkv = _normal_bf16(np.random.default_rng((seed, 9)), (nqkv, H), w_std)
+    Wo = _normal_bf16(np.random.default_rng((seed, 10)), (H, shape.nq * d), w_std)
+    cshape = (shape.T, shape.nkv, shape.Lcap, d)
+    kc = np.zeros(cshape, np.uint16)
+    vc = np.zeros(cshape, np.uint16)
+    kc[:, :, :shape.pos] = _normal_bf16(np.random.default_rng((seed, 11)), (shape.T, shape.nkv, shape.pos, d), 1.0)
+    vc[:, :, :shape.pos] = _normal_bf16(np.random.default_rng((seed, 12)), (shape.T, shape.nkv, shape.pos, d), 1.0)
+    x = _normal_bf16(np.random.default_rng((seed, 13)), (shape.T, H), 1.0)
+    if moe is None:
+        moe = make_weights(shape.moe, seed)
+    return DecoderWeights(g1, Wqkv, Wo, g2, moe), x, kc, vc
 
 
 def sweep_batches(seed: int = 0, steps: int = 200, bmax: int = 512) -> np.ndarray:

@@ -53,6 +53,12 @@ def _load():
         lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
         lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_f32.restype = ctypes.c_float
+        d = ctypes.c_double
+        lib.oracle_rmsnorm.argtypes = [i, i, P, P, d, P]
+        lib.oracle_linear.argtypes = [i, i, i, P, P, P]
+        lib.oracle_rope.argtypes = [i, i, P, d, d]
+        lib.oracle_attention.argtypes = [i, i, i, i, i, P, P, P, P]
+        lib.oracle_decoder.argtypes = [i, i, i, i, i, i, i, d, d, P, P, P, P, P, P, P, i, i, i, i] + [P] * 18
         lib.oracle_set_threads.argtypes = [i]
         lib.oracle_max_threads.restype = i
         _lib = lib
@@ -181,6 +187,77 @@ def moe_tokens(tokens, X, W13, Wd, topk_ids, topk_w):
     _check(_load().oracle_moe_tokens(H, k, I, len(tok), _p(tok), _p(X), _p(W13), _p(Wd),
                                      _p(ids), _p(w), _p(out)), "moe_tokens")
     return out
+
+
+# ------------------------------------------------------------ decoder layer --
+def rmsnorm(x, g, eps=1e-6):
+    x, g = _u16(x), _u16(g)
+    T, H = x.shape
+    y = np.empty_like(x)
+    _check(_load().oracle_rmsnorm(T, H, _p(x), _p(g), float(eps), _p(y)), "rmsnorm")
+    return y
+
+
+def linear(x, W):
+    """y = bf16(x W^T), W row-major [N, K]."""
+    x, W = _u16(x), _u16(W)
+    T, K = x.shape
+    N = W.shape[0]
+    assert W.shape[1] == K
+    y = np.empty((T, N), np.uint16)
+    _check(_load().oracle_linear(T, K, N, _p(x), _p(W), _p(y)), "linear")
+    return y
+
+
+def rope(v, pos, theta=1e6):
+    """Rotary embedding of the rows of v [n, d] at position pos (returns a copy)."""
+    v = np.array(_u16(v), copy=True)
+    n, d = v.shape
+    _check(_load().oracle_rope(n, d, _p(v), float(pos), float(theta)), "rope")
+    return v
+
+
+def attention(q, Kc, Vc, L):
+    """Decode attention of one token: q [nq, d], caches [nkv, Lcap, d]; keys 0..L-1."""
+    q, Kc, Vc = _u16(q), _u16(Kc), _u16(Vc)
+    nq, d = q.shape
+    nkv, Lcap, _ = Kc.shape
+    o = np.empty((nq, d), np.uint16)
+    _check(_load().oracle_attention(nq, nkv, d, int(L), Lcap, _p(q), _p(Kc), _p(Vc), _p(o)), "attention")
+    return o
+
+
+def decoder(x, g1, Wqkv, kcache, vcache, Wo, g2, Wr, W13, Wd, k, nq, nkv, d, pos, theta=1e6, eps=1e-6,
+            norm_topk=True):
+    """One decoder layer (attention block, then the MoE block) for the T rows
+    of x, each decoding at position pos with its own cache.  The caches are
+    copied, updated at index pos and returned with the results."""
+    x, g1, Wqkv, Wo, g2 = _u16(x), _u16(g1), _u16(Wqkv), _u16(Wo), _u16(g2)
+    Wr, W13, Wd = _u16(Wr), _u16(W13), _u16(Wd)
+    kc = np.array(_u16(kcache), copy=True)
+    vc = np.array(_u16(vcache), copy=True)
+    T, H = x.shape
+    E = Wr.shape[0]
+    I = Wd.shape[2]
+    Lcap = kc.shape[2]
+    assert kc.shape == (T, nkv, Lcap, d) and vc.shape == kc.shape
+    nqkv = (nq + 2 * nkv) * d
+    r = {"logits": np.empty((T, E), np.float32), "topk_ids": np.empty((T, k), np.int32),
+         "topk_w": np.empty((T, k), np.float32), "counts": np.empty(E, np.int32),
+         "exp_indptr": np.empty(E + 1, np.int32), "perm": np.empty(T * k, np.int32),
+         "slot": np.empty(T * k, np.int32), "out": np.empty((T, H), np.uint16),
+         "h1": np.empty((T, H), np.uint16), "qkv": np.empty((T, nqkv), np.uint16),
+         "att": np.empty((T, nq * d), np.uint16), "a": np.empty((T, H), np.uint16),
+         "x2": np.empty((T, H), np.uint16), "h2": np.empty((T, H), np.uint16),
+         "moe_out": np.empty((T, H), np.uint16)}
+    _check(_load().oracle_decoder(
+        T, H, nq, nkv, d, int(pos), Lcap, float(theta), float(eps), _p(x), _p(g1), _p(Wqkv), _p(kc), _p(vc),
+        _p(Wo), _p(g2), E, k, I, int(norm_topk), _p(Wr), _p(W13), _p(Wd), _p(r["logits"]), _p(r["topk_ids"]),
+        _p(r["topk_w"]), _p(r["counts"]), _p(r["exp_indptr"]), _p(r["perm"]), _p(r["slot"]), _p(r["out"]),
+        _p(r["h1"]), _p(r["qkv"]), _p(r["att"]), _p(r["a"]), _p(r["x2"]), _p(r["h2"]), _p(r["moe_out"])),
+        "decoder")
+    r["kcache"], r["vcache"] = kc, vc
+    return r
 
 
 def set_threads(n: int) -> int:

@@ -377,3 +377,183 @@ int oracle_splitk(int n, int nsplit, int bk, const int32_t *A, int32_t *B,
   }
   return ORACLE_OK;
 }
+
+/* ======================================================================== */
+/* One decoder layer around the MoE layer (a Qwen3-30B-A3B-shaped layer at  */
+/* decode: the fifth workload of the build).  The pages evaluate the MoE    */
+/* layer inside end-to-end serving [ET-fig 14] but print no decoder layer;  */
+/* every step below is the textbook definition, with these readings:        */
+/*   - pre-norm residual block: x2 = x + Attn(RMSNorm(x)),                  */
+/*     out = x2 + MoE(RMSNorm(x2));                                         */
+/*   - RMSNorm(v) = v / sqrt(mean(v^2) + eps) * g, eps = 1e-6;              */
+/*   - grouped-query attention: query head h reads key/value head           */
+/*     h / (nq / nkv); scores scaled by 1/sqrt(d); no QK norm;              */
+/*   - rotary embedding on q and k, rotate-half pairs (i, i + d/2) with     */
+/*     angle pos * theta^(-2i/d), theta = 1e6;                              */
+/*   - the new token sits at position `pos`: its key and value are written  */
+/*     into the cache at index pos, and it attends to cache entries 0..pos; */
+/*   - every stored activation (norm outputs, q/k/v after RoPE, attention   */
+/*     output, projection output, residual sums, layer output) is bf16;     */
+/*     sums are fp64.                                                       */
+
+/* y[t, :] = bf16( x[t, :] / sqrt(mean_h x[t, h]^2 + eps) * g ), fp64.      */
+int oracle_rmsnorm(int T, int H, const uint16_t *x, const uint16_t *g, double eps, uint16_t *y) {
+  if (T < 0 || H <= 0 || eps < 0.0) return ORACLE_ERR_INVALID;
+  for (int t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int h = 0; h < H; ++h) {
+      double v = (double)bf16_bits_to_float(x[(size_t)t * H + h]);
+      ss += v * v;
+    }
+    double r = 1.0 / sqrt(ss / (double)H + eps);
+    for (int h = 0; h < H; ++h)
+      y[(size_t)t * H + h] = float_to_bf16_bits(
+          (float)((double)bf16_bits_to_float(x[(size_t)t * H + h]) * r *
+                  (double)bf16_bits_to_float(g[h])));
+  }
+  return ORACLE_OK;
+}
+
+/* y[t, n] = bf16( sum_k x[t, k] * W[n, k] ), fp64 (W row-major [N, K]).    */
+int oracle_linear(int T, int K, int N, const uint16_t *x, const uint16_t *W, uint16_t *y) {
+  if (T < 0 || K <= 0 || N <= 0) return ORACLE_ERR_INVALID;
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n)
+    for (int t = 0; t < T; ++t) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k)
+        acc += (double)bf16_bits_to_float(x[(size_t)t * K + k]) *
+               (double)bf16_bits_to_float(W[(size_t)n * K + k]);
+      y[(size_t)t * N + n] = float_to_bf16_bits((float)acc);
+    }
+  return ORACLE_OK;
+}
+
+/* Rotary embedding, in place on nvec vectors of d bf16 values (d even):
+ * for i < d/2, a = pos * theta^(-2i/d):
+ *   v'[i]       = v[i] cos a - v[i + d/2] sin a
+ *   v'[i + d/2] = v[i + d/2] cos a + v[i] sin a      (fp64, stored bf16)  */
+int oracle_rope(int nvec, int d, uint16_t *v, double pos, double theta) {
+  if (nvec < 0 || d <= 0 || d % 2 || theta <= 0.0) return ORACLE_ERR_INVALID;
+  const int half = d / 2;
+  for (int r = 0; r < nvec; ++r) {
+    uint16_t *u = v + (size_t)r * d;
+    for (int i = 0; i < half; ++i) {
+      double a = pos * pow(theta, -2.0 * (double)i / (double)d);
+      double x0 = (double)bf16_bits_to_float(u[i]);
+      double x1 = (double)bf16_bits_to_float(u[i + half]);
+      u[i] = float_to_bf16_bits((float)(x0 * cos(a) - x1 * sin(a)));
+      u[i + half] = float_to_bf16_bits((float)(x1 * cos(a) + x0 * sin(a)));
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Decode attention of one token.  q [nq, d]; the token's key and value
+ * caches Kc, Vc [nkv, Lcap, d] (row-major), of which entries 0..L-1 are
+ * read; query head h uses key/value head h / (nq / nkv).
+ *   o[h, :] = bf16( sum_j p_j V[g, j, :] ),  p = softmax_j( q_h . K[g, j] / sqrt(d) )
+ * in fp64 (the maximum is subtracted before exp).                          */
+int oracle_attention(int nq, int nkv, int d, int L, int Lcap, const uint16_t *q, const uint16_t *Kc,
+                     const uint16_t *Vc, uint16_t *o) {
+  if (nq <= 0 || nkv <= 0 || nq % nkv || d <= 0 || L <= 0 || L > Lcap) return ORACLE_ERR_INVALID;
+  double *s = (double *)malloc(sizeof(double) * (size_t)L);
+  if (!s) return ORACLE_ERR_INVALID;
+  const double scale = 1.0 / sqrt((double)d);
+  for (int h = 0; h < nq; ++h) {
+    const int g = h / (nq / nkv);
+    const uint16_t *K = Kc + (size_t)g * Lcap * d;
+    const uint16_t *V = Vc + (size_t)g * Lcap * d;
+    double m = -INFINITY;
+    for (int j = 0; j < L; ++j) {
+      double acc = 0.0;
+      for (int c = 0; c < d; ++c)
+        acc += (double)bf16_bits_to_float(q[(size_t)h * d + c]) *
+               (double)bf16_bits_to_float(K[(size_t)j * d + c]);
+      s[j] = acc * scale;
+      if (s[j] > m) m = s[j];
+    }
+    double den = 0.0;
+    for (int j = 0; j < L; ++j) {
+      s[j] = exp(s[j] - m);
+      den += s[j];
+    }
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < L; ++j) acc += s[j] * (double)bf16_bits_to_float(V[(size_t)j * d + c]);
+      o[(size_t)h * d + c] = float_to_bf16_bits((float)(acc / den));
+    }
+  }
+  free(s);
+  return ORACLE_OK;
+}
+
+/* The decoder layer for T tokens, token t decoding at position pos with its
+ * own caches kcache/vcache [T, nkv, Lcap, d] (updated in place at index pos).
+ * Wqkv [(nq + 2 nkv) d, H]: rows of the query heads, then of the key heads,
+ * then of the value heads.  Wo [H, nq d].  The MoE arguments are those of
+ * oracle_moe; its routing outputs are returned.  Intermediates (any may be
+ * NULL): h1 [T, H], qkv [T, (nq + 2 nkv) d] after RoPE, att [T, nq d],
+ * a [T, H], x2 [T, H], h2 [T, H], moe_out [T, H].                           */
+int oracle_decoder(int T, int H, int nq, int nkv, int d, int pos, int Lcap, double theta, double eps,
+                   const uint16_t *x, const uint16_t *g1, const uint16_t *Wqkv, uint16_t *kcache,
+                   uint16_t *vcache, const uint16_t *Wo, const uint16_t *g2,
+                   int E, int k, int I, int norm_topk, const uint16_t *Wr, const uint16_t *W13,
+                   const uint16_t *Wd, float *logits, int32_t *ids, float *w, int32_t *counts,
+                   int32_t *exp_indptr, int32_t *perm, int32_t *slot, uint16_t *out,
+                   uint16_t *h1, uint16_t *qkv, uint16_t *att, uint16_t *a, uint16_t *x2, uint16_t *h2,
+                   uint16_t *moe_out) {
+  if (T <= 0 || H <= 0 || nq <= 0 || nkv <= 0 || nq % nkv || d <= 0 || d % 2 || pos < 0 || pos >= Lcap)
+    return ORACLE_ERR_INVALID;
+  const int nqkv = (nq + 2 * nkv) * d;
+  uint16_t *b_h1 = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)T * H);
+  uint16_t *b_qkv = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)T * nqkv);
+  uint16_t *b_att = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)T * nq * d);
+  uint16_t *b_a = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)T * H);
+  uint16_t *b_x2 = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)T * H);
+  uint16_t *b_h2 = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)T * H);
+  uint16_t *b_moe = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)T * H);
+  int rc = ORACLE_ERR_INVALID;
+  if (!b_h1 || !b_qkv || !b_att || !b_a || !b_x2 || !b_h2 || !b_moe) goto done;
+  /* attention block */
+  rc = oracle_rmsnorm(T, H, x, g1, eps, b_h1);
+  if (rc) goto done;
+  rc = oracle_linear(T, H, nqkv, b_h1, Wqkv, b_qkv);
+  if (rc) goto done;
+  for (int t = 0; t < T; ++t) {
+    uint16_t *row = b_qkv + (size_t)t * nqkv;
+    rc = oracle_rope(nq + nkv, d, row, (double)pos, theta); /* the query heads, then the key heads */
+    if (rc) goto done;
+    for (int g = 0; g < nkv; ++g) {
+      size_t at = (((size_t)t * nkv + g) * Lcap + pos) * d;
+      memcpy(kcache + at, row + (size_t)(nq + g) * d, sizeof(uint16_t) * (size_t)d);
+      memcpy(vcache + at, row + (size_t)(nq + nkv + g) * d, sizeof(uint16_t) * (size_t)d);
+    }
+    rc = oracle_attention(nq, nkv, d, pos + 1, Lcap, row, kcache + (size_t)t * nkv * Lcap * d,
+                          vcache + (size_t)t * nkv * Lcap * d, b_att + (size_t)t * nq * d);
+    if (rc) goto done;
+  }
+  rc = oracle_linear(T, nq * d, H, b_att, Wo, b_a);
+  if (rc) goto done;
+  for (size_t i = 0; i < (size_t)T * H; ++i)
+    b_x2[i] = float_to_bf16_bits((float)((double)bf16_bits_to_float(x[i]) + (double)bf16_bits_to_float(b_a[i])));
+  /* MoE block */
+  rc = oracle_rmsnorm(T, H, b_x2, g2, eps, b_h2);
+  if (rc) goto done;
+  rc = oracle_moe(T, H, E, k, I, norm_topk, b_h2, Wr, NULL, W13, Wd, logits, ids, w, counts, exp_indptr, perm,
+                  slot, NULL, NULL, NULL, b_moe);
+  if (rc) goto done;
+  for (size_t i = 0; i < (size_t)T * H; ++i)
+    out[i] = float_to_bf16_bits((float)((double)bf16_bits_to_float(b_x2[i]) + (double)bf16_bits_to_float(b_moe[i])));
+  if (h1) memcpy(h1, b_h1, sizeof(uint16_t) * (size_t)T * H);
+  if (qkv) memcpy(qkv, b_qkv, sizeof(uint16_t) * (size_t)T * nqkv);
+  if (att) memcpy(att, b_att, sizeof(uint16_t) * (size_t)T * nq * d);
+  if (a) memcpy(a, b_a, sizeof(uint16_t) * (size_t)T * H);
+  if (x2) memcpy(x2, b_x2, sizeof(uint16_t) * (size_t)T * H);
+  if (h2) memcpy(h2, b_h2, sizeof(uint16_t) * (size_t)T * H);
+  if (moe_out) memcpy(moe_out, b_moe, sizeof(uint16_t) * (size_t)T * H);
+  rc = ORACLE_OK;
+done:
+  free(b_h1); free(b_qkv); free(b_att); free(b_a); free(b_x2); free(b_h2); free(b_moe);
+  return rc;
+}

@@ -537,3 +537,176 @@ def test_ordered_claims_out_of_graph_order_deadlock():
               ("deal", ph["C"])]
     with pytest.raises(RuntimeError):
         ev.run_ordered(tasks, st, 4, phases, groups=4, seed=0)
+
+
+# ===================================================== decoder-layer oracle --
+# Pins of the decoder layer's steps (RMSNorm, projection, rotary embedding,
+# decode attention, the whole layer) against closed forms, special cases and
+# values worked out by hand, none of which retypes the oracle's formula.
+def _bits(a):
+    return wl.to_bf16_bits(np.asarray(a, np.float32))
+
+
+def _f(b):
+    return oracle.bf16_bits_to_f64(np.asarray(b, np.uint16))
+
+
+def test_rmsnorm_hand_values_and_weight():
+    # x = (3, 4): mean square 12.5, so y = x / sqrt(12.5) * g
+    y = oracle.rmsnorm(_bits([[3.0, 4.0]]), _bits([1.0, 2.0]), eps=0.0)
+    np.testing.assert_allclose(_f(y)[0], [3 / np.sqrt(12.5), 2 * 4 / np.sqrt(12.5)], rtol=4e-3)
+    # a constant row normalises to the sign of the constant, whatever its size
+    for c in (-7.5, 0.015625, 1000.0):
+        y = oracle.rmsnorm(_bits(np.full((1, 64), c)), _bits(np.ones(64)), eps=0.0)
+        assert np.all(_f(y) == np.sign(c))
+    # eps enters under the square root: x = 0 stays 0, and a tiny x is damped
+    y = oracle.rmsnorm(_bits(np.full((1, 8), 1e-3)), _bits(np.ones(8)), eps=1.0)
+    np.testing.assert_allclose(_f(y), 1e-3 / np.sqrt(1e-6 + 1.0), rtol=4e-3)
+
+
+def test_linear_identity_and_column_pick():
+    rng = np.random.default_rng(3)
+    x = _bits(rng.standard_normal((5, 16)))
+    eye = _bits(np.eye(16))
+    assert np.array_equal(oracle.linear(x, eye), x)  # W = I returns x exactly
+    pick = np.zeros((3, 16), np.float32)
+    pick[0, 7] = pick[1, 0] = pick[2, 15] = 1.0       # row n of W selects one input column
+    y = oracle.linear(x, _bits(pick))
+    assert np.array_equal(y, x[:, [7, 0, 15]])        # a transposed W would fail here
+
+
+def test_rope_hand_values():
+    # d = 4, theta = 10000: frequencies 1 and 1/100; pairs (0, 2) and (1, 3)
+    v = _bits([[1.0, 0.0, 0.0, 0.0], [0.0, 1.0, 0.0, 0.0], [0.0, 0.0, 1.0, 0.0]])
+    r = _f(oracle.rope(v, pos=1.0, theta=10000.0))
+    c, s = np.cos(1.0), np.sin(1.0)
+    c2, s2 = np.cos(0.01), np.sin(0.01)
+    np.testing.assert_allclose(r[0], [c, 0, s, 0], atol=4e-3)
+    np.testing.assert_allclose(r[1], [0, c2, 0, s2], atol=4e-3)
+    np.testing.assert_allclose(r[2], [-s, 0, c, 0], atol=4e-3)
+
+
+def test_rope_is_a_rotation():
+    rng = np.random.default_rng(4)
+    v = _bits(rng.standard_normal((6, 128)))
+    assert np.array_equal(oracle.rope(v, 0.0, 1e6), v)  # position 0: identity
+    r = _f(oracle.rope(v, 4096.0, 1e6))
+    x = _f(v)
+    # every (i, i + 64) pair keeps its length
+    n0 = x[:, :64] ** 2 + x[:, 64:] ** 2
+    n1 = r[:, :64] ** 2 + r[:, 64:] ** 2
+    np.testing.assert_allclose(n1, n0, rtol=2e-2, atol=1e-3)
+    # and the rotation of pair i by angle a: the dot product of two rotated
+    # vectors depends only on the difference of their positions
+    q, kv = _bits(rng.standard_normal((1, 128))), _bits(rng.standard_normal((1, 128)))
+    d1 = (_f(oracle.rope(q, 100.0, 1e6)) * _f(oracle.rope(kv, 90.0, 1e6))).sum()
+    d2 = (_f(oracle.rope(q, 10.0, 1e6)) * _f(oracle.rope(kv, 0.0, 1e6))).sum()
+    assert abs(d1 - d2) < 0.05 * (abs(d2) + 1.0)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(5)
+    nq, nkv, d, L = 4, 2, 16, 9
+    q = _bits(rng.standard_normal((nq, d)))
+    V = rng.standard_normal((nkv, L, d)).astype(np.float32)
+    # identical keys: uniform weights, the output is the mean of the values
+    K = np.repeat(rng.standard_normal((nkv, 1, d)).astype(np.float32), L, axis=1)
+    o = _f(oracle.attention(q, _bits(K), _bits(V), L))
+    mean = _f(_bits(V)).mean(axis=1)
+    for h in range(nq):
+        np.testing.assert_allclose(o[h], mean[h // 2], rtol=1e-2, atol=1e-2)
+    # one key aligned with a large query dominates: the output is its value
+    qa = np.zeros((nq, d), np.float32)
+    qa[:, 0] = 40.0
+    Ka = np.zeros((nkv, L, d), np.float32)
+    Ka[:, 5, 0] = 40.0
+    o = _f(oracle.attention(_bits(qa), _bits(Ka), _bits(V), L))
+    for h in range(nq):
+        np.testing.assert_allclose(o[h], _f(_bits(V))[h // 2, 5], atol=1e-2)
+    # a single key: the output is that value, exactly
+    o = oracle.attention(q, _bits(K), _bits(V), 1)
+    for h in range(nq):
+        assert np.array_equal(o[h], _bits(V)[h // 2, 0])
+    # grouped heads: query heads 2 and 3 read key/value head 1 only
+    Vg = np.zeros((nkv, L, d), np.float32)
+    Vg[1] = 3.0
+    o = _f(oracle.attention(q, _bits(K), _bits(Vg), L))
+    assert np.all(o[:2] == 0.0) and np.all(o[2:] == 3.0)
+    # entries past L are not read
+    V2 = V.copy()
+    V2[:, L - 1] = 1e4
+    o1 = oracle.attention(q, _bits(K), _bits(V), L - 1)
+    o2 = oracle.attention(q, _bits(K), _bits(V2), L - 1)
+    assert np.array_equal(o1, o2)
+
+
+def test_attention_is_invariant_to_the_order_of_the_entries():
+    rng = np.random.default_rng(6)
+    nq, nkv, d, L = 8, 1, 32, 40
+    q = _bits(rng.standard_normal((nq, d)))
+    K = _bits(rng.standard_normal((nkv, L, d)))
+    V = _bits(rng.standard_normal((nkv, L, d)))
+    perm = rng.permutation(L)
+    o1 = _f(oracle.attention(q, K, V, L))
+    o2 = _f(oracle.attention(q, K[:, perm], V[:, perm], L))
+    np.testing.assert_allclose(o1, o2, atol=1e-2)
+
+
+def _tiny_decoder(seed=0, zero_wo=False, zero_q=False):
+    rng = np.random.default_rng(seed)
+    T, H, nq, nkv, d, pos, Lcap = 3, 128, 4, 2, 32, 10, 16
+    E, k, I = 8, 2, 128
+    s = lambda *shape: rng.standard_normal(shape).astype(np.float32)
+    g1, g2 = _bits(1 + 0.1 * s(H)), _bits(1 + 0.1 * s(H))
+    Wqkv = s((nq + 2 * nkv) * d, H) * 0.1
+    if zero_q:
+        Wqkv[:nq * d] = 0.0
+    Wo = np.zeros((H, nq * d), np.float32) if zero_wo else s(H, nq * d) * 0.1
+    kc = np.zeros((T, nkv, Lcap, d), np.float32)
+    vc = np.zeros((T, nkv, Lcap, d), np.float32)
+    kc[:, :, :pos] = s(T, nkv, pos, d)
+    vc[:, :, :pos] = s(T, nkv, pos, d)
+    moe = dict(Wr=_bits(s(E, H) * 0.1), W13=_bits(s(E, 2 * I, H) * 0.1), Wd=_bits(s(E, H, I) * 0.1))
+    args = dict(x=_bits(s(T, H)), g1=g1, Wqkv=_bits(Wqkv), kcache=_bits(kc), vcache=_bits(vc), Wo=_bits(Wo), g2=g2,
+                k=k, nq=nq, nkv=nkv, d=d, pos=pos, **moe)
+    return args
+
+
+def test_decoder_without_attention_output_is_the_moe_block():
+    # Wo = 0: the attention block adds nothing, so x2 = x and the layer is
+    # x + MoE(RMSNorm(x)), computed here from the (pinned) MoE oracle
+    a = _tiny_decoder(zero_wo=True)
+    r = oracle.decoder(**a)
+    assert np.array_equal(r["x2"], a["x"])
+    h2 = oracle.rmsnorm(a["x"], a["g2"])
+    m = oracle.moe(h2, a["Wr"], a["W13"], a["Wd"], k=a["k"])
+    assert np.array_equal(r["moe_out"], m["out"])
+    for key in ("topk_ids", "counts", "exp_indptr", "perm", "slot"):
+        assert np.array_equal(r[key], m[key])
+    want = wl.to_bf16_bits((_f(a["x"]) + _f(m["out"])).astype(np.float32))
+    assert np.array_equal(r["out"], want)
+
+
+def test_decoder_cache_update_and_uniform_attention():
+    # Wq = 0: every score is 0, so each head averages the values of entries
+    # 0..pos, the last of which is the new token's own value
+    a = _tiny_decoder(zero_q=True)
+    r = oracle.decoder(**a)
+    T, nq, nkv, d, pos = 3, a["nq"], a["nkv"], a["d"], a["pos"]
+    qkv = _f(r["qkv"])
+    assert np.all(qkv[:, :nq * d] == 0.0)
+    for t in range(T):
+        for g in range(nkv):
+            # the new key (after RoPE) and value were written at index pos
+            assert np.array_equal(r["kcache"][t, g, pos], r["qkv"][t, (nq + g) * d:(nq + g + 1) * d])
+            assert np.array_equal(r["vcache"][t, g, pos], r["qkv"][t, (nq + nkv + g) * d:(nq + nkv + g + 1) * d])
+            # and no other entry changed
+            assert np.array_equal(np.delete(r["kcache"][t, g], pos, 0), np.delete(a["kcache"][t, g], pos, 0))
+        att = _f(r["att"])[t].reshape(nq, d)
+        for h in range(nq):
+            mean = _f(r["vcache"][t, h // (nq // nkv), :pos + 1]).mean(axis=0)
+            np.testing.assert_allclose(att[h], mean, rtol=1e-2, atol=1e-2)
+    # the projection and residual: a = att Wo^T, x2 = x + a
+    np.testing.assert_array_equal(r["a"], oracle.linear(r["att"], a["Wo"]))
+    np.testing.assert_array_equal(
+        r["x2"], wl.to_bf16_bits((_f(a["x"]) + _f(r["a"])).astype(np.float32)))
