@@ -399,6 +399,60 @@ def measure_token_counts(Wr, w13s, w2s, sp, steps, warmup, repeat, counts=(1, 12
     return out
 
 
+def measure_decoder(Wr, w13s, w2s, sp, steps, warmup, repeat):
+    """The decoder layer around the MoE layer as one persistent kernel
+    (batch 8, 32 query / 4 kv heads of 128, 4096 cached entries per
+    sequence, then the same MoE block with the decode weights), against its
+    HBM floor, and kernel by kernel."""
+    import torch
+    from dynamic_moe_task_amd import binding as B
+    from dynamic_moe_task_amd import workloads as wl
+    s = wl.DECODER
+    w, X, kc, vc = wl.make_decoder(s, 0, moe=wl.MoEWeights(None, None, None))
+    desc = B.decoder_desc(s.T, s.H, s.nq, s.nkv, s.d, s.Lcap, s.moe.E, s.moe.k, s.moe.I, s.theta, s.eps)
+    kcd, vcd = dev_bf16(kc), dev_bf16(vc)
+    bufs = B.DecoderBuffers.allocate(desc, dev_bf16(w.g1), dev_bf16(w.Wqkv), dev_bf16(w.Wo), dev_bf16(w.g2), kcd, vcd,
+                                     Wr, w13s[0], w2s[0])
+    bufs.x[:s.T].copy_(dev_bf16(X))
+    B.check(B.decoder_layer_launch(desc, s.T, s.pos, bufs.args(), B.SCHEDS["static"], sp))
+    B.check(B.etc_sync(sp))
+    n_act = int((bufs.moe.counts.cpu().numpy() > 0).sum())
+    alg = wl.decoder_algorithmic_bytes(s, n_act)
+    R = len(w13s)
+    args = [bufs.args(w13=w13s[i], w2=w2s[i]) for i in range(R)]
+
+    def timed(sched):
+        code = B.SCHEDS[sched]
+        for i in range(warmup):
+            B.check(B.decoder_layer_launch(desc, s.T, s.pos, args[i % R], code, sp))
+        B.check(B.etc_sync(sp))
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            B.check(B.decoder_layer_launch(desc, s.T, s.pos, args[i % R], code, sp))
+        end.record()
+        torch.cuda.synchronize()
+        B.check(B.etc_sync(sp))
+        return start.elapsed_time(end) * 1e3 / steps
+
+    scheds = ("static", "ordered", "kbk")
+    runs = {x: [] for x in scheds}
+    for _ in range(repeat):
+        for x in scheds:
+            runs[x].append(timed(x))
+    us = {x: float(np.median(v)) for x, v in runs.items()}
+    best = min(("static", "ordered"), key=lambda x: us[x])
+    return {
+        "workload": s.name, "T": s.T, "pos": s.pos, "heads": [s.nq, s.nkv, s.d], "active_experts": n_act,
+        "us_per_layer": {x: round(v, 2) for x, v in us.items()},
+        "tokens_per_s": round(s.T / (us[best] * 1e-6), 1), "schedule": best,
+        "algorithmic_bytes": alg, "hbm_floor_us": round(alg / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+        "hbm_frac": round(alg / (us[best] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+        "megakernel_over_kbk_speedup": round(us["kbk"] / us[best], 3),
+    }
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -492,6 +546,7 @@ def main():
                                                 a.sched)
         extra["sweep"] = measure_sweep(Wr, w13s, w2s, sp, a.sweep_steps, a.sched)
         extra["token_counts"] = measure_token_counts(Wr, w13s, w2s, sp, max(10, a.steps // 2), a.warmup, a.repeat)
+        extra["decoder_layer"] = measure_decoder(Wr, w13s, w2s, sp, max(10, a.steps // 2), a.warmup, a.repeat)
 
     cpu = None
     if not a.no_cpu:

@@ -39,7 +39,8 @@ ETC_MAX_DIMS = 8
 EXPORTED = [
     "etensor_create", "etensor_instantiate", "etensor_shape", "etensor_destroy",
     "etc_edge_compile", "etc_edge_index", "etc_splitk_launch", "moe_layer_info", "moe_layer_workspace_size", "moe_workspace_init",
-    "moe_layer_launch", "moe_layer_launch_noalloc", "etc_sync", "etc_last_error",
+    "moe_layer_launch", "moe_layer_launch_noalloc", "decoder_layer_workspace_size", "decoder_workspace_init",
+    "decoder_layer_launch", "etc_sync", "etc_last_error",
 ]
 
 
@@ -71,6 +72,18 @@ class MoeArgs(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("debug", ctypes.c_void_p), ("watchdog_us", ctypes.c_uint32),
                 ("trace_records", ctypes.c_uint32), ("trace", ctypes.c_void_p)]
+
+
+class DecoderDesc(ctypes.Structure):
+    _fields_ = [("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("L_cap", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("moe", MoeDesc)]
+
+
+class DecoderArgs(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("g1", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p),
+                ("w_o", ctypes.c_void_p), ("g2", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
+                ("v_cache", ctypes.c_void_p), ("moe", MoeArgs)]
 
 
 class MoeInfo(ctypes.Structure):
@@ -127,12 +140,17 @@ def lib():
         L.moe_workspace_init.argtypes = [ctypes.POINTER(MoeDesc), P, ctypes.c_size_t, P]
         L.moe_layer_launch.argtypes = [ctypes.POINTER(MoeDesc), I32, ctypes.POINTER(MoeArgs), ctypes.c_int, P]
         L.moe_layer_launch_noalloc.argtypes = [ctypes.POINTER(MoeDesc), I32, ctypes.POINTER(MoeArgs), ctypes.c_int, P]
+        L.decoder_layer_workspace_size.argtypes = [ctypes.POINTER(DecoderDesc)]
+        L.decoder_layer_workspace_size.restype = ctypes.c_size_t
+        L.decoder_workspace_init.argtypes = [ctypes.POINTER(DecoderDesc), P, ctypes.c_size_t, P]
+        L.decoder_layer_launch.argtypes = [ctypes.POINTER(DecoderDesc), I32, I32, ctypes.POINTER(DecoderArgs),
+                                           ctypes.c_int, P]
         L.etc_sync.argtypes = [P]
         L.etc_last_error.argtypes = []
         L.etc_last_error.restype = ctypes.c_char_p
         for name in ["etensor_create", "etensor_instantiate", "etensor_shape", "etensor_destroy",
                      "etc_edge_compile", "etc_splitk_launch", "moe_layer_info", "moe_workspace_init", "moe_layer_launch",
-                     "moe_layer_launch_noalloc",
+                     "moe_layer_launch_noalloc", "decoder_workspace_init", "decoder_layer_launch",
                      "etc_sync"]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -224,6 +242,23 @@ def moe_layer_launch_noalloc(desc: MoeDesc, T: int, args: MoeArgs, sched: int, s
     return lib().moe_layer_launch_noalloc(ctypes.byref(desc), T, ctypes.byref(args), sched, stream)
 
 
+def decoder_desc(T_max, H, n_q, n_kv, head_dim, L_cap, E, k, I, rope_theta=1e6, rms_eps=1e-6,
+                 norm_topk=True) -> DecoderDesc:
+    return DecoderDesc(n_q, n_kv, head_dim, L_cap, rope_theta, rms_eps, moe_desc(T_max, H, E, k, I, norm_topk, False))
+
+
+def decoder_layer_workspace_size(desc: DecoderDesc) -> int:
+    return lib().decoder_layer_workspace_size(ctypes.byref(desc))
+
+
+def decoder_workspace_init(desc: DecoderDesc, ws_ptr: int, ws_bytes: int, stream) -> int:
+    return lib().decoder_workspace_init(ctypes.byref(desc), ws_ptr, ws_bytes, stream)
+
+
+def decoder_layer_launch(desc: DecoderDesc, T: int, pos: int, args: DecoderArgs, sched: int, stream) -> int:
+    return lib().decoder_layer_launch(ctypes.byref(desc), T, pos, ctypes.byref(args), sched, stream)
+
+
 def etc_sync(stream) -> int:
     return lib().etc_sync(stream)
 
@@ -292,3 +327,53 @@ class MoELayerBuffers:
         import torch
         s = torch.cuda.current_stream().cuda_stream if stream is None else stream
         check(moe_layer_launch(self.desc, T, self.args(**kw), SCHEDS.get(sched, sched), s))
+
+
+@dataclass
+class DecoderBuffers:
+    """Device tensors of one decoder layer (weights, caches, the MoE block's
+    buffers and the workspace), owned by torch, handed over as pointers."""
+    desc: DecoderDesc
+    x: object
+    g1: object
+    w_qkv: object
+    w_o: object
+    g2: object
+    k_cache: object
+    v_cache: object
+    moe: MoELayerBuffers
+
+    @staticmethod
+    def allocate(desc: DecoderDesc, g1, w_qkv, w_o, g2, k_cache, v_cache, w_router, w13, w2, device="cuda",
+                 debug=False):
+        import torch
+        Tm, H, E, k = desc.moe.T_max, desc.moe.H, desc.moe.E, desc.moe.k
+        i32 = dict(dtype=torch.int32, device=device)
+        ws_bytes = decoder_layer_workspace_size(desc)
+        if ws_bytes == 0:
+            raise EtcError(ETC_ERR_INVALID, etc_last_error())
+        moe = MoELayerBuffers(
+            desc=desc.moe, x=torch.empty((Tm, H), dtype=torch.bfloat16, device=device),
+            w_router=w_router, b_router=None, w13=w13, w2=w2,
+            out=torch.empty((Tm, H), dtype=torch.bfloat16, device=device),
+            topk_ids=torch.empty((Tm, k), **i32), topk_w=torch.empty((Tm, k), dtype=torch.float32, device=device),
+            counts=torch.empty(E, **i32), exp_indptr=torch.empty(E + 1, **i32), perm=torch.empty(Tm * k, **i32),
+            slot=torch.empty(Tm * k, **i32), workspace=torch.zeros(ws_bytes, dtype=torch.uint8, device=device),
+            debug=torch.zeros(2 * E + 8, **i32) if debug else None)
+        stream = torch.cuda.current_stream().cuda_stream
+        check(decoder_workspace_init(desc, moe.workspace.data_ptr(), ws_bytes, stream))
+        x = torch.empty((Tm, H), dtype=torch.bfloat16, device=device)
+        return DecoderBuffers(desc, x, g1, w_qkv, w_o, g2, k_cache, v_cache, moe)
+
+    def args(self, w13=None, w2=None, w_qkv=None, w_o=None, k_cache=None, v_cache=None, watchdog_us: int = 0,
+             trace=None) -> DecoderArgs:
+        pick = lambda a, b: b if a is None else a
+        return DecoderArgs(self.x.data_ptr(), self.g1.data_ptr(), pick(w_qkv, self.w_qkv).data_ptr(),
+                           pick(w_o, self.w_o).data_ptr(), self.g2.data_ptr(),
+                           pick(k_cache, self.k_cache).data_ptr(), pick(v_cache, self.v_cache).data_ptr(),
+                           self.moe.args(w13=w13, w2=w2, watchdog_us=watchdog_us, trace=trace))
+
+    def launch(self, T: int, pos: int, sched="static", stream=None, **kw) -> None:
+        import torch
+        s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        check(decoder_layer_launch(self.desc, T, pos, self.args(**kw), SCHEDS.get(sched, sched), s))

@@ -469,7 +469,8 @@ extern "C" int moe_workspace_init(const etc_moe_desc* d, void* ws, size_t bytes,
 // moe_layer_launch_noalloc): validation of everything but the workspace
 // pointer, the kernel parameters, the grid and the launch.
 static int layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a, int sched, void* stream,
-                        uint8_t* ws, size_t ws_bytes) {
+                        uint8_t* ws, size_t ws_bytes, const etc_decoder_desc* dd = nullptr, int32_t pos = 0,
+                        const etc_decoder_args* da = nullptr) {
   int rc = desc_check(d);
   if (rc) return rc;
   if (!a) return fail(ETC_ERR_INVALID, "args is NULL");
@@ -481,7 +482,7 @@ static int layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a,
     return fail(ETC_ERR_UNSUPPORTED,
                 "the dynamic (push/pop) schedule is switched off: its launch did not complete on the GPU "
                 "and the cause is not yet found");
-  const void* bf[] = {a->x, a->w_router, a->w13, a->w2, a->out, ws};
+  const void* bf[] = {dd ? da->x : a->x, a->w_router, a->w13, a->w2, a->out, ws};
   const char* bfn[] = {"x", "w_router", "w13", "w2", "out", "workspace"};
   for (int i = 0; i < 6; ++i)
     if (!bf[i] || !aligned16(bf[i])) return fail(ETC_ERR_INVALID, "%s is NULL or not 16-byte aligned", bfn[i]);
@@ -493,9 +494,11 @@ static int layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a,
   if (a->debug && !aligned4(a->debug)) return fail(ETC_ERR_INVALID, "debug misaligned");
   if (a->trace && (!aligned4(a->trace) || a->trace_records == 0))
     return fail(ETC_ERR_INVALID, "trace misaligned or trace_records is 0");
-  const MoeLayout L = moe_layout(*d);
-  if (ws_bytes < (size_t)L.total_bytes)
-    return fail(ETC_ERR_INVALID, "workspace has %zu bytes, needs %lld", ws_bytes, (long long)L.total_bytes);
+  const MoeLayout L = moe_layout(*d, dd ? (int64_t)d->T_max * dd->n_kv : 0);
+  const DecLayout D = dd ? decoder_layout(*dd, L.total_bytes) : DecLayout{};
+  const int64_t need = dd ? D.total_bytes : L.total_bytes;
+  if (ws_bytes < (size_t)need)
+    return fail(ETC_ERR_INVALID, "workspace has %zu bytes, needs %lld", ws_bytes, (long long)need);
 
   MoeParams p{};
   p.x = static_cast<const uint16_t*>(a->x);
@@ -526,6 +529,7 @@ static int layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a,
   p.o_ev_h = L.o_ev_h;
   p.o_ev_y = L.o_ev_y;
   p.o_ev_c = L.o_ev_c;
+  p.o_ev_att = L.o_ev_att;
   p.o_queue = L.o_queue;
   p.q_cap = L.q_cap;
   p.T = T;
@@ -548,14 +552,48 @@ static int layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a,
   p.trace_records = a->trace ? a->trace_records : 0;
   rc = watchdog_ticks(a->watchdog_us, &p.budget);
   if (rc) return rc;
+  if (dd) {
+    const int64_t Tm = d->T_max, H = d->H, hd = dd->head_dim;
+    p.dec = 1;
+    p.dx = static_cast<const uint16_t*>(da->x);
+    p.g1 = static_cast<const uint16_t*>(da->g1);
+    p.g2 = static_cast<const uint16_t*>(da->g2);
+    p.wqkv = static_cast<const uint16_t*>(da->w_qkv);
+    p.wo = static_cast<const uint16_t*>(da->w_o);
+    p.kc = static_cast<uint16_t*>(da->k_cache);
+    p.vc = static_cast<uint16_t*>(da->v_cache);
+    p.h1 = reinterpret_cast<uint16_t*>(ws + D.b_h1);
+    p.qb = reinterpret_cast<uint16_t*>(ws + D.b_q);
+    p.part = reinterpret_cast<float*>(ws + D.b_part);
+    p.ob = reinterpret_cast<uint16_t*>(ws + D.b_o);
+    p.apart = reinterpret_cast<float*>(ws + D.b_apart);
+    p.resid = reinterpret_cast<uint16_t*>(ws + D.b_x2);
+    p.x = reinterpret_cast<const uint16_t*>(ws + D.b_h2);  // the MoE block's input: RMSNorm(x2) * g2
+    p.nq = dd->n_q;
+    p.nkv = dd->n_kv;
+    p.Lcap = dd->L_cap;
+    p.pos = pos;
+    p.nchunk = (int32_t)cdiv(pos, kDecChunk);  // cache entries 0 .. pos-1 in chunks
+    p.nchunk_max = D.nchunk_max;
+    p.part_floats = D.part_floats;
+    p.theta = dd->rope_theta;
+    p.eps = dd->rms_eps;
+    p.cache_bytes = (uint32_t)((int64_t)T * dd->n_kv * dd->L_cap * hd * 2);
+    p.h1_bytes = (uint32_t)(Tm * H * 2);
+    p.q_bytes = (uint32_t)(Tm * dd->n_q * hd * 2);
+    p.part_bytes = (uint32_t)(Tm * dd->n_kv * D.nchunk_max * D.part_floats * 4);
+    p.apart_bytes = (uint32_t)(kDecOSplit * Tm * H * 4);
+    p.resid_bytes = (uint32_t)(Tm * H * 2);
+  }
 
   const int lds = (int)lds_bytes_for(d);
   int e;
   if (sched == ETC_SCHED_KBK) {
-    e = launch_moe_kbk(p, (int)scan_lds_bytes(d->E, d->T_max), stream);
+    e = dd ? launch_decoder_kbk(p, (int)scan_lds_bytes(d->E, d->T_max), stream)
+           : launch_moe_kbk(p, (int)scan_lds_bytes(d->E, d->T_max), stream);
   } else {
     int grid = 0, solo = 0;
-    rc = persistent_grid(sched, lds, &grid, &solo);
+    rc = persistent_grid(dd ? kDecSchedBase + sched : sched, lds, &grid, &solo);
     if (rc) return rc;
     p.solo_wgs = solo;
     e = launch_moe_persistent(p, sched, grid, lds, stream);
@@ -613,6 +651,62 @@ extern "C" int moe_layer_launch_noalloc(const etc_moe_desc* d, int32_t T, const 
     }
   }
   return layer_launch(d, T, a, sched, stream, static_cast<uint8_t*>(scr), kNoallocScratchBytes);
+}
+
+// ========================================================= decoder layer ==
+static int decoder_check(const etc_decoder_desc* dd) {
+  if (!dd) return fail(ETC_ERR_INVALID, "descriptor is NULL");
+  int rc = desc_check(&dd->moe);
+  if (rc) return rc;
+  if (dd->moe.T_max > kDecMaxT) return fail(ETC_ERR_INVALID, "decoder T_max %d > %d", dd->moe.T_max, kDecMaxT);
+  if (dd->moe.has_bias) return fail(ETC_ERR_INVALID, "the decoder layer's router has no bias");
+  if (dd->head_dim != kDecHd) return fail(ETC_ERR_INVALID, "head_dim %d != %d", dd->head_dim, kDecHd);
+  if (dd->n_kv < 1 || dd->n_q < 1 || dd->n_q % dd->n_kv)
+    return fail(ETC_ERR_INVALID, "n_q %d must be a positive multiple of n_kv %d", dd->n_q, dd->n_kv);
+  const int gq = dd->n_q / dd->n_kv;
+  if (gq > kDecMaxGroup || (gq & (gq - 1)))
+    return fail(ETC_ERR_INVALID, "n_q / n_kv = %d must be 1, 2, 4 or 8", gq);
+  if ((dd->n_q * dd->head_dim) % (128 * kDecOSplit))
+    return fail(ETC_ERR_INVALID, "n_q * head_dim must be a multiple of %d", 128 * kDecOSplit);
+  if (dd->L_cap < 1 || (int64_t)kDecMaxT * dd->n_kv * dd->L_cap * dd->head_dim * 2 >= ((int64_t)1 << 31))
+    return fail(ETC_ERR_INVALID, "L_cap %d out of range", dd->L_cap);
+  if (!(dd->rope_theta > 0.f) || !(dd->rms_eps >= 0.f)) return fail(ETC_ERR_INVALID, "rope_theta / rms_eps");
+  return ETC_OK;
+}
+
+extern "C" size_t decoder_layer_workspace_size(const etc_decoder_desc* dd) {
+  if (decoder_check(dd) != ETC_OK) return 0;
+  const MoeLayout L = moe_layout(dd->moe, (int64_t)dd->moe.T_max * dd->n_kv);
+  return (size_t)decoder_layout(*dd, L.total_bytes).total_bytes;
+}
+
+extern "C" int decoder_workspace_init(const etc_decoder_desc* dd, void* ws, size_t bytes, void* stream) {
+  int rc = decoder_check(dd);
+  if (rc) return rc;
+  const MoeLayout L = moe_layout(dd->moe, (int64_t)dd->moe.T_max * dd->n_kv);
+  const DecLayout D = decoder_layout(*dd, L.total_bytes);
+  if (!ws || !aligned16(ws)) return fail(ETC_ERR_INVALID, "workspace NULL or not 16-byte aligned");
+  if (bytes < (size_t)D.total_bytes)
+    return fail(ETC_ERR_INVALID, "workspace has %zu bytes, needs %lld", bytes, (long long)D.total_bytes);
+  hipError_t e = hipMemsetAsync(ws, 0, (size_t)L.b_meta, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(workspace control)");
+  return ETC_OK;
+}
+
+extern "C" int decoder_layer_launch(const etc_decoder_desc* dd, int32_t T, int32_t pos, const etc_decoder_args* da,
+                                    int sched, void* stream) {
+  int rc = decoder_check(dd);
+  if (rc) return rc;
+  if (!da) return fail(ETC_ERR_INVALID, "args is NULL");
+  if (sched != ETC_SCHED_STATIC && sched != ETC_SCHED_ORDERED && sched != ETC_SCHED_KBK)
+    return fail(ETC_ERR_UNSUPPORTED, "the decoder layer runs under STATIC, ORDERED or KBK");
+  if (pos < 0 || pos >= dd->L_cap) return fail(ETC_ERR_INVALID, "pos %d outside [0, L_cap=%d)", pos, dd->L_cap);
+  const void* bf[] = {da->x, da->g1, da->w_qkv, da->w_o, da->g2, da->k_cache, da->v_cache};
+  const char* bfn[] = {"x", "g1", "w_qkv", "w_o", "g2", "k_cache", "v_cache"};
+  for (int i = 0; i < 7; ++i)
+    if (!bf[i] || !aligned16(bf[i])) return fail(ETC_ERR_INVALID, "%s is NULL or not 16-byte aligned", bfn[i]);
+  return layer_launch(&dd->moe, T, &da->moe, sched, stream, static_cast<uint8_t*>(da->moe.workspace),
+                      da->moe.workspace_bytes, dd, pos, da);
 }
 
 extern "C" int etc_sync(void* stream) {

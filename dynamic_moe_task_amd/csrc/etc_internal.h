@@ -65,7 +65,13 @@ enum : int {
   W_EV_ROUTE = 224,
   W_EV_SCAN = 256,
   W_CLAIM_G1 = 288,  // ORDERED: 8 claim counters for the G tiles, 32 words apart
-  W_FIXED = 544,     // start of the variable-size event tensors
+  // decoder layer: one event per phase of the attention block
+  W_DEC_N1 = 544,    // RMSNorm tasks done
+  W_DEC_QKV = 576,   // QKV projection tiles done
+  W_DEC_ATTC = 608,  // attention merges done
+  W_DEC_O = 640,     // output projection tiles done
+  W_DEC_N2 = 672,    // residual + RMSNorm tasks done
+  W_FIXED = 704,     // start of the variable-size event tensors
 };
 // split-K example: control words (u32) of its library-owned block, each on
 // its own 128-byte line, followed by the queue
@@ -80,7 +86,7 @@ struct MoeLayout {
   int32_t ntt_max, max_rt, nct_max;
   int64_t q_cap;
   // word offsets inside a counter set
-  int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_y, o_ev_c, o_queue;  // word offsets
+  int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_y, o_ev_c, o_ev_att, o_queue;  // word offsets
   int64_t set_words;
   // byte offsets inside the workspace
   int64_t b_ctrl, b_set0, b_set1, b_meta, b_rt_info, b_row_rt, b_logits, b_hh, b_y;
@@ -93,7 +99,23 @@ inline int64_t align_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 // meta words (outside the double-buffered sets): written by the scan task
 enum : int { M_NRT = 0, M_WORDS = 16 };
 
-inline MoeLayout moe_layout(const etc_moe_desc& d) {
+// Decoder layer around the MoE layer (the attention block before it):
+// geometry of its tasks.
+constexpr int kDecMaxT = 16;     // tokens a launch takes (one 16-row MFMA block)
+constexpr int kDecHd = 128;      // head size
+constexpr int kDecChunk = 512;   // cache entries per attention task
+constexpr int kDecOSplit = 4;    // K split of the output projection
+constexpr int kDecNormT = 4;     // tokens per RMSNorm task (one a wave)
+constexpr int kDecMaxGroup = 8;  // query heads per key/value head
+
+// Decoder buffers, appended to the MoE workspace.
+struct DecLayout {
+  int32_t nchunk_max;   // attention tasks per (token, kv head) at the largest position
+  int32_t part_floats;  // floats of one attention partial: gq x d values, then gq maxima, gq sums
+  int64_t b_h1, b_q, b_part, b_o, b_apart, b_x2, b_h2, total_bytes;
+};
+
+inline MoeLayout moe_layout(const etc_moe_desc& d, int64_t att_events = 0) {
   MoeLayout L{};
   const int64_t Tm = d.T_max;
   L.ntt_max = (int32_t)cdiv(Tm, kRouterT);
@@ -108,6 +130,7 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
   L.o_ev_h = w;     w += (int64_t)L.max_rt * kEvStride;
   L.o_ev_y = w;     w += (int64_t)L.max_rt * kEvStride;
   L.o_ev_c = w;     w += (int64_t)L.nct_max * kEvStride;
+  L.o_ev_att = w;   w += att_events * kEvStride;  // decoder layer: per (token, kv head)
   L.o_queue = w;    w += L.q_cap;  // 32-bit descriptors
   L.set_words = align_up(w, 64);
   int64_t b = 0;
@@ -122,6 +145,24 @@ inline MoeLayout moe_layout(const etc_moe_desc& d) {
   L.b_y = b;             b += align_up(rows * d.H * 2, 256);
   L.total_bytes = b;
   return L;
+}
+
+inline DecLayout decoder_layout(const etc_decoder_desc& dd, int64_t base) {
+  DecLayout D{};
+  const int64_t Tm = dd.moe.T_max, H = dd.moe.H, d = dd.head_dim;
+  const int64_t gq = dd.n_q / dd.n_kv;
+  D.nchunk_max = (int32_t)cdiv(dd.L_cap, kDecChunk);
+  D.part_floats = (int32_t)(gq * d + 2 * gq);
+  int64_t b = base;
+  D.b_h1 = b;    b += align_up(Tm * H * 2, 256);
+  D.b_q = b;     b += align_up(Tm * dd.n_q * d * 2, 256);
+  D.b_part = b;  b += align_up(Tm * dd.n_kv * D.nchunk_max * D.part_floats * 4, 256);
+  D.b_o = b;     b += align_up(Tm * dd.n_q * d * 2, 256);
+  D.b_apart = b; b += align_up(kDecOSplit * Tm * H * 4, 256);
+  D.b_x2 = b;    b += align_up(Tm * H * 2, 256);
+  D.b_h2 = b;    b += align_up(Tm * H * 2, 256);
+  D.total_bytes = b;
+  return D;
 }
 
 // LDS bytes the scan task needs: five per-expert tables (counts,
@@ -167,7 +208,7 @@ struct MoeParams {
   uint16_t* hh;
   uint16_t* y;
   int64_t set_words;
-  int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_y, o_ev_c, o_queue, q_cap;
+  int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_y, o_ev_c, o_ev_att, o_queue, q_cap;
   int32_t T, H, E, k, I, norm_topk, has_bias;
   int32_t max_rt;
   int32_t T_max;
@@ -177,6 +218,26 @@ struct MoeParams {
   uint64_t budget;  // watchdog, in wall-clock ticks
   uint32_t* trace;
   uint32_t trace_records;
+  // Decoder layer (dec = 1): the attention block runs first and writes the
+  // MoE block's input (x above: RMSNorm of the residual stream) and the
+  // residual the combine adds (resid); otherwise all of these are unused.
+  int32_t dec;
+  const uint16_t* dx;    // residual input [T, H]
+  const uint16_t* g1;    // RMSNorm weights [H]
+  const uint16_t* g2;
+  const uint16_t* wqkv;  // [(nq + 2 nkv) d, H]
+  const uint16_t* wo;    // [H, nq d]
+  uint16_t* kc;          // key / value caches [T, nkv, Lcap, d], written at `pos`
+  uint16_t* vc;
+  uint16_t* h1;          // RMSNorm(dx) [T_max, H]
+  uint16_t* qb;          // queries after RoPE [T_max, nq d]
+  float* part;           // attention partials [T_max, nkv, nchunk_max, part_floats]
+  uint16_t* ob;          // attention output [T_max, nq d]
+  float* apart;          // output projection partial sums [kDecOSplit, T_max, H]
+  uint16_t* resid;       // x2 = dx + attention block [T_max, H]; the combine adds it
+  int32_t nq, nkv, Lcap, pos, nchunk, nchunk_max, part_floats;
+  float theta, eps;
+  uint32_t cache_bytes, h1_bytes, q_bytes, part_bytes, apart_bytes, resid_bytes;
 };
 
 // Static device scratch of moe_layer_launch_noalloc (moe_kernels.hip): one
@@ -190,6 +251,9 @@ int moe_scratch_clear(void* ptr, size_t bytes, void* stream);
 // Host-side launchers (moe_kernels.hip).  Return a hipError_t value.
 int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes, void* stream);
 int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream);
+int launch_decoder_kbk(const MoeParams& p, int lds_bytes, void* stream);
+// occupancy queries of the decoder-layer variants: kDecSchedBase + sched
+constexpr int kDecSchedBase = 16;
 int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu);
 int launch_splitk(int n, int nsplit, int bk, const int32_t* A, int32_t* B, int32_t* C, int32_t* ev,
                   const etc_edge& notify_edge, const etc_edge& wait_edge, int32_t wait_count, uint32_t* ctl,

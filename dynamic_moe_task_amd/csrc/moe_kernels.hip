@@ -1263,6 +1263,13 @@ __device__ __forceinline__ void task_combine(const MoeParams& p, const Ctx& c, i
         }
       }
     }
+    if (p.resid) {
+      // decoder layer: out = bf16(x2 + bf16(MoE sum)), x2 the residual stream
+      float rv[8];
+      unpack8(co_ld128(make_rsrc(p.resid, p.resid_bytes), (uint32_t)(((size_t)t * c.H + ch * 8) * 2)), rv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = rv[q] + __uint_as_float(f2bf(acc[q]) << 16);
+    }
     u32x4_t o;
     o.x = f2bf(acc[0]) | (f2bf(acc[1]) << 16);
     o.y = f2bf(acc[2]) | (f2bf(acc[3]) << 16);
@@ -1271,6 +1278,8 @@ __device__ __forceinline__ void task_combine(const MoeParams& p, const Ctx& c, i
     st4(p.out + (size_t)t * c.H + ch * 8, o);
   }
 }
+
+#include "decoder_tasks.h"
 
 // =================================================== event plumbing ========
 // STATIC and ORDERED: the notifies after the router, top-k and scan tasks
@@ -1745,14 +1754,20 @@ __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ct
 // wait can be circular and the schedule cannot deadlock.  Task counts of the
 // phases after S are read from S's output (data-dependent instantiation).
 template <int MODE, bool WG>
-__device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh) {
+__device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh,
+                                          int64_t off0 = 0) {
   const int G = gridDim.x, w = blockIdx.x;
   float* red = reinterpret_cast<float*>(smem);
   constexpr bool EV = (MODE == MODE_STATIC || MODE == MODE_ORDERED);
   uint32_t bar = 0;  // BARRIER: arrivals that complete the next grid barrier
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
-  int64_t off = 0;
+  int64_t off = off0;
+  // decoder layer: the router reads the attention block's output (h2),
+  // complete once every N2 task has notified
+  if (p.dec && first_of(w, off, G) < c.nR &&
+      !wg_wait(c.set + W_DEC_N2, (uint32_t)((c.T + kDecNormT - 1) / kDecNormT), c.status, c.budget))
+    return;
   for (int i = first_of(w, off, G); i < c.nR; i += G) {
     if (tr) tw = ts = now_ticks();
     task_router<WG>(p, c, i / c.nET, i % c.nET);
@@ -1942,7 +1957,9 @@ struct DynTasks {
 // them); the other variant holds the narrow tiles only, so that small
 // batches run code that carries none of the wide tiles' register pressure.
 // Both come from the one code object; T stays a kernel argument.
-template <int MODE, bool WG>
+// DEC: the decoder layer: the attention block's tasks run first, in the same
+// kernel, and the MoE block's router waits on their last event.
+template <int MODE, bool WG, bool DEC = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 moe_persistent(MoeParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -1985,7 +2002,12 @@ moe_persistent(MoeParams p) {
       dyn::run_moe<DevPlat>(tk, q, g, dsh);
     }
   }
-  if (MODE != MODE_DYNAMIC) run_lists<MODE, WG>(p, c, smem, sh);
+  if (DEC) {
+    int64_t off = 0;
+    if (run_decoder_front(p, c, smem, off)) run_lists<MODE, WG>(p, c, smem, sh, off);
+  } else if (MODE != MODE_DYNAMIC) {
+    run_lists<MODE, WG>(p, c, smem, sh);
+  }
   wg_publish();
   if (threadIdx.x == 0) {
     const uint32_t st = ld_relaxed(c.status) & ~ST_ABORT;
@@ -2035,6 +2057,36 @@ __global__ void __launch_bounds__(kThreads) kbk_combine(MoeParams p) {
   task_combine(p, c, blockIdx.x, pairs);
 }
 
+// ------------------------------------- decoder layer, kernel by kernel --
+__global__ void __launch_bounds__(kThreads) kd_norm1(MoeParams p) {
+  const Ctx c = make_ctx(p, nullptr);
+  task_norm1(p, c, blockIdx.x);
+}
+__global__ void __launch_bounds__(kThreads) kd_qkv(MoeParams p) {
+  __shared__ float red[1024 + 256 + 128];
+  const Ctx c = make_ctx(p, nullptr);
+  task_qkv(p, c, blockIdx.x, red);
+}
+__global__ void __launch_bounds__(kThreads) kd_attn(MoeParams p) {
+  __shared__ float lds[16 * kDecChunk + 64 + 32];
+  const Ctx c = make_ctx(p, nullptr);
+  const int i = blockIdx.x;
+  task_attn(p, c, i / (p.nkv * p.nchunk), (i / p.nchunk) % p.nkv, i % p.nchunk, lds);
+}
+__global__ void __launch_bounds__(kThreads) kd_attn_merge(MoeParams p) {
+  const Ctx c = make_ctx(p, nullptr);
+  task_attn_merge(p, c, blockIdx.x / p.nkv, blockIdx.x % p.nkv);
+}
+__global__ void __launch_bounds__(kThreads) kd_oproj(MoeParams p) {
+  __shared__ float red[1024 + 256];
+  const Ctx c = make_ctx(p, nullptr);
+  task_oproj(p, c, blockIdx.x / kDecOSplit, blockIdx.x % kDecOSplit, red);
+}
+__global__ void __launch_bounds__(kThreads) kd_norm2(MoeParams p) {
+  const Ctx c = make_ctx(p, nullptr);
+  task_norm2(p, c, blockIdx.x);
+}
+
 // ------------------------------------------------------- host launchers --
 // The variant a launch of T tokens runs: the wide G1 tiles from T * k on.
 static bool wide_g1(const MoeParams& p) { return wide_variant(p.T, p.k, p.H, p.I); }
@@ -2050,6 +2102,15 @@ static void launch_variant(const MoeParams& p, bool wide, int grid, int lds_byte
 int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool wide = wide_g1(p);
+  if (p.dec) {  // decoder layer: at most 16 tokens, the small-batch variant
+    if (sched == ETC_SCHED_STATIC)
+      hipLaunchKernelGGL((moe_persistent<MODE_STATIC, false, true>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+    else if (sched == ETC_SCHED_ORDERED)
+      hipLaunchKernelGGL((moe_persistent<MODE_ORDERED, false, true>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+    else
+      return (int)hipErrorInvalidValue;
+    return (int)hipGetLastError();
+  }
   switch (sched) {
     case ETC_SCHED_STATIC:
       launch_variant<MODE_STATIC>(p, wide, grid, lds_bytes, s);
@@ -2084,6 +2145,12 @@ static hipError_t occupancy_both(int* blocks_per_cu, int lds_bytes) {
 int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu) {
   hipError_t e;
   switch (sched) {
+    case kDecSchedBase + ETC_SCHED_STATIC:
+      return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_STATIC, false, true>,
+                                                               kThreads, lds_bytes);
+    case kDecSchedBase + ETC_SCHED_ORDERED:
+      return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_ORDERED, false, true>,
+                                                               kThreads, lds_bytes);
     case ETC_SCHED_STATIC:
       e = occupancy_both<MODE_STATIC>(blocks_per_cu, lds_bytes);
       break;
@@ -2100,6 +2167,20 @@ int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu) {
       return (int)hipErrorInvalidValue;
   }
   return (int)e;
+}
+
+int launch_decoder_kbk(const MoeParams& p, int lds_bytes, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int nN = (p.T + kDecNormT - 1) / kDecNormT;
+  hipLaunchKernelGGL(kd_norm1, dim3(nN), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(kd_qkv, dim3((p.nq + 2 * p.nkv) * (kDecHd / 16)), dim3(kThreads), 0, s, p);
+  if (p.nchunk > 0) hipLaunchKernelGGL(kd_attn, dim3(p.T * p.nkv * p.nchunk), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(kd_attn_merge, dim3(p.T * p.nkv), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(kd_oproj, dim3((p.H / 16) * kDecOSplit), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(kd_norm2, dim3(nN), dim3(kThreads), 0, s, p);
+  const int e = (int)hipGetLastError();
+  if (e != (int)hipSuccess) return e;
+  return launch_moe_kbk(p, lds_bytes, stream);
 }
 
 int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream) {

@@ -164,6 +164,17 @@ def make_decoder(shape: DecoderShape, seed: int = 0, w_std: float = 0.02, moe: O
     return DecoderWeights(g1, Wqkv, Wo, g2, moe), x, kc, vc
 
 
+def decoder_algorithmic_bytes(shape: DecoderShape, n_active: int) -> int:
+    """Bytes the decoder layer must move: the attention weights, the cache
+    entries read (pos per sequence and kv head, keys and values) and written
+    (the new entry), the norm weights, activations in and out, and the MoE
+    block's algorithmic bytes."""
+    H, d, T = shape.H, shape.d, shape.T
+    w_att = 2 * ((shape.nq + 2 * shape.nkv) * d * H + H * shape.nq * d + 2 * H)
+    kv = 2 * 2 * T * shape.nkv * d * (shape.pos + 1)
+    return w_att + kv + 2 * T * H * 2 + algorithmic_bytes(shape.moe, T, n_active) - 2 * 2 * T * H
+
+
 def sweep_batches(seed: int = 0, steps: int = 200, bmax: int = 512) -> np.ndarray:
     return np.random.default_rng((seed, 5)).integers(1, bmax + 1, size=steps)
 

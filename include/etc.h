@@ -309,6 +309,75 @@ int moe_workspace_init(const etc_moe_desc* desc, void* workspace, size_t workspa
 int moe_layer_launch(const etc_moe_desc* desc, int32_t T, const etc_moe_args* args, int sched,
                      void* stream);
 
+/* -------------------------------------------------------- decoder layer -- */
+/* One decoder layer around the MoE layer, as ONE persistent kernel: the
+ * attention block, then the MoE block, each with its residual add [the
+ * pages evaluate the MoE layer inside end-to-end serving, Fig. 14; the
+ * layer's steps are the textbook pre-norm block]:
+ *   h1 = RMSNorm(x) * g1                       N1 tasks (4 tokens each)
+ *   q, k, v = h1 Wqkv^T; RoPE on q and k at position pos; k, v written into
+ *            the caches at index pos           QKV tasks (16 columns each)
+ *   o = softmax(q k^T / sqrt(d)) v over cache entries 0..pos, query head h
+ *       reading key/value head h / (n_q / n_kv)   attention tasks (512 cache
+ *            entries of one token and one kv head each), then merge tasks
+ *   x2 = x + o Wo^T                            projection tasks, N2 tasks
+ *   out = x2 + MoE(RMSNorm(x2) * g2)           the MoE layer's tasks, its
+ *            router waiting on the N2 tasks' event
+ * Every activation is stored bf16, sums are fp32.  Each phase notifies an
+ * event that the next phase's tasks wait on, as in the MoE graph.         */
+typedef struct {
+  int32_t n_q;         /* query heads                                          */
+  int32_t n_kv;        /* key / value heads; n_q / n_kv in {1, 2, 4, 8}        */
+  int32_t head_dim;    /* 128                                                   */
+  int32_t L_cap;       /* cache entries per sequence and kv head (pos < L_cap)  */
+  float rope_theta;    /* rotary base (1e6 for Qwen3)                           */
+  float rms_eps;       /* RMSNorm epsilon (1e-6)                                */
+  etc_moe_desc moe;    /* the MoE block; moe.T_max <= 16 is the largest batch,
+                          moe.has_bias must be 0                               */
+} etc_decoder_desc;
+
+/* Device pointers of one decoder-layer launch (row-major, bf16 unless said):
+ *   x       [T, H]  residual input;   g1, g2 [H] RMSNorm weights
+ *   w_qkv   [(n_q + 2 n_kv) head_dim, H]: rows of the query heads, then of
+ *           the key heads, then of the value heads
+ *   w_o     [H, n_q head_dim]
+ *   k_cache, v_cache [T, n_kv, L_cap, head_dim]: entries 0..pos-1 are read,
+ *           entry pos is written (the new token's key after RoPE, its value)
+ *   moe     the MoE block's arguments: w_router, w13, w2, out (the layer
+ *           output [T, H]), the routing outputs, workspace
+ *           (decoder_layer_workspace_size bytes, prepared once by
+ *           decoder_workspace_init), debug, watchdog_us, trace; moe.x is
+ *           ignored (the MoE block reads RMSNorm(x2) from the workspace).  */
+typedef struct {
+  const void* x;
+  const void* g1;
+  const void* w_qkv;
+  const void* w_o;
+  const void* g2;
+  void* k_cache;
+  void* v_cache;
+  etc_moe_args moe;
+} etc_decoder_args;
+
+/* Workspace bytes of a decoder-layer launch (0 if the descriptor is
+ * invalid).  Makes no HIP call.                                             */
+size_t decoder_layer_workspace_size(const etc_decoder_desc* desc);
+
+/* Zero the workspace's control block (once after allocation).  Asynchronous
+ * on `stream`.  Errors: ETC_ERR_INVALID, ETC_ERR_HIP.                        */
+int decoder_workspace_init(const etc_decoder_desc* desc, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Asynchronous launch of one decoder layer for T tokens (1 <= T <=
+ * moe.T_max), every token decoding at position pos (0 <= pos < L_cap).
+ * sched: ETC_SCHED_STATIC or ETC_SCHED_ORDERED (the MoE block's G tiles
+ * dealt or claimed, the attention block's tasks dealt), or ETC_SCHED_KBK
+ * (one kernel launch per task type).  Allocates nothing, compiles nothing.
+ * Errors: ETC_ERR_INVALID (limits, NULL or misaligned pointers, small
+ * workspace), ETC_ERR_UNSUPPORTED (sched), ETC_ERR_HIP; in-kernel errors are
+ * reported by etc_sync.                                                     */
+int decoder_layer_launch(const etc_decoder_desc* desc, int32_t T, int32_t pos, const etc_decoder_args* args,
+                         int sched, void* stream);
+
 /* moe_layer_launch without a caller workspace, for callers that cannot
  * allocate device memory (code under graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  The workspace is a static device array

@@ -37,8 +37,9 @@ def test_kernels_use_no_scratch(tmp_path):
         if m and name:
             kernels[name][m.group(1).strip()] = int(m.group(2))
     persistent = [k for k in kernels if "moe_persistent" in k]
-    # STATIC, DYNAMIC, BARRIER and ORDERED, each in a small-batch and a large-batch variant
-    assert len(persistent) == 8, sorted(kernels)
+    # STATIC, DYNAMIC, BARRIER and ORDERED, each in a small-batch and a large-batch
+    # variant, and the decoder layer's STATIC and ORDERED
+    assert len(persistent) == 10, sorted(kernels)
     for k, v in kernels.items():
         if "moe_persistentILi1E" in k:
             # DYNAMIC holds every task body in one loop over popped
