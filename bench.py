@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill_zipf", "tiny"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill_zipf", "tiny", "decoder"],
+                    help="decoder: only the decoder-layer section (diagnostics and profiling)")
     ap.add_argument("--tokens", type=int, default=0,
                     help="run the workload's layer at this many tokens instead of its own T (diagnostics, "
                          "e.g. a per-task trace at T=1)")
@@ -399,7 +400,7 @@ def measure_token_counts(Wr, w13s, w2s, sp, steps, warmup, repeat, counts=(1, 12
     return out
 
 
-def measure_decoder(Wr, w13s, w2s, sp, steps, warmup, repeat):
+def measure_decoder(Wr, w13s, w2s, sp, steps, warmup, repeat, scheds=("static", "ordered", "kbk")):
     """The decoder layer around the MoE layer as one persistent kernel
     (batch 8, 32 query / 4 kv heads of 128, 4096 cached entries per
     sequence, then the same MoE block with the decode weights), against its
@@ -436,20 +437,19 @@ def measure_decoder(Wr, w13s, w2s, sp, steps, warmup, repeat):
         B.check(B.etc_sync(sp))
         return start.elapsed_time(end) * 1e3 / steps
 
-    scheds = ("static", "ordered", "kbk")
     runs = {x: [] for x in scheds}
     for _ in range(repeat):
         for x in scheds:
             runs[x].append(timed(x))
     us = {x: float(np.median(v)) for x, v in runs.items()}
-    best = min(("static", "ordered"), key=lambda x: us[x])
+    best = min((x for x in ("static", "ordered") if x in us), key=lambda x: us[x], default=scheds[0])
     return {
         "workload": s.name, "T": s.T, "pos": s.pos, "heads": [s.nq, s.nkv, s.d], "active_experts": n_act,
         "us_per_layer": {x: round(v, 2) for x, v in us.items()},
         "tokens_per_s": round(s.T / (us[best] * 1e-6), 1), "schedule": best,
         "algorithmic_bytes": alg, "hbm_floor_us": round(alg / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
         "hbm_frac": round(alg / (us[best] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
-        "megakernel_over_kbk_speedup": round(us["kbk"] / us[best], 3),
+        "megakernel_over_kbk_speedup": round(us["kbk"] / us[best], 3) if "kbk" in us else None,
     }
 
 
@@ -466,6 +466,18 @@ def main():
     from dynamic_moe_task_amd import binding as B
     from dynamic_moe_task_amd import workloads as wl
 
+    if a.workload == "decoder":
+        import torch
+        torch.cuda.set_device(0)
+        w = wl.make_weights(wl.DECODE, 0)
+        Wr, W13, Wd = dev_bf16(w.Wr), dev_bf16(w.W13), dev_bf16(w.Wd)
+        R = max(1, a.copies)
+        w13s = [W13] + [W13.clone() for _ in range(R - 1)]
+        w2s = [Wd] + [Wd.clone() for _ in range(R - 1)]
+        sp = torch.cuda.current_stream().cuda_stream
+        scheds = (a.sched,) if a.only_sched else ("static", "ordered", "kbk")
+        print(json.dumps(measure_decoder(Wr, w13s, w2s, sp, a.steps, a.warmup, a.repeat, scheds)), flush=True)
+        return
     shape = wl.SHAPES[a.workload]
     if a.tokens > 0:
         import dataclasses

@@ -201,20 +201,26 @@ __device__ __forceinline__ void task_attn(const MoeParams& p, const Ctx& c, int 
   const size_t cbase = (((size_t)t * p.nkv + g) * p.Lcap + k0) * d;
   const uint16_t* kb = p.kc + cbase;
   f32x4_t sc[8];
-#pragma unroll
-  for (int nb = 0; nb < 8; nb += 2) {
-    u32x4_t b[2][4];
+  // two column blocks a batch; the next batch's keys load while this one multiplies
+  u32x4_t b[2][2][4];
+  auto load_k = [&](int nb, u32x4_t (&bb)[2][4]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = wv * 128 + (nb + u) * 16 + m;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) b[u][s] = e < nk ? ld4(kb + (size_t)e * d + s * 32 + kg * 8) : zero;
+      for (int s = 0; s < 4; ++s) bb[u][s] = e < nk ? ld4(kb + (size_t)e * d + s * 32 + kg * 8) : zero;
     }
+  };
+  load_k(0, b[0]);
+#pragma unroll
+  for (int nb = 0; nb < 8; nb += 2) {
+    if (nb + 2 < 8) load_k(nb + 2, b[((nb >> 1) + 1) & 1]);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(qa[s]), as_bf(b[u][s]), acc, 0, 0, 0);
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(qa[s]), as_bf(b[(nb >> 1) & 1][u][s]), acc, 0, 0, 0);
       sc[nb + u] = acc;
     }
   }
@@ -260,39 +266,77 @@ __device__ __forceinline__ void task_attn(const MoeParams& p, const Ctx& c, int 
     for (int i = 0; i < 4; ++i) wred[wv * 16 + 4 * kg + i] = sm[i];
   lds_barrier();
   if (tid < 16) mrow[16 + tid] = wred[tid] + wred[16 + tid] + wred[32 + tid] + wred[48 + tid];
-  // weighted value sum: heads 2wv and 2wv+1, dims 2 lane and 2 lane + 1
-  const int h0 = 2 * wv;
-  float o00 = 0.f, o01 = 0.f, o10 = 0.f, o11 = 0.f;
-  if (h0 < gq) {
-    const uint16_t* vb = p.vc + cbase + 2 * lane;
-    const float* P0 = P + h0 * kDecChunk;
-    const float* P1 = P0 + kDecChunk;
-    for (int e0 = 0; e0 < nk; e0 += 8) {
-      uint32_t vv[8];
+  // Weighted value sum on the VALU.  Wave wv, lane (kq = lane / 32,
+  // cg = lane % 32) takes entries e = 2 wv + kq + 8 i and dims 4 cg ..
+  // 4 cg + 3, for every head of the group; eight entries' values load while
+  // the previous eight multiply.  The 8 (wave, kq) partial sums are then
+  // added: across kq by a shuffle, across the waves in LDS (over P, which is
+  // no longer read by then).
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const int kq = lane >> 5, cg = lane & 31;
+  const int e0 = 2 * wv + kq;
+  const uint16_t* vb = p.vc + cbase + 4 * cg;
+  float acc[kDecMaxGroup][4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        vv[u] = e0 + u < nk ? *reinterpret_cast<const uint32_t*>(vb + (size_t)(e0 + u) * d) : 0u;
+  for (int h = 0; h < kDecMaxGroup; ++h)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float p0 = P0[e0 + u], p1 = P1[e0 + u];  // zero past nk
-        const float v0 = bf_lo(vv[u]), v1 = bf_hi(vv[u]);
-        o00 = __builtin_fmaf(p0, v0, o00);
-        o01 = __builtin_fmaf(p0, v1, o01);
-        o10 = __builtin_fmaf(p1, v0, o10);
-        o11 = __builtin_fmaf(p1, v1, o11);
+    for (int q = 0; q < 4; ++q) acc[h][q] = 0.f;
+  const u32x2_t zero2 = {0u, 0u};
+  auto load_v = [&](int i0, u32x2_t (&vb8)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + 8 * (i0 + u);
+      vb8[u] = e < nk ? *reinterpret_cast<const u32x2_t*>(vb + (size_t)e * d) : zero2;
+    }
+  };
+  auto consume = [&](int i0, const u32x2_t (&vb8)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + 8 * (i0 + u);
+      if (e < nk) {
+        const float v[4] = {bf_lo(vb8[u].x), bf_hi(vb8[u].x), bf_lo(vb8[u].y), bf_hi(vb8[u].y)};
+#pragma unroll
+        for (int h = 0; h < kDecMaxGroup; ++h) {
+          if (h < gq) {
+            const float pw = P[h * kDecChunk + e];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[h][q] = __builtin_fmaf(pw, v[q], acc[h][q]);
+          }
+        }
       }
     }
+  };
+  const int nsteps = (nk - e0 + 7) / 8;  // entries this thread takes
+  // two buffers, named so that no register array is indexed at run time
+  u32x2_t va[8], vbuf[8];
+  load_v(0, va);
+  for (int i0 = 0; i0 < nsteps; i0 += 16) {
+    if (i0 + 8 < nsteps) load_v(i0 + 8, vbuf);
+    consume(i0, va);
+    if (i0 + 8 < nsteps) {
+      if (i0 + 16 < nsteps) load_v(i0 + 16, va);
+      consume(i0 + 8, vbuf);
+    }
   }
-  lds_barrier();  // the sums are in mrow
+#pragma unroll
+  for (int h = 0; h < kDecMaxGroup; ++h)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[h][q] += __shfl_xor(acc[h][q], 32);
+  lds_barrier();  // every wave is done with P: its space holds the waves' sums
+  float* osum = P;  // [4 waves][gq heads][d]
+  if (kq == 0) {
+#pragma unroll
+    for (int h = 0; h < kDecMaxGroup; ++h)
+      if (h < gq)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) osum[(wv * gq + h) * d + 4 * cg + q] = acc[h][q];
+  }
+  lds_barrier();
   const rsrc_t rp = r_part(p);
   const uint32_t pbase = (uint32_t)((((size_t)t * p.nkv + g) * p.nchunk_max + ch) * p.part_floats * 4);
-  if (h0 < gq) {
-    co_stf(rp, pbase + (uint32_t)((h0 * d + 2 * lane) * 4), o00);
-    co_stf(rp, pbase + (uint32_t)((h0 * d + 2 * lane + 1) * 4), o01);
-    if (h0 + 1 < gq) {
-      co_stf(rp, pbase + (uint32_t)(((h0 + 1) * d + 2 * lane) * 4), o10);
-      co_stf(rp, pbase + (uint32_t)(((h0 + 1) * d + 2 * lane + 1) * 4), o11);
-    }
+  for (int i = tid; i < gq * d; i += kThreads) {
+    const float v = osum[i] + osum[gq * d + i] + osum[2 * gq * d + i] + osum[3 * gq * d + i];
+    co_stf(rp, pbase + (uint32_t)(i * 4), v);
   }
   if (tid < gq) {
     co_stf(rp, pbase + (uint32_t)((gq * d + tid) * 4), mrow[tid]);
@@ -325,23 +369,46 @@ __device__ __forceinline__ void task_attn_merge(const MoeParams& p, const Ctx& c
   const rsrc_t rp = r_part(p);
   const uint32_t pb0 = (uint32_t)((((size_t)t * p.nkv + g) * p.nchunk_max) * p.part_floats * 4);
   const uint32_t pstep = (uint32_t)(p.part_floats * 4);
-  float M = s;
-  for (int ch = 0; ch < p.nchunk; ++ch) M = fmaxf(M, co_ldf(rp, pb0 + ch * pstep + (uint32_t)((gq * d + h) * 4)));
-  const float fs = __expf(s - M);
-  float L = fs;
-  float acc[4] = {fs * bf_lo(v01), fs * bf_hi(v01), fs * bf_lo(v23), fs * bf_hi(v23)};
-  for (int ch = 0; ch < p.nchunk; ++ch) {
-    const uint32_t pb = pb0 + ch * pstep;
-    const float mc = co_ldf(rp, pb + (uint32_t)((gq * d + h) * 4));
-    const float lc = co_ldf(rp, pb + (uint32_t)((gq * d + gq + h) * 4));
-    const u32x4_t ov = co_ld128(rp, pb + (uint32_t)((h * d + 4 * l) * 4));
-    const float f = __expf(mc - M);
-    L = __builtin_fmaf(lc, f, L);
-    acc[0] = __builtin_fmaf(f, __uint_as_float(ov.x), acc[0]);
-    acc[1] = __builtin_fmaf(f, __uint_as_float(ov.y), acc[1]);
-    acc[2] = __builtin_fmaf(f, __uint_as_float(ov.z), acc[2]);
-    acc[3] = __builtin_fmaf(f, __uint_as_float(ov.w), acc[3]);
+  float M = s, L = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  // eight chunks a batch, every load of the batch in flight together; the
+  // running maximum rescales what is summed so far (online softmax merge)
+  for (int c0 = 0; c0 < p.nchunk; c0 += 8) {
+    float mc[8], lc[8];
+    u32x4_t ov[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t pb = pb0 + (uint32_t)(c0 + u) * pstep;
+      const bool ok = c0 + u < p.nchunk;
+      mc[u] = ok ? co_ldf(rp, pb + (uint32_t)((gq * d + h) * 4)) : -__builtin_inff();
+      lc[u] = ok ? co_ldf(rp, pb + (uint32_t)((gq * d + gq + h) * 4)) : 0.f;
+      ov[u] = ok ? co_ld128(rp, pb + (uint32_t)((h * d + 4 * l) * 4)) : (u32x4_t){0u, 0u, 0u, 0u};
+    }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) Mn = fmaxf(Mn, mc[u]);
+    const float r = __expf(M - Mn);
+    L *= r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] *= r;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float f = c0 + u < p.nchunk ? __expf(mc[u] - Mn) : 0.f;
+      L = __builtin_fmaf(lc[u], f, L);
+      acc[0] = __builtin_fmaf(f, __uint_as_float(ov[u].x), acc[0]);
+      acc[1] = __builtin_fmaf(f, __uint_as_float(ov[u].y), acc[1]);
+      acc[2] = __builtin_fmaf(f, __uint_as_float(ov[u].z), acc[2]);
+      acc[3] = __builtin_fmaf(f, __uint_as_float(ov[u].w), acc[3]);
+    }
+    M = Mn;
   }
+  // the new entry's own score and value
+  const float fs = __expf(s - M);
+  L += fs;
+  acc[0] = __builtin_fmaf(fs, bf_lo(v01), acc[0]);
+  acc[1] = __builtin_fmaf(fs, bf_hi(v01), acc[1]);
+  acc[2] = __builtin_fmaf(fs, bf_lo(v23), acc[2]);
+  acc[3] = __builtin_fmaf(fs, bf_hi(v23), acc[3]);
   const float inv = 1.0f / L;
   const uint32_t lo = f2bf(acc[0] * inv) | (f2bf(acc[1] * inv) << 16);
   const uint32_t hi = f2bf(acc[2] * inv) | (f2bf(acc[3] * inv) << 16);
