@@ -39,8 +39,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill_zipf", "tiny", "decoder"],
-                    help="decoder: only the decoder-layer section (diagnostics and profiling)")
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill_zipf", "tiny", "decoder", "tokens"],
+                    help="decoder: only the decoder-layer section; tokens: only the token-count table at "
+                         "--counts (diagnostics and profiling)")
+    ap.add_argument("--counts", default="1,128,1024,4096", help="token counts of --workload tokens")
     ap.add_argument("--tokens", type=int, default=0,
                     help="run the workload's layer at this many tokens instead of its own T (diagnostics, "
                          "e.g. a per-task trace at T=1)")
@@ -466,7 +468,7 @@ def main():
     from dynamic_moe_task_amd import binding as B
     from dynamic_moe_task_amd import workloads as wl
 
-    if a.workload == "decoder":
+    if a.workload in ("decoder", "tokens"):
         import torch
         torch.cuda.set_device(0)
         w = wl.make_weights(wl.DECODE, 0)
@@ -475,6 +477,10 @@ def main():
         w13s = [W13] + [W13.clone() for _ in range(R - 1)]
         w2s = [Wd] + [Wd.clone() for _ in range(R - 1)]
         sp = torch.cuda.current_stream().cuda_stream
+        if a.workload == "tokens":
+            counts = tuple(int(v) for v in a.counts.split(","))
+            print(json.dumps(measure_token_counts(Wr, w13s, w2s, sp, a.steps, a.warmup, a.repeat, counts)), flush=True)
+            return
         scheds = (a.sched,) if a.only_sched else ("static", "ordered", "kbk")
         print(json.dumps(measure_decoder(Wr, w13s, w2s, sp, a.steps, a.warmup, a.repeat, scheds)), flush=True)
         return

@@ -95,7 +95,21 @@ class MoeInfo(ctypes.Structure):
                 ("router_large_from", ctypes.c_int32), ("bn1_large", ctypes.c_int32),
                 ("bn1_large_from_rows", ctypes.c_int32), ("bn2_large", ctypes.c_int32),
                 ("bn1_mid", ctypes.c_int32), ("bn1_mid_from_rows", ctypes.c_int32),
-                ("router_experts_xl", ctypes.c_int32), ("router_xl_from", ctypes.c_int32)]
+                ("router_experts_xl", ctypes.c_int32), ("router_xl_from", ctypes.c_int32),
+                ("big_from_rows", ctypes.c_int32), ("bm_big", ctypes.c_int32), ("bn1_big", ctypes.c_int32),
+                ("bn2_big", ctypes.c_int32), ("grid_big", ctypes.c_int32), ("lds_bytes_big", ctypes.c_int32)]
+
+    def big_for(self, T: int, k: int) -> bool:
+        """Whether a launch at batch T, top-k k runs the big-tile variant."""
+        return self.big_from_rows > 0 and T * k >= self.big_from_rows
+
+    def bm_for(self, T: int, k: int) -> int:
+        """Grouped rows per row tile at batch T, top-k k."""
+        return self.bm_big if self.big_for(T, k) else self.bm
+
+    def grid_for(self, T: int, k: int) -> int:
+        """Persistent workgroups of a launch at batch T, top-k k."""
+        return self.grid_big if self.big_for(T, k) else self.grid
 
     def router_experts_for(self, T: int) -> int:
         """Experts per router task at batch T."""
@@ -105,12 +119,16 @@ class MoeInfo(ctypes.Structure):
 
     def bn1_for(self, T: int, k: int) -> int:
         """Gate (and up) columns per G1 tile at batch T, top-k k."""
+        if self.big_for(T, k):
+            return self.bn1_big
         if T * k >= self.bn1_large_from_rows:
             return self.bn1_large
         return self.bn1_mid if T * k >= self.bn1_mid_from_rows else self.bn1
 
     def bn2_for(self, T: int, k: int) -> int:
         """Output columns per G2 tile at batch T, top-k k."""
+        if self.big_for(T, k):
+            return self.bn2_big
         return self.bn2_large if T * k >= self.bn1_large_from_rows else self.bn2
 
 

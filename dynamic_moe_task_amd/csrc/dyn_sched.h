@@ -51,6 +51,11 @@ namespace etc {
 // (column-split G tiles, eight-experts-a-wave router tiles) once T * k
 // selects the column-split tiles.
 ETC_HD bool wide_variant(int T, int k, int H, int I) { return g1_cols(T, k, H) > 2 * kBN1 || g2_cols(T, k, I) > kBN2; }
+// the variant a launch runs: big tiles for the largest batches, else the
+// large-batch variant once it is selected, else the small-batch one
+ETC_HD int launch_variant_of(int T, int k, int H, int I) {
+  return big_variant(T, k, H, I) ? kVarBig : (wide_variant(T, k, H, I) ? kVarWide : kVarSmall);
+}
 
 namespace dyn {
 
@@ -95,17 +100,19 @@ ETC_HD MoeGraph moe_graph(int T, int E, int k, int H, int I, int router_tokens, 
   g.ctok = combine_tokens;
   return g;
 }
-// Task counts of a launch of T tokens in the variant `wide`.  The router
-// tiles and G tile widths are those the variant's bodies run: the
-// small-batch variant has no eight-experts-a-wave router tile and no
-// column-split G tiles, so there the router task count follows four
-// experts a wave and the G1 width stops at 32 columns.
-ETC_HD MoeGraph launch_graph(int T, int E, int k, int H, int I, bool wide) {
+// Task counts of a launch of T tokens in variant `var` (kVarSmall, kVarWide
+// or kVarBig).  The router tiles and G tile widths are those the variant's
+// bodies run: the small-batch variant has no eight-experts-a-wave router
+// tile and no column-split G tiles, so there the router task count follows
+// four experts a wave and the G1 width stops at 32 columns; the big-tile
+// variant runs the large-batch router and its own G tile widths.
+ETC_HD MoeGraph launch_graph(int T, int E, int k, int H, int I, int var) {
   int re = router_experts(T);
-  if (!wide && re == kRouterEXL) re = kRouterEL;
+  if (var == kVarSmall && re == kRouterEXL) re = kRouterEL;
+  if (var == kVarBig) return moe_graph(T, E, k, H, I, kRouterT, re, kCombineT, kBigBN1, kBigBN2);
   int bn1 = g1_cols(T, k, H);
-  if (!wide && bn1 > 2 * kBN1) bn1 = 2 * kBN1;
-  const int bn2 = wide ? g2_cols(T, k, I) : kBN2;
+  if (var == kVarSmall && bn1 > 2 * kBN1) bn1 = 2 * kBN1;
+  const int bn2 = var == kVarWide ? g2_cols(T, k, I) : kBN2;
   return moe_graph(T, E, k, H, I, kRouterT, re, kCombineT, bn1, bn2);
 }
 // every task a launch of nrt row tiles runs: the router prefix, then
@@ -191,7 +198,7 @@ struct Shared {
   int flag;       // thread 0's notify completed its event
   int n;          // completed events collected by this task
   int base;       // first reserved slot
-  int list[64];   // combine tasks released by a row tile (one per row at most)
+  int list[kBigBM];  // combine tasks released by a row tile (one per row at most; big tiles hold kBigBM rows)
 };
 
 // Pop index -> router task of the prefix

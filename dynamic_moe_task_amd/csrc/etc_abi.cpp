@@ -136,6 +136,11 @@ int64_t lds_bytes_for(const etc_moe_desc* d) {
   int64_t s = scan_lds_bytes(d->E, d->T_max);
   return s > kGemmLdsBytes ? s : kGemmLdsBytes;
 }
+// the big-tile variant's dynamic LDS: its G stages, or the scan's if larger
+int64_t big_lds_bytes(const etc_moe_desc* d) {
+  const int64_t s = lds_bytes_for(d);
+  return s > kBigLdsBytes ? s : kBigLdsBytes;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -447,6 +452,16 @@ extern "C" int moe_layer_info(const etc_moe_desc* d, etc_moe_info* info) {
   rc = persistent_grid(ETC_SCHED_STATIC, info->lds_bytes, &grid);
   if (rc) return rc;
   info->grid = grid;
+  if (big_variant(kBigRows, 1, d->H, d->I)) {
+    info->big_from_rows = kBigRows;
+    info->bm_big = kBigBM;
+    info->bn1_big = kBigBN1;
+    info->bn2_big = kBigBN2;
+    info->lds_bytes_big = (int32_t)big_lds_bytes(d);
+    rc = persistent_grid(kBigSchedBase + ETC_SCHED_STATIC, info->lds_bytes_big, &grid);
+    if (rc) return rc;
+    info->grid_big = grid;
+  }
   uint64_t per_ms = 0;
   rc = watchdog_ticks(1000, &per_ms);
   if (rc) return rc;
@@ -586,14 +601,17 @@ static int layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a,
     p.resid_bytes = (uint32_t)(Tm * H * 2);
   }
 
-  const int lds = (int)lds_bytes_for(d);
+  // the kernel variant of this T (the decoder layer's T <= 16 never runs
+  // the big tiles); the big-tile variant has its own LDS size and grid
+  const bool big = !dd && big_variant(T, d->k, d->H, d->I);
+  const int lds = (int)(big ? big_lds_bytes(d) : lds_bytes_for(d));
   int e;
   if (sched == ETC_SCHED_KBK) {
     e = dd ? launch_decoder_kbk(p, (int)scan_lds_bytes(d->E, d->T_max), stream)
            : launch_moe_kbk(p, (int)scan_lds_bytes(d->E, d->T_max), stream);
   } else {
     int grid = 0, solo = 0;
-    rc = persistent_grid(dd ? kDecSchedBase + sched : sched, lds, &grid, &solo);
+    rc = persistent_grid(dd ? kDecSchedBase + sched : (big ? kBigSchedBase + sched : sched), lds, &grid, &solo);
     if (rc) return rc;
     p.solo_wgs = solo;
     e = launch_moe_persistent(p, sched, grid, lds, stream);

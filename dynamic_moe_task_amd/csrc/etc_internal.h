@@ -31,7 +31,7 @@ constexpr int kEvStride = 32;   // words between event elements (one 128-byte li
 constexpr int kMaxK = 16;
 constexpr int kMaxE = 256;
 constexpr int kMaxTmax = 16384;
-constexpr int kMaxHI = 16384;
+constexpr int kMaxHI = 40960;  // covers the dense MLPs of the pages' appendix table (I up to 36864)
 constexpr int kScanChunkT = 512;       // S: tokens per bitmap pass
 constexpr int kScanW = kScanChunkT / 32;  // S: bitmap words per expert and pass
 // Small batches (T <= kScanChunkT and T*k <= kLocalRows): every persistent
@@ -254,6 +254,10 @@ int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream);
 int launch_decoder_kbk(const MoeParams& p, int lds_bytes, void* stream);
 // occupancy queries of the decoder-layer variants: kDecSchedBase + sched
 constexpr int kDecSchedBase = 16;
+// occupancy queries of the big-tile variant: kBigSchedBase + sched
+constexpr int kBigSchedBase = 32;
+// the big-tile variant's G tasks: two LDS stages of 512 rows x 64 k (bf16)
+constexpr int kBigLdsBytes = 2 * 512 * 64 * 2;
 int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu);
 int launch_splitk(int n, int nsplit, int bk, const int32_t* A, int32_t* B, int32_t* C, int32_t* ev,
                   const etc_edge& notify_edge, const etc_edge& wait_edge, int32_t wait_count, uint32_t* ctl,

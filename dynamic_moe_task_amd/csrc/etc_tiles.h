@@ -41,5 +41,20 @@ ETC_HD int g2_cols(int T, int k, int I) {
   return (T * k >= kWideG1Rows && I % 128 == 0) ? 2 * kBN2 : kBN2;
 }
 constexpr int kCombineT = 2;    // C task: tokens per task
+// Large batches run the big-tile kernel variant: row tiles of up to
+// kBigBM grouped rows, G1 tiles of kBigBN1 gate and as many up columns, G2
+// tiles of kBigBN2 output columns, K staged 64 at a time.  Each weight
+// element streamed from memory then feeds up to 256 rows (the row tiles of
+// the other variants hold at most 64), which is what lets the grouped GEMM
+// approach the matrix cores' rate once experts hold hundreds of rows.
+constexpr int kBigBM = 256;
+constexpr int kBigBN1 = 128;
+constexpr int kBigBN2 = 256;
+constexpr int kBigRows = 8192;  // T * k from which the big tiles run
+ETC_HD bool big_variant(int T, int k, int H, int I) {
+  return T * k >= kBigRows && H % kBigBN2 == 0 && I % kBigBN1 == 0;
+}
+// kernel variants: small batches, large batches (column-split tiles), big tiles
+enum : int { kVarSmall = 0, kVarWide = 1, kVarBig = 2 };
 
 }  // namespace etc

@@ -122,6 +122,7 @@ struct Ctx {
   int T, H, E, k, I;
   int bn1;  // G1 gate (and up) columns per tile, chosen per launch from T
   int bn2;  // G2 output columns per tile, chosen per launch from T
+  int bm;   // grouped rows per row tile (kBigBM in the big-tile variant, else kBM)
   int nTT, nET, nR, nK, nC, nN1, nN2;
   uint64_t budget;  // watchdog of one wait, wall-clock ticks
 };
@@ -136,10 +137,14 @@ __device__ __forceinline__ Ctx make_ctx(const MoeParams& p, uint32_t* set) {
   c.nR = c.nTT * c.nET;
   c.nK = c.nTT;
   c.nC = (p.T + kCombineT - 1) / kCombineT;
-  c.bn1 = g1_cols(p.T, p.k, p.H);
+  // tile shapes of the variant a launch of T tokens runs (the host picks the
+  // variant with the same rule)
+  const bool big = big_variant(p.T, p.k, p.H, p.I);
+  c.bn1 = big ? kBigBN1 : g1_cols(p.T, p.k, p.H);
   c.nN1 = p.I / c.bn1;
-  c.bn2 = g2_cols(p.T, p.k, p.I);
+  c.bn2 = big ? kBigBN2 : g2_cols(p.T, p.k, p.I);
   c.nN2 = p.H / c.bn2;
+  c.bm = big ? kBigBM : kBM;
   c.budget = p.budget;
   return c;
 }
@@ -620,10 +625,15 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
   }
   lds_barrier();
   const int my = tid < E ? cnt[tid] : 0;
-  const int mytiles = (my + kBM - 1) / kBM;
-  const int rem = my % kBM;
-  const int n4 = my / kBM + (rem > 32 ? 1 : 0), n2 = (rem > 16 && rem <= 32) ? 1 : 0,
-            n1 = (rem > 0 && rem <= 16) ? 1 : 0;
+  // Row tiles of bm rows.  Tiles of up to kBM rows are numbered by size
+  // class (tiles of 33 to 64 rows first, then 17 to 32, then 1 to 16, each
+  // class by expert); big tiles are numbered by expert only.
+  const int bm = c.bm;
+  const bool big = bm != kBM;
+  const int mytiles = (my + bm - 1) / bm;
+  const int rem = my % bm;
+  const int n4 = big ? mytiles : my / kBM + (rem > 32 ? 1 : 0), n2 = (!big && rem > 16 && rem <= 32) ? 1 : 0,
+            n1 = (!big && rem > 0 && rem <= 16) ? 1 : 0;
   const int sv[5] = {my, mytiles, n4, n2, n1};
   int sx[5], st[5];
   block_excl_scan_n<5>(sv, sx, st, tmp);
@@ -633,7 +643,7 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
   if (tid < E) {
     iptr[tid] = ex;
     tfirst[tid] = ex4 | (n4 << 16);
-    ttail[tid] = rem > 32 ? -1 : (rem > 16 ? tot4 + ex2 : tot4 + tot2 + ex1);
+    ttail[tid] = (big || rem > 32) ? -1 : (rem > 16 ? tot4 + ex2 : tot4 + tot2 + ex1);
     if (LOCAL) {
       lr->cnt[tid] = (uint16_t)my;
     } else {
@@ -737,7 +747,7 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
           if (q < np) {
             const int s = base[e[u]] + q;
             co_st32(rp, (uint32_t)s * 4u, (uint32_t)(f0 + fl[u]));
-            const int mt = (s - iptr[e[u]]) / kBM, tf = tfirst[e[u]];  // the row's tile, numbered as below
+            const int mt = (s - iptr[e[u]]) / bm, tf = tfirst[e[u]];  // the row's tile, numbered as below
             co_st32(rrt, (uint32_t)s * 4u, (uint32_t)(mt < (tf >> 16) ? (tf & 0xffff) + mt : ttail[e[u]]));
           }
         }
@@ -747,16 +757,16 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
   }
   const rsrc_t rr = r_rtinfo(p);
   if (tid < E) {
-    for (int mt = 0; mt * kBM < my; ++mt) {
-      const int rows = min(kBM, my - mt * kBM);
-      const int rt = rows > 32 ? ex4 + mt : (rows > 16 ? tot4 + ex2 : tot4 + tot2 + ex1);
+    for (int mt = 0; mt * bm < my; ++mt) {
+      const int rows = min(bm, my - mt * bm);
+      const int rt = (big || rows > 32) ? ex4 + mt : (rows > 16 ? tot4 + ex2 : tot4 + tot2 + ex1);
       if (LOCAL) {
-        lr->tile[rt] = (uint32_t)tid | ((uint32_t)rows << 9) | ((uint32_t)(ex + mt * kBM) << 16);
+        lr->tile[rt] = (uint32_t)tid | ((uint32_t)rows << 9) | ((uint32_t)(ex + mt * bm) << 16);
         continue;
       }
       u32x4_t q;
       q.x = (uint32_t)tid;
-      q.y = (uint32_t)(ex + mt * kBM);
+      q.y = (uint32_t)(ex + mt * bm);
       q.z = (uint32_t)rows;
       q.w = 0u;
       co_st128(rr, (uint32_t)rt * 16u, q);
@@ -1000,6 +1010,8 @@ __device__ __forceinline__ void g1_cs_body(const MoeParams& p, const Ctx& c, con
   }
 }
 
+#include "big_tiles.h"
+
 // k-steps per load batch (U) by row blocks, measured on MI355X: short
 // batches stream better in the persistent kernel (two workgroups per CU);
 // the separate G kernels of the kernel-by-kernel launch keep longer batches
@@ -1007,10 +1019,14 @@ __device__ __forceinline__ void g1_cs_body(const MoeParams& p, const Ctx& c, con
 // (c.bn1 = 32: large batches, where a four-block tile's gathered x rows
 // outweigh its weights) read each tile's x rows once for 32 gate and 32 up
 // columns instead of 16.
-template <bool KBK = false, bool WIDE = true>
+template <bool KBK = false, int WIDE = kVarWide>
 __device__ __forceinline__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt, float* red,
                         const uint32_t* pre = nullptr) {
   (void)rt;
+  if constexpr (WIDE == kVarBig) {
+    big_body<true>(p, c, tile, nt, reinterpret_cast<uint8_t*>(red));
+    return;
+  }
   if (WIDE && c.bn1 == 4 * kBN1) {
     // column-split tiles need their row tokens per row block: load them
     // here when the caller has not
@@ -1209,8 +1225,12 @@ __device__ __forceinline__ void g2_cs_body(const MoeParams& p, const Ctx& c, con
   }
 }
 
-template <bool KBK = false, bool WIDE = true>
+template <bool KBK = false, int WIDE = kVarWide>
 __device__ __forceinline__ void task_g2(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt2, float* red) {
+  if constexpr (WIDE == kVarBig) {
+    big_body<false>(p, c, tile, nt2, reinterpret_cast<uint8_t*>(red));
+    return;
+  }
   (void)rt;
   if (WIDE && c.bn2 == 2 * kBN2) {
     switch (row_blocks(tile.nrows)) {
@@ -1394,7 +1414,7 @@ __device__ __forceinline__ bool wait_rows_done(const MoeParams& p, const Ctx& c,
   return fail == 0;
 }
 
-template <bool WG>
+template <int WG>
 __device__ __forceinline__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G,
                               const LocalRoute* lr) {
   if (i0 >= n) return;
@@ -1454,7 +1474,7 @@ __device__ __forceinline__ void run_g1_static(const MoeParams& p, const Ctx& c, 
   }
 }
 
-template <bool WG>
+template <int WG>
 __device__ __forceinline__ void run_g2_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G,
                               const LocalRoute* lr) {
   if (i0 >= n) return;
@@ -1537,7 +1557,7 @@ __device__ __forceinline__ GTask gtask(const Ctx& c, int i, int nG1) {
 // I/16) for G2; its state is fetched one tile ahead, the row-tile descriptor
 // two ahead and the claim three ahead.  Returns false when a wait gave up
 // (the launch is aborting).
-template <bool WG>
+template <int WG>
 __device__ __forceinline__ bool run_g_ordered(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q, int nG1, uint32_t* sk,
                               const LocalRoute* lr) {
   const int n = q.n;
@@ -1644,7 +1664,7 @@ __device__ __forceinline__ bool run_g_ordered(const MoeParams& p, const Ctx& c, 
 // claim's result to the other threads through sk[0] and an LDS barrier.
 // Deadlock freedom as in run_g_ordered: a workgroup's tiles come in
 // ascending index order, every G1 tile below every G2 tile.
-template <bool WG>
+template <int WG>
 __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q,
                                                     int nG1, uint32_t* sk, const LocalRoute* lr) {
   const int n = q.n;
@@ -1753,7 +1773,7 @@ __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ct
 // events produced by earlier phases, so with every workgroup resident no
 // wait can be circular and the schedule cannot deadlock.  Task counts of the
 // phases after S are read from S's output (data-dependent instantiation).
-template <int MODE, bool WG>
+template <int MODE, int WG>
 __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint8_t* smem, Shared& sh,
                                           int64_t off0 = 0) {
   const int G = gridDim.x, w = blockIdx.x;
@@ -1770,7 +1790,7 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
     return;
   for (int i = first_of(w, off, G); i < c.nR; i += G) {
     if (tr) tw = ts = now_ticks();
-    task_router<WG>(p, c, i / c.nET, i % c.nET);
+    task_router<(WG != kVarSmall)>(p, c, i / c.nET, i % c.nET);
     if (tr) tb = now_ticks();
     dbg_task(p, TT_R);
     after_router<MODE>(p, c, i / c.nET);
@@ -1804,7 +1824,7 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   // Small batch: each workgroup rebuilds the routing tables in its own LDS
   // as soon as every top-k task is done, so G1 does not wait for S (S still
   // writes the routing outputs, which C reads).
-  const bool local = EV && c.T <= kScanChunkT && c.T * c.k <= kLocalRows;
+  const bool local = WG != kVarBig && EV && c.T <= kScanChunkT && c.T * c.k <= kLocalRows;
   // ORDERED claim counters: one per XCD group for large batches, where the
   // first three claims are taken while S still runs (an ordinal does not
   // depend on S's result); one for the whole grid with the LDS tables,
@@ -1907,7 +1927,7 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
 // logic (queue, pushes on completed events, the exit rule) is dyn::run_moe
 // in dyn_sched.h, shared with a host harness that drives it with threads.
 // DynTasks gives it this kernel's task bodies, event elements and trace.
-template <bool WG>
+template <int WG>
 struct DynTasks {
   const MoeParams& p;
   const Ctx& c;
@@ -1915,7 +1935,7 @@ struct DynTasks {
   Shared& ksh;
   RowTile tile;  // the row tile of the last G2 task (its rows arrive at their combine events)
   uint64_t tw, tb;
-  __device__ __forceinline__ void router(int tt, int et) { task_router<WG>(p, c, tt, et); }
+  __device__ __forceinline__ void router(int tt, int et) { task_router<(WG != kVarSmall)>(p, c, tt, et); }
   __device__ __forceinline__ void topk(int tt) { task_topk(p, c, tt); }
   __device__ __forceinline__ int scan() { return task_scan<false, false>(p, c, smem); }
   __device__ __forceinline__ void g1(int rt, int nt) {
@@ -1953,15 +1973,16 @@ struct DynTasks {
 // by the previous launch) and zeroes set[1 - (epoch & 1)] for the next one;
 // the last workgroup to finish advances the epoch.  No host memset, no host
 // state: the workspace is self-resetting, also after an aborted launch.
-// WG: the variant that holds the wide G1 tiles (launched when T * k selects
-// them); the other variant holds the narrow tiles only, so that small
-// batches run code that carries none of the wide tiles' register pressure.
-// Both come from the one code object; T stays a kernel argument.
+// WG: the kernel variant (kVarSmall, kVarWide, kVarBig), picked per launch
+// from T * k: the large-batch variant holds the wide G1 tiles, the small one
+// the narrow tiles only, so that small batches run code that carries none
+// of the wide tiles' register pressure, and the big-tile variant (its own
+// kernel, moe_persistent_big) the 256-row tiles.  All come from the one
+// code object; T stays a kernel argument.
 // DEC: the decoder layer: the attention block's tasks run first, in the same
 // kernel, and the MoE block's router waits on their last event.
-template <int MODE, bool WG, bool DEC = false>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-moe_persistent(MoeParams p) {
+template <int MODE, int WG, bool DEC>
+__device__ __forceinline__ void persistent_body(const MoeParams& p) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ Shared sh;
   __shared__ uint32_t s_epoch;
@@ -1986,6 +2007,7 @@ moe_persistent(MoeParams p) {
     c.bn1 = p.I / g.nN1;
     c.nN2 = g.nN2;
     c.bn2 = p.H / g.nN2;
+    c.bm = WG == kVarBig ? kBigBM : kBM;
     if (MODE == MODE_DYNAMIC) {
       dyn::Queue q;
       q.head = set + W_HEAD;
@@ -2015,6 +2037,18 @@ moe_persistent(MoeParams p) {
     const uint32_t old = add_relaxed(set + W_DONE, 1u);
     if (old == gridDim.x - 1u) xchg_relaxed(p.ctrl + C_EPOCH, epoch + 1u);
   }
+}
+template <int MODE, int WG, bool DEC = false>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+moe_persistent(MoeParams p) {
+  persistent_body<MODE, WG, DEC>(p);
+}
+// The big-tile variant: one workgroup a CU (its G tiles take 128 KB of LDS
+// and the full register file), so its G bodies may keep 256 accumulators.
+template <int MODE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+moe_persistent_big(MoeParams p) {
+  persistent_body<MODE, kVarBig, false>(p);
 }
 
 // ------------------------------------------- kernel-by-kernel comparator --
@@ -2050,6 +2084,23 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   if ((int)blockIdx.x >= nrt * c.nN2) return;
   const int rt = blockIdx.x / c.nN2;
   task_g2<true>(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN2, red);
+}
+// big-tile G tasks, one a workgroup (kBigLdsBytes of dynamic LDS each)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) kbk_g1_big(MoeParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const Ctx c = make_ctx(p, nullptr);
+  const int nrt = (int)ld_relaxed(p.meta + M_NRT);
+  if ((int)blockIdx.x >= nrt * c.nN1) return;
+  const int rt = blockIdx.x / c.nN1;
+  task_g1<true, kVarBig>(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN1, reinterpret_cast<float*>(smem));
+}
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) kbk_g2_big(MoeParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const Ctx c = make_ctx(p, nullptr);
+  const int nrt = (int)ld_relaxed(p.meta + M_NRT);
+  if ((int)blockIdx.x >= nrt * c.nN2) return;
+  const int rt = blockIdx.x / c.nN2;
+  task_g2<true, kVarBig>(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN2, reinterpret_cast<float*>(smem));
 }
 __global__ void __launch_bounds__(kThreads) kbk_combine(MoeParams p) {
   __shared__ int pairs[2 * kCombineT * kMaxK];
@@ -2089,24 +2140,24 @@ __global__ void __launch_bounds__(kThreads) kd_norm2(MoeParams p) {
 
 // ------------------------------------------------------- host launchers --
 // The variant a launch of T tokens runs: the wide G1 tiles from T * k on.
-static bool wide_g1(const MoeParams& p) { return wide_variant(p.T, p.k, p.H, p.I); }
-
 template <int MODE>
-static void launch_variant(const MoeParams& p, bool wide, int grid, int lds_bytes, hipStream_t s) {
-  if (wide)
-    hipLaunchKernelGGL((moe_persistent<MODE, true>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+static void launch_variant(const MoeParams& p, int var, int grid, int lds_bytes, hipStream_t s) {
+  if (var == kVarBig)
+    hipLaunchKernelGGL((moe_persistent_big<MODE>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+  else if (var == kVarWide)
+    hipLaunchKernelGGL((moe_persistent<MODE, kVarWide>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
   else
-    hipLaunchKernelGGL((moe_persistent<MODE, false>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+    hipLaunchKernelGGL((moe_persistent<MODE, kVarSmall>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
 }
 
 int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const bool wide = wide_g1(p);
+  const int wide = launch_variant_of(p.T, p.k, p.H, p.I);
   if (p.dec) {  // decoder layer: at most 16 tokens, the small-batch variant
     if (sched == ETC_SCHED_STATIC)
-      hipLaunchKernelGGL((moe_persistent<MODE_STATIC, false, true>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+      hipLaunchKernelGGL((moe_persistent<MODE_STATIC, kVarSmall, true>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
     else if (sched == ETC_SCHED_ORDERED)
-      hipLaunchKernelGGL((moe_persistent<MODE_ORDERED, false, true>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
+      hipLaunchKernelGGL((moe_persistent<MODE_ORDERED, kVarSmall, true>), dim3(grid), dim3(kThreads), lds_bytes, s, p);
     else
       return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
@@ -2130,27 +2181,44 @@ int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes
   return (int)hipGetLastError();
 }
 
-// Workgroups per CU that stay resident: the smaller of the two variants'
-// (the grid must be resident whichever variant a launch runs).
+// Workgroups per CU that stay resident: the smaller of the small- and
+// large-batch variants' (the grid must be resident whichever of the two a
+// launch runs); the big-tile variant has its own grid (kBigSchedBase).
 template <int MODE>
 static hipError_t occupancy_both(int* blocks_per_cu, int lds_bytes) {
   int a = 0, b = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, moe_persistent<MODE, false>, kThreads, lds_bytes);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, moe_persistent<MODE, kVarSmall>, kThreads, lds_bytes);
   if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, moe_persistent<MODE, true>, kThreads, lds_bytes);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, moe_persistent<MODE, kVarWide>, kThreads, lds_bytes);
   *blocks_per_cu = a < b ? a : b;
   return e;
+}
+template <int MODE>
+static hipError_t occupancy_big(int* blocks_per_cu, int lds_bytes) {
+  // the dynamic LDS above 64 KB must be allowed before the query and launch
+  hipError_t e = hipFuncSetAttribute((const void*)moe_persistent_big<MODE>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent_big<MODE>, kThreads, lds_bytes);
 }
 
 int moe_persistent_occupancy(int sched, int lds_bytes, int* blocks_per_cu) {
   hipError_t e;
   switch (sched) {
     case kDecSchedBase + ETC_SCHED_STATIC:
-      return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_STATIC, false, true>,
+      return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_STATIC, kVarSmall, true>,
                                                                kThreads, lds_bytes);
     case kDecSchedBase + ETC_SCHED_ORDERED:
-      return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_ORDERED, false, true>,
+      return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, moe_persistent<MODE_ORDERED, kVarSmall, true>,
                                                                kThreads, lds_bytes);
+    case kBigSchedBase + ETC_SCHED_STATIC:
+      return (int)occupancy_big<MODE_STATIC>(blocks_per_cu, lds_bytes);
+    case kBigSchedBase + ETC_SCHED_ORDERED:
+      return (int)occupancy_big<MODE_ORDERED>(blocks_per_cu, lds_bytes);
+    case kBigSchedBase + ETC_SCHED_BARRIER:
+      return (int)occupancy_big<MODE_BARRIER>(blocks_per_cu, lds_bytes);
+    case kBigSchedBase + ETC_SCHED_DYNAMIC:
+      return (int)occupancy_big<MODE_DYNAMIC>(blocks_per_cu, lds_bytes);
     case ETC_SCHED_STATIC:
       e = occupancy_both<MODE_STATIC>(blocks_per_cu, lds_bytes);
       break;
@@ -2189,13 +2257,24 @@ int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream) {
   const int nET = (p.E + router_experts(p.T) - 1) / router_experts(p.T);
   const int nC = (p.T + kCombineT - 1) / kCombineT;
   const int64_t rows = (int64_t)p.T * p.k;
-  const int64_t max_rt = (rows + kBM - 1) / kBM + (rows < p.E ? rows : p.E);
-  const int nN1 = p.I / g1_cols(p.T, p.k, p.H), nN2 = p.H / g2_cols(p.T, p.k, p.I);
+  const bool big = big_variant(p.T, p.k, p.H, p.I);
+  const int bm = big ? kBigBM : kBM;
+  const int64_t max_rt = (rows + bm - 1) / bm + (rows < p.E ? rows : p.E);
+  const int nN1 = p.I / (big ? kBigBN1 : g1_cols(p.T, p.k, p.H)), nN2 = p.H / (big ? kBigBN2 : g2_cols(p.T, p.k, p.I));
   hipLaunchKernelGGL(kbk_router, dim3(nTT * nET), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_topk, dim3(nTT), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_scan, dim3(1), dim3(kThreads), lds_bytes, s, p);
-  hipLaunchKernelGGL(kbk_g1, dim3((unsigned)(max_rt * nN1)), dim3(kThreads), 0, s, p);
-  hipLaunchKernelGGL(kbk_g2, dim3((unsigned)(max_rt * nN2)), dim3(kThreads), 0, s, p);
+  if (big) {
+    hipError_t e = hipFuncSetAttribute((const void*)kbk_g1_big, hipFuncAttributeMaxDynamicSharedMemorySize, kBigLdsBytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)kbk_g2_big, hipFuncAttributeMaxDynamicSharedMemorySize, kBigLdsBytes);
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(kbk_g1_big, dim3((unsigned)(max_rt * nN1)), dim3(kThreads), kBigLdsBytes, s, p);
+    hipLaunchKernelGGL(kbk_g2_big, dim3((unsigned)(max_rt * nN2)), dim3(kThreads), kBigLdsBytes, s, p);
+  } else {
+    hipLaunchKernelGGL(kbk_g1, dim3((unsigned)(max_rt * nN1)), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(kbk_g2, dim3((unsigned)(max_rt * nN2)), dim3(kThreads), 0, s, p);
+  }
   hipLaunchKernelGGL(kbk_combine, dim3(nC), dim3(kThreads), 0, s, p);
   return (int)hipGetLastError();
 }

@@ -59,6 +59,21 @@ PREFILL_ZIPF = MoEShape("qwen3-30b-a3b moe prefill T=256 zipf1.1", T=256, H=2048
                         I=768, zipf_s=1.1)
 SWEEP = MoEShape("qwen3-30b-a3b moe sweep B~U[1,512]", T=512, H=2048, E=128, k=8, I=768)
 SHAPES = {"tiny": TINY, "decode": DECODE, "prefill_zipf": PREFILL_ZIPF, "sweep": SWEEP}
+# Qwen-shape layer at the largest token count of the pages' MoE-layer table
+# (the batch where the grouped GEMM nears the matrix-core ridge)
+LARGE = MoEShape("qwen3-30b-a3b moe T=4096", T=4096, H=2048, E=128, k=8, I=768)
+
+# Dense MLPs of the pages' appendix table of MLP configurations (sequence
+# length S, hidden H, intermediate I of five public models), run through the
+# MoE path as one expert that every token picks (E = 1, k = 1: the top-k
+# weight renormalises to 1 and the layer is the dense SwiGLU MLP).
+MLP_TABLE = [
+    MoEShape("MLP-1 (Qwen3-8B) S=8192", T=8192, H=4096, E=1, k=1, I=12288),
+    MoEShape("MLP-2 (LLaMA-3.1-8B) S=8192", T=8192, H=4096, E=1, k=1, I=14336),
+    MoEShape("MLP-3 (Gemma-2-9B) S=8192", T=8192, H=3584, E=1, k=1, I=14336),
+    MoEShape("MLP-4 (Gemma-2-27B) S=8192", T=8192, H=4608, E=1, k=1, I=36864),
+    MoEShape("MLP-5 (Qwen3-32B) S=8192", T=8192, H=5120, E=1, k=1, I=25600),
+]
 
 
 def to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -92,8 +107,23 @@ def make_weights(shape: MoEShape, seed: int = 0, w_std: float = 0.02, threads: i
         W13[e] = _normal_bf16(np.random.default_rng((seed, 1, e)), (2 * I, H), w_std)
         Wd[e] = _normal_bf16(np.random.default_rng((seed, 2, e)), (H, I), w_std)
 
+    # one expert (the dense MLPs): its rows in blocks, one generator a block,
+    # so that the threads share the work
+    blk = 1024
+
+    def fill_rows(job):
+        which, r0 = job
+        if which == 1:
+            W13[0, r0:r0 + blk] = _normal_bf16(np.random.default_rng((seed, 1, 0, r0)), W13[0, r0:r0 + blk].shape, w_std)
+        else:
+            Wd[0, r0:r0 + blk] = _normal_bf16(np.random.default_rng((seed, 2, 0, r0)), Wd[0, r0:r0 + blk].shape, w_std)
+
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(fill, range(E)))
+        if E == 1:
+            jobs = [(1, r) for r in range(0, 2 * I, blk)] + [(2, r) for r in range(0, H, blk)]
+            list(ex.map(fill_rows, jobs))
+        else:
+            list(ex.map(fill, range(E)))
     return MoEWeights(Wr, W13, Wd, None, seed)
 
 

@@ -173,7 +173,7 @@ int etc_splitk_launch(etc_etensor* ev, int32_t n, int32_t nsplit, int32_t bk, co
  * plain softmax value (norm_topk = 0).  Experts: SwiGLU,
  * y = (silu(x Wg^T) * (x Wu^T)) Wd^T with Wg = w13[e, 0:I, :],
  * Wu = w13[e, I:2I, :], Wd = w2[e].  Output: sum_j topk_w[t, j] * y_j.
- * Limits: H and I multiples of 128 and <= 16384; 1 <= E <= 256;
+ * Limits: H and I multiples of 128 and <= 40960; 1 <= E <= 256;
  * 1 <= k <= min(E, 16); 1 <= T_max <= 16384 and T_max * k * max(H, I) * 2
  * bytes below 2 GiB.                                                        */
 typedef struct {
@@ -280,6 +280,11 @@ typedef struct {
   int32_t bn1_mid_from_rows;
   int32_t router_experts_xl; /* R tile's experts when T >= router_xl_from      */
   int32_t router_xl_from;    /* (below it, router_experts / _large apply)       */
+  int32_t big_from_rows;     /* T*k from which launches run the big-tile
+                                variant (0: this descriptor's H, I never do) */
+  int32_t bm_big, bn1_big, bn2_big; /* its row tile, G1 and G2 widths        */
+  int32_t grid_big;          /* its persistent workgroups (one a CU)          */
+  int32_t lds_bytes_big;     /* its dynamic LDS per workgroup                 */
 } etc_moe_info;
 
 /* Fill `info` for `desc` (host struct).  Queries the device for the grid.

@@ -137,11 +137,12 @@ struct MoeSim {
   uint32_t ev_route_w = 0;
   Runs R, Kt, S, G1, G2, C;
 
-  void build(int T_, int E_, int k_, int H, int I, bool wide, uint64_t seed) {
+  void build(int T_, int E_, int k_, int H, int I, int var, uint64_t seed) {
     T = T_;
     E = E_;
     k = k_;
-    g = launch_graph(T, E, k, H, I, wide);
+    g = launch_graph(T, E, k, H, I, var);
+    const int bm = var == kVarBig ? kBigBM : kBM;
     uint64_t s = seed * 2654435761ull + 12345;
     auto r = [&]() {
       s ^= s << 13;
@@ -161,7 +162,7 @@ struct MoeSim {
         ids[(size_t)t * k + j] = e;
       }
     }
-    // stable grouping by expert, row tiles of at most 64 rows (kBM)
+    // stable grouping by expert, row tiles of at most bm rows (the variant's)
     std::vector<int> cnt(E, 0), iptr(E + 1, 0);
     for (int e : ids) ++cnt[e];
     for (int e = 0; e < E; ++e) iptr[e + 1] = iptr[e] + cnt[e];
@@ -177,8 +178,8 @@ struct MoeSim {
       }
     row_tile.assign((size_t)T * k, 0);
     for (int e = 0; e < E; ++e)
-      for (int m = 0; m * kBM < cnt[e]; ++m) {
-        const int r0 = iptr[e] + m * kBM, n = std::min(kBM, cnt[e] - m * kBM);
+      for (int m = 0; m * bm < cnt[e]; ++m) {
+        const int r0 = iptr[e] + m * bm, n = std::min(bm, cnt[e] - m * bm);
         for (int q = 0; q < n; ++q) row_tile[r0 + q] = (int)tile_r0.size();
         tile_r0.push_back(r0);
         tile_n.push_back(n);
@@ -385,8 +386,8 @@ int moe_main(int argc, char** argv) {
             I = std::atoi(argv[6]), G = std::atoi(argv[7]);
   const uint64_t seed = std::strtoull(argv[8], nullptr, 10);
   parse_opts(9, argc, argv);
-  const bool wide = wide_variant(T, k, H, I) && !opt.narrow;
-  sim.build(T, E, k, H, I, wide, seed);
+  const int var = opt.narrow ? kVarSmall : launch_variant_of(T, k, H, I);
+  sim.build(T, E, k, H, I, var, seed);
   const int64_t rows = (int64_t)T * k;
   const int64_t max_rt = (rows + kBM - 1) / kBM + (rows < E ? rows : E);
   Queue q{};
@@ -415,10 +416,10 @@ int moe_main(int argc, char** argv) {
   const uint32_t st = ctl[96];
   const bool all = sim.R.all_once() && sim.Kt.all_once() && sim.S.all_once() && sim.G1.all_once() &&
                    sim.G2.all_once() && sim.C.all_once();
-  std::printf("{\"T\": %d, \"E\": %d, \"k\": %d, \"G\": %d, \"wide\": %d, \"nrt\": %d, \"total\": %u, "
+  std::printf("{\"T\": %d, \"E\": %d, \"k\": %d, \"G\": %d, \"variant\": %d, \"nrt\": %d, \"total\": %u, "
               "\"published_total\": %u, \"tail\": %u, \"head\": %u, \"cap\": %lld, \"status\": %u, "
               "\"violations\": %d, \"runs\": [%d, %d, %d, %d, %d, %d], \"all_once\": %d}\n",
-              T, E, k, G, (int)wide, sim.nrt, total, ctl[64], ctl[32], ctl[0], (long long)cap, st,
+              T, E, k, G, var, sim.nrt, total, ctl[64], ctl[32], ctl[0], (long long)cap, st,
               g_violations.load(), sim.R.count(), sim.Kt.count(), sim.S.count(), sim.G1.count(), sim.G2.count(),
               sim.C.count(), (int)all);
   const bool ok = all && st == 0 && g_violations.load() == 0 && ctl[64] == total && ctl[32] + sim.g.nR == total;

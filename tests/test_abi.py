@@ -84,12 +84,16 @@ def test_workspace_size_and_descriptor_limits():
     for bad in [B.moe_desc(0, 2048, 128, 8, 768), B.moe_desc(16, 2000, 128, 8, 768),
                 B.moe_desc(16, 2048, 128, 8, 700), B.moe_desc(16, 2048, 300, 8, 768),
                 B.moe_desc(16, 2048, 4, 8, 768), B.moe_desc(16, 2048, 128, 17, 768),
-                B.moe_desc(16385, 2048, 128, 8, 768), B.moe_desc(16384, 16384, 128, 16, 768)]:
+                B.moe_desc(16385, 2048, 128, 8, 768), B.moe_desc(16384, 16384, 128, 16, 768),
+                B.moe_desc(16, 41088, 128, 8, 768), B.moe_desc(16, 2048, 128, 8, 41088)]:
         assert B.moe_layer_workspace_size(bad) == 0
         assert B.etc_last_error() != ""
     # the scan walks tokens in chunks, so the largest token count is limited
     # only by T_max <= 16384 and the 2 GiB row-buffer bound
     assert B.moe_layer_workspace_size(B.moe_desc(16384, 2048, 128, 8, 768)) > 0
+    # the dense MLPs of the pages' appendix table: H, I up to 40960
+    assert B.moe_layer_workspace_size(B.moe_desc(8192, 4608, 1, 1, 36864)) > 0
+    assert B.moe_layer_workspace_size(B.moe_desc(8, 40960, 8, 2, 40960)) > 0
 
 
 @needs_lib

@@ -56,6 +56,8 @@ MOE_CASES = [
     (2048, 128, 8, 2048, 768, 64, 5, ["--body-us", "2", "--narrow"]),  # small-batch variant at T = 2048
     (37, 8, 8, 128, 256, 16, 6, []),                       # k == E
     (700, 16, 4, 128, 128, 32, 7, ["--body-us", "5"]),     # ragged combine and router tiles
+    (4096, 128, 8, 2048, 768, 64, 5, ["--body-us", "1"]),  # big-tile variant: a row tile releases up to 256 rows' combines
+    (8192, 1, 1, 4096, 12288, 32, 1, ["--body-us", "1"]),  # one expert (dense MLP): 32 row tiles of 96 + 16 G tasks
 ]
 
 

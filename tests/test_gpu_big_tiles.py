@@ -1,0 +1,81 @@
+"""GPU parity of the big-tile kernel variant (launches with T * k >= 8192 and
+H, I multiples of 256 and 128): row tiles of up to 256 grouped rows, G1 tiles
+of 128 gate + 128 up columns, G2 tiles of 256 output columns, K staged in LDS
+by direct-to-LDS loads, bf16 MFMA 32x32x16.
+
+The bar is the one of every MoE parity test: routing bit-exact, the layer
+output within 2e-2 row-wise relative error of the oracle.  The shapes reach
+ragged row tiles (an expert's last tile of a few rows, tiles of fewer than
+128 rows so that half the waves multiply nothing), several full tiles per
+expert, one expert (the dense MLP), and the dense MLPs of the pages'
+appendix table of MLP configurations at their own sizes (sampled rows)."""
+import numpy as np
+import pytest
+
+import oracle
+from dynamic_moe_task_amd import workloads as wl
+from gpu_util import DeviceLayer, announce, assert_routing_equal, assert_rows_close
+
+pytestmark = pytest.mark.gpu
+
+SCHEDS = ["static", "kbk", "barrier", "ordered"]
+
+BIG = [
+    # (T, H, E, k, I, norm, bias, T_max)
+    (1100, 256, 16, 8, 256, True, False, 1100),   # ~550 rows an expert: tiles of 256, 256 and a ragged rest
+    (2048, 512, 8, 4, 512, True, False, 2048),    # ~1024 rows an expert: four full tiles each
+    (1030, 256, 64, 8, 384, True, True, 1100),    # ~129 rows an expert: second wave row nearly idle; bias
+    (8192, 256, 1, 1, 256, True, False, 8192),    # one expert: 32 full tiles (the dense MLP)
+    (4100, 256, 2, 2, 128, True, False, 4100),    # every token to both experts: 16 full tiles and one of 4 rows
+    (1024, 768, 128, 8, 256, False, False, 1024), # 64 rows an expert, plain softmax weights, 3 G2 tiles
+]
+
+_CACHE = {}
+
+
+def _inputs(case):
+    if case not in _CACHE:
+        T, H, E, k, I, norm, has_bias, T_max = case
+        rng = np.random.default_rng(T * 31 + E)
+        Wr = wl.to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.05))
+        W13 = wl.to_bf16_bits(rng.standard_normal((E, 2 * I, H), dtype=np.float32) * np.float32(0.05))
+        Wd = wl.to_bf16_bits(rng.standard_normal((E, H, I), dtype=np.float32) * np.float32(0.05))
+        X = wl.to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+        bias = (rng.standard_normal(E) * 0.5).astype(np.float32) if has_bias else None
+        ref = oracle.moe(X, Wr, W13, Wd, k=k, norm_topk=norm, bias=bias)
+        _CACHE[case] = (Wr, W13, Wd, X, bias, ref)
+    return _CACHE[case]
+
+
+@pytest.mark.parametrize("case", BIG, ids=[f"T{c[0]}H{c[1]}E{c[2]}k{c[3]}I{c[4]}" for c in BIG])
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_big_tile_shapes_full_parity(case, sched):
+    T, H, E, k, I, norm, has_bias, T_max = case
+    assert T * k >= 8192 and H % 256 == 0 and I % 128 == 0  # the big-tile variant runs
+    Wr, W13, Wd, X, bias, ref = _inputs(case)
+    announce(f"big tiles {case} sched={sched}")
+    layer = DeviceLayer((H, E, k, I), Wr, W13, Wd, T_max=T_max, bias=bias, norm_topk=norm)
+    got = layer.run(X, sched)
+    assert_routing_equal(got, ref)
+    assert_rows_close(got["out"], ref["out"])
+
+
+@pytest.mark.parametrize("mlp", range(len(wl.MLP_TABLE)), ids=[s.name.split()[0] for s in wl.MLP_TABLE])
+def test_dense_mlp_table_sampled_rows(mlp):
+    # S = 8192 tokens through one expert: every output row is the dense
+    # SwiGLU MLP of its token; 64 sampled rows (first, last, random) against
+    # the oracle, ORDERED and kernel by kernel
+    s = wl.MLP_TABLE[mlp]
+    w = wl.make_weights(s, 0)
+    X = wl.make_tokens(s, s.T, 0)
+    layer = DeviceLayer((s.H, s.E, s.k, s.I), w.Wr, w.W13, w.Wd, T_max=s.T)
+    rng = np.random.default_rng(mlp)
+    tok = np.unique(np.concatenate([[0, s.T - 1], rng.integers(0, s.T, 62)])).astype(np.int32)
+    ref = oracle.route(X, w.Wr, s.k)
+    assert np.all(ref["topk_ids"] == 0) and np.all(ref["topk_w"] == 1.0)
+    rows = oracle.moe_tokens(tok, X, w.W13, w.Wd, ref["topk_ids"], ref["topk_w"])
+    for sched in ("ordered", "kbk"):
+        announce(f"dense {s.name} sched={sched}")
+        got = layer.run(X, sched)
+        assert_routing_equal(got, ref)
+        assert_rows_close(got["out"][tok], rows)

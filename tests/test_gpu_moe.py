@@ -259,8 +259,10 @@ EDGE = [
     (4096, 128, 64, 8, 128, True, False, 4096),  # T == T_max == 4096: eight scan chunks
     (700, 128, 16, 4, 128, True, True, 800),   # two scan chunks, the second ragged
     (16384, 128, 8, 2, 128, True, False, 16384),  # largest T_max: 32 scan chunks, 8 experts
-    (8, 16384, 8, 2, 128, True, False, 8),     # largest hidden size
-    (8, 128, 8, 2, 16384, True, False, 8),     # largest expert intermediate size
+    (8, 16384, 8, 2, 128, True, False, 8),     # hidden size 16384
+    (8, 128, 8, 2, 16384, True, False, 8),     # expert intermediate size 16384
+    (8, 40960, 8, 2, 128, True, False, 8),     # largest hidden size
+    (2, 256, 1, 1, 40960, True, False, 2),     # one expert of the largest intermediate size
     (512, 128, 16, 8, 128, True, False, 512),  # T * k = 4096: the largest batch with the routing tables in LDS
     (300, 128, 32, 14, 128, True, False, 320), # T * k = 4200: one scan chunk, routing tables in memory
     (12, 128, 64, 8, 256, True, False, 16),    # between one and two G tiles per workgroup of the grid
