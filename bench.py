@@ -39,9 +39,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill_zipf", "tiny", "decoder", "tokens"],
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill_zipf", "tiny", "decoder", "tokens", "mlp"],
                     help="decoder: only the decoder-layer section; tokens: only the token-count table at "
-                         "--counts (diagnostics and profiling)")
+                         "--counts; mlp: only the dense-MLP table (diagnostics and profiling)")
+    ap.add_argument("--mlps", default="", help="indices into the dense-MLP table for --workload mlp (default all)")
     ap.add_argument("--counts", default="1,128,1024,4096", help="token counts of --workload tokens")
     ap.add_argument("--tokens", type=int, default=0,
                     help="run the workload's layer at this many tokens instead of its own T (diagnostics, "
@@ -402,6 +404,64 @@ def measure_token_counts(Wr, w13s, w2s, sp, steps, warmup, repeat, counts=(1, 12
     return out
 
 
+def measure_dense_mlps(sp, steps, warmup, repeat, which=None):
+    """The dense MLPs of the pages' appendix table (S = 8192 tokens) run
+    through the MoE path as one expert (E = 1, k = 1): the big-tile grouped
+    GEMM with full 256-row tiles.  µs per layer (ORDERED and kernel by
+    kernel), TFLOP/s and the fraction of the 2.5 PF bf16 MFMA peak.  For
+    context (not the product path): the layer's two GEMMs alone through
+    torch.matmul (hipBLASLt), without routing, SwiGLU or combine."""
+    import torch
+    from dynamic_moe_task_amd import binding as B
+    from dynamic_moe_task_amd import workloads as wl
+    out = {}
+    for i, shape in enumerate(wl.MLP_TABLE):
+        if which is not None and i not in which:
+            continue
+        w = wl.make_weights(shape, 0)
+        W13, Wd = dev_bf16(w.W13), dev_bf16(w.Wd)
+        X = wl.make_tokens(shape, shape.T, 0)
+        desc = B.moe_desc(shape.T, shape.H, shape.E, shape.k, shape.I, True, False)
+        bufs = B.MoELayerBuffers.allocate(desc, dev_bf16(w.Wr), W13, Wd, None)
+        bufs.x[:shape.T].copy_(dev_bf16(X))
+        flops = wl.algorithmic_flops(shape, shape.T)
+        row = {"S": shape.T, "H": shape.H, "I": shape.I, "gflop": round(flops / 1e9, 1), "us_per_layer": {}}
+        for sched in ("ordered", "kbk"):
+            us = float(np.median([time_sched(bufs, shape.T, sched, steps, warmup, [W13], [Wd], sp)
+                                  for _ in range(repeat)]))
+            row["us_per_layer"][sched] = round(us, 1)
+        best = min(row["us_per_layer"].values())
+        row["tflops"] = round(flops / (best * 1e-6) / 1e12, 1)
+        row["mfma_frac"] = round(flops / (best * 1e-6) / (BF16_PEAK_TFS * 1e12), 4)
+        # hipBLASLt reference: x W13^T (2I columns) and h Wd^T, contiguous operands
+        xa = bufs.x[:shape.T]
+        w13t = W13[0].t().contiguous()
+        wdt = Wd[0].t().contiguous()
+        hm = torch.empty(shape.T, shape.I, dtype=torch.bfloat16, device="cuda")
+
+        def gemms():
+            torch.matmul(xa, w13t)
+            torch.matmul(hm, wdt)
+
+        for _ in range(warmup):
+            gemms()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            gemms()
+        e1.record()
+        torch.cuda.synchronize()
+        lib_us = e0.elapsed_time(e1) * 1e3 / steps
+        row["hipblaslt_two_gemms_us"] = round(lib_us, 1)
+        row["hipblaslt_mfma_frac"] = round(6.0 * shape.T * shape.H * shape.I / (lib_us * 1e-6) / (BF16_PEAK_TFS * 1e12), 4)
+        out[shape.name.split()[0]] = row
+        del bufs, W13, Wd, w13t, wdt, hm
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_decoder(Wr, w13s, w2s, sp, steps, warmup, repeat, scheds=("static", "ordered", "kbk")):
     """The decoder layer around the MoE layer as one persistent kernel
     (batch 8, 32 query / 4 kv heads of 128, 4096 cached entries per
@@ -468,6 +528,12 @@ def main():
     from dynamic_moe_task_amd import binding as B
     from dynamic_moe_task_amd import workloads as wl
 
+    if a.workload == "mlp":
+        torch.cuda.set_device(0)
+        sp = torch.cuda.current_stream().cuda_stream
+        which = {int(v) for v in a.mlps.split(",")} if a.mlps else None
+        print(json.dumps(measure_dense_mlps(sp, a.steps, a.warmup, a.repeat, which)), flush=True)
+        return
     if a.workload in ("decoder", "tokens"):
         import torch
         torch.cuda.set_device(0)
@@ -565,6 +631,7 @@ def main():
         extra["sweep"] = measure_sweep(Wr, w13s, w2s, sp, a.sweep_steps, a.sched)
         extra["token_counts"] = measure_token_counts(Wr, w13s, w2s, sp, max(10, a.steps // 2), a.warmup, a.repeat)
         extra["decoder_layer"] = measure_decoder(Wr, w13s, w2s, sp, max(10, a.steps // 2), a.warmup, a.repeat)
+        extra["dense_mlp"] = measure_dense_mlps(sp, 5, 2, 1)
 
     cpu = None
     if not a.no_cpu:
