@@ -21,10 +21,10 @@
 // writes 1 KB of LDS, eight rows, and each lane fetches the chunk that the
 // swizzle puts at its position.  Stage kc + 2 is requested as soon as stage
 // kc has been read, and the operand registers of the next k16 step are read
-// while the current step's MFMAs run.  Weight rows are read once per task,
-// A rows once per task and once per stage of 64 k; rows past the tile's
-// count are neither loaded (whole load instructions are skipped) nor
-// multiplied (whole 32-row blocks are skipped), and never stored.
+// while the current step's MFMAs run.  Weight rows and A rows are read once
+// per task.  Rows past the tile's count are neither read from LDS nor
+// multiplied (the K loop is specialised on each wave's count of live 32-row
+// blocks) nor stored; their loads repeat row 0.
 #pragma once
 // (included inside namespace etc)
 
@@ -38,6 +38,10 @@ constexpr int kBigLoads = 16;              // direct-to-LDS loads per wave per s
 static_assert(2 * kBigStage == kBigLdsBytes, "two stages fill the big variant's LDS");
 
 __device__ __forceinline__ int big_sw(int row, int chunk) { return (chunk ^ ((row >> 1) & 7)) << 4; }
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
 
 template <bool G1>
 __device__ __forceinline__ void big_body(const MoeParams& p, const Ctx& c, const RowTile tile, int nt, uint8_t* lds) {
@@ -54,8 +58,7 @@ __device__ __forceinline__ void big_body(const MoeParams& p, const Ctx& c, const
   // and 3 the 256 weight rows.  A wave's sources share one base (x, Hmid, or
   // the expert's weights); each lane keeps 32-bit byte offsets from it (all
   // below 2 GiB, as the descriptor limits require).  Rows past the count
-  // read row 0 (any valid row); their loads are skipped where a whole
-  // instruction is past it.
+  // read row 0 (any valid row).
   const bool wave_a = wv < 2;
   const uint16_t* base_a = G1 ? p.x : p.hh;
   const uint16_t* base_b = G1 ? p.w13 + (size_t)tile.e * 2 * I * H : p.w2 + (size_t)tile.e * H * I;
@@ -83,17 +86,21 @@ __device__ __forceinline__ void big_body(const MoeParams& p, const Ctx& c, const
     off[j] = (elem + (uint32_t)chunk * 8u) * 2u;
   }
   const int nk = K / kBigBK;
+  // Every wave issues all its loads (rows past the count repeat row 0), so
+  // that the loop holds no branch: a branch around loads or MFMAs ends the
+  // compiler's overlap of the LDS reads with the MFMAs.
   auto issue = [&](int kc) {
     uint8_t* base = lds + (kc & 1) * kBigStage + wv * kBigLoads * 1024;
     const uint8_t* g = reinterpret_cast<const uint8_t*>(gbase) + (size_t)kc * (kBigBK * 2);
-#pragma unroll
-    for (int j = 0; j < kBigLoads; ++j) {
-      if (wave_a && (wv * kBigLoads + j) * 8 >= nrows) continue;  // uniform: all eight rows past the count
+    if (!G1 && wave_a) {
       // Hmid rows (G2's A) are written during the launch: device-coherent
       // loads; x and the weights are not
-      if (!G1 && wave_a)
+#pragma unroll
+      for (int j = 0; j < kBigLoads; ++j)
         __builtin_amdgcn_global_load_lds((const void*)(g + off[j]), (lds_ptr_t)(base + j * 1024), 16, 0, kCoherent);
-      else
+    } else {
+#pragma unroll
+      for (int j = 0; j < kBigLoads; ++j)
         __builtin_amdgcn_global_load_lds((const void*)(g + off[j]), (lds_ptr_t)(base + j * 1024), 16, 0, 0);
     }
   };
@@ -111,16 +118,6 @@ __device__ __forceinline__ void big_body(const MoeParams& p, const Ctx& c, const
     const int r = G1 ? (n < 2 ? wc * 64 + 32 * n : 128 + wc * 64 + 32 * (n - 2)) : wc * 128 + 32 * n;
     brow[n] = 256 + r + l32;
   }
-  u32x4_t fa[2][4], fb[2][4];
-  auto read = [&](int kc, int s, u32x4_t (&a)[4], u32x4_t (&b4)[4]) {
-    const uint8_t* base = lds + (kc & 1) * kBigStage;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      a[b] = *reinterpret_cast<const u32x4_t*>(base + arow[b] * kBigRowB + big_sw(arow[b], 2 * s + kh));
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-      b4[n] = *reinterpret_cast<const u32x4_t*>(base + brow[n] * kBigRowB + big_sw(brow[n], 2 * s + kh));
-  };
   f32x16_t acc[4][4];
 #pragma unroll
   for (int b = 0; b < 4; ++b)
@@ -128,36 +125,58 @@ __device__ __forceinline__ void big_body(const MoeParams& p, const Ctx& c, const
     for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[b][n][q] = 0.f;
-  auto mma = [&](const u32x4_t (&a)[4], const u32x4_t (&b4)[4]) {
+  // The K loop, specialised on the wave's live 32-row blocks (NL: 4 to 0),
+  // so that no per-block test sits in it; dead blocks are neither read nor
+  // multiplied.
+  auto kloop = [&](auto nl_tag) {
+    constexpr int NL = decltype(nl_tag)::value;
+    u32x4_t fa[2][4], fb[2][4];
+    auto read = [&](int kc, int s, u32x4_t (&a)[4], u32x4_t (&b4)[4]) {
+      const uint8_t* base = lds + (kc & 1) * kBigStage;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (!live[b]) continue;
+      for (int b = 0; b < NL; ++b)
+        a[b] = *reinterpret_cast<const u32x4_t*>(base + arow[b] * kBigRowB + big_sw(arow[b], 2 * s + kh));
 #pragma unroll
       for (int n = 0; n < 4; ++n)
-        acc[b][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(a[b]), as_bf(b4[n]), acc[b][n], 0, 0, 0);
+        b4[n] = *reinterpret_cast<const u32x4_t*>(base + brow[n] * kBigRowB + big_sw(brow[n], 2 * s + kh));
+    };
+    auto mma = [&](const u32x4_t (&a)[4], const u32x4_t (&b4)[4]) {
+#pragma unroll
+      for (int b = 0; b < NL; ++b)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          acc[b][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(a[b]), as_bf(b4[n]), acc[b][n], 0, 0, 0);
+    };
+    issue(0);
+    if (nk > 1) issue(1);
+    __builtin_amdgcn_s_waitcnt(0);  // stage 0 (and 1) landed, as have the row lookups
+    __syncthreads();
+    if (NL > 0) read(0, 0, fa[0], fb[0]);
+    for (int kc = 0; kc < nk; ++kc) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s < 3) {
+          if (NL > 0) read(kc, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+        } else if (kc + 1 < nk) {
+          // stage kc + 1 is the only one in flight: wait for it, then every
+          // wave has read stage kc (the barrier waits for LDS reads), so its
+          // buffer takes stage kc + 2
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+          __syncthreads();
+          if (kc + 2 < nk) issue(kc + 2);
+          if (NL > 0) read(kc + 1, 0, fa[0], fb[0]);
+        }
+        if (NL > 0) mma(fa[s & 1], fb[s & 1]);
+      }
     }
   };
-  issue(0);
-  if (nk > 1) issue(1);
-  __builtin_amdgcn_s_waitcnt(0);  // stage 0 (and 1) landed, as have the row lookups
-  __syncthreads();
-  read(0, 0, fa[0], fb[0]);
-  for (int kc = 0; kc < nk; ++kc) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) {
-        read(kc, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-      } else if (kc + 1 < nk) {
-        // stage kc + 1 is the only one in flight: wait for it, then every
-        // wave has read stage kc (the barrier waits for LDS reads), so its
-        // buffer takes stage kc + 2
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        __syncthreads();
-        if (kc + 2 < nk) issue(kc + 2);
-        read(kc + 1, 0, fa[0], fb[0]);
-      }
-      mma(fa[s & 1], fb[s & 1]);
-    }
+  const int nlive = min(4, max(0, (nrows - 128 * wr + 31) / 32));  // uniform per wave
+  switch (nlive) {
+    case 4: kloop(IntC<4>{}); break;
+    case 3: kloop(IntC<3>{}); break;
+    case 2: kloop(IntC<2>{}); break;
+    case 1: kloop(IntC<1>{}); break;
+    default: kloop(IntC<0>{}); break;
   }
   __syncthreads();  // the stages are free for the output
   // output through LDS, one half of the rows (the waves of one row) at a

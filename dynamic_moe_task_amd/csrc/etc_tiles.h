@@ -57,4 +57,37 @@ ETC_HD bool big_variant(int T, int k, int H, int I) {
 // kernel variants: small batches, large batches (column-split tiles), big tiles
 enum : int { kVarSmall = 0, kVarWide = 1, kVarBig = 2 };
 
+// Order of the big-tile variant's G tasks.  Task i of the R x C tiles of G1
+// (or of G2) is taken by workgroup group i % 8 (the grid deals consecutive
+// workgroups, and claims, over the 8 XCDs, each with its own L2).  Two
+// steps make the tiles an XCD runs at once share operands in its L2:
+//  - dealing in chunks: the k-th task of group g is the (k % W)-th of chunk
+//    (k / W) * 8 + g, so an XCD's W concurrent tasks are W consecutive
+//    entries of the order below (positions past the last full round of 8
+//    chunks keep their own index);
+//  - grouped order: tiles come in groups of kBigGR row tiles, column-major
+//    within a group, so W consecutive entries span kBigGR row tiles (their A
+//    rows) and W / kBigGR column tiles (their weight rows).
+// A bijection of [0, R * C) onto the tiles.
+constexpr int kBigGR = 4;   // row tiles per group
+constexpr int kBigW = 32;   // tasks an XCD runs at once (one workgroup per CU)
+struct TileRC {
+  int rt, nt;
+};
+ETC_HD TileRC big_task(int i, int R, int C) {
+  const int n = R * C;
+  const int full = (n / (8 * kBigW)) * (8 * kBigW);
+  int t = i;
+  if (i < full) {
+    const int k = i >> 3, g = i & 7;
+    t = ((k / kBigW) * 8 + g) * kBigW + k % kBigW;
+  }
+  const int grp = t / (kBigGR * C), w = t % (kBigGR * C);
+  const int gsz = R - grp * kBigGR < kBigGR ? R - grp * kBigGR : kBigGR;
+  TileRC r;
+  r.rt = grp * kBigGR + w % gsz;
+  r.nt = w / gsz;
+  return r;
+}
+
 }  // namespace etc

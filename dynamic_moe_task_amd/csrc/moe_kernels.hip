@@ -1414,6 +1414,21 @@ __device__ __forceinline__ bool wait_rows_done(const MoeParams& p, const Ctx& c,
   return fail == 0;
 }
 
+// Row tile and column tile of G task i (of nrt row tiles x nn column tiles):
+// row-major, except in the big-tile variant, whose tasks follow big_task's
+// L2-friendly order.
+template <int WG>
+__device__ __forceinline__ TileRC g_tile(int i, int nrt, int nn) {
+  if constexpr (WG == kVarBig) {
+    return big_task(i, nrt, nn);
+  } else {
+    TileRC t;
+    t.rt = i / nn;
+    t.nt = i % nn;
+    return t;
+  }
+}
+
 template <int WG>
 __device__ __forceinline__ void run_g1_static(const MoeParams& p, const Ctx& c, float* red, int i0, int n, int G,
                               const LocalRoute* lr) {
@@ -1421,9 +1436,10 @@ __device__ __forceinline__ void run_g1_static(const MoeParams& p, const Ctx& c, 
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
   const rsrc_t rcnt = r_counts(p);
-  RowTile cur = get_tile(p, lr, i0 / c.nN1);
+  const int nrt = n / c.nN1;
+  RowTile cur = get_tile(p, lr, g_tile<WG>(i0, nrt, c.nN1).rt);
   RowTile nxt = cur;
-  if (i0 + G < n) nxt = get_tile(p, lr, (i0 + G) / c.nN1);
+  if (i0 + G < n) nxt = get_tile(p, lr, g_tile<WG>(i0 + G, nrt, c.nN1).rt);
   uint32_t cur_tgt = 0, cur_arr = 0;
   if (threadIdx.x == 0) {
     cur_tgt = (lr ? (uint32_t)lr->cnt[cur.e] : co_ld32(rcnt, (uint32_t)cur.e * 4u));
@@ -1442,12 +1458,13 @@ __device__ __forceinline__ void run_g1_static(const MoeParams& p, const Ctx& c, 
   // task, the previous notify's round trip included.
   __builtin_amdgcn_s_waitcnt(0);
   for (int i = i0; i < n; i += G) {
-    const int rt = i / c.nN1, nt = i % c.nN1;
+    const TileRC tt = g_tile<WG>(i, nrt, c.nN1);
+    const int rt = tt.rt, nt = tt.nt;
     if (tr) tw = now_ticks();
     if (!wait_known(ev_exp(p, c, cur.e), cur_tgt, cur_arr, c)) return;
     if (tr) ts = now_ticks();
     RowTile nn = nxt;
-    if (i + 2 * G < n) nn = get_tile(p, lr, (i + 2 * G) / c.nN1);
+    if (i + 2 * G < n) nn = get_tile(p, lr, g_tile<WG>(i + 2 * G, nrt, c.nN1).rt);
     uint32_t nxt_tgt = 0, nxt_arr = 0;
     if (threadIdx.x == 0 && i + G < n) {
       nxt_tgt = (lr ? (uint32_t)lr->cnt[nxt.e] : co_ld32(rcnt, (uint32_t)nxt.e * 4u));
@@ -1481,21 +1498,23 @@ __device__ __forceinline__ void run_g2_static(const MoeParams& p, const Ctx& c, 
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
   const uint32_t tgt = (uint32_t)c.nN1;
-  RowTile cur = get_tile(p, lr, i0 / c.nN2);
+  const int nrt = n / c.nN2;
+  RowTile cur = get_tile(p, lr, g_tile<WG>(i0, nrt, c.nN2).rt);
   RowTile nxt = cur;
-  if (i0 + G < n) nxt = get_tile(p, lr, (i0 + G) / c.nN2);
+  if (i0 + G < n) nxt = get_tile(p, lr, g_tile<WG>(i0 + G, nrt, c.nN2).rt);
   uint32_t cur_arr = 0;
-  if (threadIdx.x == 0) cur_arr = ld_relaxed(ev_h(p, c, i0 / c.nN2));
+  if (threadIdx.x == 0) cur_arr = ld_relaxed(ev_h(p, c, g_tile<WG>(i0, nrt, c.nN2).rt));
   __builtin_amdgcn_s_waitcnt(0);  // loop entry with nothing in flight (see run_g1_static)
   for (int i = i0; i < n; i += G) {
-    const int rt = i / c.nN2, nt = i % c.nN2;
+    const TileRC tt = g_tile<WG>(i, nrt, c.nN2);
+    const int rt = tt.rt, nt = tt.nt;
     if (tr) tw = now_ticks();
     if (!wait_known(ev_h(p, c, rt), tgt, cur_arr, c)) return;
     if (tr) ts = now_ticks();
     RowTile nn = nxt;
-    if (i + 2 * G < n) nn = get_tile(p, lr, (i + 2 * G) / c.nN2);
+    if (i + 2 * G < n) nn = get_tile(p, lr, g_tile<WG>(i + 2 * G, nrt, c.nN2).rt);
     uint32_t nxt_arr = 0;
-    if (threadIdx.x == 0 && i + G < n) nxt_arr = ld_relaxed(ev_h(p, c, (i + G) / c.nN2));
+    if (threadIdx.x == 0 && i + G < n) nxt_arr = ld_relaxed(ev_h(p, c, g_tile<WG>(i + G, nrt, c.nN2).rt));
     // combine tile of each row's token (wave 0, one row a lane)
     task_g2<false, WG>(p, c, cur, rt, nt, red);
     __builtin_amdgcn_s_waitcnt(0);  // wave 0 wrote the rows: drain, then notify (as in G1)
@@ -1542,12 +1561,14 @@ __device__ __forceinline__ int claimed_task(const ClaimQ& q, uint32_t k) {
 struct GTask {
   int g2, rt, nt;
 };
+template <int WG>
 __device__ __forceinline__ GTask gtask(const Ctx& c, int i, int nG1) {
   GTask t;
   t.g2 = i >= nG1;
   const int j = t.g2 ? i - nG1 : i, nn = t.g2 ? c.nN2 : c.nN1;
-  t.rt = j / nn;
-  t.nt = j % nn;
+  const TileRC r = g_tile<WG>(j, nG1 / c.nN1, nn);
+  t.rt = r.rt;
+  t.nt = r.nt;
   return t;
 }
 
@@ -1575,11 +1596,11 @@ __device__ __forceinline__ bool run_g_ordered(const MoeParams& p, const Ctx& c, 
     if (t.g2) return (uint32_t)c.nN1;
     return lr ? (uint32_t)lr->cnt[r.e] : co_ld32(rcnt, (uint32_t)r.e * 4u);
   };
-  GTask tc = gtask(c, cur, nG1), tn = tc;
+  GTask tc = gtask<WG>(c, cur, nG1), tn = tc;
   RowTile rc = get_tile(p, lr, tc.rt);
   RowTile rn = rc;
   if (nxt < n) {
-    tn = gtask(c, nxt, nG1);
+    tn = gtask<WG>(c, nxt, nG1);
     rn = get_tile(p, lr, tn.rt);
   }
   uint32_t cur_tgt = 0, cur_arr = 0;
@@ -1602,7 +1623,7 @@ __device__ __forceinline__ bool run_g_ordered(const MoeParams& p, const Ctx& c, 
     GTask ta = tn;
     RowTile ra = rn;
     if (aft < n) {
-      ta = gtask(c, aft, nG1);
+      ta = gtask<WG>(c, aft, nG1);
       ra = get_tile(p, lr, ta.rt);
     }
     uint32_t nxt_tgt = 0, nxt_arr = 0;
@@ -1681,7 +1702,7 @@ __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ct
   auto tgt_of = [&](const GTask& t, const RowTile& r) -> uint32_t {
     return t.g2 ? (uint32_t)c.nN1 : (uint32_t)lr->cnt[r.e];
   };
-  GTask tc = gtask(c, cur, nG1);
+  GTask tc = gtask<WG>(c, cur, nG1);
   RowTile rc = get_tile(p, lr, tc.rt);
   uint32_t cur_tgt = 0, cur_arr = 0;
   if (threadIdx.x == 0) {
@@ -1709,7 +1730,7 @@ __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ct
     uint32_t nxt_tgt = 0, nxt_arr = 0;
     uint32_t nxt_f[4] = {0u, 0u, 0u, 0u};
     if (nxt < n) {
-      tn = gtask(c, nxt, nG1);
+      tn = gtask<WG>(c, nxt, nG1);
       rn = get_tile(p, lr, tn.rt);
       if (threadIdx.x == 0) {
         nxt_tgt = tgt_of(tn, rn);
@@ -1752,7 +1773,7 @@ __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ct
     } else if (got < n) {
       // none was held: the tile claimed during this one runs next; its
       // event state is polled by the wait (a G1 tile's is known released)
-      tc = gtask(c, got, nG1);
+      tc = gtask<WG>(c, got, nG1);
       rc = get_tile(p, lr, tc.rt);
       if (threadIdx.x == 0) {
         cur_tgt = tgt_of(tc, rc);
@@ -1880,13 +1901,14 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
     // LDS writes (A staging, partial sums) behind the previous task's last
     // LDS reads (wave 0 reads the output stage while it stores the tile)
     for (int i = first_of(w, off, Gt); i < nG1; i += Gt) {
-      const int rt = i / c.nN1;
+      const TileRC tt = g_tile<WG>(i, nrt, c.nN1);
+      const int rt = tt.rt;
       if (i >= Gt) lds_barrier();
       if (tr) tw = ts = now_ticks();
-      task_g1<false, WG>(p, c, load_rowtile(p, rt), rt, i % c.nN1, red);
+      task_g1<false, WG>(p, c, load_rowtile(p, rt), rt, tt.nt, red);
       if (tr) tb = now_ticks();
       dbg_task(p, TT_G1);
-      trace_task(p, TT_G1, rt, i % c.nN1, tw, ts, tb);
+      trace_task(p, TT_G1, rt, tt.nt, tw, ts, tb);
     }
   }
   off += nG1;
@@ -1895,13 +1917,14 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
     run_g2_static<WG>(p, c, red, first_of(w, off, Gt), nG2, Gt, lr);
   } else {
     for (int i = first_of(w, off, Gt); i < nG2; i += Gt) {
-      const int rt = i / c.nN2;
+      const TileRC tt = g_tile<WG>(i, nrt, c.nN2);
+      const int rt = tt.rt;
       if (i >= Gt) lds_barrier();  // as in the G1 loop
       if (tr) tw = ts = now_ticks();
-      task_g2<false, WG>(p, c, load_rowtile(p, rt), rt, i % c.nN2, red);
+      task_g2<false, WG>(p, c, load_rowtile(p, rt), rt, tt.nt, red);
       if (tr) tb = now_ticks();
       dbg_task(p, TT_G2);
-      trace_task(p, TT_G2, rt, i % c.nN2, tw, ts, tb);
+      trace_task(p, TT_G2, rt, tt.nt, tw, ts, tb);
     }
   }
   off += nG2;
@@ -2091,16 +2114,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
   const Ctx c = make_ctx(p, nullptr);
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN1) return;
-  const int rt = blockIdx.x / c.nN1;
-  task_g1<true, kVarBig>(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN1, reinterpret_cast<float*>(smem));
+  const TileRC t = big_task(blockIdx.x, nrt, c.nN1);
+  task_g1<true, kVarBig>(p, c, load_rowtile(p, t.rt), t.rt, t.nt, reinterpret_cast<float*>(smem));
 }
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) kbk_g2_big(MoeParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
   const Ctx c = make_ctx(p, nullptr);
   const int nrt = (int)ld_relaxed(p.meta + M_NRT);
   if ((int)blockIdx.x >= nrt * c.nN2) return;
-  const int rt = blockIdx.x / c.nN2;
-  task_g2<true, kVarBig>(p, c, load_rowtile(p, rt), rt, blockIdx.x % c.nN2, reinterpret_cast<float*>(smem));
+  const TileRC t = big_task(blockIdx.x, nrt, c.nN2);
+  task_g2<true, kVarBig>(p, c, load_rowtile(p, t.rt), t.rt, t.nt, reinterpret_cast<float*>(smem));
 }
 __global__ void __launch_bounds__(kThreads) kbk_combine(MoeParams p) {
   __shared__ int pairs[2 * kCombineT * kMaxK];

@@ -470,7 +470,34 @@ int splitk_main(int argc, char** argv) {
 
 }  // namespace
 
+// big_task is a bijection of [0, R * C) onto the R x C tiles, and an XCD
+// group's first W tasks of a full round span kBigGR row tiles
+int tilemap_main() {
+  int bad = 0, checked = 0;
+  for (int R = 1; R <= 70; ++R)
+    for (int C = 1; C <= 40; ++C) {
+      std::vector<int> seen((size_t)R * C, 0);
+      for (int i = 0; i < R * C; ++i) {
+        const TileRC t = big_task(i, R, C);
+        if (t.rt < 0 || t.rt >= R || t.nt < 0 || t.nt >= C || seen[(size_t)t.rt * C + t.nt]++) ++bad;
+      }
+      ++checked;
+    }
+  for (const auto& rc : {std::pair<int, int>{32, 96}, {190, 6}, {194, 8}, {32, 16}, {32, 14}, {1000, 200}}) {
+    const int R = rc.first, C = rc.second;
+    std::vector<int> seen((size_t)R * C, 0);
+    for (int i = 0; i < R * C; ++i) {
+      const TileRC t = big_task(i, R, C);
+      if (t.rt < 0 || t.rt >= R || t.nt < 0 || t.nt >= C || seen[(size_t)t.rt * C + t.nt]++) ++bad;
+    }
+    ++checked;
+  }
+  std::printf("{\"checked\": %d, \"bad\": %d}\n", checked, bad);
+  return bad ? 1 : 0;
+}
+
 int main(int argc, char** argv) {
+  if (argc >= 2 && std::strcmp(argv[1], "tilemap") == 0) return tilemap_main();
   if (argc >= 2 && std::strcmp(argv[1], "moe") == 0) return moe_main(argc, argv);
   if (argc >= 2 && std::strcmp(argv[1], "splitk") == 0) return splitk_main(argc, argv);
   std::fprintf(stderr, "usage: dyn_harness moe T E k H I G seed [options] | splitk n nsplit G seed [options]\n");

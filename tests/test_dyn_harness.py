@@ -111,3 +111,13 @@ def test_workgroup_scratch_is_race_free_under_tsan(tmp_path):
                  ["splitk", 64, 4, 8, 0, "--launches", 2]):
         rc, out, err = _run(exe, args + ["--timeout-s", 100], timeout=200, env=env)
         assert rc == 0, f"{args}: rc={rc} {err[-3000:]}"
+
+
+@needs_gxx
+def test_big_tile_task_order_is_a_bijection(harness):
+    # the big-tile variant's G task order (grouped row tiles, chunks dealt
+    # over the XCD groups) runs every tile exactly once, for every grid of
+    # row and column tiles up to 70 x 40 and for the Qwen-shape and
+    # dense-MLP grids
+    rc, out, err = _run(harness, ["tilemap"])
+    assert rc == 0 and out[-1]["bad"] == 0, (out, err)
