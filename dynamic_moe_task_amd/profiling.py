@@ -4,6 +4,14 @@
         Markdown table of a `--kernel-trace --stats` run (calls, average and
         total duration per kernel).
 
+    python -m dynamic_moe_task_amd.profiling mfma COUNTER_CSV KERNEL_TRACE_CSV [--kernel REGEX]
+        Matrix-core use per kernel from one `--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
+        SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE` run: bf16
+        MFMA FLOPs (512 per MOP), their rate over the dispatch's duration
+        against the 2.5 PF peak, and the fraction of SIMD cycles the matrix
+        cores were busy (GRBM_GUI_ACTIVE summed over the 8 XCDs; 256 CUs of 4
+        SIMDs), with the shader clock that GRBM_GUI_ACTIVE implies.
+
     python -m dynamic_moe_task_amd.profiling traffic --key decode/static \\
         --kernel moe_persistent --fetch A.csv --write B.csv \\
         --copy-fetch C.csv --copy-write D.csv --copy-bytes N --copy-kernel neg \\
@@ -93,6 +101,42 @@ def traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, ke
             "copy_bytes": copy_bytes, "source_digest": kernel_source_digest()}
 
 
+def mfma_table(counter_csv, trace_csv, kernel_regex=".", xcds=8, cus=256, simds=4, peak_tfs=2500.0):
+    """Per kernel (median over its dispatches): duration, bf16 MFMA TFLOP/s
+    and fraction of peak, MFMA busy fraction of all SIMD cycles, clock."""
+    rx = re.compile(kernel_regex)
+    dur, names = {}, {}
+    for r in read_csv(trace_csv):
+        d = int(_col(r, "Dispatch_Id", "Correlation_Id"))
+        dur[d] = (int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) / 1e3
+        names[d] = _col(r, "Kernel_Name")
+    per = {}
+    for r in read_csv(counter_csv):
+        d = int(_col(r, "Dispatch_Id", "Correlation_Id"))
+        name = _col(r, "Kernel_Name")
+        if not rx.search(name):
+            continue
+        per.setdefault(d, {"name": name})
+        c = _col(r, "Counter_Name")
+        per[d][c] = per[d].get(c, 0.0) + float(_col(r, "Counter_Value"))
+    by_kernel = {}
+    for d, v in per.items():
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" not in v or d not in dur or v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] == 0:
+            continue
+        us = dur[d]
+        flops = v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+        cyc = v.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * cus * simds) if cyc else float("nan")
+        by_kernel.setdefault(v["name"], []).append((us, flops, flops / (us * 1e-6) / 1e12, busy, cyc / us / 1e3))
+    out = ["| kernel | dispatches | µs | bf16 GFLOP | TFLOP/s | of 2.5 PF | MFMA busy | clock GHz |",
+           "|---|---|---|---|---|---|---|---|"]
+    for name, rows in by_kernel.items():
+        med = lambda i: statistics.median(r[i] for r in rows)  # noqa: E731
+        out.append(f"| `{name[:70]}` | {len(rows)} | {med(0):.1f} | {med(1) / 1e9:.1f} | {med(2):.1f} | "
+                   f"{med(2) / peak_tfs:.3f} | {med(3):.3f} | {med(4):.2f} |")
+    return "\n".join(out)
+
+
 def stats_table(path, top=12):
     rows = read_csv(path)
     out = ["| kernel | calls | avg µs | min µs | max µs | total µs | % |", "|---|---|---|---|---|---|---|"]
@@ -111,6 +155,10 @@ def main(argv=None):
     s = sub.add_parser("stats")
     s.add_argument("csv")
     s.add_argument("--top", type=int, default=12)
+    m = sub.add_parser("mfma")
+    m.add_argument("counters")
+    m.add_argument("trace")
+    m.add_argument("--kernel", default=".")
     t = sub.add_parser("traffic")
     t.add_argument("--key", required=True)
     t.add_argument("--kernel", required=True)
@@ -124,6 +172,9 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.csv, a.top))
+        return 0
+    if a.cmd == "mfma":
+        print(mfma_table(a.counters, a.trace, a.kernel))
         return 0
     res = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes, a.kernel, a.copy_kernel)
     data = {}
