@@ -7,7 +7,7 @@
 //   QKV(c)      16 columns of h1 Wqkv^T; for query and key heads the 16
 //               columns are 8 rotary pairs (i, i + d/2), rotated at `pos`;
 //               queries go to qb, keys and values into the caches at `pos`
-//   ATT(t,g,ch) 512 cache entries of token t, kv head g: scores for the
+//   ATT(t,g,ch) 256 cache entries of token t, kv head g: scores for the
 //               group's query heads (bf16 MFMA), their maximum, the
 //               exponentials and the weighted value sum (fp32), stored as a
 //               partial (sum, maximum, normaliser)
@@ -174,12 +174,15 @@ __device__ __forceinline__ void task_qkv(const MoeParams& p, const Ctx& c, int c
   }
 }
 
-// ATT: cache entries k0 .. k0 + nk - 1 (k0 = ch * 512, all below pos) of
-// token t and kv head g, for the group's gq query heads.  Scores by bf16
+// ATT: cache entries k0 .. k0 + nk - 1 (k0 = ch * kDecChunk, all below pos)
+// of token t and kv head g, for the group's gq query heads.  Scores by bf16
 // MFMA (A = the heads' queries, 16 rows with gq used; B = 16 entries a
-// column block, wave w covering entries w*128 .. w*128+127); softmax
-// maximum and sums across the waves in LDS; the weighted value sum on the
-// VALU (wave w accumulates heads 2w and 2w+1, lane l dims 2l and 2l+1).
+// column block, wave w covering entries w*64 .. w*64+63); softmax maximum
+// and sums across the waves in LDS; the weighted value sum on the VALU.
+// Chunks of 256 entries give the grid two tasks a CU at the decoder
+// workload (8 tokens x 4 kv heads x 16 chunks), and each task issues all of
+// its key loads, then all of its value loads, at once: the task is a few
+// memory latencies long instead of one per batch.
 // The partial holds, per head, the unnormalised sum over the chunk, the
 // chunk's maximum score and the sum of exp(score - maximum).
 __device__ __forceinline__ void task_attn(const MoeParams& p, const Ctx& c, int t, int g, int ch, float* lds) {
@@ -200,36 +203,30 @@ __device__ __forceinline__ void task_attn(const MoeParams& p, const Ctx& c, int 
     qa[s] = m < gq ? co_ld128(rq, (uint32_t)((((size_t)t * p.nq + g * gq + m) * d + s * 32 + kg * 8) * 2)) : zero;
   const size_t cbase = (((size_t)t * p.nkv + g) * p.Lcap + k0) * d;
   const uint16_t* kb = p.kc + cbase;
-  f32x4_t sc[8];
-  // two column blocks a batch; the next batch's keys load while this one multiplies
-  u32x4_t b[2][2][4];
-  auto load_k = [&](int nb, u32x4_t (&bb)[2][4]) {
+  // every key block of the wave in flight at once: one memory latency
+  constexpr int NBW = kDecChunk / 64;  // 16-entry column blocks a wave
+  constexpr int EPW = kDecChunk / 4;   // entries a wave
+  f32x4_t sc[NBW];
+  u32x4_t b[NBW][4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = wv * 128 + (nb + u) * 16 + m;
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int e = wv * EPW + nb * 16 + m;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) bb[u][s] = e < nk ? ld4(kb + (size_t)e * d + s * 32 + kg * 8) : zero;
-    }
-  };
-  load_k(0, b[0]);
-#pragma unroll
-  for (int nb = 0; nb < 8; nb += 2) {
-    if (nb + 2 < 8) load_k(nb + 2, b[((nb >> 1) + 1) & 1]);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(qa[s]), as_bf(b[(nb >> 1) & 1][u][s]), acc, 0, 0, 0);
-      sc[nb + u] = acc;
-    }
+    for (int s = 0; s < 4; ++s) b[nb][s] = e < nk ? ld4(kb + (size_t)e * d + s * 32 + kg * 8) : zero;
   }
-  // lane holds rows 4 kg + i (heads), entry wv*128 + nb*16 + m of every block
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(qa[s]), as_bf(b[nb][s]), acc, 0, 0, 0);
+    sc[nb] = acc;
+  }
+  // lane holds rows 4 kg + i (heads), entry wv*EPW + nb*16 + m of every block
   const float NEG_INF = -__builtin_inff();
   float mx[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const bool ok = wv * 128 + nb * 16 + m < nk;
+  for (int nb = 0; nb < NBW; ++nb) {
+    const bool ok = wv * EPW + nb * 16 + m < nk;
 #pragma unroll
     for (int i = 0; i < 4; ++i) mx[i] = ok ? fmaxf(mx[i], sc[nb][i] * scale) : mx[i];
   }
@@ -247,8 +244,8 @@ __device__ __forceinline__ void task_attn(const MoeParams& p, const Ctx& c, int 
 #pragma unroll
   for (int i = 0; i < 4; ++i) rm[i] = mrow[4 * kg + i];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const int e = wv * 128 + nb * 16 + m;
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int e = wv * EPW + nb * 16 + m;
     const bool ok = e < nk;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -268,10 +265,10 @@ __device__ __forceinline__ void task_attn(const MoeParams& p, const Ctx& c, int 
   if (tid < 16) mrow[16 + tid] = wred[tid] + wred[16 + tid] + wred[32 + tid] + wred[48 + tid];
   // Weighted value sum on the VALU.  Wave wv, lane (kq = lane / 32,
   // cg = lane % 32) takes entries e = 2 wv + kq + 8 i and dims 4 cg ..
-  // 4 cg + 3, for every head of the group; eight entries' values load while
-  // the previous eight multiply.  The 8 (wave, kq) partial sums are then
-  // added: across kq by a shuffle, across the waves in LDS (over P, which is
-  // no longer read by then).
+  // 4 cg + 3, for every head of the group; all of its values load at once
+  // (one memory latency).  The 8 (wave, kq) partial sums are then added:
+  // across kq by a shuffle, across the waves in LDS (over P, which is no
+  // longer read by then).
   typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
   const int kq = lane >> 5, cg = lane & 31;
   const int e0 = 2 * wv + kq;
@@ -282,40 +279,26 @@ __device__ __forceinline__ void task_attn(const MoeParams& p, const Ctx& c, int 
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[h][q] = 0.f;
   const u32x2_t zero2 = {0u, 0u};
-  auto load_v = [&](int i0, u32x2_t (&vb8)[8]) {
+  constexpr int NV = kDecChunk / 8;  // entries a thread takes
+  u32x2_t vv[NV];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + 8 * (i0 + u);
-      vb8[u] = e < nk ? *reinterpret_cast<const u32x2_t*>(vb + (size_t)e * d) : zero2;
-    }
-  };
-  auto consume = [&](int i0, const u32x2_t (&vb8)[8]) {
+  for (int u = 0; u < NV; ++u) {
+    const int e = e0 + 8 * u;
+    vv[u] = e < nk ? *reinterpret_cast<const u32x2_t*>(vb + (size_t)e * d) : zero2;
+  }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + 8 * (i0 + u);
-      if (e < nk) {
-        const float v[4] = {bf_lo(vb8[u].x), bf_hi(vb8[u].x), bf_lo(vb8[u].y), bf_hi(vb8[u].y)};
+  for (int u = 0; u < NV; ++u) {
+    const int e = e0 + 8 * u;
+    if (e < nk) {
+      const float v[4] = {bf_lo(vv[u].x), bf_hi(vv[u].x), bf_lo(vv[u].y), bf_hi(vv[u].y)};
 #pragma unroll
-        for (int h = 0; h < kDecMaxGroup; ++h) {
-          if (h < gq) {
-            const float pw = P[h * kDecChunk + e];
+      for (int h = 0; h < kDecMaxGroup; ++h) {
+        if (h < gq) {
+          const float pw = P[h * kDecChunk + e];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[h][q] = __builtin_fmaf(pw, v[q], acc[h][q]);
-          }
+          for (int q = 0; q < 4; ++q) acc[h][q] = __builtin_fmaf(pw, v[q], acc[h][q]);
         }
       }
-    }
-  };
-  const int nsteps = (nk - e0 + 7) / 8;  // entries this thread takes
-  // two buffers, named so that no register array is indexed at run time
-  u32x2_t va[8], vbuf[8];
-  load_v(0, va);
-  for (int i0 = 0; i0 < nsteps; i0 += 16) {
-    if (i0 + 8 < nsteps) load_v(i0 + 8, vbuf);
-    consume(i0, va);
-    if (i0 + 8 < nsteps) {
-      if (i0 + 16 < nsteps) load_v(i0 + 16, va);
-      consume(i0 + 8, vbuf);
     }
   }
 #pragma unroll

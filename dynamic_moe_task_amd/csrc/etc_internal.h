@@ -103,7 +103,7 @@ enum : int { M_NRT = 0, M_WORDS = 16 };
 // geometry of its tasks.
 constexpr int kDecMaxT = 16;     // tokens a launch takes (one 16-row MFMA block)
 constexpr int kDecHd = 128;      // head size
-constexpr int kDecChunk = 512;   // cache entries per attention task
+constexpr int kDecChunk = 256;   // cache entries per attention task
 constexpr int kDecOSplit = 4;    // K split of the output projection
 constexpr int kDecNormT = 4;     // tokens per RMSNorm task (one a wave)
 constexpr int kDecMaxGroup = 8;  // query heads per key/value head
