@@ -57,30 +57,33 @@ ETC_HD bool big_variant(int T, int k, int H, int I) {
 // kernel variants: small batches, large batches (column-split tiles), big tiles
 enum : int { kVarSmall = 0, kVarWide = 1, kVarBig = 2 };
 
-// Order of the big-tile variant's G tasks.  Task i of the R x C tiles of G1
-// (or of G2) is taken by workgroup group i % 8 (the grid deals consecutive
-// workgroups, and claims, over the 8 XCDs, each with its own L2).  Two
-// steps make the tiles an XCD runs at once share operands in its L2:
+// Order of the G tasks of the large-batch and big-tile variants.  Task i
+// of the R x C tiles of G1 (or of G2) is taken by workgroup group i % 8
+// (the grid deals consecutive workgroups, and claims, over the 8 XCDs, each
+// with its own L2).  Two steps make the tiles an XCD runs at once share
+// operands in its L2:
 //  - dealing in chunks: the k-th task of group g is the (k % W)-th of chunk
-//    (k / W) * 8 + g, so an XCD's W concurrent tasks are W consecutive
-//    entries of the order below (positions past the last full round of 8
-//    chunks keep their own index);
+//    (k / W) * 8 + g, so an XCD's W concurrent tasks (W = its workgroups)
+//    are W consecutive entries of the order below (positions past the last
+//    full round of 8 chunks keep their own index);
 //  - grouped order: tiles come in groups of kBigGR row tiles, column-major
-//    within a group, so W consecutive entries span kBigGR row tiles (their A
-//    rows) and W / kBigGR column tiles (their weight rows).
+//    within a group, so consecutive entries share a weight slice across
+//    kBigGR row tiles (an expert's tiles are numbered consecutively) and W
+//    consecutive entries span W / kBigGR column tiles (their A rows).
 // A bijection of [0, R * C) onto the tiles.
 constexpr int kBigGR = 4;   // row tiles per group
-constexpr int kBigW = 32;   // tasks an XCD runs at once (one workgroup per CU)
+constexpr int kBigW = 32;   // tasks an XCD runs at once, one workgroup a CU
+constexpr int kWideW = 64;  // the same with two workgroups a CU
 struct TileRC {
   int rt, nt;
 };
-ETC_HD TileRC big_task(int i, int R, int C) {
+ETC_HD TileRC grouped_task(int i, int R, int C, int W) {
   const int n = R * C;
-  const int full = (n / (8 * kBigW)) * (8 * kBigW);
+  const int full = (n / (8 * W)) * (8 * W);
   int t = i;
   if (i < full) {
     const int k = i >> 3, g = i & 7;
-    t = ((k / kBigW) * 8 + g) * kBigW + k % kBigW;
+    t = ((k / W) * 8 + g) * W + k % W;
   }
   const int grp = t / (kBigGR * C), w = t % (kBigGR * C);
   const int gsz = R - grp * kBigGR < kBigGR ? R - grp * kBigGR : kBigGR;
@@ -89,5 +92,6 @@ ETC_HD TileRC big_task(int i, int R, int C) {
   r.nt = w / gsz;
   return r;
 }
+ETC_HD TileRC big_task(int i, int R, int C) { return grouped_task(i, R, C, kBigW); }
 
 }  // namespace etc

@@ -470,18 +470,20 @@ int splitk_main(int argc, char** argv) {
 
 }  // namespace
 
-// big_task is a bijection of [0, R * C) onto the R x C tiles, and an XCD
-// group's first W tasks of a full round span kBigGR row tiles
+// grouped_task (both chunk widths) is a bijection of [0, R * C) onto the
+// R x C tiles
 int tilemap_main() {
   int bad = 0, checked = 0;
   for (int R = 1; R <= 70; ++R)
     for (int C = 1; C <= 40; ++C) {
-      std::vector<int> seen((size_t)R * C, 0);
-      for (int i = 0; i < R * C; ++i) {
-        const TileRC t = big_task(i, R, C);
-        if (t.rt < 0 || t.rt >= R || t.nt < 0 || t.nt >= C || seen[(size_t)t.rt * C + t.nt]++) ++bad;
+      for (const int W : {kBigW, kWideW}) {
+        std::vector<int> seen((size_t)R * C, 0);
+        for (int i = 0; i < R * C; ++i) {
+          const TileRC t = grouped_task(i, R, C, W);
+          if (t.rt < 0 || t.rt >= R || t.nt < 0 || t.nt >= C || seen[(size_t)t.rt * C + t.nt]++) ++bad;
+        }
+        ++checked;
       }
-      ++checked;
     }
   for (const auto& rc : {std::pair<int, int>{32, 96}, {190, 6}, {194, 8}, {32, 16}, {32, 14}, {1000, 200}}) {
     const int R = rc.first, C = rc.second;
