@@ -538,6 +538,7 @@ static int layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a,
   p.logits = reinterpret_cast<float*>(ws + L.b_logits);
   p.hh = reinterpret_cast<uint16_t*>(ws + L.b_hh);
   p.y = reinterpret_cast<uint16_t*>(ws + L.b_y);
+  p.ccnt = reinterpret_cast<int32_t*>(ws + L.b_ccnt);
   p.set_words = L.set_words;
   p.o_ev_logit = L.o_ev_logit;
   p.o_ev_exp = L.o_ev_exp;
@@ -562,6 +563,7 @@ static int layer_launch(const etc_moe_desc* d, int32_t T, const etc_moe_args* a,
     p.y_bytes = (uint32_t)(rows * d->H * 2);
     p.logits_bytes = (uint32_t)((int64_t)d->T_max * d->E * 4);
     p.rows_bytes = (uint32_t)(rows * 4);
+    p.ccnt_bytes = (uint32_t)(cdiv(d->T_max, kScanChunkT) * d->E * 4);
   }
   p.trace = a->trace;
   p.trace_records = a->trace ? a->trace_records : 0;

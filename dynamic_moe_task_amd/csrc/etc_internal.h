@@ -71,7 +71,9 @@ enum : int {
   W_DEC_ATTC = 608,  // attention merges done
   W_DEC_O = 640,     // output projection tiles done
   W_DEC_N2 = 672,    // residual + RMSNorm tasks done
-  W_FIXED = 704,     // start of the variable-size event tensors
+  W_SCAN_S1 = 704,   // large batches: per-chunk count tasks of the scan done
+  W_SCAN_S3 = 736,   // large batches: per-chunk placement tasks of the scan done
+  W_FIXED = 768,     // start of the variable-size event tensors
 };
 // split-K example: control words (u32) of its library-owned block, each on
 // its own 128-byte line, followed by the queue
@@ -89,7 +91,7 @@ struct MoeLayout {
   int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_y, o_ev_c, o_ev_att, o_queue;  // word offsets
   int64_t set_words;
   // byte offsets inside the workspace
-  int64_t b_ctrl, b_set0, b_set1, b_meta, b_rt_info, b_row_rt, b_logits, b_hh, b_y;
+  int64_t b_ctrl, b_set0, b_set1, b_meta, b_rt_info, b_row_rt, b_logits, b_hh, b_y, b_ccnt;
   int64_t total_bytes;
 };
 
@@ -143,6 +145,7 @@ inline MoeLayout moe_layout(const etc_moe_desc& d, int64_t att_events = 0) {
   L.b_logits = b;        b += align_up(Tm * d.E * 4, 256);
   L.b_hh = b;            b += align_up(rows * d.I * 2, 256);
   L.b_y = b;             b += align_up(rows * d.H * 2, 256);
+  L.b_ccnt = b;          b += align_up(cdiv(Tm, kScanChunkT) * d.E * 4, 256);  // rows per (scan chunk, expert)
   L.total_bytes = b;
   return L;
 }
@@ -207,6 +210,7 @@ struct MoeParams {
   float* logits;
   uint16_t* hh;
   uint16_t* y;
+  int32_t* ccnt;  // [ceil(T_max / kScanChunkT)][E]: rows of each expert in each scan chunk
   int64_t set_words;
   int64_t o_ev_logit, o_ev_exp, o_ev_h, o_ev_y, o_ev_c, o_ev_att, o_queue, q_cap;
   int32_t T, H, E, k, I, norm_topk, has_bias;
@@ -214,7 +218,7 @@ struct MoeParams {
   int32_t T_max;
   int32_t solo_wgs;  // persistent grids: workgroups that each have a CU to themselves (0: no such split)
   // byte sizes of the device-coherent buffers (bounds of their resources)
-  uint32_t hh_bytes, y_bytes, logits_bytes, rows_bytes;
+  uint32_t hh_bytes, y_bytes, logits_bytes, rows_bytes, ccnt_bytes;
   uint64_t budget;  // watchdog, in wall-clock ticks
   uint32_t* trace;
   uint32_t trace_records;

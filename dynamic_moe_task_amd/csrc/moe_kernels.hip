@@ -83,6 +83,7 @@ __device__ __forceinline__ rsrc_t r_rtinfo(const MoeParams& p) { return make_rsr
 __device__ __forceinline__ rsrc_t r_rowrt(const MoeParams& p) { return make_rsrc(p.row_rt, p.rows_bytes); }
 __device__ __forceinline__ rsrc_t r_hh(const MoeParams& p) { return make_rsrc(p.hh, p.hh_bytes); }
 __device__ __forceinline__ rsrc_t r_y(const MoeParams& p) { return make_rsrc(p.y, p.y_bytes); }
+__device__ __forceinline__ rsrc_t r_ccnt(const MoeParams& p) { return make_rsrc(p.ccnt, p.ccnt_bytes); }
 
 struct RowTile {
   int e, r0, nrows;
@@ -515,8 +516,17 @@ __device__ void block_excl_scan_n(const int (&v)[N], int (&ex)[N], int (&total)[
 //
 // LOCAL: the same computation for a small batch (one chunk) into `lr`, in
 // the workgroup's own LDS, with no memory written.
-template <bool LOCAL = false, bool PREFETCH = true>
-__device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem, LocalRoute* lr = nullptr) {
+// PART 0: the whole scan in one task.  Large batches split it into per-chunk
+// tasks: PART 1 counts chunk pch's rows per expert (into ccnt[pch]); PART 3,
+// once every chunk is counted, takes the totals and the earlier chunks'
+// counts from ccnt, rebuilds the prefix sums and the tile numbering (the
+// same arithmetic as PART 0, so the same results) and places chunk pch's
+// rows; the placement of chunk 0 also writes counts, exp_indptr, the row-tile
+// count and the tile table.
+template <bool LOCAL = false, bool PREFETCH = true, int PART = 0>
+__device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8_t* smem, LocalRoute* lr = nullptr,
+                                         int pch = 0) {
+  static_assert(PART == 0 || (!LOCAL && !PREFETCH), "the per-chunk parts use the memory tables, no prefetch");
   const int tid = threadIdx.x;
   const int E = c.E, k = c.k, n = c.T * c.k;
   const int nch = (c.T + kScanChunkT - 1) / kScanChunkT;
@@ -601,7 +611,34 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
   // PREFETCH: the next chunk's first batch of ids is loaded while the
   // current chunk is stored (sixteen more registers held across the chunk)
   u32x4_t v[kLd];
-  if (nch == 1) {  // one chunk: the counts come from its bitmap
+  if constexpr (PART == 1) {
+    build_bits(pch, v, false);
+    if (tid < E) {
+      int run = 0;
+      for (int w = 0; w < W; ++w) run += __popc(bits[w * kMaxE + tid]);
+      co_st32(r_ccnt(p), (uint32_t)(pch * E + tid) * 4u, (uint32_t)run);
+    }
+    return 0;
+  }
+  int runch = 0;  // PART 3: thread e's rows in the chunks before pch
+  const bool outputs = PART != 3 || pch == 0;  // this task writes the routing outputs
+  if (PART == 3) {
+    if (tid < E) {
+      const rsrc_t rcc = r_ccnt(p);
+      int tot = 0;
+      for (int q0 = 0; q0 < nch; q0 += 8) {  // eight loads in flight at a time
+        int cv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) cv[u] = q0 + u < nch ? (int)co_ld32(rcc, (uint32_t)((q0 + u) * E + tid) * 4u) : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          tot += cv[u];
+          runch += q0 + u < pch ? cv[u] : 0;
+        }
+      }
+      cnt[tid] = tot;
+    }
+  } else if (nch == 1) {  // one chunk: the counts come from its bitmap
     build_bits(0, v, false);
     if (tid < E) {
       int run = 0;
@@ -646,19 +683,19 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
     ttail[tid] = (big || rem > 32) ? -1 : (rem > 16 ? tot4 + ex2 : tot4 + tot2 + ex1);
     if (LOCAL) {
       lr->cnt[tid] = (uint16_t)my;
-    } else {
+    } else if (outputs) {
       co_st32(rc, (uint32_t)tid * 4u, (uint32_t)my);
       co_st32(ri, (uint32_t)tid * 4u, (uint32_t)ex);
     }
   }
-  if (!LOCAL && tid < E && c.set && p.debug) {
+  if (!LOCAL && outputs && tid < E && c.set && p.debug) {
     // every routed pair has notified by now (S runs after all of K): the
     // expert event holds exactly counts[e] arrivals and fires once
     if (my > 0 && ld_relaxed(ev_exp(p, c, tid)) == (uint32_t)my) atomicAdd(p.debug + E + tid, 1);
   }
   if (tid == 0) {
     iptr[E] = tot_rows;
-    if (!LOCAL) {
+    if (!LOCAL && outputs) {
       co_st32(ri, (uint32_t)E * 4u, (uint32_t)tot_rows);
       st_relaxed(p.meta + M_NRT, (uint32_t)tot_tiles);
     }
@@ -682,8 +719,9 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
     }
   } else {
     const rsrc_t rs = r_slot(p), rp = r_perm(p), rrt = r_rowrt(p);
-    int run = 0;  // thread e: rows of expert e in earlier chunks
-    for (int ch = 0; ch < nch; ++ch) {
+    int run = runch;  // thread e: rows of expert e in earlier chunks
+    const int ch_lo = PART == 3 ? pch : 0, ch_hi = PART == 3 ? pch + 1 : nch;
+    for (int ch = ch_lo; ch < ch_hi; ++ch) {
       if (nch > 1) build_bits(ch, v, PREFETCH);
       const int f0 = ch * kScanChunkT * k, f1 = chunk_end(ch);
       if (PREFETCH && ch + 1 < nch) load_ids(f1, chunk_end(ch + 1), v);  // in flight while this chunk is stored
@@ -756,7 +794,7 @@ __device__ __forceinline__ int task_scan(const MoeParams& p, const Ctx& c, uint8
     }
   }
   const rsrc_t rr = r_rtinfo(p);
-  if (tid < E) {
+  if (tid < E && outputs) {
     for (int mt = 0; mt * bm < my; ++mt) {
       const int rows = min(bm, my - mt * bm);
       const int rt = (big || rows > 32) ? ex4 + mt : (rows > 16 ? tot4 + ex2 : tot4 + tot2 + ex1);
@@ -1833,17 +1871,50 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   }
   off += c.nK;
   if (!EV && !grid_barrier(c, G, bar)) return;
-  if (first_of(w, off, G) == 0) {
-    if (tr) tw = now_ticks();
-    if (EV && !wg_wait(c.set + W_EV_ROUTE, (uint32_t)c.nK, c.status, c.budget)) return;
-    if (tr) ts = now_ticks();
-    const int nrt_s = task_scan(p, c, smem);
-    if (tr) tb = now_ticks();
-    dbg_task(p, TT_S);
-    after_scan<MODE>(p, c, nrt_s);
-    trace_task(p, TT_S, 0, 0, tw, ts, tb);
+  // Large batches with events: the scan as per-chunk tasks (count every
+  // chunk, then place every chunk), so that no workgroup walks all T*k
+  // pairs alone; the last placement to finish releases the scan event.
+  const int nsch = (c.T + kScanChunkT - 1) / kScanChunkT;
+  if (EV && WG != kVarSmall && nsch > 1) {
+    for (int i = first_of(w, off, G); i < nsch; i += G) {
+      if (tr) tw = now_ticks();
+      if (!wg_wait(c.set + W_EV_ROUTE, (uint32_t)c.nK, c.status, c.budget)) return;
+      if (tr) ts = now_ticks();
+      task_scan<false, false, 1>(p, c, smem, nullptr, i);
+      if (tr) tb = now_ticks();
+      wg_publish();
+      if (threadIdx.x == 0) (void)add_relaxed(c.set + W_SCAN_S1, 1u);
+      trace_task(p, TT_S, i, 1, tw, ts, tb);
+    }
+    off += nsch;
+    for (int i = first_of(w, off, G); i < nsch; i += G) {
+      if (tr) tw = now_ticks();
+      if (!wg_wait(c.set + W_SCAN_S1, (uint32_t)nsch, c.status, c.budget)) return;
+      if (tr) ts = now_ticks();
+      const int nrt_s = task_scan<false, false, 3>(p, c, smem, nullptr, i);
+      if (tr) tb = now_ticks();
+      dbg_task(p, TT_S);
+      wg_publish();  // this chunk's rows (and, for chunk 0, the tables) are out
+      // the scan event is complete at any value >= 1; the last placement
+      // stores nrt + 1 (every other placement drained before its arrival)
+      if (threadIdx.x == 0 && add_relaxed(c.set + W_SCAN_S3, 1u) == (uint32_t)nsch - 1u)
+        xchg_relaxed(c.set + W_EV_SCAN, (uint32_t)nrt_s + 1u);
+      trace_task(p, TT_S, i, 3, tw, ts, tb);
+    }
+    off += nsch;
+  } else {
+    if (first_of(w, off, G) == 0) {
+      if (tr) tw = now_ticks();
+      if (EV && !wg_wait(c.set + W_EV_ROUTE, (uint32_t)c.nK, c.status, c.budget)) return;
+      if (tr) ts = now_ticks();
+      const int nrt_s = task_scan(p, c, smem);
+      if (tr) tb = now_ticks();
+      dbg_task(p, TT_S);
+      after_scan<MODE>(p, c, nrt_s);
+      trace_task(p, TT_S, 0, 0, tw, ts, tb);
+    }
+    off += 1;
   }
-  off += 1;
   // Small batch: each workgroup rebuilds the routing tables in its own LDS
   // as soon as every top-k task is done, so G1 does not wait for S (S still
   // writes the routing outputs, which C reads).
@@ -2090,6 +2161,17 @@ __global__ void __launch_bounds__(kThreads) kbk_scan(MoeParams p) {
   const Ctx c = make_ctx(p, nullptr);
   task_scan(p, c, smem);
 }
+// large batches: the scan as per-chunk tasks, one chunk a workgroup
+__global__ void __launch_bounds__(kThreads) kbk_scan_count(MoeParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const Ctx c = make_ctx(p, nullptr);
+  task_scan<false, false, 1>(p, c, smem, nullptr, blockIdx.x);
+}
+__global__ void __launch_bounds__(kThreads) kbk_scan_place(MoeParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const Ctx c = make_ctx(p, nullptr);
+  task_scan<false, false, 3>(p, c, smem, nullptr, blockIdx.x);
+}
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) kbk_g1(MoeParams p) {
   // the larger of the K-split bodies' reduction and stage and the
   // column-split body's two staged A buffers
@@ -2288,7 +2370,13 @@ int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream) {
   const int nN1 = p.I / (big ? kBigBN1 : g1_cols(p.T, p.k, p.H)), nN2 = p.H / (big ? kBigBN2 : g2_cols(p.T, p.k, p.I));
   hipLaunchKernelGGL(kbk_router, dim3(nTT * nET), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(kbk_topk, dim3(nTT), dim3(kThreads), 0, s, p);
-  hipLaunchKernelGGL(kbk_scan, dim3(1), dim3(kThreads), lds_bytes, s, p);
+  const int nsch = (p.T + kScanChunkT - 1) / kScanChunkT;
+  if (nsch > 1 && wide_variant(p.T, p.k, p.H, p.I)) {  // the persistent kernels' rule
+    hipLaunchKernelGGL(kbk_scan_count, dim3(nsch), dim3(kThreads), lds_bytes, s, p);
+    hipLaunchKernelGGL(kbk_scan_place, dim3(nsch), dim3(kThreads), lds_bytes, s, p);
+  } else {
+    hipLaunchKernelGGL(kbk_scan, dim3(1), dim3(kThreads), lds_bytes, s, p);
+  }
   if (big) {
     hipError_t e = hipFuncSetAttribute((const void*)kbk_g1_big, hipFuncAttributeMaxDynamicSharedMemorySize, kBigLdsBytes);
     if (e == hipSuccess)
