@@ -57,8 +57,8 @@ ETC_HD bool big_variant(int T, int k, int H, int I) {
 // kernel variants: small batches, large batches (column-split tiles), big tiles
 enum : int { kVarSmall = 0, kVarWide = 1, kVarBig = 2 };
 
-// Order of the G tasks of the large-batch and big-tile variants.  Task i
-// of the R x C tiles of G1 (or of G2) is taken by workgroup group i % 8
+// Order of the big-tile variant's G tasks.  Task i of the R x C tiles of G1
+// (or of G2) is taken by workgroup group i % 8
 // (the grid deals consecutive workgroups, and claims, over the 8 XCDs, each
 // with its own L2).  Two steps make the tiles an XCD runs at once share
 // operands in its L2:
@@ -73,7 +73,6 @@ enum : int { kVarSmall = 0, kVarWide = 1, kVarBig = 2 };
 // A bijection of [0, R * C) onto the tiles.
 constexpr int kBigGR = 4;   // row tiles per group
 constexpr int kBigW = 32;   // tasks an XCD runs at once, one workgroup a CU
-constexpr int kWideW = 64;  // the same with two workgroups a CU
 struct TileRC {
   int rt, nt;
 };

@@ -470,13 +470,13 @@ int splitk_main(int argc, char** argv) {
 
 }  // namespace
 
-// grouped_task (both chunk widths) is a bijection of [0, R * C) onto the
+// grouped_task (chunks of one and of two workgroups a CU) is a bijection of [0, R * C) onto the
 // R x C tiles
 int tilemap_main() {
   int bad = 0, checked = 0;
   for (int R = 1; R <= 70; ++R)
     for (int C = 1; C <= 40; ++C) {
-      for (const int W : {kBigW, kWideW}) {
+      for (const int W : {kBigW, 2 * kBigW}) {
         std::vector<int> seen((size_t)R * C, 0);
         for (int i = 0; i < R * C; ++i) {
           const TileRC t = grouped_task(i, R, C, W);
