@@ -366,6 +366,95 @@ __device__ __forceinline__ void task_router(const MoeParams& p, const Ctx& c, in
     router_body<kRouterE / 4, 4>(p, c, tt, et);
 }
 
+// Big-tile variant, all of a workgroup's router tasks (i0, i0 + G, ...) as
+// one stream: the next step's chunks load while the current step multiplies,
+// across task boundaries (one wave a SIMD in this variant, so a wave hides
+// its own load latency or nobody does), and the logits' stores are drained
+// once, after the last task, before the notifies of every task of the
+// stream.  Each logit is the same sequence of fused multiply-adds, butterfly
+// and bias as in router_body.  Full tiles only (the caller checks T, E and
+// H); EPW experts a wave, U chunks a lane a step, steps taken in pairs.
+template <int EPW, int U>
+__device__ __forceinline__ void router_stream(const MoeParams& p, const Ctx& c, int i0, int G) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int H = c.H, nit = (H >> 3) / (64 * U);  // steps a task (even)
+  const bool tr = p.trace != nullptr;
+  u32x4_t xa[U][kRouterT], wa[EPW][U], xb[U][kRouterT], wb[EPW][U];
+  auto load = [&](int i, int it, u32x4_t (&xv)[U][kRouterT], u32x4_t (&wvv)[EPW][U]) {
+    const uint16_t* xrow = p.x + (size_t)(i / c.nET) * kRouterT * H;
+    const uint16_t* wrow = p.wr + (size_t)((i % c.nET) * 4 * EPW + wv * EPW) * H;
+    const int c0 = lane + it * 64 * U;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < kRouterT; ++r) xv[u][r] = ld4(xrow + (size_t)r * H + (c0 + 64 * u) * 8);
+#pragma unroll
+    for (int j = 0; j < EPW; ++j)
+#pragma unroll
+      for (int u = 0; u < U; ++u) wvv[j][u] = ld4(wrow + (size_t)j * H + (c0 + 64 * u) * 8);
+  };
+  auto step = [&](const u32x4_t (&xv)[U][kRouterT], const u32x4_t (&wvv)[EPW][U], float (&acc)[EPW][kRouterT]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float wf[EPW][8];
+#pragma unroll
+      for (int j = 0; j < EPW; ++j) unpack8(wvv[j][u], wf[j]);
+#pragma unroll
+      for (int r = 0; r < kRouterT; ++r) {
+        float xf[8];
+        unpack8(xv[u][r], xf);
+#pragma unroll
+        for (int j = 0; j < EPW; ++j)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[j][r] = __builtin_fmaf(xf[q], wf[j][q], acc[j][r]);
+      }
+    }
+  };
+  const rsrc_t rl = r_logits(p);
+  load(i0, 0, xa, wa);
+  for (int i = i0; i < c.nR; i += G) {
+    uint64_t tw = 0;
+    if (tr) tw = now_ticks();
+    float acc[EPW][kRouterT];
+#pragma unroll
+    for (int j = 0; j < EPW; ++j)
+#pragma unroll
+      for (int r = 0; r < kRouterT; ++r) acc[j][r] = 0.0f;
+    for (int it = 0; it < nit; it += 2) {
+      load(i, it + 1, xb, wb);
+      step(xa, wa, acc);
+      if (it + 2 < nit)
+        load(i, it + 2, xa, wa);
+      else if (i + G < c.nR)
+        load(i + G, 0, xa, wa);  // the next task's first step
+      step(xb, wb, acc);
+    }
+#pragma unroll
+    for (int j = 0; j < EPW; ++j)
+#pragma unroll
+      for (int r = 0; r < kRouterT; ++r) {
+#pragma unroll
+        for (int s2 = 32; s2 >= 1; s2 >>= 1) acc[j][r] = acc[j][r] + __shfl_xor(acc[j][r], s2);
+      }
+    if (lane == 0) {
+      const int t0 = (i / c.nET) * kRouterT, e0 = (i % c.nET) * 4 * EPW + wv * EPW;
+#pragma unroll
+      for (int j = 0; j < EPW; ++j)
+#pragma unroll
+        for (int r = 0; r < kRouterT; ++r) {
+          float v = acc[j][r];
+          if (p.has_bias) v = v + p.br[e0 + j];
+          co_stf(rl, (uint32_t)((t0 + r) * c.E + e0 + j) * 4u, v);
+        }
+    }
+    dbg_task(p, TT_R);
+    if (tr) {
+      const uint64_t tb = now_ticks();
+      trace_task(p, TT_R, i / c.nET, i % c.nET, tw, tw, tb);
+    }
+  }
+}
+
 // K: top-k per token (one wave per token): k rounds of a wave-wide arg-max
 // on (logit descending, expert index ascending); weights exp(l_j - l_max)
 // normalised over the chosen k (norm_topk) or over all E.
@@ -1848,7 +1937,26 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   if (p.dec && first_of(w, off, G) < c.nR &&
       !wg_wait(c.set + W_DEC_N2, (uint32_t)((c.T + kDecNormT - 1) / kDecNormT), c.status, c.budget))
     return;
-  for (int i = first_of(w, off, G); i < c.nR; i += G) {
+  // big-tile variant, full router tiles: the workgroup's tasks as one
+  // pipelined stream, one drain, then the notifies of all of them
+  bool streamed = false;
+  if constexpr (WG == kVarBig) {
+    if (EV && router_experts(c.T) == kRouterEXL && c.T % kRouterT == 0 && c.E % kRouterEXL == 0 &&
+        (c.H >> 3) % (2 * 64) == 0) {
+      const int i0 = first_of(w, off, G);
+      if (i0 < c.nR) {
+        // one chunk a lane a step: two steps' operands and the unpacked
+        // weights stay within the 256 VGPRs (two-chunk steps spilled into
+        // the accumulation registers)
+        router_stream<kRouterEXL / 4, 1>(p, c, i0, G);
+        wg_publish();
+        if (threadIdx.x == 0)
+          for (int i = i0; i < c.nR; i += G) notify1(c, ev_logit(p, c, i / c.nET), (uint32_t)c.nET);
+      }
+      streamed = true;
+    }
+  }
+  for (int i = first_of(w, off, G); !streamed && i < c.nR; i += G) {
     if (tr) tw = ts = now_ticks();
     task_router<(WG != kVarSmall)>(p, c, i / c.nET, i % c.nET);
     if (tr) tb = now_ticks();
