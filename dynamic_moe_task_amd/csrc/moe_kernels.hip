@@ -927,7 +927,7 @@ __device__ __forceinline__ uint32_t row_perm(const MoeParams& p, const RowTile t
   if (r >= tile.nrows) return 0u;
   return lr ? (uint32_t)lr->perm[tile.r0 + r] : co_ld32(r_perm(p), (uint32_t)(tile.r0 + r) * 4u);
 }
-template <int NB, int U, int CB>
+template <int NB, int U, int CB, bool PIPE = true>
 __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const RowTile tile, int nt, float* red,
                                         const uint32_t* pre) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -955,6 +955,46 @@ __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const 
 #pragma unroll
     for (int q = 0; q < CB; ++q) accg[b][q] = accu[b][q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+  if (PIPE && nsteps % U == 0) {
+    // Rolling pipeline over U register slots: the loads of step s + U go
+    // into slot s % U as soon as step s has been multiplied, so each wave
+    // keeps U - 1 to U steps of loads in flight the whole time rather than
+    // draining a batch before issuing the next (workgroups that start their
+    // tasks together then keep the memory system busy).  Rows past the count
+    // load row 0 (a valid token row): MFMA output rows depend only on their
+    // own A rows, and those output rows are never stored.
+    u32x4_t a[U][NB], bg[U][CB], bu[U][CB];
+    auto issue = [&](int u, int st) {
+      const int k0 = st * 32;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) a[u][b] = ld4(pa[b] + k0);
+#pragma unroll
+      for (int q = 0; q < CB; ++q) {
+        bg[u][q] = ld4(pg + q * cbs + k0);
+        bu[u][q] = ld4(pu + q * cbs + k0);
+      }
+    };
+    auto mma = [&](int u) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+          accg[b][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u][b]), as_bf(bg[u][q]), accg[b][q], 0, 0, 0);
+          accu[b][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u][b]), as_bf(bu[u][q]), accu[b][q], 0, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) issue(u, u);
+    for (int s0 = U; s0 < nsteps; s0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        mma(u);
+        issue(u, s0 + u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) mma(u);
+  } else
   // batches of U k-steps ((NB + 2 CB) * U loads of 16 bytes a lane in
   // flight); two workgroups per CU overlap each other's batch boundaries
   for (int s0 = 0; s0 < nsteps; s0 += U) {
@@ -962,12 +1002,13 @@ __device__ __forceinline__ void g1_body(const MoeParams& p, const Ctx& c, const 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u < nsteps) {
+        const int k0 = (s0 + u) * 32;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) a[u][b] = valid[b] ? ld4(pa[b] + (s0 + u) * 32) : zero;
+        for (int b = 0; b < NB; ++b) a[u][b] = valid[b] ? ld4(pa[b] + k0) : zero;
 #pragma unroll
         for (int q = 0; q < CB; ++q) {
-          bg[u][q] = ld4(pg + q * cbs + (s0 + u) * 32);
-          bu[u][q] = ld4(pu + q * cbs + (s0 + u) * 32);
+          bg[u][q] = ld4(pg + q * cbs + k0);
+          bu[u][q] = ld4(pu + q * cbs + k0);
         }
       }
     }
@@ -1150,6 +1191,9 @@ template <bool KBK = false, int WIDE = kVarWide>
 __device__ __forceinline__ void task_g1(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt, float* red,
                         const uint32_t* pre = nullptr) {
   (void)rt;
+  // the rolling load pipeline in the small-batch persistent variant (the
+  // separate G kernels, three workgroups a CU, measured faster without it)
+  constexpr bool PIPE = !KBK && WIDE == kVarSmall;
   if constexpr (WIDE == kVarBig) {
     big_body<true>(p, c, tile, nt, reinterpret_cast<uint8_t*>(red));
     return;
@@ -1169,23 +1213,23 @@ __device__ __forceinline__ void task_g1(const MoeParams& p, const Ctx& c, const 
   }
   if (c.bn1 == 2 * kBN1) {  // mid-size batches: 32 gate + 32 up columns, K-split
     switch (row_blocks(tile.nrows)) {
-      case 1: g1_body<1, 2, 2>(p, c, tile, nt, red, pre); break;
-      case 2: g1_body<2, 2, 2>(p, c, tile, nt, red, pre); break;
-      default: g1_body<4, 1, 2>(p, c, tile, nt, red, pre); break;
+      case 1: g1_body<1, 2, 2, PIPE>(p, c, tile, nt, red, pre); break;
+      case 2: g1_body<2, 2, 2, PIPE>(p, c, tile, nt, red, pre); break;
+      default: g1_body<4, 1, 2, PIPE>(p, c, tile, nt, red, pre); break;
     }
     return;
   }
   switch (row_blocks(tile.nrows)) {
-    case 1: g1_body<1, 4, 1>(p, c, tile, nt, red, pre); break;
-    case 2: g1_body<2, 4, 1>(p, c, tile, nt, red, pre); break;
-    default: g1_body<4, KBK ? 4 : 2, 1>(p, c, tile, nt, red, pre); break;
+    case 1: g1_body<1, 4, 1, PIPE>(p, c, tile, nt, red, pre); break;
+    case 2: g1_body<2, 4, 1, PIPE>(p, c, tile, nt, red, pre); break;
+    default: g1_body<4, KBK ? 4 : 2, 1, PIPE>(p, c, tile, nt, red, pre); break;
   }
 }
 
 // G2: one row tile times kBN2 output columns of Wd[e]: Y = bf16(Hmid Wd^T).
 // K = I split in quarters over the waves; each wave keeps kBN2 / 16 column blocks
 // for every row block.
-template <int NB, int U>
+template <int NB, int U, bool PIPE = true>
 __device__ __forceinline__ void g2_body(const MoeParams& p, const Ctx& c, const RowTile tile, int nt2, float* red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int m = lane & 15, kg = lane >> 4;
@@ -1209,15 +1253,46 @@ __device__ __forceinline__ void g2_body(const MoeParams& p, const Ctx& c, const 
 #pragma unroll
     for (int q = 0; q < kCB2; ++q) acc[b][q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+  if (PIPE && nsteps % U == 0) {
+    // rolling pipeline over U register slots, as in g1_body (rows past the
+    // count load the tile's first row; their output rows are not stored)
+    u32x4_t a[U][NB], bb[U][kCB2];
+    auto issue = [&](int u, int st) {
+      const int ks = st;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) a[u][b] = co_ld128(rh, aoff[b] + (uint32_t)ks * 64u);
+#pragma unroll
+      for (int q = 0; q < kCB2; ++q) bb[u][q] = ld4(pb + q * cbs + ks * 32);
+    };
+    auto mma = [&](int u) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q = 0; q < kCB2; ++q)
+          acc[b][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u][b]), as_bf(bb[u][q]), acc[b][q], 0, 0, 0);
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) issue(u, u);
+    for (int s0 = U; s0 < nsteps; s0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        mma(u);
+        issue(u, s0 + u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) mma(u);
+  } else
   for (int s0 = 0; s0 < nsteps; s0 += U) {
     u32x4_t a[U][NB], bb[U][kCB2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u < nsteps) {
+        const int ks = s0 + u;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) a[u][b] = valid[b] ? co_ld128(rh, aoff[b] + (uint32_t)(s0 + u) * 64u) : zero;
+        for (int b = 0; b < NB; ++b) a[u][b] = valid[b] ? co_ld128(rh, aoff[b] + (uint32_t)ks * 64u) : zero;
 #pragma unroll
-        for (int q = 0; q < kCB2; ++q) bb[u][q] = ld4(pb + q * cbs + (s0 + u) * 32);
+        for (int q = 0; q < kCB2; ++q) bb[u][q] = ld4(pb + q * cbs + ks * 32);
       }
     }
 #pragma unroll
@@ -1354,6 +1429,7 @@ __device__ __forceinline__ void g2_cs_body(const MoeParams& p, const Ctx& c, con
 
 template <bool KBK = false, int WIDE = kVarWide>
 __device__ __forceinline__ void task_g2(const MoeParams& p, const Ctx& c, const RowTile tile, int rt, int nt2, float* red) {
+  constexpr bool PIPE = !KBK && WIDE == kVarSmall;  // as in task_g1
   if constexpr (WIDE == kVarBig) {
     big_body<false>(p, c, tile, nt2, reinterpret_cast<uint8_t*>(red));
     return;
@@ -1368,9 +1444,9 @@ __device__ __forceinline__ void task_g2(const MoeParams& p, const Ctx& c, const 
     return;
   }
   switch (row_blocks(tile.nrows)) {
-    case 1: g2_body<1, 2>(p, c, tile, nt2, red); break;
-    case 2: g2_body<2, 2>(p, c, tile, nt2, red); break;
-    default: g2_body<4, KBK ? 2 : 1>(p, c, tile, nt2, red); break;
+    case 1: g2_body<1, 2, PIPE>(p, c, tile, nt2, red); break;
+    case 2: g2_body<2, 2, PIPE>(p, c, tile, nt2, red); break;
+    default: g2_body<4, KBK ? 2 : 1, PIPE>(p, c, tile, nt2, red); break;
   }
 }
 
