@@ -91,7 +91,8 @@ def copy_calibration(mib, steps):
                       "GBps": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}))
 
 
-TASK_NAMES = {1: "R", 2: "K", 3: "S", 4: "D", 5: "G1", 6: "G2", 7: "C", 8: "L"}  # L: LDS routing tables
+TASK_NAMES = {1: "R", 2: "K", 3: "S", 4: "D", 5: "G1", 6: "G2", 7: "C", 8: "L",  # L: LDS routing tables
+              9: "N1", 10: "QKV", 11: "ATT", 12: "ATTC", 13: "O", 14: "N2"}  # the decoder's attention block
 
 
 def tile_rows(counts, bm=64):
@@ -134,14 +135,18 @@ def tile_mfma(rec_typ, rec_a, body_us, rows, H, I, grid, bn1, bn2):
     return out
 
 
-def trace_summary(bufs, T, sched, khz, stream_ptr, records=1 << 16, dump=None, shape=None):
+def trace_summary(bufs, T, sched, khz, stream_ptr, records=1 << 16, dump=None, shape=None, launch=None):
     """One traced launch: per task type, count, mean/max duration, mean
     wait, and the first start / last end in µs from the earliest wait; with
-    `shape`, the tile-level MFMA use of the four-block G tiles."""
+    `shape`, the tile-level MFMA use of the four-block G tiles.  `launch`
+    (given the trace buffer) replaces the MoE layer launch (the decoder)."""
     import torch
     from dynamic_moe_task_amd import binding as B
     tr = torch.zeros(B.trace_words(records), dtype=torch.int32, device="cuda")
-    B.check(B.moe_layer_launch(bufs.desc, T, bufs.args(trace=tr), B.SCHEDS[sched], stream_ptr))
+    if launch is not None:
+        B.check(launch(tr))
+    else:
+        B.check(B.moe_layer_launch(bufs.desc, T, bufs.args(trace=tr), B.SCHEDS[sched], stream_ptr))
     B.check(B.etc_sync(stream_ptr))
     raw = tr.cpu().numpy().view(np.uint32)
     allrec = raw[16:16 + 8 * records].reshape(records, 8)
@@ -462,7 +467,7 @@ def measure_dense_mlps(sp, steps, warmup, repeat, which=None):
     return out
 
 
-def measure_decoder(Wr, w13s, w2s, sp, steps, warmup, repeat, scheds=("static", "ordered", "kbk")):
+def measure_decoder(Wr, w13s, w2s, sp, steps, warmup, repeat, scheds=("static", "ordered", "kbk"), trace=""):
     """The decoder layer around the MoE layer as one persistent kernel
     (batch 8, 32 query / 4 kv heads of 128, 4096 cached entries per
     sequence, then the same MoE block with the decode weights), against its
@@ -505,6 +510,15 @@ def measure_decoder(Wr, w13s, w2s, sp, steps, warmup, repeat, scheds=("static", 
             runs[x].append(timed(x))
     us = {x: float(np.median(v)) for x, v in runs.items()}
     best = min((x for x in ("static", "ordered") if x in us), key=lambda x: us[x], default=scheds[0])
+    if trace:
+        khz = B.moe_layer_info(B.moe_desc(s.T, s.H, s.moe.E, s.moe.k, s.moe.I)).wall_clock_khz
+        base = os.path.splitext(trace)[0]
+        summ = {x: trace_summary(None, s.T, x, khz, sp, dump=f"{base}_{x}.npz",
+                                 launch=lambda tr, x=x: B.decoder_layer_launch(desc, s.T, s.pos, bufs.args(trace=tr),
+                                                                              B.SCHEDS[x], sp))
+                for x in scheds if x != "kbk"}
+        with open(trace, "w") as f:
+            json.dump(summ, f, indent=1)
     return {
         "workload": s.name, "T": s.T, "pos": s.pos, "heads": [s.nq, s.nkv, s.d], "active_experts": n_act,
         "us_per_layer": {x: round(v, 2) for x, v in us.items()},
@@ -548,7 +562,7 @@ def main():
             print(json.dumps(measure_token_counts(Wr, w13s, w2s, sp, a.steps, a.warmup, a.repeat, counts)), flush=True)
             return
         scheds = (a.sched,) if a.only_sched else ("static", "ordered", "kbk")
-        print(json.dumps(measure_decoder(Wr, w13s, w2s, sp, a.steps, a.warmup, a.repeat, scheds)), flush=True)
+        print(json.dumps(measure_decoder(Wr, w13s, w2s, sp, a.steps, a.warmup, a.repeat, scheds, a.trace)), flush=True)
         return
     shape = wl.SHAPES[a.workload]
     if a.tokens > 0:

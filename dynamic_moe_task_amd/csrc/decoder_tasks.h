@@ -3,7 +3,7 @@
 // after the MoE task bodies, whose helpers (bf16 conversion, coherent
 // accesses, Ctx, events) it uses.
 //
-//   N1(tt)      h1 = RMSNorm(x) * g1 for 4 tokens (one wave a token)
+//   N1(t)       h1 = RMSNorm(x) * g1 for token t (the four waves split H)
 //   QKV(c)      16 columns of h1 Wqkv^T; for query and key heads the 16
 //               columns are 8 rotary pairs (i, i + d/2), rotated at `pos`;
 //               queries go to qb, keys and values into the caches at `pos`
@@ -15,7 +15,7 @@
 //               value into the attention output of the group's heads
 //   O(c,ks)     16 columns of o Wo^T over one quarter of the inner dimension
 //               (fp32 partial sums)
-//   N2(tt)      a = bf16(sum of the quarters), x2 = bf16(x + a),
+//   N2(t)       a = bf16(sum of the quarters), x2 = bf16(x + a),
 //               h2 = RMSNorm(x2) * g2: h2 is the MoE block's input, x2 the
 //               residual its combine adds
 // Data one task writes and another reads moves through device-coherent
@@ -55,33 +55,77 @@ __device__ __forceinline__ DecCounts dec_counts(const MoeParams& p, const Ctx& c
   return n;
 }
 
-// N1: h1 = bf16(x * r * g1), r = 1 / sqrt(mean(x^2) + eps), fp32.
-__device__ __forceinline__ void task_norm1(const MoeParams& p, const Ctx& c, int tt) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t = tt * kDecNormT + wv;
-  if (t >= c.T) return;
+// Sum of one value per thread over the workgroup: a shuffle tree inside
+// each wave, then the four wave sums through LDS.
+__device__ __forceinline__ float block_sum(float v, float* s4) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) s4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+}
+// The RMSNorm tasks keep up to kNormPer 8-element chunks a thread in
+// registers between the sum of squares and the scaling (H <= 8192); chunks
+// beyond are read again.
+constexpr int kNormPer = 4;
+
+// N1: h1 = bf16(x * r * g1), r = 1 / sqrt(mean(x^2) + eps), fp32.  Every
+// chunk of the token's row and of g1 is requested at once.
+__device__ __forceinline__ void task_norm1(const MoeParams& p, const Ctx& c, int t) {
+  __shared__ float s4[4];
+  const int tid = threadIdx.x;
   const int H = c.H, nch = H >> 3;
   const uint16_t* xr = p.dx + (size_t)t * H;
+  u32x4_t xv[kNormPer], gv[kNormPer];
+#pragma unroll
+  for (int j = 0; j < kNormPer; ++j) {
+    const int ch = tid + j * kThreads;
+    if (ch < nch) {
+      xv[j] = ld4(xr + ch * 8);
+      gv[j] = ld4(p.g1 + ch * 8);
+    }
+  }
   float ss = 0.f;
-  for (int ch = lane; ch < nch; ch += 64) {
+#pragma unroll
+  for (int j = 0; j < kNormPer; ++j) {
+    if (tid + j * kThreads < nch) {
+      float f[8];
+      unpack8(xv[j], f);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ss = __builtin_fmaf(f[q], f[q], ss);
+    }
+  }
+  for (int ch = tid + kNormPer * kThreads; ch < nch; ch += kThreads) {
     float f[8];
     unpack8(ld4(xr + ch * 8), f);
 #pragma unroll
     for (int q = 0; q < 8; ++q) ss = __builtin_fmaf(f[q], f[q], ss);
   }
-  ss = wave_sum(ss);
+  ss = block_sum(ss, s4);
   const float r = 1.0f / sqrtf(ss / (float)H + p.eps);
   const rsrc_t rh = r_h1(p);
-  for (int ch = lane; ch < nch; ch += 64) {
-    float f[8], g[8];
-    unpack8(ld4(xr + ch * 8), f);
-    unpack8(ld4(p.g1 + ch * 8), g);
+  auto out = [&](int ch, const float* f, const float* g) {
     u32x4_t o;
     o.x = f2bf(f[0] * r * g[0]) | (f2bf(f[1] * r * g[1]) << 16);
     o.y = f2bf(f[2] * r * g[2]) | (f2bf(f[3] * r * g[3]) << 16);
     o.z = f2bf(f[4] * r * g[4]) | (f2bf(f[5] * r * g[5]) << 16);
     o.w = f2bf(f[6] * r * g[6]) | (f2bf(f[7] * r * g[7]) << 16);
     co_st128(rh, (uint32_t)(((size_t)t * H + ch * 8) * 2), o);
+  };
+#pragma unroll
+  for (int j = 0; j < kNormPer; ++j) {
+    const int ch = tid + j * kThreads;
+    if (ch < nch) {
+      float f[8], g[8];
+      unpack8(xv[j], f);
+      unpack8(gv[j], g);
+      out(ch, f, g);
+    }
+  }
+  for (int ch = tid + kNormPer * kThreads; ch < nch; ch += kThreads) {
+    float f[8], g[8];
+    unpack8(ld4(xr + ch * 8), f);
+    unpack8(ld4(p.g1 + ch * 8), g);
+    out(ch, f, g);
   }
 }
 
@@ -100,6 +144,29 @@ __device__ __forceinline__ void tile16(rsrc_t ra, uint32_t astride, const uint16
   const uint16_t* pb = W + (size_t)wrow(m) * wstride + kbeg + wv * kw + kg * 8;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+  constexpr int U = 8;
+  if (nsteps % U == 0) {
+    // rolling pipeline over U register slots (as the MoE block's small G
+    // tiles): U - 1 to U steps of loads in flight, so a task of one tile is
+    // about one memory latency plus its stream.  Rows past T load row 0;
+    // their output rows are never stored.
+    u32x4_t a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      a[u] = co_ld128(ra, aoff + (uint32_t)u * 64u);
+      b[u] = ld4(pb + u * 32);
+    }
+    for (int s0 = U; s0 < nsteps; s0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u]), as_bf(b[u]), acc, 0, 0, 0);
+        a[u] = co_ld128(ra, aoff + (uint32_t)(s0 + u) * 64u);
+        b[u] = ld4(pb + (s0 + u) * 32);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[u]), as_bf(b[u]), acc, 0, 0, 0);
+  } else
   for (int s0 = 0; s0 < nsteps; s0 += 4) {
     u32x4_t a[4], b[4];
 #pragma unroll
@@ -174,15 +241,23 @@ __device__ __forceinline__ void task_qkv(const MoeParams& p, const Ctx& c, int c
   }
 }
 
+// LDS of one attention task: the scores P [16 rows][kDecChunk], whose space
+// then holds the four waves' value sums [4][group heads][head size], then
+// 64 + 32 floats of maxima and sums
+constexpr int kAttnPFloats =
+    16 * kDecChunk > 4 * kDecMaxGroup * kDecHd ? 16 * kDecChunk : 4 * kDecMaxGroup * kDecHd;
+constexpr int kAttnLdsFloats = kAttnPFloats + 64 + 32;
+static_assert(kAttnLdsFloats * 4 <= kGemmLdsBytes, "the persistent kernels' LDS holds an attention task");
 // ATT: cache entries k0 .. k0 + nk - 1 (k0 = ch * kDecChunk, all below pos)
 // of token t and kv head g, for the group's gq query heads.  Scores by bf16
 // MFMA (A = the heads' queries, 16 rows with gq used; B = 16 entries a
 // column block, wave w covering entries w*64 .. w*64+63); softmax maximum
 // and sums across the waves in LDS; the weighted value sum on the VALU.
-// Chunks of 256 entries give the grid two tasks a CU at the decoder
+// Chunks of 256 entries give the grid one task a workgroup at the decoder
 // workload (8 tokens x 4 kv heads x 16 chunks), and each task issues all of
 // its key loads, then all of its value loads, at once: the task is a few
-// memory latencies long instead of one per batch.
+// memory latencies long instead of one per batch.  (Every schedule uses
+// the same chunks, so all of them sum in the same order.)
 // The partial holds, per head, the unnormalised sum over the chunk, the
 // chunk's maximum score and the sum of exp(score - maximum).
 __device__ __forceinline__ void task_attn(const MoeParams& p, const Ctx& c, int t, int g, int ch, float* lds) {
@@ -191,8 +266,8 @@ __device__ __forceinline__ void task_attn(const MoeParams& p, const Ctx& c, int 
   const int m = lane & 15, kg = lane >> 4;
   const int d = kDecHd, gq = p.nq / p.nkv;
   const int k0 = ch * kDecChunk, nk = min(kDecChunk, p.pos - k0);
-  float* P = lds;                          // [16 rows][kDecChunk]
-  float* wred = lds + 16 * kDecChunk;      // [4 waves][16 rows]
+  float* P = lds;                          // [16 rows][kDecChunk], later the waves' value sums
+  float* wred = lds + kAttnPFloats;        // [4 waves][16 rows]
   float* mrow = wred + 64;                 // [16] row maxima, then [16] sums
   const float scale = 1.0f / sqrtf((float)d);
   const u32x4_t zero = {0u, 0u, 0u, 0u};
@@ -431,37 +506,56 @@ __device__ __forceinline__ void norm2_chunk(const MoeParams& p, int t, int ch, f
 #pragma unroll
   for (int q = 0; q < 8; ++q) x2[q] = bf_round(f[q] + bf_round(a[q]));
 }
-__device__ __forceinline__ void task_norm2(const MoeParams& p, const Ctx& c, int tt) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t = tt * kDecNormT + wv;
-  if (t >= c.T) return;
+__device__ __forceinline__ void task_norm2(const MoeParams& p, const Ctx& c, int t) {
+  __shared__ float s4[4];
+  const int tid = threadIdx.x;
   const int H = c.H, nch = H >> 3;
   const rsrc_t rr = r_resid(p), rh = r_h2(p);
+  auto put = [&](rsrc_t rs, int ch, const float* v) {
+    u32x4_t o;
+    o.x = f2bf(v[0]) | (f2bf(v[1]) << 16);
+    o.y = f2bf(v[2]) | (f2bf(v[3]) << 16);
+    o.z = f2bf(v[4]) | (f2bf(v[5]) << 16);
+    o.w = f2bf(v[6]) | (f2bf(v[7]) << 16);
+    co_st128(rs, (uint32_t)(((size_t)t * H + ch * 8) * 2), o);
+  };
+  float x2[kNormPer][8];
   float ss = 0.f;
-  for (int ch = lane; ch < nch; ch += 64) {
-    float x2[8];
-    norm2_chunk(p, t, ch, x2);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) ss = __builtin_fmaf(x2[q], x2[q], ss);
-    u32x4_t o;
-    o.x = f2bf(x2[0]) | (f2bf(x2[1]) << 16);
-    o.y = f2bf(x2[2]) | (f2bf(x2[3]) << 16);
-    o.z = f2bf(x2[4]) | (f2bf(x2[5]) << 16);
-    o.w = f2bf(x2[6]) | (f2bf(x2[7]) << 16);
-    co_st128(rr, (uint32_t)(((size_t)t * H + ch * 8) * 2), o);
+  for (int j = 0; j < kNormPer; ++j) {
+    const int ch = tid + j * kThreads;
+    if (ch < nch) {
+      norm2_chunk(p, t, ch, x2[j]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ss = __builtin_fmaf(x2[j][q], x2[j][q], ss);
+      put(rr, ch, x2[j]);
+    }
   }
-  ss = wave_sum(ss);
+  for (int ch = tid + kNormPer * kThreads; ch < nch; ch += kThreads) {
+    float v[8];
+    norm2_chunk(p, t, ch, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ss = __builtin_fmaf(v[q], v[q], ss);
+    put(rr, ch, v);
+  }
+  ss = block_sum(ss, s4);
   const float r = 1.0f / sqrtf(ss / (float)H + p.eps);
-  for (int ch = lane; ch < nch; ch += 64) {
-    float x2[8], g[8];
-    norm2_chunk(p, t, ch, x2);
+  auto scaled = [&](int ch, const float* v) {
+    float g[8], h[8];
     unpack8(ld4(p.g2 + ch * 8), g);
-    u32x4_t o;
-    o.x = f2bf(x2[0] * r * g[0]) | (f2bf(x2[1] * r * g[1]) << 16);
-    o.y = f2bf(x2[2] * r * g[2]) | (f2bf(x2[3] * r * g[3]) << 16);
-    o.z = f2bf(x2[4] * r * g[4]) | (f2bf(x2[5] * r * g[5]) << 16);
-    o.w = f2bf(x2[6] * r * g[6]) | (f2bf(x2[7] * r * g[7]) << 16);
-    co_st128(rh, (uint32_t)(((size_t)t * H + ch * 8) * 2), o);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) h[q] = v[q] * r * g[q];
+    put(rh, ch, h);
+  };
+#pragma unroll
+  for (int j = 0; j < kNormPer; ++j) {
+    const int ch = tid + j * kThreads;
+    if (ch < nch) scaled(ch, x2[j]);
+  }
+  for (int ch = tid + kNormPer * kThreads; ch < nch; ch += kThreads) {
+    float v[8];
+    norm2_chunk(p, t, ch, v);
+    scaled(ch, v);
   }
 }
 
@@ -475,46 +569,66 @@ __device__ __forceinline__ bool run_decoder_front(const MoeParams& p, const Ctx&
   float* red = reinterpret_cast<float*>(smem);
   const DecCounts n = dec_counts(p, c);
   auto first = [&]() { return first_of(w, off, G); };
-  auto done = [&](uint32_t* ev, uint32_t target) {
+  // per-task trace (when asked for): before the wait, after it, after the
+  // body; the record itself is written after the notify
+  const bool tr = p.trace != nullptr;
+  uint64_t tw = 0, ts = 0, tb = 0;
+  auto t_wait = [&]() { if (tr) tw = now_ticks(); };
+  auto t_start = [&]() { if (tr) ts = now_ticks(); };
+  auto done = [&](uint32_t* ev, uint32_t target, int type, int i) {
+    if (tr) tb = now_ticks();
     wg_publish();
     if (threadIdx.x == 0) notify1(c, ev, target);
+    trace_task(p, type, i, 0, tw, ts, tb);
   };
   for (int i = first(); i < n.nN; i += G) {
+    t_wait();
+    t_start();
     task_norm1(p, c, i);
-    done(c.set + W_DEC_N1, (uint32_t)n.nN);
+    done(c.set + W_DEC_N1, (uint32_t)n.nN, TT_DN1, i);
   }
   off += n.nN;
   for (int i = first(); i < n.nQKV; i += G) {
+    t_wait();
     if (!wg_wait(c.set + W_DEC_N1, (uint32_t)n.nN, c.status, c.budget)) return false;
+    t_start();
     task_qkv(p, c, i, red);
-    done(c.set + W_DEC_QKV, (uint32_t)n.nQKV);
+    done(c.set + W_DEC_QKV, (uint32_t)n.nQKV, TT_DQKV, i);
   }
   off += n.nQKV;
   for (int i = first(); i < n.nATT; i += G) {
-    if (!wg_wait(c.set + W_DEC_QKV, (uint32_t)n.nQKV, c.status, c.budget)) return false;
+    t_wait();
     const int t = i / (p.nkv * p.nchunk), g = (i / p.nchunk) % p.nkv, ch = i % p.nchunk;
+    if (!wg_wait(c.set + W_DEC_QKV, (uint32_t)n.nQKV, c.status, c.budget)) return false;
+    t_start();
     task_attn(p, c, t, g, ch, red);
-    done(c.set + p.o_ev_att + (int64_t)(t * p.nkv + g) * kEvStride, (uint32_t)p.nchunk);
+    done(c.set + p.o_ev_att + (int64_t)(t * p.nkv + g) * kEvStride, (uint32_t)p.nchunk, TT_DATT, i);
   }
   off += n.nATT;
   for (int i = first(); i < n.nATTC; i += G) {
+    t_wait();
     if (!wg_wait(c.set + W_DEC_QKV, (uint32_t)n.nQKV, c.status, c.budget)) return false;
     if (p.nchunk > 0 && !wg_wait(c.set + p.o_ev_att + (int64_t)i * kEvStride, (uint32_t)p.nchunk, c.status, c.budget))
       return false;
+    t_start();
     task_attn_merge(p, c, i / p.nkv, i % p.nkv);
-    done(c.set + W_DEC_ATTC, (uint32_t)n.nATTC);
+    done(c.set + W_DEC_ATTC, (uint32_t)n.nATTC, TT_DATTC, i);
   }
   off += n.nATTC;
   for (int i = first(); i < n.nO; i += G) {
+    t_wait();
     if (!wg_wait(c.set + W_DEC_ATTC, (uint32_t)n.nATTC, c.status, c.budget)) return false;
+    t_start();
     task_oproj(p, c, i / kDecOSplit, i % kDecOSplit, red);
-    done(c.set + W_DEC_O, (uint32_t)n.nO);
+    done(c.set + W_DEC_O, (uint32_t)n.nO, TT_DO, i);
   }
   off += n.nO;
   for (int i = first(); i < n.nN; i += G) {
+    t_wait();
     if (!wg_wait(c.set + W_DEC_O, (uint32_t)n.nO, c.status, c.budget)) return false;
+    t_start();
     task_norm2(p, c, i);
-    done(c.set + W_DEC_N2, (uint32_t)n.nN);
+    done(c.set + W_DEC_N2, (uint32_t)n.nN, TT_DN2, i);
   }
   off += n.nN;
   return true;

@@ -45,7 +45,9 @@ constexpr uint32_t kDefaultWatchdogUs = 2000000u;
 // task types (the dynamic schedule's queue descriptors carry them in their
 // top three bits, dyn_sched.h; 0 = empty slot)
 enum TaskType : int { TT_R = 1, TT_K = 2, TT_S = 3, TT_D = 4, TT_G1 = 5, TT_G2 = 6, TT_C = 7,
-                      TT_L = 8 /* trace only: a workgroup's LDS routing tables */ };
+                      TT_L = 8 /* trace only: a workgroup's LDS routing tables */,
+                      // trace only: the decoder layer's attention-block tasks
+                      TT_DN1 = 9, TT_DQKV = 10, TT_DATT = 11, TT_DATTC = 12, TT_DO = 13, TT_DN2 = 14 };
 static_assert(dyn::T_R == TT_R && dyn::T_K == TT_K && dyn::T_S == TT_S && dyn::T_G1 == TT_G1 &&
                   dyn::T_G2 == TT_G2 && dyn::T_C == TT_C,
               "the dynamic runner's task types are the kernels' task types");
@@ -107,7 +109,7 @@ constexpr int kDecMaxT = 16;     // tokens a launch takes (one 16-row MFMA block
 constexpr int kDecHd = 128;      // head size
 constexpr int kDecChunk = 256;   // cache entries per attention task
 constexpr int kDecOSplit = 4;    // K split of the output projection
-constexpr int kDecNormT = 4;     // tokens per RMSNorm task (one a wave)
+constexpr int kDecNormT = 1;     // tokens per RMSNorm task (the four waves split H)
 constexpr int kDecMaxGroup = 8;  // query heads per key/value head
 
 // Decoder buffers, appended to the MoE workspace.

@@ -2409,7 +2409,7 @@ __global__ void __launch_bounds__(kThreads) kd_qkv(MoeParams p) {
   task_qkv(p, c, blockIdx.x, red);
 }
 __global__ void __launch_bounds__(kThreads) kd_attn(MoeParams p) {
-  __shared__ float lds[16 * kDecChunk + 64 + 32];
+  __shared__ float lds[kAttnLdsFloats];
   const Ctx c = make_ctx(p, nullptr);
   const int i = blockIdx.x;
   task_attn(p, c, i / (p.nkv * p.nchunk), (i / p.nchunk) % p.nkv, i % p.nchunk, lds);
