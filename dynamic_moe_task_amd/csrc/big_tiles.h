@@ -197,7 +197,7 @@ __device__ __forceinline__ void big_body(const MoeParams& p, const Ctx& c, const
             for (int v = 0; v < 16; ++v) {
               const float g = acc[b][n][v], u = acc[b][n + 2][v];
               const int row = 32 * b + 8 * (v >> 2) + 4 * kh + (v & 3), col = wc * 64 + 32 * n + l32;
-              st[row * SW + col] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u);
+              st[row * SW + col] = (uint16_t)f2bf_int(g / (1.0f + __expf(-g)) * u);
             }
         } else {
 #pragma unroll
@@ -205,7 +205,7 @@ __device__ __forceinline__ void big_body(const MoeParams& p, const Ctx& c, const
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
               const int row = 32 * b + 8 * (v >> 2) + 4 * kh + (v & 3), col = wc * 128 + 32 * n + l32;
-              st[row * SW + col] = (uint16_t)f2bf(acc[b][n][v]);
+              st[row * SW + col] = (uint16_t)f2bf_int(acc[b][n][v]);
             }
         }
       }

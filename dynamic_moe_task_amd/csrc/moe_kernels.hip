@@ -52,6 +52,16 @@ enum Mode : int { MODE_STATIC = ETC_SCHED_STATIC, MODE_DYNAMIC = ETC_SCHED_DYNAM
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 __device__ __forceinline__ uint32_t f2bf(float f) {
+  // fp32 -> bf16, round to nearest even: gfx950's conversion instruction
+  // (v_cvt_pk_bf16_f32).  For every non-NaN fp32 value it gives the same
+  // bits as (u + 0x7fff + ((u >> 16) & 1)) >> 16 on the value's bits u
+  // (checked on MI355X over all 2^32 patterns); a NaN stays a quiet NaN.
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// The same rounding in integer arithmetic (the big tiles' epilogue, whose
+// kernels sit at the register file's limit: the conversion instruction's
+// pairing of values there costs registers).
+__device__ __forceinline__ uint32_t f2bf_int(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
   u += 0x7fffu + ((u >> 16) & 1u);
