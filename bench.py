@@ -409,7 +409,7 @@ def measure_token_counts(Wr, w13s, w2s, sp, steps, warmup, repeat, counts=(1, 12
     return out
 
 
-def measure_dense_mlps(sp, steps, warmup, repeat, which=None):
+def measure_dense_mlps(sp, steps, warmup, repeat, which=None, trace=""):
     """The dense MLPs of the pages' appendix table (S = 8192 tokens) run
     through the MoE path as one expert (E = 1, k = 1): the big-tile grouped
     GEMM with full 256-row tiles.  µs per layer (ORDERED and kernel by
@@ -435,6 +435,10 @@ def measure_dense_mlps(sp, steps, warmup, repeat, which=None):
             us = float(np.median([time_sched(bufs, shape.T, sched, steps, warmup, [W13], [Wd], sp)
                                   for _ in range(repeat)]))
             row["us_per_layer"][sched] = round(us, 1)
+        if trace:
+            khz = B.moe_layer_info(desc).wall_clock_khz
+            base = os.path.splitext(trace)[0]
+            row["trace_ordered"] = trace_summary(bufs, shape.T, "ordered", khz, sp, dump=f"{base}_mlp{i + 1}.npz")
         best = min(row["us_per_layer"].values())
         row["tflops"] = round(flops / (best * 1e-6) / 1e12, 1)
         row["mfma_frac"] = round(flops / (best * 1e-6) / (BF16_PEAK_TFS * 1e12), 4)
@@ -546,7 +550,7 @@ def main():
         torch.cuda.set_device(0)
         sp = torch.cuda.current_stream().cuda_stream
         which = {int(v) for v in a.mlps.split(",")} if a.mlps else None
-        print(json.dumps(measure_dense_mlps(sp, a.steps, a.warmup, a.repeat, which)), flush=True)
+        print(json.dumps(measure_dense_mlps(sp, a.steps, a.warmup, a.repeat, which, a.trace)), flush=True)
         return
     if a.workload in ("decoder", "tokens"):
         import torch

@@ -231,6 +231,14 @@ __device__ __forceinline__ bool notify1(const Ctx& c, uint32_t* ev, uint32_t tar
   return old + 1u == target;
 }
 
+// n arrivals at once (a workgroup's batch of tasks); true when they complete
+// the event.
+__device__ __forceinline__ bool notify_n(const Ctx& c, uint32_t* ev, uint32_t n, uint32_t target) {
+  const uint32_t old = add_relaxed(ev, n);
+  if (old + n > target) or_relaxed(c.status, ST_OVER_NOTIFY | ST_ABORT);
+  return old + n == target;
+}
+
 // Notify without checking for over-notification unless the debug buffer is
 // set (then notify1 records any notify past the wait count).
 __device__ __forceinline__ void notify_fast(const MoeParams& p, const Ctx& c, uint32_t* ev, uint32_t target) {
@@ -491,7 +499,11 @@ __device__ __forceinline__ float wave_max(float x) {
   x = dpp_max_step<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
-__device__ __forceinline__ void task_topk(const MoeParams& p, const Ctx& c, int tt) {
+// hist: when given (a workgroup's stream of top-k tasks), the expert-event
+// arrivals are counted there, in LDS, and notified by the caller once for
+// the whole stream (one atomic per expert instead of one per routed pair:
+// with few experts, all T*k pairs would otherwise hit the same counters).
+__device__ __forceinline__ void task_topk(const MoeParams& p, const Ctx& c, int tt, int* hist = nullptr) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = tt * kRouterT + wv;
   if (t >= c.T) return;
@@ -552,7 +564,10 @@ __device__ __forceinline__ void task_topk(const MoeParams& p, const Ctx& c, int 
     // (G1 reads x, an input, and S's tables, ordered by S's own event), so
     // the notify needs no drain.
     if (c.set) {
-      notify_fast(p, c, ev_exp(p, c, my_e), 0xffffffffu);
+      if (hist)
+        atomicAdd(hist + my_e, 1);
+      else
+        notify_fast(p, c, ev_exp(p, c, my_e), 0xffffffffu);
       if (p.debug) atomicAdd(p.debug + my_e, 1);
     }
   }
@@ -1463,10 +1478,106 @@ __device__ __forceinline__ void task_g2(const MoeParams& p, const Ctx& c, const 
 // C: out[t, :] = bf16(sum_j w[t, j] * Y[slot[t*k+j], :]), fp32 in j order.
 // The task's (weight, slot) pairs are staged in LDS first; then each thread
 // issues the loads of all k expert rows of its chunk before the arithmetic.
+// The weighted sums of a list of ntok tokens: tok(n) gives list entry n's
+// token (or -1 past the end), s_pair[2 (n k + j)] and [2 (n k + j) + 1]
+// the weight and grouped row of its j-th routed row.  IB items (entry,
+// 8-column chunk) a thread at a time, JB of each item's k rows requested
+// together: IB * JB = 8 row loads in flight (one item of 8 rows for k >= 8,
+// eight items of one row for k = 1; combine_items picks by k).  Each item
+// sums its rows in ascending slot order.
+template <int IB, int JB, class Tok>
+__device__ __forceinline__ void combine_items_t(const MoeParams& p, const Ctx& c, int ntok, Tok tok, const int* s_pair) {
+  const int cpr = c.H >> 3;
+  const int k = c.k;
+  const rsrc_t ry = r_y(p);
+  const int nit = ntok * cpr;
+  for (int i0 = threadIdx.x; i0 < nit; i0 += IB * kThreads) {
+    int r[IB], ch[IB], t[IB];
+    bool ok[IB];
+    float acc[IB][8];
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      const int idx = i0 + b * kThreads;
+      const int ii = idx < nit ? idx : i0;
+      r[b] = ii / cpr;
+      ch[b] = ii - r[b] * cpr;
+      t[b] = tok(r[b]);
+      ok[b] = idx < nit && t[b] >= 0;
+      if (!ok[b]) {  // a valid row and chunk to read (nothing is stored)
+        r[b] = 0;
+        ch[b] = 0;
+        t[b] = tok(0);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[b][q] = 0.f;
+    }
+    // Every lane loads (items past the end read entry 0's rows, whose pairs
+    // are valid), so that only the uniform row-count test guards the
+    // loads: a per-lane test there costs a branch and a wait per load.
+    u32x4_t rvv[IB];
+    if (p.resid) {
+      // decoder layer: the residual stream's rows go out with the first loads
+      const rsrc_t rr = make_rsrc(p.resid, p.resid_bytes);
+#pragma unroll
+      for (int b = 0; b < IB; ++b) rvv[b] = co_ld128(rr, (uint32_t)(((size_t)t[b] * c.H + ch[b] * 8) * 2));
+    }
+    for (int j0 = 0; j0 < k; j0 += JB) {
+      u32x4_t yv[IB][JB];
+#pragma unroll
+      for (int b = 0; b < IB; ++b)
+#pragma unroll
+        for (int u = 0; u < JB; ++u)
+          if (j0 + u < k)
+            yv[b][u] = co_ld128(ry, (uint32_t)(((size_t)s_pair[2 * (r[b] * k + j0 + u) + 1] * c.H + ch[b] * 8) * 2));
+#pragma unroll
+      for (int b = 0; b < IB; ++b)
+#pragma unroll
+        for (int u = 0; u < JB; ++u) {
+          if (j0 + u < k) {
+            const float wj = __int_as_float(s_pair[2 * (r[b] * k + j0 + u)]);
+            float yf[8];
+            unpack8(yv[b][u], yf);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[b][q] = __builtin_fmaf(wj, yf[q], acc[b][q]);
+          }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      if (!ok[b]) continue;
+      if (p.resid) {
+        // decoder layer: out = bf16(x2 + bf16(MoE sum)), x2 the residual stream
+        float rv[8];
+        unpack8(rvv[b], rv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[b][q] = rv[q] + __uint_as_float(f2bf(acc[b][q]) << 16);
+      }
+      u32x4_t o;
+      o.x = f2bf(acc[b][0]) | (f2bf(acc[b][1]) << 16);
+      o.y = f2bf(acc[b][2]) | (f2bf(acc[b][3]) << 16);
+      o.z = f2bf(acc[b][4]) | (f2bf(acc[b][5]) << 16);
+      o.w = f2bf(acc[b][6]) | (f2bf(acc[b][7]) << 16);
+      st4(p.out + (size_t)t[b] * c.H + ch[b] * 8, o);
+    }
+  }
+}
+template <class Tok>
+__device__ __forceinline__ void combine_items(const MoeParams& p, const Ctx& c, int ntok, Tok tok, const int* s_pair) {
+  if (c.k >= 8)
+    combine_items_t<1, 8>(p, c, ntok, tok, s_pair);
+  else if (c.k >= 4)
+    combine_items_t<2, 4>(p, c, ntok, tok, s_pair);
+  else if (c.k >= 2)
+    combine_items_t<4, 2>(p, c, ntok, tok, s_pair);
+  else
+    combine_items_t<8, 1>(p, c, ntok, tok, s_pair);
+}
+
+// C(ct): tokens ct * kCombineT .. + kCombineT - 1.  Their (weight, slot)
+// pairs go to s_pair first, unless the caller has staged them.
 __device__ __forceinline__ void task_combine(const MoeParams& p, const Ctx& c, int ct, int* s_pair, bool staged = false) {
   const int t0 = ct * kCombineT;
   const int ntok = min(kCombineT, c.T - t0);
-  const int cpr = c.H >> 3;
   const int k = c.k;
   if (!staged && threadIdx.x < ntok * k) {
     const uint32_t fo = (uint32_t)(t0 * k + threadIdx.x) * 4u;
@@ -1474,42 +1585,7 @@ __device__ __forceinline__ void task_combine(const MoeParams& p, const Ctx& c, i
     s_pair[2 * threadIdx.x + 1] = (int)co_ld32(r_slot(p), fo);
   }
   __syncthreads();
-  const rsrc_t ry = r_y(p);
-  for (int i = threadIdx.x; i < ntok * cpr; i += kThreads) {
-    const int r = i / cpr, ch = i - r * cpr;
-    const int t = t0 + r;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < k; j0 += 8) {
-      u32x4_t yv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (j0 + u < k)
-          yv[u] = co_ld128(ry, (uint32_t)(((size_t)s_pair[2 * (r * k + j0 + u) + 1] * c.H + ch * 8) * 2));
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (j0 + u < k) {
-          const float wj = __int_as_float(s_pair[2 * (r * k + j0 + u)]);
-          float yf[8];
-          unpack8(yv[u], yf);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj, yf[q], acc[q]);
-        }
-      }
-    }
-    if (p.resid) {
-      // decoder layer: out = bf16(x2 + bf16(MoE sum)), x2 the residual stream
-      float rv[8];
-      unpack8(co_ld128(make_rsrc(p.resid, p.resid_bytes), (uint32_t)(((size_t)t * c.H + ch * 8) * 2)), rv);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = rv[q] + __uint_as_float(f2bf(acc[q]) << 16);
-    }
-    u32x4_t o;
-    o.x = f2bf(acc[0]) | (f2bf(acc[1]) << 16);
-    o.y = f2bf(acc[2]) | (f2bf(acc[3]) << 16);
-    o.z = f2bf(acc[4]) | (f2bf(acc[5]) << 16);
-    o.w = f2bf(acc[6]) | (f2bf(acc[7]) << 16);
-    st4(p.out + (size_t)t * c.H + ch * 8, o);
-  }
+  combine_items(p, c, ntok, [&](int n) { return t0 + n; }, s_pair);
 }
 
 #include "decoder_tasks.h"
@@ -1625,6 +1701,55 @@ __device__ __forceinline__ bool wait_rows_done(const MoeParams& p, const Ctx& c,
   }
   fail = __syncthreads_or(fail);
   return fail == 0;
+}
+
+// Large batches: a workgroup's combine tasks c0, c0 + G, ..., c0 + (n-1) G
+// as one stream (n kCombineT k <= kThreads routed rows).  Thread q takes
+// routed row q (task q / (kCombineT k), then its token and slot), stages
+// its (weight, slot) pair in s_pair[2 q .. 2 q + 1] and polls its row
+// tile's ev_y, all threads at once; then one item loop covers every token
+// of the stream.  Returns false when a wait gave up (uniform).
+__device__ __forceinline__ bool combine_stream(const MoeParams& p, const Ctx& c, int c0, int G, int n, int* s_pair) {
+  const int k = c.k, per = kCombineT * k;
+  int fail = 0;
+  {
+    const int q = threadIdx.x;
+    const int m = q / per, loc = q - m * per;
+    const int t = (c0 + m * G) * kCombineT + loc / k;
+    const bool mine = q < n * per && t < c.T;
+    uint32_t* ctr = ev_y(p, c, 0);
+    if (mine) {
+      const uint32_t fo = (uint32_t)(t * k + loc % k) * 4u;
+      const uint32_t sl = co_ld32(r_slot(p), fo);
+      s_pair[2 * q] = (int)co_ld32(r_topw(p), fo);
+      s_pair[2 * q + 1] = (int)sl;
+      ctr = ev_y(p, c, (int)co_ld32(r_rowrt(p), sl * 4u));
+    } else if (q < n * per) {  // a token past T: a valid row that is never stored
+      s_pair[2 * q] = 0;
+      s_pair[2 * q + 1] = 0;
+    }
+    const uint32_t tgt = (uint32_t)c.nN2;
+    const uint64_t t_start = now_ticks();
+    for (uint32_t spins = 1;; ++spins) {
+      const bool ok = !mine || ld_relaxed(ctr) >= tgt;
+      if (__all(ok)) break;
+      if ((spins & 7u) == 0u) {
+        if (ld_relaxed(c.status) & ST_ABORT) { fail = 1; break; }
+        if (now_ticks() - t_start > c.budget) {
+          if ((threadIdx.x & 63) == 0) or_relaxed(c.status, ST_TIMEOUT | ST_ABORT);
+          fail = 1;
+          break;
+        }
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  if (__syncthreads_or(fail)) return false;
+  combine_items(p, c, n * kCombineT, [&](int e) {
+    const int t = (c0 + (e / kCombineT) * G) * kCombineT + e % kCombineT;
+    return t < c.T ? t : -1;
+  }, s_pair);
+  return true;
 }
 
 // Row tile and column tile of G task i (of nrt row tiles x nn column tiles):
@@ -2052,15 +2177,59 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   }
   off += c.nR;
   if (!EV && !grid_barrier(c, G, bar)) return;
-  for (int i = first_of(w, off, G); i < c.nK; i += G) {
+  // Large batches: a workgroup's top-k tasks as one stream.  Wave 0 polls
+  // all of their logit events at once (a lane each), the tasks run back to
+  // back, and one drain and one notify of the whole count follow (top-k
+  // tasks notify nothing else that waits on their stores).
+  const int k0 = first_of(w, off, G);
+  const int nmine = k0 < c.nK ? (c.nK - k0 + G - 1) / G : 0;
+  if (EV && WG != kVarSmall && nmine > 1 && nmine <= 64) {
     if (tr) tw = now_ticks();
-    if (EV && !wg_wait(ev_logit(p, c, i), (uint32_t)c.nET, c.status, c.budget)) return;
+    int fail = 0;
+    if (threadIdx.x < 64) {
+      const bool mine = (int)threadIdx.x < nmine;
+      const uint32_t* ctr = ev_logit(p, c, mine ? k0 + (int)threadIdx.x * G : k0);
+      const uint64_t t0 = now_ticks();
+      for (uint32_t spins = 1;; ++spins) {
+        const bool ok = !mine || ld_relaxed(ctr) >= (uint32_t)c.nET;
+        if (__all(ok)) break;
+        if ((spins & 7u) == 0u) {
+          if (ld_relaxed(c.status) & ST_ABORT) { fail = 1; break; }
+          if (now_ticks() - t0 > c.budget) {
+            if (threadIdx.x == 0) or_relaxed(c.status, ST_TIMEOUT | ST_ABORT);
+            fail = 1;
+            break;
+          }
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __shared__ int khist[kMaxE];
+    for (int e = threadIdx.x; e < c.E; e += kThreads) khist[e] = 0;
+    if (__syncthreads_or(fail)) return;
     if (tr) ts = now_ticks();
-    task_topk(p, c, i);
+    for (int i = k0; i < c.nK; i += G) {
+      task_topk(p, c, i, khist);
+      dbg_task(p, TT_K);
+    }
     if (tr) tb = now_ticks();
-    dbg_task(p, TT_K);
-    after_topk<MODE>(p, c);
-    trace_task(p, TT_K, i, 0, tw, ts, tb);
+    __syncthreads();  // every task's LDS counts are in
+    for (int e = threadIdx.x; e < c.E; e += kThreads)
+      if (khist[e]) (void)add_relaxed(ev_exp(p, c, e), (uint32_t)khist[e]);
+    wg_publish();
+    if (threadIdx.x == 0) notify_n(c, c.set + W_EV_ROUTE, (uint32_t)nmine, (uint32_t)c.nK);
+    trace_task(p, TT_K, k0, nmine, tw, ts, tb);
+  } else {
+    for (int i = k0; i < c.nK; i += G) {
+      if (tr) tw = now_ticks();
+      if (EV && !wg_wait(ev_logit(p, c, i), (uint32_t)c.nET, c.status, c.budget)) return;
+      if (tr) ts = now_ticks();
+      task_topk(p, c, i);
+      if (tr) tb = now_ticks();
+      dbg_task(p, TT_K);
+      after_topk<MODE>(p, c);
+      trace_task(p, TT_K, i, 0, tw, ts, tb);
+    }
   }
   off += c.nK;
   if (!EV && !grid_barrier(c, G, bar)) return;
@@ -2198,6 +2367,19 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   }
   // C reads S's routing outputs (slot, row -> tile map)
   if (local && first_of(w, off, Gt) < c.nC && !wg_wait(c.set + W_EV_SCAN, 1u, c.status, c.budget)) return;
+  {
+    const int c0 = first_of(w, off, Gt);
+    const int nmine = c0 < c.nC ? (c.nC - c0 + Gt - 1) / Gt : 0;
+    if (EV && WG != kVarSmall && nmine > 1 && nmine * kCombineT * c.k <= kThreads) {
+      __shared__ int s_cpairs[2 * kThreads];
+      if (tr) tw = now_ticks();
+      if (!combine_stream(p, c, c0, Gt, nmine, s_cpairs)) return;
+      if (tr) ts = tb = now_ticks();
+      for (int i = c0; i < c.nC; i += Gt) dbg_task(p, TT_C);
+      trace_task(p, TT_C, c0, nmine, tw, tw, ts);
+      return;
+    }
+  }
   for (int i = first_of(w, off, Gt); i < c.nC; i += Gt) {
     // wave 0 fills sh.pairs for this task (in the wait, or in the combine)
     // while the other waves may still read the previous task's pairs
