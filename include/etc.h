@@ -319,13 +319,14 @@ int moe_layer_launch(const etc_moe_desc* desc, int32_t T, const etc_moe_args* ar
  * attention block, then the MoE block, each with its residual add [the
  * pages evaluate the MoE layer inside end-to-end serving, Fig. 14; the
  * layer's steps are the textbook pre-norm block]:
- *   h1 = RMSNorm(x) * g1                       N1 tasks (4 tokens each)
+ *   h1 = RMSNorm(x) * g1                       N1 tasks (one token each)
  *   q, k, v = h1 Wqkv^T; RoPE on q and k at position pos; k, v written into
  *            the caches at index pos           QKV tasks (16 columns each)
  *   o = softmax(q k^T / sqrt(d)) v over cache entries 0..pos, query head h
- *       reading key/value head h / (n_q / n_kv)   attention tasks (512 cache
+ *       reading key/value head h / (n_q / n_kv)   attention tasks (256 cache
  *            entries of one token and one kv head each), then merge tasks
  *   x2 = x + o Wo^T                            projection tasks, N2 tasks
+ *                                              (one token each)
  *   out = x2 + MoE(RMSNorm(x2) * g2)           the MoE layer's tasks, its
  *            router waiting on the N2 tasks' event
  * Every activation is stored bf16, sums are fp32.  Each phase notifies an
