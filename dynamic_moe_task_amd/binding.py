@@ -40,7 +40,7 @@ EXPORTED = [
     "etensor_create", "etensor_instantiate", "etensor_shape", "etensor_destroy",
     "etc_edge_compile", "etc_edge_index", "etc_splitk_launch", "moe_layer_info", "moe_layer_workspace_size", "moe_workspace_init",
     "moe_layer_launch", "moe_layer_launch_noalloc", "decoder_layer_workspace_size", "decoder_workspace_init",
-    "decoder_layer_launch", "etc_sync", "etc_last_error",
+    "decoder_layer_launch", "etc_coherence_selftest_bytes", "etc_coherence_selftest", "etc_sync", "etc_last_error",
 ]
 
 
@@ -164,6 +164,9 @@ def lib():
         L.decoder_layer_launch.argtypes = [ctypes.POINTER(DecoderDesc), I32, I32, ctypes.POINTER(DecoderArgs),
                                            ctypes.c_int, P]
         L.etc_sync.argtypes = [P]
+        L.etc_coherence_selftest_bytes.argtypes = [I32]
+        L.etc_coherence_selftest_bytes.restype = ctypes.c_size_t
+        L.etc_coherence_selftest.argtypes = [I32, I32, P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint32), P]
         L.etc_last_error.argtypes = []
         L.etc_last_error.restype = ctypes.c_char_p
         for name in ["etensor_create", "etensor_instantiate", "etensor_shape", "etensor_destroy",
@@ -279,6 +282,18 @@ def decoder_layer_launch(desc: DecoderDesc, T: int, pos: int, args: DecoderArgs,
 
 def etc_sync(stream) -> int:
     return lib().etc_sync(stream)
+
+
+def etc_coherence_selftest_bytes(pairs: int) -> int:
+    return int(lib().etc_coherence_selftest_bytes(pairs))
+
+
+def etc_coherence_selftest(pairs: int, rounds: int, workspace_ptr: int, workspace_bytes: int, stream) -> tuple:
+    """Runs the cross-workgroup message-passing self-test; returns
+    (words read wrong, wait gave up) from the library's result words."""
+    res = (ctypes.c_uint32 * 2)()
+    check(lib().etc_coherence_selftest(pairs, rounds, workspace_ptr, workspace_bytes, res, stream))
+    return int(res[0]), int(res[1])
 
 
 @dataclass

@@ -729,6 +729,40 @@ extern "C" int decoder_layer_launch(const etc_decoder_desc* dd, int32_t T, int32
                       da->moe.workspace_bytes, dd, pos, da);
 }
 
+// ==================================================== coherence self-test ==
+extern "C" size_t etc_coherence_selftest_bytes(int32_t pairs) {
+  if (pairs < 1 || pairs > kSelftestMaxPairs) return 0;
+  return coherence_selftest_words(pairs) * 4;
+}
+
+extern "C" int etc_coherence_selftest(int32_t pairs, int32_t rounds, void* workspace, size_t workspace_bytes,
+                                      uint32_t* result, void* stream) {
+  if (pairs < 1 || pairs > kSelftestMaxPairs) return fail(ETC_ERR_INVALID, "pairs %d outside [1, %d]", pairs, kSelftestMaxPairs);
+  if (rounds < 1 || rounds > (1 << 20)) return fail(ETC_ERR_INVALID, "rounds %d outside [1, 2^20]", rounds);
+  if (!workspace || !aligned16(workspace)) return fail(ETC_ERR_INVALID, "workspace NULL or not 16-byte aligned");
+  if (workspace_bytes < coherence_selftest_words(pairs) * 4)
+    return fail(ETC_ERR_INVALID, "workspace %zu bytes, need %zu", workspace_bytes, coherence_selftest_words(pairs) * 4);
+  if (!result) return fail(ETC_ERR_INVALID, "result is NULL");
+  // every pair's two workgroups must be resident together
+  int cus = 0, nb = 0;
+  int rc = device_cus(&cus);
+  if (rc) return rc;
+  hipError_t e = (hipError_t)coherence_selftest_occupancy(&nb);
+  if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  if ((int64_t)2 * pairs > (int64_t)nb * cus)
+    return fail(ETC_ERR_INVALID, "%d pairs do not fit at once (%d workgroups a CU, %d CUs)", pairs, nb, cus);
+  uint64_t ticks = 0;
+  rc = watchdog_ticks(0, &ticks);
+  if (rc) return rc;
+  e = (hipError_t)launch_coherence_selftest(static_cast<uint32_t*>(workspace), pairs, rounds, ticks, stream);
+  if (e != hipSuccess) return hip_fail(e, "coherence self-test launch");
+  e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  e = hipMemcpy(result, workspace, 2 * sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  return ETC_OK;
+}
+
 extern "C" int etc_sync(void* stream) {
   hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");

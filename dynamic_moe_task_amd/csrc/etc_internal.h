@@ -28,6 +28,7 @@ static_assert(ST_TIMEOUT == dyn::kStTimeout && ST_OVER_NOTIFY == dyn::kStOverNot
               "one status word, one set of bits");
 
 constexpr int kEvStride = 32;   // words between event elements (one 128-byte line each)
+constexpr int kSelftestMaxPairs = 1024;  // coherence self-test: producer/consumer pairs at most
 constexpr int kMaxK = 16;
 constexpr int kMaxE = 256;
 constexpr int kMaxTmax = 16384;
@@ -258,6 +259,12 @@ int moe_scratch_clear(void* ptr, size_t bytes, void* stream);
 int launch_moe_persistent(const MoeParams& p, int sched, int grid, int lds_bytes, void* stream);
 int launch_moe_kbk(const MoeParams& p, int lds_bytes, void* stream);
 int launch_decoder_kbk(const MoeParams& p, int lds_bytes, void* stream);
+// The coherence self-test (moe_kernels.hip): its workspace words for
+// `pairs` producer/consumer pairs, and the launch (a fill kernel zeroes the
+// workspace first).
+size_t coherence_selftest_words(int pairs);
+int launch_coherence_selftest(uint32_t* ws, int pairs, int rounds, uint64_t budget, void* stream);
+int coherence_selftest_occupancy(int* blocks_per_cu);
 // occupancy queries of the decoder-layer variants: kDecSchedBase + sched
 constexpr int kDecSchedBase = 16;
 // occupancy queries of the big-tile variant: kBigSchedBase + sched

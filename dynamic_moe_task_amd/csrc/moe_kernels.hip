@@ -2806,4 +2806,61 @@ int moe_scratch_clear(void* ptr, size_t bytes, void* stream) {
   return (int)hipGetLastError();
 }
 
+// ------------------------------------------- coherence self-test --
+// Message passing between workgroups on different XCDs with exactly the
+// protocol every notify and wait of the kernels relies on (no fences):
+// the producer writes a 4 KB message with device-coherent stores, every
+// wave waits for its stores, a workgroup barrier, then thread 0's relaxed
+// device-scope atomic add; the consumer's thread 0 polls the counter with
+// relaxed device-scope loads, a workgroup barrier, then device-coherent
+// loads of the message, every word checked.  The consumer acknowledges
+// each round the same way before the producer writes the next.  Workgroup
+// 2 i produces for workgroup 2 i + 1 (consecutive workgroups are dealt to
+// different XCDs).  Every wait has the watchdog, so the grid always drains.
+// Words: ws[0] mismatched words, ws[1] timed-out waits; then per pair a
+// ready and an ack counter on lines of their own, then the messages.
+constexpr int kSelftestWords = kThreads * 4;  // message words a pair
+__global__ void __launch_bounds__(kThreads) coherence_selftest(uint32_t* ws, int rounds, uint32_t msg_off,
+                                                               uint64_t budget) {
+  const int pair = blockIdx.x >> 1, role = blockIdx.x & 1, tid = threadIdx.x;
+  uint32_t* ready = ws + kEvStride * (1 + 2 * pair);
+  uint32_t* ack = ready + kEvStride;
+  const rsrc_t rm = make_rsrc(ws + msg_off + (size_t)pair * kSelftestWords, kSelftestWords * 4u);
+  uint32_t* status = ws + 1;  // a timeout sets it; every wait then gives up
+  uint32_t bad = 0;
+  for (int r = 1; r <= rounds; ++r) {
+    if (role == 0) {
+      if (r > 1 && !wg_wait(ack, (uint32_t)(r - 1), status, budget)) break;
+      const u32x4_t v = {(uint32_t)r, (uint32_t)r ^ (uint32_t)tid, (uint32_t)r * 7u + (uint32_t)tid, ~(uint32_t)r};
+      co_st128(rm, (uint32_t)tid * 16u, v);
+      wg_publish();
+      if (tid == 0) (void)add_relaxed(ready, 1u);
+    } else {
+      if (!wg_wait(ready, (uint32_t)r, status, budget)) break;
+      const u32x4_t v = co_ld128(rm, (uint32_t)tid * 16u);
+      bad += (v.x != (uint32_t)r) + (v.y != ((uint32_t)r ^ (uint32_t)tid)) +
+             (v.z != (uint32_t)r * 7u + (uint32_t)tid) + (v.w != ~(uint32_t)r);
+      __syncthreads();  // every thread has its message words before the ack
+      if (tid == 0) (void)add_relaxed(ack, 1u);
+    }
+  }
+  if (bad) atomicAdd(ws, bad);
+}
+
+int launch_coherence_selftest(uint32_t* ws, int pairs, int rounds, uint64_t budget, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t words = (size_t)kEvStride * (1 + 2 * pairs) + (size_t)pairs * kSelftestWords;
+  hipLaunchKernelGGL(fill_zero_u32, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, ws, words);
+  hipLaunchKernelGGL(coherence_selftest, dim3(2 * pairs), dim3(kThreads), 0, s, ws, rounds,
+                     (uint32_t)(kEvStride * (1 + 2 * pairs)), budget);
+  return (int)hipGetLastError();
+}
+int coherence_selftest_occupancy(int* blocks_per_cu) {
+  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, coherence_selftest, kThreads, 0);
+}
+size_t coherence_selftest_words(int pairs) {
+  return (size_t)kEvStride * (1 + 2 * pairs) + (size_t)pairs * kSelftestWords;
+}
+
+
 }  // namespace etc

@@ -404,6 +404,31 @@ int decoder_layer_launch(const etc_decoder_desc* desc, int32_t T, int32_t pos, c
 int moe_layer_launch_noalloc(const etc_moe_desc* desc, int32_t T, const etc_moe_args* args, int sched,
                              void* stream);
 
+/* ------------------------------------------------- coherence self-test -- */
+/* Every notify and wait of the kernels moves data between workgroups with
+ * the same protocol and no fences (an event is released by arrivals on its
+ * counter [Event Tensor pages, Fig. 7]; the data it guards must be visible
+ * to the waiter): the producer writes with device-coherent stores, waits for
+ * its stores, passes a workgroup barrier, then one thread adds to the
+ * counter with a relaxed device-scope atomic; the consumer polls the counter
+ * with relaxed device-scope loads, passes a barrier, then reads with
+ * device-coherent loads.  This self-test runs that protocol between `pairs`
+ * producer/consumer workgroup pairs placed on different XCDs, `rounds`
+ * messages of 4 KB each way with an acknowledgement per round, and checks
+ * every word the consumers read.
+ *   etc_coherence_selftest_bytes: device workspace the test needs (0 if
+ *            pairs is outside [1, 1024]).
+ *   workspace: caller-owned device memory of at least that size, 16-byte
+ *            aligned; zeroed by the call on `stream`.
+ *   result:  host pointer to 2 words: [0] message words read wrong, [1]
+ *            non-zero if a wait gave up (the watchdog); both 0 on success.
+ * Blocks until the test has run.  Errors: ETC_ERR_INVALID (ranges, NULL or
+ * misaligned pointers, a workspace too small, more pairs than fit on the
+ * GPU at once), ETC_ERR_HIP.                                               */
+size_t etc_coherence_selftest_bytes(int32_t pairs);
+int etc_coherence_selftest(int32_t pairs, int32_t rounds, void* workspace, size_t workspace_bytes,
+                           uint32_t* result, void* stream);
+
 /* Wait for `stream`, then report the first in-kernel error of every launch
  * made on it since the previous etc_sync (and clear it): ETC_OK,
  * ETC_ERR_TIMEOUT, ETC_ERR_INVARIANT, ETC_ERR_NONFINITE or ETC_ERR_HIP.

@@ -236,3 +236,15 @@ def test_dynamic_schedule_is_switched_off_with_an_error():
     args = B.MoeArgs(*([0x1000] * 13), 1 << 30, None, 0, 0, None)
     assert B.moe_layer_launch(d, 4, args, B.ETC_SCHED_DYNAMIC, None) == B.ETC_ERR_UNSUPPORTED
     assert "switched off" in B.etc_last_error()
+
+
+def test_coherence_selftest_validation_before_any_gpu_call():
+    # ranges and pointers are checked before the library touches the GPU
+    assert B.etc_coherence_selftest_bytes(0) == 0
+    assert B.etc_coherence_selftest_bytes(1025) == 0
+    assert B.etc_coherence_selftest_bytes(1) > 0
+    for pairs, rounds, ptr, nbytes in [(0, 1, 16, 1 << 20), (1, 0, 16, 1 << 20), (1, 1, 0, 1 << 20),
+                                       (1, 1, 8, 1 << 20), (1, 1, 16, 4)]:
+        with pytest.raises(B.EtcError) as ei:
+            B.etc_coherence_selftest(pairs, rounds, ptr, nbytes, None)
+        assert ei.value.code == B.ETC_ERR_INVALID
