@@ -1564,7 +1564,7 @@ __device__ __forceinline__ void combine_items_t(const MoeParams& p, const Ctx& c
 template <class Tok>
 __device__ __forceinline__ void combine_items(const MoeParams& p, const Ctx& c, int ntok, Tok tok, const int* s_pair) {
   if (c.k >= 8)
-    combine_items_t<1, 8>(p, c, ntok, tok, s_pair);
+    combine_items_t<2, 8>(p, c, ntok, tok, s_pair);
   else if (c.k >= 4)
     combine_items_t<2, 4>(p, c, ntok, tok, s_pair);
   else if (c.k >= 2)
@@ -2152,14 +2152,17 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   // pipelined stream, one drain, then the notifies of all of them
   bool streamed = false;
   if constexpr (WG == kVarBig) {
-    if (EV && router_experts(c.T) == kRouterEXL && c.T % kRouterT == 0 && c.E % kRouterEXL == 0 &&
-        (c.H >> 3) % (2 * 64) == 0) {
+    const int rx = router_experts(c.T);
+    if (EV && rx >= kRouterEL && c.T % kRouterT == 0 && c.E % rx == 0 && (c.H >> 3) % (2 * 64) == 0) {
       const int i0 = first_of(w, off, G);
       if (i0 < c.nR) {
         // one chunk a lane a step: two steps' operands and the unpacked
         // weights stay within the 256 VGPRs (two-chunk steps spilled into
         // the accumulation registers)
-        router_stream<kRouterEXL / 4, 1>(p, c, i0, G);
+        if (rx == kRouterEXL)
+          router_stream<kRouterEXL / 4, 1>(p, c, i0, G);
+        else
+          router_stream<kRouterEL / 4, 1>(p, c, i0, G);
         wg_publish();
         if (threadIdx.x == 0)
           for (int i = i0; i < c.nR; i += G) notify1(c, ev_logit(p, c, i / c.nET), (uint32_t)c.nET);

@@ -28,6 +28,7 @@ BIG = [
     (8192, 256, 1, 1, 256, True, False, 8192),    # one expert: 32 full tiles (the dense MLP)
     (4100, 256, 2, 2, 128, True, False, 4100),    # every token to both experts: 16 full tiles and one of 4 rows
     (1024, 768, 128, 8, 256, False, False, 1024), # 64 rows an expert, plain softmax weights, 3 G2 tiles
+    (1100, 1024, 32, 8, 128, True, True, 1100),   # 16-expert router tiles as one stream (H a multiple of 1024), bias
 ]
 
 _CACHE = {}
