@@ -92,7 +92,8 @@ def copy_calibration(mib, steps):
 
 
 TASK_NAMES = {1: "R", 2: "K", 3: "S", 4: "D", 5: "G1", 6: "G2", 7: "C", 8: "L",  # L: LDS routing tables
-              9: "N1", 10: "QKV", 11: "ATT", 12: "ATTC", 13: "O", 14: "N2"}  # the decoder's attention block
+              9: "N1", 10: "QKV", 11: "ATT", 12: "ATTC", 13: "O", 14: "N2",  # the decoder's attention block
+              15: "WG"}  # per workgroup: wait = entry to counter set known, body = task lists, notify = exit
 
 
 def tile_rows(counts, bm=64):

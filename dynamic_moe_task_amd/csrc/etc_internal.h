@@ -48,7 +48,11 @@ constexpr uint32_t kDefaultWatchdogUs = 2000000u;
 enum TaskType : int { TT_R = 1, TT_K = 2, TT_S = 3, TT_D = 4, TT_G1 = 5, TT_G2 = 6, TT_C = 7,
                       TT_L = 8 /* trace only: a workgroup's LDS routing tables */,
                       // trace only: the decoder layer's attention-block tasks
-                      TT_DN1 = 9, TT_DQKV = 10, TT_DATT = 11, TT_DATTC = 12, TT_DO = 13, TT_DN2 = 14 };
+                      TT_DN1 = 9, TT_DQKV = 10, TT_DATT = 11, TT_DATTC = 12, TT_DO = 13, TT_DN2 = 14,
+                      // trace only: one record a workgroup of the persistent kernel, stamped
+                      // at entry, once its counter set is known, after its task lists and
+                      // after its exit arrival
+                      TT_WG = 15 };
 static_assert(dyn::T_R == TT_R && dyn::T_K == TT_K && dyn::T_S == TT_S && dyn::T_G1 == TT_G1 &&
                   dyn::T_G2 == TT_G2 && dyn::T_C == TT_C,
               "the dynamic runner's task types are the kernels' task types");

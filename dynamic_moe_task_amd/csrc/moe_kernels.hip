@@ -2017,23 +2017,27 @@ __device__ __forceinline__ bool run_g_ordered(const MoeParams& p, const Ctx& c, 
 // gone idle (decode 169.3 us; 168.8 with this endgame).
 // One counter serves the whole grid, so the XCDs, which stream at somewhat
 // different rates, end together (with one counter per XCD group the groups
-// ended up to 6 us apart at decode).  Workgroup w's first two tiles are
-// dealt (w and G + w), so that the grid's first claims do not all meet on
+// ended up to 6 us apart at decode).  A workgroup's first two tiles are
+// dealt (d and G + d), so that the grid's first claims do not all meet on
 // that counter at once (claimed, they held the first G1 tile back by
-// 6 us); ordinal o of the counter is tile 2G + o.  Thread 0 hands a
+// 6 us); ordinal o of the counter is tile 2G + o.  d = w, except that the
+// workgroup that ran S and workgroup G - 1 swap: the one still busy with S
+// and its tables is dealt the last tile of each round, not an early G1
+// tile that later G2 tiles wait for (every workgroup's tiles still ascend,
+// and the dealt set is the same).  Thread 0 hands a
 // claim's result to the other threads through sk[0] and an LDS barrier.
 // Deadlock freedom as in run_g_ordered: a workgroup's tiles come in
 // ascending index order, every G1 tile below every G2 tile.
 template <int WG>
 __device__ __forceinline__ bool run_g_ordered_local(const MoeParams& p, const Ctx& c, float* red, const ClaimQ& q,
-                                                    int nG1, uint32_t* sk, const LocalRoute* lr) {
+                                                    int nG1, uint32_t* sk, const LocalRoute* lr, int d) {
   const int n = q.n;
   const bool tr = p.trace != nullptr;
   uint64_t tw = 0, ts = 0, tb = 0;
-  const int G = gridDim.x, w = blockIdx.x;
-  int cur = w < n ? w : n;
+  const int G = gridDim.x;
+  int cur = d < n ? d : n;
   if (cur >= n) return true;
-  int nxt = G + w < n ? G + w : n;  // the tile held after the running one (n: none)
+  int nxt = G + d < n ? G + d : n;  // the tile held after the running one (n: none)
   bool more = true;                 // the counter may still hand out tiles
   auto ev_of = [&](const GTask& t, const RowTile& r) -> uint32_t* {
     return t.g2 ? ev_h(p, c, t.rt) : ev_exp(p, c, r.e);
@@ -2164,8 +2168,10 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
         else
           router_stream<kRouterEL / 4, 1>(p, c, i0, G);
         wg_publish();
-        if (threadIdx.x == 0)
-          for (int i = i0; i < c.nR; i += G) notify1(c, ev_logit(p, c, i / c.nET), (uint32_t)c.nET);
+        // one thread a task: the arrivals leave together, not one round trip
+        // after another
+        for (int i = i0 + (int)threadIdx.x * G; i < c.nR; i += G * kThreads)
+          notify1(c, ev_logit(p, c, i / c.nET), (uint32_t)c.nET);
       }
       streamed = true;
     }
@@ -2328,7 +2334,10 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
   if (w >= Gt) return;
   if (MODE == MODE_ORDERED) {
     const ClaimQ q{c.set + W_CLAIM_G1 + grp * 32, grp, ngrp, nG1 + nG2, local ? 2 * G : 0};
-    if (lr ? !run_g_ordered_local<WG>(p, c, red, q, nG1, sh.claim, lr) : !run_g_ordered<WG>(p, c, red, q, nG1, sh.claim, lr))
+    const int s_wg = (int)((off - 1) % G);  // the workgroup that ran S (one task, the local tables' case)
+    const int d = w == s_wg ? G - 1 : (w == G - 1 ? s_wg : w);
+    if (lr ? !run_g_ordered_local<WG>(p, c, red, q, nG1, sh.claim, lr, d)
+           : !run_g_ordered<WG>(p, c, red, q, nG1, sh.claim, lr))
       return;
     off += nG1 + nG2;
   } else {
@@ -2460,6 +2469,8 @@ __device__ __forceinline__ void persistent_body(const MoeParams& p) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ Shared sh;
   __shared__ uint32_t s_epoch;
+  __shared__ uint64_t s_wgt[2];  // trace: entry, counter set known (kept out of the registers)
+  if (p.trace && threadIdx.x == 0) s_wgt[0] = now_ticks();
   if (threadIdx.x == 0) s_epoch = ld_relaxed(p.ctrl + C_EPOCH);
   trace_init(p);
   __syncthreads();
@@ -2470,6 +2481,7 @@ __device__ __forceinline__ void persistent_body(const MoeParams& p) {
        i += (int64_t)gridDim.x * kThreads)
     other[i] = 0u;
   Ctx c = make_ctx(p, set);
+  if (p.trace && threadIdx.x == 0) s_wgt[1] = now_ticks();
   {
     // task counts and tile widths of the variant this launch runs (the
     // small-batch variant holds neither the eight-experts-a-wave router tile
@@ -2504,6 +2516,7 @@ __device__ __forceinline__ void persistent_body(const MoeParams& p) {
   } else if (MODE != MODE_DYNAMIC) {
     run_lists<MODE, WG>(p, c, smem, sh);
   }
+  const uint64_t t_out = p.trace ? now_ticks() : 0;  // end of the task lists
   wg_publish();
   if (threadIdx.x == 0) {
     const uint32_t st = ld_relaxed(c.status) & ~ST_ABORT;
@@ -2511,6 +2524,7 @@ __device__ __forceinline__ void persistent_body(const MoeParams& p) {
     const uint32_t old = add_relaxed(set + W_DONE, 1u);
     if (old == gridDim.x - 1u) xchg_relaxed(p.ctrl + C_EPOCH, epoch + 1u);
   }
+  if (p.trace) trace_task(p, TT_WG, 0, 0, s_wgt[0], s_wgt[1], t_out);
 }
 template <int MODE, int WG, bool DEC = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))

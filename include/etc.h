@@ -239,7 +239,10 @@ typedef struct {
  * words [16 + 8r, 16 + 8r + 8), workgroup w's records start at r = w*per_wg:
  *   workgroup | task type << 24 (type 1..7 = R, K, S, D, G1, G2, C; type 8 =
  *   the routing tables a workgroup rebuilds in its LDS for a small batch,
- *   waiting on the route event), task
+ *   waiting on the route event; 9..14 = the decoder layer's N1, QKV,
+ *   attention, merge, output projection, N2; type 15 = the workgroup
+ *   itself, its last record: entry, counter set known, end of its task
+ *   lists, after its exit arrival), task
  *   index a, b, then wall-clock ticks: before the task's wait (low, high 32
  *   bits), and the low 32 bits after the wait, after the task body, and after
  *   its notifies.  Ticks are those of the device's constant wall clock

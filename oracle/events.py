@@ -170,7 +170,7 @@ def run_dynamic(tasks: List[Task], state: EventState, seed: int = 0) -> List[int
 
 def run_ordered(tasks: List[Task], state: EventState, workers: int,
                 phases: Sequence[Tuple[str, Sequence[int]]], groups: int = 8, ahead: int = 3,
-                seed: int = 0, dealt: int = 0) -> List[int]:
+                seed: int = 0, dealt: int = 0, swap: int = -1) -> List[int]:
     """Workers go through `phases` in order.  A ("deal", ids) phase gives
     worker w every task ids[i] with (i + off) % workers == w, where off is
     the number of tasks dealt in earlier phases (round-robin continuing from
@@ -182,7 +182,9 @@ def run_ordered(tasks: List[Task], state: EventState, workers: int,
     until an ordinal falls past the end.  With `dealt` = d > 0 the first d
     of a worker's `ahead` tasks are dealt instead (worker w gets ids[w],
     ids[workers + w], ...) and ordinal k of group g is ids[d * workers +
-    k * ngroups + g].  Each step advances one worker
+    k * ngroups + g].  With `swap` = s >= 0, workers s and workers - 1
+    exchange their dealt tasks (the small-batch runner hands the worker
+    that ran S the last dealt slot).  Each step advances one worker
     chosen at random (random speeds); a worker whose next task waits on an
     unreleased event stalls.  Returns the completion order; raises
     RuntimeError on deadlock."""
@@ -203,7 +205,8 @@ def run_ordered(tasks: List[Task], state: EventState, workers: int,
             if mode == "deal":
                 queue[w] = [ids[i] for i in range(len(ids)) if (i + offs[phase[w]]) % workers == w]
             else:
-                queue[w] = [ids[r * workers + w] for r in range(dealt) if r * workers + w < len(ids)]
+                v = workers - 1 if w == swap else (swap if (swap >= 0 and w == workers - 1) else w)
+                queue[w] = [ids[r * workers + v] for r in range(dealt) if r * workers + v < len(ids)]
                 for _ in range(ahead - dealt):
                     claim(w)
             if queue[w]:

@@ -140,6 +140,8 @@ def test_task_trace(qwen_weights, decode_case, sched):
               7: -(-T // info.combine_tokens)}
     assert {t: int((typ == t).sum()) for t in expect} == expect
     assert wg.max() < info.grid
+    # one entry/exit record a workgroup (type 15), every workgroup once
+    assert sorted(wg[typ == 15].tolist()) == list(range(info.grid))
     tw = (rec[:, 4] << 32) | rec[:, 3]
     stamps = [tw] + [((rec[:, 4] << 32) | rec[:, j]) for j in (5, 6, 7)]
     stamps = [np.where(t < tw, t + (1 << 32), t) for t in stamps]

@@ -518,13 +518,15 @@ def test_ordered_claims_complete_the_moe_graph(workers, seed):
 @pytest.mark.parametrize("seed", range(3))
 def test_ordered_small_batch_runner_completes_the_moe_graph(workers, seed):
     # The small-batch form: one counter for all workers, each worker's first
-    # two G tiles dealt (w, workers + w), then one claim per finished tile,
-    # two tiles held.  With fewer tiles than two per worker (40 workers)
-    # some workers get one dealt tile or none and claim nothing.
+    # two G tiles dealt (w, workers + w; the worker that ran S and worker
+    # workers - 1 swap theirs), then one claim per finished tile, two tiles
+    # held.  With fewer tiles than two per worker (40 workers) some workers
+    # get one dealt tile or none and claim nothing.
     tasks, st, ph = _moe_layer_graph(T=12, E=8, k=2, bm=4, n1=3, n2=2, seed=seed)
     phases = [("deal", ph["R"]), ("deal", ph["K"]), ("deal", ph["S"]), ("claim", ph["G1"] + ph["G2"]),
               ("deal", ph["C"])]
-    order = ev.run_ordered(tasks, st, workers, phases, groups=1, ahead=2, dealt=2, seed=seed)
+    s_worker = (len(ph["R"]) + len(ph["K"])) % workers
+    order = ev.run_ordered(tasks, st, workers, phases, groups=1, ahead=2, dealt=2, seed=seed, swap=s_worker)
     assert sorted(order) == list(range(len(tasks))) and not st.errors
     assert all(v == 1 for v in st.fired.values())
 
