@@ -260,6 +260,38 @@ __device__ __forceinline__ void notify_fast(const MoeParams& p, const Ctx& c, ui
 // the bias.  This fixed order is what makes the top-k decision reproducible
 // bit for bit.  A batch of four chunks per lane is loaded before its
 // arithmetic.
+// The big-tile router stream's logits, after the butterfly: every lane
+// holds every sum (each xor step adds the same two values in either order,
+// so all 64 lanes end with lane 0's bits).  Lane r stores token r's EPW
+// logits as 16-byte stores of four consecutive experts, EPW / 4 of them,
+// instead of lane 0 storing 4 * EPW values one by one (the token index stays
+// a compile-time constant: a lane-indexed pick would put the sums in
+// scratch memory).  Full tiles only: E a multiple of 4 * EPW.
+template <int EPW>
+__device__ __forceinline__ void router_store_tile(const MoeParams& p, const Ctx& c, int t0, int e0,
+                                                  const float (&acc)[EPW][kRouterT]) {
+  static_assert(EPW % 4 == 0, "four consecutive experts a store");
+  const int lane = threadIdx.x & 63;
+  const rsrc_t rl = r_logits(p);
+#pragma unroll
+  for (int r = 0; r < kRouterT; ++r) {
+    if (lane != r) continue;
+    float v[EPW];
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) v[j] = p.has_bias ? acc[j][r] + p.br[e0 + j] : acc[j][r];
+    const uint32_t off = (uint32_t)((t0 + r) * c.E + e0) * 4u;
+#pragma unroll
+    for (int q = 0; q < EPW / 4; ++q) {
+      u32x4_t o;
+      o.x = __float_as_uint(v[4 * q]);
+      o.y = __float_as_uint(v[4 * q + 1]);
+      o.z = __float_as_uint(v[4 * q + 2]);
+      o.w = __float_as_uint(v[4 * q + 3]);
+      co_st128(rl, off + 16u * q, o);
+    }
+  }
+}
+
 template <int EPW, int U>
 __device__ __forceinline__ void router_body(const MoeParams& p, const Ctx& c, int tt, int et) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -428,7 +460,6 @@ __device__ __forceinline__ void router_stream(const MoeParams& p, const Ctx& c, 
       }
     }
   };
-  const rsrc_t rl = r_logits(p);
   load(i0, 0, xa, wa);
   for (int i = i0; i < c.nR; i += G) {
     uint64_t tw = 0;
@@ -454,17 +485,7 @@ __device__ __forceinline__ void router_stream(const MoeParams& p, const Ctx& c, 
 #pragma unroll
         for (int s2 = 32; s2 >= 1; s2 >>= 1) acc[j][r] = acc[j][r] + __shfl_xor(acc[j][r], s2);
       }
-    if (lane == 0) {
-      const int t0 = (i / c.nET) * kRouterT, e0 = (i % c.nET) * 4 * EPW + wv * EPW;
-#pragma unroll
-      for (int j = 0; j < EPW; ++j)
-#pragma unroll
-        for (int r = 0; r < kRouterT; ++r) {
-          float v = acc[j][r];
-          if (p.has_bias) v = v + p.br[e0 + j];
-          co_stf(rl, (uint32_t)((t0 + r) * c.E + e0 + j) * 4u, v);
-        }
-    }
+    router_store_tile<EPW>(p, c, (i / c.nET) * kRouterT, (i % c.nET) * 4 * EPW + wv * EPW, acc);
     dbg_task(p, TT_R);
     if (tr) {
       const uint64_t tb = now_ticks();
@@ -2531,6 +2552,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 moe_persistent(MoeParams p) {
   persistent_body<MODE, WG, DEC>(p);
 }
+// The small- and large-batch kernels are instantiated here, ahead of the
+// big-tile kernels, so that their place in the code object does not move
+// when a big-tile kernel changes size (the same instructions, moved, were
+// measured up to 1.5 us a decode layer apart).
+template __global__ void moe_persistent<MODE_ORDERED, kVarSmall, false>(MoeParams);
+template __global__ void moe_persistent<MODE_STATIC, kVarSmall, false>(MoeParams);
+template __global__ void moe_persistent<MODE_BARRIER, kVarSmall, false>(MoeParams);
+template __global__ void moe_persistent<MODE_DYNAMIC, kVarSmall, false>(MoeParams);
+template __global__ void moe_persistent<MODE_ORDERED, kVarWide, false>(MoeParams);
+template __global__ void moe_persistent<MODE_STATIC, kVarWide, false>(MoeParams);
+template __global__ void moe_persistent<MODE_BARRIER, kVarWide, false>(MoeParams);
+template __global__ void moe_persistent<MODE_DYNAMIC, kVarWide, false>(MoeParams);
 // The big-tile variant: one workgroup a CU (its G tiles take 128 KB of LDS
 // and the full register file), so its G bodies may keep 256 accumulators.
 template <int MODE>
