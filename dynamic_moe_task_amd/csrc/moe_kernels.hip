@@ -594,6 +594,96 @@ __device__ __forceinline__ void task_topk(const MoeParams& p, const Ctx& c, int 
   }
 }
 
+// K over up to NT of a workgroup's token tiles at once (k0, k0 + G, ...,
+// n of them): wave w takes token tile * kRouterT + w of each, issues the
+// logit loads of all of them together and runs their selections side by
+// side, so the tiles cost about one memory latency instead of one each.
+// Per token the arithmetic is task_topk's: the same maximum, tie rule,
+// weights and stores.  The routed pairs join their experts' events through
+// the LDS histogram `hist`.
+template <int NT>
+__device__ __forceinline__ void task_topk_n(const MoeParams& p, const Ctx& c, int k0, int G, int n, int* hist) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const float NEG_INF = -__builtin_inff();
+  const rsrc_t rl = r_logits(p);
+  int t[NT];
+  bool live[NT];
+  float v[NT][4];
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    t[i] = (k0 + i * G) * kRouterT + wv;
+    live[i] = i < n && t[i] < c.T;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      float x = NEG_INF;
+      if (live[i] && e < c.E) {
+        x = co_ldf(rl, (uint32_t)(t[i] * c.E + e) * 4u);
+        if (x != x) { bad = true; x = NEG_INF; }
+      }
+      v[i][j] = x;
+    }
+  }
+  if (__any(bad) && lane == 0) or_relaxed(c.status, ST_NONFINITE);
+  uint32_t avail[NT];
+  float my_v[NT], v0[NT];
+  int my_e[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    avail[i] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j < c.E) avail[i] |= 1u << j;
+    my_v[i] = 0.0f;
+    v0[i] = 0.0f;
+    my_e[i] = 0;
+  }
+  for (int r = 0; r < c.k; ++r) {
+    float m[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      float lv = NEG_INF;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((avail[i] >> j) & 1u) lv = fmaxf(lv, v[i][j]);
+      m[i] = wave_max(lv);
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      int be = -1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const unsigned long long hit = __ballot(((avail[i] >> j) & 1u) && v[i][j] == m[i]);
+        if (be < 0 && hit) be = 64 * j + (__ffsll(hit) - 1);
+      }
+      if ((be & 63) == lane) avail[i] &= ~(1u << (be >> 6));
+      if (lane == r) { my_v[i] = m[i]; my_e[i] = be; }
+      if (r == 0) v0[i] = m[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    float part = 0.0f;
+    if (p.norm_topk) {
+      if (lane < c.k) part = expf(my_v[i] - v0[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (lane + 64 * j < c.E) part += expf(v[i][j] - v0[i]);
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) part = part + __shfl_xor(part, s);
+    if (live[i] && lane < c.k) {
+      const uint32_t off = (uint32_t)(t[i] * c.k + lane) * 4u;
+      co_st32(r_ids(p), off, (uint32_t)my_e[i]);
+      co_stf(r_topw(p), off, expf(my_v[i] - v0[i]) / part);
+      atomicAdd(hist + my_e[i], 1);
+      if (p.debug) atomicAdd(p.debug + my_e[i], 1);
+    }
+  }
+}
+
 // N exclusive scans at once over the workgroup (one pair of barriers for
 // all of them); tmp holds 4 * N ints.
 template <int N>
@@ -2238,10 +2328,9 @@ __device__ __forceinline__ void run_lists(const MoeParams& p, const Ctx& c, uint
     for (int e = threadIdx.x; e < c.E; e += kThreads) khist[e] = 0;
     if (__syncthreads_or(fail)) return;
     if (tr) ts = now_ticks();
-    for (int i = k0; i < c.nK; i += G) {
-      task_topk(p, c, i, khist);
-      dbg_task(p, TT_K);
-    }
+    // four token tiles at a time, their loads and selections side by side
+    for (int q = 0; q < nmine; q += 4) task_topk_n<4>(p, c, k0 + q * G, G, min(4, nmine - q), khist);
+    for (int i = k0; i < c.nK; i += G) dbg_task(p, TT_K);
     if (tr) tb = now_ticks();
     __syncthreads();  // every task's LDS counts are in
     for (int e = threadIdx.x; e < c.E; e += kThreads)
